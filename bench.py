@@ -1,0 +1,274 @@
+"""CSA2 decode benchmark: layer-steps/s of one decode group (Full + Reindex + Reuse) at 1M
+context on one MI355X, with the scan kernel's HBM roofline and the CPU oracle beside it.
+
+A step is one decode group over the whole batch: for every layer the current token's window
+row is appended, the Full layer also appends its global-KV row and runs the full indexer,
+Reindex rescores the pool, Reuse keeps the previous top-k, and every layer runs sparse
+attention.  Inputs are seeded synthetic tensors resident in HBM before timing starts.  Each
+step uses the next of R cache replicas so the 256 MB Infinity Cache cannot hold the
+working set; the group is replayed from a HIP graph (one per replica).
+
+Prints ONE JSON line.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+for p in (ROOT, os.path.join(ROOT, "tests")):
+    if p not in sys.path:
+        sys.path.insert(0, p)
+
+import numpy as np  # noqa: E402
+import torch  # noqa: E402
+
+METRIC = "CSA2 decode layer-steps/s at 1M ctx (Full+Reindex+Reuse); % HBM roofline"
+HBM_PEAK_GBS = 8000.0
+SCAN_KERNEL = "k_scan"
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", default="long_1m")
+    ap.add_argument("--replicas", type=int, default=0, help="0 = enough for >= 1 GiB")
+    ap.add_argument("--scan-reps", type=int, default=40)
+    ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--eager", action="store_true", help="no HIP graph")
+    return ap.parse_args()
+
+
+class Bench:
+    def __init__(self, wl, replicas):
+        import kv_cache_decode_csa2_amd as k
+        import synth_inputs as si
+        from gpu_harness import GpuState, dev
+        from harness import make_table
+
+        self.k, self.wl = k, wl
+        table, nblk = make_table(wl.ctx, seed=wl.seed, permute=False)
+        t0 = time.time()
+        g = GpuState(wl, table, nblk, with_latent=True)
+        log(f"caches built in {time.time() - t0:.1f}s")
+        self.g = g
+        self.cfg = g.cfg
+        per_rep = g.kv.numel() + g.idx.numel()
+        R = replicas or max(2, int(np.ceil((1 << 30) / per_rep)))
+        self.kv = [g.kv] + [g.kv.clone() for _ in range(R - 1)]
+        self.idx = [g.idx] + [g.idx.clone() for _ in range(R - 1)]
+        self.R = R
+        B, maxb = table.shape
+        self.maxb = maxb
+        # per-layer inputs
+        self.layers = []
+        for li, mode in enumerate(wl.layers):
+            qc, qs, w = g.layer_q(li)
+            swa = g.layer_swa(li)
+            last = np.asarray(wl.ctx, np.int64) - 1
+            lay = dict(mode=mode, qc=qc, qs=qs, w=w, q=g.attn_q(li), swa=swa,
+                       swa_row=dev(np.stack([si.layer_swa_rows(wl, li, b, min(wl.ctx[b], wl.W))[-1]
+                                             for b in range(B)])),
+                       pos=dev(last.astype(np.int32)))
+            self.layers.append(lay)
+        # the current token's global row (position L-1), re-appended every step
+        self.tok_lat = dev(np.stack([si.latent_rows(wl, b, wl.ctx[b])[-1] for b in range(B)]))
+        self.tok_key = dev(np.stack([si.idx_keys(wl, b)[-1] for b in range(B)]))
+        self.ws = [torch.zeros(k.csa2_workspace_bytes(self.cfg, k.CSA2_OP_INDEX_FULL, B, maxb),
+                               dtype=torch.uint8, device="cuda") for _ in range(R)]
+        self.ws_attn = torch.empty(k.csa2_workspace_bytes(self.cfg, k.CSA2_OP_SPARSE_ATTN, B, maxb),
+                                   dtype=torch.uint8, device="cuda")
+        i32 = dict(dtype=torch.int32, device="cuda")
+        self.pool = torch.empty((B, wl.K_blk), **i32)
+        self.pool_len = torch.empty(B, **i32)
+        self.topk = torch.empty((B, wl.k), **i32)
+        self.topk_len = torch.empty(B, **i32)
+        self.out = torch.empty((B, wl.H_q, wl.D), dtype=torch.float32, device="cuda")
+        self.lse = torch.empty((B, wl.H_q), dtype=torch.float32, device="cuda")
+        torch.cuda.synchronize()
+
+    def step(self, r):
+        k, g, c = self.k, self.g, self.cfg
+        kv, idx, ws = self.kv[r], self.idx[r], self.ws[r]
+        for lay in self.layers:
+            if lay["mode"] == "F":
+                k.csa2_append_global(c, self.tok_lat, self.tok_key, g.table, g.n_blocks,
+                                     lay["pos"], 1, kv, idx)
+            k.csa2_append_swa(c, lay["swa_row"], lay["pos"], 1, lay["swa"], g.C)
+            if lay["mode"] == "F":
+                k.csa2_index_full(c, lay["qc"], lay["qs"], lay["w"], idx, g.n_blocks, g.table,
+                                  g.ctx, self.pool, self.pool_len, self.topk, self.topk_len, ws)
+            elif lay["mode"] == "R":
+                k.csa2_index_reindex(c, lay["qc"], lay["qs"], lay["w"], idx, g.n_blocks, g.table,
+                                     g.ctx, self.pool, self.pool_len, self.topk, self.topk_len, ws)
+            k.csa2_sparse_attn(c, lay["q"], kv, g.n_blocks, g.table, lay["swa"], g.C, g.ctx,
+                               self.topk, self.topk_len, self.out, self.lse, self.ws_attn)
+
+    def scan(self, r):
+        lay = self.layers[0]
+        self.k.csa2_index_full_scan(self.cfg, lay["qc"], lay["qs"], lay["w"], self.idx[r],
+                                    self.g.n_blocks, self.g.table, self.g.ctx, self.ws[r])
+
+
+def capture(fn):
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        fn()  # one eager run on the side stream before capture
+    torch.cuda.current_stream().wait_stream(s)
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        fn()
+    return graph
+
+
+def timed(fn, n):
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record()
+    for i in range(n):
+        fn(i)
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / n
+
+
+def algorithmic_bytes(wl, layout):
+    """Bytes the method must move per group (see the measurement notes of the design)."""
+    B = wl.B
+    idx_pos = layout.idx_block_bytes // 8
+    L = np.asarray(wl.ctx, np.int64)
+    scan = int(L.sum()) * idx_pos
+    pool_pos = int(np.minimum(L, wl.K_blk * 8).sum())
+    reindex = pool_pos * idx_pos
+    rows_main = int(np.minimum(L, wl.k).sum()) * layout.kv_row_bytes
+    rows_win = int(np.minimum(L, wl.W).sum()) * layout.swa_row_bytes
+    qio = B * wl.H_q * (wl.D * 2 + wl.D * 4 + 4)
+    attn = rows_main + rows_win + qio
+    n_r = wl.layers.count("R")
+    total = scan + n_r * reindex + len(wl.layers) * attn
+    return dict(scan=scan, reindex=reindex, attn=attn, total=total)
+
+
+def cpu_baseline(wl, seconds):
+    import oracle
+    from harness import OracleState, make_table
+    table, nblk = make_table(wl.ctx, seed=wl.seed, permute=False)
+    t0 = time.time()
+    o = OracleState(wl, table, nblk, with_latent=True)
+    log(f"oracle caches built in {time.time() - t0:.1f}s")
+    ins = []
+    for li, mode in enumerate(wl.layers):
+        ins.append((mode, o.layer_q(li), o.layer_swa(li)))
+    import synth_inputs as si
+    qa = [si.layer_attn_q(wl, li) for li in range(len(wl.layers))]
+    groups = 0
+    t0 = time.time()
+    while True:
+        pool = topk = None
+        for li, (mode, q, swa) in enumerate(ins):
+            if mode == "F":
+                p, pl, t, tl = oracle.index_full(o.cfg, *q, o.idx, o.table, o.ctx)
+                pool, topk = (p, pl), (t, tl)
+            elif mode == "R":
+                topk = oracle.index_reindex(o.cfg, *q, o.idx, o.table, o.ctx, *pool)
+            oracle.sparse_attn(o.cfg, qa[li], o.kv, o.table, swa, o.C, o.ctx, *topk)
+        groups += 1
+        el = time.time() - t0
+        if el >= seconds:
+            break
+    try:
+        cores = len(os.sched_getaffinity(0))
+    except AttributeError:
+        cores = os.cpu_count()
+    cores = int(os.environ.get("OMP_NUM_THREADS", cores))
+    return dict(value=groups * len(wl.layers) / el, unit="layer-steps/s", cores=cores,
+                kind="oracle",
+                sample=f"{groups} full {''.join(wl.layers)} groups of the {wl.name} workload "
+                       f"(all {sum(wl.ctx)} positions scanned per Full layer), {el:.1f} s wall")
+
+
+def traffic_for(kernel_src_hash):
+    path = os.path.join(ROOT, "profiles", "scan_long_1m_counters.json")
+    try:
+        with open(path) as f:
+            d = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if d.get("source_sha256") != kernel_src_hash:
+        return None
+    return d.get("bytes_per_launch")
+
+
+def main():
+    a = parse()
+    if a.gpus != 1:
+        print(json.dumps({"error": "this build runs on one GPU; --gpus must be 1 (multi-GPU "
+                                   "sharding is a design note, not implemented)"}))
+        sys.exit(2)
+    import hashlib
+
+    import synth_inputs as si
+    wl = si.workload(a.workload)
+    torch.cuda.set_device(0)
+    bench = Bench(wl, a.replicas)
+    layout = bench.k.csa2_layout(bench.cfg)
+    ab = algorithmic_bytes(wl, layout)
+    R = bench.R
+    log(f"workload {wl.name}: {R} replicas, algorithmic bytes/group {ab['total'] / 1e6:.1f} MB")
+
+    if a.eager:
+        step = lambda i: bench.step(i % R)  # noqa: E731
+    else:
+        graphs = [capture(lambda r=r: bench.step(r)) for r in range(R)]
+        step = lambda i: graphs[i % R].replay()  # noqa: E731
+    timed(step, a.warmup)
+    ms = timed(step, a.steps)
+    n_layers = len(wl.layers)
+    value = n_layers / (ms / 1e3)
+    log(f"group {ms * 1e3:.1f} us -> {value:.0f} layer-steps/s")
+
+    # scan kernel alone: a graph of back-to-back scans over rotating replicas
+    reps = a.scan_reps
+    sg = capture(lambda: [bench.scan(i % R) for i in range(reps)])
+    timed(lambda i: sg.replay(), 2)
+    scan_ms = timed(lambda i: sg.replay(), 5) / reps
+    achieved = ab["scan"] / (scan_ms / 1e3) / 1e9
+    src = open(os.path.join(ROOT, "kv_cache_decode_csa2_amd", "csrc", "csa2_index.hip"), "rb").read()
+    traffic = traffic_for(hashlib.sha256(src).hexdigest())
+    log(f"scan {scan_ms * 1e3:.2f} us -> {achieved:.0f} GB/s")
+
+    result = {
+        "metric": METRIC, "value": round(value, 1), "unit": "layer-steps/s", "n_gpus": 1,
+        "steps": a.steps, "warmup": a.warmup, "ms_per_step": round(ms, 5),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "mxfp4",
+        "data": "synthetic",
+        "config": {"workload": wl.name, "batch": wl.B, "context": wl.max_ctx,
+                   "indexer": f"{wl.H_I}x{wl.d_I} fp4", "pool_blocks": wl.K_blk, "topk": wl.k,
+                   "q_heads": wl.H_q, "window": wl.W, "layers": wl.layers,
+                   "replicas": R, "graph": not a.eager},
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                     "traffic": traffic, "kernel": SCAN_KERNEL,
+                     "kernel_us": round(scan_ms * 1e3, 3), "algorithmic_bytes": ab["scan"]},
+        "group": {"algorithmic_bytes": ab["total"],
+                  "hbm_frac": round(ab["total"] / (ms / 1e3) / 1e9 / HBM_PEAK_GBS, 4)},
+        "cpu_baseline": None,
+    }
+    if not a.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(wl, a.cpu_seconds)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,333 @@
+// csa2_attn.hip -- sparse attention over the selected FP4 main-KV rows plus the FP8
+// sliding window, one softmax per (sequence, head).
+//
+// The pages: Reuse layers only run attention over reused indices, every decoder layer
+// keeps a local window (dbyun.net/article/10794, "KV Cache 成为这一代架构改造的核心";
+// 10100.com/article/150771503, "三招压缩，各有分工"); the window is 128 tokens
+// (prism.simon-ai.net/article/7901, "短期记忆的去留：从SSD存储到GPU重算").  The attention
+// form itself is this library's reading: K = V = the dequantised 512-d latent (or window
+// row), shared by all H_q query heads; logits sm_scale * q.k; selected and window rows are
+// not de-duplicated.
+//
+// Work split: the row list of a sequence is [0, k) = top-k entries (padding masked),
+// then [k, k+W) = window positions; workgroup (split, b) owns 64 consecutive rows.
+//   1. Each lane gathers one row's 128-dim quarter straight from HBM and converts it to
+//      bf16 with the gfx950 scaled converters (exact: E2M1 / E4M3 values times a power of
+//      two fit bf16).  Those registers are the B operand of S = Q K^T on MFMA
+//      16x16x32 bf16 (fp32 accumulation); the same values go to LDS transposed (V^T).
+//   2. Softmax statistics per head over the 64 rows (wave shuffles + LDS).
+//   3. O += P V on MFMA with P split into bf16 hi + lo parts (error ~2^-17 relative).
+//   4. Partial (O, max, sum) per split -> k_attn_merge combines the splits.
+#include "csa2_common.h"
+
+namespace csa2 {
+
+constexpr int kAttnThreads = 256;
+constexpr int kD = 512;            // latent dim handled by these kernels
+constexpr int kPStride = 64 + 4;   // padded row of the P tile (floats)
+
+struct AttnArgs {
+    const uint16_t *q;
+    const uint8_t *kv;
+    int64_t n_blocks;
+    const int32_t *table;
+    int32_t maxb;
+    const uint8_t *swa;
+    int32_t C;
+    const int32_t *ctx_len;
+    int32_t B;
+    const int32_t *topk;
+    const int32_t *topk_len;
+    int32_t k;
+    int32_t W;
+    int32_t Hq;
+    float scale_log2;  // sm_scale * log2(e)
+    float sm_scale;
+    int32_t nsplit;
+    float *part_o;
+    float *part_ml;
+    float *out;
+    float *lse;
+};
+
+__device__ __forceinline__ int clamp_ctx(int32_t L, int maxb) {
+    const int64_t cap = (int64_t)maxb * kBlk;
+    return L < 0 ? 0 : (int)(L > cap ? cap : L);
+}
+
+__device__ __forceinline__ uint32_t word_of(const uint4 &u, int i) {
+    return i == 0 ? u.x : i == 1 ? u.y : i == 2 ? u.z : u.w;
+}
+
+__device__ __forceinline__ bf16x8_t join4(bf16x2_t a, bf16x2_t b, bf16x2_t c, bf16x2_t d) {
+    bf16x8_t v;
+    v[0] = a[0]; v[1] = a[1]; v[2] = b[0]; v[3] = b[1];
+    v[4] = c[0]; v[5] = c[1]; v[6] = d[0]; v[7] = d[1];
+    return v;
+}
+
+// Position in the swizzled V^T tile [512][64] of element (dim d, row r): 8-row chunks are
+// XOR-permuted by (d >> 1) & 7 so that 16 lanes reading 16 consecutive d hit all banks.
+__device__ __forceinline__ int vt_index(int d, int r) {
+    return d * 64 + ((((r >> 3) ^ (d >> 1)) & 7) << 3) + (r & 7);
+}
+
+__global__ __launch_bounds__(kAttnThreads) void k_attn_split(AttnArgs a) {
+    __shared__ __align__(16) __bf16 vt[kD * 64];
+    __shared__ __align__(16) float ptile[16 * kPStride];
+    __shared__ float red_m[4][16], red_l[4][16];
+    __shared__ int any_valid;
+
+    const int s = blockIdx.x, b = blockIdx.y;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int c16 = lane & 15, g4 = lane >> 4;
+    const int L = clamp_ctx(a.ctx_len[b], a.maxb);
+    const int tl = max(0, min(a.topk_len[b], a.k));
+    const int w0 = max(0, L - a.W), nwin = L - w0;
+    const int r_loc = 16 * wave + c16;
+    const int rg = s * kAttnRows + r_loc;
+
+    // ---- locate this lane's row
+    const uint8_t *rp = nullptr;
+    bool fp8 = false;
+    if (rg < a.k) {
+        if (rg < tl) {
+            const int p = a.topk[(int64_t)b * a.k + rg];
+            if (p >= 0 && p < L) {
+                const int64_t phys = a.table[(int64_t)b * a.maxb + p / kBlk];
+                if (phys >= 0 && phys < a.n_blocks)
+                    rp = a.kv + phys * (kBlk * (kD / 2 + kD / 32)) + (p % kBlk) * (kD / 2 + kD / 32);
+            }
+        }
+    } else {
+        const int wi = rg - a.k;
+        if (wi < nwin && wi < a.W) {
+            const int p = w0 + wi;
+            rp = a.swa + ((int64_t)b * a.C + p % a.C) * (kD + kD / 32);
+            fp8 = true;
+        }
+    }
+    const bool valid = rp != nullptr;
+    if (tid == 0) any_valid = 0;
+    __syncthreads();
+    if (valid) any_valid = 1;
+    __syncthreads();
+    const int64_t pbase = ((int64_t)b * a.nsplit + s) * a.Hq;
+    if (!any_valid) {
+        for (int h = tid; h < a.Hq; h += kAttnThreads) {
+            a.part_ml[2 * (pbase + h)] = -INFINITY;
+            a.part_ml[2 * (pbase + h) + 1] = 0.0f;
+        }
+        return;
+    }
+
+    // ---- gather + exact conversion to bf16: kb[t] = dims g4*128 + 8t .. +8 of the row
+    bf16x8_t kb[16];
+    if (valid && !fp8) {
+        const uint4 *src = reinterpret_cast<const uint4 *>(rp + g4 * 64);
+        const uint4 u0 = src[0], u1 = src[1], u2 = src[2], u3 = src[3];
+        const uint32_t sc4 = *reinterpret_cast<const uint32_t *>(rp + kD / 2 + 4 * g4);
+        const uint4 uu[4] = {u0, u1, u2, u3};
+#pragma unroll
+        for (int t = 0; t < 16; t++) {
+            const uint32_t wd = word_of(uu[t >> 2], t & 3);
+            const float sc = e8m0_to_f32((sc4 >> (8 * (t >> 2))) & 255u);
+            kb[t] = join4(__builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(wd, sc, 0),
+                          __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(wd, sc, 1),
+                          __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(wd, sc, 2),
+                          __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(wd, sc, 3));
+        }
+    } else if (valid) {
+        const uint4 *src = reinterpret_cast<const uint4 *>(rp + g4 * 128);
+        uint4 uu[8];
+#pragma unroll
+        for (int i = 0; i < 8; i++) uu[i] = src[i];
+        const uint32_t sc4 = *reinterpret_cast<const uint32_t *>(rp + kD + 4 * g4);
+#pragma unroll
+        for (int t = 0; t < 16; t++) {
+            const uint32_t w0d = word_of(uu[t >> 1], 2 * (t & 1)), w1d = word_of(uu[t >> 1], 2 * (t & 1) + 1);
+            const float sc = e8m0_to_f32((sc4 >> (8 * (t >> 2))) & 255u);
+            kb[t] = join4(__builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w0d, sc, false),
+                          __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w0d, sc, true),
+                          __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w1d, sc, false),
+                          __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w1d, sc, true));
+        }
+    } else {
+#pragma unroll
+        for (int t = 0; t < 16; t++)
+#pragma unroll
+            for (int i = 0; i < 8; i++) kb[t][i] = (__bf16)0.0f;
+    }
+
+    // ---- V^T into LDS
+#pragma unroll
+    for (int t = 0; t < 16; t++)
+#pragma unroll
+        for (int i = 0; i < 8; i++) vt[vt_index(g4 * 128 + 8 * t + i, r_loc)] = kb[t][i];
+    __syncthreads();
+
+    for (int hg = 0; hg < a.Hq / 16; hg++) {
+        // ---- S = Q K^T for this wave's 16 rows and 16 heads
+        const uint16_t *qh = a.q + ((int64_t)b * a.Hq + hg * 16 + c16) * kD + g4 * 128;
+        f32x4_t acc = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+        for (int t = 0; t < 16; t++) {
+            const bf16x8_t qa = *reinterpret_cast<const bf16x8_t *>(qh + 8 * t);
+            acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa, kb[t], acc, 0, 0, 0);
+        }
+        // lane holds S[head 4*g4 + j][row c16 of this wave]
+        float sv[4], mx[4];
+#pragma unroll
+        for (int j = 0; j < 4; j++) {
+            sv[j] = valid ? acc[j] : -INFINITY;
+            float m = sv[j];
+            m = fmaxf(m, __shfl_xor(m, 1, kWave));
+            m = fmaxf(m, __shfl_xor(m, 2, kWave));
+            m = fmaxf(m, __shfl_xor(m, 4, kWave));
+            m = fmaxf(m, __shfl_xor(m, 8, kWave));
+            mx[j] = m;
+        }
+        if (c16 == 0)
+#pragma unroll
+            for (int j = 0; j < 4; j++) red_m[wave][4 * g4 + j] = mx[j];
+        __syncthreads();
+        float pv[4], ls[4];
+#pragma unroll
+        for (int j = 0; j < 4; j++) {
+            const int h = 4 * g4 + j;
+            const float M = fmaxf(fmaxf(red_m[0][h], red_m[1][h]), fmaxf(red_m[2][h], red_m[3][h]));
+            pv[j] = valid ? exp2f((sv[j] - M) * a.scale_log2) : 0.0f;
+            float l = pv[j];
+            l += __shfl_xor(l, 1, kWave);
+            l += __shfl_xor(l, 2, kWave);
+            l += __shfl_xor(l, 4, kWave);
+            l += __shfl_xor(l, 8, kWave);
+            ls[j] = l;
+            ptile[h * kPStride + r_loc] = pv[j];
+        }
+        if (c16 == 0)
+#pragma unroll
+            for (int j = 0; j < 4; j++) red_l[wave][4 * g4 + j] = ls[j];
+        __syncthreads();
+        if (tid < 16) {
+            const int h = tid;
+            const float M = fmaxf(fmaxf(red_m[0][h], red_m[1][h]), fmaxf(red_m[2][h], red_m[3][h]));
+            const float l = red_l[0][h] + red_l[1][h] + red_l[2][h] + red_l[3][h];
+            a.part_ml[2 * (pbase + hg * 16 + h)] = M;
+            a.part_ml[2 * (pbase + hg * 16 + h) + 1] = l;
+        }
+
+        // ---- O = P V for this wave's 8 column tiles (128 dims)
+        bf16x8_t ph[2], plo[2];
+#pragma unroll
+        for (int ks = 0; ks < 2; ks++) {
+            const float4 *pr = reinterpret_cast<const float4 *>(ptile + c16 * kPStride + 32 * ks + 8 * g4);
+            const float4 x0 = pr[0], x1 = pr[1];
+            const float f[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
+#pragma unroll
+            for (int i = 0; i < 8; i++) {
+                const __bf16 hi = (__bf16)f[i];
+                ph[ks][i] = hi;
+                plo[ks][i] = (__bf16)(f[i] - (float)hi);
+            }
+        }
+        float *po = a.part_o + (pbase + hg * 16) * kD;
+#pragma unroll
+        for (int n = 0; n < 8; n++) {
+            const int nt = 8 * wave + n;
+            const int d = 16 * nt + c16;
+            f32x4_t o = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+            for (int ks = 0; ks < 2; ks++) {
+                const int chunk = 4 * ks + g4;
+                const bf16x8_t vb = *reinterpret_cast<const bf16x8_t *>(
+                    &vt[d * 64 + (((chunk ^ (d >> 1)) & 7) << 3)]);
+                o = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ph[ks], vb, o, 0, 0, 0);
+                o = __builtin_amdgcn_mfma_f32_16x16x32_bf16(plo[ks], vb, o, 0, 0, 0);
+            }
+#pragma unroll
+            for (int j = 0; j < 4; j++) po[(4 * g4 + j) * kD + d] = o[j];
+        }
+        __syncthreads();  // ptile / red reused by the next head group
+    }
+}
+
+// Combine the splits: out = sum_s 2^((m_s - M) c) O_s / sum_s 2^((m_s - M) c) l_s.
+__global__ __launch_bounds__(128) void k_attn_merge(AttnArgs a) {
+    const int h = blockIdx.x, b = blockIdx.y, tid = threadIdx.x;
+    const int64_t base = (int64_t)b * a.nsplit * a.Hq;
+    float M = -INFINITY;
+    for (int s = 0; s < a.nsplit; s++) {
+        const int64_t i = base + (int64_t)s * a.Hq + h;
+        if (a.part_ml[2 * i + 1] > 0.0f) M = fmaxf(M, a.part_ml[2 * i]);
+    }
+    float4 acc = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+    float lw = 0.0f;
+    for (int s = 0; s < a.nsplit; s++) {
+        const int64_t i = base + (int64_t)s * a.Hq + h;
+        const float l = a.part_ml[2 * i + 1];
+        if (!(l > 0.0f)) continue;
+        const float wgt = exp2f((a.part_ml[2 * i] - M) * a.scale_log2);
+        lw += wgt * l;
+        const float4 v = reinterpret_cast<const float4 *>(a.part_o + i * kD)[tid];
+        acc.x += wgt * v.x;
+        acc.y += wgt * v.y;
+        acc.z += wgt * v.z;
+        acc.w += wgt * v.w;
+    }
+    float4 r = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+    if (lw > 0.0f) {
+        const float inv = 1.0f / lw;
+        r = make_float4(acc.x * inv, acc.y * inv, acc.z * inv, acc.w * inv);
+    }
+    reinterpret_cast<float4 *>(a.out + ((int64_t)b * a.Hq + h) * kD)[tid] = r;
+    if (tid == 0)
+        a.lse[(int64_t)b * a.Hq + h] = lw > 0.0f ? a.sm_scale * M + logf(lw) : -INFINITY;
+}
+
+}  // namespace csa2
+
+using namespace csa2;
+
+extern "C" int csa2_sparse_attn(const csa2_config *c, const uint16_t *q, const uint8_t *kv_cache,
+                                int64_t n_blocks, const int32_t *block_table, int32_t maxb,
+                                const uint8_t *swa_cache, int32_t C, const int32_t *ctx_len,
+                                int32_t batch, const int32_t *topk, const int32_t *topk_len,
+                                float *out, float *lse, void *ws, size_t ws_bytes,
+                                hipStream_t stream) {
+    if (!c || !q || !kv_cache || n_blocks <= 0 || !block_table || maxb <= 0 || !ctx_len ||
+        batch < 0 || !topk || !topk_len || !out || !lse || !ws || c->topk <= 0 ||
+        c->swa_window < 0 || c->n_q_heads <= 0 || c->kv_dim <= 0)
+        return CSA2_ERR_INVALID;
+    if (c->swa_window > 0 && (!swa_cache || C < c->swa_window)) return CSA2_ERR_INVALID;
+    if (c->kv_dim != kD || c->n_q_heads % 16 || c->n_q_heads > 128) return CSA2_ERR_UNSUPPORTED;
+    const int nsplit = attn_splits(c->topk, c->swa_window);
+    const WsAttn wl = ws_attn(batch, c->n_q_heads, c->kv_dim, nsplit);
+    if (ws_bytes < wl.total) return CSA2_ERR_WORKSPACE;
+    if (batch == 0) return CSA2_OK;
+    AttnArgs a{};
+    a.q = q;
+    a.kv = kv_cache;
+    a.n_blocks = n_blocks;
+    a.table = block_table;
+    a.maxb = maxb;
+    a.swa = swa_cache;
+    a.C = C > 0 ? C : 1;
+    a.ctx_len = ctx_len;
+    a.B = batch;
+    a.topk = topk;
+    a.topk_len = topk_len;
+    a.k = c->topk;
+    a.W = c->swa_window;
+    a.Hq = c->n_q_heads;
+    a.sm_scale = c->sm_scale;
+    a.scale_log2 = c->sm_scale * 1.4426950408889634f;
+    a.nsplit = nsplit;
+    a.part_o = (float *)((uint8_t *)ws + wl.part_o);
+    a.part_ml = (float *)((uint8_t *)ws + wl.part_ml);
+    a.out = out;
+    a.lse = lse;
+    k_attn_split<<<dim3(nsplit, batch), kAttnThreads, 0, stream>>>(a);
+    k_attn_merge<<<dim3(c->n_q_heads, batch), 128, 0, stream>>>(a);
+    return hipGetLastError() == hipSuccess ? CSA2_OK : CSA2_ERR_HIP;
+}

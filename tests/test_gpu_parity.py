@@ -1,0 +1,204 @@
+"""GPU parity: every step of the HIP path against the CPU oracle on the same seeded inputs.
+
+Bar: packed bytes, dequantised values, scores, block scores and index sets bit-exact;
+attention within 2e-3 of the fp64 oracle per (sequence, head) row (max_d |o - r| over
+max_d |r|) and 2e-3 * max(1, |lse|) on the log-sum-exp.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth_inputs as si
+from gpu_harness import GpuState, attn_close, dev
+from harness import OracleState, make_table
+
+pytestmark = pytest.mark.gpu
+
+
+def _np(t):
+    return t.detach().cpu().numpy()
+
+
+def _first_diff(a, b, n=5):
+    idx = np.argwhere(a != b)[:n]
+    return [(tuple(i), a[tuple(i)], b[tuple(i)]) for i in idx]
+
+
+# ------------------------------------------------------------------ codecs
+
+def _special_inputs(rng, e_max=120):
+    grid = np.array([0.0, 0.25, 0.5, 0.75, 1.0, 1.25, 1.5, 1.75, 2.0, 2.5, 3.0, 3.5, 4.0, 5.0,
+                     5.5, 6.0, 7.0, 7.99], np.float32)
+    rows = []
+    for e in (-130, -126, -20, -2, 0, 3, 60, e_max):
+        g = np.concatenate([[7.5], rng.choice(grid, 31) * rng.choice([-1.0, 1.0], 31)])
+        rows.append((g * np.float64(2.0) ** e).astype(np.float32))
+    rows.append(np.zeros(32, np.float32))
+    z = np.zeros(32, np.float32)
+    z[3] = -0.0
+    z[5] = -1e-40
+    rows.append(z)
+    rows.append(np.full(32, 1e-42, np.float32))
+    rows.append(np.array([3e38] + [-1e-3] * 31, np.float32))
+    return np.stack(rows)
+
+
+def test_quantize_fp4_bit_exact():
+    rng = np.random.default_rng(1)
+    x = np.concatenate([_special_inputs(rng).reshape(-1, 64),
+                        (rng.standard_normal((300, 64)) * 2.0 ** rng.integers(-20, 20, (300, 1))).astype(np.float32)])
+    oc, os_ = oracle.quantize_mxfp4(x)
+    gc = torch.empty(oc.shape, dtype=torch.uint8, device="cuda")
+    gs = torch.empty(os_.shape, dtype=torch.uint8, device="cuda")
+    import kv_cache_decode_csa2_amd as k
+    k.csa2_quantize_mxfp4(dev(x), gc, gs)
+    assert np.array_equal(_np(gs), os_), _first_diff(_np(gs), os_)
+    assert np.array_equal(_np(gc), oc), _first_diff(_np(gc), oc)
+
+
+def test_quantize_fp8_bit_exact():
+    rng = np.random.default_rng(2)
+    sp8 = _special_inputs(rng, e_max=100).astype(np.float64)
+    big = np.abs(sp8[:, 0]) > 1e36          # inputs must stay finite
+    sp8[~big, 0] = sp8[~big, 0] / 7.5 * 500.0
+    sp8 = sp8.astype(np.float32)
+    x = np.concatenate([sp8.reshape(-1, 64),
+                        (rng.standard_normal((300, 64)) * 2.0 ** rng.integers(-20, 20, (300, 1))).astype(np.float32)])
+    oc, os_ = oracle.quantize_mxfp8(x)
+    import kv_cache_decode_csa2_amd as k
+    gc = torch.empty(oc.shape, dtype=torch.uint8, device="cuda")
+    gs = torch.empty(os_.shape, dtype=torch.uint8, device="cuda")
+    k.csa2_quantize_mxfp8(dev(x), gc, gs)
+    assert np.array_equal(_np(gs), os_), _first_diff(_np(gs), os_)
+    assert np.array_equal(_np(gc), oc), _first_diff(_np(gc), oc)
+
+
+def test_dequant_bit_exact():
+    import kv_cache_decode_csa2_amd as k
+    rng = np.random.default_rng(3)
+    codes4 = np.tile(np.arange(256, dtype=np.uint8), 8).reshape(16, 128)
+    scales = rng.integers(60, 200, (16, 8), dtype=np.uint8)
+    ref4 = oracle.dequant_mxfp4(codes4, scales)
+    out = torch.empty((16, 256), dtype=torch.float32, device="cuda")
+    k.csa2_dequant_mxfp4(dev(codes4), dev(scales), out)
+    assert np.array_equal(_np(out).astype(np.float64), ref4), _first_diff(_np(out).astype(np.float64), ref4)
+    codes8 = np.tile(np.arange(256, dtype=np.uint8), 4).reshape(8, 128)
+    codes8[(codes8 & 0x7F) == 0x7F] = 0x00  # NaN codes are never produced
+    s8 = rng.integers(60, 200, (8, 4), dtype=np.uint8)
+    ref8 = oracle.dequant_mxfp8(codes8, s8)
+    out8 = torch.empty((8, 128), dtype=torch.float32, device="cuda")
+    k.csa2_dequant_mxfp8(dev(codes8), dev(s8), out8)
+    assert np.array_equal(_np(out8).astype(np.float64), ref8), _first_diff(_np(out8).astype(np.float64), ref8)
+
+
+# ------------------------------------------------------------------ caches and scores
+
+def _pair(wl, with_latent=True, permute=True):
+    table, nblk = make_table(wl.ctx, seed=wl.seed, permute=permute)
+    return OracleState(wl, table, nblk, with_latent), GpuState(wl, table, nblk, with_latent)
+
+
+def test_append_caches_bit_exact():
+    wl = si.small("app", 50, [300, 77, 1029, 0, 8], H_I=4, d_I=64, K_blk=16, k=40, W=32)
+    o, g = _pair(wl)
+    assert np.array_equal(_np(g.idx), o.idx), _first_diff(_np(g.idx), o.idx)
+    assert np.array_equal(_np(g.kv), o.kv), _first_diff(_np(g.kv), o.kv)
+    for layer in (0, 1):
+        assert np.array_equal(_np(g.layer_swa(layer)), o.layer_swa(layer))
+        qo = o.layer_q(layer)
+        qg = g.layer_q(layer)
+        assert np.array_equal(_np(qg[0]), qo[0]) and np.array_equal(_np(qg[1]), qo[1])
+
+
+@pytest.mark.parametrize("H,d,mixed", [(4, 64, False), (8, 128, False), (1, 32, False),
+                                       (2, 64, True), (8, 32, True), (4, 128, False)])
+def test_scores_bit_exact(H, d, mixed):
+    wl = si.small("sc", 60 + H + d, [1000, 333, 9, 4096], H_I=H, d_I=d, K_blk=16, k=40)
+    o, g = _pair(wl, with_latent=False)
+    qo, qg = o.layer_q(0, mixed), g.layer_q(0, mixed)
+    sc, bs = g.index_scores(*qg)
+    sc, bs = _np(sc), _np(bs)
+    for b, L in enumerate(wl.ctx):
+        ref = oracle.index_scores(o.cfg, qo[0][b], qo[1][b], qo[2][b], o.idx, o.table[b], L)
+        got = sc[b, :L]
+        assert np.array_equal(got.view(np.uint32), ref.view(np.uint32)), (b, _first_diff(got, ref))
+        rb = oracle.block_scores(ref, L)
+        assert np.array_equal(bs[b, :len(rb)].view(np.uint32), rb.view(np.uint32)), b
+
+
+# ------------------------------------------------------------------ index + attention groups
+
+def _run_group(wl, permute=True, with_attn=True, mixed_layers=()):
+    o, g = _pair(wl, with_latent=with_attn, permute=permute)
+    pool_o = pool_g = topk_o = topk_g = None
+    report = []
+    for li, mode in enumerate(wl.layers):
+        mixed = li in mixed_layers
+        if mode == "F":
+            qo, qg = o.layer_q(li, mixed), g.layer_q(li, mixed)
+            po, plo, to, tlo = oracle.index_full(o.cfg, *qo, o.idx, o.table, o.ctx)
+            pg, plg, tg, tlg = g.index_full(*qg)
+            assert np.array_equal(_np(plg), plo), (li, "pool_len")
+            assert np.array_equal(_np(pg), po), (li, "pool", _first_diff(_np(pg), po))
+            pool_o, pool_g = (po, plo), (pg, plg)
+            topk_o, topk_g = (to, tlo), (tg, tlg)
+        elif mode == "R":
+            qo, qg = o.layer_q(li, mixed), g.layer_q(li, mixed)
+            to, tlo = oracle.index_reindex(o.cfg, *qo, o.idx, o.table, o.ctx, *pool_o)
+            tg, tlg = g.index_reindex(*qg, *pool_g)
+            topk_o, topk_g = (to, tlo), (tg, tlg)
+        assert np.array_equal(_np(topk_g[1]), topk_o[1]), (li, mode, "topk_len")
+        assert np.array_equal(_np(topk_g[0]), topk_o[0]), (li, mode, "topk",
+                                                           _first_diff(_np(topk_g[0]), topk_o[0]))
+        if with_attn:
+            qa = si.layer_attn_q(wl, li)
+            swo, swg = o.layer_swa(li), g.layer_swa(li)
+            ro, rl = oracle.sparse_attn(o.cfg, qa, o.kv, o.table, swo, o.C, o.ctx, *topk_o)
+            go, gl = g.attn(g.attn_q(li), swg, *topk_g)
+            ok, rel, lerr = attn_close(_np(go), _np(gl), ro, rl)
+            report.append((li, mode, rel, lerr))
+            assert ok, (li, mode, rel, lerr)
+    return report
+
+
+def test_group_small_shapes():
+    wl = si.small("grp", 70, [0, 5, 64, 130, 1000, 2049, 9000], H_I=4, d_I=64, K_blk=16, k=40, W=32)
+    print(_run_group(wl))
+
+
+def test_group_pool_covers_everything_and_ties():
+    # nb <= K_blk for most sequences: the hierarchy reduces to a flat top-k
+    wl = si.small("cov", 71, [7, 100, 512, 513], H_I=2, d_I=64, K_blk=64, k=200, W=16)
+    print(_run_group(wl, mixed_layers=(1,)))
+
+
+def test_group_64_heads_and_wide_indexer():
+    wl = si.small("h64", 72, [4000, 3000], H_I=8, d_I=128, K_blk=32, k=96, H_q=64, W=128,
+                  layers="FRURU")
+    print(_run_group(wl))
+
+
+def test_group_tiny_workload():
+    """The tiny decode workload at its full size: batch 1, 4096 positions, 4 x 64 indexer,
+    pool 64 blocks, top-128, 16 heads, window 128; layers F, R, U."""
+    print(_run_group(si.workload("tiny")))
+
+
+@pytest.mark.slow
+def test_group_long_1m_workload():
+    """Batch 1, 1,048,576 positions, pool 2048 -> top-512, 64 planted blocks."""
+    wl = si.workload("long_1m")
+    print(_run_group(wl, permute=False))
+
+
+@pytest.mark.slow
+def test_group_b8_64k_workload():
+    wl = si.workload("b8_64k")
+    print(_run_group(wl, permute=False))
+
+
+@pytest.mark.slow
+def test_group_ragged64_workload():
+    wl = si.workload("ragged64")
+    print(_run_group(wl, permute=False))
