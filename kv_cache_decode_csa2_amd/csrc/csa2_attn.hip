@@ -252,28 +252,52 @@ __global__ __launch_bounds__(kAttnThreads) void k_attn_split(AttnArgs a) {
     }
 }
 
-// Combine the splits: out = sum_s 2^((m_s - M) c) O_s / sum_s 2^((m_s - M) c) l_s.
-__global__ __launch_bounds__(128) void k_attn_merge(AttnArgs a) {
+// Combine the splits: out = sum_s 2^((m_s - M) c) O_s / sum_s 2^((m_s - M) c) l_s.  The
+// split statistics go through LDS first so that the partial rows load independently.
+constexpr int kMergeThreads = 128;
+constexpr int kMaxMergeSplits = 512;
+
+__global__ __launch_bounds__(kMergeThreads) void k_attn_merge(AttnArgs a) {
+    __shared__ float wgt[kMaxMergeSplits];
+    __shared__ float red[kMergeThreads / kWave][2];
     const int h = blockIdx.x, b = blockIdx.y, tid = threadIdx.x;
     const int64_t base = (int64_t)b * a.nsplit * a.Hq;
-    float M = -INFINITY;
-    for (int s = 0; s < a.nsplit; s++) {
+    float mloc = -INFINITY;
+    for (int s = tid; s < a.nsplit; s += kMergeThreads) {
         const int64_t i = base + (int64_t)s * a.Hq + h;
-        if (a.part_ml[2 * i + 1] > 0.0f) M = fmaxf(M, a.part_ml[2 * i]);
+        const float m = a.part_ml[2 * i], l = a.part_ml[2 * i + 1];
+        wgt[s] = l > 0.0f ? m : -INFINITY;
+        if (l > 0.0f) mloc = fmaxf(mloc, m);
     }
-    float4 acc = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
-    float lw = 0.0f;
-    for (int s = 0; s < a.nsplit; s++) {
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) mloc = fmaxf(mloc, __shfl_xor(mloc, o, kWave));
+    if ((tid & (kWave - 1)) == 0) red[tid / kWave][0] = mloc;
+    __syncthreads();
+    const float M = fmaxf(red[0][0], red[1][0]);
+    float lloc = 0.0f;
+    for (int s = tid; s < a.nsplit; s += kMergeThreads) {
         const int64_t i = base + (int64_t)s * a.Hq + h;
-        const float l = a.part_ml[2 * i + 1];
-        if (!(l > 0.0f)) continue;
-        const float wgt = exp2f((a.part_ml[2 * i] - M) * a.scale_log2);
-        lw += wgt * l;
-        const float4 v = reinterpret_cast<const float4 *>(a.part_o + i * kD)[tid];
-        acc.x += wgt * v.x;
-        acc.y += wgt * v.y;
-        acc.z += wgt * v.z;
-        acc.w += wgt * v.w;
+        const float m = wgt[s];
+        const float e = m == -INFINITY ? 0.0f : exp2f((m - M) * a.scale_log2);
+        lloc += e * a.part_ml[2 * i + 1];
+        wgt[s] = e;
+    }
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) lloc += __shfl_xor(lloc, o, kWave);
+    if ((tid & (kWave - 1)) == 0) red[tid / kWave][1] = lloc;
+    __syncthreads();
+    const float lw = red[0][1] + red[1][1];
+    float4 acc = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+#pragma unroll 8
+    for (int s = 0; s < a.nsplit; s++) {
+        const float e = wgt[s];
+        const float4 v = reinterpret_cast<const float4 *>(a.part_o + (base + (int64_t)s * a.Hq + h) * kD)[tid];
+        if (e != 0.0f) {
+            acc.x += e * v.x;
+            acc.y += e * v.y;
+            acc.z += e * v.z;
+            acc.w += e * v.w;
+        }
     }
     float4 r = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
     if (lw > 0.0f) {
@@ -302,6 +326,7 @@ extern "C" int csa2_sparse_attn(const csa2_config *c, const uint16_t *q, const u
     if (c->swa_window > 0 && (!swa_cache || C < c->swa_window)) return CSA2_ERR_INVALID;
     if (c->kv_dim != kD || c->n_q_heads % 16 || c->n_q_heads > 128) return CSA2_ERR_UNSUPPORTED;
     const int nsplit = attn_splits(c->topk, c->swa_window);
+    if (nsplit > kMaxMergeSplits) return CSA2_ERR_UNSUPPORTED;
     const WsAttn wl = ws_attn(batch, c->n_q_heads, c->kv_dim, nsplit);
     if (ws_bytes < wl.total) return CSA2_ERR_WORKSPACE;
     if (batch == 0) return CSA2_OK;
@@ -328,6 +353,6 @@ extern "C" int csa2_sparse_attn(const csa2_config *c, const uint16_t *q, const u
     a.out = out;
     a.lse = lse;
     k_attn_split<<<dim3(nsplit, batch), kAttnThreads, 0, stream>>>(a);
-    k_attn_merge<<<dim3(c->n_q_heads, batch), 128, 0, stream>>>(a);
+    k_attn_merge<<<dim3(c->n_q_heads, batch), kMergeThreads, 0, stream>>>(a);
     return hipGetLastError() == hipSuccess ? CSA2_OK : CSA2_ERR_HIP;
 }

@@ -28,15 +28,17 @@ __device__ __forceinline__ uint32_t order_key(float f) {
 
 __device__ __forceinline__ int lane_id() { return threadIdx.x & (kWave - 1); }
 
-// Inclusive scan over the 64 lanes of a wave.
+// Inclusive scan over the 64 lanes of a wave: DPP row shifts within rows of 16 lanes,
+// then row broadcasts of lanes 15 and 31 into the rows above.
 __device__ __forceinline__ uint32_t wave_incl_scan(uint32_t v) {
-    const int l = lane_id();
-#pragma unroll
-    for (int o = 1; o < kWave; o <<= 1) {
-        uint32_t t = __shfl_up(v, o, kWave);
-        if (l >= o) v += t;
-    }
-    return v;
+    int x = (int)v;
+    x += __builtin_amdgcn_update_dpp(0, x, 0x111, 0xf, 0xf, false);  // row_shr:1
+    x += __builtin_amdgcn_update_dpp(0, x, 0x112, 0xf, 0xf, false);  // row_shr:2
+    x += __builtin_amdgcn_update_dpp(0, x, 0x114, 0xf, 0xf, false);  // row_shr:4
+    x += __builtin_amdgcn_update_dpp(0, x, 0x118, 0xf, 0xf, false);  // row_shr:8
+    x += __builtin_amdgcn_update_dpp(0, x, 0x142, 0xa, 0xf, false);  // row_bcast:15
+    x += __builtin_amdgcn_update_dpp(0, x, 0x143, 0xc, 0xf, false);  // row_bcast:31
+    return (uint32_t)x;
 }
 
 __device__ __forceinline__ uint64_t ballot(bool p) { return __ballot(p); }
@@ -58,45 +60,9 @@ __device__ __forceinline__ int32_t load_coherent(const int32_t *p) {
 
 namespace csa2 {
 
-// Radix digit of the block-score histogram built during the scan (top 12 bits of the
-// order-preserving key).
-constexpr int kHistBits = 12;
-constexpr int kHistBins = 1 << kHistBits;
-
-// Per-sequence state kept in the workspace between the kernels of one Full call.  The
-// counters are zero on entry and are zero again when the call has finished (the last
-// scan workgroup of a sequence resets `done`, k_pool_final resets n_sel / n_cand).
-struct SeqState {
-    int32_t thr;     // threshold digit of the pool (-1: every block qualifies)
-    int32_t above;   // blocks with a digit above thr
-    int32_t n_sel;   // blocks appended to the selected list
-    int32_t n_cand;  // blocks appended to the candidate list (digit == thr)
-    int32_t done;    // scan chunks finished
-    int32_t pad[3];
-};
-
-constexpr int kMaxBatch = 4096;  // sequences per call (the scan keeps a work list in LDS)
+constexpr int kMaxBatch = 4096;  // sequences per index call (the scan keeps a prefix in LDS)
 
 __host__ __device__ inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
-
-// Workspace of the index calls.  Offsets in bytes from the workspace base.  The state and
-// histogram regions must be zero before the first call that uses the workspace.
-struct WsIndex {
-    size_t st, hist, bscore, sel, cand, pscore, total;
-};
-
-__host__ __device__ inline WsIndex ws_index(int B, int maxb, int K_blk) {
-    WsIndex w;
-    size_t o = 0;
-    w.st = o;           o = align256(o + sizeof(SeqState) * (size_t)B);
-    w.hist = o;         o = align256(o + sizeof(uint32_t) * (size_t)B * kHistBins);
-    w.bscore = o;       o = align256(o + sizeof(float) * (size_t)B * maxb);
-    w.sel = o;          o = align256(o + sizeof(int32_t) * (size_t)B * K_blk);
-    w.cand = o;         o = align256(o + sizeof(uint32_t) * 2 * (size_t)B * maxb);
-    w.pscore = o;       o = align256(o + sizeof(float) * (size_t)B * K_blk * kBlk);
-    w.total = o;
-    return w;
-}
 
 // Workspace of the attention call: per split partial numerators and (max, sum) pairs.
 constexpr int kAttnRows = 64;  // rows per attention workgroup

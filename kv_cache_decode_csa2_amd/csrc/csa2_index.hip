@@ -6,23 +6,31 @@
 // keeps a pool of the K_blk best blocks, then the k best positions inside the pool; a
 // Reindex layer rescores only the pool.
 //
-// Kernels of one Full call (all asynchronous on the caller's stream):
-//   k_scan         HBM stream over every visible key: exact FP4 dot products (gfx950
-//                  scaled FP4->f16 converts + v_dot2_f32_f16), fixed-order fp32 score,
-//                  block max, 12-bit radix histogram of the block keys in LDS; the last
-//                  workgroup of each sequence turns the histogram into the pool threshold
-//                  and clears the histogram for the next call
-//   k_pool_filter  blocks above the threshold digit -> selected list, at it -> candidates
-//   k_pool_final   one workgroup per sequence: exact radix select among the candidates,
-//                  bitonic sort -> ascending pool
-//   k_rescore      scores of the <= 8*K_blk pool positions (shared with Reindex)
-//   k_select_topk  one workgroup per sequence: exact radix select, ordered compaction
+// Kernels (all asynchronous on the caller's stream, no atomics on shared counters):
+//   k_scan<.., false>  HBM stream over every visible key.  Exact FP4 dot products (gfx950
+//                      scaled FP4->f16 converts + v_dot2_f32_f16), fixed-order fp32 score,
+//                      written per position; block maxima; and the maximum of every group
+//                      of 8 consecutive blocks.
+//   k_scan<.., true>   the same arithmetic over the 8 positions of every pool block
+//                      (Reindex rescoring).
+//   k_select           one workgroup per sequence.  Full: the pool from the block maxima,
+//                      then the top-k inside the pool from the stored position scores.
+//                      Reindex: the top-k from the rescored pool.
+//
+// Pool selection without a full pass over the block maxima: with m_g the maximum of group
+// g and lambda the K_blk-th largest m_g, K_blk distinct blocks (the group maxima) score
+// >= lambda, so the K_blk-th largest block score is >= lambda.  Every pool block therefore
+// lies in a group with m_g >= lambda and scores >= lambda itself; only those blocks
+// (about K_blk of them on unstructured data) enter the exact selection.
 //
 // Score (this library's definition; the pages give none): s(p) = sum_h w_h ReLU(q_h.k_{p,h})
 // in a fixed fp32 order.  Per 32-group the dot of the unscaled E2M1 values is exact in
 // fp32 (products are multiples of 1/4, |sum| <= 1152), so v_dot2_f32_f16 accumulates it
 // exactly in any order; t_j = dot * 2^(E_j) is exact; the group sum, ReLU and the fma chain
 // over heads then follow one fixed order, so the result is bit-reproducible.
+//
+// Selection order: score descending, lower index first on equal scores; outputs ascending.
+// Scores are compared through an order-preserving map to uint32 (s is never -0 or NaN).
 #include <algorithm>
 
 #include "csa2_common.h"
@@ -30,7 +38,9 @@
 namespace csa2 {
 
 constexpr int kScanThreads = 256;
-constexpr int kChunkBlocks = 32;  // blocks per scan work unit
+constexpr int kScanWaves = kScanThreads / kWave;
+constexpr int kScanGridMax = 1024;  // workgroups of a scan (grid-stride over waves)
+constexpr int kItemBlocks = 8;      // blocks per scan item = blocks per group maximum
 
 // ------------------------------------------------------------------ query + score core
 
@@ -90,7 +100,7 @@ __device__ __forceinline__ uint32_t load_scales(const uint8_t *p) {
 
 // r_h = ReLU(D_h) for one (position, head): groups summed in order in fp32.
 template <int H, int G>
-__device__ __forceinline__ float head_relu(const Query<H, G> &Q, const uint4 (&kc)[G], uint32_t ks) {
+__device__ __forceinline__ float head_relu(const Query<H, G> &Q, const uint4 *kc, uint32_t ks) {
     float D = 0.0f;
 #pragma unroll
     for (int g = 0; g < G; g++) {
@@ -111,44 +121,41 @@ __device__ __forceinline__ float combine_heads(const Query<H, G> &Q, float r, in
     return s;
 }
 
-// Geometry of one indexer-key block as seen by a wave: 8 positions x H heads per block,
-// 8/H blocks per wave; lane = (position in wave) * H + head.
-template <int H, int G>
-struct KeyBlock {
-    static constexpr int BPW = 8 / H;             // blocks per wave step
-    static constexpr int BPS = BPW * (kScanThreads / kWave);  // blocks per workgroup step
-    static constexpr int CODES = kBlk * H * 16 * G;
-    static constexpr int BYTES = CODES + kBlk * H * G;
-};
-
-template <int H, int G>
-__device__ __forceinline__ float block_position_relu(const uint8_t *bp, int slot, int h,
-                                                     const Query<H, G> &Q) {
-    uint4 kc[G];
-#pragma unroll
-    for (int g = 0; g < G; g++)
-        kc[g] = *reinterpret_cast<const uint4 *>(bp + ((g * kBlk + slot) * H + h) * 16);
-    const uint32_t ks = load_scales<G>(bp + KeyBlock<H, G>::CODES + (slot * H + h) * G);
-    return head_relu<H, G>(Q, kc, ks);
-}
-
 // ------------------------------------------------------------------ block-level helpers
 
+// Wave reductions through DPP: quad swaps, half-row and row mirrors, then row broadcasts of
+// lanes 15 and 31; the result is complete in lane 63.
+template <class Op>
+__device__ __forceinline__ uint32_t wave_reduce_to63(uint32_t v, Op op) {
+    int x = (int)v;
+    x = (int)op((uint32_t)x, (uint32_t)__builtin_amdgcn_mov_dpp(x, 0xB1, 0xf, 0xf, false));   // quad [1,0,3,2]
+    x = (int)op((uint32_t)x, (uint32_t)__builtin_amdgcn_mov_dpp(x, 0x4E, 0xf, 0xf, false));   // quad [2,3,0,1]
+    x = (int)op((uint32_t)x, (uint32_t)__builtin_amdgcn_mov_dpp(x, 0x141, 0xf, 0xf, false));  // row_half_mirror
+    x = (int)op((uint32_t)x, (uint32_t)__builtin_amdgcn_mov_dpp(x, 0x140, 0xf, 0xf, false));  // row_mirror
+    x = (int)op((uint32_t)x, (uint32_t)__builtin_amdgcn_update_dpp(x, x, 0x142, 0xa, 0xf, false));  // row_bcast:15
+    x = (int)op((uint32_t)x, (uint32_t)__builtin_amdgcn_update_dpp(x, x, 0x143, 0xc, 0xf, false));  // row_bcast:31
+    return (uint32_t)x;
+}
+
+// Block-wide sum (every thread gets the total).  sh: NT/64 words.
 template <int NT>
 __device__ __forceinline__ uint32_t block_sum(uint32_t v, uint32_t *sh) {
     const int lane = lane_id(), wave = threadIdx.x / kWave;
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, kWave);
+    v = wave_reduce_to63(v, [](uint32_t x, uint32_t y) { return x + y; });
     __syncthreads();
-    if (lane == 0) sh[wave] = v;
+    if (lane == kWave - 1) sh[wave] = v;
     __syncthreads();
     uint32_t t = 0;
 #pragma unroll
-    for (int i = 0; i < NT / kWave; i++) t += sh[i];
+    for (int i = 0; i < NT / kWave; i += 4) {
+        const uint4 q = *reinterpret_cast<const uint4 *>(sh + i);
+        t += q.x + q.y + q.z + q.w;
+    }
     return t;
 }
 
 // Exclusive scan over the threads of the block (thread order), returns total via *tot.
+// sh: NT/64 words, 16-byte aligned.
 template <int NT>
 __device__ __forceinline__ uint32_t block_excl_scan(uint32_t v, uint32_t *sh, uint32_t *tot) {
     const int lane = lane_id(), wave = threadIdx.x / kWave;
@@ -158,118 +165,27 @@ __device__ __forceinline__ uint32_t block_excl_scan(uint32_t v, uint32_t *sh, ui
     __syncthreads();
     uint32_t before = 0, all = 0;
 #pragma unroll
-    for (int i = 0; i < NT / kWave; i++) {
-        const uint32_t x = sh[i];
-        before += (i < wave) ? x : 0u;
-        all += x;
+    for (int i = 0; i < NT / kWave; i += 4) {
+        const uint4 q = *reinterpret_cast<const uint4 *>(sh + i);
+        const uint32_t x[4] = {q.x, q.y, q.z, q.w};
+#pragma unroll
+        for (int j = 0; j < 4 && i + j < NT / kWave; j++) {
+            before += (i + j < wave) ? x[j] : 0u;
+            all += x[j];
+        }
     }
     *tot = all;
     return before + incl - v;
 }
 
-template <int NT>
-__device__ __forceinline__ void block_and_or(uint64_t &va, uint64_t &vo, uint64_t *sh) {
-    const int lane = lane_id(), wave = threadIdx.x / kWave;
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) {
-        va &= __shfl_xor(va, o, kWave);
-        vo |= __shfl_xor(vo, o, kWave);
-    }
-    __syncthreads();
-    if (lane == 0) {
-        sh[2 * wave] = va;
-        sh[2 * wave + 1] = vo;
-    }
-    __syncthreads();
-    va = ~0ull;
-    vo = 0ull;
-#pragma unroll
-    for (int i = 0; i < NT / kWave; i++) {
-        va &= sh[2 * i];
-        vo |= sh[2 * i + 1];
-    }
+__device__ __forceinline__ int clamp_len(int32_t L, int maxb) {
+    const int64_t cap = (int64_t)maxb * kBlk;
+    return L < 0 ? 0 : (int)(L > cap ? cap : L);
 }
 
-// ------------------------------------------------------------------ exact block-wide select
-//
-// Selects the `need` largest of a set of distinct 64-bit keys (score key << 32 | ~index, so
-// ties in score go to the lower index).  Radix select with 8-bit digits over LDS
-// histograms, starting at the first bit where the keys differ.  On return an item is
-// selected iff (key >> shift) >= prefix.  `src.each(f)` calls f(key) for every item the
-// calling thread owns.
+// ------------------------------------------------------------------ k_scan
 
-template <int NT>
-struct SelShared {
-    uint32_t hist[256];
-    uint64_t red[2 * (NT / kWave)];
-    uint32_t chosen, above, count;
-};
-
-template <int NT, class Src>
-__device__ void block_select(const Src &src, uint32_t need, SelShared<NT> &sh, uint64_t &prefix_out,
-                             int &shift_out) {
-    uint64_t va = ~0ull, vo = 0ull;
-    src.each([&](uint64_t c) {
-        va &= c;
-        vo |= c;
-    });
-    block_and_or<NT>(va, vo, sh.red);
-    const uint64_t diff = va ^ vo;
-    if (diff == 0) {  // at most one distinct key
-        prefix_out = va;
-        shift_out = 0;
-        return;
-    }
-    int shift = ((63 - __clzll((long long)diff)) / 8) * 8;
-    uint64_t prefix = (shift + 8 >= 64) ? 0ull : (va >> (shift + 8));
-    uint32_t remaining = need;
-    const int tid = threadIdx.x;
-    while (true) {
-        for (int i = tid; i < 256; i += NT) sh.hist[i] = 0;
-        __syncthreads();
-        src.each([&](uint64_t c) {
-            if (shift + 8 >= 64 || (c >> (shift + 8)) == prefix)
-                atomicAdd(&sh.hist[(uint32_t)(c >> shift) & 255u], 1u);
-        });
-        __syncthreads();
-        if (tid < kWave) {
-            const int l = tid;
-            const uint32_t c0 = sh.hist[255 - 4 * l], c1 = sh.hist[254 - 4 * l],
-                           c2 = sh.hist[253 - 4 * l], c3 = sh.hist[252 - 4 * l];
-            const uint32_t tot = c0 + c1 + c2 + c3;
-            const uint32_t incl = wave_incl_scan(tot);
-            const uint32_t excl = incl - tot;
-            if (excl < remaining && remaining <= incl) {
-                uint32_t cum = excl, d = 255 - 4 * l, cnt = c0;
-                if (cum + c0 < remaining) {
-                    cum += c0; d -= 1; cnt = c1;
-                    if (cum + c1 < remaining) {
-                        cum += c1; d -= 1; cnt = c2;
-                        if (cum + c2 < remaining) {
-                            cum += c2; d -= 1; cnt = c3;
-                        }
-                    }
-                }
-                sh.chosen = d;
-                sh.above = cum;
-                sh.count = cnt;
-            }
-        }
-        __syncthreads();
-        const uint32_t d = sh.chosen, above = sh.above, cnt = sh.count;
-        __syncthreads();  // everyone has read before the next pass rewrites
-        prefix = (prefix << 8) | d;
-        remaining -= above;
-        if (cnt == remaining || shift == 0) break;
-        shift -= 8;
-    }
-    prefix_out = prefix;
-    shift_out = shift;
-}
-
-// ------------------------------------------------------------------ kernel arguments
-
-struct IndexArgs {
+struct ScanArgs {
     const uint8_t *q_codes;
     const uint8_t *q_scales;
     const float *w;
@@ -277,38 +193,41 @@ struct IndexArgs {
     int64_t n_blocks;
     const int32_t *table;
     int32_t maxb;
-    int32_t B;
-    int32_t K_blk;
-    int32_t k;
     const int32_t *ctx_len;
-    SeqState *st;
-    uint32_t *hist;
-    float *bscore;
-    int32_t *sel;
-    uint2 *cand;
+    int32_t B;
+    // scan outputs (any may be null): position scores [B][maxb*8], block maxima [B][maxb],
+    // group maxima [B][ngmax]
     float *pscore;
-    float *scores_out;        // inspection only
-    float *block_scores_out;  // inspection only
-    const int32_t *pool_blocks;
+    float *bscore;
+    float *gmax;
+    int32_t ngmax;
+    int32_t bstride;  // row stride of bscore (floats)
+    // rescore mode: pool [B][K_blk], pool_len [B] -> pool scores [B][K_blk*8]
+    const int32_t *pool;
     const int32_t *pool_len;
+    int32_t K_blk;
+    float *poolsc;
+    float *poolbmax;  // rescore: pool block maxima [B][K_blk]
 };
 
-__device__ __forceinline__ int clamp_len(int32_t L, int maxb) {
-    const int64_t cap = (int64_t)maxb * kBlk;
-    return L < 0 ? 0 : (int)(L > cap ? cap : L);
+// Items (8 blocks or 8 pool entries) of sequence b.
+template <bool RESCORE>
+__device__ __forceinline__ int items_of(const ScanArgs &a, int b) {
+    if (RESCORE) {
+        const int pl = max(0, min(a.pool_len[b], a.K_blk));
+        return (pl + kItemBlocks - 1) / kItemBlocks;
+    }
+    const int nb = (clamp_len(a.ctx_len[b], a.maxb) + kBlk - 1) / kBlk;
+    return (nb + kItemBlocks - 1) / kItemBlocks;
 }
 
-// Work list of the scan: sequence b owns chunks [prefix[b], prefix[b+1]) of kChunkBlocks
-// blocks.  Every scan workgroup rebuilds it in LDS from ctx_len (B <= kMaxBatch).
-__device__ int build_chunk_prefix(const IndexArgs &a, int32_t *prefix, uint32_t *sh_scan) {
+// Exclusive prefix of items per sequence in LDS (prefix[0..B]); returns the total.
+template <bool RESCORE>
+__device__ int build_item_prefix(const ScanArgs &a, int32_t *prefix, uint32_t *sh_scan) {
     uint32_t running = 0;
     for (int base = 0; base < a.B; base += kScanThreads) {
         const int b = base + (int)threadIdx.x;
-        uint32_t v = 0;
-        if (b < a.B) {
-            const int nb = (clamp_len(a.ctx_len[b], a.maxb) + kBlk - 1) / kBlk;
-            v = (uint32_t)((nb + kChunkBlocks - 1) / kChunkBlocks);
-        }
+        const uint32_t v = b < a.B ? (uint32_t)items_of<RESCORE>(a, b) : 0u;
         uint32_t tot;
         const uint32_t ex = block_excl_scan<kScanThreads>(v, sh_scan, &tot);
         if (b < a.B) prefix[b] = (int32_t)(running + ex);
@@ -319,442 +238,763 @@ __device__ int build_chunk_prefix(const IndexArgs &a, int32_t *prefix, uint32_t 
     return (int)running;
 }
 
-// ------------------------------------------------------------------ k_scan
-
-__device__ __forceinline__ int seq_of_chunk(const int32_t *prefix, int B, int c) {
-    int lo = 0, hi = B - 1;  // largest b with prefix[b] <= c
+__device__ __forceinline__ int seq_of_item(const int32_t *prefix, int B, int it) {
+    int lo = 0, hi = B - 1;  // largest b with prefix[b] <= it
     while (lo < hi) {
         const int mid = (lo + hi + 1) >> 1;
-        if (prefix[mid] <= c) lo = mid;
+        if (prefix[mid] <= it) lo = mid;
         else hi = mid - 1;
     }
     return lo;
 }
 
-// The pool threshold of sequence b from its complete histogram: the digit d such that
-// fewer than K_blk blocks have a larger digit and at least K_blk have d or larger (-1 when
-// every block fits in the pool).  Then clears the histogram and the chunk counter.
-__device__ void pool_threshold(const IndexArgs &a, int b, int nb, uint32_t *sh_scan) {
-    SeqState *S = a.st + b;
-    const int K = a.K_blk, tid = threadIdx.x;
-    uint32_t *gh = a.hist + (size_t)b * kHistBins;
-    if (nb <= K) {
-        if (tid == 0) {
-            S->thr = -1;
-            S->above = 0;
-        }
+// s = fma(w_{H-1}, r_{H-1}, ... fma(w_0, r_0, +0)) where lane base+j holds r_j; quad
+// broadcasts (DPP) for H <= 4, a permute otherwise.
+template <int H, int G>
+__device__ __forceinline__ float combine_heads_dpp(const Query<H, G> &Q, float r, int lane) {
+    if constexpr (H == 1) {
+        return __builtin_fmaf(Q.w[0], r, 0.0f);
+    } else if constexpr (H == 2) {
+        const float r0 = __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(r), 0xA0, 0xf, 0xf, false));
+        const float r1 = __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(r), 0xF5, 0xf, 0xf, false));
+        return __builtin_fmaf(Q.w[1], r1, __builtin_fmaf(Q.w[0], r0, 0.0f));
+    } else if constexpr (H == 4) {
+        float s = __builtin_fmaf(Q.w[0], __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(r), 0x00, 0xf, 0xf, false)), 0.0f);
+        s = __builtin_fmaf(Q.w[1], __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(r), 0x55, 0xf, 0xf, false)), s);
+        s = __builtin_fmaf(Q.w[2], __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(r), 0xAA, 0xf, 0xf, false)), s);
+        s = __builtin_fmaf(Q.w[3], __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(r), 0xFF, 0xf, 0xf, false)), s);
+        return s;
     } else {
-        uint32_t cnt[16], tsum = 0;
-#pragma unroll
-        for (int i = 0; i < 16; i++) {
-            cnt[i] = load_coherent(gh + (kHistBins - 1 - 16 * tid - i));
-            tsum += cnt[i];
-        }
-        uint32_t tot;
-        const uint32_t excl = block_excl_scan<kScanThreads>(tsum, sh_scan, &tot);
-        const uint32_t incl = excl + tsum;
-        if (excl < (uint32_t)K && (uint32_t)K <= incl) {
-            uint32_t cum = excl;
-            for (int i = 0; i < 16; i++) {
-                if (cum + cnt[i] >= (uint32_t)K) {
-                    S->thr = kHistBins - 1 - 16 * tid - i;
-                    S->above = (int)cum;
-                    break;
-                }
-                cum += cnt[i];
-            }
-        }
+        return combine_heads<H, G>(Q, r, lane);
     }
-    __syncthreads();
-    for (int i = tid; i < kHistBins; i += kScanThreads) gh[i] = 0;
-    if (tid == 0) S->done = 0;
 }
 
-// FULL: block scores + histogram + pool threshold.  Otherwise: inspection outputs only.
-template <int H, int G, bool FULL>
-__global__ __launch_bounds__(kScanThreads) void k_scan(IndexArgs a) {
-    using KB = KeyBlock<H, G>;
-    __shared__ uint32_t sh_hist[FULL ? kHistBins : 1];
-    __shared__ int32_t sh_prefix[kMaxBatch + 1];
-    __shared__ uint32_t sh_scan[kScanThreads / kWave];
-    __shared__ int sh_last;
-    const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid / kWave;
-    const int h = lane % H, pw = lane / H, bw = pw / kBlk, slot = pw % kBlk;
-    const int total = build_chunk_prefix(a, sh_prefix, sh_scan);
-    const int per = (total + (int)gridDim.x - 1) / (int)gridDim.x;
-    const int c0 = (int)blockIdx.x * per, c1 = min(total, c0 + per);
-    if (c0 >= c1) return;
-    if (FULL) {
-        for (int i = tid; i < kHistBins; i += kScanThreads) sh_hist[i] = 0;
-    }
-    Query<H, G> Q;
-    int cur = -1, credits = 0, L = 0, nb = 0;
-    const int32_t *trow = nullptr;
+__device__ __forceinline__ float fmax_sel(float a, float b) { return a > b ? a : b; }
 
-    auto flush = [&](int b) {
-        __syncthreads();
-        uint32_t *gh = a.hist + (size_t)b * kHistBins;
-        for (int i = tid; i < kHistBins; i += kScanThreads) {
-            const uint32_t v = sh_hist[i];
-            if (v) {
-                atomicAdd(gh + i, v);
-                sh_hist[i] = 0;
-            }
+// Key bytes of one position-head as one lane loads them: G chunks of 16 code bytes and G
+// scale bytes.
+template <int G>
+struct KeyRegs {
+    uint4 kc[G];
+    uint32_t ks;
+};
+
+// One wave processes a contiguous range of items; an item is 8 consecutive blocks (scan)
+// or 8 consecutive pool entries (rescore) of one sequence, BPW blocks per step, lane =
+// (position in step) * H + head.  Software pipeline per step k: the keys of step k+1 and
+// the block-table entry of step k+2 (and, rescoring, the pool entry of step k+3) are in
+// flight while step k is computed.  Loads never branch: an absent block reads physical
+// block 0 and its positions are masked.  OFF32: every key byte lies within 4 GiB of the
+// cache base, so addresses are a scalar base plus a 32-bit lane offset.
+template <int H, int G, bool RESCORE, bool OFF32>
+__global__ __launch_bounds__(kScanThreads) void k_scan(ScanArgs a) {
+    constexpr int BPW = 8 / H;                         // blocks per wave step
+    constexpr int NSTEP = kItemBlocks / BPW;           // steps per item
+    constexpr int CODES = kBlk * H * 16 * G;
+    constexpr int BYTES = CODES + kBlk * H * G;
+    extern __shared__ int32_t sh_dyn[];  // item prefix [B + 1], clamped lengths [B]
+    __shared__ __align__(16) uint32_t sh_scan[kScanWaves];
+    int32_t *sh_prefix = sh_dyn, *sh_len = sh_dyn + a.B + 1;
+
+    const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
+    const int h = lane % H, pw = lane / H, bw = pw / kBlk, slot = pw % kBlk;
+    for (int b = threadIdx.x; b < a.B; b += kScanThreads) sh_len[b] = clamp_len(a.ctx_len[b], a.maxb);
+    const int total = build_item_prefix<RESCORE>(a, sh_prefix, sh_scan);
+    const int nwaves = (int)gridDim.x * kScanWaves;
+    const int gw = (int)blockIdx.x * kScanWaves + wave;
+    const int per = (total + nwaves - 1) / nwaves;
+    const int it_begin = gw * per, it_end = min(total, it_begin + per);
+    if (it_begin >= it_end) return;
+    const int nsteps = (it_end - it_begin) * NSTEP;
+    const uint32_t lane_off = (uint32_t)((slot * H + h) * 16);
+    const uint32_t sc_off = (uint32_t)(CODES + (slot * H + h) * G);
+
+    // step k -> (sequence, entry index: block (scan) or pool entry (rescore))
+    auto step_pos = [&](int k, int &b, int &e) {
+        const int it = it_begin + k / NSTEP;
+        b = a.B == 1 ? 0 : seq_of_item(sh_prefix, a.B, it);
+        e = (it - sh_prefix[b]) * kItemBlocks + (k % NSTEP) * BPW + bw;
+    };
+    // logical block of step k (-1: none).  Rescoring reads it from the pool.
+    auto block_of = [&](int k) -> int {
+        if (k >= nsteps) return -1;
+        int b, e;
+        step_pos(k, b, e);
+        const int nb = (sh_len[b] + kBlk - 1) / kBlk;
+        int j = e;
+        if (RESCORE) {
+            const int n_ent = max(0, min(a.pool_len[b], a.K_blk));
+            j = e < n_ent ? a.pool[(int64_t)b * a.K_blk + e] : -1;
         }
-        __threadfence();
-        __syncthreads();
-        if (tid == 0) {
-            const int nch = sh_prefix[b + 1] - sh_prefix[b];
-            const int old = atomicAdd(&a.st[b].done, credits);
-            sh_last = (old + credits == nch);
+        return (j >= 0 && j < nb) ? j : -1;
+    };
+    auto phys_of = [&](int k, int j) -> int {  // physical block of step k (-1: none)
+        if (k >= nsteps || j < 0) return -1;
+        int b, e;
+        step_pos(k, b, e);
+        const int32_t ph = a.table[(int64_t)b * a.maxb + j];
+        return (ph >= 0 && ph < a.n_blocks) ? ph : -1;
+    };
+    auto load_keys = [&](int ph, KeyRegs<G> &kr) {
+        const uint32_t p = (uint32_t)(ph >= 0 ? ph : 0);
+        if constexpr (OFF32) {
+            const uint32_t base = p * (uint32_t)BYTES;
+#pragma unroll
+            for (int g = 0; g < G; g++)
+                kr.kc[g] = *reinterpret_cast<const uint4 *>(a.idx_cache + (base + lane_off + (uint32_t)(g * kBlk * H * 16)));
+            kr.ks = load_scales<G>(a.idx_cache + (base + sc_off));
+        } else {
+            const uint8_t *bp = a.idx_cache + (int64_t)p * BYTES;
+#pragma unroll
+            for (int g = 0; g < G; g++)
+                kr.kc[g] = *reinterpret_cast<const uint4 *>(bp + lane_off + g * kBlk * H * 16);
+            kr.ks = load_scales<G>(bp + sc_off);
         }
-        __syncthreads();
-        if (sh_last) {
-            __threadfence();
-            pool_threshold(a, b, nb, sh_scan);
-        }
-        __syncthreads();
     };
 
-    for (int c = c0; c < c1; c++) {
-        const int b = seq_of_chunk(sh_prefix, a.B, c);
-        if (b != cur) {
-            if (FULL && cur >= 0) flush(cur);
-            cur = b;
-            credits = 0;
-            L = clamp_len(a.ctx_len[b], a.maxb);
-            nb = (L + kBlk - 1) / kBlk;
+    Query<H, G> Q;
+    int qb = -1;
+    float gm = -INFINITY;
+    // pipeline: logical blocks of steps k .. k+3, physical blocks of steps k, k+1
+    int j0 = block_of(0), j1 = block_of(1), j2 = block_of(2), j3 = RESCORE ? block_of(3) : -1;
+    int ph0 = phys_of(0, j0), ph1 = phys_of(1, j1);
+    KeyRegs<G> kA, kB;
+    load_keys(ph0, kA);
+    auto body = [&](int k, KeyRegs<G> &cur, KeyRegs<G> &nxt) {
+        load_keys(ph1, nxt);
+        const int ph2 = phys_of(k + 2, j2);
+        const int j4 = RESCORE ? block_of(k + 4) : -1;
+        int b, e;
+        step_pos(k, b, e);
+        if (b != qb) {
+            qb = b;
             load_query<H, G>(Q, a.q_codes + (size_t)b * H * 16 * G, a.q_scales + (size_t)b * H * G,
                              a.w + (size_t)b * H, h);
-            trow = a.table + (int64_t)b * a.maxb;
         }
-        const int cb0 = (c - sh_prefix[b]) * kChunkBlocks;
-        const int cb1 = min(nb, cb0 + kChunkBlocks);
-        for (int base = cb0; base < cb1; base += KB::BPS) {
-            const int blk = base + wave * KB::BPW + bw;
-            const bool active = blk < cb1;
-            float r = 0.0f;
-            bool vis = false;
-            if (active) {
-                const int64_t phys = trow[blk];
-                if (phys >= 0 && phys < a.n_blocks) {
-                    r = block_position_relu<H, G>(a.idx_cache + phys * KB::BYTES, slot, h, Q);
-                    vis = blk * kBlk + slot < L;
-                }
-            }
-            const float s = combine_heads<H, G>(Q, r, lane);
+        const int L = sh_len[b];
+        const float r = head_relu<H, G>(Q, cur.kc, cur.ks);
+        const float s = combine_heads_dpp<H, G>(Q, r, lane);
+        const bool vis = ph0 >= 0 && j0 * kBlk + slot < L;
+        if (RESCORE) {
+            const int n_ent = max(0, min(a.pool_len[b], a.K_blk));
             float m = vis ? s : -INFINITY;
-            m = fmaxf(m, __shfl_xor(m, H, kWave));
-            m = fmaxf(m, __shfl_xor(m, 2 * H, kWave));
-            m = fmaxf(m, __shfl_xor(m, 4 * H, kWave));
-            if (!FULL && a.scores_out && vis && h == 0)
-                a.scores_out[(int64_t)b * a.maxb * kBlk + (int64_t)blk * kBlk + slot] = s;
-            if (active && slot == 0 && h == 0) {
-                if (FULL) {
-                    a.bscore[(int64_t)b * a.maxb + blk] = m;
-                    atomicAdd(&sh_hist[order_key(m) >> (32 - kHistBits)], 1u);
-                } else if (a.block_scores_out) {
-                    a.block_scores_out[(int64_t)b * a.maxb + blk] = m;
-                }
+            m = fmax_sel(m, __shfl_xor(m, H, kWave));
+            m = fmax_sel(m, __shfl_xor(m, 2 * H, kWave));
+            m = fmax_sel(m, __shfl_xor(m, 4 * H, kWave));
+            if (e < n_ent && h == 0) {
+                a.poolsc[((int64_t)b * a.K_blk + e) * kBlk + slot] = vis ? s : -INFINITY;
+                if (slot == 0) a.poolbmax[(int64_t)b * a.K_blk + e] = m;
             }
-        }
-        credits++;
-    }
-    if (FULL && cur >= 0) flush(cur);
-}
-
-// ------------------------------------------------------------------ k_pool_filter
-
-__global__ __launch_bounds__(256) void k_pool_filter(IndexArgs a) {
-    const int b = blockIdx.y, tid = threadIdx.x, lane = lane_id();
-    SeqState *S = a.st + b;
-    const int nb = (clamp_len(a.ctx_len[b], a.maxb) + kBlk - 1) / kBlk;
-    const int j0 = blockIdx.x * 1024;
-    if (j0 >= nb) return;
-    const int thr = S->thr;
-    for (int i = 0; i < 4; i++) {
-        const int j = j0 + i * 256 + tid;
-        const bool valid = j < nb;
-        const uint32_t key = valid ? order_key(a.bscore[(int64_t)b * a.maxb + j]) : 0u;
-        const int d = (int)(key >> (32 - kHistBits));
-        const bool is_sel = valid && d > thr, is_cand = valid && d == thr;
-        const uint64_t ms = ballot(is_sel), mc = ballot(is_cand);
-        if (ms) {
-            const int leader = __ffsll((long long)ms) - 1;
-            int base = 0;
-            if (lane == leader) base = atomicAdd(&S->n_sel, (int)__popcll(ms));
-            base = __shfl(base, leader, kWave);
-            const int off = base + (int)lanes_below(ms);
-            if (is_sel && off < a.K_blk) a.sel[(int64_t)b * a.K_blk + off] = j;
-        }
-        if (mc) {
-            const int leader = __ffsll((long long)mc) - 1;
-            int base = 0;
-            if (lane == leader) base = atomicAdd(&S->n_cand, (int)__popcll(mc));
-            base = __shfl(base, leader, kWave);
-            const int off = base + (int)lanes_below(mc);
-            if (is_cand && off < a.maxb) a.cand[(int64_t)b * a.maxb + off] = make_uint2(key, (uint32_t)j);
-        }
-    }
-}
-
-// ------------------------------------------------------------------ k_pool_final
-
-constexpr int kFinalThreads = 1024;
-constexpr int kCandPerThread = 8;
-
-struct CandRegs {
-    uint64_t c[kCandPerThread];
-    uint32_t valid;  // bit i: item i holds a candidate
-    template <class F>
-    __device__ void each(F f) const {
+        } else {
+            const int nb = (L + kBlk - 1) / kBlk;
+            float m = vis ? s : -INFINITY;
+            m = fmax_sel(m, __shfl_xor(m, H, kWave));
+            m = fmax_sel(m, __shfl_xor(m, 2 * H, kWave));
+            m = fmax_sel(m, __shfl_xor(m, 4 * H, kWave));
+            if (vis && h == 0 && a.pscore) a.pscore[(int64_t)b * a.maxb * kBlk + (int64_t)e * kBlk + slot] = s;
+            if (e < nb && slot == 0 && h == 0 && a.bscore) a.bscore[(int64_t)b * a.bstride + e] = m;
+            gm = fmax_sel(gm, m);
+            if (k % NSTEP == NSTEP - 1) {
 #pragma unroll
-        for (int i = 0; i < kCandPerThread; i++)
-            if (valid & (1u << i)) f(c[i]);
+                for (int o = kBlk * H; o < kWave; o <<= 1) gm = fmax_sel(gm, __shfl_xor(gm, o, kWave));
+                if (lane == 0 && a.gmax) a.gmax[(int64_t)b * a.ngmax + e / kItemBlocks] = gm;
+                gm = -INFINITY;
+            }
+        }
+        j0 = j1;
+        j1 = j2;
+        j2 = RESCORE ? j3 : block_of(k + 3);
+        j3 = j4;
+        ph0 = ph1;
+        ph1 = ph2;
+    };
+    int k = 0;
+    for (; k + 1 < nsteps; k += 2) {
+        body(k, kA, kB);
+        body(k + 1, kB, kA);
     }
+    if (k < nsteps) body(k, kA, kB);
+}
+
+// ------------------------------------------------------------------ exact block-wide select
+//
+// The K largest of a multiset of uint32 keys, lower index first among equal keys.  The
+// digits adapt to the keys present: each pass histograms the current key range [lo, hi]
+// into at most 2048 bins of width 2^s (LDS), keeps the bin that holds the K-th largest and
+// narrows the range to it, so scores crowded into a few binades still spread over the
+// bins.  Result: an item is selected iff key > thr, or key == thr and fewer than `need`
+// such items precede it in index order.
+
+constexpr int kSelThreads = 1024;
+constexpr int kIPT = 16;                            // register items per thread
+constexpr int kRegCap = kSelThreads * kIPT;         // 16384
+constexpr int kHistBins = 2048;
+constexpr uint32_t kAllTies = 0xFFFFFFFFu;
+
+struct SelShared {
+    uint32_t hist[kHistBins];
+    __align__(16) uint32_t scan[kSelThreads / kWave];
+    __align__(16) uint32_t red[2][kSelThreads / kWave];
+    uint32_t res[3];
 };
 
-struct CandGlobal {
-    const uint2 *p;
-    int n;
-    template <class F>
-    __device__ void each(F f) const {
-        for (int i = threadIdx.x; i < n; i += kFinalThreads) {
-            const uint2 v = p[i];
-            f(((uint64_t)v.x << 32) | (uint64_t)(0xFFFFFFFFu - v.y));
+struct SelResult {
+    uint32_t thr;
+    uint32_t need;
+};
+
+// Inverse of order_key.
+__device__ __forceinline__ float key_value(uint32_t k) {
+    return __uint_as_float((k & 0x80000000u) ? (k & 0x7FFFFFFFu) : ~k);
+}
+
+// Block-wide min and max of (lo, hi).
+__device__ __forceinline__ void block_min_max(uint32_t &lo, uint32_t &hi, SelShared &sm) {
+    const int lane = lane_id(), wave = threadIdx.x / kWave;
+    lo = wave_reduce_to63(lo, [](uint32_t x, uint32_t y) { return x < y ? x : y; });
+    hi = wave_reduce_to63(hi, [](uint32_t x, uint32_t y) { return x > y ? x : y; });
+    __syncthreads();
+    if (lane == kWave - 1) {
+        sm.red[0][wave] = lo;
+        sm.red[1][wave] = hi;
+    }
+    __syncthreads();
+    lo = 0xFFFFFFFFu;
+    hi = 0u;
+#pragma unroll
+    for (int i = 0; i < kSelThreads / kWave; i += 4) {
+        const uint4 a4 = *reinterpret_cast<const uint4 *>(&sm.red[0][i]);
+        const uint4 b4 = *reinterpret_cast<const uint4 *>(&sm.red[1][i]);
+        lo = min(min(min(lo, a4.x), min(a4.y, a4.z)), a4.w);
+        hi = max(max(max(hi, b4.x), max(b4.y, b4.z)), b4.w);
+    }
+}
+
+// From a histogram of nbins bins (counts per bin, bin nbins-1 highest): the bin d holding
+// the `remaining`-th largest item, the count of items in higher bins, and d's count.
+__device__ __forceinline__ void find_bin(SelShared &sm, int nbins, uint32_t remaining, uint32_t &d,
+                                         uint32_t &above, uint32_t &cnt) {
+    const int tid = threadIdx.x;
+    const int d0 = nbins - 1 - 2 * tid, d1 = d0 - 1;
+    const uint32_t c0 = d0 >= 0 ? sm.hist[d0] : 0u, c1 = d1 >= 0 ? sm.hist[d1] : 0u;
+    uint32_t tot;
+    const uint32_t before = block_excl_scan<kSelThreads>(c0 + c1, sm.scan, &tot);
+    if (before < remaining && remaining <= before + c0 + c1) {
+        if (before + c0 >= remaining) {
+            sm.res[0] = (uint32_t)d0;
+            sm.res[1] = before;
+            sm.res[2] = c0;
+        } else {
+            sm.res[0] = (uint32_t)d1;
+            sm.res[1] = before + c0;
+            sm.res[2] = c1;
         }
     }
-};
+    __syncthreads();
+    d = sm.res[0];
+    above = sm.res[1];
+    cnt = sm.res[2];
+    __syncthreads();
+}
 
-__device__ __forceinline__ void bitonic_sort_lds(int32_t *v, int n_pow2) {
-    for (int k = 2; k <= n_pow2; k <<= 1) {
-        for (int j = k >> 1; j > 0; j >>= 1) {
-            for (int i = threadIdx.x; i < n_pow2 / 2; i += blockDim.x) {
-                const int lo = 2 * i - (i & (j - 1));
-                const int hi = lo + j;
-                const bool up = ((lo & k) == 0);
-                const int32_t x = v[lo], y = v[hi];
-                if ((x > y) == up) {
-                    v[lo] = y;
-                    v[hi] = x;
-                }
-            }
+// Histogram increment with the wave's most common case folded: lanes whose bin equals the
+// first active lane's bin add through one atomic (a pile of equal keys, e.g. scores that
+// are exactly 0 after the ReLU, would otherwise serialise on one LDS address).
+__device__ __forceinline__ void hist_add(uint32_t *hist, int bin) {
+    const int first = __builtin_amdgcn_readfirstlane(bin);
+    const uint64_t same = __ballot(bin == first);
+    const int leader = __ffsll((long long)same) - 1;
+    if (bin != first) atomicAdd(&hist[bin], 1u);
+    else if (lane_id() == leader) atomicAdd(&hist[bin], (uint32_t)__popcll(same));
+}
+
+// Src::each(f) calls f(key) for every item the calling thread owns.  Precondition: the
+// number of items is >= K >= 1.
+//   Pass 1 (wide key ranges of finite scores): bins linear in the score value, which
+//   spreads scores that crowd into a few binades; the chosen bin's exact key range
+//   follows from a min/max over its items (the bin map is monotone).
+//   Further passes: bins of width 2^s in key space over the current range.
+template <class Src>
+__device__ __forceinline__ SelResult range_select(const Src &src, uint32_t K, SelShared &sm) {
+    const int tid = threadIdx.x;
+    uint32_t lo = 0xFFFFFFFFu, hi = 0u;
+    src.each([&](uint32_t key) {
+        lo = min(lo, key);
+        hi = max(hi, key);
+    });
+    block_min_max(lo, hi, sm);
+    uint32_t remaining = K;
+    if (hi - lo >= (uint32_t)kHistBins) {
+        const float vlo = key_value(lo), vhi = key_value(hi);
+        const float span = vhi - vlo;
+        if (__builtin_isfinite(vlo) && __builtin_isfinite(vhi) && __builtin_isfinite(span) && span > 0.0f) {
+            const float scale = (float)kHistBins / span;
+            auto vbin = [&](uint32_t key) {
+                const float t = (key_value(key) - vlo) * scale;  // monotone in key, >= 0
+                return min(kHistBins - 1, (int)t);
+            };
+            for (int i = tid; i < kHistBins; i += kSelThreads) sm.hist[i] = 0u;
             __syncthreads();
-        }
-    }
-}
-
-__global__ __launch_bounds__(kFinalThreads) void k_pool_final(IndexArgs a, int32_t *pool_blocks,
-                                                              int32_t *pool_len) {
-    __shared__ int32_t out[CSA2_MAX_POOL_BLOCKS];
-    __shared__ int out_n;
-    __shared__ SelShared<kFinalThreads> sh;
-    const int b = blockIdx.x, tid = threadIdx.x;
-    const SeqState S = a.st[b];
-    const int K = a.K_blk;
-    const int nb = (clamp_len(a.ctx_len[b], a.maxb) + kBlk - 1) / kBlk;
-    const int Kp = min(K, nb);
-    const int n_sel = min(S.n_sel, Kp);
-    const int n_cand = min(S.n_cand, a.maxb);
-    const int need = Kp - n_sel;
-    for (int i = tid; i < n_sel; i += kFinalThreads) out[i] = a.sel[(int64_t)b * K + i];
-    if (tid == 0) out_n = n_sel;
-    __syncthreads();
-    const uint2 *cp = a.cand + (int64_t)b * a.maxb;
-    if (need > 0 && need >= n_cand) {
-        for (int i = tid; i < n_cand; i += kFinalThreads) out[n_sel + i] = (int32_t)cp[i].y;
-    } else if (need > 0 && n_cand <= kFinalThreads * kCandPerThread) {
-        CandRegs src;
-        src.valid = 0;
-#pragma unroll
-        for (int i = 0; i < kCandPerThread; i++) {
-            const int idx = tid + i * kFinalThreads;
-            uint2 v = make_uint2(0u, 0u);
-            if (idx < n_cand) {
-                v = cp[idx];
-                src.valid |= 1u << i;
-            }
-            src.c[i] = ((uint64_t)v.x << 32) | (uint64_t)(0xFFFFFFFFu - v.y);
-        }
-        uint64_t prefix;
-        int shift;
-        block_select<kFinalThreads>(src, (uint32_t)need, sh, prefix, shift);
-        src.each([&](uint64_t c) {
-            if ((c >> shift) >= prefix) {
-                const int o = atomicAdd(&out_n, 1);
-                if (o < Kp) out[o] = (int32_t)(0xFFFFFFFFu - (uint32_t)c);
-            }
-        });
-    } else if (need > 0) {
-        CandGlobal src{cp, n_cand};
-        uint64_t prefix;
-        int shift;
-        block_select<kFinalThreads>(src, (uint32_t)need, sh, prefix, shift);
-        src.each([&](uint64_t c) {
-            if ((c >> shift) >= prefix) {
-                const int o = atomicAdd(&out_n, 1);
-                if (o < Kp) out[o] = (int32_t)(0xFFFFFFFFu - (uint32_t)c);
-            }
-        });
-    }
-    __syncthreads();
-    int np2 = 1;
-    while (np2 < Kp) np2 <<= 1;
-    for (int i = Kp + tid; i < np2; i += kFinalThreads) out[i] = 0x7FFFFFFF;
-    __syncthreads();
-    bitonic_sort_lds(out, np2);
-    for (int i = tid; i < K; i += kFinalThreads)
-        pool_blocks[(int64_t)b * K + i] = i < Kp ? out[i] : -1;
-    if (tid == 0) {
-        pool_len[b] = Kp;
-        a.st[b].n_sel = 0;  // leave the workspace counters cleared
-        a.st[b].n_cand = 0;
-    }
-}
-
-// ------------------------------------------------------------------ k_rescore
-
-constexpr int kRescoreBlocks = 16;  // pool entries per workgroup (at least one step)
-
-template <int H, int G>
-__global__ __launch_bounds__(kScanThreads) void k_rescore(IndexArgs a) {
-    using KB = KeyBlock<H, G>;
-    constexpr int RB = kRescoreBlocks > KB::BPS ? kRescoreBlocks : KB::BPS;
-    const int b = blockIdx.y, tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid / kWave;
-    const int h = lane % H, pw = lane / H, bw = pw / kBlk, slot = pw % kBlk;
-    const int plen = max(0, min(a.pool_len[b], a.K_blk));
-    const int e0 = blockIdx.x * RB, e1 = min(plen, e0 + RB);
-    if (e0 >= e1) return;
-    const int L = clamp_len(a.ctx_len[b], a.maxb), nb = (L + kBlk - 1) / kBlk;
-    Query<H, G> Q;
-    load_query<H, G>(Q, a.q_codes + (size_t)b * H * 16 * G, a.q_scales + (size_t)b * H * G,
-                     a.w + (size_t)b * H, h);
-    const int32_t *trow = a.table + (int64_t)b * a.maxb;
-    const int32_t *pool = a.pool_blocks + (int64_t)b * a.K_blk;
-    for (int base = e0; base < e1; base += KB::BPS) {
-        const int e = base + wave * KB::BPW + bw;
-        const bool active = e < e1;
-        float r = 0.0f;
-        bool vis = false;
-        if (active) {
-            const int j = pool[e];
-            if (j >= 0 && j < nb) {
-                const int64_t phys = trow[j];
-                if (phys >= 0 && phys < a.n_blocks) {
-                    r = block_position_relu<H, G>(a.idx_cache + phys * KB::BYTES, slot, h, Q);
-                    vis = j * kBlk + slot < L;
+            src.each([&](uint32_t key) { hist_add(sm.hist, vbin(key)); });
+            __syncthreads();
+            uint32_t d, above, cnt;
+            find_bin(sm, kHistBins, remaining, d, above, cnt);
+            remaining -= above;
+            uint32_t blo = 0xFFFFFFFFu, bhi = 0u;
+            src.each([&](uint32_t key) {
+                if (vbin(key) == (int)d) {
+                    blo = min(blo, key);
+                    bhi = max(bhi, key);
                 }
-            }
+            });
+            block_min_max(blo, bhi, sm);
+            if (cnt == remaining) return {blo, kAllTies};  // the whole bin is needed
+            lo = blo;
+            hi = bhi;
         }
-        const float s = combine_heads<H, G>(Q, r, lane);
-        if (active && h == 0)
-            a.pscore[((int64_t)b * a.K_blk + e) * kBlk + slot] = vis ? s : -INFINITY;
     }
+#pragma unroll 1
+    for (int pass = 0; pass < 6 && lo != hi; pass++) {
+        const uint32_t w = hi - lo;
+        const int s = max(0, 32 - __clz((int)w) - 11);  // (w >> s) < 2048
+        const int nbins = (int)(w >> s) + 1;
+        for (int i = tid; i < nbins; i += kSelThreads) sm.hist[i] = 0u;
+        __syncthreads();
+        src.each([&](uint32_t key) {
+            if (key >= lo && key <= hi) hist_add(sm.hist, (int)((key - lo) >> s));
+        });
+        __syncthreads();
+        uint32_t d, above, cnt;
+        find_bin(sm, nbins, remaining, d, above, cnt);
+        remaining -= above;
+        const uint32_t nlo = lo + (d << s);
+        if (cnt == remaining) return {nlo, kAllTies};  // the whole bin is needed
+        const uint64_t top = (uint64_t)nlo + ((1ull << s) - 1ull);
+        hi = (uint32_t)min((uint64_t)hi, top);
+        lo = nlo;
+    }
+    return {lo, remaining};
 }
 
-// ------------------------------------------------------------------ k_select_topk
-
-constexpr int kSelItems = 16;  // pool slots per thread (1024 * 16 = 8 * 2048)
-
-struct SlotRegs {
-    uint64_t c[kSelItems];
-    uint32_t valid;  // bit i: item i is a visible candidate
+template <int N>
+struct RegItems {
+    uint32_t key[N];
+    uint32_t valid;  // bit i: item i exists
     template <class F>
-    __device__ void each(F f) const {
+    __device__ __forceinline__ void each(F f) const {
 #pragma unroll
-        for (int i = 0; i < kSelItems; i++)
-            if (valid & (1u << i)) f(c[i]);
+        for (int i = 0; i < N; i++)
+            if (valid & (1u << i)) f(key[i]);
     }
 };
 
-__global__ __launch_bounds__(kFinalThreads) void k_select_topk(IndexArgs a, int32_t *topk,
-                                                               int32_t *topk_len) {
-    __shared__ SelShared<kFinalThreads> sh;
-    __shared__ uint32_t sh_scan[kFinalThreads / kWave];
-    const int b = blockIdx.x, tid = threadIdx.x;
-    const int plen = max(0, min(a.pool_len[b], a.K_blk));
-    const int n = plen * kBlk;
-    const int s0 = tid * kSelItems;
-    const float *ps = a.pscore + (int64_t)b * a.K_blk * kBlk;
-    SlotRegs src;
-    src.valid = 0;
+// Ordered emission of the selected items of a register set whose items are in index order
+// within the thread and threads in index order.  One packed scan gives, per thread, the
+// items above the threshold and the ties before it; ties are taken lowest index first, so
+// min(need, ties before) of them precede the thread's own.  `tie_base` / `out_base` carry
+// the ties seen and items written by earlier chunks; both are advanced.  id(i) is written to
+// out[position] for selected items (positions < out_cap).  Counts per chunk < 2^16.
+template <int N, class IdF>
+__device__ __forceinline__ void emit_selected(const RegItems<N> &it, IdF id, SelResult r,
+                                              int32_t *out, uint32_t out_cap,
+                                              uint32_t &tie_base, uint32_t &out_base,
+                                              SelShared &sm) {
+    uint32_t ngt = 0, neq = 0;
 #pragma unroll
-    for (int i = 0; i < kSelItems; i += 4) {
-        float4 v = make_float4(-INFINITY, -INFINITY, -INFINITY, -INFINITY);
-        if (s0 + i < n) v = *reinterpret_cast<const float4 *>(ps + s0 + i);
-        const float f[4] = {v.x, v.y, v.z, v.w};
-#pragma unroll
-        for (int t = 0; t < 4; t++) {
-            const int slot = s0 + i + t;
-            const bool ok = slot < n && f[t] != -INFINITY;
-            src.c[i + t] = ((uint64_t)order_key(f[t]) << 32) | (uint64_t)(0xFFFFFFFFu - (uint32_t)slot);
-            if (ok) src.valid |= 1u << (i + t);
-        }
-    }
-    const uint32_t n_valid = block_sum<kFinalThreads>((uint32_t)__popc(src.valid), sh_scan);
-    const uint32_t need = min((uint32_t)a.k, n_valid);
-    uint32_t selmask = 0;
-    if (need == n_valid) {
-        selmask = src.valid;
-    } else if (need > 0) {
-        uint64_t prefix;
-        int shift;
-        block_select<kFinalThreads>(src, need, sh, prefix, shift);
-#pragma unroll
-        for (int i = 0; i < kSelItems; i++)
-            if ((src.valid & (1u << i)) && (src.c[i] >> shift) >= prefix) selmask |= 1u << i;
+    for (int i = 0; i < N; i++) {
+        if (!(it.valid & (1u << i))) continue;
+        ngt += it.key[i] > r.thr;
+        neq += it.key[i] == r.thr;
     }
     uint32_t tot;
-    const uint32_t off = block_excl_scan<kFinalThreads>((uint32_t)__popc(selmask), sh_scan, &tot);
-    const int32_t *pool = a.pool_blocks + (int64_t)b * a.K_blk;
-    int32_t *out = topk + (int64_t)b * a.k;
-    uint32_t o = off;
+    const uint32_t ex = block_excl_scan<kSelThreads>((ngt << 16) | neq, sm.scan, &tot);
+    const uint32_t gt_before = ex >> 16, eq_before = ex & 0xFFFFu;
+    uint32_t tr = tie_base + eq_before;  // ties before this thread's first item
+    const uint32_t need = r.need;
+    uint32_t o = out_base + gt_before + min(need, tr) - min(need, tie_base);
+    const uint32_t all_gt = tot >> 16, all_eq = tot & 0xFFFFu;
+    out_base += all_gt + (need == kAllTies ? all_eq : min(all_eq, need > tie_base ? need - tie_base : 0u));
+    tie_base += all_eq;
 #pragma unroll
-    for (int i = 0; i < kSelItems; i++) {
-        if (selmask & (1u << i)) {
-            const int slot = s0 + i;
-            if (o < (uint32_t)a.k) out[o] = pool[slot / kBlk] * kBlk + slot % kBlk;
+    for (int i = 0; i < N; i++) {
+        if (!(it.valid & (1u << i))) continue;
+        bool take = it.key[i] > r.thr;
+        if (it.key[i] == r.thr) {
+            take = tr < need;
+            tr++;
+        }
+        if (take) {
+            if (o < out_cap) out[o] = id(i);
             o++;
         }
     }
-    for (int i = (int)need + tid; i < a.k; i += kFinalThreads) out[i] = -1;
-    if (tid == 0) topk_len[b] = (int32_t)need;
+}
+
+// Select-all variant (fewer items than requested): every valid item in order.
+template <int N, class IdF>
+__device__ __forceinline__ void emit_all(const RegItems<N> &it, IdF id, int32_t *out,
+                                         uint32_t out_cap, uint32_t &out_base, SelShared &sm) {
+    uint32_t tot;
+    uint32_t o = out_base + block_excl_scan<kSelThreads>((uint32_t)__popc(it.valid), sm.scan, &tot);
+    out_base += tot;
+#pragma unroll
+    for (int i = 0; i < N; i++)
+        if (it.valid & (1u << i)) {
+            if (o < out_cap) out[o] = id(i);
+            o++;
+        }
+}
+
+// ------------------------------------------------------------------ k_select
+
+struct SelectArgs {
+    const int32_t *ctx_len;
+    int32_t maxb;
+    int32_t B;
+    int32_t K_blk;
+    int32_t k;
+    const float *pscore;  // Full: position scores [B][maxb*8]
+    const float *bscore;  // Full: block maxima [B][bstride]
+    int32_t bstride;
+    const float *gmax;    // Full: group maxima [B][ngmax]
+    int32_t ngmax;
+    const float *poolsc;    // Reindex: pool scores [B][K_blk*8]
+    const float *poolbmax;  // Reindex: pool block maxima [B][K_blk]
+    int32_t *pool_blocks;  // Full: out; Reindex: in
+    int32_t *pool_len;     // Full: out; Reindex: in
+    int32_t *topk;
+    int32_t *topk_len;
+};
+
+constexpr int kCompactCap = 4096;  // candidates redistributed through LDS (4 per thread)
+
+struct SelectShared {
+    SelShared sel;
+    int32_t flag[2 * kSelThreads];         // flagged groups (ascending)
+    int32_t pool[CSA2_MAX_POOL_BLOCKS];    // pool blocks (ascending)
+    uint32_t ckey[kCompactCap];            // compacted candidates: keys
+    int32_t cid[kCompactCap];              //                      ids
+};
+
+// Candidates held sparsely in a thread's register slots (index order) move to a dense
+// ascending list in LDS and back, at most 4 per thread.  Returns false (nothing moved)
+// when there are more than kCompactCap of them.
+template <int N, class IdF>
+__device__ __forceinline__ bool compact(const RegItems<N> &it, IdF id, SelectShared &sm,
+                                        RegItems<4> &out, int32_t (&oid)[4], uint32_t &count) {
+    uint32_t tot;
+    uint32_t o = block_excl_scan<kSelThreads>((uint32_t)__popc(it.valid), sm.sel.scan, &tot);
+    count = tot;
+    if (tot > (uint32_t)kCompactCap) return false;
+#pragma unroll
+    for (int i = 0; i < N; i++)
+        if (it.valid & (1u << i)) {
+            sm.ckey[o] = it.key[i];
+            sm.cid[o] = id(i);
+            o++;
+        }
+    __syncthreads();
+    const uint32_t per = (tot + kSelThreads - 1) / kSelThreads;  // <= 4
+    out.valid = 0;
+#pragma unroll
+    for (int i = 0; i < 4; i++) {
+        const uint32_t li = threadIdx.x * per + i;
+        out.key[i] = 0u;
+        oid[i] = -1;
+        if ((uint32_t)i < per && li < tot) {
+            out.key[i] = sm.ckey[li];
+            oid[i] = sm.cid[li];
+            out.valid |= 1u << i;
+        }
+    }
+    __syncthreads();
+    return true;
+}
+
+// Exact top-K (K >= 1) of a sparse register set (index order), emitted ascending into out.
+// Compacts first when the candidates fit; the multiset must hold >= K items.
+template <int N, class IdF>
+__device__ __forceinline__ void select_emit(const RegItems<N> &it, IdF id, uint32_t K, int32_t *out,
+                                            uint32_t out_cap, SelectShared &sm) {
+    RegItems<4> c;
+    int32_t cid[4];
+    uint32_t count;
+    uint32_t tie_base = 0, out_base = 0;
+    if (compact(it, id, sm, c, cid, count)) {
+        auto cidf = [&](int i) { return cid[i]; };
+        if (K >= count) {
+            emit_all(c, cidf, out, out_cap, out_base, sm.sel);
+        } else {
+            const SelResult r = range_select(c, K, sm.sel);
+            emit_selected(c, cidf, r, out, out_cap, tie_base, out_base, sm.sel);
+        }
+    } else {
+        if (K >= count) {
+            emit_all(it, id, out, out_cap, out_base, sm.sel);
+        } else {
+            const SelResult r = range_select(it, K, sm.sel);
+            emit_selected(it, id, r, out, out_cap, tie_base, out_base, sm.sel);
+        }
+    }
+}
+
+// Items of the streaming path: all blocks j < nb whose maximum is >= lam, in chunks of kRegCap.
+__device__ __forceinline__ void load_block_chunk(const float *bs, int nb, uint32_t lam, int c0,
+                                                 RegItems<kIPT> &it) {
+    const int j0 = c0 + (int)threadIdx.x * kIPT;
+    it.valid = 0;
+#pragma unroll
+    for (int i = 0; i < kIPT; i++) {
+        const int j = j0 + i;
+        it.key[i] = 0u;
+        if (j < nb) {
+            const uint32_t key = order_key(bs[j]);
+            it.key[i] = key;
+            if (key >= lam) it.valid |= 1u << i;
+        }
+    }
+}
+
+struct GlobalBlocks {
+    const float *bs;
+    int nb;
+    uint32_t lam;
+    template <class F>
+    __device__ __forceinline__ void each(F f) const {
+        for (int j = threadIdx.x; j < nb; j += kSelThreads) {
+            const uint32_t key = order_key(bs[j]);
+            if (key >= lam) f(key);
+        }
+    }
+};
+
+// Pool of the Full layer: the K_blk best blocks of sequence b, ascending, into sm.pool.
+// Returns the pool length.
+//   1. lambda = K_blk-th largest group maximum (exact select over <= 16384 group maxima
+//      in registers), or no bound when there are at most K_blk groups;
+//   2. the groups with maximum >= lambda, in ascending order (LDS), two per thread: their
+//      blocks scoring >= lambda are the candidates;
+//   3. exact select of K_blk among the candidates, ordered emission.
+// More than 2048 such groups (heavy ties) or more than 16384 groups take a streaming path
+// over all block maxima instead.
+__device__ __forceinline__ int select_pool(const SelectArgs &a, int b, int nb, SelectShared &sm) {
+    const int tid = threadIdx.x, K = a.K_blk;
+    if (nb <= K) {
+        for (int j = tid; j < nb; j += kSelThreads) sm.pool[j] = j;
+        __syncthreads();
+        return nb;
+    }
+    const float *bs = a.bscore + (int64_t)b * a.bstride;
+    const int ng = (nb + kItemBlocks - 1) / kItemBlocks;
+    uint32_t lam = 0u;  // lower bound of the K-th largest block key
+    bool fast = ng <= kRegCap;
+    if (fast) {
+        // group maxima: thread t owns groups [t*16, t*16 + 16)
+        const float *gm = a.gmax + (int64_t)b * a.ngmax;
+        RegItems<kIPT> g;
+        g.valid = 0;
+        const int g0 = tid * kIPT;
+#pragma unroll
+        for (int i = 0; i < kIPT; i += 4) {
+            float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
+            if (g0 + i + 3 < ng) {
+                v = *reinterpret_cast<const float4 *>(gm + g0 + i);
+            } else {
+                if (g0 + i < ng) v.x = gm[g0 + i];
+                if (g0 + i + 1 < ng) v.y = gm[g0 + i + 1];
+                if (g0 + i + 2 < ng) v.z = gm[g0 + i + 2];
+            }
+            const float f[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+            for (int t = 0; t < 4; t++) {
+                g.key[i + t] = order_key(f[t]);
+                if (g0 + i + t < ng) g.valid |= 1u << (i + t);
+            }
+        }
+        if (ng > K) lam = range_select(g, (uint32_t)K, sm.sel).thr;
+        // ascending list of the groups whose maximum is >= lam
+        uint32_t fl = 0;
+#pragma unroll
+        for (int i = 0; i < kIPT; i++)
+            if ((g.valid & (1u << i)) && g.key[i] >= lam) fl |= 1u << i;
+        uint32_t nfg;
+        uint32_t o = block_excl_scan<kSelThreads>((uint32_t)__popc(fl), sm.sel.scan, &nfg);
+        if (nfg <= 2u * kSelThreads) {
+#pragma unroll
+            for (int i = 0; i < kIPT; i++)
+                if (fl & (1u << i)) sm.flag[o++] = g0 + i;
+        }
+        __syncthreads();
+        if (nfg <= 2u * kSelThreads) {
+            // candidates: blocks >= lam of flagged groups 2t and 2t+1
+            RegItems<kIPT> c;
+            c.valid = 0;
+            int gid[2];
+#pragma unroll
+            for (int q = 0; q < 2; q++) {
+                const int fi = 2 * tid + q;
+                gid[q] = fi < (int)nfg ? sm.flag[fi] : -1;
+                float v[kItemBlocks];
+                if (gid[q] >= 0) {
+                    const int j0 = gid[q] * kItemBlocks;
+                    if (j0 + kItemBlocks <= nb) {
+                        const float4 *src = reinterpret_cast<const float4 *>(bs + j0);
+                        const float4 x0 = src[0], x1 = src[1];
+                        v[0] = x0.x; v[1] = x0.y; v[2] = x0.z; v[3] = x0.w;
+                        v[4] = x1.x; v[5] = x1.y; v[6] = x1.z; v[7] = x1.w;
+                    } else {
+#pragma unroll
+                        for (int t = 0; t < kItemBlocks; t++) v[t] = j0 + t < nb ? bs[j0 + t] : -INFINITY;
+                    }
+                }
+#pragma unroll
+                for (int t = 0; t < kItemBlocks; t++) {
+                    const int i = q * kItemBlocks + t;
+                    c.key[i] = 0u;
+                    if (gid[q] >= 0 && gid[q] * kItemBlocks + t < nb) {
+                        const uint32_t key = order_key(v[t]);
+                        c.key[i] = key;
+                        if (key >= lam) c.valid |= 1u << i;
+                    }
+                }
+            }
+            select_emit(c, [&](int i) { return gid[i / kItemBlocks] * kItemBlocks + i % kItemBlocks; },
+                        (uint32_t)K, sm.pool, (uint32_t)K, sm);
+        } else {
+            fast = false;
+        }
+    }
+    if (!fast) {
+        // streaming path: every block maximum >= lam, in chunks of kRegCap
+        uint32_t tie_base = 0, out_base = 0;
+        GlobalBlocks src{bs, nb, lam};
+        const SelResult r = range_select(src, (uint32_t)K, sm.sel);
+        for (int c0 = 0; c0 < nb; c0 += kRegCap) {
+            RegItems<kIPT> c;
+            load_block_chunk(bs, nb, lam, c0, c);
+            emit_selected(c, [&](int i) { return c0 + tid * kIPT + i; }, r, sm.pool, (uint32_t)K,
+                          tie_base, out_base, sm.sel);
+        }
+    }
+    __syncthreads();
+    return K;
+}
+
+// Top-k among the visible positions of the pool.  Thread t owns pool entries 2t and 2t+1.
+// The k-th largest block maximum among the pool entries bounds the k-th largest position
+// score from below (k distinct positions reach it), so only positions scoring >= that bound
+// in entries whose maximum reaches it are candidates.  Scores and block maxima come from the
+// Full scan (pscore / bscore, by block) or from the Reindex rescoring (poolsc / poolbmax, by
+// pool entry; -inf marks an invisible position).
+template <bool REINDEX>
+__device__ __forceinline__ void select_topk(const SelectArgs &a, int b, int L, const int32_t *pool,
+                                            int plen, SelectShared &sm) {
+    const int tid = threadIdx.x;
+    int pj[2];
+    RegItems<2> bm;  // block maxima of the thread's entries
+    bm.valid = 0;
+    uint32_t nvis = 0;
+#pragma unroll
+    for (int q = 0; q < 2; q++) {
+        const int e = 2 * tid + q;
+        pj[q] = e < plen ? pool[e] : -1;
+        bm.key[q] = 0u;
+        if (pj[q] >= 0 && pj[q] * kBlk < L) {
+            const float m = REINDEX ? a.poolbmax[(int64_t)b * a.K_blk + e]
+                                    : a.bscore[(int64_t)b * a.bstride + pj[q]];
+            bm.key[q] = order_key(m);
+            bm.valid |= 1u << q;
+            nvis += (uint32_t)min(kBlk, L - pj[q] * kBlk);
+        }
+    }
+    const uint32_t n_vis = block_sum<kSelThreads>(nvis, sm.sel.scan);
+    const uint32_t need = min((uint32_t)a.k, n_vis);
+    int32_t *out = a.topk + (int64_t)b * a.k;
+    uint32_t lam = 0u;
+    if (need > 0 && need < n_vis) {
+        uint32_t n_ent = block_sum<kSelThreads>((uint32_t)__popc(bm.valid), sm.sel.scan);
+        if (n_ent > need) lam = range_select(bm, need, sm.sel).thr;
+    }
+    // candidate positions: entries whose maximum reaches lam, positions scoring >= lam
+    RegItems<kIPT> it;
+    it.valid = 0;
+#pragma unroll
+    for (int q = 0; q < 2; q++) {
+        float sc[kBlk];
+        const bool live = (bm.valid & (1u << q)) && bm.key[q] >= lam;
+        if (live) {
+            const float4 *src = REINDEX
+                ? reinterpret_cast<const float4 *>(a.poolsc + ((int64_t)b * a.K_blk + 2 * tid + q) * kBlk)
+                : reinterpret_cast<const float4 *>(a.pscore + (int64_t)b * a.maxb * kBlk + (int64_t)pj[q] * kBlk);
+            const float4 x0 = src[0], x1 = src[1];
+            sc[0] = x0.x; sc[1] = x0.y; sc[2] = x0.z; sc[3] = x0.w;
+            sc[4] = x1.x; sc[5] = x1.y; sc[6] = x1.z; sc[7] = x1.w;
+        }
+#pragma unroll
+        for (int t = 0; t < kBlk; t++) {
+            const int i = q * kBlk + t;
+            it.key[i] = 0u;
+            if (live && pj[q] * kBlk + t < L && (!REINDEX || sc[t] != -INFINITY)) {
+                const uint32_t key = order_key(sc[t]);
+                it.key[i] = key;
+                if (key >= lam) it.valid |= 1u << i;
+            }
+        }
+    }
+    if (need > 0)
+        select_emit(it, [&](int i) { return pj[i / kBlk] * kBlk + i % kBlk; }, need, out,
+                    (uint32_t)a.k, sm);
+    for (int i = (int)need + tid; i < a.k; i += kSelThreads) out[i] = -1;
+    if (tid == 0) a.topk_len[b] = (int32_t)need;
+}
+
+template <bool REINDEX>
+__global__ __launch_bounds__(kSelThreads) void k_select(SelectArgs a) {
+    extern __shared__ __align__(16) uint8_t sh_raw[];
+    SelectShared &sm = *reinterpret_cast<SelectShared *>(sh_raw);
+    const int b = blockIdx.x, tid = threadIdx.x;
+    const int L = clamp_len(a.ctx_len[b], a.maxb);
+    const int nb = (L + kBlk - 1) / kBlk;
+    if (REINDEX) {
+        const int plen = max(0, min(a.pool_len[b], a.K_blk));
+        select_topk<true>(a, b, L, a.pool_blocks + (int64_t)b * a.K_blk, plen, sm);
+        return;
+    }
+    const int plen = select_pool(a, b, nb, sm);
+    const int np = min(plen, nb);
+    int32_t *pool_out = a.pool_blocks + (int64_t)b * a.K_blk;
+    for (int i = tid; i < a.K_blk; i += kSelThreads) pool_out[i] = i < np ? sm.pool[i] : -1;
+    if (tid == 0) a.pool_len[b] = np;
+    select_topk<false>(a, b, L, sm.pool, np, sm);
 }
 
 // ------------------------------------------------------------------ dispatch
 
-template <int H, int G>
-struct Kern {
-    static void scan_full(dim3 g, hipStream_t s, const IndexArgs &a) {
-        k_scan<H, G, true><<<g, kScanThreads, 0, s>>>(a);
-    }
-    static void scan_inspect(dim3 g, hipStream_t s, const IndexArgs &a) {
-        k_scan<H, G, false><<<g, kScanThreads, 0, s>>>(a);
-    }
-    static void rescore(dim3 g, hipStream_t s, const IndexArgs &a) {
-        k_rescore<H, G><<<g, kScanThreads, 0, s>>>(a);
-    }
-    static int rescore_blocks() {
-        return kRescoreBlocks > KeyBlock<H, G>::BPS ? kRescoreBlocks : KeyBlock<H, G>::BPS;
-    }
-};
-
-typedef void (*LaunchFn)(dim3, hipStream_t, const IndexArgs &);
+typedef void (*ScanFn)(dim3, size_t, hipStream_t, const ScanArgs &);
 struct KernSet {
-    LaunchFn scan_full, scan_inspect, rescore;
-    int rescore_blocks;
+    ScanFn scan, rescore;
 };
 
 template <int H, int G>
-KernSet kern_set() {
-    return {Kern<H, G>::scan_full, Kern<H, G>::scan_inspect, Kern<H, G>::rescore,
-            Kern<H, G>::rescore_blocks()};
+bool off32(const ScanArgs &a) {
+    constexpr int64_t BYTES = kBlk * H * 17 * G;
+    return a.n_blocks * BYTES <= ((int64_t)1 << 32);
+}
+template <int H, int G>
+void launch_scan(dim3 g, size_t sh, hipStream_t s, const ScanArgs &a) {
+    if (off32<H, G>(a)) k_scan<H, G, false, true><<<g, kScanThreads, sh, s>>>(a);
+    else k_scan<H, G, false, false><<<g, kScanThreads, sh, s>>>(a);
+}
+template <int H, int G>
+void launch_rescore(dim3 g, size_t sh, hipStream_t s, const ScanArgs &a) {
+    if (off32<H, G>(a)) k_scan<H, G, true, true><<<g, kScanThreads, sh, s>>>(a);
+    else k_scan<H, G, true, false><<<g, kScanThreads, sh, s>>>(a);
 }
 
 bool pick(int H, int dI, KernSet *ks) {
     const int G = dI / 32;
 #define CSA2_CASE(h, g) \
-    if (H == h && G == g) { *ks = kern_set<h, g>(); return true; }
+    if (H == h && G == g) { *ks = {launch_scan<h, g>, launch_rescore<h, g>}; return true; }
     CSA2_CASE(1, 1) CSA2_CASE(1, 2) CSA2_CASE(1, 4)
     CSA2_CASE(2, 1) CSA2_CASE(2, 2) CSA2_CASE(2, 4)
     CSA2_CASE(4, 1) CSA2_CASE(4, 2) CSA2_CASE(4, 4)
@@ -783,12 +1023,13 @@ int check_cfg(const csa2_config *c) {
 
 int launched() { return hipGetLastError() == hipSuccess ? CSA2_OK : CSA2_ERR_HIP; }
 
-IndexArgs make_args(const csa2_config *c, const uint8_t *qc, const uint8_t *qs, const float *w,
-                    const uint8_t *idx, int64_t n_blocks, const int32_t *table, int32_t maxb,
-                    const int32_t *ctx, int32_t B, void *ws) {
-    const WsIndex L = ws_index(B, maxb, c->pool_blocks);
-    uint8_t *base = (uint8_t *)ws;
-    IndexArgs a{};
+// Row stride of the group maxima (rounded to 4 floats for 16-byte loads).
+int ngmax_of(int maxb) { return (((maxb + kItemBlocks - 1) / kItemBlocks) + 3) & ~3; }
+
+ScanArgs scan_args(const csa2_config *c, const uint8_t *qc, const uint8_t *qs, const float *w,
+                   const uint8_t *idx, int64_t n_blocks, const int32_t *table, int32_t maxb,
+                   const int32_t *ctx, int32_t B) {
+    ScanArgs a{};
     a.q_codes = qc;
     a.q_scales = qs;
     a.w = w;
@@ -796,25 +1037,43 @@ IndexArgs make_args(const csa2_config *c, const uint8_t *qc, const uint8_t *qs, 
     a.n_blocks = n_blocks;
     a.table = table;
     a.maxb = maxb;
-    a.B = B;
-    a.K_blk = c->pool_blocks;
-    a.k = c->topk;
     a.ctx_len = ctx;
-    a.st = (SeqState *)(base + L.st);
-    a.hist = (uint32_t *)(base + L.hist);
-    a.bscore = (float *)(base + L.bscore);
-    a.sel = (int32_t *)(base + L.sel);
-    a.cand = (uint2 *)(base + L.cand);
-    a.pscore = (float *)(base + L.pscore);
+    a.B = B;
+    a.ngmax = ngmax_of(maxb);
+    a.bstride = maxb;
+    a.K_blk = c->pool_blocks;
     return a;
 }
 
-int scan_grid(int B, int maxb) {
-    const int64_t chunks = (int64_t)B * ((maxb + kChunkBlocks - 1) / kChunkBlocks);
-    return (int)std::max<int64_t>(1, std::min<int64_t>(chunks, 2048));
+int scan_grid(int64_t items) {
+    const int64_t wgs = (items + kScanWaves - 1) / kScanWaves;
+    return (int)std::max<int64_t>(1, std::min<int64_t>(wgs, kScanGridMax));
 }
 
+size_t prefix_bytes(int B) { return sizeof(int32_t) * (2 * (size_t)B + 1); }
+
+constexpr size_t kSelectShared = sizeof(SelectShared);
+
 }  // namespace
+
+// Workspace of the index calls: position scores, block maxima, group maxima (Full) and
+// pool scores (Reindex).  No initialisation is needed.
+namespace csa2 {
+struct WsIdx {
+    size_t pscore, bscore, gmax, poolsc, poolbmax, total;
+};
+static WsIdx ws_idx(int B, int maxb, int K_blk) {
+    WsIdx w;
+    size_t o = 0;
+    w.pscore = o;  o = align256(o + sizeof(float) * (size_t)B * maxb * kBlk);
+    w.bscore = o;  o = align256(o + sizeof(float) * (size_t)B * ngmax_of(maxb) * kItemBlocks);
+    w.gmax = o;    o = align256(o + sizeof(float) * (size_t)B * ngmax_of(maxb));
+    w.poolsc = o;  o = align256(o + sizeof(float) * (size_t)B * K_blk * kBlk);
+    w.poolbmax = o; o = align256(o + sizeof(float) * (size_t)B * K_blk);
+    w.total = o;
+    return w;
+}
+}  // namespace csa2
 
 extern "C" int csa2_layout(const csa2_config *c, csa2_layout_info *out) {
     if (!c || !out || c->n_idx_heads <= 0 || c->idx_dim <= 0 || c->idx_dim % 32 ||
@@ -833,7 +1092,7 @@ extern "C" int csa2_workspace_bytes(const csa2_config *c, int op, int32_t batch,
     if (op == CSA2_OP_INDEX_FULL || op == CSA2_OP_INDEX_REINDEX) {
         const int st = check_cfg(c);
         if (st) return st;
-        *bytes = ws_index(batch, maxb, c->pool_blocks).total;
+        *bytes = ws_idx(batch, maxb, c->pool_blocks).total;
         return CSA2_OK;
     }
     if (op == CSA2_OP_SPARSE_ATTN) {
@@ -868,6 +1127,26 @@ namespace {
         if (batch > kMaxBatch) return CSA2_ERR_UNSUPPORTED;                                 \
     } while (0)
 
+SelectArgs select_args(const csa2_config *c, const int32_t *ctx, int32_t maxb, int32_t B,
+                       void *ws) {
+    const WsIdx L = ws_idx(B, maxb, c->pool_blocks);
+    uint8_t *base = (uint8_t *)ws;
+    SelectArgs s{};
+    s.ctx_len = ctx;
+    s.maxb = maxb;
+    s.B = B;
+    s.K_blk = c->pool_blocks;
+    s.k = c->topk;
+    s.pscore = (const float *)(base + L.pscore);
+    s.bscore = (const float *)(base + L.bscore);
+    s.bstride = ngmax_of(maxb) * kItemBlocks;
+    s.gmax = (const float *)(base + L.gmax);
+    s.ngmax = ngmax_of(maxb);
+    s.poolsc = (const float *)(base + L.poolsc);
+    s.poolbmax = (const float *)(base + L.poolbmax);
+    return s;
+}
+
 }  // namespace
 
 extern "C" int csa2_index_scores(const csa2_config *c, const uint8_t *q_codes,
@@ -880,21 +1159,11 @@ extern "C" int csa2_index_scores(const csa2_config *c, const uint8_t *q_codes,
     if (batch == 0 || (!scores && !block_scores)) return CSA2_OK;
     KernSet ks;
     pick(c->n_idx_heads, c->idx_dim, &ks);
-    IndexArgs a{};
-    a.q_codes = q_codes;
-    a.q_scales = q_scales;
-    a.w = w;
-    a.idx_cache = idx_cache;
-    a.n_blocks = n_blocks;
-    a.table = block_table;
-    a.maxb = maxb;
-    a.B = batch;
-    a.K_blk = c->pool_blocks;
-    a.k = c->topk;
-    a.ctx_len = ctx_len;
-    a.scores_out = scores;
-    a.block_scores_out = block_scores;
-    ks.scan_inspect(dim3(scan_grid(batch, maxb)), stream, a);
+    ScanArgs a = scan_args(c, q_codes, q_scales, w, idx_cache, n_blocks, block_table, maxb,
+                           ctx_len, batch);
+    a.pscore = scores;
+    a.bscore = block_scores;
+    ks.scan(dim3(scan_grid((int64_t)batch * ngmax_of(maxb))), prefix_bytes(batch), stream, a);
     return launched();
 }
 
@@ -906,13 +1175,19 @@ extern "C" int csa2_index_full_scan(const csa2_config *c, const uint8_t *q_codes
                                     size_t ws_bytes, hipStream_t stream) {
     CSA2_CHECK_INDEX_ARGS();
     if (!ws) return CSA2_ERR_INVALID;
-    if (ws_bytes < ws_index(batch, maxb, c->pool_blocks).total) return CSA2_ERR_WORKSPACE;
+    const WsIdx L = ws_idx(batch, maxb, c->pool_blocks);
+    if (ws_bytes < L.total) return CSA2_ERR_WORKSPACE;
     if (batch == 0) return CSA2_OK;
     KernSet ks;
     pick(c->n_idx_heads, c->idx_dim, &ks);
-    const IndexArgs a = make_args(c, q_codes, q_scales, w, idx_cache, n_blocks, block_table,
-                                  maxb, ctx_len, batch, ws);
-    ks.scan_full(dim3(scan_grid(batch, maxb)), stream, a);
+    ScanArgs a = scan_args(c, q_codes, q_scales, w, idx_cache, n_blocks, block_table, maxb,
+                           ctx_len, batch);
+    uint8_t *base = (uint8_t *)ws;
+    a.pscore = (float *)(base + L.pscore);
+    a.bscore = (float *)(base + L.bscore);
+    a.bstride = ngmax_of(maxb) * kItemBlocks;
+    a.gmax = (float *)(base + L.gmax);
+    ks.scan(dim3(scan_grid((int64_t)batch * ngmax_of(maxb))), prefix_bytes(batch), stream, a);
     return launched();
 }
 
@@ -926,19 +1201,14 @@ extern "C" int csa2_index_full_finish(const csa2_config *c, const uint8_t *q_cod
                                       hipStream_t stream) {
     CSA2_CHECK_INDEX_ARGS();
     if (!pool_blocks || !pool_len || !topk || !topk_len || !ws) return CSA2_ERR_INVALID;
-    if (ws_bytes < ws_index(batch, maxb, c->pool_blocks).total) return CSA2_ERR_WORKSPACE;
+    if (ws_bytes < ws_idx(batch, maxb, c->pool_blocks).total) return CSA2_ERR_WORKSPACE;
     if (batch == 0) return CSA2_OK;
-    KernSet ks;
-    pick(c->n_idx_heads, c->idx_dim, &ks);
-    IndexArgs a = make_args(c, q_codes, q_scales, w, idx_cache, n_blocks, block_table, maxb,
-                            ctx_len, batch, ws);
-    k_pool_filter<<<dim3((maxb + 1023) / 1024, batch), 256, 0, stream>>>(a);
-    k_pool_final<<<batch, kFinalThreads, 0, stream>>>(a, pool_blocks, pool_len);
-    a.pool_blocks = pool_blocks;
-    a.pool_len = pool_len;
-    const int rb = ks.rescore_blocks;
-    ks.rescore(dim3((c->pool_blocks + rb - 1) / rb, batch), stream, a);
-    k_select_topk<<<batch, kFinalThreads, 0, stream>>>(a, topk, topk_len);
+    SelectArgs s = select_args(c, ctx_len, maxb, batch, ws);
+    s.pool_blocks = pool_blocks;
+    s.pool_len = pool_len;
+    s.topk = topk;
+    s.topk_len = topk_len;
+    k_select<false><<<batch, kSelThreads, kSelectShared, stream>>>(s);
     return launched();
 }
 
@@ -968,16 +1238,24 @@ extern "C" int csa2_index_reindex(const csa2_config *c, const uint8_t *q_codes,
                                   hipStream_t stream) {
     CSA2_CHECK_INDEX_ARGS();
     if (!pool_blocks || !pool_len || !topk || !topk_len || !ws) return CSA2_ERR_INVALID;
-    if (ws_bytes < ws_index(batch, maxb, c->pool_blocks).total) return CSA2_ERR_WORKSPACE;
+    const WsIdx L = ws_idx(batch, maxb, c->pool_blocks);
+    if (ws_bytes < L.total) return CSA2_ERR_WORKSPACE;
     if (batch == 0) return CSA2_OK;
     KernSet ks;
     pick(c->n_idx_heads, c->idx_dim, &ks);
-    IndexArgs a = make_args(c, q_codes, q_scales, w, idx_cache, n_blocks, block_table, maxb,
-                            ctx_len, batch, ws);
-    a.pool_blocks = pool_blocks;
+    ScanArgs a = scan_args(c, q_codes, q_scales, w, idx_cache, n_blocks, block_table, maxb,
+                           ctx_len, batch);
+    a.pool = pool_blocks;
     a.pool_len = pool_len;
-    const int rb = ks.rescore_blocks;
-    ks.rescore(dim3((c->pool_blocks + rb - 1) / rb, batch), stream, a);
-    k_select_topk<<<batch, kFinalThreads, 0, stream>>>(a, topk, topk_len);
+    a.poolsc = (float *)((uint8_t *)ws + L.poolsc);
+    a.poolbmax = (float *)((uint8_t *)ws + L.poolbmax);
+    const int64_t items = (int64_t)batch * ((c->pool_blocks + kItemBlocks - 1) / kItemBlocks);
+    ks.rescore(dim3(scan_grid(items)), prefix_bytes(batch), stream, a);
+    SelectArgs s = select_args(c, ctx_len, maxb, batch, ws);
+    s.pool_blocks = const_cast<int32_t *>(pool_blocks);
+    s.pool_len = const_cast<int32_t *>(pool_len);
+    s.topk = topk;
+    s.topk_len = topk_len;
+    k_select<true><<<batch, kSelThreads, kSelectShared, stream>>>(s);
     return launched();
 }

@@ -202,3 +202,25 @@ def test_group_b8_64k_workload():
 def test_group_ragged64_workload():
     wl = si.workload("ragged64")
     print(_run_group(wl, permute=False))
+
+
+def test_group_all_equal_keys_long():
+    """Every position holds the same indexer key, so every score, block maximum and group
+    maximum ties: the pool must be blocks 0..K_blk-1 and the top-k positions 0..k-1 (lower
+    index first).  With more than 2048 tied groups this takes the streaming pool path."""
+    wl = si.small("tie", 81, [140000], H_I=4, d_I=64, K_blk=2048, k=512, W=16)
+    row = si.normal(81, 999, (1, wl.H_I, wl.d_I))
+    orig = si.idx_keys
+    try:
+        si.idx_keys = lambda w, b, L=None: np.repeat(row, w.ctx[b] if L is None else L, axis=0)
+        o, g = _pair(wl, with_latent=False)
+        qo, qg = o.layer_q(0), g.layer_q(0)
+        po, plo, to, tlo = oracle.index_full(o.cfg, *qo, o.idx, o.table, o.ctx)
+    finally:
+        si.idx_keys = orig
+    assert np.array_equal(po[0], np.arange(2048)) and np.array_equal(to[0], np.arange(512))
+    pg, plg, tg, tlg = g.index_full(*qg)
+    assert np.array_equal(_np(pg), po) and np.array_equal(_np(plg), plo)
+    assert np.array_equal(_np(tg), to) and np.array_equal(_np(tlg), tlo)
+    tg2, tlg2 = g.index_reindex(*qg, pg, plg)
+    assert np.array_equal(_np(tg2), to)
