@@ -86,7 +86,7 @@ class Bench:
         self.tok_key = dev(np.stack([si.idx_keys(wl, b)[-1] for b in range(B)]))
         self.ws = [torch.zeros(k.csa2_workspace_bytes(self.cfg, k.CSA2_OP_INDEX_FULL, B, maxb),
                                dtype=torch.uint8, device="cuda") for _ in range(R)]
-        self.ws_attn = torch.empty(k.csa2_workspace_bytes(self.cfg, k.CSA2_OP_SPARSE_ATTN, B, maxb),
+        self.ws_attn = torch.zeros(k.csa2_workspace_bytes(self.cfg, k.CSA2_OP_SPARSE_ATTN, B, maxb),
                                    dtype=torch.uint8, device="cuda")
         i32 = dict(dtype=torch.int32, device="cuda")
         self.pool = torch.empty((B, wl.K_blk), **i32)
@@ -104,15 +104,16 @@ class Bench:
             if lay["mode"] == "F":
                 k.csa2_append_global(c, self.tok_lat, self.tok_key, g.table, g.n_blocks,
                                      lay["pos"], 1, kv, idx)
-            k.csa2_append_swa(c, lay["swa_row"], lay["pos"], 1, lay["swa"], g.C)
             if lay["mode"] == "F":
                 k.csa2_index_full(c, lay["qc"], lay["qs"], lay["w"], idx, g.n_blocks, g.table,
                                   g.ctx, self.pool, self.pool_len, self.topk, self.topk_len, ws)
             elif lay["mode"] == "R":
                 k.csa2_index_reindex(c, lay["qc"], lay["qs"], lay["w"], idx, g.n_blocks, g.table,
                                      g.ctx, self.pool, self.pool_len, self.topk, self.topk_len, ws)
-            k.csa2_sparse_attn(c, lay["q"], kv, g.n_blocks, g.table, lay["swa"], g.C, g.ctx,
-                               self.topk, self.topk_len, self.out, self.lse, self.ws_attn)
+            # the layer's window row (position L-1) is appended inside the attention call
+            k.csa2_sparse_attn_append(c, lay["swa_row"], lay["pos"], lay["q"], kv, g.n_blocks,
+                                      g.table, lay["swa"], g.C, g.ctx, self.topk, self.topk_len,
+                                      self.out, self.lse, self.ws_attn)
 
     def scan(self, r):
         lay = self.layers[0]

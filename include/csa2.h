@@ -27,8 +27,8 @@
  *     entries that are out of range, so a bad value never reads or writes outside the
  *     buffers described here; the results for such entries are unspecified.
  *   - A workspace `ws` of at least csa2_workspace_bytes() bytes is needed by the index
- *     and attention calls (one per kind of call; the index workspace must be zero-filled
- *     before first use).  Calls that share a workspace must not run concurrently.
+ *     and attention calls (one per kind of call); neither needs initialisation.  Calls
+ *     that share a workspace must not run concurrently.
  */
 #ifndef CSA2_H
 #define CSA2_H
@@ -149,8 +149,7 @@ int csa2_index_scores(const csa2_config *cfg, const uint8_t *q_codes, const uint
  * descending, lower index first on ties.  Outputs ascending, padded with -1:
  * pool_blocks [batch][K_blk] (logical block ids), pool_len [batch], topk [batch][k]
  * (positions), topk_len [batch].  A sequence with L_b <= 0 gets empty outputs.
- * Workspace: CSA2_OP_INDEX_FULL bytes, zero-filled before its first use; every Full /
- * Reindex call leaves it ready for the next one (do not share it with csa2_sparse_attn).
+ * Workspace: CSA2_OP_INDEX_FULL bytes (do not share it with csa2_sparse_attn).
  * batch <= 4096. */
 int csa2_index_full(const csa2_config *cfg, const uint8_t *q_codes, const uint8_t *q_scales,
                     const float *w, const uint8_t *idx_cache, int64_t n_blocks,
@@ -195,6 +194,20 @@ int csa2_sparse_attn(const csa2_config *cfg, const uint16_t *q, const uint8_t *k
                      const uint8_t *swa_cache, int32_t C, const int32_t *ctx_len,
                      int32_t batch, const int32_t *topk, const int32_t *topk_len, float *out,
                      float *lse, void *ws, size_t ws_bytes, hipStream_t stream);
+
+/* Window append fused with sparse attention (every layer appends its own window row [W]
+ * and then attends [KV][3]): exactly csa2_append_swa(cfg, swa_rows, pos, batch, 1,
+ * swa_cache, C) followed by csa2_sparse_attn(cfg, q, ...), in one launch pair.  swa_rows
+ * [batch][D] fp32 on the device; pos [batch] device positions (negative: no append).  The
+ * appended row is quantised once and attended from registers, so it is bit-identical to
+ * the two-call sequence.  Precondition (as for the two calls): slot pos[b] % C holds no row
+ * of the attended window other than position pos[b] itself (C > W, or pos[b] = L_b - 1). */
+int csa2_sparse_attn_append(const csa2_config *cfg, const float *swa_rows, const int32_t *pos,
+                            const uint16_t *q, const uint8_t *kv_cache, int64_t n_blocks,
+                            const int32_t *block_table, int32_t maxb, uint8_t *swa_cache,
+                            int32_t C, const int32_t *ctx_len, int32_t batch,
+                            const int32_t *topk, const int32_t *topk_len, float *out,
+                            float *lse, void *ws, size_t ws_bytes, hipStream_t stream);
 
 /* Human-readable status. */
 const char *csa2_status_str(int status);

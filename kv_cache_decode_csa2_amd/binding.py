@@ -22,7 +22,7 @@ EXPORTS = [
     "csa2_layout", "csa2_workspace_bytes", "csa2_quantize_mxfp4", "csa2_quantize_mxfp8",
     "csa2_dequant_mxfp4", "csa2_dequant_mxfp8", "csa2_append_global", "csa2_append_swa",
     "csa2_index_scores", "csa2_index_full", "csa2_index_full_scan", "csa2_index_full_finish",
-    "csa2_index_reindex", "csa2_sparse_attn", "csa2_status_str",
+    "csa2_index_reindex", "csa2_sparse_attn", "csa2_sparse_attn_append", "csa2_status_str",
 ]
 
 
@@ -75,6 +75,8 @@ def load() -> C.CDLL:
                                    vp, sz, vp],
             "csa2_sparse_attn": [cfgp, vp, vp, i64, vp, i32, vp, i32, vp, i32, vp, vp, vp, vp, vp,
                                  sz, vp],
+            "csa2_sparse_attn_append": [cfgp, vp, vp, vp, vp, i64, vp, i32, vp, i32, vp, i32, vp, vp,
+                                        vp, vp, vp, sz, vp],
         }
         for name, args in sig.items():
             f = getattr(lib, name)
@@ -210,3 +212,11 @@ def csa2_sparse_attn(cfg, q, kv_cache, n_blocks, block_table, swa_cache, C_slots
     _call("csa2_sparse_attn", C.byref(cfg), _p(q), _p(kv_cache), int(n_blocks), _p(block_table),
           maxb, _p(swa_cache), int(C_slots), _p(ctx_len), batch, _p(topk), _p(topk_len),
           _p(out), _p(lse), _p(ws), ws.numel(), _stream(stream))
+
+
+def csa2_sparse_attn_append(cfg, swa_rows, pos, q, kv_cache, n_blocks, block_table, swa_cache,
+                            C_slots, ctx_len, topk, topk_len, out, lse, ws, stream=None):
+    batch, maxb = block_table.shape
+    _call("csa2_sparse_attn_append", C.byref(cfg), _p(swa_rows), _p(pos), _p(q), _p(kv_cache),
+          int(n_blocks), _p(block_table), maxb, _p(swa_cache), int(C_slots), _p(ctx_len), batch,
+          _p(topk), _p(topk_len), _p(out), _p(lse), _p(ws), ws.numel(), _stream(stream))

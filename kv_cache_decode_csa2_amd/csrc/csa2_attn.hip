@@ -10,21 +10,25 @@
 // not de-duplicated.
 //
 // Work split: the row list of a sequence is [0, k) = top-k entries (padding masked),
-// then [k, k+W) = window positions; workgroup (split, b) owns 64 consecutive rows.
-//   1. Each lane gathers one row's 128-dim quarter straight from HBM and converts it to
-//      bf16 with the gfx950 scaled converters (exact: E2M1 / E4M3 values times a power of
-//      two fit bf16).  Those registers are the B operand of S = Q K^T on MFMA
-//      16x16x32 bf16 (fp32 accumulation); the same values go to LDS transposed (V^T).
-//   2. Softmax statistics per head over the 64 rows (wave shuffles + LDS).
-//   3. O += P V on MFMA with P split into bf16 hi + lo parts (error ~2^-17 relative).
-//   4. Partial (O, max, sum) per split -> k_attn_merge combines the splits.
-#include "csa2_common.h"
+// then [k, k+W) = window positions; workgroup (split, sequence, head group of 16) owns 64
+// consecutive rows.
+//   1. Each lane loads its slice of the 16 query rows while the row addresses resolve
+//      (top-k entry, then block table), so those loads overlap that chain.
+//   2. Each lane gathers one row's 128-dim quarter and converts it to bf16 with the
+//      gfx950 scaled converters (exact: E2M1 / E4M3 values times a power of two fit
+//      bf16).  Those registers are the B operand of S = Q K^T on MFMA 16x16x32 bf16 (fp32
+//      accumulation); the same values go to LDS transposed (V^T).
+//   3. Softmax statistics per head over the 64 rows (wave shuffles + LDS).
+//   4. O = P V on MFMA with P split into bf16 hi + lo parts (error ~2^-17 relative).
+//   5. The partial (O, max, sum) goes to the workspace; k_attn_merge combines the splits.
+#include "csa2_quant.h"
 
 namespace csa2 {
 
 constexpr int kAttnThreads = 256;
 constexpr int kD = 512;            // latent dim handled by these kernels
 constexpr int kPStride = 64 + 4;   // padded row of the P tile (floats)
+constexpr int kMaxSplits = 512;    // splits a merge handles (k + W <= 32768)
 
 struct AttnArgs {
     const uint16_t *q;
@@ -41,6 +45,7 @@ struct AttnArgs {
     int32_t k;
     int32_t W;
     int32_t Hq;
+    int32_t HG;        // head groups of 16
     float scale_log2;  // sm_scale * log2(e)
     float sm_scale;
     int32_t nsplit;
@@ -48,6 +53,11 @@ struct AttnArgs {
     float *part_ml;
     float *out;
     float *lse;
+    // fused window append (null: none): row swa_new[b] (fp32, D) is quantised into ring
+    // slot new_pos[b] % C before it is attended
+    const float *swa_new;
+    const int32_t *new_pos;
+    uint8_t *swa_out;
 };
 
 __device__ __forceinline__ int clamp_ctx(int32_t L, int maxb) {
@@ -72,193 +82,21 @@ __device__ __forceinline__ int vt_index(int d, int r) {
     return d * 64 + ((((r >> 3) ^ (d >> 1)) & 7) << 3) + (r & 7);
 }
 
-__global__ __launch_bounds__(kAttnThreads) void k_attn_split(AttnArgs a) {
-    __shared__ __align__(16) __bf16 vt[kD * 64];
-    __shared__ __align__(16) float ptile[16 * kPStride];
-    __shared__ float red_m[4][16], red_l[4][16];
-    __shared__ int any_valid;
+struct AttnShared {
+    __bf16 vt[kD * 64];                    // V^T tile (64 KB)
+    float ptile[16 * kPStride];
+    float red_m[4][16], red_l[4][16];
+    __align__(16) uint8_t fresh_row[kD + kD / 32];  // the appended window row (MXFP8)
+    int any_valid, has_fresh;
+};
 
-    const int s = blockIdx.x, b = blockIdx.y;
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int c16 = lane & 15, g4 = lane >> 4;
-    const int L = clamp_ctx(a.ctx_len[b], a.maxb);
-    const int tl = max(0, min(a.topk_len[b], a.k));
-    const int w0 = max(0, L - a.W), nwin = L - w0;
-    const int r_loc = 16 * wave + c16;
-    const int rg = s * kAttnRows + r_loc;
-
-    // ---- locate this lane's row
-    const uint8_t *rp = nullptr;
-    bool fp8 = false;
-    if (rg < a.k) {
-        if (rg < tl) {
-            const int p = a.topk[(int64_t)b * a.k + rg];
-            if (p >= 0 && p < L) {
-                const int64_t phys = a.table[(int64_t)b * a.maxb + p / kBlk];
-                if (phys >= 0 && phys < a.n_blocks)
-                    rp = a.kv + phys * (kBlk * (kD / 2 + kD / 32)) + (p % kBlk) * (kD / 2 + kD / 32);
-            }
-        }
-    } else {
-        const int wi = rg - a.k;
-        if (wi < nwin && wi < a.W) {
-            const int p = w0 + wi;
-            rp = a.swa + ((int64_t)b * a.C + p % a.C) * (kD + kD / 32);
-            fp8 = true;
-        }
-    }
-    const bool valid = rp != nullptr;
-    if (tid == 0) any_valid = 0;
-    __syncthreads();
-    if (valid) any_valid = 1;
-    __syncthreads();
-    const int64_t pbase = ((int64_t)b * a.nsplit + s) * a.Hq;
-    if (!any_valid) {
-        for (int h = tid; h < a.Hq; h += kAttnThreads) {
-            a.part_ml[2 * (pbase + h)] = -INFINITY;
-            a.part_ml[2 * (pbase + h) + 1] = 0.0f;
-        }
-        return;
-    }
-
-    // ---- gather + exact conversion to bf16: kb[t] = dims g4*128 + 8t .. +8 of the row
-    bf16x8_t kb[16];
-    if (valid && !fp8) {
-        const uint4 *src = reinterpret_cast<const uint4 *>(rp + g4 * 64);
-        const uint4 u0 = src[0], u1 = src[1], u2 = src[2], u3 = src[3];
-        const uint32_t sc4 = *reinterpret_cast<const uint32_t *>(rp + kD / 2 + 4 * g4);
-        const uint4 uu[4] = {u0, u1, u2, u3};
-#pragma unroll
-        for (int t = 0; t < 16; t++) {
-            const uint32_t wd = word_of(uu[t >> 2], t & 3);
-            const float sc = e8m0_to_f32((sc4 >> (8 * (t >> 2))) & 255u);
-            kb[t] = join4(__builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(wd, sc, 0),
-                          __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(wd, sc, 1),
-                          __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(wd, sc, 2),
-                          __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(wd, sc, 3));
-        }
-    } else if (valid) {
-        const uint4 *src = reinterpret_cast<const uint4 *>(rp + g4 * 128);
-        uint4 uu[8];
-#pragma unroll
-        for (int i = 0; i < 8; i++) uu[i] = src[i];
-        const uint32_t sc4 = *reinterpret_cast<const uint32_t *>(rp + kD + 4 * g4);
-#pragma unroll
-        for (int t = 0; t < 16; t++) {
-            const uint32_t w0d = word_of(uu[t >> 1], 2 * (t & 1)), w1d = word_of(uu[t >> 1], 2 * (t & 1) + 1);
-            const float sc = e8m0_to_f32((sc4 >> (8 * (t >> 2))) & 255u);
-            kb[t] = join4(__builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w0d, sc, false),
-                          __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w0d, sc, true),
-                          __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w1d, sc, false),
-                          __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w1d, sc, true));
-        }
-    } else {
-#pragma unroll
-        for (int t = 0; t < 16; t++)
-#pragma unroll
-            for (int i = 0; i < 8; i++) kb[t][i] = (__bf16)0.0f;
-    }
-
-    // ---- V^T into LDS
-#pragma unroll
-    for (int t = 0; t < 16; t++)
-#pragma unroll
-        for (int i = 0; i < 8; i++) vt[vt_index(g4 * 128 + 8 * t + i, r_loc)] = kb[t][i];
-    __syncthreads();
-
-    for (int hg = 0; hg < a.Hq / 16; hg++) {
-        // ---- S = Q K^T for this wave's 16 rows and 16 heads
-        const uint16_t *qh = a.q + ((int64_t)b * a.Hq + hg * 16 + c16) * kD + g4 * 128;
-        f32x4_t acc = {0.0f, 0.0f, 0.0f, 0.0f};
-#pragma unroll
-        for (int t = 0; t < 16; t++) {
-            const bf16x8_t qa = *reinterpret_cast<const bf16x8_t *>(qh + 8 * t);
-            acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa, kb[t], acc, 0, 0, 0);
-        }
-        // lane holds S[head 4*g4 + j][row c16 of this wave]
-        float sv[4], mx[4];
-#pragma unroll
-        for (int j = 0; j < 4; j++) {
-            sv[j] = valid ? acc[j] : -INFINITY;
-            float m = sv[j];
-            m = fmaxf(m, __shfl_xor(m, 1, kWave));
-            m = fmaxf(m, __shfl_xor(m, 2, kWave));
-            m = fmaxf(m, __shfl_xor(m, 4, kWave));
-            m = fmaxf(m, __shfl_xor(m, 8, kWave));
-            mx[j] = m;
-        }
-        if (c16 == 0)
-#pragma unroll
-            for (int j = 0; j < 4; j++) red_m[wave][4 * g4 + j] = mx[j];
-        __syncthreads();
-        float pv[4], ls[4];
-#pragma unroll
-        for (int j = 0; j < 4; j++) {
-            const int h = 4 * g4 + j;
-            const float M = fmaxf(fmaxf(red_m[0][h], red_m[1][h]), fmaxf(red_m[2][h], red_m[3][h]));
-            pv[j] = valid ? exp2f((sv[j] - M) * a.scale_log2) : 0.0f;
-            float l = pv[j];
-            l += __shfl_xor(l, 1, kWave);
-            l += __shfl_xor(l, 2, kWave);
-            l += __shfl_xor(l, 4, kWave);
-            l += __shfl_xor(l, 8, kWave);
-            ls[j] = l;
-            ptile[h * kPStride + r_loc] = pv[j];
-        }
-        if (c16 == 0)
-#pragma unroll
-            for (int j = 0; j < 4; j++) red_l[wave][4 * g4 + j] = ls[j];
-        __syncthreads();
-        if (tid < 16) {
-            const int h = tid;
-            const float M = fmaxf(fmaxf(red_m[0][h], red_m[1][h]), fmaxf(red_m[2][h], red_m[3][h]));
-            const float l = red_l[0][h] + red_l[1][h] + red_l[2][h] + red_l[3][h];
-            a.part_ml[2 * (pbase + hg * 16 + h)] = M;
-            a.part_ml[2 * (pbase + hg * 16 + h) + 1] = l;
-        }
-
-        // ---- O = P V for this wave's 8 column tiles (128 dims)
-        bf16x8_t ph[2], plo[2];
-#pragma unroll
-        for (int ks = 0; ks < 2; ks++) {
-            const float4 *pr = reinterpret_cast<const float4 *>(ptile + c16 * kPStride + 32 * ks + 8 * g4);
-            const float4 x0 = pr[0], x1 = pr[1];
-            const float f[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
-#pragma unroll
-            for (int i = 0; i < 8; i++) {
-                const __bf16 hi = (__bf16)f[i];
-                ph[ks][i] = hi;
-                plo[ks][i] = (__bf16)(f[i] - (float)hi);
-            }
-        }
-        float *po = a.part_o + (pbase + hg * 16) * kD;
-#pragma unroll
-        for (int n = 0; n < 8; n++) {
-            const int nt = 8 * wave + n;
-            const int d = 16 * nt + c16;
-            f32x4_t o = {0.0f, 0.0f, 0.0f, 0.0f};
-#pragma unroll
-            for (int ks = 0; ks < 2; ks++) {
-                const int chunk = 4 * ks + g4;
-                const bf16x8_t vb = *reinterpret_cast<const bf16x8_t *>(
-                    &vt[d * 64 + (((chunk ^ (d >> 1)) & 7) << 3)]);
-                o = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ph[ks], vb, o, 0, 0, 0);
-                o = __builtin_amdgcn_mfma_f32_16x16x32_bf16(plo[ks], vb, o, 0, 0, 0);
-            }
-#pragma unroll
-            for (int j = 0; j < 4; j++) po[(4 * g4 + j) * kD + d] = o[j];
-        }
-        __syncthreads();  // ptile / red reused by the next head group
-    }
-}
-
-// Combine the splits: out = sum_s 2^((m_s - M) c) O_s / sum_s 2^((m_s - M) c) l_s.  The
-// split statistics go through LDS first so that the partial rows load independently.
+// Combine the splits of (b, head h): out = sum_s 2^((m_s - M) c) O_s / sum_s 2^((m_s - M) c) l_s.
+// The split statistics go through LDS first, then every partial row loads in one batch
+// (the loop over splits is unrolled by 8).
 constexpr int kMergeThreads = 128;
-constexpr int kMaxMergeSplits = 512;
 
 __global__ __launch_bounds__(kMergeThreads) void k_attn_merge(AttnArgs a) {
-    __shared__ float wgt[kMaxMergeSplits];
+    __shared__ float wgt[kMaxSplits];
     __shared__ float red[kMergeThreads / kWave][2];
     const int h = blockIdx.x, b = blockIdx.y, tid = threadIdx.x;
     const int64_t base = (int64_t)b * a.nsplit * a.Hq;
@@ -292,7 +130,7 @@ __global__ __launch_bounds__(kMergeThreads) void k_attn_merge(AttnArgs a) {
     for (int s = 0; s < a.nsplit; s++) {
         const float e = wgt[s];
         const float4 v = reinterpret_cast<const float4 *>(a.part_o + (base + (int64_t)s * a.Hq + h) * kD)[tid];
-        if (e != 0.0f) {
+        if (e != 0.0f) {  // an empty split's partial row was never written
             acc.x += e * v.x;
             acc.y += e * v.y;
             acc.z += e * v.z;
@@ -309,24 +147,246 @@ __global__ __launch_bounds__(kMergeThreads) void k_attn_merge(AttnArgs a) {
         a.lse[(int64_t)b * a.Hq + h] = lw > 0.0f ? a.sm_scale * M + logf(lw) : -INFINITY;
 }
 
+__global__ __launch_bounds__(kAttnThreads) void k_attn(AttnArgs a) {
+    __shared__ __align__(16) AttnShared sh;
+
+    const int s = blockIdx.x, b = blockIdx.y / a.HG, hg = blockIdx.y % a.HG;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int c16 = lane & 15, g4 = lane >> 4;
+
+    // ---- this lane's query slice (head c16, dims g4*128 ..), the A operand of S = Q K^T;
+    //      loaded first so that it overlaps the row-address chain
+    bf16x8_t qa[16];
+    {
+        const bf16x8_t *qh = reinterpret_cast<const bf16x8_t *>(
+            a.q + ((int64_t)b * a.Hq + hg * 16 + c16) * kD + g4 * 128);
+#pragma unroll
+        for (int t = 0; t < 16; t++) qa[t] = qh[t];
+    }
+
+    const int L = clamp_ctx(a.ctx_len[b], a.maxb);
+    const int tl = max(0, min(a.topk_len[b], a.k));
+    const int w0 = max(0, L - a.W), nwin = L - w0;
+    const int r_loc = 16 * wave + c16;
+    const int rg = s * kAttnRows + r_loc;
+
+    const int np_b = a.swa_new ? a.new_pos[b] : -1;
+
+    // ---- locate this lane's row
+    const uint8_t *rp = nullptr;
+    bool fp8 = false, fresh = false;
+    if (rg < a.k) {
+        if (rg < tl) {
+            const int p = a.topk[(int64_t)b * a.k + rg];
+            if (p >= 0 && p < L) {
+                const int64_t phys = a.table[(int64_t)b * a.maxb + p / kBlk];
+                if (phys >= 0 && phys < a.n_blocks)
+                    rp = a.kv + phys * (kBlk * (kD / 2 + kD / 32)) + (p % kBlk) * (kD / 2 + kD / 32);
+            }
+        }
+    } else {
+        const int wi = rg - a.k;
+        if (wi < nwin && wi < a.W) {
+            const int p = w0 + wi;
+            rp = a.swa + ((int64_t)b * a.C + p % a.C) * (kD + kD / 32);
+            fp8 = true;
+            fresh = p == np_b;  // the appended row: quantised here, not read back
+        }
+    }
+
+    // ---- an appended row outside the attended window is still written (split 0, hg 0)
+    if (a.swa_new && s == 0 && hg == 0 && np_b >= 0 && !(np_b >= w0 && np_b < L && np_b - w0 < a.W) &&
+        tid < kD / 32) {
+        uint8_t *dst = a.swa_out + ((int64_t)b * a.C + np_b % a.C) * (kD + kD / 32);
+        quant_fp8(a.swa_new + (int64_t)b * kD + 32 * tid, dst + 32 * tid, dst + kD + tid);
+    }
+    const bool valid = rp != nullptr;
+    if (tid == 0) {
+        sh.any_valid = 0;
+        sh.has_fresh = 0;
+    }
+    __syncthreads();
+    if (valid) sh.any_valid = 1;
+    if (fresh) sh.has_fresh = 1;
+    __syncthreads();
+    if (sh.has_fresh) {
+        // the appended row: 16 threads quantise one group each into LDS (and, for the first
+        // head group, into the ring); its lanes then read it from LDS
+        if (tid < kD / 32) {
+            float v[32];
+            load_group(a.swa_new + (int64_t)b * kD + 32 * tid, v);
+            uint32_t w[8];
+            const uint32_t sc = quant_fp8_regs(v, w);
+            uint4 *d4 = reinterpret_cast<uint4 *>(sh.fresh_row + 32 * tid);
+            d4[0] = make_uint4(w[0], w[1], w[2], w[3]);
+            d4[1] = make_uint4(w[4], w[5], w[6], w[7]);
+            sh.fresh_row[kD + tid] = (uint8_t)sc;
+            if (hg == 0) {
+                uint8_t *dst = a.swa_out + ((int64_t)b * a.C + np_b % a.C) * (kD + kD / 32);
+                uint4 *g4p = reinterpret_cast<uint4 *>(dst + 32 * tid);
+                g4p[0] = d4[0];
+                g4p[1] = d4[1];
+                dst[kD + tid] = (uint8_t)sc;
+            }
+        }
+        __syncthreads();
+        if (fresh) rp = sh.fresh_row;
+    }
+    const int64_t pbase = ((int64_t)b * a.nsplit + s) * a.Hq + hg * 16;
+
+    if (sh.any_valid) {
+        // ---- gather + exact conversion to bf16: kb[t] = dims g4*128 + 8t .. +8 of the row
+        bf16x8_t kb[16];
+        if (valid && !fp8) {
+            const uint4 *src = reinterpret_cast<const uint4 *>(rp + g4 * 64);
+            const uint4 u0 = src[0], u1 = src[1], u2 = src[2], u3 = src[3];
+            const uint32_t sc4 = *reinterpret_cast<const uint32_t *>(rp + kD / 2 + 4 * g4);
+            const uint4 uu[4] = {u0, u1, u2, u3};
+#pragma unroll
+            for (int t = 0; t < 16; t++) {
+                const uint32_t wd = word_of(uu[t >> 2], t & 3);
+                const float sc = e8m0_to_f32((sc4 >> (8 * (t >> 2))) & 255u);
+                kb[t] = join4(__builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(wd, sc, 0),
+                              __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(wd, sc, 1),
+                              __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(wd, sc, 2),
+                              __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(wd, sc, 3));
+            }
+        } else if (valid) {
+            const uint4 *src = reinterpret_cast<const uint4 *>(rp + g4 * 128);
+            uint4 uu[8];
+#pragma unroll
+            for (int i = 0; i < 8; i++) uu[i] = src[i];
+            const uint32_t sc4 = *reinterpret_cast<const uint32_t *>(rp + kD + 4 * g4);
+#pragma unroll
+            for (int t = 0; t < 16; t++) {
+                const uint32_t w0d = word_of(uu[t >> 1], 2 * (t & 1)), w1d = word_of(uu[t >> 1], 2 * (t & 1) + 1);
+                const float sc = e8m0_to_f32((sc4 >> (8 * (t >> 2))) & 255u);
+                kb[t] = join4(__builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w0d, sc, false),
+                              __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w0d, sc, true),
+                              __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w1d, sc, false),
+                              __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w1d, sc, true));
+            }
+        } else {
+#pragma unroll
+            for (int t = 0; t < 16; t++)
+#pragma unroll
+                for (int i = 0; i < 8; i++) kb[t][i] = (__bf16)0.0f;
+        }
+
+        // ---- V^T into LDS
+#pragma unroll
+        for (int t = 0; t < 16; t++)
+#pragma unroll
+            for (int i = 0; i < 8; i++) sh.vt[vt_index(g4 * 128 + 8 * t + i, r_loc)] = kb[t][i];
+        __syncthreads();  // V^T is in LDS
+
+        // ---- S = Q K^T for this wave's 16 rows and the 16 heads
+        f32x4_t acc = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+        for (int t = 0; t < 16; t++) acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[t], kb[t], acc, 0, 0, 0);
+        // lane holds S[head 4*g4 + j][row c16 of this wave]
+        float sv[4], mx[4];
+#pragma unroll
+        for (int j = 0; j < 4; j++) {
+            sv[j] = valid ? acc[j] : -INFINITY;
+            float m = sv[j];
+            m = fmaxf(m, __shfl_xor(m, 1, kWave));
+            m = fmaxf(m, __shfl_xor(m, 2, kWave));
+            m = fmaxf(m, __shfl_xor(m, 4, kWave));
+            m = fmaxf(m, __shfl_xor(m, 8, kWave));
+            mx[j] = m;
+        }
+        if (c16 == 0)
+#pragma unroll
+            for (int j = 0; j < 4; j++) sh.red_m[wave][4 * g4 + j] = mx[j];
+        __syncthreads();
+        float pv[4], ls[4];
+#pragma unroll
+        for (int j = 0; j < 4; j++) {
+            const int h = 4 * g4 + j;
+            const float M = fmaxf(fmaxf(sh.red_m[0][h], sh.red_m[1][h]), fmaxf(sh.red_m[2][h], sh.red_m[3][h]));
+            pv[j] = valid ? exp2f((sv[j] - M) * a.scale_log2) : 0.0f;
+            float l = pv[j];
+            l += __shfl_xor(l, 1, kWave);
+            l += __shfl_xor(l, 2, kWave);
+            l += __shfl_xor(l, 4, kWave);
+            l += __shfl_xor(l, 8, kWave);
+            ls[j] = l;
+            sh.ptile[h * kPStride + r_loc] = pv[j];
+        }
+        if (c16 == 0)
+#pragma unroll
+            for (int j = 0; j < 4; j++) sh.red_l[wave][4 * g4 + j] = ls[j];
+        __syncthreads();
+        if (tid < 16) {
+            const int h = tid;
+            const float M = fmaxf(fmaxf(sh.red_m[0][h], sh.red_m[1][h]), fmaxf(sh.red_m[2][h], sh.red_m[3][h]));
+            const float l = sh.red_l[0][h] + sh.red_l[1][h] + sh.red_l[2][h] + sh.red_l[3][h];
+            a.part_ml[2 * (pbase + h)] = M;
+            a.part_ml[2 * (pbase + h) + 1] = l;
+        }
+
+        // ---- O = P V for this wave's 8 column tiles (128 dims)
+        bf16x8_t ph[2], plo[2];
+#pragma unroll
+        for (int ks = 0; ks < 2; ks++) {
+            const float4 *pr = reinterpret_cast<const float4 *>(sh.ptile + c16 * kPStride + 32 * ks + 8 * g4);
+            const float4 x0 = pr[0], x1 = pr[1];
+            const float f[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
+#pragma unroll
+            for (int i = 0; i < 8; i++) {
+                const __bf16 hi = (__bf16)f[i];
+                ph[ks][i] = hi;
+                plo[ks][i] = (__bf16)(f[i] - (float)hi);
+            }
+        }
+        float *po = a.part_o + pbase * kD;
+#pragma unroll
+        for (int n = 0; n < 8; n++) {
+            const int nt = 8 * wave + n;
+            const int d = 16 * nt + c16;
+            f32x4_t o = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+            for (int ks = 0; ks < 2; ks++) {
+                const int chunk = 4 * ks + g4;
+                const bf16x8_t vb = *reinterpret_cast<const bf16x8_t *>(
+                    &sh.vt[d * 64 + (((chunk ^ (d >> 1)) & 7) << 3)]);
+                o = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ph[ks], vb, o, 0, 0, 0);
+                o = __builtin_amdgcn_mfma_f32_16x16x32_bf16(plo[ks], vb, o, 0, 0, 0);
+            }
+#pragma unroll
+            for (int j = 0; j < 4; j++) po[(4 * g4 + j) * kD + d] = o[j];
+        }
+    } else {
+        for (int h = tid; h < 16; h += kAttnThreads) {
+            a.part_ml[2 * (pbase + h)] = -INFINITY;
+            a.part_ml[2 * (pbase + h) + 1] = 0.0f;
+        }
+    }
+
+}
+
 }  // namespace csa2
 
 using namespace csa2;
 
-extern "C" int csa2_sparse_attn(const csa2_config *c, const uint16_t *q, const uint8_t *kv_cache,
-                                int64_t n_blocks, const int32_t *block_table, int32_t maxb,
-                                const uint8_t *swa_cache, int32_t C, const int32_t *ctx_len,
-                                int32_t batch, const int32_t *topk, const int32_t *topk_len,
-                                float *out, float *lse, void *ws, size_t ws_bytes,
-                                hipStream_t stream) {
+namespace {
+
+int sparse_attn(const csa2_config *c, const float *swa_new, const int32_t *new_pos,
+                const uint16_t *q, const uint8_t *kv_cache, int64_t n_blocks,
+                const int32_t *block_table, int32_t maxb, const uint8_t *swa_cache,
+                uint8_t *swa_out, int32_t C, const int32_t *ctx_len, int32_t batch,
+                const int32_t *topk, const int32_t *topk_len, float *out, float *lse, void *ws,
+                size_t ws_bytes, hipStream_t stream) {
     if (!c || !q || !kv_cache || n_blocks <= 0 || !block_table || maxb <= 0 || !ctx_len ||
         batch < 0 || !topk || !topk_len || !out || !lse || !ws || c->topk <= 0 ||
         c->swa_window < 0 || c->n_q_heads <= 0 || c->kv_dim <= 0)
         return CSA2_ERR_INVALID;
     if (c->swa_window > 0 && (!swa_cache || C < c->swa_window)) return CSA2_ERR_INVALID;
+    if (swa_new && (!new_pos || !swa_out || C <= 0)) return CSA2_ERR_INVALID;
     if (c->kv_dim != kD || c->n_q_heads % 16 || c->n_q_heads > 128) return CSA2_ERR_UNSUPPORTED;
     const int nsplit = attn_splits(c->topk, c->swa_window);
-    if (nsplit > kMaxMergeSplits) return CSA2_ERR_UNSUPPORTED;
+    if (nsplit > kMaxSplits) return CSA2_ERR_UNSUPPORTED;
     const WsAttn wl = ws_attn(batch, c->n_q_heads, c->kv_dim, nsplit);
     if (ws_bytes < wl.total) return CSA2_ERR_WORKSPACE;
     if (batch == 0) return CSA2_OK;
@@ -345,6 +405,7 @@ extern "C" int csa2_sparse_attn(const csa2_config *c, const uint16_t *q, const u
     a.k = c->topk;
     a.W = c->swa_window;
     a.Hq = c->n_q_heads;
+    a.HG = c->n_q_heads / 16;
     a.sm_scale = c->sm_scale;
     a.scale_log2 = c->sm_scale * 1.4426950408889634f;
     a.nsplit = nsplit;
@@ -352,7 +413,35 @@ extern "C" int csa2_sparse_attn(const csa2_config *c, const uint16_t *q, const u
     a.part_ml = (float *)((uint8_t *)ws + wl.part_ml);
     a.out = out;
     a.lse = lse;
-    k_attn_split<<<dim3(nsplit, batch), kAttnThreads, 0, stream>>>(a);
+    a.swa_new = swa_new;
+    a.new_pos = new_pos;
+    a.swa_out = swa_out;
+    k_attn<<<dim3(nsplit, batch * a.HG), kAttnThreads, 0, stream>>>(a);
     k_attn_merge<<<dim3(c->n_q_heads, batch), kMergeThreads, 0, stream>>>(a);
     return hipGetLastError() == hipSuccess ? CSA2_OK : CSA2_ERR_HIP;
+}
+
+}  // namespace
+
+extern "C" int csa2_sparse_attn(const csa2_config *c, const uint16_t *q, const uint8_t *kv_cache,
+                                int64_t n_blocks, const int32_t *block_table, int32_t maxb,
+                                const uint8_t *swa_cache, int32_t C, const int32_t *ctx_len,
+                                int32_t batch, const int32_t *topk, const int32_t *topk_len,
+                                float *out, float *lse, void *ws, size_t ws_bytes,
+                                hipStream_t stream) {
+    return sparse_attn(c, nullptr, nullptr, q, kv_cache, n_blocks, block_table, maxb, swa_cache,
+                       nullptr, C, ctx_len, batch, topk, topk_len, out, lse, ws, ws_bytes, stream);
+}
+
+extern "C" int csa2_sparse_attn_append(const csa2_config *c, const float *swa_rows,
+                                       const int32_t *pos, const uint16_t *q,
+                                       const uint8_t *kv_cache, int64_t n_blocks,
+                                       const int32_t *block_table, int32_t maxb,
+                                       uint8_t *swa_cache, int32_t C, const int32_t *ctx_len,
+                                       int32_t batch, const int32_t *topk,
+                                       const int32_t *topk_len, float *out, float *lse, void *ws,
+                                       size_t ws_bytes, hipStream_t stream) {
+    if (!swa_rows || !pos || !swa_cache) return CSA2_ERR_INVALID;
+    return sparse_attn(c, swa_rows, pos, q, kv_cache, n_blocks, block_table, maxb, swa_cache,
+                       swa_cache, C, ctx_len, batch, topk, topk_len, out, lse, ws, ws_bytes, stream);
 }

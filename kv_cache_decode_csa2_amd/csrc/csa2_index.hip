@@ -432,10 +432,10 @@ constexpr int kHistBins = 2048;
 constexpr uint32_t kAllTies = 0xFFFFFFFFu;
 
 struct SelShared {
-    uint32_t hist[kHistBins];
+    __align__(16) uint32_t hist[kHistBins];  // reversed: hist[nbins - 1 - bin]; zero between passes
     __align__(16) uint32_t scan[kSelThreads / kWave];
-    __align__(16) uint32_t red[2][kSelThreads / kWave];
-    uint32_t res[3];
+    __align__(16) uint32_t red[3][kSelThreads / kWave];
+    uint32_t res[4];
 };
 
 struct SelResult {
@@ -443,136 +443,111 @@ struct SelResult {
     uint32_t need;
 };
 
-// Inverse of order_key.
-__device__ __forceinline__ float key_value(uint32_t k) {
-    return __uint_as_float((k & 0x80000000u) ? (k & 0x7FFFFFFFu) : ~k);
-}
-
-// Block-wide min and max of (lo, hi).
-__device__ __forceinline__ void block_min_max(uint32_t &lo, uint32_t &hi, SelShared &sm) {
+// Block-wide min, max and sum of (lo, hi, n).
+__device__ __forceinline__ void block_min_max_count(uint32_t &lo, uint32_t &hi, uint32_t &n,
+                                                    SelShared &sm) {
     const int lane = lane_id(), wave = threadIdx.x / kWave;
     lo = wave_reduce_to63(lo, [](uint32_t x, uint32_t y) { return x < y ? x : y; });
     hi = wave_reduce_to63(hi, [](uint32_t x, uint32_t y) { return x > y ? x : y; });
+    n = wave_reduce_to63(n, [](uint32_t x, uint32_t y) { return x + y; });
     __syncthreads();
     if (lane == kWave - 1) {
         sm.red[0][wave] = lo;
         sm.red[1][wave] = hi;
+        sm.red[2][wave] = n;
     }
     __syncthreads();
     lo = 0xFFFFFFFFu;
     hi = 0u;
+    n = 0u;
 #pragma unroll
     for (int i = 0; i < kSelThreads / kWave; i += 4) {
         const uint4 a4 = *reinterpret_cast<const uint4 *>(&sm.red[0][i]);
         const uint4 b4 = *reinterpret_cast<const uint4 *>(&sm.red[1][i]);
+        const uint4 c4 = *reinterpret_cast<const uint4 *>(&sm.red[2][i]);
         lo = min(min(min(lo, a4.x), min(a4.y, a4.z)), a4.w);
         hi = max(max(max(hi, b4.x), max(b4.y, b4.z)), b4.w);
+        n += c4.x + c4.y + c4.z + c4.w;
     }
 }
 
-// From a histogram of nbins bins (counts per bin, bin nbins-1 highest): the bin d holding
-// the `remaining`-th largest item, the count of items in higher bins, and d's count.
-__device__ __forceinline__ void find_bin(SelShared &sm, int nbins, uint32_t remaining, uint32_t &d,
-                                         uint32_t &above, uint32_t &cnt) {
-    const int tid = threadIdx.x;
-    const int d0 = nbins - 1 - 2 * tid, d1 = d0 - 1;
-    const uint32_t c0 = d0 >= 0 ? sm.hist[d0] : 0u, c1 = d1 >= 0 ? sm.hist[d1] : 0u;
-    uint32_t tot;
-    const uint32_t before = block_excl_scan<kSelThreads>(c0 + c1, sm.scan, &tot);
-    if (before < remaining && remaining <= before + c0 + c1) {
-        if (before + c0 >= remaining) {
-            sm.res[0] = (uint32_t)d0;
-            sm.res[1] = before;
-            sm.res[2] = c0;
-        } else {
-            sm.res[0] = (uint32_t)d1;
-            sm.res[1] = before + c0;
-            sm.res[2] = c1;
-        }
-    }
-    __syncthreads();
-    d = sm.res[0];
-    above = sm.res[1];
-    cnt = sm.res[2];
-    __syncthreads();
-}
-
-// Histogram increment with the wave's most common case folded: lanes whose bin equals the
-// first active lane's bin add through one atomic (a pile of equal keys, e.g. scores that
-// are exactly 0 after the ReLU, would otherwise serialise on one LDS address).
-__device__ __forceinline__ void hist_add(uint32_t *hist, int bin) {
-    const int first = __builtin_amdgcn_readfirstlane(bin);
-    const uint64_t same = __ballot(bin == first);
-    const int leader = __ffsll((long long)same) - 1;
-    if (bin != first) atomicAdd(&hist[bin], 1u);
-    else if (lane_id() == leader) atomicAdd(&hist[bin], (uint32_t)__popcll(same));
-}
-
-// Src::each(f) calls f(key) for every item the calling thread owns.  Precondition: the
-// number of items is >= K >= 1.
-//   Pass 1 (wide key ranges of finite scores): bins linear in the score value, which
-//   spreads scores that crowd into a few binades; the chosen bin's exact key range
-//   follows from a min/max over its items (the bin map is monotone).
-//   Further passes: bins of width 2^s in key space over the current range.
+// Exact K-th largest of a multiset of uint32 keys (items owned by the threads; Src::each(f)
+// calls f(key) for each), K >= 1 and <= the number of items.  Each pass histograms the
+// current key range [lo, hi] into <= 2048 bins of width 2^s in LDS and narrows the range to
+// the bin that holds the K-th largest.  Wave 0 alone scans the histogram (and zeroes it for
+// the next pass), so a pass costs two barriers.  The lowest bin gets no atomics: its count
+// is the range's item count minus the other bins (a pile of equal minimal keys, such as
+// scores that are exactly 0 after the ReLU, never serialises on one LDS address).
+// Result: an item is selected iff key > thr, or key == thr and fewer than `need` such items
+// precede it in index order (need == kAllTies: all of them).
 template <class Src>
 __device__ __forceinline__ SelResult range_select(const Src &src, uint32_t K, SelShared &sm) {
-    const int tid = threadIdx.x;
-    uint32_t lo = 0xFFFFFFFFu, hi = 0u;
+    const int tid = threadIdx.x, lane = lane_id(), wave = threadIdx.x / kWave;
+    uint32_t lo = 0xFFFFFFFFu, hi = 0u, n_in = 0u;
     src.each([&](uint32_t key) {
         lo = min(lo, key);
         hi = max(hi, key);
+        n_in++;
     });
-    block_min_max(lo, hi, sm);
+    block_min_max_count(lo, hi, n_in, sm);
     uint32_t remaining = K;
-    if (hi - lo >= (uint32_t)kHistBins) {
-        const float vlo = key_value(lo), vhi = key_value(hi);
-        const float span = vhi - vlo;
-        if (__builtin_isfinite(vlo) && __builtin_isfinite(vhi) && __builtin_isfinite(span) && span > 0.0f) {
-            const float scale = (float)kHistBins / span;
-            auto vbin = [&](uint32_t key) {
-                const float t = (key_value(key) - vlo) * scale;  // monotone in key, >= 0
-                return min(kHistBins - 1, (int)t);
-            };
-            for (int i = tid; i < kHistBins; i += kSelThreads) sm.hist[i] = 0u;
-            __syncthreads();
-            src.each([&](uint32_t key) { hist_add(sm.hist, vbin(key)); });
-            __syncthreads();
-            uint32_t d, above, cnt;
-            find_bin(sm, kHistBins, remaining, d, above, cnt);
-            remaining -= above;
-            uint32_t blo = 0xFFFFFFFFu, bhi = 0u;
-            src.each([&](uint32_t key) {
-                if (vbin(key) == (int)d) {
-                    blo = min(blo, key);
-                    bhi = max(bhi, key);
-                }
-            });
-            block_min_max(blo, bhi, sm);
-            if (cnt == remaining) return {blo, kAllTies};  // the whole bin is needed
-            lo = blo;
-            hi = bhi;
-        }
-    }
 #pragma unroll 1
     for (int pass = 0; pass < 6 && lo != hi; pass++) {
         const uint32_t w = hi - lo;
         const int s = max(0, 32 - __clz((int)w) - 11);  // (w >> s) < 2048
         const int nbins = (int)(w >> s) + 1;
-        for (int i = tid; i < nbins; i += kSelThreads) sm.hist[i] = 0u;
-        __syncthreads();
         src.each([&](uint32_t key) {
-            if (key >= lo && key <= hi) hist_add(sm.hist, (int)((key - lo) >> s));
+            if (key > lo && key <= hi) {
+                const int bin = (int)((key - lo) >> s);
+                if (bin > 0) atomicAdd(&sm.hist[nbins - 1 - bin], 1u);
+            }
         });
         __syncthreads();
-        uint32_t d, above, cnt;
-        find_bin(sm, nbins, remaining, d, above, cnt);
+        if (wave == 0) {
+            // lane l: reversed bins [32 l, 32 l + 32) = bins nbins-1-32l down to nbins-32-32l
+            const int li0 = nbins - 1;  // reversed index of the lowest bin (no atomics)
+            uint4 *h4 = reinterpret_cast<uint4 *>(sm.hist) + 8 * lane;
+            uint32_t part = 0;
+#pragma unroll
+            for (int i = 0; i < 8; i++) {
+                const uint4 v = h4[i];
+                const int r0 = 32 * lane + 4 * i;
+                part += (r0 < li0 ? v.x : 0u) + (r0 + 1 < li0 ? v.y : 0u) + (r0 + 2 < li0 ? v.z : 0u) +
+                        (r0 + 3 < li0 ? v.w : 0u);
+            }
+            const uint32_t incl = wave_incl_scan(part);
+            const uint32_t explicit_total = (uint32_t)__builtin_amdgcn_readlane((int)incl, kWave - 1);
+            const uint32_t bin0 = n_in - explicit_total;  // the lowest bin, counted implicitly
+            const bool has0 = li0 >= 32 * lane && li0 < 32 * lane + 32;
+            const uint32_t before = incl - part;
+            const bool here = before < remaining && remaining <= before + part + (has0 ? bin0 : 0u);
+            // the lane holding the target bin; its 32 bins are scanned by 32 lanes
+            const int tl = __ffsll((long long)__ballot(here)) - 1;
+            const uint32_t tbefore = (uint32_t)__builtin_amdgcn_readlane((int)before, tl);
+            const int ri = 32 * tl + (lane & 31);
+            const uint32_t ci = lane >= 32 || ri > li0 ? 0u : (ri == li0 ? bin0 : sm.hist[ri]);
+            const uint32_t cincl = tbefore + wave_incl_scan(ci);
+            const uint64_t reach = __ballot(lane < 32 && ri <= li0 && cincl >= remaining);
+            const int tb = __ffsll((long long)reach) - 1;
+            if (lane == tb) {
+                sm.res[0] = (uint32_t)(li0 - ri);
+                sm.res[1] = cincl - ci;
+                sm.res[2] = ci;
+            }
+#pragma unroll
+            for (int i = 0; i < 8; i++) h4[i] = make_uint4(0u, 0u, 0u, 0u);
+        }
+        __syncthreads();
+        const uint32_t d = sm.res[0], above = sm.res[1], cnt = sm.res[2];
         remaining -= above;
+        n_in = cnt;
         const uint32_t nlo = lo + (d << s);
         if (cnt == remaining) return {nlo, kAllTies};  // the whole bin is needed
         const uint64_t top = (uint64_t)nlo + ((1ull << s) - 1ull);
         hi = (uint32_t)min((uint64_t)hi, top);
         lo = nlo;
     }
+    (void)tid;
     return {lo, remaining};
 }
 
@@ -666,76 +641,21 @@ struct SelectArgs {
     int32_t *topk_len;
 };
 
-constexpr int kCompactCap = 4096;  // candidates redistributed through LDS (4 per thread)
-
 struct SelectShared {
     SelShared sel;
     int32_t flag[2 * kSelThreads];         // flagged groups (ascending)
     int32_t pool[CSA2_MAX_POOL_BLOCKS];    // pool blocks (ascending)
-    uint32_t ckey[kCompactCap];            // compacted candidates: keys
-    int32_t cid[kCompactCap];              //                      ids
 };
 
-// Candidates held sparsely in a thread's register slots (index order) move to a dense
-// ascending list in LDS and back, at most 4 per thread.  Returns false (nothing moved)
-// when there are more than kCompactCap of them.
+// Exact top-K (K >= 1) of a register set (index order), emitted ascending into out.  The
+// multiset must hold >= K items.
 template <int N, class IdF>
-__device__ __forceinline__ bool compact(const RegItems<N> &it, IdF id, SelectShared &sm,
-                                        RegItems<4> &out, int32_t (&oid)[4], uint32_t &count) {
-    uint32_t tot;
-    uint32_t o = block_excl_scan<kSelThreads>((uint32_t)__popc(it.valid), sm.sel.scan, &tot);
-    count = tot;
-    if (tot > (uint32_t)kCompactCap) return false;
-#pragma unroll
-    for (int i = 0; i < N; i++)
-        if (it.valid & (1u << i)) {
-            sm.ckey[o] = it.key[i];
-            sm.cid[o] = id(i);
-            o++;
-        }
-    __syncthreads();
-    const uint32_t per = (tot + kSelThreads - 1) / kSelThreads;  // <= 4
-    out.valid = 0;
-#pragma unroll
-    for (int i = 0; i < 4; i++) {
-        const uint32_t li = threadIdx.x * per + i;
-        out.key[i] = 0u;
-        oid[i] = -1;
-        if ((uint32_t)i < per && li < tot) {
-            out.key[i] = sm.ckey[li];
-            oid[i] = sm.cid[li];
-            out.valid |= 1u << i;
-        }
-    }
-    __syncthreads();
-    return true;
-}
-
-// Exact top-K (K >= 1) of a sparse register set (index order), emitted ascending into out.
-// Compacts first when the candidates fit; the multiset must hold >= K items.
-template <int N, class IdF>
-__device__ __forceinline__ void select_emit(const RegItems<N> &it, IdF id, uint32_t K, int32_t *out,
-                                            uint32_t out_cap, SelectShared &sm) {
-    RegItems<4> c;
-    int32_t cid[4];
-    uint32_t count;
+__device__ __forceinline__ SelResult select_emit(const RegItems<N> &it, IdF id, uint32_t K,
+                                                 int32_t *out, uint32_t out_cap, SelectShared &sm) {
     uint32_t tie_base = 0, out_base = 0;
-    if (compact(it, id, sm, c, cid, count)) {
-        auto cidf = [&](int i) { return cid[i]; };
-        if (K >= count) {
-            emit_all(c, cidf, out, out_cap, out_base, sm.sel);
-        } else {
-            const SelResult r = range_select(c, K, sm.sel);
-            emit_selected(c, cidf, r, out, out_cap, tie_base, out_base, sm.sel);
-        }
-    } else {
-        if (K >= count) {
-            emit_all(it, id, out, out_cap, out_base, sm.sel);
-        } else {
-            const SelResult r = range_select(it, K, sm.sel);
-            emit_selected(it, id, r, out, out_cap, tie_base, out_base, sm.sel);
-        }
-    }
+    const SelResult r = range_select(it, K, sm.sel);
+    emit_selected(it, id, r, out, out_cap, tie_base, out_base, sm.sel);
+    return r;
 }
 
 // Items of the streaming path: all blocks j < nb whose maximum is >= lam, in chunks of kRegCap.
@@ -777,8 +697,12 @@ struct GlobalBlocks {
 //   3. exact select of K_blk among the candidates, ordered emission.
 // More than 2048 such groups (heavy ties) or more than 16384 groups take a streaming path
 // over all block maxima instead.
-__device__ __forceinline__ int select_pool(const SelectArgs &a, int b, int nb, SelectShared &sm) {
+// *thr receives the pool's threshold key (every pool block's maximum is >= it; 0 when the
+// pool holds every block).
+__device__ __forceinline__ int select_pool(const SelectArgs &a, int b, int nb, SelectShared &sm,
+                                           uint32_t *thr) {
     const int tid = threadIdx.x, K = a.K_blk;
+    *thr = 0u;
     if (nb <= K) {
         for (int j = tid; j < nb; j += kSelThreads) sm.pool[j] = j;
         __syncthreads();
@@ -858,8 +782,8 @@ __device__ __forceinline__ int select_pool(const SelectArgs &a, int b, int nb, S
                     }
                 }
             }
-            select_emit(c, [&](int i) { return gid[i / kItemBlocks] * kItemBlocks + i % kItemBlocks; },
-                        (uint32_t)K, sm.pool, (uint32_t)K, sm);
+            *thr = select_emit(c, [&](int i) { return gid[i / kItemBlocks] * kItemBlocks + i % kItemBlocks; },
+                               (uint32_t)K, sm.pool, (uint32_t)K, sm).thr;
         } else {
             fast = false;
         }
@@ -869,6 +793,7 @@ __device__ __forceinline__ int select_pool(const SelectArgs &a, int b, int nb, S
         uint32_t tie_base = 0, out_base = 0;
         GlobalBlocks src{bs, nb, lam};
         const SelResult r = range_select(src, (uint32_t)K, sm.sel);
+        *thr = r.thr;
         for (int c0 = 0; c0 < nb; c0 += kRegCap) {
             RegItems<kIPT> c;
             load_block_chunk(bs, nb, lam, c0, c);
@@ -881,17 +806,19 @@ __device__ __forceinline__ int select_pool(const SelectArgs &a, int b, int nb, S
 }
 
 // Top-k among the visible positions of the pool.  Thread t owns pool entries 2t and 2t+1.
-// The k-th largest block maximum among the pool entries bounds the k-th largest position
-// score from below (k distinct positions reach it), so only positions scoring >= that bound
-// in entries whose maximum reaches it are candidates.  Scores and block maxima come from the
-// Full scan (pscore / bscore, by block) or from the Reindex rescoring (poolsc / poolbmax, by
-// pool entry; -inf marks an invisible position).
+// Only positions scoring >= a lower bound of the k-th largest position score are
+// candidates.  Full: the pool threshold (each of the plen pool blocks has a position at
+// its maximum, which is >= the threshold), valid when k <= plen.  Reindex: the k-th largest
+// rescored block maximum among the pool entries (k distinct positions reach it); only
+// entries whose maximum reaches it are read.  Scores come from the Full scan (pscore, by
+// position) or from the Reindex rescoring (poolsc / poolbmax, by pool entry; -inf marks an
+// invisible position).
 template <bool REINDEX>
 __device__ __forceinline__ void select_topk(const SelectArgs &a, int b, int L, const int32_t *pool,
-                                            int plen, SelectShared &sm) {
+                                            int plen, uint32_t pool_thr, SelectShared &sm) {
     const int tid = threadIdx.x;
     int pj[2];
-    RegItems<2> bm;  // block maxima of the thread's entries
+    RegItems<2> bm;  // Reindex: block maxima of the thread's entries
     bm.valid = 0;
     uint32_t nvis = 0;
 #pragma unroll
@@ -900,28 +827,28 @@ __device__ __forceinline__ void select_topk(const SelectArgs &a, int b, int L, c
         pj[q] = e < plen ? pool[e] : -1;
         bm.key[q] = 0u;
         if (pj[q] >= 0 && pj[q] * kBlk < L) {
-            const float m = REINDEX ? a.poolbmax[(int64_t)b * a.K_blk + e]
-                                    : a.bscore[(int64_t)b * a.bstride + pj[q]];
-            bm.key[q] = order_key(m);
+            if (REINDEX) bm.key[q] = order_key(a.poolbmax[(int64_t)b * a.K_blk + e]);
             bm.valid |= 1u << q;
             nvis += (uint32_t)min(kBlk, L - pj[q] * kBlk);
         }
     }
-    const uint32_t n_vis = block_sum<kSelThreads>(nvis, sm.sel.scan);
-    const uint32_t need = min((uint32_t)a.k, n_vis);
+    uint32_t n_ent = __popc(bm.valid);
+    const uint32_t n_vis = block_sum<kSelThreads>((nvis << 16) | n_ent, sm.sel.scan);
+    n_ent = n_vis & 0xFFFFu;
+    const uint32_t need = min((uint32_t)a.k, n_vis >> 16);
     int32_t *out = a.topk + (int64_t)b * a.k;
     uint32_t lam = 0u;
-    if (need > 0 && need < n_vis) {
-        uint32_t n_ent = block_sum<kSelThreads>((uint32_t)__popc(bm.valid), sm.sel.scan);
-        if (n_ent > need) lam = range_select(bm, need, sm.sel).thr;
+    if (need > 0 && need < (n_vis >> 16) && need <= n_ent) {
+        if (REINDEX) lam = n_ent > need ? range_select(bm, need, sm.sel).thr : 0u;
+        else lam = pool_thr;
     }
-    // candidate positions: entries whose maximum reaches lam, positions scoring >= lam
+    // candidate positions scoring >= lam (Reindex: of entries whose maximum reaches lam)
     RegItems<kIPT> it;
     it.valid = 0;
 #pragma unroll
     for (int q = 0; q < 2; q++) {
         float sc[kBlk];
-        const bool live = (bm.valid & (1u << q)) && bm.key[q] >= lam;
+        const bool live = (bm.valid & (1u << q)) && (!REINDEX || bm.key[q] >= lam);
         if (live) {
             const float4 *src = REINDEX
                 ? reinterpret_cast<const float4 *>(a.poolsc + ((int64_t)b * a.K_blk + 2 * tid + q) * kBlk)
@@ -941,9 +868,15 @@ __device__ __forceinline__ void select_topk(const SelectArgs &a, int b, int L, c
             }
         }
     }
-    if (need > 0)
-        select_emit(it, [&](int i) { return pj[i / kBlk] * kBlk + i % kBlk; }, need, out,
-                    (uint32_t)a.k, sm);
+    if (need > 0) {
+        auto pos = [&](int i) { return pj[i / kBlk] * kBlk + i % kBlk; };
+        if (need == (n_vis >> 16) && lam == 0u) {
+            uint32_t ob = 0;
+            emit_all(it, pos, out, (uint32_t)a.k, ob, sm.sel);
+        } else {
+            select_emit(it, pos, need, out, (uint32_t)a.k, sm);
+        }
+    }
     for (int i = (int)need + tid; i < a.k; i += kSelThreads) out[i] = -1;
     if (tid == 0) a.topk_len[b] = (int32_t)need;
 }
@@ -955,17 +888,20 @@ __global__ __launch_bounds__(kSelThreads) void k_select(SelectArgs a) {
     const int b = blockIdx.x, tid = threadIdx.x;
     const int L = clamp_len(a.ctx_len[b], a.maxb);
     const int nb = (L + kBlk - 1) / kBlk;
+    for (int i = tid; i < kHistBins; i += kSelThreads) sm.sel.hist[i] = 0u;  // kept zero between passes
+    __syncthreads();
     if (REINDEX) {
         const int plen = max(0, min(a.pool_len[b], a.K_blk));
-        select_topk<true>(a, b, L, a.pool_blocks + (int64_t)b * a.K_blk, plen, sm);
+        select_topk<true>(a, b, L, a.pool_blocks + (int64_t)b * a.K_blk, plen, 0u, sm);
         return;
     }
-    const int plen = select_pool(a, b, nb, sm);
+    uint32_t thr;
+    const int plen = select_pool(a, b, nb, sm, &thr);
     const int np = min(plen, nb);
     int32_t *pool_out = a.pool_blocks + (int64_t)b * a.K_blk;
     for (int i = tid; i < a.K_blk; i += kSelThreads) pool_out[i] = i < np ? sm.pool[i] : -1;
     if (tid == 0) a.pool_len[b] = np;
-    select_topk<false>(a, b, L, sm.pool, np, sm);
+    select_topk<false>(a, b, L, sm.pool, np, thr, sm);
 }
 
 // ------------------------------------------------------------------ dispatch

@@ -52,7 +52,7 @@ class GpuState:
         maxb = table.shape[1]
         self.ws = torch.zeros(k.csa2_workspace_bytes(self.cfg, k.CSA2_OP_INDEX_FULL, wl.B, maxb),
                               dtype=torch.uint8, device="cuda")
-        self.ws_attn = torch.empty(
+        self.ws_attn = torch.zeros(
             k.csa2_workspace_bytes(self.cfg, k.CSA2_OP_SPARSE_ATTN, wl.B, maxb),
             dtype=torch.uint8, device="cuda")
         torch.cuda.synchronize()

@@ -224,3 +224,40 @@ def test_group_all_equal_keys_long():
     assert np.array_equal(_np(tg), to) and np.array_equal(_np(tlg), tlo)
     tg2, tlg2 = g.index_reindex(*qg, pg, plg)
     assert np.array_equal(_np(tg2), to)
+
+
+@pytest.mark.parametrize("ahead", [0, 3])
+def test_fused_window_append_matches_two_calls(ahead):
+    """csa2_sparse_attn_append == csa2_append_swa followed by csa2_sparse_attn: same ring
+    bytes, bit-identical outputs.  ahead = 0 appends position L-1 (attended from the fused
+    registers); ahead = 3 appends a position past the window (written, not attended)."""
+    import kv_cache_decode_csa2_amd as k
+    wl = si.small("fuse", 90 + ahead, [700, 5000, 64, 1], H_I=4, d_I=64, K_blk=16, k=40, W=32)
+    o, g = _pair(wl)
+    qg = g.layer_q(0)
+    _, _, tg, tlg = g.index_full(*qg)
+    C = 48
+    lay = k.csa2_layout(g.cfg)
+    ring = torch.zeros((wl.B, C, lay.swa_row_bytes), dtype=torch.uint8, device="cuda")
+    for b in range(wl.B):
+        L = wl.ctx[b]
+        n = min(L, wl.W)
+        rows = dev(si.layer_swa_rows(wl, 0, b, n))
+        k.csa2_append_swa(g.cfg, rows, dev(np.array([L - n], np.int32)), n, ring[b:b + 1], C)
+    new_rows = dev(si.normal(90, 555, (wl.B, wl.D)))
+    pos = dev(np.asarray(wl.ctx, np.int32) - 1 + ahead)
+    qa = g.attn_q(0)
+    ring_a, ring_b = ring.clone(), ring.clone()
+    k.csa2_append_swa(g.cfg, new_rows, pos, 1, ring_a, C)
+    out_a = torch.full((wl.B, wl.H_q, wl.D), float("nan"), device="cuda")
+    lse_a = torch.full((wl.B, wl.H_q), float("nan"), device="cuda")
+    k.csa2_sparse_attn(g.cfg, qa, g.kv, g.n_blocks, g.table, ring_a, C, g.ctx, tg, tlg, out_a,
+                       lse_a, g.ws_attn)
+    out_b = torch.full_like(out_a, float("nan"))
+    lse_b = torch.full_like(lse_a, float("nan"))
+    k.csa2_sparse_attn_append(g.cfg, new_rows, pos, qa, g.kv, g.n_blocks, g.table, ring_b, C,
+                              g.ctx, tg, tlg, out_b, lse_b, g.ws_attn)
+    torch.cuda.synchronize()
+    assert torch.equal(ring_a, ring_b)
+    assert np.array_equal(_np(out_a).view(np.uint32), _np(out_b).view(np.uint32))
+    assert np.array_equal(_np(lse_a).view(np.uint32), _np(lse_b).view(np.uint32))
