@@ -52,7 +52,12 @@ enum {
     CSA2_ERR_HIP = -4          /* a kernel launch failed */
 };
 
-enum { CSA2_OP_INDEX_FULL = 1, CSA2_OP_INDEX_REINDEX = 2, CSA2_OP_SPARSE_ATTN = 3 };
+enum {
+    CSA2_OP_INDEX_FULL = 1,
+    CSA2_OP_INDEX_REINDEX = 2,
+    CSA2_OP_SPARSE_ATTN = 3,
+    CSA2_OP_INDEX_PREFILL = 4 /* batch = number of prefill queries */
+};
 
 /* Shapes of one CSA2 layer. */
 typedef struct csa2_config {
@@ -182,6 +187,22 @@ int csa2_index_reindex(const csa2_config *cfg, const uint8_t *q_codes,
                        const int32_t *ctx_len, int32_t batch, const int32_t *pool_blocks,
                        const int32_t *pool_len, int32_t *topk, int32_t *topk_len, void *ws,
                        size_t ws_bytes, hipStream_t stream);
+
+/* Prefill indexer [KV]: n_q consecutive query tokens of ONE sequence, query i at position
+ * t_i = q_pos0 + i, each run the Full-mode steps of csa2_index_full on their own causal
+ * prefix (context length L_i = t_i + 1): score every position p <= t_i, block maxima, pool
+ * of the K_blk best blocks, top-k inside the pool.  Same score definition, order and
+ * output conventions as csa2_index_full, per query: pool_blocks [n_q][K_blk], pool_len
+ * [n_q], topk [n_q][k], topk_len [n_q].  q_codes [n_q][H_I*d_I/2], q_scales
+ * [n_q][H_I*d_I/32], w [n_q][H_I]; block_table is the sequence's row of maxb entries
+ * (device), q_pos0 and n_q are host values with q_pos0 + n_q <= 8*maxb.  The products run
+ * on the FP4 matrix cores; results are bit-identical to the per-query Full mode.
+ * Workspace: CSA2_OP_INDEX_PREFILL bytes for batch = n_q (about 32*maxb bytes per query). */
+int csa2_index_prefill(const csa2_config *cfg, const uint8_t *q_codes, const uint8_t *q_scales,
+                       const float *w, int32_t q_pos0, int32_t n_q, const uint8_t *idx_cache,
+                       int64_t n_blocks, const int32_t *block_table, int32_t maxb,
+                       int32_t *pool_blocks, int32_t *pool_len, int32_t *topk,
+                       int32_t *topk_len, void *ws, size_t ws_bytes, hipStream_t stream);
 
 /* Sparse attention [KV][3][W]: for each sequence b and head h, one softmax over
  *   the main-KV rows of positions topk[b][0 .. topk_len[b]) (entries -1 are padding), and

@@ -15,14 +15,15 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libcsa2.so")
 
 CSA2_OK, CSA2_ERR_INVALID, CSA2_ERR_UNSUPPORTED, CSA2_ERR_WORKSPACE, CSA2_ERR_HIP = 0, -1, -2, -3, -4
-CSA2_OP_INDEX_FULL, CSA2_OP_INDEX_REINDEX, CSA2_OP_SPARSE_ATTN = 1, 2, 3
+CSA2_OP_INDEX_FULL, CSA2_OP_INDEX_REINDEX, CSA2_OP_SPARSE_ATTN, CSA2_OP_INDEX_PREFILL = 1, 2, 3, 4
 CSA2_BLOCK = 8
 
 EXPORTS = [
     "csa2_layout", "csa2_workspace_bytes", "csa2_quantize_mxfp4", "csa2_quantize_mxfp8",
     "csa2_dequant_mxfp4", "csa2_dequant_mxfp8", "csa2_append_global", "csa2_append_swa",
     "csa2_index_scores", "csa2_index_full", "csa2_index_full_scan", "csa2_index_full_finish",
-    "csa2_index_reindex", "csa2_sparse_attn", "csa2_sparse_attn_append", "csa2_status_str",
+    "csa2_index_reindex", "csa2_index_prefill", "csa2_sparse_attn", "csa2_sparse_attn_append",
+    "csa2_status_str",
 ]
 
 
@@ -72,6 +73,8 @@ def load() -> C.CDLL:
             "csa2_index_full_finish": [cfgp, vp, vp, vp, vp, i64, vp, i32, vp, i32, vp, vp, vp,
                                        vp, vp, sz, vp],
             "csa2_index_reindex": [cfgp, vp, vp, vp, vp, i64, vp, i32, vp, i32, vp, vp, vp, vp,
+                                   vp, sz, vp],
+            "csa2_index_prefill": [cfgp, vp, vp, vp, i32, i32, vp, i64, vp, i32, vp, vp, vp, vp,
                                    vp, sz, vp],
             "csa2_sparse_attn": [cfgp, vp, vp, i64, vp, i32, vp, i32, vp, i32, vp, vp, vp, vp, vp,
                                  sz, vp],
@@ -203,6 +206,15 @@ def csa2_index_reindex(cfg, q_codes, q_scales, w, idx_cache, n_blocks, block_tab
     batch, maxb = block_table.shape
     _call("csa2_index_reindex", C.byref(cfg), _p(q_codes), _p(q_scales), _p(w), _p(idx_cache),
           int(n_blocks), _p(block_table), maxb, _p(ctx_len), batch, _p(pool_blocks),
+          _p(pool_len), _p(topk), _p(topk_len), _p(ws), ws.numel(), _stream(stream))
+
+
+def csa2_index_prefill(cfg, q_codes, q_scales, w, q_pos0, idx_cache, n_blocks, table_row,
+                       pool_blocks, pool_len, topk, topk_len, ws, stream=None):
+    n_q = q_codes.shape[0]
+    maxb = table_row.numel()
+    _call("csa2_index_prefill", C.byref(cfg), _p(q_codes), _p(q_scales), _p(w), int(q_pos0),
+          int(n_q), _p(idx_cache), int(n_blocks), _p(table_row), maxb, _p(pool_blocks),
           _p(pool_len), _p(topk), _p(topk_len), _p(ws), ws.numel(), _stream(stream))
 
 

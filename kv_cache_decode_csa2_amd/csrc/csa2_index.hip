@@ -34,6 +34,7 @@
 #include <algorithm>
 
 #include "csa2_common.h"
+#include "csa2_select.h"
 
 namespace csa2 {
 
@@ -622,24 +623,7 @@ __device__ __forceinline__ void emit_all(const RegItems<N> &it, IdF id, int32_t 
 
 // ------------------------------------------------------------------ k_select
 
-struct SelectArgs {
-    const int32_t *ctx_len;
-    int32_t maxb;
-    int32_t B;
-    int32_t K_blk;
-    int32_t k;
-    const float *pscore;  // Full: position scores [B][maxb*8]
-    const float *bscore;  // Full: block maxima [B][bstride]
-    int32_t bstride;
-    const float *gmax;    // Full: group maxima [B][ngmax]
-    int32_t ngmax;
-    const float *poolsc;    // Reindex: pool scores [B][K_blk*8]
-    const float *poolbmax;  // Reindex: pool block maxima [B][K_blk]
-    int32_t *pool_blocks;  // Full: out; Reindex: in
-    int32_t *pool_len;     // Full: out; Reindex: in
-    int32_t *topk;
-    int32_t *topk_len;
-};
+// SelectArgs: csa2_select.h
 
 struct SelectShared {
     SelShared sel;
@@ -886,7 +870,7 @@ __global__ __launch_bounds__(kSelThreads) void k_select(SelectArgs a) {
     extern __shared__ __align__(16) uint8_t sh_raw[];
     SelectShared &sm = *reinterpret_cast<SelectShared *>(sh_raw);
     const int b = blockIdx.x, tid = threadIdx.x;
-    const int L = clamp_len(a.ctx_len[b], a.maxb);
+    const int L = clamp_len(a.ctx_len ? a.ctx_len[b] : a.q_pos0 + b + 1, a.maxb);
     const int nb = (L + kBlk - 1) / kBlk;
     for (int i = tid; i < kHistBins; i += kSelThreads) sm.sel.hist[i] = 0u;  // kept zero between passes
     __syncthreads();
@@ -939,13 +923,7 @@ bool pick(int H, int dI, KernSet *ks) {
     return false;
 }
 
-}  // namespace csa2
-
-using namespace csa2;
-
-namespace {
-
-int check_cfg(const csa2_config *c) {
+int check_index_cfg(const csa2_config *c) {
     if (!c) return CSA2_ERR_INVALID;
     if (c->n_idx_heads <= 0 || c->idx_dim <= 0 || c->idx_dim % 32 || c->kv_dim <= 0 ||
         c->kv_dim % 32 || c->n_q_heads <= 0 || c->swa_window < 0 || c->pool_blocks <= 0 ||
@@ -957,10 +935,27 @@ int check_cfg(const csa2_config *c) {
     return CSA2_OK;
 }
 
-int launched() { return hipGetLastError() == hipSuccess ? CSA2_OK : CSA2_ERR_HIP; }
-
 // Row stride of the group maxima (rounded to 4 floats for 16-byte loads).
 int ngmax_of(int maxb) { return (((maxb + kItemBlocks - 1) / kItemBlocks) + 3) & ~3; }
+
+constexpr size_t kSelectShared = sizeof(SelectShared);
+
+int launch_select(const SelectArgs &a, bool reindex, hipStream_t stream) {
+    if (a.B <= 0) return CSA2_OK;
+    if (reindex) k_select<true><<<a.B, kSelThreads, kSelectShared, stream>>>(a);
+    else k_select<false><<<a.B, kSelThreads, kSelectShared, stream>>>(a);
+    return hipGetLastError() == hipSuccess ? CSA2_OK : CSA2_ERR_HIP;
+}
+
+}  // namespace csa2
+
+using namespace csa2;
+
+namespace {
+
+int check_cfg(const csa2_config *c) { return check_index_cfg(c); }
+
+int launched() { return hipGetLastError() == hipSuccess ? CSA2_OK : CSA2_ERR_HIP; }
 
 ScanArgs scan_args(const csa2_config *c, const uint8_t *qc, const uint8_t *qs, const float *w,
                    const uint8_t *idx, int64_t n_blocks, const int32_t *table, int32_t maxb,
@@ -987,8 +982,6 @@ int scan_grid(int64_t items) {
 }
 
 size_t prefix_bytes(int B) { return sizeof(int32_t) * (2 * (size_t)B + 1); }
-
-constexpr size_t kSelectShared = sizeof(SelectShared);
 
 }  // namespace
 
@@ -1029,6 +1022,12 @@ extern "C" int csa2_workspace_bytes(const csa2_config *c, int op, int32_t batch,
         const int st = check_cfg(c);
         if (st) return st;
         *bytes = ws_idx(batch, maxb, c->pool_blocks).total;
+        return CSA2_OK;
+    }
+    if (op == CSA2_OP_INDEX_PREFILL) {
+        const int st = check_cfg(c);
+        if (st) return st;
+        *bytes = prefill_ws_bytes(c, batch, maxb);
         return CSA2_OK;
     }
     if (op == CSA2_OP_SPARSE_ATTN) {
@@ -1144,8 +1143,7 @@ extern "C" int csa2_index_full_finish(const csa2_config *c, const uint8_t *q_cod
     s.pool_len = pool_len;
     s.topk = topk;
     s.topk_len = topk_len;
-    k_select<false><<<batch, kSelThreads, kSelectShared, stream>>>(s);
-    return launched();
+    return launch_select(s, false, stream);
 }
 
 extern "C" int csa2_index_full(const csa2_config *c, const uint8_t *q_codes,
@@ -1192,6 +1190,5 @@ extern "C" int csa2_index_reindex(const csa2_config *c, const uint8_t *q_codes,
     s.pool_len = const_cast<int32_t *>(pool_len);
     s.topk = topk;
     s.topk_len = topk_len;
-    k_select<true><<<batch, kSelThreads, kSelectShared, stream>>>(s);
-    return launched();
+    return launch_select(s, true, stream);
 }

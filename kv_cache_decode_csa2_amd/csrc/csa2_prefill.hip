@@ -1,0 +1,466 @@
+// csa2_prefill.hip -- the indexer of a prefill chunk: n_q consecutive query tokens of one
+// sequence, query i at position t_i = q_pos0 + i, each scoring the positions p <= t_i and
+// selecting its own pool and top-k exactly as a Full-mode decode step on that prefix
+// (dbyun.net/article/10794, "KV Cache 成为这一代架构改造的核心": the Full layer's scan, pool
+// of 2048 blocks of 8 and top-512; the per-layer kernel counts quoted there cover prefill).
+//
+// With many queries against the same keys the score is a dense contraction, so the products
+// run on the gfx950 scaled FP4 matrix cores (v_mfma_scale_f32_16x16x128_f8f6f4): per head
+// one 16 positions x 16 queries tile consumes the head's 128 (4 groups of 32) FP4 elements,
+// each lane carrying one 32-group and its E8M0 scale.  The library's score definition is a
+// fixed-order fp32 sum of exact per-group terms t_g = N_g * 2^(E_g - 2); the matrix core
+// instead adds the scaled group dot products in an undisclosed order.  Both give the exact
+// sum D_h whenever every partial sum is representable: with |N_g| <= 4608 < 2^13, the four
+// terms are multiples of 2^(min E - 2) below 2^(max E - 2 + 15), so an exponent span
+// max_g E_g - min_g E_g <= 9 keeps every partial inside 24 bits.  Tiles whose key and query
+// scale spans could exceed that take an exact path instead: one matrix instruction per
+// group (the other groups' operands zeroed) and the fp32 group sum in the defined order.
+// The epilogue (ReLU, fma chain over heads in head order, causal mask, block and group
+// maxima) runs on the vector ALUs and writes what the Full-mode selection reads.
+//
+// Kernels:
+//   k_prefill_span  per logical block: the largest exponent span of any key head vector.
+//   k_prefill<H,G>  a workgroup = 128 queries x 2048 positions; keys staged through LDS in
+//                   stages of 8 blocks (double-buffered), queries and head weights held in
+//                   registers, 4 waves x 2 query tiles of 16.
+//   k_select        (shared with Full mode) one workgroup per query.
+#include <algorithm>
+
+#include "csa2_common.h"
+#include "csa2_select.h"
+
+namespace csa2 {
+namespace {
+
+typedef int v8i_t __attribute__((ext_vector_type(8)));
+
+constexpr int kPfThreads = 256;
+constexpr int kPfWaves = kPfThreads / kWave;
+constexpr int kPfNQ = 2;                          // 16-query tiles per wave
+constexpr int kPfQT = kPfWaves * kPfNQ * 16;      // queries per workgroup
+constexpr int kPfStageBlocks = 8;                 // blocks per LDS stage (one group maximum)
+constexpr int kPfChunkStages = 32;                // stages per workgroup (2048 positions)
+constexpr int kPfChunkBlocks = kPfChunkStages * kPfStageBlocks;
+constexpr int kSpanExact = 9;                     // largest exact exponent span
+constexpr int kBlockPad = 128;                    // LDS bytes between staged blocks
+
+struct PrefillArgs {
+    const uint8_t *q_codes;   // [n_q][H*G*16]
+    const uint8_t *q_scales;  // [n_q][H*G]
+    const float *w;           // [n_q][H]
+    int32_t q_pos0, n_q;
+    const uint8_t *idx_cache;
+    int64_t n_blocks;
+    const int32_t *table;  // one row of maxb entries
+    int32_t maxb;
+    int32_t nb;            // logical blocks touched: ceil((q_pos0 + n_q) / 8)
+    uint8_t *kspan;        // [round8(nb)]
+    float *pscore;         // [n_q][maxb*8]
+    float *bscore;         // [n_q][bstride]
+    float *gmax;           // [n_q][ngmax]
+    int32_t bstride, ngmax;
+    int32_t n_qt, n_pc;    // query tiles, position chunks
+};
+
+__device__ __forceinline__ int64_t phys_block(const PrefillArgs &a, int j) {
+    if (j >= a.nb) return -1;
+    const int32_t ph = a.table[j];
+    return (ph >= 0 && ph < a.n_blocks) ? ph : -1;
+}
+
+// kspan[j] = max over the 8 positions and H heads of block j of
+// (largest - smallest E8M0 code among the head's G groups); 0 for absent blocks.
+template <int H, int G>
+__global__ __launch_bounds__(256) void k_prefill_span(PrefillArgs a) {
+    constexpr int CODES = kBlk * H * 16 * G;
+    constexpr int BYTES = CODES + kBlk * H * G;
+    const int gid = blockIdx.x * 256 + threadIdx.x;  // (block, slot)
+    const int j = gid / kBlk, s = gid % kBlk;
+    const int nbr = (a.nb + kBlk - 1) / kBlk * kBlk;
+    int span = 0;
+    const int64_t ph = j < a.nb ? phys_block(a, j) : -1;
+    if (ph >= 0) {
+        const uint8_t *sc = a.idx_cache + ph * BYTES + CODES + s * H * G;
+#pragma unroll
+        for (int h = 0; h < H; h++) {
+            int lo = 255, hi = 0;
+#pragma unroll
+            for (int g = 0; g < G; g++) {
+                const int e = sc[h * G + g];
+                lo = min(lo, e);
+                hi = max(hi, e);
+            }
+            span = max(span, hi - lo);
+        }
+    }
+    span = max(span, __shfl_xor(span, 1, kWave));
+    span = max(span, __shfl_xor(span, 2, kWave));
+    span = max(span, __shfl_xor(span, 4, kWave));
+    if (s == 0 && j < nbr) a.kspan[j] = (uint8_t)span;
+}
+
+// One key stage in LDS: the code bytes of 8 blocks (rows of H 16-byte chunks, chunk h of
+// row R stored at position h ^ (R mod H), blocks kBlockPad apart) and their scale bytes.
+template <int H, int G>
+struct PfStage {
+    static constexpr int CODES = kBlk * H * 16 * G;
+    static constexpr int SCB = kBlk * H * G;
+    static constexpr int BSTR = CODES + kBlockPad;
+    __align__(16) uint8_t codes[kPfStageBlocks * BSTR];
+    __align__(16) uint32_t scales[kPfStageBlocks * SCB / 4];
+};
+
+// Per-thread prefetch of one stage from global memory.
+template <int H, int G>
+struct PfFetch {
+    static constexpr int CH = kPfStageBlocks * PfStage<H, G>::CODES / 16;  // 16-B chunks
+    static constexpr int NC = (CH + kPfThreads - 1) / kPfThreads;
+    static constexpr int SD = kPfStageBlocks * PfStage<H, G>::SCB / 4;    // scale dwords
+    static constexpr int NS = (SD + kPfThreads - 1) / kPfThreads;
+    uint4 c[NC];
+    uint32_t s[NS];
+};
+
+template <int H, int G>
+__device__ __forceinline__ void pf_fetch(const PrefillArgs &a, int J0, PfFetch<H, G> &f) {
+    using S = PfStage<H, G>;
+    using F = PfFetch<H, G>;
+    constexpr int BYTES = S::CODES + S::SCB;
+    constexpr int CPB = S::CODES / 16;  // chunks per block
+    constexpr int DPB = S::SCB / 4;     // scale dwords per block
+#pragma unroll
+    for (int i = 0; i < F::NC; i++) {
+        const int c = (int)threadIdx.x + i * kPfThreads;
+        f.c[i] = make_uint4(0u, 0u, 0u, 0u);
+        if (F::CH % kPfThreads == 0 || c < F::CH) {
+            const int64_t ph = phys_block(a, J0 + c / CPB);
+            const uint8_t *src = a.idx_cache + (ph >= 0 ? ph : 0) * BYTES + (c % CPB) * 16;
+            f.c[i] = *reinterpret_cast<const uint4 *>(src);
+        }
+    }
+#pragma unroll
+    for (int i = 0; i < F::NS; i++) {
+        const int d = (int)threadIdx.x + i * kPfThreads;
+        f.s[i] = 0u;
+        if (F::SD % kPfThreads == 0 || d < F::SD) {
+            const int64_t ph = phys_block(a, J0 + d / DPB);
+            const uint8_t *src = a.idx_cache + (ph >= 0 ? ph : 0) * BYTES + S::CODES + (d % DPB) * 4;
+            f.s[i] = *reinterpret_cast<const uint32_t *>(src);
+        }
+    }
+}
+
+template <int H, int G>
+__device__ __forceinline__ void pf_store(const PfFetch<H, G> &f, PfStage<H, G> &st) {
+    using S = PfStage<H, G>;
+    using F = PfFetch<H, G>;
+    constexpr int CPB = S::CODES / 16;
+#pragma unroll
+    for (int i = 0; i < F::NC; i++) {
+        const int c = (int)threadIdx.x + i * kPfThreads;
+        if (F::CH % kPfThreads == 0 || c < F::CH) {
+            const int blk = c / CPB, r = c % CPB;
+            const int row = r / H, h = r % H;
+            *reinterpret_cast<uint4 *>(st.codes + blk * S::BSTR + (row * H + (h ^ (row & (H - 1)))) * 16) = f.c[i];
+        }
+    }
+#pragma unroll
+    for (int i = 0; i < F::NS; i++) {
+        const int d = (int)threadIdx.x + i * kPfThreads;
+        if (F::SD % kPfThreads == 0 || d < F::SD) st.scales[d] = f.s[i];
+    }
+}
+
+__device__ __forceinline__ f32x4_t mfma_fp4(const uint4 &a, const uint4 &b, uint32_t sa, uint32_t sb) {
+    const v8i_t av = {(int)a.x, (int)a.y, (int)a.z, (int)a.w, 0, 0, 0, 0};
+    const v8i_t bv = {(int)b.x, (int)b.y, (int)b.z, (int)b.w, 0, 0, 0, 0};
+    const f32x4_t z = {0.f, 0.f, 0.f, 0.f};
+    // formats 4/4: both operands FP4 E2M1; scale byte 0 of sa / sb
+    return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(av, bv, z, 4, 4, 0, (int)sa, 0, (int)sb);
+}
+
+__device__ __forceinline__ float relu0(float x) { return x > 0.0f ? x : 0.0f; }
+
+// Query tile held by a lane: column q (16 queries), group g = lane / 16 of every head.
+template <int H>
+struct PfQuery {
+    uint4 c[H];     // FP4 codes of group g of head h
+    uint32_t s[H];  // E8M0 code of group g of head h
+    float w[H];
+};
+
+template <int H, int G>
+__global__ __launch_bounds__(kPfThreads, 2) void k_prefill(PrefillArgs a) {
+    using S = PfStage<H, G>;
+    __shared__ S st[2];
+
+    // workgroup -> (position chunk, query tile); the workgroups of one chunk are consecutive
+    // on one XCD (dispatch places workgroup i on XCD i % 8) so its keys are fetched once
+    const int T = a.n_qt * a.n_pc;
+    const int bid = (int)blockIdx.x, x = bid % 8, i8 = bid / 8, per = T / 8, rem = T % 8;
+    const int lin = x < rem ? x * (per + 1) + i8 : rem * (per + 1) + (x - rem) * per + i8;
+    const int pc = lin / a.n_qt, qt = lin % a.n_qt;
+    const int Q0 = qt * kPfQT;
+    const int qlast = min(a.n_q, Q0 + kPfQT) - 1;
+    const int Jbeg = pc * kPfChunkBlocks;
+    // blocks this tile can see: j*8 <= q_pos0 + qlast
+    const int Jend = min(min(a.nb, Jbeg + kPfChunkBlocks), (a.q_pos0 + qlast) / kBlk + 1);
+    if (Jbeg >= Jend) return;  // uniform per workgroup
+    const int nstage = (Jend - Jbeg + kPfStageBlocks - 1) / kPfStageBlocks;
+
+    const int lane = lane_id(), wave = (int)threadIdx.x / kWave;
+    const int col = lane & 15, g = lane >> 4;
+    const bool gl = g < G;  // lanes of groups >= G carry zeros (d_I < 128)
+
+    // queries of this wave's tiles, their scale spans and causal limits
+    PfQuery<H> Q[kPfNQ];
+    int qspan[kPfNQ], qb[kPfNQ];
+#pragma unroll
+    for (int jq = 0; jq < kPfNQ; jq++) {
+        qb[jq] = Q0 + (wave * kPfNQ + jq) * 16;
+        const int q = min(qb[jq] + col, a.n_q - 1);
+        const uint8_t *qc = a.q_codes + (int64_t)q * H * G * 16;
+        const uint8_t *qs = a.q_scales + (int64_t)q * H * G;
+        int span = 0;
+#pragma unroll
+        for (int h = 0; h < H; h++) {
+            Q[jq].c[h] = gl ? *reinterpret_cast<const uint4 *>(qc + (h * G + (gl ? g : 0)) * 16)
+                            : make_uint4(0u, 0u, 0u, 0u);
+            Q[jq].s[h] = gl ? qs[h * G + g] : 127u;
+            Q[jq].w[h] = a.w[(int64_t)q * H + h];
+            int lo = 255, hi = 0;
+#pragma unroll
+            for (int gg = 0; gg < G; gg++) {
+                lo = min(lo, (int)qs[h * G + gg]);
+                hi = max(hi, (int)qs[h * G + gg]);
+            }
+            span = max(span, hi - lo);
+        }
+        // wave maximum (queries past n_q repeat query n_q - 1)
+#pragma unroll
+        for (int o = 1; o < kWave; o <<= 1) span = max(span, __shfl_xor(span, o, kWave));
+        qspan[jq] = __builtin_amdgcn_readfirstlane(span);
+    }
+
+    float gm[kPfNQ];
+    PfFetch<H, G> f;
+    pf_fetch<H, G>(a, Jbeg, f);
+    pf_store<H, G>(f, st[0]);
+    __syncthreads();
+
+    for (int sidx = 0; sidx < nstage; sidx++) {
+        const int J0 = Jbeg + sidx * kPfStageBlocks;
+        if (sidx + 1 < nstage) pf_fetch<H, G>(a, J0 + kPfStageBlocks, f);
+        const S &cur = st[sidx & 1];
+        // stage metadata (uniform): present-block bits and key spans
+        uint32_t present = 0;
+#pragma unroll
+        for (int b = 0; b < kPfStageBlocks; b++)
+            if (phys_block(a, J0 + b) >= 0) present |= 1u << b;
+        const uint2 ks8 = *reinterpret_cast<const uint2 *>(a.kspan + J0);
+#pragma unroll
+        for (int jq = 0; jq < kPfNQ; jq++) gm[jq] = -INFINITY;
+
+#pragma unroll
+        for (int u = 0; u < kPfStageBlocks / 2; u++) {  // 16-position tiles
+            const int p0 = (J0 + 2 * u) * kBlk;
+            // this lane's key row: position p0 + col, group g
+            const int bi = 2 * u + (col >> 3), s = col & 7;
+            const int row = g * kBlk + s;
+            uint4 kc[H];
+            uint32_t ksc[H];
+            {
+                const uint8_t *cb = cur.codes + bi * S::BSTR;
+#pragma unroll
+                for (int h = 0; h < H; h++)
+                    kc[h] = gl ? *reinterpret_cast<const uint4 *>(cb + (row * H + (h ^ (row & (H - 1)))) * 16)
+                               : make_uint4(0u, 0u, 0u, 0u);
+                if constexpr (H * G >= 4) {
+                    // the position's H*G scale bytes start on a dword; byte h*G + g of
+                    // them is byte ((h*G) & 3) + g of dword (h*G) / 4
+                    const uint32_t *sd = cur.scales + (bi * S::SCB + s * H * G) / 4;
+#pragma unroll
+                    for (int h = 0; h < H; h++) {
+                        const uint32_t dw = sd[(h * G) / 4];
+                        ksc[h] = gl ? (dw >> (8 * (((h * G) & 3) + g))) : 127u;
+                    }
+                } else {
+                    const int boff = bi * S::SCB + s * H * G + (gl ? g : 0);
+#pragma unroll
+                    for (int h = 0; h < H; h++) {
+                        const int o = boff + h * G;
+                        ksc[h] = gl ? (cur.scales[o >> 2] >> (8 * (o & 3))) : 127u;
+                    }
+                }
+            }
+            // largest key span of the tile's two blocks (bytes 2u, 2u + 1)
+            const uint32_t ksp_w = u < 2 ? ks8.x : ks8.y;
+            const uint32_t kspan_t = max((ksp_w >> (16 * (u & 1))) & 0xffu, (ksp_w >> (16 * (u & 1) + 8)) & 0xffu);
+            const bool pres0 = (present >> (2 * u)) & 1u, pres1 = (present >> (2 * u + 1)) & 1u;
+#pragma unroll
+            for (int jq = 0; jq < kPfNQ; jq++) {
+                if (qb[jq] >= a.n_q) continue;                       // no queries (uniform)
+                const int tmin = a.q_pos0 + qb[jq];
+                const int tmax = a.q_pos0 + min(qb[jq] + 15, a.n_q - 1);
+                if (p0 > tmax) continue;                             // all masked (uniform)
+                f32x4_t sc = {0.f, 0.f, 0.f, 0.f};
+                if ((int)kspan_t + qspan[jq] <= kSpanExact) {
+#pragma unroll
+                    for (int h = 0; h < H; h++) {
+                        const f32x4_t d = mfma_fp4(kc[h], Q[jq].c[h], ksc[h], Q[jq].s[h]);
+#pragma unroll
+                        for (int e = 0; e < 4; e++) sc[e] = __builtin_fmaf(Q[jq].w[h], relu0(d[e]), sc[e]);
+                    }
+                } else {
+#pragma unroll
+                    for (int h = 0; h < H; h++) {
+                        f32x4_t d = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                        for (int g2 = 0; g2 < G; g2++) {
+                            const uint4 kz = g == g2 ? kc[h] : make_uint4(0u, 0u, 0u, 0u);
+                            const f32x4_t t = mfma_fp4(kz, Q[jq].c[h], ksc[h], Q[jq].s[h]);
+#pragma unroll
+                            for (int e = 0; e < 4; e++) d[e] = d[e] + t[e];
+                        }
+#pragma unroll
+                        for (int e = 0; e < 4; e++) sc[e] = __builtin_fmaf(Q[jq].w[h], relu0(d[e]), sc[e]);
+                    }
+                }
+                // lane: query qb + col, positions p0 + 4*g + e
+                const int q = qb[jq] + col;
+                const int t = a.q_pos0 + q;
+                const int pl = p0 + 4 * g;
+                const bool pres = g < 2 ? pres0 : pres1;
+                if (p0 + 15 > tmin || !pres0 || !pres1) {
+#pragma unroll
+                    for (int e = 0; e < 4; e++)
+                        if (!pres || pl + e > t) sc[e] = -INFINITY;
+                }
+                float m = fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3]));
+                m = fmaxf(m, __shfl_xor(m, 16, kWave));
+                gm[jq] = fmaxf(gm[jq], m);
+                // blocks past nb (the tile's second block when nb is odd) are not stored:
+                // the position-score row ends at block maxb - 1 >= nb - 1
+                const int jb = J0 + 2 * u + (g >> 1);
+                if (q < a.n_q && jb < a.nb) {
+                    *reinterpret_cast<f32x4_t *>(a.pscore + (int64_t)q * a.maxb * kBlk + pl) = sc;
+                    if ((g & 1) == 0) a.bscore[(int64_t)q * a.bstride + jb] = m;
+                }
+            }
+        }
+#pragma unroll
+        for (int jq = 0; jq < kPfNQ; jq++) {
+            const float v = fmaxf(gm[jq], __shfl_xor(gm[jq], 32, kWave));
+            const int q = qb[jq] + col;
+            if (g == 0 && q < a.n_q && J0 * kBlk <= a.q_pos0 + q)
+                a.gmax[(int64_t)q * a.ngmax + J0 / kPfStageBlocks] = v;
+        }
+        if (sidx + 1 < nstage) pf_store<H, G>(f, st[(sidx + 1) & 1]);
+        __syncthreads();
+    }
+}
+
+typedef void (*PfFn)(const PrefillArgs &, hipStream_t);
+
+template <int H, int G>
+void launch_prefill(const PrefillArgs &a, hipStream_t s) {
+    const int spans = (a.nb * kBlk + 255) / 256;
+    k_prefill_span<H, G><<<spans, 256, 0, s>>>(a);
+    k_prefill<H, G><<<a.n_qt * a.n_pc, kPfThreads, 0, s>>>(a);
+}
+
+bool pick_prefill(int H, int dI, PfFn *fn) {
+    const int G = dI / 32;
+#define CSA2_PF_CASE(h, g) \
+    if (H == h && G == g) { *fn = launch_prefill<h, g>; return true; }
+    CSA2_PF_CASE(1, 1) CSA2_PF_CASE(1, 2) CSA2_PF_CASE(1, 4)
+    CSA2_PF_CASE(2, 1) CSA2_PF_CASE(2, 2) CSA2_PF_CASE(2, 4)
+    CSA2_PF_CASE(4, 1) CSA2_PF_CASE(4, 2) CSA2_PF_CASE(4, 4)
+    CSA2_PF_CASE(8, 1) CSA2_PF_CASE(8, 2) CSA2_PF_CASE(8, 4)
+#undef CSA2_PF_CASE
+    return false;
+}
+
+struct WsPrefill {
+    size_t pscore, bscore, gmax, kspan, total;
+};
+WsPrefill ws_prefill(int n_q, int maxb) {
+    WsPrefill w;
+    const int ng = ngmax_of(maxb);
+    size_t o = 0;
+    w.pscore = o; o = align256(o + sizeof(float) * (size_t)n_q * maxb * kBlk);
+    w.bscore = o; o = align256(o + sizeof(float) * (size_t)n_q * ng * kPfStageBlocks);
+    w.gmax = o;   o = align256(o + sizeof(float) * (size_t)n_q * ng);
+    w.kspan = o;  o = align256(o + (size_t)ng * kPfStageBlocks);
+    w.total = o;
+    return w;
+}
+
+}  // namespace
+
+size_t prefill_ws_bytes(const csa2_config *, int32_t n_q, int32_t maxb) {
+    return ws_prefill(std::max(n_q, 0), maxb).total;
+}
+
+}  // namespace csa2
+
+using namespace csa2;
+
+extern "C" int csa2_index_prefill(const csa2_config *c, const uint8_t *q_codes,
+                                  const uint8_t *q_scales, const float *w, int32_t q_pos0,
+                                  int32_t n_q, const uint8_t *idx_cache, int64_t n_blocks,
+                                  const int32_t *block_table, int32_t maxb, int32_t *pool_blocks,
+                                  int32_t *pool_len, int32_t *topk, int32_t *topk_len, void *ws,
+                                  size_t ws_bytes, hipStream_t stream) {
+    const int st = check_index_cfg(c);
+    if (st) return st;
+    if (!q_codes || !q_scales || !w || !idx_cache || n_blocks <= 0 || !block_table ||
+        maxb <= 0 || q_pos0 < 0 || n_q < 0 || !pool_blocks || !pool_len || !topk ||
+        !topk_len || !ws)
+        return CSA2_ERR_INVALID;
+    if ((int64_t)q_pos0 + n_q > (int64_t)maxb * kBlk) return CSA2_ERR_INVALID;
+    const WsPrefill L = ws_prefill(n_q, maxb);
+    if (ws_bytes < L.total) return CSA2_ERR_WORKSPACE;
+    if (n_q == 0) return CSA2_OK;
+    PfFn fn;
+    if (!pick_prefill(c->n_idx_heads, c->idx_dim, &fn)) return CSA2_ERR_UNSUPPORTED;
+    uint8_t *base = (uint8_t *)ws;
+    PrefillArgs a{};
+    a.q_codes = q_codes;
+    a.q_scales = q_scales;
+    a.w = w;
+    a.q_pos0 = q_pos0;
+    a.n_q = n_q;
+    a.idx_cache = idx_cache;
+    a.n_blocks = n_blocks;
+    a.table = block_table;
+    a.maxb = maxb;
+    a.nb = (int32_t)(((int64_t)q_pos0 + n_q + kBlk - 1) / kBlk);
+    a.kspan = base + L.kspan;
+    a.pscore = (float *)(base + L.pscore);
+    a.bscore = (float *)(base + L.bscore);
+    a.gmax = (float *)(base + L.gmax);
+    a.ngmax = ngmax_of(maxb);
+    a.bstride = a.ngmax * kPfStageBlocks;
+    a.n_qt = (n_q + kPfQT - 1) / kPfQT;
+    a.n_pc = (a.nb + kPfChunkBlocks - 1) / kPfChunkBlocks;
+    fn(a, stream);
+    if (hipGetLastError() != hipSuccess) return CSA2_ERR_HIP;
+    SelectArgs s{};
+    s.ctx_len = nullptr;
+    s.q_pos0 = q_pos0;
+    s.maxb = maxb;
+    s.B = n_q;
+    s.K_blk = c->pool_blocks;
+    s.k = c->topk;
+    s.pscore = a.pscore;
+    s.bscore = a.bscore;
+    s.bstride = a.bstride;
+    s.gmax = a.gmax;
+    s.ngmax = a.ngmax;
+    s.pool_blocks = pool_blocks;
+    s.pool_len = pool_len;
+    s.topk = topk;
+    s.topk_len = topk_len;
+    return launch_select(s, false, stream);
+}

@@ -213,3 +213,21 @@ def layer_swa_rows(wl: Workload, layer: int, b: int, n: int) -> np.ndarray:
     """fp32 sliding-window rows of a layer for the last n positions of sequence b, [n, D]."""
     base = T_LAYER + 16 * layer
     return normal(wl.seed, base + 3 + 1000 * b, (n, wl.D))
+
+
+# ----------------------------------------------------------------------------- prefill
+
+def prefill_idx_q(wl: Workload, layer: int, n_q: int) -> np.ndarray:
+    """fp32 indexer queries of the n_q prefill tokens of a layer, [n_q, H_I, d_I], N(0, 1)."""
+    return normal(wl.seed, T_LAYER + 16 * layer + 4, (n_q, wl.H_I, wl.d_I))
+
+
+def prefill_idx_w(wl: Workload, layer: int, n_q: int) -> np.ndarray:
+    """fp32 indexer head weights of the n_q prefill tokens of a layer, [n_q, H_I],
+    U(0.5, 1.5)."""
+    return uniform(wl.seed, T_LAYER + 16 * layer + 5, (n_q, wl.H_I), 0.5, 1.5)
+
+
+def prefill_attn_q(wl: Workload, layer: int, n_q: int) -> np.ndarray:
+    """bf16 bits of the attention queries of the n_q prefill tokens, [n_q, H_q, D]."""
+    return to_bf16_bits(normal(wl.seed, T_LAYER + 16 * layer + 6, (n_q, wl.H_q, wl.D)))

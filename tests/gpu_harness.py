@@ -134,3 +134,33 @@ def attn_close(out, lse, ref_out, ref_lse, tol=2e-3):
                         np.abs(lse - ref_lse) / np.maximum(1.0, np.abs(ref_lse)))
     ok = bool(np.all(rel <= tol) and np.all(lerr <= tol) and np.all(out[empty] == 0))
     return ok, float(rel.max(initial=0.0)), float(np.nanmax(lerr, initial=0.0))
+
+
+def prefill_q(wl: si.Workload, layer: int, n_q: int, scale_fn=None):
+    """Prefill indexer queries on the GPU: (q_codes, q_scales, w).  scale_fn, if given,
+    edits the fp32 queries first (numpy, in place)."""
+    q = si.prefill_idx_q(wl, layer, n_q)
+    if scale_fn is not None:
+        scale_fn(q)
+    q = dev(q.reshape(n_q, wl.H_I * wl.d_I))
+    qc = torch.empty((n_q, wl.H_I * wl.d_I // 2), dtype=torch.uint8, device="cuda")
+    qs = torch.empty((n_q, wl.H_I * wl.d_I // 32), dtype=torch.uint8, device="cuda")
+    k.csa2_quantize_mxfp4(q, qc, qs)
+    return qc, qs, dev(si.prefill_idx_w(wl, layer, n_q))
+
+
+def index_prefill(g: GpuState, qc, qs, w, q_pos0: int, ws=None):
+    """csa2_index_prefill over sequence 0 of g: (pool, pool_len, topk, topk_len)."""
+    wl = g.wl
+    n_q = qc.shape[0]
+    maxb = g.table.shape[1]
+    if ws is None:
+        ws = torch.empty(k.csa2_workspace_bytes(g.cfg, k.CSA2_OP_INDEX_PREFILL, n_q, maxb),
+                         dtype=torch.uint8, device="cuda")
+    pool = torch.full((n_q, wl.K_blk), -7, dtype=torch.int32, device="cuda")
+    pl = torch.zeros(n_q, dtype=torch.int32, device="cuda")
+    topk = torch.full((n_q, wl.k), -7, dtype=torch.int32, device="cuda")
+    tl = torch.zeros(n_q, dtype=torch.int32, device="cuda")
+    k.csa2_index_prefill(g.cfg, qc, qs, w, q_pos0, g.idx, g.n_blocks, g.table[0].contiguous(),
+                         pool, pl, topk, tl, ws)
+    return pool, pl, topk, tl
