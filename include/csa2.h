@@ -230,6 +230,21 @@ int csa2_sparse_attn_append(const csa2_config *cfg, const float *swa_rows, const
                             const int32_t *topk, const int32_t *topk_len, float *out,
                             float *lse, void *ws, size_t ws_bytes, hipStream_t stream);
 
+/* Prefill attention [KV][3][W]: n_q consecutive query tokens of ONE sequence, query i at
+ * position t_i = q_pos0 + i, each attend as csa2_sparse_attn does for a sequence of length
+ * t_i + 1: the main-KV rows of topk[i][0 .. topk_len[i]) and the window rows
+ * max(0, t_i + 1 - W) .. t_i.  block_table is the sequence's row of maxb entries;
+ * swa_ring is the sequence's ring of C slots (position p in slot p % C), which must still
+ * hold every attended window row, i.e. C >= n_q + W - 1 once the chunk's rows are in it.
+ * q [n_q][H_q][D] bf16 bits; out [n_q][H_q][D], lse [n_q][H_q].  q_pos0, n_q are host values
+ * with q_pos0 + n_q <= 8*maxb.  Workspace: CSA2_OP_SPARSE_ATTN bytes for batch = n_q. */
+int csa2_sparse_attn_prefill(const csa2_config *cfg, const uint16_t *q,
+                             const uint8_t *kv_cache, int64_t n_blocks,
+                             const int32_t *block_table, int32_t maxb, const uint8_t *swa_ring,
+                             int32_t C, int32_t q_pos0, int32_t n_q, const int32_t *topk,
+                             const int32_t *topk_len, float *out, float *lse, void *ws,
+                             size_t ws_bytes, hipStream_t stream);
+
 /* Human-readable status. */
 const char *csa2_status_str(int status);
 

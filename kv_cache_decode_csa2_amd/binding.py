@@ -23,7 +23,7 @@ EXPORTS = [
     "csa2_dequant_mxfp4", "csa2_dequant_mxfp8", "csa2_append_global", "csa2_append_swa",
     "csa2_index_scores", "csa2_index_full", "csa2_index_full_scan", "csa2_index_full_finish",
     "csa2_index_reindex", "csa2_index_prefill", "csa2_sparse_attn", "csa2_sparse_attn_append",
-    "csa2_status_str",
+    "csa2_sparse_attn_prefill", "csa2_status_str",
 ]
 
 
@@ -78,6 +78,8 @@ def load() -> C.CDLL:
                                    vp, sz, vp],
             "csa2_sparse_attn": [cfgp, vp, vp, i64, vp, i32, vp, i32, vp, i32, vp, vp, vp, vp, vp,
                                  sz, vp],
+            "csa2_sparse_attn_prefill": [cfgp, vp, vp, i64, vp, i32, vp, i32, i32, i32, vp, vp,
+                                         vp, vp, vp, sz, vp],
             "csa2_sparse_attn_append": [cfgp, vp, vp, vp, vp, i64, vp, i32, vp, i32, vp, i32, vp, vp,
                                         vp, vp, vp, sz, vp],
         }
@@ -231,4 +233,12 @@ def csa2_sparse_attn_append(cfg, swa_rows, pos, q, kv_cache, n_blocks, block_tab
     batch, maxb = block_table.shape
     _call("csa2_sparse_attn_append", C.byref(cfg), _p(swa_rows), _p(pos), _p(q), _p(kv_cache),
           int(n_blocks), _p(block_table), maxb, _p(swa_cache), int(C_slots), _p(ctx_len), batch,
+          _p(topk), _p(topk_len), _p(out), _p(lse), _p(ws), ws.numel(), _stream(stream))
+
+
+def csa2_sparse_attn_prefill(cfg, q, kv_cache, n_blocks, table_row, swa_ring, C_slots, q_pos0,
+                             topk, topk_len, out, lse, ws, stream=None):
+    n_q = q.shape[0]
+    _call("csa2_sparse_attn_prefill", C.byref(cfg), _p(q), _p(kv_cache), int(n_blocks),
+          _p(table_row), table_row.numel(), _p(swa_ring), int(C_slots), int(q_pos0), int(n_q),
           _p(topk), _p(topk_len), _p(out), _p(lse), _p(ws), ws.numel(), _stream(stream))

@@ -36,9 +36,12 @@ struct AttnArgs {
     int64_t n_blocks;
     const int32_t *table;
     int32_t maxb;
+    int32_t tstride;   // block-table row stride (maxb; 0 when every row is one sequence's)
     const uint8_t *swa;
     int32_t C;
-    const int32_t *ctx_len;
+    int32_t rstride;   // ring stride in slots (C; 0 when the rows share one ring)
+    const int32_t *ctx_len;  // [B]; NULL: row b is the prefill query at q_pos0 + b
+    int32_t q_pos0;
     int32_t B;
     const int32_t *topk;
     const int32_t *topk_len;
@@ -164,7 +167,7 @@ __global__ __launch_bounds__(kAttnThreads) void k_attn(AttnArgs a) {
         for (int t = 0; t < 16; t++) qa[t] = qh[t];
     }
 
-    const int L = clamp_ctx(a.ctx_len[b], a.maxb);
+    const int L = clamp_ctx(a.ctx_len ? a.ctx_len[b] : a.q_pos0 + b + 1, a.maxb);
     const int tl = max(0, min(a.topk_len[b], a.k));
     const int w0 = max(0, L - a.W), nwin = L - w0;
     const int r_loc = 16 * wave + c16;
@@ -179,7 +182,7 @@ __global__ __launch_bounds__(kAttnThreads) void k_attn(AttnArgs a) {
         if (rg < tl) {
             const int p = a.topk[(int64_t)b * a.k + rg];
             if (p >= 0 && p < L) {
-                const int64_t phys = a.table[(int64_t)b * a.maxb + p / kBlk];
+                const int64_t phys = a.table[(int64_t)b * a.tstride + p / kBlk];
                 if (phys >= 0 && phys < a.n_blocks)
                     rp = a.kv + phys * (kBlk * (kD / 2 + kD / 32)) + (p % kBlk) * (kD / 2 + kD / 32);
             }
@@ -188,7 +191,7 @@ __global__ __launch_bounds__(kAttnThreads) void k_attn(AttnArgs a) {
         const int wi = rg - a.k;
         if (wi < nwin && wi < a.W) {
             const int p = w0 + wi;
-            rp = a.swa + ((int64_t)b * a.C + p % a.C) * (kD + kD / 32);
+            rp = a.swa + ((int64_t)b * a.rstride + p % a.C) * (kD + kD / 32);
             fp8 = true;
             fresh = p == np_b;  // the appended row: quantised here, not read back
         }
@@ -197,7 +200,7 @@ __global__ __launch_bounds__(kAttnThreads) void k_attn(AttnArgs a) {
     // ---- an appended row outside the attended window is still written (split 0, hg 0)
     if (a.swa_new && s == 0 && hg == 0 && np_b >= 0 && !(np_b >= w0 && np_b < L && np_b - w0 < a.W) &&
         tid < kD / 32) {
-        uint8_t *dst = a.swa_out + ((int64_t)b * a.C + np_b % a.C) * (kD + kD / 32);
+        uint8_t *dst = a.swa_out + ((int64_t)b * a.rstride + np_b % a.C) * (kD + kD / 32);
         quant_fp8(a.swa_new + (int64_t)b * kD + 32 * tid, dst + 32 * tid, dst + kD + tid);
     }
     const bool valid = rp != nullptr;
@@ -222,7 +225,7 @@ __global__ __launch_bounds__(kAttnThreads) void k_attn(AttnArgs a) {
             d4[1] = make_uint4(w[4], w[5], w[6], w[7]);
             sh.fresh_row[kD + tid] = (uint8_t)sc;
             if (hg == 0) {
-                uint8_t *dst = a.swa_out + ((int64_t)b * a.C + np_b % a.C) * (kD + kD / 32);
+                uint8_t *dst = a.swa_out + ((int64_t)b * a.rstride + np_b % a.C) * (kD + kD / 32);
                 uint4 *g4p = reinterpret_cast<uint4 *>(dst + 32 * tid);
                 g4p[0] = d4[0];
                 g4p[1] = d4[1];
@@ -375,10 +378,10 @@ namespace {
 int sparse_attn(const csa2_config *c, const float *swa_new, const int32_t *new_pos,
                 const uint16_t *q, const uint8_t *kv_cache, int64_t n_blocks,
                 const int32_t *block_table, int32_t maxb, const uint8_t *swa_cache,
-                uint8_t *swa_out, int32_t C, const int32_t *ctx_len, int32_t batch,
-                const int32_t *topk, const int32_t *topk_len, float *out, float *lse, void *ws,
-                size_t ws_bytes, hipStream_t stream) {
-    if (!c || !q || !kv_cache || n_blocks <= 0 || !block_table || maxb <= 0 || !ctx_len ||
+                uint8_t *swa_out, int32_t C, const int32_t *ctx_len, int32_t q_pos0,
+                int32_t batch, const int32_t *topk, const int32_t *topk_len, float *out,
+                float *lse, void *ws, size_t ws_bytes, hipStream_t stream) {
+    if (!c || !q || !kv_cache || n_blocks <= 0 || !block_table || maxb <= 0 ||
         batch < 0 || !topk || !topk_len || !out || !lse || !ws || c->topk <= 0 ||
         c->swa_window < 0 || c->n_q_heads <= 0 || c->kv_dim <= 0)
         return CSA2_ERR_INVALID;
@@ -396,9 +399,12 @@ int sparse_attn(const csa2_config *c, const float *swa_new, const int32_t *new_p
     a.n_blocks = n_blocks;
     a.table = block_table;
     a.maxb = maxb;
+    a.tstride = ctx_len ? maxb : 0;
     a.swa = swa_cache;
     a.C = C > 0 ? C : 1;
+    a.rstride = ctx_len ? a.C : 0;
     a.ctx_len = ctx_len;
+    a.q_pos0 = q_pos0;
     a.B = batch;
     a.topk = topk;
     a.topk_len = topk_len;
@@ -429,8 +435,24 @@ extern "C" int csa2_sparse_attn(const csa2_config *c, const uint16_t *q, const u
                                 int32_t batch, const int32_t *topk, const int32_t *topk_len,
                                 float *out, float *lse, void *ws, size_t ws_bytes,
                                 hipStream_t stream) {
+    if (!ctx_len) return CSA2_ERR_INVALID;
     return sparse_attn(c, nullptr, nullptr, q, kv_cache, n_blocks, block_table, maxb, swa_cache,
-                       nullptr, C, ctx_len, batch, topk, topk_len, out, lse, ws, ws_bytes, stream);
+                       nullptr, C, ctx_len, 0, batch, topk, topk_len, out, lse, ws, ws_bytes,
+                       stream);
+}
+
+extern "C" int csa2_sparse_attn_prefill(const csa2_config *c, const uint16_t *q,
+                                        const uint8_t *kv_cache, int64_t n_blocks,
+                                        const int32_t *block_table, int32_t maxb,
+                                        const uint8_t *swa_ring, int32_t C, int32_t q_pos0,
+                                        int32_t n_q, const int32_t *topk,
+                                        const int32_t *topk_len, float *out, float *lse,
+                                        void *ws, size_t ws_bytes, hipStream_t stream) {
+    if (q_pos0 < 0 || n_q < 0 || (int64_t)q_pos0 + n_q > (int64_t)maxb * kBlk)
+        return CSA2_ERR_INVALID;
+    return sparse_attn(c, nullptr, nullptr, q, kv_cache, n_blocks, block_table, maxb, swa_ring,
+                       nullptr, C, nullptr, q_pos0, n_q, topk, topk_len, out, lse, ws, ws_bytes,
+                       stream);
 }
 
 extern "C" int csa2_sparse_attn_append(const csa2_config *c, const float *swa_rows,
@@ -441,7 +463,8 @@ extern "C" int csa2_sparse_attn_append(const csa2_config *c, const float *swa_ro
                                        int32_t batch, const int32_t *topk,
                                        const int32_t *topk_len, float *out, float *lse, void *ws,
                                        size_t ws_bytes, hipStream_t stream) {
-    if (!swa_rows || !pos || !swa_cache) return CSA2_ERR_INVALID;
+    if (!swa_rows || !pos || !swa_cache || !ctx_len) return CSA2_ERR_INVALID;
     return sparse_attn(c, swa_rows, pos, q, kv_cache, n_blocks, block_table, maxb, swa_cache,
-                       swa_cache, C, ctx_len, batch, topk, topk_len, out, lse, ws, ws_bytes, stream);
+                       swa_cache, C, ctx_len, 0, batch, topk, topk_len, out, lse, ws, ws_bytes,
+                       stream);
 }

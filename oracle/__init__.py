@@ -254,6 +254,25 @@ def sparse_attn(c: Cfg, q_bf16, kv_cache, table, swa_cache, C_slots, ctx_len, to
     return out, lse
 
 
+def sparse_attn_prefill(c: Cfg, q_bf16, kv_cache, table_row, swa_ring, C_slots, q_pos0, topk,
+                        topk_len):
+    """Prefill attention: q_bf16 [n_q, H_q, D]; query i attends as a decode step at context
+    length q_pos0 + i + 1 of the one sequence (its top-k rows + its window from the ring
+    [C_slots, row]).  Returns (out [n_q, H_q, D] f64, lse [n_q, H_q] f64)."""
+    q = np.ascontiguousarray(q_bf16, np.uint16)
+    n_q = q.shape[0]
+    table = np.ascontiguousarray(np.asarray(table_row, np.int32).reshape(-1))
+    out = np.zeros((n_q, c.n_q_heads, c.kv_dim), np.float64)
+    lse = np.zeros((n_q, c.n_q_heads), np.float64)
+    _check(lib().csa2o_sparse_attn_prefill(
+        C.byref(c), _p(q), _p(kv_cache), C.c_int64(kv_cache.shape[0]), _p(table),
+        C.c_int32(table.shape[0]), _p(np.ascontiguousarray(swa_ring, np.uint8)),
+        C.c_int32(C_slots), C.c_int32(q_pos0), C.c_int32(n_q),
+        _p(np.ascontiguousarray(topk, np.int32)), _p(np.ascontiguousarray(topk_len, np.int32)),
+        _p(out), _p(lse)), "sparse_attn_prefill")
+    return out, lse
+
+
 # ------------------------------------------------------------------------- workload driver
 
 @dataclass

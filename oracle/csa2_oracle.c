@@ -607,3 +607,25 @@ int csa2o_sparse_attn(const o_cfg *c, const uint16_t *q, const uint8_t *kv_cache
     }
     return status;
 }
+
+/* Prefill attention: query i sits at position t = q_pos0 + i of the one sequence and
+ * attends, as a decode step with context length t + 1 would, to its own top-k rows and to
+ * the window rows max(0, t+1-W) .. t of the sequence's ring (the ring must still hold
+ * them).  q [n_q, H_q, D]; out [n_q, H_q, D], lse [n_q, H_q]. */
+int csa2o_sparse_attn_prefill(const o_cfg *c, const uint16_t *q, const uint8_t *kv_cache,
+                              int64_t n_blocks, const int32_t *table_row, int32_t maxb,
+                              const uint8_t *swa_ring, int32_t C, int32_t q_pos0, int32_t n_q,
+                              const int32_t *topk, const int32_t *topk_len, double *out,
+                              double *lse) {
+    if (!cfg_ok(c) || n_q < 0 || q_pos0 < 0) return O_BAD;
+    size_t qrow = (size_t)c->n_q_heads * c->kv_dim;
+    for (int32_t i = 0; i < n_q; i++) {
+        int32_t L = q_pos0 + i + 1;
+        int st = csa2o_sparse_attn(c, q + i * qrow, kv_cache, n_blocks, table_row, maxb,
+                                   swa_ring, C, &L, 1, topk + (int64_t)i * c->topk,
+                                   topk_len + i, out + i * qrow,
+                                   lse + (size_t)i * c->n_q_heads);
+        if (st != O_OK) return st;
+    }
+    return O_OK;
+}

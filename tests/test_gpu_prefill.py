@@ -11,7 +11,8 @@ import torch
 
 import oracle
 import synth_inputs as si
-from gpu_harness import GpuState, index_prefill, prefill_q
+import kv_cache_decode_csa2_amd as k
+from gpu_harness import GpuState, attn_close, dev, index_prefill, prefill_q
 from harness import OracleState, make_table
 
 pytestmark = pytest.mark.gpu
@@ -96,21 +97,76 @@ def test_prefill_wide_exponent_spans_take_the_exact_path():
         si.idx_keys = orig
 
 
+def _rings(wl, o, g, q_pos0, n_q):
+    """The sequence's window ring holding positions q_pos0-W+1 .. q_pos0+n_q-1 (oracle and
+    GPU, same seeded rows), C = n_q + W slots."""
+    C = n_q + wl.W
+    first = max(0, q_pos0 - wl.W + 1)
+    rows = si.layer_swa_rows(wl, 0, 0, q_pos0 + n_q - first)
+    ro = oracle.alloc_swa(o.cfg, 1, C)
+    oracle.append_swa(o.cfg, rows[None], np.array([first], np.int32), ro, C)
+    rg = torch.zeros((1, C, g.lay.swa_row_bytes), dtype=torch.uint8, device="cuda")
+    k.csa2_append_swa(g.cfg, dev(rows), dev(np.array([first], np.int32)), rows.shape[0], rg, C)
+    return C, ro, rg
+
+
+def _attn_prefill(g, q, ring, C, q_pos0, topk, tl):
+    n_q = q.shape[0]
+    wl = g.wl
+    ws = torch.empty(k.csa2_workspace_bytes(g.cfg, k.CSA2_OP_SPARSE_ATTN, n_q, g.table.shape[1]),
+                     dtype=torch.uint8, device="cuda")
+    out = torch.full((n_q, wl.H_q, wl.D), float("nan"), dtype=torch.float32, device="cuda")
+    lse = torch.full((n_q, wl.H_q), float("nan"), dtype=torch.float32, device="cuda")
+    k.csa2_sparse_attn_prefill(g.cfg, q, g.kv, g.n_blocks, g.table[0].contiguous(), ring, C,
+                               q_pos0, topk, tl, out, lse, ws)
+    return out, lse
+
+
+@pytest.mark.parametrize("L,n_q,H_q,W", [(3000, 200, 32, 32), (300, 300, 16, 128)])
+def test_prefill_attention_within_tolerance(L, n_q, H_q, W):
+    """Per-query sparse attention of a prefill chunk: each query's own top-k (from the GPU
+    prefill indexer, checked equal to the oracle's) plus its own window from the shared
+    ring; within 2e-3 of the fp64 oracle."""
+    wl = si.small("pfat", 130 + L, [L], H_I=8, d_I=128, K_blk=64, k=128, H_q=H_q, W=W)
+    q_pos0 = L - n_q
+    table, nblk = make_table(wl.ctx, seed=wl.seed)
+    o = OracleState(wl, table, nblk)
+    g = GpuState(wl, table, nblk)
+    qo = _oracle_q(wl, n_q)
+    _, _, to, tlo = oracle.index_prefill(o.cfg, *qo, q_pos0, o.idx, o.table[0])
+    _, _, tg, tlg = index_prefill(g, *prefill_q(wl, 0, n_q), q_pos0)
+    assert np.array_equal(_np(tg), to) and np.array_equal(_np(tlg), tlo)
+    C, ring_o, ring_g = _rings(wl, o, g, q_pos0, n_q)
+    assert np.array_equal(_np(ring_g), ring_o)
+    qa = si.prefill_attn_q(wl, 0, n_q)
+    ro, rl = oracle.sparse_attn_prefill(o.cfg, qa, o.kv, o.table[0], ring_o[0], C, q_pos0, to, tlo)
+    go, gl = _attn_prefill(g, dev(qa.view(np.int16)), ring_g, C, q_pos0, tg, tlg)
+    ok, rel, lerr = attn_close(_np(go), _np(gl), ro, rl)
+    print("prefill attention rel", rel, "lse", lerr)
+    assert ok, (rel, lerr)
+
+
 @pytest.mark.slow
 def test_prefill_workload_sampled():
     """The prefill workload at full size: 4096 queries at positions 258048..262143 of a
-    262,144-token context, indexer 8 x 128, pool 2048 blocks, top-512.  Six queries are
-    checked bit-exactly against the oracle; every query is checked for the properties
-    that hold at any size (lengths, ascending order, top-k inside the pool, causality)."""
+    262,144-token context, indexer 8 x 128, pool 2048 blocks, top-512, then attention of
+    64 heads over each query's top-512 and window.  Six queries are checked against the
+    oracle (index sets bit-exact, attention within 2e-3); every query is checked for the
+    properties that hold at any size (lengths, ascending order, top-k inside the pool,
+    causality)."""
     wl = si.workload("prefill")
     n_q, L = wl.n_q, wl.ctx[0]
     q_pos0 = L - n_q
     table, nblk = make_table(wl.ctx, seed=wl.seed, permute=False)
-    g = GpuState(wl, table, nblk, with_latent=False)
+    g = GpuState(wl, table, nblk)
+    o = OracleState(wl, table, nblk)
     qc, qs, wg = prefill_q(wl, 0, n_q)
-    pg, plg, tg, tlg = index_prefill(g, qc, qs, wg, q_pos0)
-    torch.cuda.synchronize()
-    pg, plg, tg, tlg = _np(pg), _np(plg), _np(tg), _np(tlg)
+    pgd, plgd, tgd, tlgd = index_prefill(g, qc, qs, wg, q_pos0)
+    pg, plg, tg, tlg = [_np(x) for x in (pgd, plgd, tgd, tlgd)]
+    C, ring_o, ring_g = _rings(wl, o, g, q_pos0, n_q)
+    qa = si.prefill_attn_q(wl, 0, n_q)
+    go, gl = _attn_prefill(g, dev(qa.view(np.int16)), ring_g, C, q_pos0, tgd, tlgd)
+    go, gl = _np(go), _np(gl)
     del g
     torch.cuda.empty_cache()
     assert np.all(plg == wl.K_blk) and np.all(tlg == wl.k)
@@ -118,7 +174,6 @@ def test_prefill_workload_sampled():
     t = q_pos0 + np.arange(n_q)
     assert np.all(tg[:, -1] <= t) and np.all(pg[:, -1] <= t // 8)
     assert all(np.isin(tg[i] // 8, pg[i]).all() for i in range(0, n_q, 97))
-    o = OracleState(wl, table, nblk, with_latent=False)
     qo = _oracle_q(wl, n_q)
     for i in (0, 1, 127, 128, 2049, n_q - 1):
         ctx = np.array([q_pos0 + i + 1], np.int32)
@@ -126,3 +181,6 @@ def test_prefill_workload_sampled():
                                              qo[2][i:i + 1], o.idx, o.table, ctx)
         assert np.array_equal(pg[i], po[0]), (i, _first_diff(pg[i], po[0]))
         assert np.array_equal(tg[i], to[0]), (i, _first_diff(tg[i], to[0]))
+        ro, rl = oracle.sparse_attn(o.cfg, qa[i:i + 1], o.kv, o.table, ring_o, C, ctx, to, tlo)
+        ok, rel, lerr = attn_close(go[i:i + 1], gl[i:i + 1], ro, rl)
+        assert ok, (i, rel, lerr)

@@ -119,3 +119,38 @@ def test_no_dedup_padding_and_empty():
     ro, rl = _sdpa(_qf64(q[0]), rows, float(np.float32(wl.sm_scale)))
     assert np.allclose(out[0], ro, rtol=1e-12, atol=1e-12) and np.allclose(lse[0], rl)
     assert np.all(out[1] == 0) and np.all(np.isneginf(lse[1]))
+
+
+def test_prefill_attention_is_per_query_dense_attention():
+    """Prefill query i at position t = q_pos0 + i attends to its own top-k main rows and to
+    the window rows max(0, t+1-W) .. t of the shared ring: against SDPA over exactly those
+    dequantised rows, per query."""
+    L, n_q, W = 260, 20, 16
+    wl, st = _setup([L], 37, k=12, W=W, H_q=4)
+    q_pos0 = L - n_q
+    C = n_q + W  # the ring keeps every window row of the chunk
+    first = q_pos0 - W + 1
+    rows = si.layer_swa_rows(wl, 0, 0, L - first)
+    ring = oracle.alloc_swa(st.cfg, 1, C)
+    oracle.append_swa(st.cfg, rows[None], np.array([first], np.int32), ring, C)
+    rc, rs = oracle.quantize_mxfp8(rows)
+    win = oracle.dequant_mxfp8(rc, rs)                 # row r = position first + r
+    rng = np.random.default_rng(9)
+    topk = np.full((n_q, wl.k), -1, np.int32)
+    tl = np.zeros(n_q, np.int32)
+    for i in range(n_q):
+        t = q_pos0 + i
+        n = int(rng.integers(0, wl.k + 1))
+        sel = np.sort(rng.choice(t + 1, n, replace=False))
+        topk[i, :n], tl[i] = sel, n
+    qb = si.prefill_attn_q(wl, 0, n_q)
+    out, lse = oracle.sparse_attn_prefill(st.cfg, qb, st.kv, st.table[0], ring[0], C, q_pos0,
+                                          topk, tl)
+    for i in range(n_q):
+        t = q_pos0 + i
+        w0 = max(0, t + 1 - W)
+        main = _rows_main(wl, 0, topk[i, :tl[i]])
+        rr = np.concatenate([main, win[w0 - first:t + 1 - first]])
+        ro, rl = _sdpa(_qf64(qb[i]), rr, float(np.float32(wl.sm_scale)))
+        np.testing.assert_allclose(out[i], ro, rtol=1e-10, atol=1e-12)
+        np.testing.assert_allclose(lse[i], rl, rtol=1e-12)
