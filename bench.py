@@ -121,6 +121,123 @@ class Bench:
                                     self.g.n_blocks, self.g.table, self.g.ctx, self.ws[r])
 
 
+class PrefillBench:
+    """The prefill-chunk workload: n_q query tokens at the end of one sequence run the
+    prefill indexer (matrix-core scoring + per-query selection) and the per-query sparse
+    attention over their top-k and window."""
+
+    def __init__(self, wl):
+        import kv_cache_decode_csa2_amd as k
+        import synth_inputs as si
+        from gpu_harness import GpuState, dev, prefill_q
+        from harness import make_table
+
+        self.k, self.wl = k, wl
+        table, nblk = make_table(wl.ctx, seed=wl.seed, permute=False)
+        t0 = time.time()
+        g = GpuState(wl, table, nblk, with_latent=True)
+        log(f"caches built in {time.time() - t0:.1f}s")
+        self.g, self.cfg = g, g.cfg
+        self.n_q = wl.n_q
+        self.q_pos0 = wl.ctx[0] - wl.n_q
+        self.row = g.table[0].contiguous()
+        self.maxb = self.row.numel()
+        self.qc, self.qs, self.w = prefill_q(wl, 0, self.n_q)
+        self.C = self.n_q + wl.W
+        first = max(0, self.q_pos0 - wl.W + 1)
+        rows = si.layer_swa_rows(wl, 0, 0, self.q_pos0 + self.n_q - first)
+        self.ring = torch.zeros((1, self.C, g.lay.swa_row_bytes), dtype=torch.uint8, device="cuda")
+        k.csa2_append_swa(self.cfg, dev(rows), dev(np.array([first], np.int32)), rows.shape[0],
+                          self.ring, self.C)
+        self.qa = dev(si.prefill_attn_q(wl, 0, self.n_q).view(np.int16))
+        n = self.n_q
+        self.ws = torch.zeros(k.csa2_workspace_bytes(self.cfg, k.CSA2_OP_INDEX_PREFILL, n, self.maxb),
+                              dtype=torch.uint8, device="cuda")
+        self.ws_attn = torch.zeros(k.csa2_workspace_bytes(self.cfg, k.CSA2_OP_SPARSE_ATTN, n, self.maxb),
+                                   dtype=torch.uint8, device="cuda")
+        i32 = dict(dtype=torch.int32, device="cuda")
+        self.pool = torch.empty((n, wl.K_blk), **i32)
+        self.pool_len = torch.empty(n, **i32)
+        self.topk = torch.empty((n, wl.k), **i32)
+        self.topk_len = torch.empty(n, **i32)
+        self.out = torch.empty((n, wl.H_q, wl.D), dtype=torch.float32, device="cuda")
+        self.lse = torch.empty((n, wl.H_q), dtype=torch.float32, device="cuda")
+        torch.cuda.synchronize()
+
+    def step(self, r=0):
+        k, g, c = self.k, self.g, self.cfg
+        k.csa2_index_prefill(c, self.qc, self.qs, self.w, self.q_pos0, g.idx, g.n_blocks, self.row,
+                             self.pool, self.pool_len, self.topk, self.topk_len, self.ws)
+        k.csa2_sparse_attn_prefill(c, self.qa, g.kv, g.n_blocks, self.row, self.ring, self.C,
+                                   self.q_pos0, self.topk, self.topk_len, self.out, self.lse,
+                                   self.ws_attn)
+
+    def scan(self, r=0):
+        self.k.csa2_index_prefill_scan(self.cfg, self.qc, self.qs, self.w, self.q_pos0, self.g.idx,
+                                       self.g.n_blocks, self.row, self.ws)
+
+
+def prefill_work(wl, layout):
+    """Algorithmic work of the prefill scoring kernel (matrix-core scores + epilogue): causal
+    (query, position) pairs, FP4 flops, vector-ALU epilogue instructions and the HBM bytes
+    of this design (keys read once, exact position scores, block and group maxima written)."""
+    n_q, L = wl.n_q, wl.ctx[0]
+    t = np.arange(L - n_q, L, dtype=np.int64)
+    pairs = int((t + 1).sum())
+    blocks = int(((t + 8) // 8).sum())
+    flops = 2 * pairs * wl.H_I * wl.d_I
+    alu = 2 * pairs * wl.H_I  # ReLU + fma per (pair, head)
+    bytes_ = L * (layout.idx_block_bytes // 8) + 4 * pairs + 4 * blocks + 4 * ((blocks + 7) // 8)
+    return dict(pairs=pairs, flops=flops, alu=alu, bytes=bytes_)
+
+
+MFMA_FP4_PEAK_TFLOPS = 10100.0
+ALU_PEAK_TOPS = 256 * 64 * 2.4e9 / 1e12  # fp32 lane-instructions/s without packed math
+
+
+def main_prefill(a, wl):
+    bench = PrefillBench(wl)
+    layout = bench.k.csa2_layout(bench.cfg)
+    pw = prefill_work(wl, layout)
+    graph = None if a.eager else capture(lambda: bench.step())
+    step = (lambda i: bench.step()) if graph is None else (lambda i: graph.replay())
+    timed(step, max(1, a.warmup // 4))
+    steps = max(1, a.steps // 20)
+    ms = timed(step, steps)
+    value = bench.n_q / (ms / 1e3)
+    log(f"prefill step {ms:.3f} ms -> {value:.0f} query-tokens/s")
+    reps = 5
+    sg = capture(lambda: [bench.scan() for _ in range(reps)])
+    timed(lambda i: sg.replay(), 1)
+    scan_ms = timed(lambda i: sg.replay(), 3) / reps
+    sec = scan_ms / 1e3
+    fr = {"hbm": pw["bytes"] / sec / 1e9 / HBM_PEAK_GBS,
+          "mfma": pw["flops"] / sec / 1e12 / MFMA_FP4_PEAK_TFLOPS,
+          "alu": pw["alu"] / sec / 1e12 / ALU_PEAK_TOPS}
+    log(f"prefill scoring {scan_ms:.3f} ms: hbm {fr['hbm']:.3f}, mfma {fr['mfma']:.3f}, "
+        f"alu {fr['alu']:.3f} of peak")
+    bound = max(fr, key=fr.get)
+    ach = {"hbm": pw["bytes"] / sec / 1e9, "mfma": pw["flops"] / sec / 1e12,
+           "alu": pw["alu"] / sec / 1e12}[bound]
+    peak = {"hbm": HBM_PEAK_GBS, "mfma": MFMA_FP4_PEAK_TFLOPS, "alu": ALU_PEAK_TOPS}[bound]
+    unit = {"hbm": "GB/s", "mfma": "TFLOP/s", "alu": "Tops/s"}[bound]
+    result = {
+        "metric": "CSA2 prefill-chunk query-tokens/s (prefill indexer + sparse attention)",
+        "value": round(value, 1), "unit": "query-tokens/s", "n_gpus": 1, "steps": steps,
+        "warmup": max(1, a.warmup // 4), "ms_per_step": round(ms, 4), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "mxfp4", "data": "synthetic",
+        "config": {"workload": wl.name, "queries": wl.n_q, "context": wl.ctx[0],
+                   "indexer": f"{wl.H_I}x{wl.d_I} fp4", "pool_blocks": wl.K_blk, "topk": wl.k,
+                   "q_heads": wl.H_q, "window": wl.W, "graph": graph is not None},
+        "roofline": {"bound": bound, "achieved": round(ach, 2), "peak": peak, "unit": unit,
+                     "frac": round(fr[bound], 4), "traffic": None, "kernel": "k_prefill",
+                     "kernel_us": round(scan_ms * 1e3, 2),
+                     "fractions": {k_: round(v, 4) for k_, v in fr.items()}, "work": pw},
+        "cpu_baseline": None,
+    }
+    print(json.dumps(result), flush=True)
+
+
 def capture(fn):
     s = torch.cuda.Stream()
     s.wait_stream(torch.cuda.current_stream())
@@ -222,6 +339,8 @@ def main():
     import synth_inputs as si
     wl = si.workload(a.workload)
     torch.cuda.set_device(0)
+    if wl.n_q:
+        return main_prefill(a, wl)
     bench = Bench(wl, a.replicas)
     layout = bench.k.csa2_layout(bench.cfg)
     ab = algorithmic_bytes(wl, layout)

@@ -230,6 +230,21 @@ int csa2_sparse_attn_append(const csa2_config *cfg, const float *swa_rows, const
                             const int32_t *topk, const int32_t *topk_len, float *out,
                             float *lse, void *ws, size_t ws_bytes, hipStream_t stream);
 
+/* csa2_index_prefill in two phases on the same workspace and arguments: the scoring (key
+ * spans + the matrix-core kernel: position scores, block and group maxima of every query)
+ * and the per-query selection.  prefill == prefill_scan followed by prefill_finish. */
+int csa2_index_prefill_scan(const csa2_config *cfg, const uint8_t *q_codes,
+                            const uint8_t *q_scales, const float *w, int32_t q_pos0,
+                            int32_t n_q, const uint8_t *idx_cache, int64_t n_blocks,
+                            const int32_t *block_table, int32_t maxb, void *ws, size_t ws_bytes,
+                            hipStream_t stream);
+int csa2_index_prefill_finish(const csa2_config *cfg, const uint8_t *q_codes,
+                              const uint8_t *q_scales, const float *w, int32_t q_pos0,
+                              int32_t n_q, const uint8_t *idx_cache, int64_t n_blocks,
+                              const int32_t *block_table, int32_t maxb, int32_t *pool_blocks,
+                              int32_t *pool_len, int32_t *topk, int32_t *topk_len, void *ws,
+                              size_t ws_bytes, hipStream_t stream);
+
 /* Prefill attention [KV][3][W]: n_q consecutive query tokens of ONE sequence, query i at
  * position t_i = q_pos0 + i, each attend as csa2_sparse_attn does for a sequence of length
  * t_i + 1: the main-KV rows of topk[i][0 .. topk_len[i]) and the window rows

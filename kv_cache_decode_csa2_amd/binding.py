@@ -22,7 +22,8 @@ EXPORTS = [
     "csa2_layout", "csa2_workspace_bytes", "csa2_quantize_mxfp4", "csa2_quantize_mxfp8",
     "csa2_dequant_mxfp4", "csa2_dequant_mxfp8", "csa2_append_global", "csa2_append_swa",
     "csa2_index_scores", "csa2_index_full", "csa2_index_full_scan", "csa2_index_full_finish",
-    "csa2_index_reindex", "csa2_index_prefill", "csa2_sparse_attn", "csa2_sparse_attn_append",
+    "csa2_index_reindex", "csa2_index_prefill", "csa2_index_prefill_scan",
+    "csa2_index_prefill_finish", "csa2_sparse_attn", "csa2_sparse_attn_append",
     "csa2_sparse_attn_prefill", "csa2_status_str",
 ]
 
@@ -76,6 +77,9 @@ def load() -> C.CDLL:
                                    vp, sz, vp],
             "csa2_index_prefill": [cfgp, vp, vp, vp, i32, i32, vp, i64, vp, i32, vp, vp, vp, vp,
                                    vp, sz, vp],
+            "csa2_index_prefill_scan": [cfgp, vp, vp, vp, i32, i32, vp, i64, vp, i32, vp, sz, vp],
+            "csa2_index_prefill_finish": [cfgp, vp, vp, vp, i32, i32, vp, i64, vp, i32, vp, vp, vp,
+                                          vp, vp, sz, vp],
             "csa2_sparse_attn": [cfgp, vp, vp, i64, vp, i32, vp, i32, vp, i32, vp, vp, vp, vp, vp,
                                  sz, vp],
             "csa2_sparse_attn_prefill": [cfgp, vp, vp, i64, vp, i32, vp, i32, i32, i32, vp, vp,
@@ -218,6 +222,21 @@ def csa2_index_prefill(cfg, q_codes, q_scales, w, q_pos0, idx_cache, n_blocks, t
     _call("csa2_index_prefill", C.byref(cfg), _p(q_codes), _p(q_scales), _p(w), int(q_pos0),
           int(n_q), _p(idx_cache), int(n_blocks), _p(table_row), maxb, _p(pool_blocks),
           _p(pool_len), _p(topk), _p(topk_len), _p(ws), ws.numel(), _stream(stream))
+
+
+def csa2_index_prefill_scan(cfg, q_codes, q_scales, w, q_pos0, idx_cache, n_blocks, table_row,
+                            ws, stream=None):
+    _call("csa2_index_prefill_scan", C.byref(cfg), _p(q_codes), _p(q_scales), _p(w),
+          int(q_pos0), int(q_codes.shape[0]), _p(idx_cache), int(n_blocks), _p(table_row),
+          table_row.numel(), _p(ws), ws.numel(), _stream(stream))
+
+
+def csa2_index_prefill_finish(cfg, q_codes, q_scales, w, q_pos0, idx_cache, n_blocks, table_row,
+                              pool_blocks, pool_len, topk, topk_len, ws, stream=None):
+    _call("csa2_index_prefill_finish", C.byref(cfg), _p(q_codes), _p(q_scales), _p(w),
+          int(q_pos0), int(q_codes.shape[0]), _p(idx_cache), int(n_blocks), _p(table_row),
+          table_row.numel(), _p(pool_blocks), _p(pool_len), _p(topk), _p(topk_len), _p(ws),
+          ws.numel(), _stream(stream))
 
 
 def csa2_sparse_attn(cfg, q, kv_cache, n_blocks, block_table, swa_cache, C_slots, ctx_len,

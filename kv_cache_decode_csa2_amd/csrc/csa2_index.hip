@@ -642,8 +642,17 @@ __device__ __forceinline__ SelResult select_emit(const RegItems<N> &it, IdF id, 
     return r;
 }
 
+// Block maxima of one sequence: block j at base[(j/8)*gstride + j%8] (groups of 8 blocks
+// are contiguous).
+struct BlockRow {
+    const float *base;
+    int64_t gstride;
+    __device__ __forceinline__ float operator[](int j) const { return base[(j >> 3) * gstride + (j & 7)]; }
+    __device__ __forceinline__ const float *group(int g) const { return base + g * gstride; }
+};
+
 // Items of the streaming path: all blocks j < nb whose maximum is >= lam, in chunks of kRegCap.
-__device__ __forceinline__ void load_block_chunk(const float *bs, int nb, uint32_t lam, int c0,
+__device__ __forceinline__ void load_block_chunk(const BlockRow &bs, int nb, uint32_t lam, int c0,
                                                  RegItems<kIPT> &it) {
     const int j0 = c0 + (int)threadIdx.x * kIPT;
     it.valid = 0;
@@ -660,7 +669,7 @@ __device__ __forceinline__ void load_block_chunk(const float *bs, int nb, uint32
 }
 
 struct GlobalBlocks {
-    const float *bs;
+    BlockRow bs;
     int nb;
     uint32_t lam;
     template <class F>
@@ -692,7 +701,7 @@ __device__ __forceinline__ int select_pool(const SelectArgs &a, int b, int nb, S
         __syncthreads();
         return nb;
     }
-    const float *bs = a.bscore + (int64_t)b * a.bstride;
+    const BlockRow bs{a.bscore + (int64_t)b * a.bs_b, a.bs_g};
     const int ng = (nb + kItemBlocks - 1) / kItemBlocks;
     uint32_t lam = 0u;  // lower bound of the K-th largest block key
     bool fast = ng <= kRegCap;
@@ -746,7 +755,7 @@ __device__ __forceinline__ int select_pool(const SelectArgs &a, int b, int nb, S
                 if (gid[q] >= 0) {
                     const int j0 = gid[q] * kItemBlocks;
                     if (j0 + kItemBlocks <= nb) {
-                        const float4 *src = reinterpret_cast<const float4 *>(bs + j0);
+                        const float4 *src = reinterpret_cast<const float4 *>(bs.group(gid[q]));
                         const float4 x0 = src[0], x1 = src[1];
                         v[0] = x0.x; v[1] = x0.y; v[2] = x0.z; v[3] = x0.w;
                         v[4] = x1.x; v[5] = x1.y; v[6] = x1.z; v[7] = x1.w;
@@ -836,7 +845,7 @@ __device__ __forceinline__ void select_topk(const SelectArgs &a, int b, int L, c
         if (live) {
             const float4 *src = REINDEX
                 ? reinterpret_cast<const float4 *>(a.poolsc + ((int64_t)b * a.K_blk + 2 * tid + q) * kBlk)
-                : reinterpret_cast<const float4 *>(a.pscore + (int64_t)b * a.maxb * kBlk + (int64_t)pj[q] * kBlk);
+                : reinterpret_cast<const float4 *>(a.pscore + (int64_t)b * a.ps_b + (int64_t)pj[q] * a.ps_j);
             const float4 x0 = src[0], x1 = src[1];
             sc[0] = x0.x; sc[1] = x0.y; sc[2] = x0.z; sc[3] = x0.w;
             sc[4] = x1.x; sc[5] = x1.y; sc[6] = x1.z; sc[7] = x1.w;
@@ -1074,7 +1083,10 @@ SelectArgs select_args(const csa2_config *c, const int32_t *ctx, int32_t maxb, i
     s.k = c->topk;
     s.pscore = (const float *)(base + L.pscore);
     s.bscore = (const float *)(base + L.bscore);
-    s.bstride = ngmax_of(maxb) * kItemBlocks;
+    s.ps_b = (int64_t)maxb * kBlk;
+    s.ps_j = kBlk;
+    s.bs_b = (int64_t)ngmax_of(maxb) * kItemBlocks;
+    s.bs_g = kItemBlocks;
     s.gmax = (const float *)(base + L.gmax);
     s.ngmax = ngmax_of(maxb);
     s.poolsc = (const float *)(base + L.poolsc);

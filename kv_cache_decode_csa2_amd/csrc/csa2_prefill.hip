@@ -55,10 +55,10 @@ struct PrefillArgs {
     int32_t maxb;
     int32_t nb;            // logical blocks touched: ceil((q_pos0 + n_q) / 8)
     uint8_t *kspan;        // [round8(nb)]
-    float *pscore;         // [n_q][maxb*8]
-    float *bscore;         // [n_q][bstride]
+    float *pscore;         // block-major: (q, p) at ((p/8)*n_q + q)*8 + p%8
+    float *bscore;         // group-major: (q, j) at ((j/8)*n_q + q)*8 + j%8
     float *gmax;           // [n_q][ngmax]
-    int32_t bstride, ngmax;
+    int32_t ngmax;
     int32_t n_qt, n_pc;    // query tiles, position chunks
 };
 
@@ -100,99 +100,108 @@ __global__ __launch_bounds__(256) void k_prefill_span(PrefillArgs a) {
 }
 
 // One key stage in LDS: the code bytes of 8 blocks (rows of H 16-byte chunks, chunk h of
-// row R stored at position h ^ (R mod H), blocks kBlockPad apart) and their scale bytes.
+// row R stored at position h ^ (R mod H), blocks kBlockPad apart, the whole region a
+// multiple of 1 KB) and their scale bytes (a multiple of 256 B).
 template <int H, int G>
 struct PfStage {
-    static constexpr int CODES = kBlk * H * 16 * G;
-    static constexpr int SCB = kBlk * H * G;
-    static constexpr int BSTR = CODES + kBlockPad;
-    __align__(16) uint8_t codes[kPfStageBlocks * BSTR];
-    __align__(16) uint32_t scales[kPfStageBlocks * SCB / 4];
+    static constexpr int CODES = kBlk * H * 16 * G;  // code bytes per block
+    static constexpr int SCB = kBlk * H * G;         // scale bytes per block
+    static constexpr int BSTR = CODES + kBlockPad;   // LDS bytes per staged block
+    static constexpr int SLOTS = (kPfStageBlocks * BSTR / 16 + kWave - 1) / kWave * kWave;
+    static constexpr int SDW = (kPfStageBlocks * SCB / 4 + kWave - 1) / kWave * kWave;
+    __align__(16) uint8_t codes[SLOTS * 16];
+    __align__(16) uint32_t scales[SDW];
 };
 
-// Per-thread prefetch of one stage from global memory.
-template <int H, int G>
-struct PfFetch {
-    static constexpr int CH = kPfStageBlocks * PfStage<H, G>::CODES / 16;  // 16-B chunks
-    static constexpr int NC = (CH + kPfThreads - 1) / kPfThreads;
-    static constexpr int SD = kPfStageBlocks * PfStage<H, G>::SCB / 4;    // scale dwords
-    static constexpr int NS = (SD + kPfThreads - 1) / kPfThreads;
-    uint4 c[NC];
-    uint32_t s[NS];
+// Block-table entries and key spans of a workgroup's position chunk, staged once in LDS so
+// that no per-stage lookup waits on global memory.
+struct PfMeta {
+    int32_t phys[kPfChunkBlocks];  // physical block, -1 when absent
+    uint8_t kspan[kPfChunkBlocks];
 };
 
+typedef __attribute__((address_space(3))) void *lds_ptr_t;
+
+// Stage the keys of blocks jrel .. jrel+7 of the chunk into dst with LDS DMA
+// (global_load_lds): one instruction moves 64 lanes x 16 bytes into 1 KB of consecutive LDS,
+// lane i to byte 16*i, so each lane fetches the global chunk that the swizzled layout puts
+// at its slot.  Padding slots fetch chunk 0 of a block.  Absent blocks read physical block 0.
 template <int H, int G>
-__device__ __forceinline__ void pf_fetch(const PrefillArgs &a, int J0, PfFetch<H, G> &f) {
+__device__ __forceinline__ void pf_dma(const PrefillArgs &a, const PfMeta &meta, int jrel,
+                                       PfStage<H, G> &dst) {
     using S = PfStage<H, G>;
-    using F = PfFetch<H, G>;
     constexpr int BYTES = S::CODES + S::SCB;
-    constexpr int CPB = S::CODES / 16;  // chunks per block
+    constexpr int CPB = S::CODES / 16;  // code chunks per block
+    constexpr int SPB = S::BSTR / 16;   // LDS slots per staged block
     constexpr int DPB = S::SCB / 4;     // scale dwords per block
+    const int lane = lane_id(), wave = (int)threadIdx.x / kWave;
 #pragma unroll
-    for (int i = 0; i < F::NC; i++) {
-        const int c = (int)threadIdx.x + i * kPfThreads;
-        f.c[i] = make_uint4(0u, 0u, 0u, 0u);
-        if (F::CH % kPfThreads == 0 || c < F::CH) {
-            const int64_t ph = phys_block(a, J0 + c / CPB);
-            const uint8_t *src = a.idx_cache + (ph >= 0 ? ph : 0) * BYTES + (c % CPB) * 16;
-            f.c[i] = *reinterpret_cast<const uint4 *>(src);
+    for (int r = wave; r < S::SLOTS / kWave; r += kPfWaves) {
+        const int slot = kWave * r + lane;
+        const int blk = min(slot / SPB, kPfStageBlocks - 1), c = slot - blk * SPB;
+        int chunk = 0;
+        if (c < CPB) {
+            const int row = c / H, hs = c % H;
+            chunk = row * H + (hs ^ (row & (H - 1)));
         }
+        const int64_t ph = meta.phys[jrel + blk];
+        const uint8_t *src = a.idx_cache + (ph >= 0 ? ph : 0) * BYTES + chunk * 16;
+        __builtin_amdgcn_global_load_lds(src, (lds_ptr_t)(dst.codes + kWave * 16 * r), 16, 0, 0);
     }
 #pragma unroll
-    for (int i = 0; i < F::NS; i++) {
-        const int d = (int)threadIdx.x + i * kPfThreads;
-        f.s[i] = 0u;
-        if (F::SD % kPfThreads == 0 || d < F::SD) {
-            const int64_t ph = phys_block(a, J0 + d / DPB);
-            const uint8_t *src = a.idx_cache + (ph >= 0 ? ph : 0) * BYTES + S::CODES + (d % DPB) * 4;
-            f.s[i] = *reinterpret_cast<const uint32_t *>(src);
-        }
+    for (int r = wave; r < S::SDW / kWave; r += kPfWaves) {
+        const int d = kWave * r + lane;
+        const int blk = min(d / DPB, kPfStageBlocks - 1), k = min(d - blk * DPB, DPB - 1);
+        const int64_t ph = meta.phys[jrel + blk];
+        const uint8_t *src = a.idx_cache + (ph >= 0 ? ph : 0) * BYTES + S::CODES + k * 4;
+        __builtin_amdgcn_global_load_lds(src, (lds_ptr_t)(dst.scales + kWave * r), 4, 0, 0);
     }
 }
 
-template <int H, int G>
-__device__ __forceinline__ void pf_store(const PfFetch<H, G> &f, PfStage<H, G> &st) {
-    using S = PfStage<H, G>;
-    using F = PfFetch<H, G>;
-    constexpr int CPB = S::CODES / 16;
-#pragma unroll
-    for (int i = 0; i < F::NC; i++) {
-        const int c = (int)threadIdx.x + i * kPfThreads;
-        if (F::CH % kPfThreads == 0 || c < F::CH) {
-            const int blk = c / CPB, r = c % CPB;
-            const int row = r / H, h = r % H;
-            *reinterpret_cast<uint4 *>(st.codes + blk * S::BSTR + (row * H + (h ^ (row & (H - 1)))) * 16) = f.c[i];
-        }
-    }
-#pragma unroll
-    for (int i = 0; i < F::NS; i++) {
-        const int d = (int)threadIdx.x + i * kPfThreads;
-        if (F::SD % kPfThreads == 0 || d < F::SD) st.scales[d] = f.s[i];
-    }
-}
-
+// One 16x16x128 FP4 tile product; the scale of operand A is byte 0 of sa, that of B byte
+// SB of sb (operand selects are immediates).
+template <int SB>
 __device__ __forceinline__ f32x4_t mfma_fp4(const uint4 &a, const uint4 &b, uint32_t sa, uint32_t sb) {
     const v8i_t av = {(int)a.x, (int)a.y, (int)a.z, (int)a.w, 0, 0, 0, 0};
     const v8i_t bv = {(int)b.x, (int)b.y, (int)b.z, (int)b.w, 0, 0, 0, 0};
     const f32x4_t z = {0.f, 0.f, 0.f, 0.f};
-    // formats 4/4: both operands FP4 E2M1; scale byte 0 of sa / sb
-    return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(av, bv, z, 4, 4, 0, (int)sa, 0, (int)sb);
+    // formats 4/4: both operands FP4 E2M1
+    return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(av, bv, z, 4, 4, 0, (int)sa, SB, (int)sb);
 }
 
-__device__ __forceinline__ float relu0(float x) { return x > 0.0f ? x : 0.0f; }
+// mfma_fp4 with the B scale in byte i (0..3, unrolled) of sb.
+__device__ __forceinline__ f32x4_t mfma_pick(const uint4 &a, const uint4 &b, uint32_t sa, uint32_t sb, int i) {
+    switch (i) {
+    case 0: return mfma_fp4<0>(a, b, sa, sb);
+    case 1: return mfma_fp4<1>(a, b, sa, sb);
+    case 2: return mfma_fp4<2>(a, b, sa, sb);
+    default: return mfma_fp4<3>(a, b, sa, sb);
+    }
+}
+
+// max(x, +0) exactly as defined (every negative value and -0 give +0) in one integer max:
+// finite floats with the sign bit clear order like their bit patterns, and every float with
+// the sign bit set is a negative integer.
+__device__ __forceinline__ float relu0(float x) { return __int_as_float(max(__float_as_int(x), 0)); }
+
+// Maximum of scores (finite or -inf, never NaN) without the IEEE-mode canonicalisation.
+__device__ __forceinline__ float smax(float a, float b) { return __builtin_elementwise_maximum(a, b); }
 
 // Query tile held by a lane: column q (16 queries), group g = lane / 16 of every head.
 template <int H>
 struct PfQuery {
-    uint4 c[H];     // FP4 codes of group g of head h
-    uint32_t s[H];  // E8M0 code of group g of head h
+    uint4 c[H];                // FP4 codes of group g of head h
+    uint32_t s[(H + 3) / 4];   // E8M0 code of group g of head h in byte h % 4 of s[h / 4]
     float w[H];
 };
 
 template <int H, int G>
 __global__ __launch_bounds__(kPfThreads, 2) void k_prefill(PrefillArgs a) {
     using S = PfStage<H, G>;
-    __shared__ S st[2];
+    // two stage buffers as distinct objects, so that the reads of one are known not to
+    // alias the DMA into the other
+    __shared__ S stA, stB;
+    __shared__ PfMeta meta;
 
     // workgroup -> (position chunk, query tile); the workgroups of one chunk are consecutive
     // on one XCD (dispatch places workgroup i on XCD i % 8) so its keys are fetched once
@@ -212,6 +221,15 @@ __global__ __launch_bounds__(kPfThreads, 2) void k_prefill(PrefillArgs a) {
     const int col = lane & 15, g = lane >> 4;
     const bool gl = g < G;  // lanes of groups >= G carry zeros (d_I < 128)
 
+    // the chunk's table entries and key spans (blocks past Jend: absent, span 0)
+    for (int i = (int)threadIdx.x; i < kPfChunkBlocks; i += kPfThreads) {
+        const int j = Jbeg + i;
+        meta.phys[i] = j < Jend ? (int32_t)phys_block(a, j) : -1;
+        meta.kspan[i] = j < Jend ? a.kspan[j] : (uint8_t)0;
+    }
+    __syncthreads();
+    pf_dma<H, G>(a, meta, 0, stA);
+
     // queries of this wave's tiles, their scale spans and causal limits
     PfQuery<H> Q[kPfNQ];
     int qspan[kPfNQ], qb[kPfNQ];
@@ -223,10 +241,12 @@ __global__ __launch_bounds__(kPfThreads, 2) void k_prefill(PrefillArgs a) {
         const uint8_t *qs = a.q_scales + (int64_t)q * H * G;
         int span = 0;
 #pragma unroll
+        for (int i = 0; i < (H + 3) / 4; i++) Q[jq].s[i] = 0u;
+#pragma unroll
         for (int h = 0; h < H; h++) {
             Q[jq].c[h] = gl ? *reinterpret_cast<const uint4 *>(qc + (h * G + (gl ? g : 0)) * 16)
                             : make_uint4(0u, 0u, 0u, 0u);
-            Q[jq].s[h] = gl ? qs[h * G + g] : 127u;
+            Q[jq].s[h / 4] |= (gl ? (uint32_t)qs[h * G + g] : 127u) << (8 * (h % 4));
             Q[jq].w[h] = a.w[(int64_t)q * H + h];
             int lo = 255, hi = 0;
 #pragma unroll
@@ -242,26 +262,21 @@ __global__ __launch_bounds__(kPfThreads, 2) void k_prefill(PrefillArgs a) {
         qspan[jq] = __builtin_amdgcn_readfirstlane(span);
     }
 
-    float gm[kPfNQ];
-    PfFetch<H, G> f;
-    pf_fetch<H, G>(a, Jbeg, f);
-    pf_store<H, G>(f, st[0]);
-    __syncthreads();
-
-    for (int sidx = 0; sidx < nstage; sidx++) {
+    // scores of one staged stage: 4 tiles of 16 positions x the wave's 2 tiles of 16 queries
+    auto compute = [&](const S &cur, int sidx) {
         const int J0 = Jbeg + sidx * kPfStageBlocks;
-        if (sidx + 1 < nstage) pf_fetch<H, G>(a, J0 + kPfStageBlocks, f);
-        const S &cur = st[sidx & 1];
-        // stage metadata (uniform): present-block bits and key spans
+        const int jrel = sidx * kPfStageBlocks;
         uint32_t present = 0;
 #pragma unroll
         for (int b = 0; b < kPfStageBlocks; b++)
-            if (phys_block(a, J0 + b) >= 0) present |= 1u << b;
-        const uint2 ks8 = *reinterpret_cast<const uint2 *>(a.kspan + J0);
+            if (meta.phys[jrel + b] >= 0) present |= 1u << b;
+        const uint2 ks8 = *reinterpret_cast<const uint2 *>(meta.kspan + jrel);
+        float *ps_stage = a.pscore + (int64_t)J0 * a.n_q * kBlk;
+        float *bs_stage = a.bscore + (int64_t)(J0 >> 3) * a.n_q * kBlk;
+        float gm[kPfNQ];
 #pragma unroll
         for (int jq = 0; jq < kPfNQ; jq++) gm[jq] = -INFINITY;
-
-#pragma unroll
+#pragma unroll 1
         for (int u = 0; u < kPfStageBlocks / 2; u++) {  // 16-position tiles
             const int p0 = (J0 + 2 * u) * kBlk;
             // this lane's key row: position p0 + col, group g
@@ -303,28 +318,38 @@ __global__ __launch_bounds__(kPfThreads, 2) void k_prefill(PrefillArgs a) {
                 const int tmin = a.q_pos0 + qb[jq];
                 const int tmax = a.q_pos0 + min(qb[jq] + 15, a.n_q - 1);
                 if (p0 > tmax) continue;                             // all masked (uniform)
+                const bool exact = (int)kspan_t + qspan[jq] <= kSpanExact;
                 f32x4_t sc = {0.f, 0.f, 0.f, 0.f};
-                if ((int)kspan_t + qspan[jq] <= kSpanExact) {
+                // four heads at a time: their products are issued before the epilogue
+                // consumes them
 #pragma unroll
-                    for (int h = 0; h < H; h++) {
-                        const f32x4_t d = mfma_fp4(kc[h], Q[jq].c[h], ksc[h], Q[jq].s[h]);
+                for (int h0 = 0; h0 < H; h0 += 4) {
+                    constexpr int NH = H < 4 ? H : 4;
+                    f32x4_t d[NH];
+                    if (exact) {
 #pragma unroll
-                        for (int e = 0; e < 4; e++) sc[e] = __builtin_fmaf(Q[jq].w[h], relu0(d[e]), sc[e]);
-                    }
-                } else {
+                        for (int i = 0; i < NH; i++)
+                            d[i] = mfma_pick(kc[h0 + i], Q[jq].c[h0 + i], ksc[h0 + i], Q[jq].s[h0 / 4], i);
+                    } else {
+                        // exact by construction: one product per group (the other groups'
+                        // key lanes zeroed), summed in group order
 #pragma unroll
-                    for (int h = 0; h < H; h++) {
-                        f32x4_t d = {0.f, 0.f, 0.f, 0.f};
+                        for (int i = 0; i < NH; i++) {
+                            d[i] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-                        for (int g2 = 0; g2 < G; g2++) {
-                            const uint4 kz = g == g2 ? kc[h] : make_uint4(0u, 0u, 0u, 0u);
-                            const f32x4_t t = mfma_fp4(kz, Q[jq].c[h], ksc[h], Q[jq].s[h]);
+                            for (int g2 = 0; g2 < G; g2++) {
+                                const uint4 kz = g == g2 ? kc[h0 + i] : make_uint4(0u, 0u, 0u, 0u);
+                                const f32x4_t t = mfma_pick(kz, Q[jq].c[h0 + i], ksc[h0 + i], Q[jq].s[h0 / 4], i);
 #pragma unroll
-                            for (int e = 0; e < 4; e++) d[e] = d[e] + t[e];
+                                for (int e = 0; e < 4; e++) d[i][e] = d[i][e] + t[e];
+                            }
                         }
-#pragma unroll
-                        for (int e = 0; e < 4; e++) sc[e] = __builtin_fmaf(Q[jq].w[h], relu0(d[e]), sc[e]);
                     }
+#pragma unroll
+                    for (int i = 0; i < NH; i++)
+#pragma unroll
+                        for (int e = 0; e < 4; e++)
+                            sc[e] = __builtin_fmaf(Q[jq].w[h0 + i], relu0(d[i][e]), sc[e]);
                 }
                 // lane: query qb + col, positions p0 + 4*g + e
                 const int q = qb[jq] + col;
@@ -336,26 +361,42 @@ __global__ __launch_bounds__(kPfThreads, 2) void k_prefill(PrefillArgs a) {
                     for (int e = 0; e < 4; e++)
                         if (!pres || pl + e > t) sc[e] = -INFINITY;
                 }
-                float m = fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3]));
-                m = fmaxf(m, __shfl_xor(m, 16, kWave));
-                gm[jq] = fmaxf(gm[jq], m);
+                float m = smax(smax(sc[0], sc[1]), smax(sc[2], sc[3]));
+                m = smax(m, __shfl_xor(m, 16, kWave));
+                gm[jq] = smax(gm[jq], m);
                 // blocks past nb (the tile's second block when nb is odd) are not stored:
-                // the position-score row ends at block maxb - 1 >= nb - 1
+                // the score arrays hold blocks 0 .. nb - 1 only
                 const int jb = J0 + 2 * u + (g >> 1);
                 if (q < a.n_q && jb < a.nb) {
-                    *reinterpret_cast<f32x4_t *>(a.pscore + (int64_t)q * a.maxb * kBlk + pl) = sc;
-                    if ((g & 1) == 0) a.bscore[(int64_t)q * a.bstride + jb] = m;
+                    // uniform stage bases, 32-bit lane offsets (< 8 blocks of n_q rows)
+                    const uint32_t po = (uint32_t)(((2 * u + (g >> 1)) * a.n_q + q) * kBlk + 4 * (g & 1));
+                    *reinterpret_cast<f32x4_t *>(ps_stage + po) = sc;
+                    if ((g & 1) == 0) bs_stage[(uint32_t)(q * kBlk + 2 * u + (g >> 1))] = m;
                 }
             }
         }
 #pragma unroll
         for (int jq = 0; jq < kPfNQ; jq++) {
-            const float v = fmaxf(gm[jq], __shfl_xor(gm[jq], 32, kWave));
+            const float v = smax(gm[jq], __shfl_xor(gm[jq], 32, kWave));
             const int q = qb[jq] + col;
             if (g == 0 && q < a.n_q && J0 * kBlk <= a.q_pos0 + q)
                 a.gmax[(int64_t)q * a.ngmax + J0 / kPfStageBlocks] = v;
         }
-        if (sidx + 1 < nstage) pf_store<H, G>(f, st[(sidx + 1) & 1]);
+    };
+
+    // pipeline: the DMA of stage s+1 runs while stage s is computed; a stage ends with every
+    // wave's DMA complete (vmcnt 0) and a barrier
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    for (int sidx = 0; sidx < nstage; sidx += 2) {
+        if (sidx + 1 < nstage) pf_dma<H, G>(a, meta, (sidx + 1) * kPfStageBlocks, stB);
+        compute(stA, sidx);
+        __builtin_amdgcn_s_waitcnt(0);
+        __syncthreads();
+        if (sidx + 1 >= nstage) break;
+        if (sidx + 2 < nstage) pf_dma<H, G>(a, meta, (sidx + 2) * kPfStageBlocks, stA);
+        compute(stB, sidx + 1);
+        __builtin_amdgcn_s_waitcnt(0);
         __syncthreads();
     }
 }
@@ -406,46 +447,75 @@ size_t prefill_ws_bytes(const csa2_config *, int32_t n_q, int32_t maxb) {
 
 using namespace csa2;
 
-extern "C" int csa2_index_prefill(const csa2_config *c, const uint8_t *q_codes,
-                                  const uint8_t *q_scales, const float *w, int32_t q_pos0,
-                                  int32_t n_q, const uint8_t *idx_cache, int64_t n_blocks,
-                                  const int32_t *block_table, int32_t maxb, int32_t *pool_blocks,
-                                  int32_t *pool_len, int32_t *topk, int32_t *topk_len, void *ws,
-                                  size_t ws_bytes, hipStream_t stream) {
+namespace {
+
+// Arguments of both prefill phases; returns a status (CSA2_OK: *a / *sel filled).
+int prefill_setup(const csa2_config *c, const uint8_t *q_codes, const uint8_t *q_scales,
+                  const float *w, int32_t q_pos0, int32_t n_q, const uint8_t *idx_cache,
+                  int64_t n_blocks, const int32_t *block_table, int32_t maxb, void *ws,
+                  size_t ws_bytes, PrefillArgs *a, PfFn *fn) {
     const int st = check_index_cfg(c);
     if (st) return st;
     if (!q_codes || !q_scales || !w || !idx_cache || n_blocks <= 0 || !block_table ||
-        maxb <= 0 || q_pos0 < 0 || n_q < 0 || !pool_blocks || !pool_len || !topk ||
-        !topk_len || !ws)
+        maxb <= 0 || q_pos0 < 0 || n_q < 0 || !ws)
         return CSA2_ERR_INVALID;
     if ((int64_t)q_pos0 + n_q > (int64_t)maxb * kBlk) return CSA2_ERR_INVALID;
     const WsPrefill L = ws_prefill(n_q, maxb);
     if (ws_bytes < L.total) return CSA2_ERR_WORKSPACE;
-    if (n_q == 0) return CSA2_OK;
-    PfFn fn;
-    if (!pick_prefill(c->n_idx_heads, c->idx_dim, &fn)) return CSA2_ERR_UNSUPPORTED;
+    if (!pick_prefill(c->n_idx_heads, c->idx_dim, fn)) return CSA2_ERR_UNSUPPORTED;
     uint8_t *base = (uint8_t *)ws;
-    PrefillArgs a{};
-    a.q_codes = q_codes;
-    a.q_scales = q_scales;
-    a.w = w;
-    a.q_pos0 = q_pos0;
-    a.n_q = n_q;
-    a.idx_cache = idx_cache;
-    a.n_blocks = n_blocks;
-    a.table = block_table;
-    a.maxb = maxb;
-    a.nb = (int32_t)(((int64_t)q_pos0 + n_q + kBlk - 1) / kBlk);
-    a.kspan = base + L.kspan;
-    a.pscore = (float *)(base + L.pscore);
-    a.bscore = (float *)(base + L.bscore);
-    a.gmax = (float *)(base + L.gmax);
-    a.ngmax = ngmax_of(maxb);
-    a.bstride = a.ngmax * kPfStageBlocks;
-    a.n_qt = (n_q + kPfQT - 1) / kPfQT;
-    a.n_pc = (a.nb + kPfChunkBlocks - 1) / kPfChunkBlocks;
+    *a = PrefillArgs{};
+    a->q_codes = q_codes;
+    a->q_scales = q_scales;
+    a->w = w;
+    a->q_pos0 = q_pos0;
+    a->n_q = n_q;
+    a->idx_cache = idx_cache;
+    a->n_blocks = n_blocks;
+    a->table = block_table;
+    a->maxb = maxb;
+    a->nb = (int32_t)(((int64_t)q_pos0 + n_q + kBlk - 1) / kBlk);
+    a->kspan = base + L.kspan;
+    a->pscore = (float *)(base + L.pscore);
+    a->bscore = (float *)(base + L.bscore);
+    a->gmax = (float *)(base + L.gmax);
+    a->ngmax = ngmax_of(maxb);
+    a->n_qt = (n_q + kPfQT - 1) / kPfQT;
+    a->n_pc = (a->nb + kPfChunkBlocks - 1) / kPfChunkBlocks;
+    return CSA2_OK;
+}
+
+}  // namespace
+
+extern "C" int csa2_index_prefill_scan(const csa2_config *c, const uint8_t *q_codes,
+                                       const uint8_t *q_scales, const float *w, int32_t q_pos0,
+                                       int32_t n_q, const uint8_t *idx_cache, int64_t n_blocks,
+                                       const int32_t *block_table, int32_t maxb, void *ws,
+                                       size_t ws_bytes, hipStream_t stream) {
+    PrefillArgs a;
+    PfFn fn;
+    const int st = prefill_setup(c, q_codes, q_scales, w, q_pos0, n_q, idx_cache, n_blocks,
+                                 block_table, maxb, ws, ws_bytes, &a, &fn);
+    if (st) return st;
+    if (n_q == 0) return CSA2_OK;
     fn(a, stream);
-    if (hipGetLastError() != hipSuccess) return CSA2_ERR_HIP;
+    return hipGetLastError() == hipSuccess ? CSA2_OK : CSA2_ERR_HIP;
+}
+
+extern "C" int csa2_index_prefill_finish(const csa2_config *c, const uint8_t *q_codes,
+                                         const uint8_t *q_scales, const float *w,
+                                         int32_t q_pos0, int32_t n_q, const uint8_t *idx_cache,
+                                         int64_t n_blocks, const int32_t *block_table,
+                                         int32_t maxb, int32_t *pool_blocks, int32_t *pool_len,
+                                         int32_t *topk, int32_t *topk_len, void *ws,
+                                         size_t ws_bytes, hipStream_t stream) {
+    PrefillArgs a;
+    PfFn fn;
+    const int st = prefill_setup(c, q_codes, q_scales, w, q_pos0, n_q, idx_cache, n_blocks,
+                                 block_table, maxb, ws, ws_bytes, &a, &fn);
+    if (st) return st;
+    if (!pool_blocks || !pool_len || !topk || !topk_len) return CSA2_ERR_INVALID;
+    if (n_q == 0) return CSA2_OK;
     SelectArgs s{};
     s.ctx_len = nullptr;
     s.q_pos0 = q_pos0;
@@ -455,7 +525,10 @@ extern "C" int csa2_index_prefill(const csa2_config *c, const uint8_t *q_codes,
     s.k = c->topk;
     s.pscore = a.pscore;
     s.bscore = a.bscore;
-    s.bstride = a.bstride;
+    s.ps_b = kBlk;
+    s.ps_j = (int64_t)n_q * kBlk;
+    s.bs_b = kBlk;
+    s.bs_g = (int64_t)n_q * kBlk;
     s.gmax = a.gmax;
     s.ngmax = a.ngmax;
     s.pool_blocks = pool_blocks;
@@ -463,4 +536,19 @@ extern "C" int csa2_index_prefill(const csa2_config *c, const uint8_t *q_codes,
     s.topk = topk;
     s.topk_len = topk_len;
     return launch_select(s, false, stream);
+}
+
+extern "C" int csa2_index_prefill(const csa2_config *c, const uint8_t *q_codes,
+                                  const uint8_t *q_scales, const float *w, int32_t q_pos0,
+                                  int32_t n_q, const uint8_t *idx_cache, int64_t n_blocks,
+                                  const int32_t *block_table, int32_t maxb, int32_t *pool_blocks,
+                                  int32_t *pool_len, int32_t *topk, int32_t *topk_len, void *ws,
+                                  size_t ws_bytes, hipStream_t stream) {
+    if (!pool_blocks || !pool_len || !topk || !topk_len) return CSA2_ERR_INVALID;
+    const int st = csa2_index_prefill_scan(c, q_codes, q_scales, w, q_pos0, n_q, idx_cache,
+                                           n_blocks, block_table, maxb, ws, ws_bytes, stream);
+    if (st) return st;
+    return csa2_index_prefill_finish(c, q_codes, q_scales, w, q_pos0, n_q, idx_cache, n_blocks,
+                                     block_table, maxb, pool_blocks, pool_len, topk, topk_len,
+                                     ws, ws_bytes, stream);
 }

@@ -15,9 +15,13 @@ struct SelectArgs {
     int32_t B;
     int32_t K_blk;
     int32_t k;
-    const float *pscore;  // Full: position scores [B][maxb*8]
-    const float *bscore;  // Full: block maxima [B][bstride]
-    int32_t bstride;
+    // Full: position score of (b, p) at pscore[b*ps_b + (p/8)*ps_j + p%8] and block maximum
+    // of (b, j) at bscore[b*bs_b + (j/8)*bs_g + j%8]: row-major per sequence for decode,
+    // block-major for the prefill queries
+    const float *pscore;
+    int64_t ps_b, ps_j;
+    const float *bscore;
+    int64_t bs_b, bs_g;
     const float *gmax;    // Full: group maxima (8 blocks) [B][ngmax]
     int32_t ngmax;
     const float *poolsc;    // Reindex: pool scores [B][K_blk*8]
