@@ -52,6 +52,7 @@ struct AttnArgs {
     float scale_log2;  // sm_scale * log2(e)
     float sm_scale;
     int32_t nsplit;
+    int32_t cps;       // 64-row chunks per split
     float *part_o;
     float *part_ml;
     float *out;
@@ -150,7 +151,7 @@ __global__ __launch_bounds__(kMergeThreads) void k_attn_merge(AttnArgs a) {
         a.lse[(int64_t)b * a.Hq + h] = lw > 0.0f ? a.sm_scale * M + logf(lw) : -INFINITY;
 }
 
-__global__ __launch_bounds__(kAttnThreads) void k_attn(AttnArgs a) {
+__global__ __launch_bounds__(kAttnThreads, 2) void k_attn(AttnArgs a) {
     __shared__ __align__(16) AttnShared sh;
 
     const int s = blockIdx.x, b = blockIdx.y / a.HG, hg = blockIdx.y % a.HG;
@@ -171,31 +172,7 @@ __global__ __launch_bounds__(kAttnThreads) void k_attn(AttnArgs a) {
     const int tl = max(0, min(a.topk_len[b], a.k));
     const int w0 = max(0, L - a.W), nwin = L - w0;
     const int r_loc = 16 * wave + c16;
-    const int rg = s * kAttnRows + r_loc;
-
     const int np_b = a.swa_new ? a.new_pos[b] : -1;
-
-    // ---- locate this lane's row
-    const uint8_t *rp = nullptr;
-    bool fp8 = false, fresh = false;
-    if (rg < a.k) {
-        if (rg < tl) {
-            const int p = a.topk[(int64_t)b * a.k + rg];
-            if (p >= 0 && p < L) {
-                const int64_t phys = a.table[(int64_t)b * a.tstride + p / kBlk];
-                if (phys >= 0 && phys < a.n_blocks)
-                    rp = a.kv + phys * (kBlk * (kD / 2 + kD / 32)) + (p % kBlk) * (kD / 2 + kD / 32);
-            }
-        }
-    } else {
-        const int wi = rg - a.k;
-        if (wi < nwin && wi < a.W) {
-            const int p = w0 + wi;
-            rp = a.swa + ((int64_t)b * a.rstride + p % a.C) * (kD + kD / 32);
-            fp8 = true;
-            fresh = p == np_b;  // the appended row: quantised here, not read back
-        }
-    }
 
     // ---- an appended row outside the attended window is still written (split 0, hg 0)
     if (a.swa_new && s == 0 && hg == 0 && np_b >= 0 && !(np_b >= w0 && np_b < L && np_b - w0 < a.W) &&
@@ -203,41 +180,78 @@ __global__ __launch_bounds__(kAttnThreads) void k_attn(AttnArgs a) {
         uint8_t *dst = a.swa_out + ((int64_t)b * a.rstride + np_b % a.C) * (kD + kD / 32);
         quant_fp8(a.swa_new + (int64_t)b * kD + 32 * tid, dst + 32 * tid, dst + kD + tid);
     }
-    const bool valid = rp != nullptr;
-    if (tid == 0) {
-        sh.any_valid = 0;
-        sh.has_fresh = 0;
+
+    // running softmax state of heads 4*g4 + j (j = 0..3): max M (score units), sum l, and
+    // the unnormalised output of this wave's 8 column tiles
+    float M[4], lsum[4];
+    f32x4_t o[8];
+#pragma unroll
+    for (int j = 0; j < 4; j++) {
+        M[j] = -INFINITY;
+        lsum[j] = 0.0f;
     }
-    __syncthreads();
-    if (valid) sh.any_valid = 1;
-    if (fresh) sh.has_fresh = 1;
-    __syncthreads();
-    if (sh.has_fresh) {
-        // the appended row: 16 threads quantise one group each into LDS (and, for the first
-        // head group, into the ring); its lanes then read it from LDS
-        if (tid < kD / 32) {
-            float v[32];
-            load_group(a.swa_new + (int64_t)b * kD + 32 * tid, v);
-            uint32_t w[8];
-            const uint32_t sc = quant_fp8_regs(v, w);
-            uint4 *d4 = reinterpret_cast<uint4 *>(sh.fresh_row + 32 * tid);
-            d4[0] = make_uint4(w[0], w[1], w[2], w[3]);
-            d4[1] = make_uint4(w[4], w[5], w[6], w[7]);
-            sh.fresh_row[kD + tid] = (uint8_t)sc;
-            if (hg == 0) {
-                uint8_t *dst = a.swa_out + ((int64_t)b * a.rstride + np_b % a.C) * (kD + kD / 32);
-                uint4 *g4p = reinterpret_cast<uint4 *>(dst + 32 * tid);
-                g4p[0] = d4[0];
-                g4p[1] = d4[1];
-                dst[kD + tid] = (uint8_t)sc;
+#pragma unroll
+    for (int n = 0; n < 8; n++) o[n] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+
+    const int nchunk = attn_splits(a.k, a.W);
+    const int c_end = min(nchunk, (s + 1) * a.cps);
+    for (int c = s * a.cps; c < c_end; c++) {
+        const int rg = c * kAttnRows + r_loc;
+        // ---- locate this lane's row
+        const uint8_t *rp = nullptr;
+        bool fp8 = false, fresh = false;
+        if (rg < a.k) {
+            if (rg < tl) {
+                const int p = a.topk[(int64_t)b * a.k + rg];
+                if (p >= 0 && p < L) {
+                    const int64_t phys = a.table[(int64_t)b * a.tstride + p / kBlk];
+                    if (phys >= 0 && phys < a.n_blocks)
+                        rp = a.kv + phys * (kBlk * (kD / 2 + kD / 32)) + (p % kBlk) * (kD / 2 + kD / 32);
+                }
+            }
+        } else {
+            const int wi = rg - a.k;
+            if (wi < nwin && wi < a.W) {
+                const int p = w0 + wi;
+                rp = a.swa + ((int64_t)b * a.rstride + p % a.C) * (kD + kD / 32);
+                fp8 = true;
+                fresh = p == np_b;  // the appended row: quantised here, not read back
             }
         }
+        const bool valid = rp != nullptr;
+        if (tid == 0) {
+            sh.any_valid = 0;
+            sh.has_fresh = 0;
+        }
+        __syncthreads();  // also: the previous chunk is done with V^T, P and the reductions
+        if (valid) sh.any_valid = 1;
+        if (fresh) sh.has_fresh = 1;
         __syncthreads();
-        if (fresh) rp = sh.fresh_row;
-    }
-    const int64_t pbase = ((int64_t)b * a.nsplit + s) * a.Hq + hg * 16;
+        if (!sh.any_valid) continue;  // uniform
+        if (sh.has_fresh) {
+            // the appended row: 16 threads quantise one group each into LDS (and, for the
+            // first head group, into the ring); its lanes then read it from LDS
+            if (tid < kD / 32) {
+                float v[32];
+                load_group(a.swa_new + (int64_t)b * kD + 32 * tid, v);
+                uint32_t w[8];
+                const uint32_t sc = quant_fp8_regs(v, w);
+                uint4 *d4 = reinterpret_cast<uint4 *>(sh.fresh_row + 32 * tid);
+                d4[0] = make_uint4(w[0], w[1], w[2], w[3]);
+                d4[1] = make_uint4(w[4], w[5], w[6], w[7]);
+                sh.fresh_row[kD + tid] = (uint8_t)sc;
+                if (hg == 0) {
+                    uint8_t *dst = a.swa_out + ((int64_t)b * a.rstride + np_b % a.C) * (kD + kD / 32);
+                    uint4 *g4p = reinterpret_cast<uint4 *>(dst + 32 * tid);
+                    g4p[0] = d4[0];
+                    g4p[1] = d4[1];
+                    dst[kD + tid] = (uint8_t)sc;
+                }
+            }
+            __syncthreads();
+            if (fresh) rp = sh.fresh_row;
+        }
 
-    if (sh.any_valid) {
         // ---- gather + exact conversion to bf16: kb[t] = dims g4*128 + 8t .. +8 of the row
         bf16x8_t kb[16];
         if (valid && !fp8) {
@@ -281,14 +295,13 @@ __global__ __launch_bounds__(kAttnThreads) void k_attn(AttnArgs a) {
         for (int t = 0; t < 16; t++)
 #pragma unroll
             for (int i = 0; i < 8; i++) sh.vt[vt_index(g4 * 128 + 8 * t + i, r_loc)] = kb[t][i];
-        __syncthreads();  // V^T is in LDS
 
         // ---- S = Q K^T for this wave's 16 rows and the 16 heads
         f32x4_t acc = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
         for (int t = 0; t < 16; t++) acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[t], kb[t], acc, 0, 0, 0);
         // lane holds S[head 4*g4 + j][row c16 of this wave]
-        float sv[4], mx[4];
+        float sv[4];
 #pragma unroll
         for (int j = 0; j < 4; j++) {
             sv[j] = valid ? acc[j] : -INFINITY;
@@ -297,39 +310,36 @@ __global__ __launch_bounds__(kAttnThreads) void k_attn(AttnArgs a) {
             m = fmaxf(m, __shfl_xor(m, 2, kWave));
             m = fmaxf(m, __shfl_xor(m, 4, kWave));
             m = fmaxf(m, __shfl_xor(m, 8, kWave));
-            mx[j] = m;
+            if (c16 == 0) sh.red_m[wave][4 * g4 + j] = m;
         }
-        if (c16 == 0)
-#pragma unroll
-            for (int j = 0; j < 4; j++) sh.red_m[wave][4 * g4 + j] = mx[j];
-        __syncthreads();
-        float pv[4], ls[4];
+        __syncthreads();  // V^T and the row maxima are in LDS
+        // new running maxima (finite: the chunk has a valid row, so every head has a finite
+        // score), rescale factors, probabilities of this lane's row
+        float alpha[4];
 #pragma unroll
         for (int j = 0; j < 4; j++) {
             const int h = 4 * g4 + j;
-            const float M = fmaxf(fmaxf(sh.red_m[0][h], sh.red_m[1][h]), fmaxf(sh.red_m[2][h], sh.red_m[3][h]));
-            pv[j] = valid ? exp2f((sv[j] - M) * a.scale_log2) : 0.0f;
-            float l = pv[j];
+            const float mc = fmaxf(fmaxf(sh.red_m[0][h], sh.red_m[1][h]), fmaxf(sh.red_m[2][h], sh.red_m[3][h]));
+            const float mn = fmaxf(M[j], mc);
+            alpha[j] = exp2f((M[j] - mn) * a.scale_log2);  // 0 for the first chunk
+            M[j] = mn;
+            const float pv = valid ? exp2f((sv[j] - mn) * a.scale_log2) : 0.0f;
+            float l = pv;
             l += __shfl_xor(l, 1, kWave);
             l += __shfl_xor(l, 2, kWave);
             l += __shfl_xor(l, 4, kWave);
             l += __shfl_xor(l, 8, kWave);
-            ls[j] = l;
-            sh.ptile[h * kPStride + r_loc] = pv[j];
+            if (c16 == 0) sh.red_l[wave][h] = l;
+            sh.ptile[h * kPStride + r_loc] = pv;
         }
-        if (c16 == 0)
+        __syncthreads();  // P and the row sums are in LDS
 #pragma unroll
-            for (int j = 0; j < 4; j++) sh.red_l[wave][4 * g4 + j] = ls[j];
-        __syncthreads();
-        if (tid < 16) {
-            const int h = tid;
-            const float M = fmaxf(fmaxf(sh.red_m[0][h], sh.red_m[1][h]), fmaxf(sh.red_m[2][h], sh.red_m[3][h]));
-            const float l = sh.red_l[0][h] + sh.red_l[1][h] + sh.red_l[2][h] + sh.red_l[3][h];
-            a.part_ml[2 * (pbase + h)] = M;
-            a.part_ml[2 * (pbase + h) + 1] = l;
+        for (int j = 0; j < 4; j++) {
+            const int h = 4 * g4 + j;
+            lsum[j] = lsum[j] * alpha[j] + ((sh.red_l[0][h] + sh.red_l[1][h]) + (sh.red_l[2][h] + sh.red_l[3][h]));
         }
 
-        // ---- O = P V for this wave's 8 column tiles (128 dims)
+        // ---- O = alpha O + P V for this wave's 8 column tiles (128 dims)
         bf16x8_t ph[2], plo[2];
 #pragma unroll
         for (int ks = 0; ks < 2; ks++) {
@@ -343,30 +353,58 @@ __global__ __launch_bounds__(kAttnThreads) void k_attn(AttnArgs a) {
                 plo[ks][i] = (__bf16)(f[i] - (float)hi);
             }
         }
-        float *po = a.part_o + pbase * kD;
 #pragma unroll
         for (int n = 0; n < 8; n++) {
             const int nt = 8 * wave + n;
             const int d = 16 * nt + c16;
-            f32x4_t o = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+            for (int j = 0; j < 4; j++) o[n][j] *= alpha[j];
 #pragma unroll
             for (int ks = 0; ks < 2; ks++) {
                 const int chunk = 4 * ks + g4;
                 const bf16x8_t vb = *reinterpret_cast<const bf16x8_t *>(
                     &sh.vt[d * 64 + (((chunk ^ (d >> 1)) & 7) << 3)]);
-                o = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ph[ks], vb, o, 0, 0, 0);
-                o = __builtin_amdgcn_mfma_f32_16x16x32_bf16(plo[ks], vb, o, 0, 0, 0);
+                o[n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ph[ks], vb, o[n], 0, 0, 0);
+                o[n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(plo[ks], vb, o[n], 0, 0, 0);
             }
-#pragma unroll
-            for (int j = 0; j < 4; j++) po[(4 * g4 + j) * kD + d] = o[j];
-        }
-    } else {
-        for (int h = tid; h < 16; h += kAttnThreads) {
-            a.part_ml[2 * (pbase + h)] = -INFINITY;
-            a.part_ml[2 * (pbase + h) + 1] = 0.0f;
         }
     }
 
+    // ---- one split: normalised output and log-sum-exp; several: the partial state
+    if (a.nsplit == 1) {
+#pragma unroll
+        for (int n = 0; n < 8; n++) {
+            const int d = 16 * (8 * wave + n) + c16;
+#pragma unroll
+            for (int j = 0; j < 4; j++) {
+                const int h = hg * 16 + 4 * g4 + j;
+                a.out[((int64_t)b * a.Hq + h) * kD + d] = lsum[j] > 0.0f ? o[n][j] * (1.0f / lsum[j]) : 0.0f;
+            }
+        }
+        if (wave == 0 && c16 == 0)
+#pragma unroll
+            for (int j = 0; j < 4; j++)
+                a.lse[(int64_t)b * a.Hq + hg * 16 + 4 * g4 + j] =
+                    lsum[j] > 0.0f ? a.sm_scale * M[j] + logf(lsum[j]) : -INFINITY;
+    } else {
+        const int64_t pbase = ((int64_t)b * a.nsplit + s) * a.Hq + hg * 16;
+        if (wave == 0 && c16 == 0)
+#pragma unroll
+            for (int j = 0; j < 4; j++) {
+                const int64_t i = pbase + 4 * g4 + j;
+                a.part_ml[2 * i] = lsum[j] > 0.0f ? M[j] : -INFINITY;
+                a.part_ml[2 * i + 1] = lsum[j];
+            }
+        if (lsum[0] > 0.0f || lsum[1] > 0.0f || lsum[2] > 0.0f || lsum[3] > 0.0f) {
+            float *po = a.part_o + pbase * kD;
+#pragma unroll
+            for (int n = 0; n < 8; n++) {
+                const int d = 16 * (8 * wave + n) + c16;
+#pragma unroll
+                for (int j = 0; j < 4; j++) po[(4 * g4 + j) * kD + d] = o[n][j];
+            }
+        }
+    }
 }
 
 }  // namespace csa2
@@ -388,8 +426,9 @@ int sparse_attn(const csa2_config *c, const float *swa_new, const int32_t *new_p
     if (c->swa_window > 0 && (!swa_cache || C < c->swa_window)) return CSA2_ERR_INVALID;
     if (swa_new && (!new_pos || !swa_out || C <= 0)) return CSA2_ERR_INVALID;
     if (c->kv_dim != kD || c->n_q_heads % 16 || c->n_q_heads > 128) return CSA2_ERR_UNSUPPORTED;
-    const int nsplit = attn_splits(c->topk, c->swa_window);
-    if (nsplit > kMaxSplits) return CSA2_ERR_UNSUPPORTED;
+    if (attn_splits(c->topk, c->swa_window) > kMaxSplits) return CSA2_ERR_UNSUPPORTED;
+    const AttnPlan plan = attn_plan(batch, c->n_q_heads, c->topk, c->swa_window);
+    const int nsplit = plan.nsplit;
     const WsAttn wl = ws_attn(batch, c->n_q_heads, c->kv_dim, nsplit);
     if (ws_bytes < wl.total) return CSA2_ERR_WORKSPACE;
     if (batch == 0) return CSA2_OK;
@@ -415,6 +454,7 @@ int sparse_attn(const csa2_config *c, const float *swa_new, const int32_t *new_p
     a.sm_scale = c->sm_scale;
     a.scale_log2 = c->sm_scale * 1.4426950408889634f;
     a.nsplit = nsplit;
+    a.cps = plan.cps;
     a.part_o = (float *)((uint8_t *)ws + wl.part_o);
     a.part_ml = (float *)((uint8_t *)ws + wl.part_ml);
     a.out = out;
@@ -423,7 +463,7 @@ int sparse_attn(const csa2_config *c, const float *swa_new, const int32_t *new_p
     a.new_pos = new_pos;
     a.swa_out = swa_out;
     k_attn<<<dim3(nsplit, batch * a.HG), kAttnThreads, 0, stream>>>(a);
-    k_attn_merge<<<dim3(c->n_q_heads, batch), kMergeThreads, 0, stream>>>(a);
+    if (nsplit > 1) k_attn_merge<<<dim3(c->n_q_heads, batch), kMergeThreads, 0, stream>>>(a);
     return hipGetLastError() == hipSuccess ? CSA2_OK : CSA2_ERR_HIP;
 }
 

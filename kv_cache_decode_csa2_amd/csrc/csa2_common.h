@@ -70,9 +70,29 @@ struct WsAttn {
     size_t part_o, part_ml, total;
 };
 __host__ __device__ inline int attn_splits(int k, int W) { return (k + W + kAttnRows - 1) / kAttnRows; }
+
+// Row chunks of 64 per workgroup: enough workgroups (sequences x head groups x splits) to
+// fill the chip, one split per sequence when the batch alone does.
+struct AttnPlan {
+    int nsplit, cps;  // splits, chunks per split
+};
+__host__ __device__ inline AttnPlan attn_plan(int B, int Hq, int k, int W) {
+    const int nchunk = attn_splits(k, W);
+    const int groups = (B > 0 ? B : 1) * (Hq / 16 > 0 ? Hq / 16 : 1);
+    int ns = (1024 + groups - 1) / groups;
+    ns = ns < 1 ? 1 : (ns > nchunk ? nchunk : ns);
+    const int cps = (nchunk + ns - 1) / ns;
+    return AttnPlan{(nchunk + cps - 1) / cps, cps};
+}
+
 __host__ __device__ inline WsAttn ws_attn(int B, int Hq, int D, int nsplit) {
     WsAttn w;
     size_t o = 0;
+    if (nsplit <= 1) {  // one split: the kernel writes the outputs, no partials
+        w.part_o = w.part_ml = 0;
+        w.total = 256;
+        return w;
+    }
     w.part_o = o;  o = align256(o + sizeof(float) * (size_t)B * nsplit * Hq * D);
     w.part_ml = o; o = align256(o + sizeof(float) * 2 * (size_t)B * nsplit * Hq);
     w.total = o;
