@@ -46,6 +46,10 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--eager", action="store_true", help="no HIP graph")
+    ap.add_argument("--counters", action="store_true",
+                    help="for rocprofv3 --pmc: a few eager launches of the dominant kernel, then a "
+                         "device-to-device copy of --calib-mb MiB (counter calibration); no timing")
+    ap.add_argument("--calib-mb", type=int, default=512)
     return ap.parse_args()
 
 
@@ -195,8 +199,24 @@ MFMA_FP4_PEAK_TFLOPS = 10100.0
 ALU_PEAK_TOPS = 256 * 64 * 2.4e9 / 1e12  # fp32 lane-instructions/s without packed math
 
 
+def calibration_copy(mb):
+    """A plain device copy of known size (mb MiB read, mb MiB written) for counter scaling."""
+    src = torch.ones(mb << 18, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    log(f"calibration copy: {mb} MiB")
+
+
 def main_prefill(a, wl):
     bench = PrefillBench(wl)
+    if a.counters:
+        for _ in range(3):
+            bench.scan()
+        torch.cuda.synchronize()
+        calibration_copy(a.calib_mb)
+        return
     layout = bench.k.csa2_layout(bench.cfg)
     pw = prefill_work(wl, layout)
     graph = None if a.eager else capture(lambda: bench.step())
@@ -206,6 +226,9 @@ def main_prefill(a, wl):
     ms = timed(step, steps)
     value = bench.n_q / (ms / 1e3)
     log(f"prefill step {ms:.3f} ms -> {value:.0f} query-tokens/s")
+    import hashlib
+    src = open(os.path.join(ROOT, "kv_cache_decode_csa2_amd", "csrc", "csa2_prefill.hip"), "rb").read()
+    traffic = traffic_for(hashlib.sha256(src).hexdigest(), "prefill_counters.json")
     reps = 5
     sg = capture(lambda: [bench.scan() for _ in range(reps)])
     timed(lambda i: sg.replay(), 1)
@@ -230,7 +253,7 @@ def main_prefill(a, wl):
                    "indexer": f"{wl.H_I}x{wl.d_I} fp4", "pool_blocks": wl.K_blk, "topk": wl.k,
                    "q_heads": wl.H_q, "window": wl.W, "graph": graph is not None},
         "roofline": {"bound": bound, "achieved": round(ach, 2), "peak": peak, "unit": unit,
-                     "frac": round(fr[bound], 4), "traffic": None, "kernel": "k_prefill",
+                     "frac": round(fr[bound], 4), "traffic": traffic, "kernel": "k_prefill",
                      "kernel_us": round(scan_ms * 1e3, 2),
                      "fractions": {k_: round(v, 4) for k_, v in fr.items()}, "work": pw},
         "cpu_baseline": None,
@@ -316,8 +339,10 @@ def cpu_baseline(wl, seconds):
                        f"(all {sum(wl.ctx)} positions scanned per Full layer), {el:.1f} s wall")
 
 
-def traffic_for(kernel_src_hash):
-    path = os.path.join(ROOT, "profiles", "scan_long_1m_counters.json")
+def traffic_for(kernel_src_hash, name="scan_long_1m_counters.json"):
+    """HBM bytes per launch measured by the counter runs recorded in profiles/<name>, if they
+    were taken on the current kernel source (else None)."""
+    path = os.path.join(ROOT, "profiles", name)
     try:
         with open(path) as f:
             d = json.load(f)
@@ -342,6 +367,12 @@ def main():
     if wl.n_q:
         return main_prefill(a, wl)
     bench = Bench(wl, a.replicas)
+    if a.counters:
+        for i in range(3):
+            bench.scan(i % bench.R)
+        torch.cuda.synchronize()
+        calibration_copy(a.calib_mb)
+        return
     layout = bench.k.csa2_layout(bench.cfg)
     ab = algorithmic_bytes(wl, layout)
     R = bench.R
