@@ -280,15 +280,80 @@ struct KeyRegs {
     uint32_t ks;
 };
 
+// DPP max of x with the lane selected by `ctrl` (lanes outside row_mask keep x).
+template <int CTRL, int ROW_MASK = 0xf>
+__device__ __forceinline__ float dpp_max(float x) {
+    const int y = __builtin_amdgcn_update_dpp(__float_as_int(x), __float_as_int(x), CTRL, ROW_MASK, 0xf, false);
+    return __builtin_elementwise_maximum(x, __int_as_float(y));
+}
+
+// Maximum over the 8*H lanes of a block (the H lanes of a position hold the same value);
+// the block's last lane (lane % (8H) == 8H - 1) holds it.
+template <int H>
+__device__ __forceinline__ float block_max_lanes(float m) {
+    if constexpr (H == 1) {
+        m = dpp_max<0xB1>(m);          // quad [1,0,3,2]
+        m = dpp_max<0x4E>(m);          // quad [2,3,0,1]
+        m = dpp_max<0x141>(m);         // row_half_mirror
+    } else if constexpr (H == 2) {
+        m = dpp_max<0x4E>(m);
+        m = dpp_max<0x141>(m);
+        m = dpp_max<0x140>(m);         // row_mirror
+    } else if constexpr (H == 4) {
+        m = dpp_max<0x141>(m);
+        m = dpp_max<0x140>(m);
+        m = dpp_max<0x142, 0xa>(m);    // row_bcast:15 into rows 1, 3
+    } else {
+        m = dpp_max<0x140>(m);
+        m = dpp_max<0x142, 0xa>(m);
+        m = dpp_max<0x143, 0xc>(m);    // row_bcast:31 into rows 2, 3
+    }
+    return m;
+}
+
+// Maximum over the blocks' last lanes into lane 63.
+template <int H>
+__device__ __forceinline__ float blocks_to_lane63(float m) {
+    if constexpr (H == 1) m = dpp_max<0x140>(m);
+    if constexpr (H <= 2) m = dpp_max<0x142, 0xa>(m);
+    if constexpr (H <= 4) m = dpp_max<0x143, 0xc>(m);
+    return m;
+}
+
+// Target of stores a lane has nothing to write (so every step issues the same stores and the
+// loads of the next step never wait for them); its contents are never read.  Every wave of
+// a scan owns 4 x 64 floats of it, so these stores never contend for one cache line.
+__device__ float g_junk[kScanGridMax * kScanWaves * 4 * kWave];
+
+// Uniform load through the scalar data cache (read-only data; waits count on lgkmcnt, so they
+// never wait for the vector loads in flight).
+template <class T>
+__device__ __forceinline__ T sload(const T *p, int64_t i) {
+    return ((const __attribute__((address_space(4))) T *)(uintptr_t)p)[i];
+}
+
+// Per-step block bookkeeping of one wave (wave-uniform): the BPW logical blocks of step k and
+// their physical blocks (-1: none).
+template <int BPW>
+struct StepMeta {
+    int b;        // sequence
+    int e0;       // entry index (block or pool entry) of the step's first block
+    int j[BPW];   // logical blocks
+    int ph[BPW];  // physical blocks
+};
+
 // One wave processes a contiguous range of items; an item is 8 consecutive blocks (scan)
 // or 8 consecutive pool entries (rescore) of one sequence, BPW blocks per step, lane =
-// (position in step) * H + head.  Software pipeline per step k: the keys of step k+1 and
-// the block-table entry of step k+2 (and, rescoring, the pool entry of step k+3) are in
-// flight while step k is computed.  Loads never branch: an absent block reads physical
-// block 0 and its positions are masked.  OFF32: every key byte lies within 4 GiB of the
-// cache base, so addresses are a scalar base plus a 32-bit lane offset.
+// (position in step) * H + head.  Software pipeline per step k: the keys of step k+1 and the
+// block-table entries of step k+2 (rescoring: the pool entries of step k+3) are in flight
+// while step k is computed.  Block-table and pool entries are uniform per step and come
+// through scalar loads; every step issues the same vector stores (lanes without output
+// write to g_junk), so the wait for a step's keys never covers the stores or the next
+// step's loads.  Loads never branch: an absent block reads physical block 0 and its
+// positions are masked.  OFF32: every key byte lies within 4 GiB of the cache base, so
+// addresses are a scalar base plus a 32-bit lane offset.
 template <int H, int G, bool RESCORE, bool OFF32>
-__global__ __launch_bounds__(kScanThreads) void k_scan(ScanArgs a) {
+__global__ __launch_bounds__(kScanThreads, G == 4 ? 2 : 4) void k_scan(ScanArgs a) {
     constexpr int BPW = 8 / H;                         // blocks per wave step
     constexpr int NSTEP = kItemBlocks / BPW;           // steps per item
     constexpr int CODES = kBlk * H * 16 * G;
@@ -297,124 +362,187 @@ __global__ __launch_bounds__(kScanThreads) void k_scan(ScanArgs a) {
     __shared__ __align__(16) uint32_t sh_scan[kScanWaves];
     int32_t *sh_prefix = sh_dyn, *sh_len = sh_dyn + a.B + 1;
 
-    const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
+    const int lane = threadIdx.x & (kWave - 1);
+    const int wave = __builtin_amdgcn_readfirstlane((int)threadIdx.x / kWave);
     const int h = lane % H, pw = lane / H, bw = pw / kBlk, slot = pw % kBlk;
     for (int b = threadIdx.x; b < a.B; b += kScanThreads) sh_len[b] = clamp_len(a.ctx_len[b], a.maxb);
-    const int total = build_item_prefix<RESCORE>(a, sh_prefix, sh_scan);
+    const int total = __builtin_amdgcn_readfirstlane(build_item_prefix<RESCORE>(a, sh_prefix, sh_scan));
     const int nwaves = (int)gridDim.x * kScanWaves;
     const int gw = (int)blockIdx.x * kScanWaves + wave;
+    // Items of a wave: one sequence -> items gw, gw + nwaves, ... (all resident waves read
+    // one contiguous window of the cache at a time, spread over every HBM channel);
+    // several sequences -> a contiguous range, so each wave meets few sequences.
+    const bool inter = a.B == 1;
     const int per = (total + nwaves - 1) / nwaves;
-    const int it_begin = gw * per, it_end = min(total, it_begin + per);
+    const int it_begin = inter ? gw : gw * per;
+    const int it_end = inter ? total : min(total, it_begin + per);
     if (it_begin >= it_end) return;
-    const int nsteps = (it_end - it_begin) * NSTEP;
+    const int nsteps = inter ? (total - gw + nwaves - 1) / nwaves * NSTEP : (it_end - it_begin) * NSTEP;
     const uint32_t lane_off = (uint32_t)((slot * H + h) * 16);
-    const uint32_t sc_off = (uint32_t)(CODES + (slot * H + h) * G);
+    // the lane's G scale bytes, read as the aligned dword that holds them (blocks are
+    // multiples of 8 bytes) and shifted where they are used, so that nothing in the loading
+    // step consumes the value
+    const uint32_t sc_byte = (uint32_t)(CODES + (slot * H + h) * G);
+    const uint32_t sc_off = sc_byte & ~3u, sc_sh = 8u * (sc_byte & 3u);
+    float *junk = g_junk + (size_t)gw * 4 * kWave + lane;
 
-    // step k -> (sequence, entry index: block (scan) or pool entry (rescore))
-    auto step_pos = [&](int k, int &b, int &e) {
-        const int it = it_begin + k / NSTEP;
-        b = a.B == 1 ? 0 : seq_of_item(sh_prefix, a.B, it);
-        e = (it - sh_prefix[b]) * kItemBlocks + (k % NSTEP) * BPW + bw;
+    constexpr int PPS = kBlk * BPW;                    // positions per step
+    constexpr int STEPS = NSTEP >= 4 ? NSTEP : 4;      // steps per loop iteration (whole items)
+    // gather sources: position l of an item is computed in lane (l % PPS) * H of step l / PPS;
+    // block i of an item ends in lane (i % BPW + 1) * 8H - 1 of step i / BPW
+    const int src_p = (lane % PPS) * H;
+    const int src_b = ((lane % BPW) + 1) * kBlk * H - 1;
+
+    auto lane_sel = [&](const int (&v)[BPW]) -> int {
+        int r = v[0];
+#pragma unroll
+        for (int w = 1; w < BPW; w++) r = bw == w ? v[w] : r;
+        return r;
     };
-    // logical block of step k (-1: none).  Rescoring reads it from the pool.
-    auto block_of = [&](int k) -> int {
-        if (k >= nsteps) return -1;
-        int b, e;
-        step_pos(k, b, e);
-        const int nb = (sh_len[b] + kBlk - 1) / kBlk;
-        int j = e;
-        if (RESCORE) {
-            const int n_ent = max(0, min(a.pool_len[b], a.K_blk));
-            j = e < n_ent ? a.pool[(int64_t)b * a.K_blk + e] : -1;
-        }
-        return (j >= 0 && j < nb) ? j : -1;
-    };
-    auto phys_of = [&](int k, int j) -> int {  // physical block of step k (-1: none)
-        if (k >= nsteps || j < 0) return -1;
-        int b, e;
-        step_pos(k, b, e);
-        const int32_t ph = a.table[(int64_t)b * a.maxb + j];
-        return (ph >= 0 && ph < a.n_blocks) ? ph : -1;
-    };
-    auto load_keys = [&](int ph, KeyRegs<G> &kr) {
+    auto load_keys = [&](const StepMeta<BPW> &m, KeyRegs<G> &kr) {
+        const int ph = lane_sel(m.ph);
         const uint32_t p = (uint32_t)(ph >= 0 ? ph : 0);
         if constexpr (OFF32) {
             const uint32_t base = p * (uint32_t)BYTES;
 #pragma unroll
             for (int g = 0; g < G; g++)
                 kr.kc[g] = *reinterpret_cast<const uint4 *>(a.idx_cache + (base + lane_off + (uint32_t)(g * kBlk * H * 16)));
-            kr.ks = load_scales<G>(a.idx_cache + (base + sc_off));
+            kr.ks = *reinterpret_cast<const uint32_t *>(a.idx_cache + (base + sc_off));
         } else {
             const uint8_t *bp = a.idx_cache + (int64_t)p * BYTES;
 #pragma unroll
             for (int g = 0; g < G; g++)
                 kr.kc[g] = *reinterpret_cast<const uint4 *>(bp + lane_off + g * kBlk * H * 16);
-            kr.ks = load_scales<G>(bp + sc_off);
+            kr.ks = *reinterpret_cast<const uint32_t *>(bp + sc_off);
         }
     };
-
     Query<H, G> Q;
-    int qb = -1;
     float gm = -INFINITY;
-    // pipeline: logical blocks of steps k .. k+3, physical blocks of steps k, k+1
-    int j0 = block_of(0), j1 = block_of(1), j2 = block_of(2), j3 = RESCORE ? block_of(3) : -1;
-    int ph0 = phys_of(0, j0), ph1 = phys_of(1, j1);
-    KeyRegs<G> kA, kB;
-    load_keys(ph0, kA);
-    auto body = [&](int k, KeyRegs<G> &cur, KeyRegs<G> &nxt) {
-        load_keys(ph1, nxt);
-        const int ph2 = phys_of(k + 2, j2);
-        const int j4 = RESCORE ? block_of(k + 4) : -1;
-        int b, e;
-        step_pos(k, b, e);
-        if (b != qb) {
-            qb = b;
-            load_query<H, G>(Q, a.q_codes + (size_t)b * H * 16 * G, a.q_scales + (size_t)b * H * G,
-                             a.w + (size_t)b * H, h);
-        }
-        const int L = sh_len[b];
-        const float r = head_relu<H, G>(Q, cur.kc, cur.ks);
-        const float s = combine_heads_dpp<H, G>(Q, r, lane);
-        const bool vis = ph0 >= 0 && j0 * kBlk + slot < L;
-        if (RESCORE) {
-            const int n_ent = max(0, min(a.pool_len[b], a.K_blk));
-            float m = vis ? s : -INFINITY;
-            m = fmax_sel(m, __shfl_xor(m, H, kWave));
-            m = fmax_sel(m, __shfl_xor(m, 2 * H, kWave));
-            m = fmax_sel(m, __shfl_xor(m, 4 * H, kWave));
-            if (e < n_ent && h == 0) {
-                a.poolsc[((int64_t)b * a.K_blk + e) * kBlk + slot] = vis ? s : -INFINITY;
-                if (slot == 0) a.poolbmax[(int64_t)b * a.K_blk + e] = m;
-            }
-        } else {
-            const int nb = (L + kBlk - 1) / kBlk;
-            float m = vis ? s : -INFINITY;
-            m = fmax_sel(m, __shfl_xor(m, H, kWave));
-            m = fmax_sel(m, __shfl_xor(m, 2 * H, kWave));
-            m = fmax_sel(m, __shfl_xor(m, 4 * H, kWave));
-            if (vis && h == 0 && a.pscore) a.pscore[(int64_t)b * a.maxb * kBlk + (int64_t)e * kBlk + slot] = s;
-            if (e < nb && slot == 0 && h == 0 && a.bscore) a.bscore[(int64_t)b * a.bstride + e] = m;
-            gm = fmax_sel(gm, m);
-            if (k % NSTEP == NSTEP - 1) {
-#pragma unroll
-                for (int o = kBlk * H; o < kWave; o <<= 1) gm = fmax_sel(gm, __shfl_xor(gm, o, kWave));
-                if (lane == 0 && a.gmax) a.gmax[(int64_t)b * a.ngmax + e / kItemBlocks] = gm;
-                gm = -INFINITY;
-            }
-        }
-        j0 = j1;
-        j1 = j2;
-        j2 = RESCORE ? j3 : block_of(k + 3);
-        j3 = j4;
-        ph0 = ph1;
-        ph1 = ph2;
-    };
+
+    // The wave's steps split into segments of one sequence each (items are 8-aligned, so a
+    // segment starts at an item boundary).  Per segment: the query, row bases and lengths;
+    // per step only an entry index that advances by BPW.
+    int cur_b = 0;
     int k = 0;
-    for (; k + 1 < nsteps; k += 2) {
-        body(k, kA, kB);
-        body(k + 1, kB, kA);
+    while (k < nsteps) {
+        const int it0 = it_begin + k / NSTEP;
+        if (a.B > 1)
+            while (cur_b + 1 < a.B && __builtin_amdgcn_readfirstlane(sh_prefix[cur_b + 1]) <= it0) cur_b++;
+        const int b = cur_b;
+        const int kend = b + 1 < a.B
+            ? min(nsteps, (__builtin_amdgcn_readfirstlane(sh_prefix[b + 1]) - it_begin) * NSTEP)
+            : nsteps;
+        const int kseg = k;
+        const int e_start = (it0 - __builtin_amdgcn_readfirstlane(sh_prefix[b])) * kItemBlocks;
+        const int L = __builtin_amdgcn_readfirstlane(sh_len[b]);
+        const int nb = (L + kBlk - 1) / kBlk;
+        const int32_t *table_row = a.table + (int64_t)b * a.maxb;
+        const int32_t *pool_row = RESCORE ? a.pool + (int64_t)b * a.K_blk : nullptr;
+        const int n_ent = RESCORE ? max(0, min(sload(a.pool_len, b), a.K_blk)) : 0;
+
+        // entries of step k2 of this segment (-1 past its end)
+        auto meta_entries = [&](int k2, StepMeta<BPW> &m) {
+            m.e0 = inter ? (it_begin + (k2 / NSTEP) * nwaves) * kItemBlocks + (k2 % NSTEP) * BPW
+                         : e_start + (k2 - kseg) * BPW;
+#pragma unroll
+            for (int w = 0; w < BPW; w++) {
+                m.ph[w] = -1;
+                const int e = m.e0 + w;
+                int jv = -1;
+                if (k2 < kend) {
+                    if (RESCORE) jv = e < n_ent ? sload(pool_row, e) : -1;
+                    else jv = e;
+                }
+                m.j[w] = (jv >= 0 && jv < nb) ? jv : -1;
+            }
+        };
+        auto meta_phys = [&](StepMeta<BPW> &m) {
+#pragma unroll
+            for (int w = 0; w < BPW; w++) {
+                const int32_t ph = m.j[w] >= 0 ? sload(table_row, m.j[w]) : -1;
+                m.ph[w] = (ph >= 0 && ph < a.n_blocks) ? ph : -1;
+            }
+        };
+
+        load_query<H, G>(Q, a.q_codes + (size_t)b * H * 16 * G, a.q_scales + (size_t)b * H * G,
+                         a.w + (size_t)b * H, h);
+        // pipeline, two steps deep: the keys of steps k+1 and k+2 are in flight while step k is
+        // computed; physical blocks are known up to step k+2, entries up to step k+3
+        StepMeta<BPW> m0, m1, m2, m3;
+        meta_entries(k, m0);
+        meta_phys(m0);
+        meta_entries(k + 1, m1);
+        meta_phys(m1);
+        meta_entries(k + 2, m2);
+        meta_phys(m2);
+        meta_entries(k + 3, m3);
+        KeyRegs<G> K[4];
+        load_keys(m0, K[0]);
+        load_keys(m1, K[1]);
+        // an item's two stores, once: the loop is entered with the memory operations in
+        // flight that every iteration leaves (its waits stay minimal)
+        junk[kWave] = 0.0f;
+        junk[2 * kWave] = 0.0f;
+
+        float *ps_row = RESCORE ? a.poolsc + (int64_t)b * a.K_blk * kBlk : a.pscore + (int64_t)b * a.maxb * kBlk;
+        float *pb_row = RESCORE ? a.poolbmax + (int64_t)b * a.K_blk : a.bscore + (int64_t)b * a.bstride;
+        float *pg_row = RESCORE ? nullptr : a.gmax + (int64_t)b * a.ngmax;
+        const bool ps_on = RESCORE || a.pscore, pb_on = RESCORE || a.bscore, pg_on = !RESCORE && a.gmax;
+        const int n_lim = RESCORE ? n_ent : nb;  // entries of the segment's row
+
+        // scores and block maxima of the current item, gathered so that lane l holds position
+        // l (acc_p) and lanes 0..7 the maxima of blocks 0..7 (acc_b)
+        float acc_p = 0.0f, acc_b = 0.0f;
+        auto body = [&](int k2, int si, KeyRegs<G> &cur, KeyRegs<G> &nxt2) {
+            load_keys(m2, nxt2);
+            meta_phys(m3);
+            StepMeta<BPW> m4;
+            meta_entries(k2 + 4, m4);
+            const float r = head_relu<H, G>(Q, cur.kc, cur.ks >> sc_sh);
+            const float sc = combine_heads_dpp<H, G>(Q, r, lane);
+            const int j = lane_sel(m0.j), ph = lane_sel(m0.ph);
+            const bool vis = ph >= 0 && j * kBlk + slot < L;
+            const float val = vis ? sc : -INFINITY;
+            const float m = block_max_lanes<H>(val);
+            const float vp = __shfl(val, src_p, kWave);
+            const float vb = __shfl(m, src_b, kWave);
+            acc_p = lane / PPS == si ? vp : acc_p;
+            acc_b = lane / BPW == si ? vb : acc_b;
+            if (!RESCORE) {
+                // the item's group maximum so far, in lane 63
+                gm = __builtin_elementwise_maximum(si == 0 ? -INFINITY : gm, m);
+            }
+            if (si == NSTEP - 1) {
+                // item stores: 64 position scores, 8 block maxima (+ the group maximum)
+                const int e_item = m0.e0 - (NSTEP - 1) * BPW;
+                const bool item_ok = k2 < kend;
+                const bool pos_ok = item_ok && e_item + lane / kBlk < n_lim;
+                float *ps = pos_ok && ps_on ? ps_row + (int64_t)e_item * kBlk + lane : junk;
+                float *pb = junk + kWave;
+                float vstore = acc_b;
+                if (lane < kBlk && item_ok && e_item + lane < n_lim && pb_on) pb = pb_row + e_item + lane;
+                if (!RESCORE) {
+                    const float g63 = blocks_to_lane63<H>(gm);
+                    if (lane == kWave - 1) {
+                        vstore = g63;
+                        if (item_ok && pg_on) pb = pg_row + e_item / kItemBlocks;
+                    }
+                }
+                *ps = acc_p;
+                *pb = vstore;
+            }
+            m0 = m1;
+            m1 = m2;
+            m2 = m3;
+            m3 = m4;
+        };
+        // iterations of STEPS steps (whole items); steps past the segment end are masked
+        for (; k < kend; k += STEPS) {
+#pragma unroll
+            for (int st = 0; st < STEPS; st++) body(k + st, st % NSTEP, K[st % 4], K[(st + 2) % 4]);
+        }
+        (void)ps_on;
     }
-    if (k < nsteps) body(k, kA, kB);
 }
 
 // ------------------------------------------------------------------ exact block-wide select
