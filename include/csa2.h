@@ -27,8 +27,11 @@
  *     entries that are out of range, so a bad value never reads or writes outside the
  *     buffers described here; the results for such entries are unspecified.
  *   - A workspace `ws` of at least csa2_workspace_bytes() bytes is needed by the index
- *     and attention calls (one per kind of call); neither needs initialisation.  Calls
- *     that share a workspace must not run concurrently.
+ *     and attention calls (one per kind of call).  An index workspace needs no
+ *     initialisation.  An attention workspace holds arrival counters: zero it once after
+ *     allocating it (hipMemset); every attention call leaves them at zero again, so it
+ *     must not be shared with other kinds of call.  Calls that share a workspace must
+ *     not run concurrently.
  */
 #ifndef CSA2_H
 #define CSA2_H

@@ -20,7 +20,9 @@
 //      accumulation); the same values go to LDS transposed (V^T).
 //   3. Softmax statistics per head over the 64 rows (wave shuffles + LDS).
 //   4. O = P V on MFMA with P split into bf16 hi + lo parts (error ~2^-17 relative).
-//   5. The partial (O, max, sum) goes to the workspace; k_attn_merge combines the splits.
+//   5. One split per sequence writes the outputs; with several, each writes its partial
+//      (O, max, sum) to the workspace and the last split of (sequence, head group) to
+//      arrive (an atomic counter) combines them.
 #include "csa2_quant.h"
 
 namespace csa2 {
@@ -55,6 +57,7 @@ struct AttnArgs {
     int32_t cps;       // 64-row chunks per split
     float *part_o;
     float *part_ml;
+    int32_t *count;   // [B][HG] arrivals of splits; zero between calls
     float *out;
     float *lse;
     // fused window append (null: none): row swa_new[b] (fp32, D) is quantised into ring
@@ -67,6 +70,25 @@ struct AttnArgs {
 __device__ __forceinline__ int clamp_ctx(int32_t L, int maxb) {
     const int64_t cap = (int64_t)maxb * kBlk;
     return L < 0 ? 0 : (int)(L > cap ? cap : L);
+}
+
+// Reductions over the 16 lanes of a DPP row (quad swaps, half-row and row mirrors); every
+// lane of the row receives the result.
+template <int CTRL>
+__device__ __forceinline__ float dpp_f(float x) {
+    return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), CTRL, 0xf, 0xf, false));
+}
+__device__ __forceinline__ float row16_max(float x) {
+    x = fmaxf(x, dpp_f<0xB1>(x));   // quad [1,0,3,2]
+    x = fmaxf(x, dpp_f<0x4E>(x));   // quad [2,3,0,1]
+    x = fmaxf(x, dpp_f<0x141>(x));  // row_half_mirror
+    return fmaxf(x, dpp_f<0x140>(x));  // row_mirror
+}
+__device__ __forceinline__ float row16_sum(float x) {
+    x += dpp_f<0xB1>(x);
+    x += dpp_f<0x4E>(x);
+    x += dpp_f<0x141>(x);
+    return x + dpp_f<0x140>(x);
 }
 
 __device__ __forceinline__ uint32_t word_of(const uint4 &u, int i) {
@@ -91,64 +113,75 @@ struct AttnShared {
     float ptile[16 * kPStride];
     float red_m[4][16], red_l[4][16];
     __align__(16) uint8_t fresh_row[kD + kD / 32];  // the appended window row (MXFP8)
-    int any_valid, has_fresh;
+    int any_valid, has_fresh, last;
 };
 
-// Combine the splits of (b, head h): out = sum_s 2^((m_s - M) c) O_s / sum_s 2^((m_s - M) c) l_s.
-// The split statistics go through LDS first, then every partial row loads in one batch
-// (the loop over splits is unrolled by 8).
-constexpr int kMergeThreads = 128;
+// Combine the splits of (b, head group hg), run by the last split to finish:
+// out = sum_s 2^((m_s - M) c) O_s / sum_s 2^((m_s - M) c) l_s per head, accumulated with a
+// running maximum over batches of kMergeBatch splits.  Thread (head h = tid / 16,
+// q = tid % 16) owns dims 4q + 64i (i = 0..7) of head h, so 16 threads read one partial row
+// in 256-byte runs; a batch's rows and (max, sum) pairs are all loaded before any is used.
+// An empty split's row was never written: its values are discarded by a select, which
+// keeps the loads unconditional.
+constexpr int kMergeBatch = 4;
 
-__global__ __launch_bounds__(kMergeThreads) void k_attn_merge(AttnArgs a) {
-    __shared__ float wgt[kMaxSplits];
-    __shared__ float red[kMergeThreads / kWave][2];
-    const int h = blockIdx.x, b = blockIdx.y, tid = threadIdx.x;
-    const int64_t base = (int64_t)b * a.nsplit * a.Hq;
-    float mloc = -INFINITY;
-    for (int s = tid; s < a.nsplit; s += kMergeThreads) {
-        const int64_t i = base + (int64_t)s * a.Hq + h;
-        const float m = a.part_ml[2 * i], l = a.part_ml[2 * i + 1];
-        wgt[s] = l > 0.0f ? m : -INFINITY;
-        if (l > 0.0f) mloc = fmaxf(mloc, m);
-    }
+__device__ __forceinline__ void merge_splits(const AttnArgs &a, int b, int hg) {
+    const int tid = threadIdx.x, h = tid >> 4, q = tid & 15;
+    const int64_t row0 = (int64_t)b * a.nsplit * a.Hq + hg * 16 + h;  // split 0, head h
+    const float4 *src = reinterpret_cast<const float4 *>(a.part_o + row0 * kD) + q;
+    const float2 *mlp = reinterpret_cast<const float2 *>(a.part_ml) + row0;
+    const int64_t sstride = (int64_t)a.Hq * kD / 4;  // float4s between splits
+    float4 acc[8];
 #pragma unroll
-    for (int o = 32; o > 0; o >>= 1) mloc = fmaxf(mloc, __shfl_xor(mloc, o, kWave));
-    if ((tid & (kWave - 1)) == 0) red[tid / kWave][0] = mloc;
-    __syncthreads();
-    const float M = fmaxf(red[0][0], red[1][0]);
-    float lloc = 0.0f;
-    for (int s = tid; s < a.nsplit; s += kMergeThreads) {
-        const int64_t i = base + (int64_t)s * a.Hq + h;
-        const float m = wgt[s];
-        const float e = m == -INFINITY ? 0.0f : exp2f((m - M) * a.scale_log2);
-        lloc += e * a.part_ml[2 * i + 1];
-        wgt[s] = e;
-    }
+    for (int i = 0; i < 8; i++) acc[i] = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+    float M = -INFINITY, lw = 0.0f;
+    for (int s0 = 0; s0 < a.nsplit; s0 += kMergeBatch) {
+        float2 st[kMergeBatch];
+        float4 v[kMergeBatch][8];
 #pragma unroll
-    for (int o = 32; o > 0; o >>= 1) lloc += __shfl_xor(lloc, o, kWave);
-    if ((tid & (kWave - 1)) == 0) red[tid / kWave][1] = lloc;
-    __syncthreads();
-    const float lw = red[0][1] + red[1][1];
-    float4 acc = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
-#pragma unroll 8
-    for (int s = 0; s < a.nsplit; s++) {
-        const float e = wgt[s];
-        const float4 v = reinterpret_cast<const float4 *>(a.part_o + (base + (int64_t)s * a.Hq + h) * kD)[tid];
-        if (e != 0.0f) {  // an empty split's partial row was never written
-            acc.x += e * v.x;
-            acc.y += e * v.y;
-            acc.z += e * v.z;
-            acc.w += e * v.w;
+        for (int u = 0; u < kMergeBatch; u++) {
+            const int sp = min(s0 + u, a.nsplit - 1);
+            st[u] = mlp[(int64_t)sp * a.Hq];
+#pragma unroll
+            for (int i = 0; i < 8; i++) v[u][i] = src[sp * sstride + 16 * i];
         }
+        float mu[kMergeBatch], mb = M;
+#pragma unroll
+        for (int u = 0; u < kMergeBatch; u++) {
+            mu[u] = s0 + u < a.nsplit && st[u].y > 0.0f ? st[u].x : -INFINITY;
+            mb = fmaxf(mb, mu[u]);
+        }
+        const float alpha = M == -INFINITY ? 0.0f : exp2f((M - mb) * a.scale_log2);
+        lw *= alpha;
+#pragma unroll
+        for (int i = 0; i < 8; i++) {
+            acc[i].x *= alpha;
+            acc[i].y *= alpha;
+            acc[i].z *= alpha;
+            acc[i].w *= alpha;
+        }
+#pragma unroll
+        for (int u = 0; u < kMergeBatch; u++) {
+            const bool use = mu[u] != -INFINITY;
+            const float e = use ? exp2f((mu[u] - mb) * a.scale_log2) : 0.0f;
+            lw += use ? e * st[u].y : 0.0f;
+#pragma unroll
+            for (int i = 0; i < 8; i++) {
+                acc[i].x += use ? e * v[u][i].x : 0.0f;
+                acc[i].y += use ? e * v[u][i].y : 0.0f;
+                acc[i].z += use ? e * v[u][i].z : 0.0f;
+                acc[i].w += use ? e * v[u][i].w : 0.0f;
+            }
+        }
+        M = mb;
     }
-    float4 r = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
-    if (lw > 0.0f) {
-        const float inv = 1.0f / lw;
-        r = make_float4(acc.x * inv, acc.y * inv, acc.z * inv, acc.w * inv);
-    }
-    reinterpret_cast<float4 *>(a.out + ((int64_t)b * a.Hq + h) * kD)[tid] = r;
-    if (tid == 0)
-        a.lse[(int64_t)b * a.Hq + h] = lw > 0.0f ? a.sm_scale * M + logf(lw) : -INFINITY;
+    const float inv = lw > 0.0f ? 1.0f / lw : 0.0f;
+    float4 *dst = reinterpret_cast<float4 *>(a.out + ((int64_t)b * a.Hq + hg * 16 + h) * kD) + q;
+#pragma unroll
+    for (int i = 0; i < 8; i++)
+        dst[16 * i] = make_float4(acc[i].x * inv, acc[i].y * inv, acc[i].z * inv, acc[i].w * inv);
+    if (q == 0)
+        a.lse[(int64_t)b * a.Hq + hg * 16 + h] = lw > 0.0f ? a.sm_scale * M + logf(lw) : -INFINITY;
 }
 
 __global__ __launch_bounds__(kAttnThreads, 2) void k_attn(AttnArgs a) {
@@ -305,11 +338,7 @@ __global__ __launch_bounds__(kAttnThreads, 2) void k_attn(AttnArgs a) {
 #pragma unroll
         for (int j = 0; j < 4; j++) {
             sv[j] = valid ? acc[j] : -INFINITY;
-            float m = sv[j];
-            m = fmaxf(m, __shfl_xor(m, 1, kWave));
-            m = fmaxf(m, __shfl_xor(m, 2, kWave));
-            m = fmaxf(m, __shfl_xor(m, 4, kWave));
-            m = fmaxf(m, __shfl_xor(m, 8, kWave));
+            const float m = row16_max(sv[j]);
             if (c16 == 0) sh.red_m[wave][4 * g4 + j] = m;
         }
         __syncthreads();  // V^T and the row maxima are in LDS
@@ -324,11 +353,7 @@ __global__ __launch_bounds__(kAttnThreads, 2) void k_attn(AttnArgs a) {
             alpha[j] = exp2f((M[j] - mn) * a.scale_log2);  // 0 for the first chunk
             M[j] = mn;
             const float pv = valid ? exp2f((sv[j] - mn) * a.scale_log2) : 0.0f;
-            float l = pv;
-            l += __shfl_xor(l, 1, kWave);
-            l += __shfl_xor(l, 2, kWave);
-            l += __shfl_xor(l, 4, kWave);
-            l += __shfl_xor(l, 8, kWave);
+            const float l = row16_sum(pv);
             if (c16 == 0) sh.red_l[wave][h] = l;
             sh.ptile[h * kPStride + r_loc] = pv;
         }
@@ -404,6 +429,19 @@ __global__ __launch_bounds__(kAttnThreads, 2) void k_attn(AttnArgs a) {
                 for (int j = 0; j < 4; j++) po[(4 * g4 + j) * kD + d] = o[n][j];
             }
         }
+        // The last split of (b, hg) to arrive combines them all.  Every wave's stores are
+        // ordered before the barrier; thread 0's agent-scope release then publishes them
+        // device-wide and its acquire (for the last split) covers the other splits' partials.
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+        __syncthreads();
+        int32_t *cnt = a.count + (int64_t)b * a.HG + hg;
+        if (tid == 0)
+            sh.last = __hip_atomic_fetch_add(cnt, 1, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT) ==
+                      a.nsplit - 1;
+        __syncthreads();
+        if (!sh.last) return;  // uniform
+        merge_splits(a, b, hg);
+        if (tid == 0) __hip_atomic_store(cnt, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
 }
 
@@ -457,13 +495,13 @@ int sparse_attn(const csa2_config *c, const float *swa_new, const int32_t *new_p
     a.cps = plan.cps;
     a.part_o = (float *)((uint8_t *)ws + wl.part_o);
     a.part_ml = (float *)((uint8_t *)ws + wl.part_ml);
+    a.count = (int32_t *)((uint8_t *)ws + wl.count);
     a.out = out;
     a.lse = lse;
     a.swa_new = swa_new;
     a.new_pos = new_pos;
     a.swa_out = swa_out;
     k_attn<<<dim3(nsplit, batch * a.HG), kAttnThreads, 0, stream>>>(a);
-    if (nsplit > 1) k_attn_merge<<<dim3(c->n_q_heads, batch), kMergeThreads, 0, stream>>>(a);
     return hipGetLastError() == hipSuccess ? CSA2_OK : CSA2_ERR_HIP;
 }
 

@@ -64,10 +64,11 @@ constexpr int kMaxBatch = 4096;  // sequences per index call (the scan keeps a p
 
 __host__ __device__ inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
-// Workspace of the attention call: per split partial numerators and (max, sum) pairs.
+// Workspace of the attention call: per split partial numerators and (max, sum) pairs, and
+// one arrival counter per (sequence, head group), which every call leaves at zero.
 constexpr int kAttnRows = 64;  // rows per attention workgroup
 struct WsAttn {
-    size_t part_o, part_ml, total;
+    size_t part_o, part_ml, count, total;
 };
 __host__ __device__ inline int attn_splits(int k, int W) { return (k + W + kAttnRows - 1) / kAttnRows; }
 
@@ -89,12 +90,13 @@ __host__ __device__ inline WsAttn ws_attn(int B, int Hq, int D, int nsplit) {
     WsAttn w;
     size_t o = 0;
     if (nsplit <= 1) {  // one split: the kernel writes the outputs, no partials
-        w.part_o = w.part_ml = 0;
+        w.part_o = w.part_ml = w.count = 0;
         w.total = 256;
         return w;
     }
     w.part_o = o;  o = align256(o + sizeof(float) * (size_t)B * nsplit * Hq * D);
     w.part_ml = o; o = align256(o + sizeof(float) * 2 * (size_t)B * nsplit * Hq);
+    w.count = o;   o = align256(o + sizeof(int32_t) * (size_t)B * ((Hq + 15) / 16));
     w.total = o;
     return w;
 }

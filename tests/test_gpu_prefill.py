@@ -113,7 +113,7 @@ def _rings(wl, o, g, q_pos0, n_q):
 def _attn_prefill(g, q, ring, C, q_pos0, topk, tl):
     n_q = q.shape[0]
     wl = g.wl
-    ws = torch.empty(k.csa2_workspace_bytes(g.cfg, k.CSA2_OP_SPARSE_ATTN, n_q, g.table.shape[1]),
+    ws = torch.zeros(k.csa2_workspace_bytes(g.cfg, k.CSA2_OP_SPARSE_ATTN, n_q, g.table.shape[1]),
                      dtype=torch.uint8, device="cuda")
     out = torch.full((n_q, wl.H_q, wl.D), float("nan"), dtype=torch.float32, device="cuda")
     lse = torch.full((n_q, wl.H_q), float("nan"), dtype=torch.float32, device="cuda")
