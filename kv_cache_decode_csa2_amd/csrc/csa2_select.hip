@@ -1,0 +1,511 @@
+// csa2_select.hip -- the per-sequence selection of the hierarchical indexer: the pool of
+// the K_blk best blocks and the k best positions inside it (Full), or the k best rescored
+// pool positions (Reindex).
+//
+// What runs (dbyun.net/article/10794, "KV Cache 成为这一代架构改造的核心"; and
+// prism.simon-ai.net/article/7901, "层级稀疏索引器：精准筛选关键信息"): the indexer keeps a
+// pool of the best 8-position blocks and then the best positions inside the pool.
+//
+// Selection order: score descending, lower index first on equal scores; outputs ascending.
+// Scores are compared through an order-preserving map to uint32 (s is never -0 or NaN).
+//
+// Pool selection without a full pass over the block maxima: with m_g the maximum of group
+// g (8 consecutive blocks) and lambda the K_blk-th largest m_g, K_blk distinct blocks (the
+// group maxima) score >= lambda, so the K_blk-th largest block score is >= lambda.  Every
+// pool block therefore lies in a group with m_g >= lambda and scores >= lambda itself;
+// only those blocks (about K_blk of them on unstructured data) enter the exact selection.
+#include "csa2_block.h"
+#include "csa2_select.h"
+
+namespace csa2 {
+
+// ------------------------------------------------------------------ exact block-wide select
+//
+// The K largest of a multiset of uint32 keys, lower index first among equal keys.  The
+// digits adapt to the keys present: each pass histograms the current key range [lo, hi]
+// into at most 2048 bins of width 2^s (LDS), keeps the bin that holds the K-th largest and
+// narrows the range to it, so scores crowded into a few binades still spread over the
+// bins.  Result: an item is selected iff key > thr, or key == thr and fewer than `need`
+// such items precede it in index order.
+
+constexpr int kSelThreads = 1024;
+constexpr int kIPT = 16;                            // register items per thread
+constexpr int kRegCap = kSelThreads * kIPT;         // 16384
+constexpr int kHistBins = 2048;
+constexpr uint32_t kAllTies = 0xFFFFFFFFu;
+
+struct SelShared {
+    __align__(16) uint32_t hist[kHistBins];  // reversed: hist[nbins - 1 - bin]; zero between passes
+    __align__(16) uint32_t scan[kSelThreads / kWave];
+    __align__(16) uint32_t red[3][kSelThreads / kWave];
+    uint32_t res[4];
+};
+
+struct SelResult {
+    uint32_t thr;
+    uint32_t need;
+};
+
+// Block-wide min, max and sum of (lo, hi, n).
+__device__ __forceinline__ void block_min_max_count(uint32_t &lo, uint32_t &hi, uint32_t &n,
+                                                    SelShared &sm) {
+    const int lane = lane_id(), wave = threadIdx.x / kWave;
+    lo = wave_reduce_to63(lo, [](uint32_t x, uint32_t y) { return x < y ? x : y; });
+    hi = wave_reduce_to63(hi, [](uint32_t x, uint32_t y) { return x > y ? x : y; });
+    n = wave_reduce_to63(n, [](uint32_t x, uint32_t y) { return x + y; });
+    __syncthreads();
+    if (lane == kWave - 1) {
+        sm.red[0][wave] = lo;
+        sm.red[1][wave] = hi;
+        sm.red[2][wave] = n;
+    }
+    __syncthreads();
+    lo = 0xFFFFFFFFu;
+    hi = 0u;
+    n = 0u;
+#pragma unroll
+    for (int i = 0; i < kSelThreads / kWave; i += 4) {
+        const uint4 a4 = *reinterpret_cast<const uint4 *>(&sm.red[0][i]);
+        const uint4 b4 = *reinterpret_cast<const uint4 *>(&sm.red[1][i]);
+        const uint4 c4 = *reinterpret_cast<const uint4 *>(&sm.red[2][i]);
+        lo = min(min(min(lo, a4.x), min(a4.y, a4.z)), a4.w);
+        hi = max(max(max(hi, b4.x), max(b4.y, b4.z)), b4.w);
+        n += c4.x + c4.y + c4.z + c4.w;
+    }
+}
+
+// Exact K-th largest of a multiset of uint32 keys (items owned by the threads; Src::each(f)
+// calls f(key) for each), K >= 1 and <= the number of items.  Each pass histograms the
+// current key range [lo, hi] into <= 2048 bins of width 2^s in LDS and narrows the range to
+// the bin that holds the K-th largest.  Wave 0 alone scans the histogram (and zeroes it for
+// the next pass), so a pass costs two barriers.  The lowest bin gets no atomics: its count
+// is the range's item count minus the other bins (a pile of equal minimal keys, such as
+// scores that are exactly 0 after the ReLU, never serialises on one LDS address).
+// Result: an item is selected iff key > thr, or key == thr and fewer than `need` such items
+// precede it in index order (need == kAllTies: all of them).
+template <class Src>
+__device__ __forceinline__ SelResult range_select(const Src &src, uint32_t K, SelShared &sm) {
+    const int tid = threadIdx.x, lane = lane_id(), wave = threadIdx.x / kWave;
+    uint32_t lo = 0xFFFFFFFFu, hi = 0u, n_in = 0u;
+    src.each([&](uint32_t key) {
+        lo = min(lo, key);
+        hi = max(hi, key);
+        n_in++;
+    });
+    block_min_max_count(lo, hi, n_in, sm);
+    uint32_t remaining = K;
+#pragma unroll 1
+    for (int pass = 0; pass < 6 && lo != hi; pass++) {
+        const uint32_t w = hi - lo;
+        const int s = max(0, 32 - __clz((int)w) - 11);  // (w >> s) < 2048
+        const int nbins = (int)(w >> s) + 1;
+        src.each([&](uint32_t key) {
+            if (key > lo && key <= hi) {
+                const int bin = (int)((key - lo) >> s);
+                if (bin > 0) atomicAdd(&sm.hist[nbins - 1 - bin], 1u);
+            }
+        });
+        __syncthreads();
+        if (wave == 0) {
+            // lane l: reversed bins [32 l, 32 l + 32) = bins nbins-1-32l down to nbins-32-32l
+            const int li0 = nbins - 1;  // reversed index of the lowest bin (no atomics)
+            uint4 *h4 = reinterpret_cast<uint4 *>(sm.hist) + 8 * lane;
+            uint32_t part = 0;
+#pragma unroll
+            for (int i = 0; i < 8; i++) {
+                const uint4 v = h4[i];
+                const int r0 = 32 * lane + 4 * i;
+                part += (r0 < li0 ? v.x : 0u) + (r0 + 1 < li0 ? v.y : 0u) + (r0 + 2 < li0 ? v.z : 0u) +
+                        (r0 + 3 < li0 ? v.w : 0u);
+            }
+            const uint32_t incl = wave_incl_scan(part);
+            const uint32_t explicit_total = (uint32_t)__builtin_amdgcn_readlane((int)incl, kWave - 1);
+            const uint32_t bin0 = n_in - explicit_total;  // the lowest bin, counted implicitly
+            const bool has0 = li0 >= 32 * lane && li0 < 32 * lane + 32;
+            const uint32_t before = incl - part;
+            const bool here = before < remaining && remaining <= before + part + (has0 ? bin0 : 0u);
+            // the lane holding the target bin; its 32 bins are scanned by 32 lanes
+            const int tl = __ffsll((long long)__ballot(here)) - 1;
+            const uint32_t tbefore = (uint32_t)__builtin_amdgcn_readlane((int)before, tl);
+            const int ri = 32 * tl + (lane & 31);
+            const uint32_t ci = lane >= 32 || ri > li0 ? 0u : (ri == li0 ? bin0 : sm.hist[ri]);
+            const uint32_t cincl = tbefore + wave_incl_scan(ci);
+            const uint64_t reach = __ballot(lane < 32 && ri <= li0 && cincl >= remaining);
+            const int tb = __ffsll((long long)reach) - 1;
+            if (lane == tb) {
+                sm.res[0] = (uint32_t)(li0 - ri);
+                sm.res[1] = cincl - ci;
+                sm.res[2] = ci;
+            }
+#pragma unroll
+            for (int i = 0; i < 8; i++) h4[i] = make_uint4(0u, 0u, 0u, 0u);
+        }
+        __syncthreads();
+        const uint32_t d = sm.res[0], above = sm.res[1], cnt = sm.res[2];
+        remaining -= above;
+        n_in = cnt;
+        const uint32_t nlo = lo + (d << s);
+        if (cnt == remaining) return {nlo, kAllTies};  // the whole bin is needed
+        const uint64_t top = (uint64_t)nlo + ((1ull << s) - 1ull);
+        hi = (uint32_t)min((uint64_t)hi, top);
+        lo = nlo;
+    }
+    (void)tid;
+    return {lo, remaining};
+}
+
+template <int N>
+struct RegItems {
+    uint32_t key[N];
+    uint32_t valid;  // bit i: item i exists
+    template <class F>
+    __device__ __forceinline__ void each(F f) const {
+#pragma unroll
+        for (int i = 0; i < N; i++)
+            if (valid & (1u << i)) f(key[i]);
+    }
+};
+
+// Ordered emission of the selected items of a register set whose items are in index order
+// within the thread and threads in index order.  One packed scan gives, per thread, the
+// items above the threshold and the ties before it; ties are taken lowest index first, so
+// min(need, ties before) of them precede the thread's own.  `tie_base` / `out_base` carry
+// the ties seen and items written by earlier chunks; both are advanced.  id(i) is written to
+// out[position] for selected items (positions < out_cap).  Counts per chunk < 2^16.
+template <int N, class IdF>
+__device__ __forceinline__ void emit_selected(const RegItems<N> &it, IdF id, SelResult r,
+                                              int32_t *out, uint32_t out_cap,
+                                              uint32_t &tie_base, uint32_t &out_base,
+                                              SelShared &sm) {
+    uint32_t ngt = 0, neq = 0;
+#pragma unroll
+    for (int i = 0; i < N; i++) {
+        if (!(it.valid & (1u << i))) continue;
+        ngt += it.key[i] > r.thr;
+        neq += it.key[i] == r.thr;
+    }
+    uint32_t tot;
+    const uint32_t ex = block_excl_scan<kSelThreads>((ngt << 16) | neq, sm.scan, &tot);
+    const uint32_t gt_before = ex >> 16, eq_before = ex & 0xFFFFu;
+    uint32_t tr = tie_base + eq_before;  // ties before this thread's first item
+    const uint32_t need = r.need;
+    uint32_t o = out_base + gt_before + min(need, tr) - min(need, tie_base);
+    const uint32_t all_gt = tot >> 16, all_eq = tot & 0xFFFFu;
+    out_base += all_gt + (need == kAllTies ? all_eq : min(all_eq, need > tie_base ? need - tie_base : 0u));
+    tie_base += all_eq;
+#pragma unroll
+    for (int i = 0; i < N; i++) {
+        if (!(it.valid & (1u << i))) continue;
+        bool take = it.key[i] > r.thr;
+        if (it.key[i] == r.thr) {
+            take = tr < need;
+            tr++;
+        }
+        if (take) {
+            if (o < out_cap) out[o] = id(i);
+            o++;
+        }
+    }
+}
+
+// Select-all variant (fewer items than requested): every valid item in order.
+template <int N, class IdF>
+__device__ __forceinline__ void emit_all(const RegItems<N> &it, IdF id, int32_t *out,
+                                         uint32_t out_cap, uint32_t &out_base, SelShared &sm) {
+    uint32_t tot;
+    uint32_t o = out_base + block_excl_scan<kSelThreads>((uint32_t)__popc(it.valid), sm.scan, &tot);
+    out_base += tot;
+#pragma unroll
+    for (int i = 0; i < N; i++)
+        if (it.valid & (1u << i)) {
+            if (o < out_cap) out[o] = id(i);
+            o++;
+        }
+}
+
+// ------------------------------------------------------------------ k_select
+
+// SelectArgs: csa2_select.h
+
+struct SelectShared {
+    SelShared sel;
+    int32_t flag[2 * kSelThreads];         // flagged groups (ascending)
+    int32_t pool[CSA2_MAX_POOL_BLOCKS];    // pool blocks (ascending)
+};
+
+// Exact top-K (K >= 1) of a register set (index order), emitted ascending into out.  The
+// multiset must hold >= K items.
+template <int N, class IdF>
+__device__ __forceinline__ SelResult select_emit(const RegItems<N> &it, IdF id, uint32_t K,
+                                                 int32_t *out, uint32_t out_cap, SelectShared &sm) {
+    uint32_t tie_base = 0, out_base = 0;
+    const SelResult r = range_select(it, K, sm.sel);
+    emit_selected(it, id, r, out, out_cap, tie_base, out_base, sm.sel);
+    return r;
+}
+
+// Block maxima of one sequence: block j at base[(j/8)*gstride + j%8] (groups of 8 blocks
+// are contiguous).
+struct BlockRow {
+    const float *base;
+    int64_t gstride;
+    __device__ __forceinline__ float operator[](int j) const { return base[(j >> 3) * gstride + (j & 7)]; }
+    __device__ __forceinline__ const float *group(int g) const { return base + g * gstride; }
+};
+
+// Items of the streaming path: all blocks j < nb whose maximum is >= lam, in chunks of kRegCap.
+__device__ __forceinline__ void load_block_chunk(const BlockRow &bs, int nb, uint32_t lam, int c0,
+                                                 RegItems<kIPT> &it) {
+    const int j0 = c0 + (int)threadIdx.x * kIPT;
+    it.valid = 0;
+#pragma unroll
+    for (int i = 0; i < kIPT; i++) {
+        const int j = j0 + i;
+        it.key[i] = 0u;
+        if (j < nb) {
+            const uint32_t key = order_key(bs[j]);
+            it.key[i] = key;
+            if (key >= lam) it.valid |= 1u << i;
+        }
+    }
+}
+
+struct GlobalBlocks {
+    BlockRow bs;
+    int nb;
+    uint32_t lam;
+    template <class F>
+    __device__ __forceinline__ void each(F f) const {
+        for (int j = threadIdx.x; j < nb; j += kSelThreads) {
+            const uint32_t key = order_key(bs[j]);
+            if (key >= lam) f(key);
+        }
+    }
+};
+
+// Pool of the Full layer: the K_blk best blocks of sequence b, ascending, into sm.pool.
+// Returns the pool length.
+//   1. lambda = K_blk-th largest group maximum (exact select over <= 16384 group maxima
+//      in registers), or no bound when there are at most K_blk groups;
+//   2. the groups with maximum >= lambda, in ascending order (LDS), two per thread: their
+//      blocks scoring >= lambda are the candidates;
+//   3. exact select of K_blk among the candidates, ordered emission.
+// More than 2048 such groups (heavy ties) or more than 16384 groups take a streaming path
+// over all block maxima instead.
+// *thr receives the pool's threshold key (every pool block's maximum is >= it; 0 when the
+// pool holds every block).
+__device__ __forceinline__ int select_pool(const SelectArgs &a, int b, int nb, SelectShared &sm,
+                                           uint32_t *thr) {
+    const int tid = threadIdx.x, K = a.K_blk;
+    *thr = 0u;
+    if (nb <= K) {
+        for (int j = tid; j < nb; j += kSelThreads) sm.pool[j] = j;
+        __syncthreads();
+        return nb;
+    }
+    const BlockRow bs{a.bscore + (int64_t)b * a.bs_b, a.bs_g};
+    const int ng = (nb + kItemBlocks - 1) / kItemBlocks;
+    uint32_t lam = 0u;  // lower bound of the K-th largest block key
+    bool fast = ng <= kRegCap;
+    if (fast) {
+        // group maxima: thread t owns groups [t*16, t*16 + 16)
+        const float *gm = a.gmax + (int64_t)b * a.ngmax;
+        RegItems<kIPT> g;
+        g.valid = 0;
+        const int g0 = tid * kIPT;
+#pragma unroll
+        for (int i = 0; i < kIPT; i += 4) {
+            float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
+            if (g0 + i + 3 < ng) {
+                v = *reinterpret_cast<const float4 *>(gm + g0 + i);
+            } else {
+                if (g0 + i < ng) v.x = gm[g0 + i];
+                if (g0 + i + 1 < ng) v.y = gm[g0 + i + 1];
+                if (g0 + i + 2 < ng) v.z = gm[g0 + i + 2];
+            }
+            const float f[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+            for (int t = 0; t < 4; t++) {
+                g.key[i + t] = order_key(f[t]);
+                if (g0 + i + t < ng) g.valid |= 1u << (i + t);
+            }
+        }
+        if (ng > K) lam = range_select(g, (uint32_t)K, sm.sel).thr;
+        // ascending list of the groups whose maximum is >= lam
+        uint32_t fl = 0;
+#pragma unroll
+        for (int i = 0; i < kIPT; i++)
+            if ((g.valid & (1u << i)) && g.key[i] >= lam) fl |= 1u << i;
+        uint32_t nfg;
+        uint32_t o = block_excl_scan<kSelThreads>((uint32_t)__popc(fl), sm.sel.scan, &nfg);
+        if (nfg <= 2u * kSelThreads) {
+#pragma unroll
+            for (int i = 0; i < kIPT; i++)
+                if (fl & (1u << i)) sm.flag[o++] = g0 + i;
+        }
+        __syncthreads();
+        if (nfg <= 2u * kSelThreads) {
+            // candidates: blocks >= lam of flagged groups 2t and 2t+1
+            RegItems<kIPT> c;
+            c.valid = 0;
+            int gid[2];
+#pragma unroll
+            for (int q = 0; q < 2; q++) {
+                const int fi = 2 * tid + q;
+                gid[q] = fi < (int)nfg ? sm.flag[fi] : -1;
+                float v[kItemBlocks];
+                if (gid[q] >= 0) {
+                    const int j0 = gid[q] * kItemBlocks;
+                    if (j0 + kItemBlocks <= nb) {
+                        const float4 *src = reinterpret_cast<const float4 *>(bs.group(gid[q]));
+                        const float4 x0 = src[0], x1 = src[1];
+                        v[0] = x0.x; v[1] = x0.y; v[2] = x0.z; v[3] = x0.w;
+                        v[4] = x1.x; v[5] = x1.y; v[6] = x1.z; v[7] = x1.w;
+                    } else {
+#pragma unroll
+                        for (int t = 0; t < kItemBlocks; t++) v[t] = j0 + t < nb ? bs[j0 + t] : -INFINITY;
+                    }
+                }
+#pragma unroll
+                for (int t = 0; t < kItemBlocks; t++) {
+                    const int i = q * kItemBlocks + t;
+                    c.key[i] = 0u;
+                    if (gid[q] >= 0 && gid[q] * kItemBlocks + t < nb) {
+                        const uint32_t key = order_key(v[t]);
+                        c.key[i] = key;
+                        if (key >= lam) c.valid |= 1u << i;
+                    }
+                }
+            }
+            *thr = select_emit(c, [&](int i) { return gid[i / kItemBlocks] * kItemBlocks + i % kItemBlocks; },
+                               (uint32_t)K, sm.pool, (uint32_t)K, sm).thr;
+        } else {
+            fast = false;
+        }
+    }
+    if (!fast) {
+        // streaming path: every block maximum >= lam, in chunks of kRegCap
+        uint32_t tie_base = 0, out_base = 0;
+        GlobalBlocks src{bs, nb, lam};
+        const SelResult r = range_select(src, (uint32_t)K, sm.sel);
+        *thr = r.thr;
+        for (int c0 = 0; c0 < nb; c0 += kRegCap) {
+            RegItems<kIPT> c;
+            load_block_chunk(bs, nb, lam, c0, c);
+            emit_selected(c, [&](int i) { return c0 + tid * kIPT + i; }, r, sm.pool, (uint32_t)K,
+                          tie_base, out_base, sm.sel);
+        }
+    }
+    __syncthreads();
+    return K;
+}
+
+// Top-k among the visible positions of the pool.  Thread t owns pool entries 2t and 2t+1.
+// Only positions scoring >= a lower bound of the k-th largest position score are
+// candidates.  Full: the pool threshold (each of the plen pool blocks has a position at
+// its maximum, which is >= the threshold), valid when k <= plen.  Reindex: the k-th largest
+// rescored block maximum among the pool entries (k distinct positions reach it); only
+// entries whose maximum reaches it are read.  Scores come from the Full scan (pscore, by
+// position) or from the Reindex rescoring (poolsc / poolbmax, by pool entry; -inf marks an
+// invisible position).
+template <bool REINDEX>
+__device__ __forceinline__ void select_topk(const SelectArgs &a, int b, int L, const int32_t *pool,
+                                            int plen, uint32_t pool_thr, SelectShared &sm) {
+    const int tid = threadIdx.x;
+    int pj[2];
+    RegItems<2> bm;  // Reindex: block maxima of the thread's entries
+    bm.valid = 0;
+    uint32_t nvis = 0;
+#pragma unroll
+    for (int q = 0; q < 2; q++) {
+        const int e = 2 * tid + q;
+        pj[q] = e < plen ? pool[e] : -1;
+        bm.key[q] = 0u;
+        if (pj[q] >= 0 && pj[q] * kBlk < L) {
+            if (REINDEX) bm.key[q] = order_key(a.poolbmax[(int64_t)b * a.K_blk + e]);
+            bm.valid |= 1u << q;
+            nvis += (uint32_t)min(kBlk, L - pj[q] * kBlk);
+        }
+    }
+    uint32_t n_ent = __popc(bm.valid);
+    const uint32_t n_vis = block_sum<kSelThreads>((nvis << 16) | n_ent, sm.sel.scan);
+    n_ent = n_vis & 0xFFFFu;
+    const uint32_t need = min((uint32_t)a.k, n_vis >> 16);
+    int32_t *out = a.topk + (int64_t)b * a.k;
+    uint32_t lam = 0u;
+    if (need > 0 && need < (n_vis >> 16) && need <= n_ent) {
+        if (REINDEX) lam = n_ent > need ? range_select(bm, need, sm.sel).thr : 0u;
+        else lam = pool_thr;
+    }
+    // candidate positions scoring >= lam (Reindex: of entries whose maximum reaches lam)
+    RegItems<kIPT> it;
+    it.valid = 0;
+#pragma unroll
+    for (int q = 0; q < 2; q++) {
+        float sc[kBlk];
+        const bool live = (bm.valid & (1u << q)) && (!REINDEX || bm.key[q] >= lam);
+        if (live) {
+            const float4 *src = REINDEX
+                ? reinterpret_cast<const float4 *>(a.poolsc + ((int64_t)b * a.K_blk + 2 * tid + q) * kBlk)
+                : reinterpret_cast<const float4 *>(a.pscore + (int64_t)b * a.ps_b + (int64_t)pj[q] * a.ps_j);
+            const float4 x0 = src[0], x1 = src[1];
+            sc[0] = x0.x; sc[1] = x0.y; sc[2] = x0.z; sc[3] = x0.w;
+            sc[4] = x1.x; sc[5] = x1.y; sc[6] = x1.z; sc[7] = x1.w;
+        }
+#pragma unroll
+        for (int t = 0; t < kBlk; t++) {
+            const int i = q * kBlk + t;
+            it.key[i] = 0u;
+            if (live && pj[q] * kBlk + t < L && (!REINDEX || sc[t] != -INFINITY)) {
+                const uint32_t key = order_key(sc[t]);
+                it.key[i] = key;
+                if (key >= lam) it.valid |= 1u << i;
+            }
+        }
+    }
+    if (need > 0) {
+        auto pos = [&](int i) { return pj[i / kBlk] * kBlk + i % kBlk; };
+        if (need == (n_vis >> 16) && lam == 0u) {
+            uint32_t ob = 0;
+            emit_all(it, pos, out, (uint32_t)a.k, ob, sm.sel);
+        } else {
+            select_emit(it, pos, need, out, (uint32_t)a.k, sm);
+        }
+    }
+    for (int i = (int)need + tid; i < a.k; i += kSelThreads) out[i] = -1;
+    if (tid == 0) a.topk_len[b] = (int32_t)need;
+}
+
+template <bool REINDEX>
+__global__ __launch_bounds__(kSelThreads) void k_select(SelectArgs a) {
+    extern __shared__ __align__(16) uint8_t sh_raw[];
+    SelectShared &sm = *reinterpret_cast<SelectShared *>(sh_raw);
+    const int b = blockIdx.x, tid = threadIdx.x;
+    const int L = clamp_len(a.ctx_len ? a.ctx_len[b] : a.q_pos0 + b + 1, a.maxb);
+    const int nb = (L + kBlk - 1) / kBlk;
+    for (int i = tid; i < kHistBins; i += kSelThreads) sm.sel.hist[i] = 0u;  // kept zero between passes
+    __syncthreads();
+    if (REINDEX) {
+        const int plen = max(0, min(a.pool_len[b], a.K_blk));
+        select_topk<true>(a, b, L, a.pool_blocks + (int64_t)b * a.K_blk, plen, 0u, sm);
+        return;
+    }
+    uint32_t thr;
+    const int plen = select_pool(a, b, nb, sm, &thr);
+    const int np = min(plen, nb);
+    int32_t *pool_out = a.pool_blocks + (int64_t)b * a.K_blk;
+    for (int i = tid; i < a.K_blk; i += kSelThreads) pool_out[i] = i < np ? sm.pool[i] : -1;
+    if (tid == 0) a.pool_len[b] = np;
+    select_topk<false>(a, b, L, sm.pool, np, thr, sm);
+}
+
+constexpr size_t kSelectShared = sizeof(SelectShared);
+
+int launch_select(const SelectArgs &a, bool reindex, hipStream_t stream) {
+    if (a.B <= 0) return CSA2_OK;
+    if (reindex) k_select<true><<<a.B, kSelThreads, kSelectShared, stream>>>(a);
+    else k_select<false><<<a.B, kSelThreads, kSelectShared, stream>>>(a);
+    return hipGetLastError() == hipSuccess ? CSA2_OK : CSA2_ERR_HIP;
+}
+
+}  // namespace csa2
