@@ -10,24 +10,29 @@
 // not de-duplicated.
 //
 // Work split: the row list of a sequence is [0, k) = top-k entries (padding masked),
-// then [k, k+W) = window positions; workgroup (split, sequence, head group of 16) owns 64
-// consecutive rows.
-//   1. Each lane loads its slice of the 16 query rows while the row addresses resolve
-//      (top-k entry, then block table), so those loads overlap that chain.
-//   2. Each lane gathers one row's 128-dim quarter and converts it to bf16 with the
-//      gfx950 scaled converters (exact: E2M1 / E4M3 values times a power of two fit
-//      bf16).  Those registers are the B operand of S = Q K^T on MFMA 16x16x32 bf16 (fp32
-//      accumulation); the same values go to LDS transposed (V^T).
-//   3. Softmax statistics per head over the 64 rows (wave shuffles + LDS).
+// then [k, k+W) = window positions, in chunks of 64 rows.  A workgroup (split, sequence,
+// head group of 16) runs NS chunk streams of 4 waves (16 rows each) over its cps chunks with
+// an online softmax; NS = 2 for batches too small to fill the chip (the two streams take the
+// chunks of each pair side by side and join through LDS at the end), NS = 1 otherwise.
+//   1. The query rows are loaded while the row addresses resolve (top-k entry, then block
+//      table), so those loads overlap that chain; NS = 2 also requests each lane's row
+//      bytes before the chunk's first barriers.
+//   2. Each lane converts one row's 128-dim quarter to bf16 with the gfx950 scaled
+//      converters (exact: E2M1 / E4M3 values times a power of two fit bf16).  Those
+//      registers are the B operand of S = Q K^T on MFMA 16x16x32 bf16 (fp32 accumulation);
+//      the same values go to LDS transposed (V^T).
+//   3. Softmax statistics per head over the 64 rows (DPP row reductions + LDS).
 //   4. O = P V on MFMA with P split into bf16 hi + lo parts (error ~2^-17 relative).
 //   5. One split per sequence writes the outputs; with several, each writes its partial
 //      (O, max, sum) to the workspace and the last split of (sequence, head group) to
 //      arrive (an atomic counter) combines them.
+// The appended window row of the fused append is staged in LDS by DMA at kernel start and
+// quantised once by the stream whose chunk attends it.
 #include "csa2_quant.h"
 
 namespace csa2 {
 
-constexpr int kAttnThreads = 256;
+constexpr int kStreamThreads = 256;  // one chunk stream: 4 waves of 16 rows
 constexpr int kD = 512;            // latent dim handled by these kernels
 constexpr int kPStride = 64 + 4;   // padded row of the P tile (floats)
 constexpr int kMaxSplits = 512;    // splits a merge handles (k + W <= 32768)
@@ -113,60 +118,60 @@ struct AttnShared {
     float ptile[16 * kPStride];
     float red_m[4][16], red_l[4][16];
     __align__(16) uint8_t fresh_row[kD + kD / 32];  // the appended window row (MXFP8)
-    int any_valid, has_fresh, last;
+    int any_valid, last;
 };
 
 // Combine the splits of (b, head group hg), run by the last split to finish:
 // out = sum_s 2^((m_s - M) c) O_s / sum_s 2^((m_s - M) c) l_s per head, accumulated with a
-// running maximum over batches of kMergeBatch splits.  Thread (head h = tid / 16,
-// q = tid % 16) owns dims 4q + 64i (i = 0..7) of head h, so 16 threads read one partial row
-// in 256-byte runs; a batch's rows and (max, sum) pairs are all loaded before any is used.
-// An empty split's row was never written: its values are discarded by a select, which
-// keeps the loads unconditional.
-constexpr int kMergeBatch = 4;
-
+// running maximum over batches of splits.  With T = 16 NS threads per head, thread
+// (head h = tid / T, q = tid % T) owns dims 4q + 4Ti of head h, so T threads read one
+// partial row in 16T-byte runs; a batch's rows and (max, sum) pairs are all loaded before
+// any is used (one memory round trip per batch).  An empty split's row was never written:
+// its values are discarded by a select, which keeps the loads unconditional.
+template <int NS>
 __device__ __forceinline__ void merge_splits(const AttnArgs &a, int b, int hg) {
-    const int tid = threadIdx.x, h = tid >> 4, q = tid & 15;
+    constexpr int T = 16 * NS, NV = kD / 4 / T, NB = NS == 2 ? 5 : 4;
+    const int tid = threadIdx.x, h = tid / T, q = tid % T;
     const int64_t row0 = (int64_t)b * a.nsplit * a.Hq + hg * 16 + h;  // split 0, head h
     const float4 *src = reinterpret_cast<const float4 *>(a.part_o + row0 * kD) + q;
     const float2 *mlp = reinterpret_cast<const float2 *>(a.part_ml) + row0;
     const int64_t sstride = (int64_t)a.Hq * kD / 4;  // float4s between splits
-    float4 acc[8];
+    float4 acc[NV];
 #pragma unroll
-    for (int i = 0; i < 8; i++) acc[i] = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+    for (int i = 0; i < NV; i++) acc[i] = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
     float M = -INFINITY, lw = 0.0f;
-    for (int s0 = 0; s0 < a.nsplit; s0 += kMergeBatch) {
-        float2 st[kMergeBatch];
-        float4 v[kMergeBatch][8];
+    for (int s0 = 0; s0 < a.nsplit; s0 += NB) {
+        float2 st[NB];
+        float4 v[NB][NV];
 #pragma unroll
-        for (int u = 0; u < kMergeBatch; u++) {
+        for (int u = 0; u < NB; u++) {
             const int sp = min(s0 + u, a.nsplit - 1);
             st[u] = mlp[(int64_t)sp * a.Hq];
 #pragma unroll
-            for (int i = 0; i < 8; i++) v[u][i] = src[sp * sstride + 16 * i];
+            for (int i = 0; i < NV; i++) v[u][i] = src[sp * sstride + T * i];
         }
-        float mu[kMergeBatch], mb = M;
+        float mu[NB], mb = M;
 #pragma unroll
-        for (int u = 0; u < kMergeBatch; u++) {
+        for (int u = 0; u < NB; u++) {
             mu[u] = s0 + u < a.nsplit && st[u].y > 0.0f ? st[u].x : -INFINITY;
             mb = fmaxf(mb, mu[u]);
         }
         const float alpha = M == -INFINITY ? 0.0f : exp2f((M - mb) * a.scale_log2);
         lw *= alpha;
 #pragma unroll
-        for (int i = 0; i < 8; i++) {
+        for (int i = 0; i < NV; i++) {
             acc[i].x *= alpha;
             acc[i].y *= alpha;
             acc[i].z *= alpha;
             acc[i].w *= alpha;
         }
 #pragma unroll
-        for (int u = 0; u < kMergeBatch; u++) {
+        for (int u = 0; u < NB; u++) {
             const bool use = mu[u] != -INFINITY;
             const float e = use ? exp2f((mu[u] - mb) * a.scale_log2) : 0.0f;
             lw += use ? e * st[u].y : 0.0f;
 #pragma unroll
-            for (int i = 0; i < 8; i++) {
+            for (int i = 0; i < NV; i++) {
                 acc[i].x += use ? e * v[u][i].x : 0.0f;
                 acc[i].y += use ? e * v[u][i].y : 0.0f;
                 acc[i].z += use ? e * v[u][i].z : 0.0f;
@@ -178,23 +183,39 @@ __device__ __forceinline__ void merge_splits(const AttnArgs &a, int b, int hg) {
     const float inv = lw > 0.0f ? 1.0f / lw : 0.0f;
     float4 *dst = reinterpret_cast<float4 *>(a.out + ((int64_t)b * a.Hq + hg * 16 + h) * kD) + q;
 #pragma unroll
-    for (int i = 0; i < 8; i++)
-        dst[16 * i] = make_float4(acc[i].x * inv, acc[i].y * inv, acc[i].z * inv, acc[i].w * inv);
+    for (int i = 0; i < NV; i++)
+        dst[T * i] = make_float4(acc[i].x * inv, acc[i].y * inv, acc[i].z * inv, acc[i].w * inv);
     if (q == 0)
         a.lse[(int64_t)b * a.Hq + hg * 16 + h] = lw > 0.0f ? a.sm_scale * M + logf(lw) : -INFINITY;
 }
 
-__global__ __launch_bounds__(kAttnThreads, 2) void k_attn(AttnArgs a) {
-    __shared__ __align__(16) AttnShared sh;
+// NS chunk streams of 4 waves per workgroup.  NS = 2 (batches too small to fill the chip):
+// streams 0 and 1 take chunks c0 and c0 + 1 of each pair side by side, and stream 1's state
+// joins stream 0's through LDS at the end, which halves the splits the merge reads; the 16
+// query rows are loaded once into LDS for both.  NS = 1: one stream, query rows loaded by
+// every wave straight into registers.
+template <int NS>
+__global__ __launch_bounds__(NS * kStreamThreads, 3 - NS) void k_attn(AttnArgs a) {
+    __shared__ __align__(16) AttnShared shs[NS];
+    __shared__ __align__(16) uint4 qtile[NS == 2 ? 16 * (kD / 8 + 1) : 1];  // 16 query rows, padded
+    __shared__ __align__(16) float4 fstage[kD / 4];  // the appended fp32 row, staged by DMA
 
     const int s = blockIdx.x, b = blockIdx.y / a.HG, hg = blockIdx.y % a.HG;
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int st = NS == 2 ? tid / kStreamThreads : 0, ts = tid % kStreamThreads, wave = ts >> 6;
     const int c16 = lane & 15, g4 = lane >> 4;
+    AttnShared &sh = shs[st];
 
-    // ---- this lane's query slice (head c16, dims g4*128 ..), the A operand of S = Q K^T;
-    //      loaded first so that it overlaps the row-address chain
+    // ---- this lane's query slice (head c16, dims g4*128 ..), the A operand of S = Q K^T,
+    //      loaded first so that it overlaps the row-address chain.  NS = 2: the 16 rows
+    //      (16 KB) go to LDS, 32 bytes per thread, rows 65 16-byte chunks apart (8 lanes
+    //      reading one chunk of 8 rows hit distinct banks), and are read before each S.
     bf16x8_t qa[16];
-    {
+    if (NS == 2) {
+        const uint4 *qg = reinterpret_cast<const uint4 *>(a.q + ((int64_t)b * a.Hq + hg * 16) * kD);
+#pragma unroll
+        for (int i = tid; i < 16 * kD / 8; i += NS * kStreamThreads) qtile[(i >> 6) * 65 + (i & 63)] = qg[i];
+    } else {
         const bf16x8_t *qh = reinterpret_cast<const bf16x8_t *>(
             a.q + ((int64_t)b * a.Hq + hg * 16 + c16) * kD + g4 * 128);
 #pragma unroll
@@ -206,10 +227,27 @@ __global__ __launch_bounds__(kAttnThreads, 2) void k_attn(AttnArgs a) {
     const int w0 = max(0, L - a.W), nwin = L - w0;
     const int r_loc = 16 * wave + c16;
     const int np_b = a.swa_new ? a.new_pos[b] : -1;
+    const int nchunk = attn_splits(a.k, a.W);
+    const int c_beg = s * a.cps, c_end = min(nchunk, (s + 1) * a.cps);
+
+    // ---- the appended row, when one of this workgroup's chunks attends it: its 16 quantising
+    //      threads (lanes 0..15 of the stream's first wave) stage the fp32 row in LDS by DMA
+    //      now, so that the quantisation does not wait for it later
+    const bool in_win = np_b >= w0 && np_b < L && np_b - w0 < a.W;
+    const int fc = a.swa_new && np_b >= 0 && in_win ? (a.k + np_b - w0) / kAttnRows : -1;  // its chunk
+    if (fc >= 0) {
+        if (fc >= c_beg && fc < c_end && (NS == 1 || (fc & 1) == st) && ts < kD / 32) {
+            const uint8_t *src = reinterpret_cast<const uint8_t *>(a.swa_new + (int64_t)b * kD) + 128 * ts;
+#pragma unroll
+            for (int j = 0; j < 8; j++)
+                __builtin_amdgcn_global_load_lds(src + 16 * j,
+                                                 (__attribute__((address_space(3))) void *)(fstage + 16 * j),
+                                                 16, 0, 0);
+        }
+    }
 
     // ---- an appended row outside the attended window is still written (split 0, hg 0)
-    if (a.swa_new && s == 0 && hg == 0 && np_b >= 0 && !(np_b >= w0 && np_b < L && np_b - w0 < a.W) &&
-        tid < kD / 32) {
+    if (a.swa_new && s == 0 && hg == 0 && np_b >= 0 && !in_win && tid < kD / 32) {
         uint8_t *dst = a.swa_out + ((int64_t)b * a.rstride + np_b % a.C) * (kD + kD / 32);
         quant_fp8(a.swa_new + (int64_t)b * kD + 32 * tid, dst + 32 * tid, dst + kD + tid);
     }
@@ -226,14 +264,15 @@ __global__ __launch_bounds__(kAttnThreads, 2) void k_attn(AttnArgs a) {
 #pragma unroll
     for (int n = 0; n < 8; n++) o[n] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
 
-    const int nchunk = attn_splits(a.k, a.W);
-    const int c_end = min(nchunk, (s + 1) * a.cps);
-    for (int c = s * a.cps; c < c_end; c++) {
+    // the split's chunks [c_beg, c_end) in groups of NS: stream st takes chunk c0 + st
+    for (int c0 = c_beg; c0 < c_end; c0 += NS) {
+        const int c = c0 + st;
         const int rg = c * kAttnRows + r_loc;
-        // ---- locate this lane's row
+        // ---- locate this lane's row (none when the stream's chunk is past the split)
         const uint8_t *rp = nullptr;
         bool fp8 = false, fresh = false;
-        if (rg < a.k) {
+        if (c >= c_end) {
+        } else if (rg < a.k) {
             if (rg < tl) {
                 const int p = a.topk[(int64_t)b * a.k + rg];
                 if (p >= 0 && p < L) {
@@ -252,46 +291,76 @@ __global__ __launch_bounds__(kAttnThreads, 2) void k_attn(AttnArgs a) {
             }
         }
         const bool valid = rp != nullptr;
-        if (tid == 0) {
-            sh.any_valid = 0;
-            sh.has_fresh = 0;
-        }
-        __syncthreads();  // also: the previous chunk is done with V^T, P and the reductions
-        if (valid) sh.any_valid = 1;
-        if (fresh) sh.has_fresh = 1;
-        __syncthreads();
-        if (!sh.any_valid) continue;  // uniform
-        if (sh.has_fresh) {
-            // the appended row: 16 threads quantise one group each into LDS (and, for the
-            // first head group, into the ring); its lanes then read it from LDS
-            if (tid < kD / 32) {
-                float v[32];
-                load_group(a.swa_new + (int64_t)b * kD + 32 * tid, v);
-                uint32_t w[8];
-                const uint32_t sc = quant_fp8_regs(v, w);
-                uint4 *d4 = reinterpret_cast<uint4 *>(sh.fresh_row + 32 * tid);
-                d4[0] = make_uint4(w[0], w[1], w[2], w[3]);
-                d4[1] = make_uint4(w[4], w[5], w[6], w[7]);
-                sh.fresh_row[kD + tid] = (uint8_t)sc;
-                if (hg == 0) {
-                    uint8_t *dst = a.swa_out + ((int64_t)b * a.rstride + np_b % a.C) * (kD + kD / 32);
-                    uint4 *g4p = reinterpret_cast<uint4 *>(dst + 32 * tid);
-                    g4p[0] = d4[0];
-                    g4p[1] = d4[1];
-                    dst[kD + tid] = (uint8_t)sc;
+        // ---- this lane's row bytes: a main row's 64 code bytes and 4 scale bytes of dims
+        //      g4*128 .., a window row's 128 and 4 (the appended row comes from LDS instead).
+        //      NS = 2 requests them before the barriers below, so that they overlap them
+        //      (NS = 1, whose query slice holds 64 registers across the loop, after them).
+        uint4 uu[8];
+        uint32_t sc4 = 0u;
+        auto load_row = [&] {
+            if (valid && !fresh) {
+                const uint4 *src = reinterpret_cast<const uint4 *>(rp + g4 * (fp8 ? 128 : 64));
+                if (fp8) {
+#pragma unroll
+                    for (int i = 0; i < 8; i++) uu[i] = src[i];
+                    sc4 = *reinterpret_cast<const uint32_t *>(rp + kD + 4 * g4);
+                } else {
+#pragma unroll
+                    for (int i = 0; i < 4; i++) uu[i] = src[i];
+                    sc4 = *reinterpret_cast<const uint32_t *>(rp + kD / 2 + 4 * g4);
                 }
             }
-            __syncthreads();
-            if (fresh) rp = sh.fresh_row;
+        };
+        // ---- the appended row, when this stream's chunk attends it: its 16 threads quantise
+        //      one group each from the staged fp32 row into LDS (and, for the first head group,
+        //      into the ring).  NS = 2 does it before the barriers below, which then order the
+        //      writes before its lane reads them; NS = 1 after them, behind a barrier of its own.
+        auto quant_fresh = [&] {
+        if (c == fc && ts < kD / 32) {
+            float v[32];
+#pragma unroll
+            for (int j = 0; j < 8; j++) {
+                const float4 t4 = fstage[16 * j + ts];
+                v[4 * j] = t4.x;
+                v[4 * j + 1] = t4.y;
+                v[4 * j + 2] = t4.z;
+                v[4 * j + 3] = t4.w;
+            }
+            uint32_t w[8];
+            const uint32_t sc = quant_fp8_regs(v, w);
+            uint4 *d4 = reinterpret_cast<uint4 *>(sh.fresh_row + 32 * ts);
+            d4[0] = make_uint4(w[0], w[1], w[2], w[3]);
+            d4[1] = make_uint4(w[4], w[5], w[6], w[7]);
+            sh.fresh_row[kD + ts] = (uint8_t)sc;
+            if (hg == 0) {
+                uint8_t *dst = a.swa_out + ((int64_t)b * a.rstride + np_b % a.C) * (kD + kD / 32);
+                uint4 *g4p = reinterpret_cast<uint4 *>(dst + 32 * ts);
+                g4p[0] = d4[0];
+                g4p[1] = d4[1];
+                dst[kD + ts] = (uint8_t)sc;
+            }
+        }
+        };
+        if (NS == 2) {
+            load_row();
+            quant_fresh();
+        }
+        if (ts == 0) sh.any_valid = 0;
+        __syncthreads();  // also: the previous chunks are done with V^T, P and the reductions
+        if (valid) sh.any_valid = 1;
+        __syncthreads();
+        if (!shs[0].any_valid && !shs[NS - 1].any_valid) continue;  // uniform over the workgroup
+        if (NS == 1) {
+            if (fc == c0) {  // uniform: fc and c0 are the workgroup's
+                quant_fresh();
+                __syncthreads();
+            }
+            load_row();
         }
 
-        // ---- gather + exact conversion to bf16: kb[t] = dims g4*128 + 8t .. +8 of the row
+        // ---- exact conversion to bf16: kb[t] = dims g4*128 + 8t .. +8 of the row
         bf16x8_t kb[16];
         if (valid && !fp8) {
-            const uint4 *src = reinterpret_cast<const uint4 *>(rp + g4 * 64);
-            const uint4 u0 = src[0], u1 = src[1], u2 = src[2], u3 = src[3];
-            const uint32_t sc4 = *reinterpret_cast<const uint32_t *>(rp + kD / 2 + 4 * g4);
-            const uint4 uu[4] = {u0, u1, u2, u3};
 #pragma unroll
             for (int t = 0; t < 16; t++) {
                 const uint32_t wd = word_of(uu[t >> 2], t & 3);
@@ -302,11 +371,13 @@ __global__ __launch_bounds__(kAttnThreads, 2) void k_attn(AttnArgs a) {
                               __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(wd, sc, 3));
             }
         } else if (valid) {
-            const uint4 *src = reinterpret_cast<const uint4 *>(rp + g4 * 128);
-            uint4 uu[8];
+            if (fresh) {  // the appended row from LDS (bytewise scales: kept an LDS read)
+                const uint4 *src = reinterpret_cast<const uint4 *>(sh.fresh_row + g4 * 128);
 #pragma unroll
-            for (int i = 0; i < 8; i++) uu[i] = src[i];
-            const uint32_t sc4 = *reinterpret_cast<const uint32_t *>(rp + kD + 4 * g4);
+                for (int i = 0; i < 8; i++) uu[i] = src[i];
+                const uint8_t *fs = sh.fresh_row + kD + 4 * g4;
+                sc4 = fs[0] | (uint32_t)fs[1] << 8 | (uint32_t)fs[2] << 16 | (uint32_t)fs[3] << 24;
+            }
 #pragma unroll
             for (int t = 0; t < 16; t++) {
                 const uint32_t w0d = word_of(uu[t >> 1], 2 * (t & 1)), w1d = word_of(uu[t >> 1], 2 * (t & 1) + 1);
@@ -329,7 +400,15 @@ __global__ __launch_bounds__(kAttnThreads, 2) void k_attn(AttnArgs a) {
 #pragma unroll
             for (int i = 0; i < 8; i++) sh.vt[vt_index(g4 * 128 + 8 * t + i, r_loc)] = kb[t][i];
 
-        // ---- S = Q K^T for this wave's 16 rows and the 16 heads
+        // ---- S = Q K^T for this wave's 16 rows and the 16 heads (NS = 2: the query slice is
+        //      read from the LDS tile here, so that it holds no registers across the loop)
+        if (NS == 2) {
+#pragma unroll
+            for (int t = 0; t < 16; t++) {
+                const uint4 u = qtile[c16 * 65 + g4 * 16 + t];
+                qa[t] = *reinterpret_cast<const bf16x8_t *>(&u);
+            }
+        }
         f32x4_t acc = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
         for (int t = 0; t < 16; t++) acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[t], kb[t], acc, 0, 0, 0);
@@ -342,15 +421,15 @@ __global__ __launch_bounds__(kAttnThreads, 2) void k_attn(AttnArgs a) {
             if (c16 == 0) sh.red_m[wave][4 * g4 + j] = m;
         }
         __syncthreads();  // V^T and the row maxima are in LDS
-        // new running maxima (finite: the chunk has a valid row, so every head has a finite
-        // score), rescale factors, probabilities of this lane's row
+        // new running maxima, rescale factors, probabilities of this lane's row (a stream
+        // whose chunk has no row keeps its state: mn = M, alpha = 1, p = 0)
         float alpha[4];
 #pragma unroll
         for (int j = 0; j < 4; j++) {
             const int h = 4 * g4 + j;
             const float mc = fmaxf(fmaxf(sh.red_m[0][h], sh.red_m[1][h]), fmaxf(sh.red_m[2][h], sh.red_m[3][h]));
             const float mn = fmaxf(M[j], mc);
-            alpha[j] = exp2f((M[j] - mn) * a.scale_log2);  // 0 for the first chunk
+            alpha[j] = M[j] == mn ? 1.0f : exp2f((M[j] - mn) * a.scale_log2);  // 0 for a first row
             M[j] = mn;
             const float pv = valid ? exp2f((sv[j] - mn) * a.scale_log2) : 0.0f;
             const float l = row16_sum(pv);
@@ -395,23 +474,59 @@ __global__ __launch_bounds__(kAttnThreads, 2) void k_attn(AttnArgs a) {
         }
     }
 
-    // ---- one split: normalised output and log-sum-exp; several: the partial state
-    if (a.nsplit == 1) {
+    // ---- stream 1's state joins stream 0's through LDS (stream 1's V^T tile, 32 KB)
+    if (NS == 2) {
+    __syncthreads();  // both streams are done with their V^T tiles
+    float *xo = reinterpret_cast<float *>(shs[NS - 1].vt);
+    if (st == 1) {
 #pragma unroll
-        for (int n = 0; n < 8; n++) {
-            const int d = 16 * (8 * wave + n) + c16;
+        for (int n = 0; n < 8; n++)
+#pragma unroll
+            for (int j = 0; j < 4; j++) xo[(4 * n + j) * kStreamThreads + ts] = o[n][j];
+        if (c16 == 0)
 #pragma unroll
             for (int j = 0; j < 4; j++) {
-                const int h = hg * 16 + 4 * g4 + j;
-                a.out[((int64_t)b * a.Hq + h) * kD + d] = lsum[j] > 0.0f ? o[n][j] * (1.0f / lsum[j]) : 0.0f;
+                shs[NS - 1].red_m[wave][4 * g4 + j] = M[j];
+                shs[NS - 1].red_l[wave][4 * g4 + j] = lsum[j];
             }
-        }
-        if (wave == 0 && c16 == 0)
+    }
+    __syncthreads();
+    if (st == 0) {
 #pragma unroll
-            for (int j = 0; j < 4; j++)
-                a.lse[(int64_t)b * a.Hq + hg * 16 + 4 * g4 + j] =
-                    lsum[j] > 0.0f ? a.sm_scale * M[j] + logf(lsum[j]) : -INFINITY;
-    } else {
+        for (int j = 0; j < 4; j++) {
+            const float m1 = shs[NS - 1].red_m[wave][4 * g4 + j], l1 = shs[NS - 1].red_l[wave][4 * g4 + j];
+            const float mn = fmaxf(M[j], m1);
+            const float a0 = M[j] == mn ? 1.0f : exp2f((M[j] - mn) * a.scale_log2);
+            const float a1 = m1 == mn ? 1.0f : exp2f((m1 - mn) * a.scale_log2);
+            M[j] = mn;
+            lsum[j] = lsum[j] * a0 + l1 * a1;
+#pragma unroll
+            for (int n = 0; n < 8; n++) o[n][j] = o[n][j] * a0 + xo[(4 * n + j) * kStreamThreads + ts] * a1;
+        }
+    }
+    }
+
+    // ---- one split: normalised output and log-sum-exp; several: the partial state
+    if (a.nsplit == 1) {
+        if (st == 0) {
+#pragma unroll
+            for (int n = 0; n < 8; n++) {
+                const int d = 16 * (8 * wave + n) + c16;
+#pragma unroll
+                for (int j = 0; j < 4; j++) {
+                    const int h = hg * 16 + 4 * g4 + j;
+                    a.out[((int64_t)b * a.Hq + h) * kD + d] = lsum[j] > 0.0f ? o[n][j] * (1.0f / lsum[j]) : 0.0f;
+                }
+            }
+            if (wave == 0 && c16 == 0)
+#pragma unroll
+                for (int j = 0; j < 4; j++)
+                    a.lse[(int64_t)b * a.Hq + hg * 16 + 4 * g4 + j] =
+                        lsum[j] > 0.0f ? a.sm_scale * M[j] + logf(lsum[j]) : -INFINITY;
+        }
+        return;
+    }
+    if (st == 0) {
         const int64_t pbase = ((int64_t)b * a.nsplit + s) * a.Hq + hg * 16;
         if (wave == 0 && c16 == 0)
 #pragma unroll
@@ -429,20 +544,20 @@ __global__ __launch_bounds__(kAttnThreads, 2) void k_attn(AttnArgs a) {
                 for (int j = 0; j < 4; j++) po[(4 * g4 + j) * kD + d] = o[n][j];
             }
         }
-        // The last split of (b, hg) to arrive combines them all.  Every wave's stores are
-        // ordered before the barrier; thread 0's agent-scope release then publishes them
-        // device-wide and its acquire (for the last split) covers the other splits' partials.
-        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
-        __syncthreads();
-        int32_t *cnt = a.count + (int64_t)b * a.HG + hg;
-        if (tid == 0)
-            sh.last = __hip_atomic_fetch_add(cnt, 1, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT) ==
-                      a.nsplit - 1;
-        __syncthreads();
-        if (!sh.last) return;  // uniform
-        merge_splits(a, b, hg);
-        if (tid == 0) __hip_atomic_store(cnt, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
+    // The last split of (b, hg) to arrive combines them all.  Every wave's stores are
+    // ordered before the barrier; thread 0's agent-scope release then publishes them
+    // device-wide and its acquire (for the last split) covers the other splits' partials.
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+    __syncthreads();
+    int32_t *cnt = a.count + (int64_t)b * a.HG + hg;
+    if (tid == 0)
+        shs[0].last = __hip_atomic_fetch_add(cnt, 1, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT) ==
+                      a.nsplit - 1;
+    __syncthreads();
+    if (!shs[0].last) return;  // uniform
+    merge_splits<NS>(a, b, hg);
+    if (tid == 0) __hip_atomic_store(cnt, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 }  // namespace csa2
@@ -501,7 +616,8 @@ int sparse_attn(const csa2_config *c, const float *swa_new, const int32_t *new_p
     a.swa_new = swa_new;
     a.new_pos = new_pos;
     a.swa_out = swa_out;
-    k_attn<<<dim3(nsplit, batch * a.HG), kAttnThreads, 0, stream>>>(a);
+    if (plan.ns == 2) k_attn<2><<<dim3(nsplit, batch * a.HG), 2 * kStreamThreads, 0, stream>>>(a);
+    else k_attn<1><<<dim3(nsplit, batch * a.HG), kStreamThreads, 0, stream>>>(a);
     return hipGetLastError() == hipSuccess ? CSA2_OK : CSA2_ERR_HIP;
 }
 

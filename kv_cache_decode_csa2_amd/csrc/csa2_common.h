@@ -72,18 +72,22 @@ struct WsAttn {
 };
 __host__ __device__ inline int attn_splits(int k, int W) { return (k + W + kAttnRows - 1) / kAttnRows; }
 
-// Row chunks of 64 per workgroup: enough workgroups (sequences x head groups x splits) to
-// fill the chip, one split per sequence when the batch alone does.
+// Row chunks of 64 per workgroup stream.  A batch of at least 512 (sequence, head group)
+// pairs fills the chip with one-stream workgroups (splits up to about 1024 workgroups);
+// smaller batches take two-stream workgroups, each owning cps consecutive chunks (cps even),
+// about 512 of them.
 struct AttnPlan {
-    int nsplit, cps;  // splits, chunks per split
+    int nsplit, cps, ns;  // splits, chunks per split, chunk streams per workgroup
 };
 __host__ __device__ inline AttnPlan attn_plan(int B, int Hq, int k, int W) {
     const int nchunk = attn_splits(k, W);
     const int groups = (B > 0 ? B : 1) * (Hq / 16 > 0 ? Hq / 16 : 1);
-    int ns = (1024 + groups - 1) / groups;
-    ns = ns < 1 ? 1 : (ns > nchunk ? nchunk : ns);
-    const int cps = (nchunk + ns - 1) / ns;
-    return AttnPlan{(nchunk + cps - 1) / cps, cps};
+    const int ns = groups >= 512 ? 1 : 2;
+    const int units = (nchunk + ns - 1) / ns;  // chunks, or chunk pairs
+    int sp = ((ns == 1 ? 1024 : 512) + groups - 1) / groups;
+    sp = sp < 1 ? 1 : (sp > units ? units : sp);
+    const int ups = (units + sp - 1) / sp;  // units per split
+    return AttnPlan{(units + ups - 1) / ups, ns * ups, ns};
 }
 
 __host__ __device__ inline WsAttn ws_attn(int B, int Hq, int D, int nsplit) {
