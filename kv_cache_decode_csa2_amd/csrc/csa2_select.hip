@@ -345,27 +345,25 @@ __device__ __forceinline__ int select_pool(const SelectArgs &a, int b, int nb, S
         }
         __syncthreads();
         if (nfg <= 2u * kSelThreads) {
-            // candidates: blocks >= lam of flagged groups 2t and 2t+1
+            // candidates: blocks >= lam of flagged groups 2t and 2t+1.  Both groups' maxima
+            // are requested before either is used (one memory round trip); an absent group
+            // reads group 0 and blocks past nb (in the last group's row) are masked.
             RegItems<kIPT> c;
             c.valid = 0;
             int gid[2];
+            float4 x[2][2];
 #pragma unroll
             for (int q = 0; q < 2; q++) {
                 const int fi = 2 * tid + q;
                 gid[q] = fi < (int)nfg ? sm.flag[fi] : -1;
-                float v[kItemBlocks];
-                if (gid[q] >= 0) {
-                    const int j0 = gid[q] * kItemBlocks;
-                    if (j0 + kItemBlocks <= nb) {
-                        const float4 *src = reinterpret_cast<const float4 *>(bs.group(gid[q]));
-                        const float4 x0 = src[0], x1 = src[1];
-                        v[0] = x0.x; v[1] = x0.y; v[2] = x0.z; v[3] = x0.w;
-                        v[4] = x1.x; v[5] = x1.y; v[6] = x1.z; v[7] = x1.w;
-                    } else {
+                const float4 *src = reinterpret_cast<const float4 *>(bs.group(max(gid[q], 0)));
+                x[q][0] = src[0];
+                x[q][1] = src[1];
+            }
 #pragma unroll
-                        for (int t = 0; t < kItemBlocks; t++) v[t] = j0 + t < nb ? bs[j0 + t] : -INFINITY;
-                    }
-                }
+            for (int q = 0; q < 2; q++) {
+                const float v[kItemBlocks] = {x[q][0].x, x[q][0].y, x[q][0].z, x[q][0].w,
+                                              x[q][1].x, x[q][1].y, x[q][1].z, x[q][1].w};
 #pragma unroll
                 for (int t = 0; t < kItemBlocks; t++) {
                     const int i = q * kItemBlocks + t;
@@ -412,20 +410,47 @@ template <bool REINDEX>
 __device__ __forceinline__ void select_topk(const SelectArgs &a, int b, int L, const int32_t *pool,
                                             int plen, uint32_t pool_thr, SelectShared &sm) {
     const int tid = threadIdx.x;
+    // Everything read for the thread's pool entries e = 2t, 2t+1 is requested in one batch
+    // (one memory round trip): Full, the position scores of the entries' blocks (the entry
+    // itself comes from LDS); Reindex, the entry, its rescored maximum and its rescored
+    // positions.  Reads of an absent entry are clamped into the row and masked below.
     int pj[2];
+    float4 x[2][2];
+    float bmax[2];
+#pragma unroll
+    for (int q = 0; q < 2; q++) {
+        const int e = 2 * tid + q;
+        const int ec = min(e, a.K_blk - 1);
+        const int pv = pool[ec];
+        pj[q] = e < plen ? pv : -1;
+        if (REINDEX) {
+            bmax[q] = a.poolbmax[(int64_t)b * a.K_blk + ec];
+            const float4 *src = reinterpret_cast<const float4 *>(a.poolsc + ((int64_t)b * a.K_blk + ec) * kBlk);
+            x[q][0] = src[0];
+            x[q][1] = src[1];
+        }
+    }
+    // the maxima are only used under a condition: pinned here, so that their loads are not
+    // sunk behind the entries' loads
+    if (REINDEX) asm volatile("" : "+v"(bmax[0]), "+v"(bmax[1]));
+    if (!REINDEX) {
+#pragma unroll
+        for (int q = 0; q < 2; q++) {
+            const int pc = pj[q] >= 0 && pj[q] * kBlk < L ? pj[q] : 0;
+            const float4 *src = reinterpret_cast<const float4 *>(a.pscore + (int64_t)b * a.ps_b + (int64_t)pc * a.ps_j);
+            x[q][0] = src[0];
+            x[q][1] = src[1];
+        }
+    }
     RegItems<2> bm;  // Reindex: block maxima of the thread's entries
     bm.valid = 0;
     uint32_t nvis = 0;
 #pragma unroll
-    for (int q = 0; q < 2; q++) {
-        const int e = 2 * tid + q;
-        pj[q] = e < plen ? pool[e] : -1;
-        bm.key[q] = 0u;
-        if (pj[q] >= 0 && pj[q] * kBlk < L) {
-            if (REINDEX) bm.key[q] = order_key(a.poolbmax[(int64_t)b * a.K_blk + e]);
-            bm.valid |= 1u << q;
-            nvis += (uint32_t)min(kBlk, L - pj[q] * kBlk);
-        }
+    for (int q = 0; q < 2; q++) {  // branch-free, so that no load sinks behind another
+        const bool ok = pj[q] >= 0 && pj[q] * kBlk < L;
+        bm.key[q] = REINDEX && ok ? order_key(bmax[q]) : 0u;
+        bm.valid |= ok ? 1u << q : 0u;
+        nvis += ok ? (uint32_t)min(kBlk, L - pj[q] * kBlk) : 0u;
     }
     uint32_t n_ent = __popc(bm.valid);
     const uint32_t n_vis = block_sum<kSelThreads>((nvis << 16) | n_ent, sm.sel.scan);
@@ -442,16 +467,9 @@ __device__ __forceinline__ void select_topk(const SelectArgs &a, int b, int L, c
     it.valid = 0;
 #pragma unroll
     for (int q = 0; q < 2; q++) {
-        float sc[kBlk];
+        const float sc[kBlk] = {x[q][0].x, x[q][0].y, x[q][0].z, x[q][0].w,
+                                x[q][1].x, x[q][1].y, x[q][1].z, x[q][1].w};
         const bool live = (bm.valid & (1u << q)) && (!REINDEX || bm.key[q] >= lam);
-        if (live) {
-            const float4 *src = REINDEX
-                ? reinterpret_cast<const float4 *>(a.poolsc + ((int64_t)b * a.K_blk + 2 * tid + q) * kBlk)
-                : reinterpret_cast<const float4 *>(a.pscore + (int64_t)b * a.ps_b + (int64_t)pj[q] * a.ps_j);
-            const float4 x0 = src[0], x1 = src[1];
-            sc[0] = x0.x; sc[1] = x0.y; sc[2] = x0.z; sc[3] = x0.w;
-            sc[4] = x1.x; sc[5] = x1.y; sc[6] = x1.z; sc[7] = x1.w;
-        }
 #pragma unroll
         for (int t = 0; t < kBlk; t++) {
             const int i = q * kBlk + t;
