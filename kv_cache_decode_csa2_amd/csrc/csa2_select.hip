@@ -83,16 +83,27 @@ __device__ __forceinline__ void block_min_max_count(uint32_t &lo, uint32_t &hi, 
 // scores that are exactly 0 after the ReLU, never serialises on one LDS address).
 // Result: an item is selected iff key > thr, or key == thr and fewer than `need` such items
 // precede it in index order (need == kAllTies: all of them).
+// With `bounded`, every key lies in [lo0, hi0] and the caller's bounds replace the block-wide
+// min / max / count: the first pass then counts the lowest bin with atomics too.  max_out
+// (unbounded only) receives the largest key.
 template <class Src>
-__device__ __forceinline__ SelResult range_select(const Src &src, uint32_t K, SelShared &sm) {
+__device__ __forceinline__ SelResult range_select(const Src &src, uint32_t K, SelShared &sm,
+                                                  bool bounded = false, uint32_t lo0 = 0u,
+                                                  uint32_t hi0 = 0u, uint32_t *max_out = nullptr) {
     const int tid = threadIdx.x, lane = lane_id(), wave = threadIdx.x / kWave;
-    uint32_t lo = 0xFFFFFFFFu, hi = 0u, n_in = 0u;
-    src.each([&](uint32_t key) {
-        lo = min(lo, key);
-        hi = max(hi, key);
-        n_in++;
-    });
-    block_min_max_count(lo, hi, n_in, sm);
+    uint32_t lo = lo0, hi = hi0, n_in = 0u;
+    bool imp0 = !bounded;  // the lowest bin counted implicitly (n_in known)
+    if (!bounded) {
+        lo = 0xFFFFFFFFu;
+        hi = 0u;
+        src.each([&](uint32_t key) {
+            lo = min(lo, key);
+            hi = max(hi, key);
+            n_in++;
+        });
+        block_min_max_count(lo, hi, n_in, sm);
+        if (max_out) *max_out = hi;
+    }
     uint32_t remaining = K;
 #pragma unroll 1
     for (int pass = 0; pass < 6 && lo != hi; pass++) {
@@ -100,27 +111,28 @@ __device__ __forceinline__ SelResult range_select(const Src &src, uint32_t K, Se
         const int s = max(0, 32 - __clz((int)w) - 11);  // (w >> s) < 2048
         const int nbins = (int)(w >> s) + 1;
         src.each([&](uint32_t key) {
-            if (key > lo && key <= hi) {
+            if (key >= lo && key <= hi) {
                 const int bin = (int)((key - lo) >> s);
-                if (bin > 0) atomicAdd(&sm.hist[nbins - 1 - bin], 1u);
+                if (bin > 0 || !imp0) atomicAdd(&sm.hist[nbins - 1 - bin], 1u);
             }
         });
         __syncthreads();
         if (wave == 0) {
             // lane l: reversed bins [32 l, 32 l + 32) = bins nbins-1-32l down to nbins-32-32l
-            const int li0 = nbins - 1;  // reversed index of the lowest bin (no atomics)
+            const int li0 = nbins - 1;  // reversed index of the lowest bin
+            const int lim = imp0 ? li0 : li0 + 1;  // reversed bins below lim hold atomic counts
             uint4 *h4 = reinterpret_cast<uint4 *>(sm.hist) + 8 * lane;
             uint32_t part = 0;
 #pragma unroll
             for (int i = 0; i < 8; i++) {
                 const uint4 v = h4[i];
                 const int r0 = 32 * lane + 4 * i;
-                part += (r0 < li0 ? v.x : 0u) + (r0 + 1 < li0 ? v.y : 0u) + (r0 + 2 < li0 ? v.z : 0u) +
-                        (r0 + 3 < li0 ? v.w : 0u);
+                part += (r0 < lim ? v.x : 0u) + (r0 + 1 < lim ? v.y : 0u) + (r0 + 2 < lim ? v.z : 0u) +
+                        (r0 + 3 < lim ? v.w : 0u);
             }
             const uint32_t incl = wave_incl_scan(part);
             const uint32_t explicit_total = (uint32_t)__builtin_amdgcn_readlane((int)incl, kWave - 1);
-            const uint32_t bin0 = n_in - explicit_total;  // the lowest bin, counted implicitly
+            const uint32_t bin0 = imp0 ? n_in - explicit_total : 0u;  // the lowest bin, if implicit
             const bool has0 = li0 >= 32 * lane && li0 < 32 * lane + 32;
             const uint32_t before = incl - part;
             const bool here = before < remaining && remaining <= before + part + (has0 ? bin0 : 0u);
@@ -128,7 +140,7 @@ __device__ __forceinline__ SelResult range_select(const Src &src, uint32_t K, Se
             const int tl = __ffsll((long long)__ballot(here)) - 1;
             const uint32_t tbefore = (uint32_t)__builtin_amdgcn_readlane((int)before, tl);
             const int ri = 32 * tl + (lane & 31);
-            const uint32_t ci = lane >= 32 || ri > li0 ? 0u : (ri == li0 ? bin0 : sm.hist[ri]);
+            const uint32_t ci = lane >= 32 || ri > li0 ? 0u : (ri == li0 && imp0 ? bin0 : sm.hist[ri]);
             const uint32_t cincl = tbefore + wave_incl_scan(ci);
             const uint64_t reach = __ballot(lane < 32 && ri <= li0 && cincl >= remaining);
             const int tb = __ffsll((long long)reach) - 1;
@@ -144,6 +156,7 @@ __device__ __forceinline__ SelResult range_select(const Src &src, uint32_t K, Se
         const uint32_t d = sm.res[0], above = sm.res[1], cnt = sm.res[2];
         remaining -= above;
         n_in = cnt;
+        imp0 = true;
         const uint32_t nlo = lo + (d << s);
         if (cnt == remaining) return {nlo, kAllTies};  // the whole bin is needed
         const uint64_t top = (uint64_t)nlo + ((1ull << s) - 1ull);
@@ -237,9 +250,11 @@ struct SelectShared {
 // multiset must hold >= K items.
 template <int N, class IdF>
 __device__ __forceinline__ SelResult select_emit(const RegItems<N> &it, IdF id, uint32_t K,
-                                                 int32_t *out, uint32_t out_cap, SelectShared &sm) {
+                                                 int32_t *out, uint32_t out_cap, SelectShared &sm,
+                                                 bool bounded = false, uint32_t lo0 = 0u,
+                                                 uint32_t hi0 = 0u) {
     uint32_t tie_base = 0, out_base = 0;
-    const SelResult r = range_select(it, K, sm.sel);
+    const SelResult r = range_select(it, K, sm.sel, bounded, lo0, hi0);
     emit_selected(it, id, r, out, out_cap, tie_base, out_base, sm.sel);
     return r;
 }
@@ -295,9 +310,11 @@ struct GlobalBlocks {
 // *thr receives the pool's threshold key (every pool block's maximum is >= it; 0 when the
 // pool holds every block).
 __device__ __forceinline__ int select_pool(const SelectArgs &a, int b, int nb, SelectShared &sm,
-                                           uint32_t *thr) {
+                                           const float4 (&graw)[kIPT / 4], uint32_t *thr,
+                                           uint32_t *kmax) {
     const int tid = threadIdx.x, K = a.K_blk;
     *thr = 0u;
+    *kmax = 0u;  // largest block key when known (0: unknown)
     if (nb <= K) {
         for (int j = tid; j < nb; j += kSelThreads) sm.pool[j] = j;
         __syncthreads();
@@ -308,21 +325,13 @@ __device__ __forceinline__ int select_pool(const SelectArgs &a, int b, int nb, S
     uint32_t lam = 0u;  // lower bound of the K-th largest block key
     bool fast = ng <= kRegCap;
     if (fast) {
-        // group maxima: thread t owns groups [t*16, t*16 + 16)
-        const float *gm = a.gmax + (int64_t)b * a.ngmax;
+        // group maxima (already loaded): thread t owns groups [t*16, t*16 + 16)
         RegItems<kIPT> g;
         g.valid = 0;
         const int g0 = tid * kIPT;
 #pragma unroll
         for (int i = 0; i < kIPT; i += 4) {
-            float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
-            if (g0 + i + 3 < ng) {
-                v = *reinterpret_cast<const float4 *>(gm + g0 + i);
-            } else {
-                if (g0 + i < ng) v.x = gm[g0 + i];
-                if (g0 + i + 1 < ng) v.y = gm[g0 + i + 1];
-                if (g0 + i + 2 < ng) v.z = gm[g0 + i + 2];
-            }
+            const float4 v = graw[i / 4];
             const float f[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
             for (int t = 0; t < 4; t++) {
@@ -330,7 +339,7 @@ __device__ __forceinline__ int select_pool(const SelectArgs &a, int b, int nb, S
                 if (g0 + i + t < ng) g.valid |= 1u << (i + t);
             }
         }
-        if (ng > K) lam = range_select(g, (uint32_t)K, sm.sel).thr;
+        if (ng > K) lam = range_select(g, (uint32_t)K, sm.sel, false, 0u, 0u, kmax).thr;
         // ascending list of the groups whose maximum is >= lam
         uint32_t fl = 0;
 #pragma unroll
@@ -375,8 +384,9 @@ __device__ __forceinline__ int select_pool(const SelectArgs &a, int b, int nb, S
                     }
                 }
             }
+            // every candidate key lies in [lam, largest group maximum]
             *thr = select_emit(c, [&](int i) { return gid[i / kItemBlocks] * kItemBlocks + i % kItemBlocks; },
-                               (uint32_t)K, sm.pool, (uint32_t)K, sm).thr;
+                               (uint32_t)K, sm.pool, (uint32_t)K, sm, *kmax != 0u, lam, *kmax).thr;
         } else {
             fast = false;
         }
@@ -408,7 +418,8 @@ __device__ __forceinline__ int select_pool(const SelectArgs &a, int b, int nb, S
 // invisible position).
 template <bool REINDEX>
 __device__ __forceinline__ void select_topk(const SelectArgs &a, int b, int L, const int32_t *pool,
-                                            int plen, uint32_t pool_thr, SelectShared &sm) {
+                                            int plen, uint32_t pool_thr, uint32_t kmax,
+                                            SelectShared &sm) {
     const int tid = threadIdx.x;
     // Everything read for the thread's pool entries e = 2t, 2t+1 is requested in one batch
     // (one memory round trip): Full, the position scores of the entries' blocks (the entry
@@ -487,7 +498,9 @@ __device__ __forceinline__ void select_topk(const SelectArgs &a, int b, int L, c
             uint32_t ob = 0;
             emit_all(it, pos, out, (uint32_t)a.k, ob, sm.sel);
         } else {
-            select_emit(it, pos, need, out, (uint32_t)a.k, sm);
+            // Full with a pool threshold: every candidate key lies in [lam, largest key]
+            const bool bounded = !REINDEX && lam != 0u && kmax != 0u;
+            select_emit(it, pos, need, out, (uint32_t)a.k, sm, bounded, lam, kmax);
         }
     }
     for (int i = (int)need + tid; i < a.k; i += kSelThreads) out[i] = -1;
@@ -499,22 +512,40 @@ __global__ __launch_bounds__(kSelThreads) void k_select(SelectArgs a) {
     extern __shared__ __align__(16) uint8_t sh_raw[];
     SelectShared &sm = *reinterpret_cast<SelectShared *>(sh_raw);
     const int b = blockIdx.x, tid = threadIdx.x;
+    // Full: the thread's 16 group maxima are requested before the sequence length arrives
+    // (reads clamped into the allocated row of ngmax >= 4 floats; groups past the length are
+    // masked, so a clamped read is never used)
+    float4 graw[kIPT / 4];
+    if (!REINDEX) {
+        const float *gm = a.gmax + (int64_t)b * a.ngmax;
+#pragma unroll
+        for (int i = 0; i < kIPT / 4; i++) {
+            const int gi = min(tid * kIPT + 4 * i, a.ngmax - 4);  // clamped into the row
+            graw[i] = *reinterpret_cast<const float4 *>(gm + gi);
+        }
+    }
     const int L = clamp_len(a.ctx_len ? a.ctx_len[b] : a.q_pos0 + b + 1, a.maxb);
+    if (!REINDEX) {  // pinned here, so that the loads are not sunk behind the length's branches
+#pragma unroll
+        for (int i = 0; i < kIPT / 4; i++)
+            asm volatile("" : "+v"(graw[i].x), "+v"(graw[i].y), "+v"(graw[i].z), "+v"(graw[i].w));
+    }
     const int nb = (L + kBlk - 1) / kBlk;
     for (int i = tid; i < kHistBins; i += kSelThreads) sm.sel.hist[i] = 0u;  // kept zero between passes
     __syncthreads();
     if (REINDEX) {
         const int plen = max(0, min(a.pool_len[b], a.K_blk));
-        select_topk<true>(a, b, L, a.pool_blocks + (int64_t)b * a.K_blk, plen, 0u, sm);
+        select_topk<true>(a, b, L, a.pool_blocks + (int64_t)b * a.K_blk, plen, 0u, 0u, sm);
         return;
     }
     uint32_t thr;
-    const int plen = select_pool(a, b, nb, sm, &thr);
+    uint32_t kmax;
+    const int plen = select_pool(a, b, nb, sm, graw, &thr, &kmax);
     const int np = min(plen, nb);
     int32_t *pool_out = a.pool_blocks + (int64_t)b * a.K_blk;
     for (int i = tid; i < a.K_blk; i += kSelThreads) pool_out[i] = i < np ? sm.pool[i] : -1;
     if (tid == 0) a.pool_len[b] = np;
-    select_topk<false>(a, b, L, sm.pool, np, thr, sm);
+    select_topk<false>(a, b, L, sm.pool, np, thr, kmax, sm);
 }
 
 constexpr size_t kSelectShared = sizeof(SelectShared);
