@@ -20,7 +20,7 @@
 //   2. Each lane converts one row's 128-dim quarter to bf16 with the gfx950 scaled
 //      converters (exact: E2M1 / E4M3 values times a power of two fit bf16).  Those
 //      registers are the B operand of S = Q K^T on MFMA 16x16x32 bf16 (fp32 accumulation);
-//      the same values go to LDS transposed (V^T).
+//      the same values go to LDS row-major (V), read back with transpose reads.
 //   3. Softmax statistics per head over the 64 rows (DPP row reductions + LDS).
 //   4. O = P V on MFMA with P split into bf16 hi + lo parts (error ~2^-17 relative).
 //   5. One split per sequence writes the outputs; with several, each writes its partial
@@ -107,14 +107,26 @@ __device__ __forceinline__ bf16x8_t join4(bf16x2_t a, bf16x2_t b, bf16x2_t c, bf
     return v;
 }
 
-// Position in the swizzled V^T tile [512][64] of element (dim d, row r): 8-row chunks are
-// XOR-permuted by (d >> 1) & 7 so that 16 lanes reading 16 consecutive d hit all banks.
-__device__ __forceinline__ int vt_index(int d, int r) {
-    return d * 64 + ((((r >> 3) ^ (d >> 1)) & 7) << 3) + (r & 7);
+// The V tile: the chunk's 64 rows in row order, kVStride elements apart (one 16-byte pad
+// per row, so that the 8 lanes of a 16-byte store phase land on distinct banks).  The B
+// operand of O = P V (8 consecutive rows of one dim per lane) comes from gfx950 transpose
+// reads: in each 16-lane group, lane j = 4a + c receives element c of the 8-byte chunks
+// addressed by lanes a, a + 4, a + 8 and a + 12, so when lane i addresses row r0 + i/4,
+// dims d0 + 4 (i % 4) .. + 3, lane j receives rows r0 .. r0 + 3 of dim d0 + j.
+constexpr int kVStride = kD + 8;
+typedef short i16x4_t __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ bf16x8_t v_rows8(const __bf16 *p) {  // rows r0 .. r0 + 7
+    typedef __attribute__((address_space(3))) i16x4_t lds_i16x4;
+    typedef short i16x8_t __attribute__((ext_vector_type(8)));
+    const i16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4 *)p);
+    const i16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4 *)(p + 4 * kVStride));
+    const i16x8_t w = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+    return __builtin_bit_cast(bf16x8_t, w);  // whole-vector cast (no per-element inserts)
 }
 
 struct AttnShared {
-    __bf16 vt[kD * 64];                    // V^T tile (64 KB)
+    __bf16 vt[64 * kVStride];              // V tile, row-major (65 KB)
     float ptile[16 * kPStride];
     float red_m[4][16], red_l[4][16];
     __align__(16) uint8_t fresh_row[kD + kD / 32];  // the appended window row (MXFP8)
@@ -346,7 +358,7 @@ __global__ __launch_bounds__(NS * kStreamThreads, 3 - NS) void k_attn(AttnArgs a
             quant_fresh();
         }
         if (ts == 0) sh.any_valid = 0;
-        __syncthreads();  // also: the previous chunks are done with V^T, P and the reductions
+        __syncthreads();  // also: the previous chunks are done with V, P and the reductions
         if (valid) sh.any_valid = 1;
         __syncthreads();
         if (!shs[0].any_valid && !shs[NS - 1].any_valid) continue;  // uniform over the workgroup
@@ -394,11 +406,10 @@ __global__ __launch_bounds__(NS * kStreamThreads, 3 - NS) void k_attn(AttnArgs a
                 for (int i = 0; i < 8; i++) kb[t][i] = (__bf16)0.0f;
         }
 
-        // ---- V^T into LDS
+        // ---- V into LDS, row-major: this lane's 128 dims as 16-byte stores
 #pragma unroll
         for (int t = 0; t < 16; t++)
-#pragma unroll
-            for (int i = 0; i < 8; i++) sh.vt[vt_index(g4 * 128 + 8 * t + i, r_loc)] = kb[t][i];
+            *reinterpret_cast<bf16x8_t *>(&sh.vt[r_loc * kVStride + g4 * 128 + 8 * t]) = kb[t];
 
         // ---- S = Q K^T for this wave's 16 rows and the 16 heads (NS = 2: the query slice is
         //      read from the LDS tile here, so that it holds no registers across the loop)
@@ -420,7 +431,7 @@ __global__ __launch_bounds__(NS * kStreamThreads, 3 - NS) void k_attn(AttnArgs a
             const float m = row16_max(sv[j]);
             if (c16 == 0) sh.red_m[wave][4 * g4 + j] = m;
         }
-        __syncthreads();  // V^T and the row maxima are in LDS
+        __syncthreads();  // V and the row maxima are in LDS
         // new running maxima, rescale factors, probabilities of this lane's row (a stream
         // whose chunk has no row keeps its state: mn = M, alpha = 1, p = 0)
         float alpha[4];
@@ -457,26 +468,25 @@ __global__ __launch_bounds__(NS * kStreamThreads, 3 - NS) void k_attn(AttnArgs a
                 plo[ks][i] = (__bf16)(f[i] - (float)hi);
             }
         }
+        // this lane's transpose-read address: rows 8 g4 + c16/4 (+ 32 ks), dims 4 (c16 % 4) (+ 16 nt)
+        const __bf16 *vrow = &sh.vt[(8 * g4 + (c16 >> 2)) * kVStride + 4 * (c16 & 3)];
 #pragma unroll
         for (int n = 0; n < 8; n++) {
             const int nt = 8 * wave + n;
-            const int d = 16 * nt + c16;
 #pragma unroll
             for (int j = 0; j < 4; j++) o[n][j] *= alpha[j];
 #pragma unroll
             for (int ks = 0; ks < 2; ks++) {
-                const int chunk = 4 * ks + g4;
-                const bf16x8_t vb = *reinterpret_cast<const bf16x8_t *>(
-                    &sh.vt[d * 64 + (((chunk ^ (d >> 1)) & 7) << 3)]);
+                const bf16x8_t vb = v_rows8(vrow + 32 * ks * kVStride + 16 * nt);
                 o[n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ph[ks], vb, o[n], 0, 0, 0);
                 o[n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(plo[ks], vb, o[n], 0, 0, 0);
             }
         }
     }
 
-    // ---- stream 1's state joins stream 0's through LDS (stream 1's V^T tile, 32 KB)
+    // ---- stream 1's state joins stream 0's through LDS (stream 1's V tile, 32 KB of it)
     if (NS == 2) {
-    __syncthreads();  // both streams are done with their V^T tiles
+    __syncthreads();  // both streams are done with their V tiles
     float *xo = reinterpret_cast<float *>(shs[NS - 1].vt);
     if (st == 1) {
 #pragma unroll

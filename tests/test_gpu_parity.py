@@ -226,17 +226,21 @@ def test_group_all_equal_keys_long():
     assert np.array_equal(_np(tg2), to)
 
 
-@pytest.mark.parametrize("ahead", [0, 3])
-def test_fused_window_append_matches_two_calls(ahead):
+@pytest.mark.parametrize("ahead,kk,W", [(0, 40, 32), (3, 40, 32), (0, 450, 100), (3, 450, 100)])
+def test_fused_window_append_matches_two_calls(ahead, kk, W):
     """csa2_sparse_attn_append == csa2_append_swa followed by csa2_sparse_attn: same ring
     bytes, bit-identical outputs.  ahead = 0 appends position L-1 (attended from the fused
-    registers); ahead = 3 appends a position past the window (written, not attended)."""
+    registers); ahead = 3 appends a position past the window (written, not attended).
+    k = 40, W = 32: one chunk pair, the appended row in either stream; k = 450, W = 100:
+    nine chunks (an odd count) split over several workgroups whose partials are merged by
+    the last to arrive, both calls on one workspace (its counters must come back to zero)."""
     import kv_cache_decode_csa2_amd as k
-    wl = si.small("fuse", 90 + ahead, [700, 5000, 64, 1], H_I=4, d_I=64, K_blk=16, k=40, W=32)
+    K_blk = 16 if kk <= 128 else 64
+    wl = si.small("fuse", 90 + ahead + kk, [700, 5000, 64, 1], H_I=4, d_I=64, K_blk=K_blk, k=kk, W=W)
     o, g = _pair(wl)
     qg = g.layer_q(0)
     _, _, tg, tlg = g.index_full(*qg)
-    C = 48
+    C = W + 16
     lay = k.csa2_layout(g.cfg)
     ring = torch.zeros((wl.B, C, lay.swa_row_bytes), dtype=torch.uint8, device="cuda")
     for b in range(wl.B):
