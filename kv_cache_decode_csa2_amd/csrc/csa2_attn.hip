@@ -276,6 +276,21 @@ __global__ __launch_bounds__(NS * kStreamThreads, 3 - NS) void k_attn(AttnArgs a
 #pragma unroll
     for (int n = 0; n < 8; n++) o[n] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
 
+    // The top-k row chain, pipelined across the stream's chunks: while chunk c is computed,
+    // the block-table entry of chunk c + NS and the top-k entry of chunk c + 2 NS are in
+    // flight (entry -1 / block -1: no row).
+    auto topk_at = [&](int c) -> int {
+        const int rg = c * kAttnRows + r_loc;
+        return c < c_end && rg < a.k && rg < tl ? a.topk[(int64_t)b * a.k + rg] : -1;
+    };
+    auto block_of = [&](int p) -> int64_t {
+        if (p < 0 || p >= L) return -1;
+        const int64_t ph = a.table[(int64_t)b * a.tstride + p / kBlk];
+        return ph >= 0 && ph < a.n_blocks ? ph : -1;
+    };
+    int p_cur = topk_at(c_beg + st), p_nxt = topk_at(c_beg + st + NS);
+    int64_t ph_cur = block_of(p_cur);
+
     // the split's chunks [c_beg, c_end) in groups of NS: stream st takes chunk c0 + st
     for (int c0 = c_beg; c0 < c_end; c0 += NS) {
         const int c = c0 + st;
@@ -285,14 +300,8 @@ __global__ __launch_bounds__(NS * kStreamThreads, 3 - NS) void k_attn(AttnArgs a
         bool fp8 = false, fresh = false;
         if (c >= c_end) {
         } else if (rg < a.k) {
-            if (rg < tl) {
-                const int p = a.topk[(int64_t)b * a.k + rg];
-                if (p >= 0 && p < L) {
-                    const int64_t phys = a.table[(int64_t)b * a.tstride + p / kBlk];
-                    if (phys >= 0 && phys < a.n_blocks)
-                        rp = a.kv + phys * (kBlk * (kD / 2 + kD / 32)) + (p % kBlk) * (kD / 2 + kD / 32);
-                }
-            }
+            if (ph_cur >= 0)
+                rp = a.kv + ph_cur * (kBlk * (kD / 2 + kD / 32)) + (p_cur % kBlk) * (kD / 2 + kD / 32);
         } else {
             const int wi = rg - a.k;
             if (wi < nwin && wi < a.W) {
@@ -303,6 +312,13 @@ __global__ __launch_bounds__(NS * kStreamThreads, 3 - NS) void k_attn(AttnArgs a
             }
         }
         const bool valid = rp != nullptr;
+        {  // the chain of the next chunks (see above)
+            const int64_t ph_nxt = block_of(p_nxt);
+            const int p_nn = topk_at(c + 2 * NS);
+            p_cur = p_nxt;
+            ph_cur = ph_nxt;
+            p_nxt = p_nn;
+        }
         // ---- this lane's row bytes: a main row's 64 code bytes and 4 scale bytes of dims
         //      g4*128 .., a window row's 128 and 4 (the appended row comes from LDS instead).
         //      NS = 2 requests them before the barriers below, so that they overlap them
