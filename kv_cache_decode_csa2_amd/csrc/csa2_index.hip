@@ -32,7 +32,9 @@ namespace csa2 {
 
 constexpr int kScanThreads = 256;
 constexpr int kScanWaves = kScanThreads / kWave;
-constexpr int kScanGridMax = 1024;  // workgroups of a scan (grid-stride over waves)
+constexpr int kScanGridMax = 512;   // workgroups of a scan (grid-stride over waves): two per
+                                    // CU, so that each wave runs enough steps to amortise its
+                                    // pipeline fill
 
 // ------------------------------------------------------------------ query + score core
 
