@@ -75,17 +75,19 @@ __device__ __forceinline__ void block_min_max_count(uint32_t &lo, uint32_t &hi, 
 }
 
 // Exact K-th largest of a multiset of uint32 keys (items owned by the threads; Src::each(f)
-// calls f(key) for each), K >= 1 and <= the number of items.  Each pass histograms the
-// current key range [lo, hi] into <= 2048 bins of width 2^s in LDS and narrows the range to
-// the bin that holds the K-th largest.  Wave 0 alone scans the histogram (and zeroes it for
-// the next pass), so a pass costs two barriers.  The lowest bin gets no atomics: its count
-// is the range's item count minus the other bins (a pile of equal minimal keys, such as
-// scores that are exactly 0 after the ReLU, never serialises on one LDS address).
+// calls f(key) for each item, and may also call it with key 0, which stands for no item:
+// real keys are >= 1 because no score is NaN), K >= 1 and <= the number of items.  Each
+// pass histograms the current key range [lo, hi] into <= 2048 bins of width 2^s in LDS and
+// narrows the range to the bin that holds the K-th largest.  All threads scan the bins
+// (two per thread, highest bin first), so a pass costs three barriers and no serial
+// section.  The lowest bin gets no atomics after the first pass: its count is the range's
+// item count minus the other bins (a pile of equal minimal keys, such as scores that are
+// exactly 0 after the ReLU, never serialises on one LDS address).
 // Result: an item is selected iff key > thr, or key == thr and fewer than `need` such items
 // precede it in index order (need == kAllTies: all of them).
-// With `bounded`, every key lies in [lo0, hi0] and the caller's bounds replace the block-wide
-// min / max / count: the first pass then counts the lowest bin with atomics too.  max_out
-// (unbounded only) receives the largest key.
+// With `bounded`, every key lies in [lo0, hi0] (lo0 >= 1) and the caller's bounds replace
+// the block-wide min / max / count: the first pass then counts the lowest bin with atomics
+// too.  max_out (unbounded only) receives the largest key.
 template <class Src>
 __device__ __forceinline__ SelResult range_select(const Src &src, uint32_t K, SelShared &sm,
                                                   bool bounded = false, uint32_t lo0 = 0u,
@@ -97,9 +99,9 @@ __device__ __forceinline__ SelResult range_select(const Src &src, uint32_t K, Se
         lo = 0xFFFFFFFFu;
         hi = 0u;
         src.each([&](uint32_t key) {
-            lo = min(lo, key);
+            lo = min(lo, key ? key : 0xFFFFFFFFu);
             hi = max(hi, key);
-            n_in++;
+            n_in += key != 0u;
         });
         block_min_max_count(lo, hi, n_in, sm);
         if (max_out) *max_out = hi;
@@ -110,47 +112,52 @@ __device__ __forceinline__ SelResult range_select(const Src &src, uint32_t K, Se
         const uint32_t w = hi - lo;
         const int s = max(0, 32 - __clz((int)w) - 11);  // (w >> s) < 2048
         const int nbins = (int)(w >> s) + 1;
-        src.each([&](uint32_t key) {
-            if (key >= lo && key <= hi) {
-                const int bin = (int)((key - lo) >> s);
-                if (bin > 0 || !imp0) atomicAdd(&sm.hist[nbins - 1 - bin], 1u);
-            }
-        });
+        const int li0 = nbins - 1;                      // reversed index of the lowest bin
+        // explicit bins: keys with lo + cut <= key <= hi (cut skips the implicit lowest bin)
+        const uint32_t cut = imp0 ? (1u << s) : 0u;
+        if (cut <= w) {
+            const uint32_t wc = w - cut, base = lo + cut;
+            src.each([&](uint32_t key) {
+                const uint32_t off = key - base;  // wraps below the range (and for key 0)
+                if (off <= wc) atomicAdd(&sm.hist[li0 - (int)((off + cut) >> s)], 1u);
+            });
+        }
         __syncthreads();
-        if (wave == 0) {
-            // lane l: reversed bins [32 l, 32 l + 32) = bins nbins-1-32l down to nbins-32-32l
-            const int li0 = nbins - 1;  // reversed index of the lowest bin
-            const int lim = imp0 ? li0 : li0 + 1;  // reversed bins below lim hold atomic counts
-            uint4 *h4 = reinterpret_cast<uint4 *>(sm.hist) + 8 * lane;
-            uint32_t part = 0;
+        // thread t: reversed bins 2t, 2t + 1 (read, then cleared for the next pass)
+        const int r0 = 2 * tid;
+        const int lim = imp0 ? li0 : li0 + 1;  // reversed bins below lim hold atomic counts
+        uint2 hv = make_uint2(0u, 0u);
+        if (r0 < lim) {
+            hv = *reinterpret_cast<const uint2 *>(&sm.hist[r0]);
+            *reinterpret_cast<uint2 *>(&sm.hist[r0]) = make_uint2(0u, 0u);
+        }
+        const uint32_t c0 = hv.x, c1 = r0 + 1 < lim ? hv.y : 0u, v = c0 + c1;
+        const uint32_t incl = wave_incl_scan(v);
+        if (lane == kWave - 1) sm.scan[wave] = incl;
+        __syncthreads();
+        uint32_t pw = 0u, total = 0u;
 #pragma unroll
-            for (int i = 0; i < 8; i++) {
-                const uint4 v = h4[i];
-                const int r0 = 32 * lane + 4 * i;
-                part += (r0 < lim ? v.x : 0u) + (r0 + 1 < lim ? v.y : 0u) + (r0 + 2 < lim ? v.z : 0u) +
-                        (r0 + 3 < lim ? v.w : 0u);
-            }
-            const uint32_t incl = wave_incl_scan(part);
-            const uint32_t explicit_total = (uint32_t)__builtin_amdgcn_readlane((int)incl, kWave - 1);
-            const uint32_t bin0 = imp0 ? n_in - explicit_total : 0u;  // the lowest bin, if implicit
-            const bool has0 = li0 >= 32 * lane && li0 < 32 * lane + 32;
-            const uint32_t before = incl - part;
-            const bool here = before < remaining && remaining <= before + part + (has0 ? bin0 : 0u);
-            // the lane holding the target bin; its 32 bins are scanned by 32 lanes
-            const int tl = __ffsll((long long)__ballot(here)) - 1;
-            const uint32_t tbefore = (uint32_t)__builtin_amdgcn_readlane((int)before, tl);
-            const int ri = 32 * tl + (lane & 31);
-            const uint32_t ci = lane >= 32 || ri > li0 ? 0u : (ri == li0 && imp0 ? bin0 : sm.hist[ri]);
-            const uint32_t cincl = tbefore + wave_incl_scan(ci);
-            const uint64_t reach = __ballot(lane < 32 && ri <= li0 && cincl >= remaining);
-            const int tb = __ffsll((long long)reach) - 1;
-            if (lane == tb) {
-                sm.res[0] = (uint32_t)(li0 - ri);
-                sm.res[1] = cincl - ci;
-                sm.res[2] = ci;
-            }
+        for (int i = 0; i < kSelThreads / kWave; i += 4) {
+            const uint4 q = *reinterpret_cast<const uint4 *>(&sm.scan[i]);
+            const uint32_t x[4] = {q.x, q.y, q.z, q.w};
 #pragma unroll
-            for (int i = 0; i < 8; i++) h4[i] = make_uint4(0u, 0u, 0u, 0u);
+            for (int j = 0; j < 4; j++) {
+                pw += i + j < wave ? x[j] : 0u;
+                total += x[j];
+            }
+        }
+        const uint32_t before = pw + incl - v;
+        if (remaining <= total) {
+            if (before < remaining && remaining <= before + v) {
+                const bool first = remaining <= before + c0;
+                sm.res[0] = (uint32_t)(li0 - (first ? r0 : r0 + 1));
+                sm.res[1] = first ? before : before + c0;
+                sm.res[2] = first ? c0 : c1;
+            }
+        } else if (tid == 0) {  // the implicit lowest bin (imp0 only)
+            sm.res[0] = 0u;
+            sm.res[1] = total;
+            sm.res[2] = n_in - total;
         }
         __syncthreads();
         const uint32_t d = sm.res[0], above = sm.res[1], cnt = sm.res[2];
@@ -163,19 +170,22 @@ __device__ __forceinline__ SelResult range_select(const Src &src, uint32_t K, Se
         hi = (uint32_t)min((uint64_t)hi, top);
         lo = nlo;
     }
-    (void)tid;
     return {lo, remaining};
 }
 
 template <int N>
 struct RegItems {
-    uint32_t key[N];
-    uint32_t valid;  // bit i: item i exists
+    uint32_t key[N];  // 0: no item
     template <class F>
     __device__ __forceinline__ void each(F f) const {
 #pragma unroll
-        for (int i = 0; i < N; i++)
-            if (valid & (1u << i)) f(key[i]);
+        for (int i = 0; i < N; i++) f(key[i]);
+    }
+    __device__ __forceinline__ uint32_t count() const {
+        uint32_t n = 0;
+#pragma unroll
+        for (int i = 0; i < N; i++) n += key[i] != 0u;
+        return n;
     }
 };
 
@@ -190,10 +200,9 @@ __device__ __forceinline__ void emit_selected(const RegItems<N> &it, IdF id, Sel
                                               int32_t *out, uint32_t out_cap,
                                               uint32_t &tie_base, uint32_t &out_base,
                                               SelShared &sm) {
-    uint32_t ngt = 0, neq = 0;
+    uint32_t ngt = 0, neq = 0;  // thr >= 1, so absent items (key 0) count in neither
 #pragma unroll
     for (int i = 0; i < N; i++) {
-        if (!(it.valid & (1u << i))) continue;
         ngt += it.key[i] > r.thr;
         neq += it.key[i] == r.thr;
     }
@@ -208,32 +217,27 @@ __device__ __forceinline__ void emit_selected(const RegItems<N> &it, IdF id, Sel
     tie_base += all_eq;
 #pragma unroll
     for (int i = 0; i < N; i++) {
-        if (!(it.valid & (1u << i))) continue;
-        bool take = it.key[i] > r.thr;
-        if (it.key[i] == r.thr) {
-            take = tr < need;
-            tr++;
-        }
-        if (take) {
-            if (o < out_cap) out[o] = id(i);
-            o++;
-        }
+        const bool eq = it.key[i] == r.thr;
+        const bool take = it.key[i] > r.thr || (eq && tr < need);
+        tr += eq;
+        if (take && o < out_cap) out[o] = id(i);
+        o += take;
     }
 }
 
-// Select-all variant (fewer items than requested): every valid item in order.
+// Select-all variant (fewer items than requested): every item in order.
 template <int N, class IdF>
 __device__ __forceinline__ void emit_all(const RegItems<N> &it, IdF id, int32_t *out,
                                          uint32_t out_cap, uint32_t &out_base, SelShared &sm) {
     uint32_t tot;
-    uint32_t o = out_base + block_excl_scan<kSelThreads>((uint32_t)__popc(it.valid), sm.scan, &tot);
+    uint32_t o = out_base + block_excl_scan<kSelThreads>(it.count(), sm.scan, &tot);
     out_base += tot;
 #pragma unroll
-    for (int i = 0; i < N; i++)
-        if (it.valid & (1u << i)) {
-            if (o < out_cap) out[o] = id(i);
-            o++;
-        }
+    for (int i = 0; i < N; i++) {
+        const bool take = it.key[i] != 0u;
+        if (take && o < out_cap) out[o] = id(i);
+        o += take;
+    }
 }
 
 // ------------------------------------------------------------------ k_select
@@ -272,15 +276,13 @@ struct BlockRow {
 __device__ __forceinline__ void load_block_chunk(const BlockRow &bs, int nb, uint32_t lam, int c0,
                                                  RegItems<kIPT> &it) {
     const int j0 = c0 + (int)threadIdx.x * kIPT;
-    it.valid = 0;
 #pragma unroll
     for (int i = 0; i < kIPT; i++) {
         const int j = j0 + i;
         it.key[i] = 0u;
         if (j < nb) {
             const uint32_t key = order_key(bs[j]);
-            it.key[i] = key;
-            if (key >= lam) it.valid |= 1u << i;
+            it.key[i] = key >= lam ? key : 0u;
         }
     }
 }
@@ -327,24 +329,20 @@ __device__ __forceinline__ int select_pool(const SelectArgs &a, int b, int nb, S
     if (fast) {
         // group maxima (already loaded): thread t owns groups [t*16, t*16 + 16)
         RegItems<kIPT> g;
-        g.valid = 0;
         const int g0 = tid * kIPT;
 #pragma unroll
         for (int i = 0; i < kIPT; i += 4) {
             const float4 v = graw[i / 4];
             const float f[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
-            for (int t = 0; t < 4; t++) {
-                g.key[i + t] = order_key(f[t]);
-                if (g0 + i + t < ng) g.valid |= 1u << (i + t);
-            }
+            for (int t = 0; t < 4; t++) g.key[i + t] = g0 + i + t < ng ? order_key(f[t]) : 0u;
         }
         if (ng > K) lam = range_select(g, (uint32_t)K, sm.sel, false, 0u, 0u, kmax).thr;
         // ascending list of the groups whose maximum is >= lam
         uint32_t fl = 0;
 #pragma unroll
         for (int i = 0; i < kIPT; i++)
-            if ((g.valid & (1u << i)) && g.key[i] >= lam) fl |= 1u << i;
+            fl |= g.key[i] != 0u && g.key[i] >= lam ? 1u << i : 0u;
         uint32_t nfg;
         uint32_t o = block_excl_scan<kSelThreads>((uint32_t)__popc(fl), sm.sel.scan, &nfg);
         if (nfg <= 2u * kSelThreads) {
@@ -358,7 +356,6 @@ __device__ __forceinline__ int select_pool(const SelectArgs &a, int b, int nb, S
             // are requested before either is used (one memory round trip); an absent group
             // reads group 0 and blocks past nb (in the last group's row) are masked.
             RegItems<kIPT> c;
-            c.valid = 0;
             int gid[2];
             float4 x[2][2];
 #pragma unroll
@@ -376,12 +373,8 @@ __device__ __forceinline__ int select_pool(const SelectArgs &a, int b, int nb, S
 #pragma unroll
                 for (int t = 0; t < kItemBlocks; t++) {
                     const int i = q * kItemBlocks + t;
-                    c.key[i] = 0u;
-                    if (gid[q] >= 0 && gid[q] * kItemBlocks + t < nb) {
-                        const uint32_t key = order_key(v[t]);
-                        c.key[i] = key;
-                        if (key >= lam) c.valid |= 1u << i;
-                    }
+                    const uint32_t key = order_key(v[t]);
+                    c.key[i] = gid[q] >= 0 && gid[q] * kItemBlocks + t < nb && key >= lam ? key : 0u;
                 }
             }
             // every candidate key lies in [lam, largest group maximum]
@@ -453,17 +446,16 @@ __device__ __forceinline__ void select_topk(const SelectArgs &a, int b, int L, c
             x[q][1] = src[1];
         }
     }
-    RegItems<2> bm;  // Reindex: block maxima of the thread's entries
-    bm.valid = 0;
-    uint32_t nvis = 0;
+    RegItems<2> bm;  // Reindex: block maxima of the thread's entries (0: no entry)
+    uint32_t okm = 0, nvis = 0;  // okm bit q: entry q holds a visible block
 #pragma unroll
     for (int q = 0; q < 2; q++) {  // branch-free, so that no load sinks behind another
         const bool ok = pj[q] >= 0 && pj[q] * kBlk < L;
         bm.key[q] = REINDEX && ok ? order_key(bmax[q]) : 0u;
-        bm.valid |= ok ? 1u << q : 0u;
+        okm |= ok ? 1u << q : 0u;
         nvis += ok ? (uint32_t)min(kBlk, L - pj[q] * kBlk) : 0u;
     }
-    uint32_t n_ent = __popc(bm.valid);
+    uint32_t n_ent = __popc(okm);
     const uint32_t n_vis = block_sum<kSelThreads>((nvis << 16) | n_ent, sm.sel.scan);
     n_ent = n_vis & 0xFFFFu;
     const uint32_t need = min((uint32_t)a.k, n_vis >> 16);
@@ -475,21 +467,17 @@ __device__ __forceinline__ void select_topk(const SelectArgs &a, int b, int L, c
     }
     // candidate positions scoring >= lam (Reindex: of entries whose maximum reaches lam)
     RegItems<kIPT> it;
-    it.valid = 0;
 #pragma unroll
     for (int q = 0; q < 2; q++) {
         const float sc[kBlk] = {x[q][0].x, x[q][0].y, x[q][0].z, x[q][0].w,
                                 x[q][1].x, x[q][1].y, x[q][1].z, x[q][1].w};
-        const bool live = (bm.valid & (1u << q)) && (!REINDEX || bm.key[q] >= lam);
+        const bool live = (okm & (1u << q)) && (!REINDEX || bm.key[q] >= lam);
 #pragma unroll
         for (int t = 0; t < kBlk; t++) {
             const int i = q * kBlk + t;
-            it.key[i] = 0u;
-            if (live && pj[q] * kBlk + t < L && (!REINDEX || sc[t] != -INFINITY)) {
-                const uint32_t key = order_key(sc[t]);
-                it.key[i] = key;
-                if (key >= lam) it.valid |= 1u << i;
-            }
+            const uint32_t key = order_key(sc[t]);
+            it.key[i] = live && pj[q] * kBlk + t < L && (!REINDEX || sc[t] != -INFINITY) && key >= lam
+                            ? key : 0u;
         }
     }
     if (need > 0) {
