@@ -218,29 +218,49 @@ __global__ __launch_bounds__(NS * kStreamThreads, 3 - NS) void k_attn(AttnArgs a
     const int c16 = lane & 15, g4 = lane >> 4;
     AttnShared &sh = shs[st];
 
-    // ---- this lane's query slice (head c16, dims g4*128 ..), the A operand of S = Q K^T,
-    //      loaded first so that it overlaps the row-address chain.  NS = 2: the 16 rows
-    //      (16 KB) go to LDS, 32 bytes per thread, rows 65 16-byte chunks apart (8 lanes
-    //      reading one chunk of 8 rows hit distinct banks), and are read before each S.
+    // ---- every load that depends on nothing else is requested before any result is used:
+    //      this lane's query slice (head c16, dims g4*128 ..; the A operand of S = Q K^T),
+    //      the sequence's length, top-k length and append position, and the lane's top-k
+    //      entries of the stream's first two chunks (read clamped into the row, masked once
+    //      the length arrives).  NS = 2: the 16 query rows (16 KB) go to LDS, 32 bytes per
+    //      thread, rows 65 16-byte chunks apart (8 lanes reading one chunk of 8 rows hit
+    //      distinct banks), and are read before each S.
     bf16x8_t qa[16];
+    uint4 qv[2];
     if (NS == 2) {
         const uint4 *qg = reinterpret_cast<const uint4 *>(a.q + ((int64_t)b * a.Hq + hg * 16) * kD);
 #pragma unroll
-        for (int i = tid; i < 16 * kD / 8; i += NS * kStreamThreads) qtile[(i >> 6) * 65 + (i & 63)] = qg[i];
+        for (int j = 0; j < 2; j++) qv[j] = qg[tid + j * NS * kStreamThreads];  // 1024 pieces
     } else {
         const bf16x8_t *qh = reinterpret_cast<const bf16x8_t *>(
             a.q + ((int64_t)b * a.Hq + hg * 16 + c16) * kD + g4 * 128);
 #pragma unroll
         for (int t = 0; t < 16; t++) qa[t] = qh[t];
     }
-
-    const int L = clamp_ctx(a.ctx_len ? a.ctx_len[b] : a.q_pos0 + b + 1, a.maxb);
-    const int tl = max(0, min(a.topk_len[b], a.k));
-    const int w0 = max(0, L - a.W), nwin = L - w0;
+    // (absent pointers are replaced by topk_len, which is always valid, and the value ignored)
+    const int32_t len_v = *(a.ctx_len ? a.ctx_len + b : a.topk_len + b);
+    const int32_t tl_v = a.topk_len[b];
+    const int32_t np_v = *(a.swa_new ? a.new_pos + b : a.topk_len + b);
     const int r_loc = 16 * wave + c16;
-    const int np_b = a.swa_new ? a.new_pos[b] : -1;
     const int nchunk = attn_splits(a.k, a.W);
     const int c_beg = s * a.cps, c_end = min(nchunk, (s + 1) * a.cps);
+    auto topk_raw = [&](int c) -> int32_t {
+        const int rg = c * kAttnRows + r_loc;
+        return a.topk[(int64_t)b * a.k + min(rg, a.k - 1)];
+    };
+    const int32_t e_first = topk_raw(c_beg + st), e_second = topk_raw(c_beg + st + NS);
+    if (NS == 2) {
+#pragma unroll
+        for (int j = 0; j < 2; j++) {
+            const int i = tid + j * NS * kStreamThreads;
+            qtile[(i >> 6) * 65 + (i & 63)] = qv[j];
+        }
+    }
+
+    const int L = clamp_ctx(a.ctx_len ? len_v : a.q_pos0 + b + 1, a.maxb);
+    const int tl = max(0, min(tl_v, a.k));
+    const int w0 = max(0, L - a.W), nwin = L - w0;
+    const int np_b = a.swa_new ? np_v : -1;
 
     // ---- the appended row, when one of this workgroup's chunks attends it: its 16 quantising
     //      threads (lanes 0..15 of the stream's first wave) stage the fp32 row in LDS by DMA
@@ -278,17 +298,19 @@ __global__ __launch_bounds__(NS * kStreamThreads, 3 - NS) void k_attn(AttnArgs a
 
     // The top-k row chain, pipelined across the stream's chunks: while chunk c is computed,
     // the block-table entry of chunk c + NS and the top-k entry of chunk c + 2 NS are in
-    // flight (entry -1 / block -1: no row).
-    auto topk_at = [&](int c) -> int {
+    // flight (entry -1 / block -1: no row).  Reads are clamped into their rows and masked, so
+    // no load sits behind a branch.
+    auto entry_of = [&](int c, int32_t raw) -> int {
         const int rg = c * kAttnRows + r_loc;
-        return c < c_end && rg < a.k && rg < tl ? a.topk[(int64_t)b * a.k + rg] : -1;
+        return c < c_end && rg < a.k && rg < tl ? raw : -1;
     };
+    auto topk_at = [&](int c) -> int { return entry_of(c, topk_raw(c)); };
     auto block_of = [&](int p) -> int64_t {
-        if (p < 0 || p >= L) return -1;
-        const int64_t ph = a.table[(int64_t)b * a.tstride + p / kBlk];
-        return ph >= 0 && ph < a.n_blocks ? ph : -1;
+        const bool in = p >= 0 && p < L;
+        const int64_t ph = a.table[(int64_t)b * a.tstride + (in ? p : 0) / kBlk];
+        return in && ph >= 0 && ph < a.n_blocks ? ph : -1;
     };
-    int p_cur = topk_at(c_beg + st), p_nxt = topk_at(c_beg + st + NS);
+    int p_cur = entry_of(c_beg + st, e_first), p_nxt = entry_of(c_beg + st + NS, e_second);
     int64_t ph_cur = block_of(p_cur);
 
     // the split's chunks [c_beg, c_end) in groups of NS: stream st takes chunk c0 + st

@@ -71,25 +71,34 @@ __global__ void k_append_global(const float *latent, const float *idx_k,
     if (t >= n_rows * gpr) return;
     const int64_t row = t / gpr;
     const int grp = (int)(t % gpr);
+    const bool is_main = grp < gl;
+    if (!(is_main ? latent : idx_k)) return;
+    const int G = dI / 32, hg = grp - gl, h = hg / G, g = hg % G;
+    // the group's 32 values are requested first: they do not depend on the slot lookup
+    float v[32];
+    load_group(is_main ? latent + row * D + grp * 32 : idx_k + row * (H * dI) + hg * 32, v);
     const int b = (int)(row / n_new);
     const int64_t p = (int64_t)pos0[b] + (row % n_new);
     if (p < 0 || p / kBlk >= maxb) return;
     const int64_t phys = block_table[(int64_t)b * maxb + p / kBlk];
     if (phys < 0 || phys >= n_blocks) return;
     const int s = (int)(p % kBlk);
-    if (grp < gl) {
-        if (!latent) return;
+    uint32_t w[4];
+    const uint32_t sc = quant_fp4_regs(v, w);
+    uint8_t *codes, *scale;
+    if (is_main) {
         const int64_t rb = D / 2 + D / 32;
         uint8_t *dst = kv_cache + phys * (kBlk * rb) + s * rb;
-        quant_fp4(latent + row * D + grp * 32, dst + grp * 16, dst + D / 2 + grp);
+        codes = dst + grp * 16;
+        scale = dst + D / 2 + grp;
     } else {
-        if (!idx_k) return;
-        const int G = dI / 32, hg = grp - gl, h = hg / G, g = hg % G;
         const int64_t codes_bytes = (int64_t)kBlk * H * dI / 2;
         uint8_t *blk = idx_cache + phys * (codes_bytes + (int64_t)kBlk * H * G);
-        quant_fp4(idx_k + row * (H * dI) + hg * 32, blk + ((g * kBlk + s) * H + h) * 16,
-                  blk + codes_bytes + (s * H + h) * G + g);
+        codes = blk + ((g * kBlk + s) * H + h) * 16;
+        scale = blk + codes_bytes + (s * H + h) * G + g;
     }
+    *reinterpret_cast<uint4 *>(codes) = make_uint4(w[0], w[1], w[2], w[3]);
+    *scale = (uint8_t)sc;
 }
 
 __global__ void k_append_swa(const float *rows, const int32_t *pos0, int32_t n_new,

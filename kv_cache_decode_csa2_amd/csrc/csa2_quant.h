@@ -61,12 +61,10 @@ __device__ __forceinline__ float group_amax(const float v[32]) {
     return m;
 }
 
-// Quantise one group to 16 code bytes + 1 scale byte.
-__device__ __forceinline__ void quant_fp4(const float *src, uint8_t *codes, uint8_t *scale) {
-    float v[32];
-    load_group(src, v);
+// One FP4 group quantised into registers: w[0..3] hold the 32 codes (8 per word, element
+// 8i+j in bits 4j..4j+3 of w[i]); returns the E8M0 scale code.
+__device__ __forceinline__ uint32_t quant_fp4_regs(const float v[32], uint32_t w[4]) {
     const int e = group_exponent(group_amax(v), 2);
-    uint32_t w[4];
 #pragma unroll
     for (int i = 0; i < 4; i++) {
         uint32_t acc = 0;
@@ -74,8 +72,17 @@ __device__ __forceinline__ void quant_fp4(const float *src, uint8_t *codes, uint
         for (int j = 0; j < 8; j++) acc |= fp4_code(v[8 * i + j], e) << (4 * j);
         w[i] = acc;
     }
+    return (uint32_t)(e + 127);
+}
+
+// Quantise one group to 16 code bytes + 1 scale byte.
+__device__ __forceinline__ void quant_fp4(const float *src, uint8_t *codes, uint8_t *scale) {
+    float v[32];
+    load_group(src, v);
+    uint32_t w[4];
+    const uint32_t sc = quant_fp4_regs(v, w);
     *reinterpret_cast<uint4 *>(codes) = make_uint4(w[0], w[1], w[2], w[3]);
-    *scale = (uint8_t)(e + 127);
+    *scale = (uint8_t)sc;
 }
 
 __device__ __forceinline__ void quant_fp8(const float *src, uint8_t *codes, uint8_t *scale) {
