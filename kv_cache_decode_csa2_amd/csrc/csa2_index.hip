@@ -52,21 +52,52 @@ struct Query {
     float w[H];         // head weights
 };
 
+// The query bytes of head h as loaded (codes, scales, weights), decoded by decode_query;
+// split so that the loads can be issued long before the values are needed.
+template <int H, int G>
+struct QueryRaw {
+    uint4 c[G];
+    uint32_t s;  // the G scale bytes of the head (byte g: group g)
+    float w[H];
+};
+
+template <int H, int G>
+__device__ __forceinline__ void load_query_raw(QueryRaw<H, G> &R, const uint8_t *qc,
+                                               const uint8_t *qs, const float *w, int h) {
+    const uint4 *c4 = reinterpret_cast<const uint4 *>(qc + h * 16 * G);
+#pragma unroll
+    for (int g = 0; g < G; g++) R.c[g] = c4[g];
+    if constexpr (G == 1) R.s = qs[h];
+    else if constexpr (G == 2) R.s = *reinterpret_cast<const uint16_t *>(qs + h * 2);
+    else R.s = *reinterpret_cast<const uint32_t *>(qs + h * 4);
+#pragma unroll
+    for (int j = 0; j < H; j++) R.w[j] = w[j];
+}
+
+// (the raw values are pinned here, so that their first use -- and the wait for the loads --
+// is not hoisted up to the loads)
+template <int H, int G>
+__device__ __forceinline__ void decode_query(Query<H, G> &Q, QueryRaw<H, G> R) {
+    asm volatile("" : "+v"(R.s));
+#pragma unroll
+    for (int g = 0; g < G; g++) {
+        asm volatile("" : "+v"(R.c[g].x), "+v"(R.c[g].y), "+v"(R.c[g].z), "+v"(R.c[g].w));
+        cvt_fp4x8_f16(R.c[g].x, Q.q + 16 * g + 0);
+        cvt_fp4x8_f16(R.c[g].y, Q.q + 16 * g + 4);
+        cvt_fp4x8_f16(R.c[g].z, Q.q + 16 * g + 8);
+        cvt_fp4x8_f16(R.c[g].w, Q.q + 16 * g + 12);
+        Q.e[g] = (int)((R.s >> (8 * g)) & 255u) - 127;
+    }
+#pragma unroll
+    for (int j = 0; j < H; j++) Q.w[j] = R.w[j];
+}
+
 template <int H, int G>
 __device__ __forceinline__ void load_query(Query<H, G> &Q, const uint8_t *qc, const uint8_t *qs,
                                            const float *w, int h) {
-    const uint4 *c4 = reinterpret_cast<const uint4 *>(qc + h * 16 * G);
-#pragma unroll
-    for (int g = 0; g < G; g++) {
-        const uint4 c = c4[g];
-        cvt_fp4x8_f16(c.x, Q.q + 16 * g + 0);
-        cvt_fp4x8_f16(c.y, Q.q + 16 * g + 4);
-        cvt_fp4x8_f16(c.z, Q.q + 16 * g + 8);
-        cvt_fp4x8_f16(c.w, Q.q + 16 * g + 12);
-        Q.e[g] = (int)qs[h * G + g] - 127;
-    }
-#pragma unroll
-    for (int j = 0; j < H; j++) Q.w[j] = w[j];
+    QueryRaw<H, G> R;
+    load_query_raw(R, qc, qs, w, h);
+    decode_query(Q, R);
 }
 
 // Exact dot of one 32-group (returns N/4 where N is the dot of doubled codes).
@@ -155,13 +186,24 @@ __device__ __forceinline__ int items_of(const ScanArgs &a, int b) {
     return (nb + kItemBlocks - 1) / kItemBlocks;
 }
 
-// Exclusive prefix of items per sequence in LDS (prefix[0..B]); returns the total.
+// Exclusive prefix of items per sequence in LDS (prefix[0..B]) and the clamped lengths
+// (lens[0..B-1]); returns the total.  Each length (and pool length) is loaded once.
 template <bool RESCORE>
-__device__ int build_item_prefix(const ScanArgs &a, int32_t *prefix, uint32_t *sh_scan) {
+__device__ int build_item_prefix(const ScanArgs &a, int32_t *prefix, int32_t *lens, uint32_t *sh_scan) {
     uint32_t running = 0;
     for (int base = 0; base < a.B; base += kScanThreads) {
         const int b = base + (int)threadIdx.x;
-        const uint32_t v = b < a.B ? (uint32_t)items_of<RESCORE>(a, b) : 0u;
+        uint32_t v = 0u;
+        if (b < a.B) {
+            const int L = clamp_len(a.ctx_len[b], a.maxb);
+            lens[b] = L;
+            if (RESCORE) {
+                const int pl = max(0, min(a.pool_len[b], a.K_blk));
+                v = (uint32_t)((pl + kItemBlocks - 1) / kItemBlocks);
+            } else {
+                v = (uint32_t)((((L + kBlk - 1) / kBlk) + kItemBlocks - 1) / kItemBlocks);
+            }
+        }
         uint32_t tot;
         const uint32_t ex = block_excl_scan<kScanThreads>(v, sh_scan, &tot);
         if (b < a.B) prefix[b] = (int32_t)(running + ex);
@@ -265,28 +307,29 @@ __device__ __forceinline__ T sload(const T *p, int64_t i) {
     return ((const __attribute__((address_space(4))) T *)(uintptr_t)p)[i];
 }
 
-// Per-step block bookkeeping of one wave (wave-uniform): the BPW logical blocks of step k and
-// their physical blocks (-1: none).
-template <int BPW>
+// Per-step block bookkeeping of one wave: the entry index of the step's first block
+// (uniform) and, per lane, the logical and physical block of the lane's own block (-1: none).
+// Block-table and pool entries are per-lane vector loads: vector loads complete in issue
+// order, so waiting for the entries of an earlier step never waits for later ones (scalar
+// loads complete out of order, and a wait for any one of them is a wait for all).
 struct StepMeta {
-    int b;        // sequence
-    int e0;       // entry index (block or pool entry) of the step's first block
-    int j[BPW];   // logical blocks
-    int ph[BPW];  // physical blocks
+    int e0;    // entry index (block or pool entry) of the step's first block
+    int jraw;  // rescore: the loaded pool entry (validated when the block is looked up)
+    int j;     // logical block (-1: none)
+    int ph;    // physical block as loaded (validated where it is used)
 };
 
 // One wave processes a contiguous range of items; an item is 8 consecutive blocks (scan)
 // or 8 consecutive pool entries (rescore) of one sequence, BPW blocks per step, lane =
-// (position in step) * H + head.  Software pipeline per step k: the keys of step k+1 and the
-// block-table entries of step k+2 (rescoring: the pool entries of step k+3) are in flight
-// while step k is computed.  Block-table and pool entries are uniform per step and come
-// through scalar loads; every step issues the same vector stores (lanes without output
-// write to g_junk), so the wait for a step's keys never covers the stores or the next
-// step's loads.  Loads never branch: an absent block reads physical block 0 and its
+// (position in step) * H + head.  Software pipeline: step k issues the pool entries of step
+// k+6 (rescoring), the block-table entries of step k+4 and the keys of step k+2, in that
+// order, then computes step k.  Every value step k uses was requested by step k-2 or
+// earlier, and vector loads complete in issue order, so no wait covers a load of step k-1.  Every item issues the same vector stores (lanes without output write to
+// g_junk), so the wait for a step's keys never covers the stores or the next step's loads.  Loads never branch: an absent block reads physical block 0 and its
 // positions are masked.  OFF32: every key byte lies within 4 GiB of the cache base, so
 // addresses are a scalar base plus a 32-bit lane offset.
 template <int H, int G, bool RESCORE, bool OFF32>
-__global__ __launch_bounds__(kScanThreads, G == 4 ? 2 : 4) void k_scan(ScanArgs a) {
+__global__ __launch_bounds__(kScanThreads, 2) void k_scan(ScanArgs a) {
     constexpr int BPW = 8 / H;                         // blocks per wave step
     constexpr int NSTEP = kItemBlocks / BPW;           // steps per item
     constexpr int CODES = kBlk * H * 16 * G;
@@ -298,14 +341,33 @@ __global__ __launch_bounds__(kScanThreads, G == 4 ? 2 : 4) void k_scan(ScanArgs 
     const int lane = threadIdx.x & (kWave - 1);
     const int wave = __builtin_amdgcn_readfirstlane((int)threadIdx.x / kWave);
     const int h = lane % H, pw = lane / H, bw = pw / kBlk, slot = pw % kBlk;
-    for (int b = threadIdx.x; b < a.B; b += kScanThreads) sh_len[b] = clamp_len(a.ctx_len[b], a.maxb);
-    const int total = __builtin_amdgcn_readfirstlane(build_item_prefix<RESCORE>(a, sh_prefix, sh_scan));
     const int nwaves = (int)gridDim.x * kScanWaves;
     const int gw = (int)blockIdx.x * kScanWaves + wave;
     // Items of a wave: one sequence -> items gw, gw + nwaves, ... (all resident waves read
     // one contiguous window of the cache at a time, spread over every HBM channel);
     // several sequences -> a contiguous range, so each wave meets few sequences.
     const bool inter = a.B == 1;
+    // pipeline depth: bookkeeping of steps k .. k+DM-1, block-table entries of steps k .. k+DPH-1
+    constexpr int DM = 7, DPH = 4;
+    // One sequence: the query and the first steps' entries (scan: block-table entries;
+    // rescoring: pool entries) depend on no length and are requested before the item prefix,
+    // whose length load and barriers they overlap (entries read clamped into the row and
+    // masked once the length is known).
+    auto entry0 = [&](int k2) {  // first entry of step k2 of an interleaved wave
+        return (gw + (k2 / NSTEP) * nwaves) * kItemBlocks + (k2 % NSTEP) * BPW;
+    };
+    Query<H, G> Q;
+    QueryRaw<H, G> QR;
+    int pre[DM - 1];
+    if (inter) {
+#pragma unroll
+        for (int i = 0; i < (RESCORE ? DM - 1 : DPH); i++) {
+            const int e = entry0(i) + bw;
+            pre[i] = RESCORE ? a.pool[min(e, a.K_blk - 1)] : a.table[min(e, a.maxb - 1)];
+        }
+        load_query_raw<H, G>(QR, a.q_codes, a.q_scales, a.w, h);
+    }
+    const int total = __builtin_amdgcn_readfirstlane(build_item_prefix<RESCORE>(a, sh_prefix, sh_len, sh_scan));
     const int per = (total + nwaves - 1) / nwaves;
     const int it_begin = inter ? gw : gw * per;
     const int it_end = inter ? total : min(total, it_begin + per);
@@ -326,14 +388,13 @@ __global__ __launch_bounds__(kScanThreads, G == 4 ? 2 : 4) void k_scan(ScanArgs 
     const int src_p = (lane % PPS) * H;
     const int src_b = ((lane % BPW) + 1) * kBlk * H - 1;
 
-    auto lane_sel = [&](const int (&v)[BPW]) -> int {
-        int r = v[0];
-#pragma unroll
-        for (int w = 1; w < BPW; w++) r = bw == w ? v[w] : r;
-        return r;
+    // a lane's physical block: the loaded table entry when its logical block exists and the
+    // entry lies in the cache, else -1
+    auto phys_of = [&](const StepMeta &m) -> int {
+        return m.j >= 0 && m.ph >= 0 && (int64_t)m.ph < a.n_blocks ? m.ph : -1;
     };
-    auto load_keys = [&](const StepMeta<BPW> &m, KeyRegs<G> &kr) {
-        const int ph = lane_sel(m.ph);
+    auto load_keys = [&](const StepMeta &m, KeyRegs<G> &kr) {
+        const int ph = phys_of(m);
         const uint32_t p = (uint32_t)(ph >= 0 ? ph : 0);
         if constexpr (OFF32) {
             const uint32_t base = p * (uint32_t)BYTES;
@@ -349,7 +410,6 @@ __global__ __launch_bounds__(kScanThreads, G == 4 ? 2 : 4) void k_scan(ScanArgs 
             kr.ks = *reinterpret_cast<const uint32_t *>(bp + sc_off);
         }
     };
-    Query<H, G> Q;
     float gm = -INFINITY;
 
     // The wave's steps split into segments of one sequence each (items are 8-aligned, so a
@@ -373,45 +433,46 @@ __global__ __launch_bounds__(kScanThreads, G == 4 ? 2 : 4) void k_scan(ScanArgs 
         const int32_t *pool_row = RESCORE ? a.pool + (int64_t)b * a.K_blk : nullptr;
         const int n_ent = RESCORE ? max(0, min(sload(a.pool_len, b), a.K_blk)) : 0;
 
-        // entries of step k2 of this segment (-1 past its end)
-        auto meta_entries = [&](int k2, StepMeta<BPW> &m) {
-            m.e0 = inter ? (it_begin + (k2 / NSTEP) * nwaves) * kItemBlocks + (k2 % NSTEP) * BPW
-                         : e_start + (k2 - kseg) * BPW;
-#pragma unroll
-            for (int w = 0; w < BPW; w++) {
-                m.ph[w] = -1;
-                const int e = m.e0 + w;
-                int jv = -1;
-                if (k2 < kend) {
-                    if (RESCORE) jv = e < n_ent ? sload(pool_row, e) : -1;
-                    else jv = e;
-                }
-                m.j[w] = (jv >= 0 && jv < nb) ? jv : -1;
+        // entries of step k2 of this segment (-1 past its end); rescoring loads the lane's pool
+        // entry (read clamped into the row, checked by meta_phys a step later) unless `have`
+        // holds it already
+        auto meta_entries = [&](int k2, StepMeta &m, const int *have = nullptr) {
+            m.e0 = inter ? entry0(k2) : e_start + (k2 - kseg) * BPW;
+            const int e = m.e0 + bw;
+            const bool live = k2 < kend && e < (RESCORE ? n_ent : nb);
+            if (RESCORE) {
+                m.jraw = have ? *have : pool_row[live ? e : 0];
+                m.j = live ? 0 : -1;
+            } else {
+                m.j = live ? e : -1;
             }
+            m.ph = -1;
         };
-        auto meta_phys = [&](StepMeta<BPW> &m) {
-#pragma unroll
-            for (int w = 0; w < BPW; w++) {
-                const int32_t ph = m.j[w] >= 0 ? sload(table_row, m.j[w]) : -1;
-                m.ph[w] = (ph >= 0 && ph < a.n_blocks) ? ph : -1;
-            }
+        // the lane's block-table entry (its use comes at least a step later)
+        auto meta_phys = [&](StepMeta &m) {
+            if (RESCORE) m.j = m.j >= 0 && m.jraw >= 0 && m.jraw < nb ? m.jraw : -1;
+            m.ph = table_row[m.j >= 0 ? m.j : 0];
         };
 
-        load_query<H, G>(Q, a.q_codes + (size_t)b * H * 16 * G, a.q_scales + (size_t)b * H * G,
-                         a.w + (size_t)b * H, h);
-        // pipeline, two steps deep: the keys of steps k+1 and k+2 are in flight while step k is
-        // computed; physical blocks are known up to step k+2, entries up to step k+3
-        StepMeta<BPW> m0, m1, m2, m3;
-        meta_entries(k, m0);
-        meta_phys(m0);
-        meta_entries(k + 1, m1);
-        meta_phys(m1);
-        meta_entries(k + 2, m2);
-        meta_phys(m2);
-        meta_entries(k + 3, m3);
+        if (inter)
+            decode_query<H, G>(Q, QR);
+        else
+            load_query<H, G>(Q, a.q_codes + (size_t)b * H * 16 * G, a.q_scales + (size_t)b * H * G,
+                             a.w + (size_t)b * H, h);
+        // pipeline state at step k: entries of steps k..k+5 (rescoring: pool entries loaded),
+        // table entries of steps k..k+3 loaded, keys of steps k and k+1 loaded (one sequence:
+        // k = 0 here, and the early requests above stand in for the first loads)
+        StepMeta mt[DM];
+#pragma unroll
+        for (int i = 0; i < DM - 1; i++) meta_entries(k + i, mt[i], RESCORE && inter ? &pre[i] : nullptr);
+#pragma unroll
+        for (int i = 0; i < DPH; i++) {
+            if (!RESCORE && inter) mt[i].ph = pre[i];
+            else meta_phys(mt[i]);
+        }
         KeyRegs<G> K[4];
-        load_keys(m0, K[0]);
-        load_keys(m1, K[1]);
+        load_keys(mt[0], K[0]);
+        load_keys(mt[1], K[1]);
         // an item's two stores, once: the loop is entered with the memory operations in
         // flight that every iteration leaves (its waits stay minimal)
         junk[kWave] = 0.0f;
@@ -427,13 +488,12 @@ __global__ __launch_bounds__(kScanThreads, G == 4 ? 2 : 4) void k_scan(ScanArgs 
         // l (acc_p) and lanes 0..7 the maxima of blocks 0..7 (acc_b)
         float acc_p = 0.0f, acc_b = 0.0f;
         auto body = [&](int k2, int si, KeyRegs<G> &cur, KeyRegs<G> &nxt2) {
-            load_keys(m2, nxt2);
-            meta_phys(m3);
-            StepMeta<BPW> m4;
-            meta_entries(k2 + 4, m4);
+            meta_entries(k2 + 6, mt[6]);
+            meta_phys(mt[4]);
+            load_keys(mt[2], nxt2);
             const float r = head_relu<H, G>(Q, cur.kc, cur.ks >> sc_sh);
             const float sc = combine_heads_dpp<H, G>(Q, r, lane);
-            const int j = lane_sel(m0.j), ph = lane_sel(m0.ph);
+            const int j = mt[0].j, ph = phys_of(mt[0]);
             const bool vis = ph >= 0 && j * kBlk + slot < L;
             const float val = vis ? sc : -INFINITY;
             const float m = block_max_lanes<H>(val);
@@ -447,7 +507,7 @@ __global__ __launch_bounds__(kScanThreads, G == 4 ? 2 : 4) void k_scan(ScanArgs 
             }
             if (si == NSTEP - 1) {
                 // item stores: 64 position scores, 8 block maxima (+ the group maximum)
-                const int e_item = m0.e0 - (NSTEP - 1) * BPW;
+                const int e_item = mt[0].e0 - (NSTEP - 1) * BPW;
                 const bool item_ok = k2 < kend;
                 const bool pos_ok = item_ok && e_item + lane / kBlk < n_lim;
                 float *ps = pos_ok && ps_on ? ps_row + (int64_t)e_item * kBlk + lane : junk;
@@ -464,10 +524,8 @@ __global__ __launch_bounds__(kScanThreads, G == 4 ? 2 : 4) void k_scan(ScanArgs 
                 *ps = acc_p;
                 *pb = vstore;
             }
-            m0 = m1;
-            m1 = m2;
-            m2 = m3;
-            m3 = m4;
+#pragma unroll
+            for (int i = 0; i < DM - 1; i++) mt[i] = mt[i + 1];
         };
         // iterations of STEPS steps (whole items); steps past the segment end are masked
         for (; k < kend; k += STEPS) {
