@@ -50,6 +50,10 @@ def parse():
                     help="for rocprofv3 --pmc: a few eager launches of the dominant kernel, then a "
                          "device-to-device copy of --calib-mb MiB (counter calibration); no timing")
     ap.add_argument("--calib-mb", type=int, default=512)
+    ap.add_argument("--counter-summary", metavar="DIR",
+                    help="no GPU: write profiles/<kernel counters>.json from the FETCH_SIZE and "
+                         "WRITE_SIZE csv files that two rocprofv3 --pmc runs of --counters left in "
+                         "DIR (file prefix dec_ for decode, pf_ for --workload prefill)")
     return ap.parse_args()
 
 
@@ -353,8 +357,78 @@ def traffic_for(kernel_src_hash, name="scan_long_1m_counters.json"):
     return d.get("bytes_per_launch")
 
 
+COUNTER_RUNS = {  # workload kind -> (file prefix, kernel, kernel source, profile name, workload)
+    "decode": ("dec", "k_scan<", "csa2_index.hip", "scan_long_1m_counters.json",
+               "long_1m: B=1, L=1,048,576, indexer 4x64 FP4"),
+    "prefill": ("pf", "k_prefill<", "csa2_prefill.hip", "prefill_counters.json",
+                "prefill: 4096 queries at 258048..262143, L=262,144, indexer 8x128 FP4"),
+}
+
+
+def counter_summary(a, wl):
+    """HBM bytes per launch of the dominant kernel from two rocprofv3 --pmc runs (FETCH_SIZE,
+    WRITE_SIZE; KiB per dispatch), each scaled by what the same counter reads for the
+    calibration copy of a.calib_mb MiB that --counters runs after the kernel."""
+    import csv
+    import hashlib
+    kind = "prefill" if wl.n_q else "decode"
+    prefix, kname, src_name, out_name, wl_text = COUNTER_RUNS[kind]
+    raw = {}
+    for ctr in ("FETCH_SIZE", "WRITE_SIZE"):
+        with open(os.path.join(a.counter_summary, f"{prefix}_{ctr}_counter_collection.csv")) as f:
+            rows = [r for r in csv.DictReader(f) if r["Counter_Name"] == ctr]
+        kern = [float(r["Counter_Value"]) for r in rows
+                if kname in r["Kernel_Name"] and ", true," not in r["Kernel_Name"].split(kname)[1][:12]]
+        copies = [float(r["Counter_Value"]) for r in rows if "copyBuffer" in r["Kernel_Name"]]
+        if not kern or not copies:
+            raise SystemExit(f"{ctr}: no {kname} or copy dispatches in {a.counter_summary}")
+        raw[ctr] = (sum(kern) / len(kern), len(kern), max(copies))
+    calib = a.calib_mb << 20
+    # the copy reads and writes calib bytes; FETCH_SIZE counts half of them on this box
+    ff = calib / (raw["FETCH_SIZE"][2] * 1024.0)
+    wf = calib / (raw["WRITE_SIZE"][2] * 1024.0)
+    fetch = raw["FETCH_SIZE"][0] * 1024.0 * ff
+    write = raw["WRITE_SIZE"][0] * 1024.0 * wf
+    src_path = os.path.join(ROOT, "kv_cache_decode_csa2_amd", "csrc", src_name)
+    if kind == "prefill":
+        alg = prefill_work(wl, _layout_of(wl))["bytes"]
+    else:
+        alg = wl.max_ctx * (wl.H_I * (wl.d_I // 2 + wl.d_I // 32))
+    wl_flag = " --workload prefill" if kind == "prefill" else ""
+    d = {
+        "kernel": kname, "dispatches": raw["FETCH_SIZE"][1],
+        "fetch_kib_raw": round(raw["FETCH_SIZE"][0], 1), "write_kib_raw": round(raw["WRITE_SIZE"][0], 1),
+        "calibration": {"copy_mib": a.calib_mb, "fetch_kib_raw": raw["FETCH_SIZE"][2],
+                        "write_kib_raw": raw["WRITE_SIZE"][2], "fetch_factor": round(ff, 4),
+                        "write_factor": round(wf, 4)},
+        "fetch_bytes": int(fetch), "write_bytes": int(write), "bytes_per_launch": int(fetch + write),
+        "algorithmic_bytes": int(alg),
+        "source_sha256": hashlib.sha256(open(src_path, "rb").read()).hexdigest(),
+        "source": f"kv_cache_decode_csa2_amd/csrc/{src_name}",
+        "command": [f"rocprofv3 --pmc {c} --kernel-include-regex '{kname.rstrip('<')}|copyBuffer|copy' "
+                    f"--output-format csv -d gpurun_out/pmc -o {prefix}_{c} -- python3 bench.py"
+                    f"{wl_flag} --counters" for c in ("FETCH_SIZE", "WRITE_SIZE")]
+                   + [f"python3 bench.py{wl_flag} --counter-summary gpurun_out/pmc"],
+        "workload": wl_text,
+    }
+    with open(os.path.join(ROOT, "profiles", out_name), "w") as f:
+        json.dump(d, f, indent=1)
+        f.write("\n")
+    log(f"wrote profiles/{out_name}: {d['bytes_per_launch'] / 1e6:.1f} MB per launch "
+        f"(algorithmic {alg / 1e6:.1f} MB)")
+
+
+def _layout_of(wl):
+    class L:  # the index-cache block size, as csa2_layout states it
+        idx_block_bytes = 8 * wl.H_I * (wl.d_I // 2 + wl.d_I // 32)
+    return L
+
+
 def main():
     a = parse()
+    if a.counter_summary:
+        import synth_inputs as si
+        return counter_summary(a, si.workload(a.workload))
     if a.gpus != 1:
         print(json.dumps({"error": "this build runs on one GPU; --gpus must be 1 (multi-GPU "
                                    "sharding is a design note, not implemented)"}))
