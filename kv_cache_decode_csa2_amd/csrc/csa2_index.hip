@@ -295,11 +295,6 @@ __device__ __forceinline__ float blocks_to_lane63(float m) {
     return m;
 }
 
-// Target of stores a lane has nothing to write (so every step issues the same stores and the
-// loads of the next step never wait for them); its contents are never read.  Every wave of
-// a scan owns 4 x 64 floats of it, so these stores never contend for one cache line.
-__device__ float g_junk[kScanGridMax * kScanWaves * 4 * kWave];
-
 // Uniform load through the scalar data cache (read-only data; waits count on lgkmcnt, so they
 // never wait for the vector loads in flight).
 template <class T>
@@ -324,8 +319,9 @@ struct StepMeta {
 // (position in step) * H + head.  Software pipeline: step k issues the pool entries of step
 // k+6 (rescoring), the block-table entries of step k+4 and the keys of step k+2, in that
 // order, then computes step k.  Every value step k uses was requested by step k-2 or
-// earlier, and vector loads complete in issue order, so no wait covers a load of step k-1.  Every item issues the same vector stores (lanes without output write to
-// g_junk), so the wait for a step's keys never covers the stores or the next step's loads.  Loads never branch: an absent block reads physical block 0 and its
+// earlier, and vector loads complete in issue order, so no wait covers a load of step k-1.
+// An item's scores and maxima leave in two stores at its last step, masked to the lanes
+// that hold output.  Loads never branch: an absent block reads physical block 0 and its
 // positions are masked.  OFF32: every key byte lies within 4 GiB of the cache base, so
 // addresses are a scalar base plus a 32-bit lane offset.
 template <int H, int G, bool RESCORE, bool OFF32>
@@ -379,7 +375,6 @@ __global__ __launch_bounds__(kScanThreads, 2) void k_scan(ScanArgs a) {
     // step consumes the value
     const uint32_t sc_byte = (uint32_t)(CODES + (slot * H + h) * G);
     const uint32_t sc_off = sc_byte & ~3u, sc_sh = 8u * (sc_byte & 3u);
-    float *junk = g_junk + (size_t)gw * 4 * kWave + lane;
 
     constexpr int PPS = kBlk * BPW;                    // positions per step
     constexpr int STEPS = NSTEP >= 4 ? NSTEP : 4;      // steps per loop iteration (whole items)
@@ -473,10 +468,6 @@ __global__ __launch_bounds__(kScanThreads, 2) void k_scan(ScanArgs a) {
         KeyRegs<G> K[4];
         load_keys(mt[0], K[0]);
         load_keys(mt[1], K[1]);
-        // an item's two stores, once: the loop is entered with the memory operations in
-        // flight that every iteration leaves (its waits stay minimal)
-        junk[kWave] = 0.0f;
-        junk[2 * kWave] = 0.0f;
 
         float *ps_row = RESCORE ? a.poolsc + (int64_t)b * a.K_blk * kBlk : a.pscore + (int64_t)b * a.maxb * kBlk;
         float *pb_row = RESCORE ? a.poolbmax + (int64_t)b * a.K_blk : a.bscore + (int64_t)b * a.bstride;
@@ -510,19 +501,21 @@ __global__ __launch_bounds__(kScanThreads, 2) void k_scan(ScanArgs a) {
                 const int e_item = mt[0].e0 - (NSTEP - 1) * BPW;
                 const bool item_ok = k2 < kend;
                 const bool pos_ok = item_ok && e_item + lane / kBlk < n_lim;
-                float *ps = pos_ok && ps_on ? ps_row + (int64_t)e_item * kBlk + lane : junk;
-                float *pb = junk + kWave;
+                // (lanes without output are masked off: no store of theirs reaches memory)
+                float *ps = ps_row + (int64_t)e_item * kBlk + lane;
+                float *pb = pb_row + e_item + lane;
                 float vstore = acc_b;
-                if (lane < kBlk && item_ok && e_item + lane < n_lim && pb_on) pb = pb_row + e_item + lane;
+                bool pb_ok = lane < kBlk && item_ok && e_item + lane < n_lim && pb_on;
                 if (!RESCORE) {
                     const float g63 = blocks_to_lane63<H>(gm);
                     if (lane == kWave - 1) {
                         vstore = g63;
-                        if (item_ok && pg_on) pb = pg_row + e_item / kItemBlocks;
+                        pb_ok = item_ok && pg_on;
+                        pb = pg_row + e_item / kItemBlocks;
                     }
                 }
-                *ps = acc_p;
-                *pb = vstore;
+                if (pos_ok && ps_on) *ps = acc_p;
+                if (pb_ok) *pb = vstore;
             }
 #pragma unroll
             for (int i = 0; i < DM - 1; i++) mt[i] = mt[i + 1];
