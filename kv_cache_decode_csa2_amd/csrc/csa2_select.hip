@@ -462,7 +462,9 @@ __device__ __forceinline__ void select_topk(const SelectArgs &a, int b, int L, c
     int32_t *out = a.topk + (int64_t)b * a.k;
     uint32_t lam = 0u;
     if (need > 0 && need < (n_vis >> 16) && need <= n_ent) {
-        if (REINDEX) lam = n_ent > need ? range_select(bm, need, sm.sel).thr : 0u;
+        // Reindex: kmax receives the largest rescored block maximum, the upper end of every
+        // candidate key
+        if (REINDEX) lam = n_ent > need ? range_select(bm, need, sm.sel, false, 0u, 0u, &kmax).thr : 0u;
         else lam = pool_thr;
     }
     // candidate positions scoring >= lam (Reindex: of entries whose maximum reaches lam)
@@ -486,8 +488,9 @@ __device__ __forceinline__ void select_topk(const SelectArgs &a, int b, int L, c
             uint32_t ob = 0;
             emit_all(it, pos, out, (uint32_t)a.k, ob, sm.sel);
         } else {
-            // Full with a pool threshold: every candidate key lies in [lam, largest key]
-            const bool bounded = !REINDEX && lam != 0u && kmax != 0u;
+            // with a lower bound, every candidate key lies in [lam, largest key] (Full: the
+            // largest group maximum; Reindex: the largest rescored block maximum)
+            const bool bounded = lam != 0u && kmax != 0u;
             select_emit(it, pos, need, out, (uint32_t)a.k, sm, bounded, lam, kmax);
         }
     }
