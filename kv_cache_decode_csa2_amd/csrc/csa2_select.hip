@@ -533,10 +533,12 @@ __global__ __launch_bounds__(kSelThreads) void k_select(SelectArgs a) {
     uint32_t kmax;
     const int plen = select_pool(a, b, nb, sm, graw, &thr, &kmax);
     const int np = min(plen, nb);
+    select_topk<false>(a, b, L, sm.pool, np, thr, kmax, sm);
+    // the pool leaves last: stores complete in issue order with loads, so a store issued
+    // before the top-k's score loads would have delayed their use by its write round trip
     int32_t *pool_out = a.pool_blocks + (int64_t)b * a.K_blk;
     for (int i = tid; i < a.K_blk; i += kSelThreads) pool_out[i] = i < np ? sm.pool[i] : -1;
     if (tid == 0) a.pool_len[b] = np;
-    select_topk<false>(a, b, L, sm.pool, np, thr, kmax, sm);
 }
 
 constexpr size_t kSelectShared = sizeof(SelectShared);
