@@ -361,33 +361,35 @@ __global__ __launch_bounds__(NS * kStreamThreads, 3 - NS) void k_attn(AttnArgs a
                 }
             }
         };
-        // ---- the appended row, when this stream's chunk attends it: its 16 threads quantise
-        //      one group each from the staged fp32 row into LDS (and, for the first head group,
-        //      into the ring).  NS = 2 does it before the barriers below, which then order the
+        // ---- the appended row, when this stream's chunk attends it: the stream's first wave
+        //      quantises it from the staged fp32 row into LDS (and, for the first head group,
+        //      into the ring), four lanes per 32-group (8 elements each, the group's amax by a
+        //      quad max).  NS = 2 does it before the barriers below, which then order the
         //      writes before its lane reads them; NS = 1 after them, behind a barrier of its own.
         auto quant_fresh = [&] {
-        if (c == fc && ts < kD / 32) {
-            float v[32];
+        if (c == fc && ts < kWave) {
+            const int g = ts >> 2, qq = ts & 3;  // group, quarter of the group
+            const float4 t0 = fstage[16 * (2 * qq) + g], t1 = fstage[16 * (2 * qq + 1) + g];
+            const float v[8] = {t0.x, t0.y, t0.z, t0.w, t1.x, t1.y, t1.z, t1.w};
+            float am = 0.0f;
 #pragma unroll
-            for (int j = 0; j < 8; j++) {
-                const float4 t4 = fstage[16 * j + ts];
-                v[4 * j] = t4.x;
-                v[4 * j + 1] = t4.y;
-                v[4 * j + 2] = t4.z;
-                v[4 * j + 3] = t4.w;
+            for (int i = 0; i < 8; i++) am = fmaxf(am, fabsf(v[i]));
+            am = fmaxf(am, dpp_f<0xB1>(am));  // quad [1,0,3,2]
+            am = fmaxf(am, dpp_f<0x4E>(am));  // quad [2,3,0,1]
+            const int e = group_exponent(am, 8);
+            uint32_t w0 = 0u, w1 = 0u;
+#pragma unroll
+            for (int j = 0; j < 4; j++) {
+                w0 |= fp8_code(v[j], e) << (8 * j);
+                w1 |= fp8_code(v[4 + j], e) << (8 * j);
             }
-            uint32_t w[8];
-            const uint32_t sc = quant_fp8_regs(v, w);
-            uint4 *d4 = reinterpret_cast<uint4 *>(sh.fresh_row + 32 * ts);
-            d4[0] = make_uint4(w[0], w[1], w[2], w[3]);
-            d4[1] = make_uint4(w[4], w[5], w[6], w[7]);
-            sh.fresh_row[kD + ts] = (uint8_t)sc;
+            const uint2 w01 = make_uint2(w0, w1);
+            *reinterpret_cast<uint2 *>(sh.fresh_row + 32 * g + 8 * qq) = w01;
+            if (qq == 0) sh.fresh_row[kD + g] = (uint8_t)(e + 127);
             if (hg == 0) {
                 uint8_t *dst = a.swa_out + ((int64_t)b * a.rstride + np_b % a.C) * (kD + kD / 32);
-                uint4 *g4p = reinterpret_cast<uint4 *>(dst + 32 * ts);
-                g4p[0] = d4[0];
-                g4p[1] = d4[1];
-                dst[kD + ts] = (uint8_t)sc;
+                *reinterpret_cast<uint2 *>(dst + 32 * g + 8 * qq) = w01;
+                if (qq == 0) dst[kD + g] = (uint8_t)(e + 127);
             }
         }
         };
