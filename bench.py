@@ -2,7 +2,8 @@
 context on one MI355X, with the scan kernel's HBM roofline and the CPU oracle beside it.
 
 A step is one decode group over the whole batch: for every layer the current token's window
-row is appended, the Full layer also appends its global-KV row and runs the full indexer,
+row is appended, the Full layer also appends its global-KV row and runs the full indexer
+(one fused call),
 Reindex rescores the pool, Reuse keeps the previous top-k, and every layer runs sparse
 attention.  Inputs are seeded synthetic tensors resident in HBM before timing starts.  Each
 step uses the next of R cache replicas so the 256 MB Infinity Cache cannot hold the
@@ -110,11 +111,10 @@ class Bench:
         kv, idx, ws = self.kv[r], self.idx[r], self.ws[r]
         for lay in self.layers:
             if lay["mode"] == "F":
-                k.csa2_append_global(c, self.tok_lat, self.tok_key, g.table, g.n_blocks,
-                                     lay["pos"], 1, kv, idx)
-            if lay["mode"] == "F":
-                k.csa2_index_full(c, lay["qc"], lay["qs"], lay["w"], idx, g.n_blocks, g.table,
-                                  g.ctx, self.pool, self.pool_len, self.topk, self.topk_len, ws)
+                # the token's global-KV row (position L-1) is appended inside the index call
+                k.csa2_index_full_append(c, self.tok_lat, self.tok_key, lay["qc"], lay["qs"],
+                                         lay["w"], kv, idx, g.n_blocks, g.table, g.ctx,
+                                         self.pool, self.pool_len, self.topk, self.topk_len, ws)
             elif lay["mode"] == "R":
                 k.csa2_index_reindex(c, lay["qc"], lay["qs"], lay["w"], idx, g.n_blocks, g.table,
                                      g.ctx, self.pool, self.pool_len, self.topk, self.topk_len, ws)

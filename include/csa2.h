@@ -180,6 +180,24 @@ int csa2_index_full_finish(const csa2_config *cfg, const uint8_t *q_codes,
                            int32_t *pool_len, int32_t *topk, int32_t *topk_len, void *ws,
                            size_t ws_bytes, hipStream_t stream);
 
+/* Global append fused with the Full index step (a Full layer appends its token to the
+ * global caches [KV], then indexes the context that includes it): exactly
+ * csa2_append_global(cfg, latent, idx_k, block_table, maxb, n_blocks, pos0 = ctx_len - 1,
+ * batch, 1, kv_cache, idx_cache) followed by csa2_index_full(cfg, q_codes, ...), bit for bit
+ * (cache bytes, pool and top-k), in one scan launch and one selection launch: the wave that
+ * scores the block of position ctx_len[b] - 1 quantises that token's key and writes it (and
+ * the latent row) before it reads the block.  latent [batch][512] fp32 (may be NULL: no
+ * main-KV append; kv_cache may then be NULL), idx_k [batch][H_I*d_I] fp32, on the device.
+ * A sequence with ctx_len <= 0 or ctx_len > 8*maxb appends nothing (as the two calls).
+ * Workspace: CSA2_OP_INDEX_FULL bytes.  UNSUPPORTED if latent is given and kv_dim != 512. */
+int csa2_index_full_append(const csa2_config *cfg, const float *latent, const float *idx_k,
+                           const uint8_t *q_codes, const uint8_t *q_scales, const float *w,
+                           uint8_t *kv_cache, uint8_t *idx_cache, int64_t n_blocks,
+                           const int32_t *block_table, int32_t maxb, const int32_t *ctx_len,
+                           int32_t batch, int32_t *pool_blocks, int32_t *pool_len,
+                           int32_t *topk, int32_t *topk_len, void *ws, size_t ws_bytes,
+                           hipStream_t stream);
+
 /* Reindex mode [KV][RR]: rescore only the positions of the stored pool (pool_blocks /
  * pool_len of the latest Full layer) with this layer's q/w and keep the k best, as in
  * csa2_index_full (same workspace rules).  Reuse mode has no index call: pass the previous

@@ -24,7 +24,7 @@ EXPORTS = [
     "csa2_index_scores", "csa2_index_full", "csa2_index_full_scan", "csa2_index_full_finish",
     "csa2_index_reindex", "csa2_index_prefill", "csa2_index_prefill_scan",
     "csa2_index_prefill_finish", "csa2_sparse_attn", "csa2_sparse_attn_append",
-    "csa2_sparse_attn_prefill", "csa2_status_str",
+    "csa2_sparse_attn_prefill", "csa2_index_full_append", "csa2_status_str",
 ]
 
 
@@ -73,6 +73,8 @@ def load() -> C.CDLL:
             "csa2_index_full_scan": [cfgp, vp, vp, vp, vp, i64, vp, i32, vp, i32, vp, sz, vp],
             "csa2_index_full_finish": [cfgp, vp, vp, vp, vp, i64, vp, i32, vp, i32, vp, vp, vp,
                                        vp, vp, sz, vp],
+            "csa2_index_full_append": [cfgp, vp, vp, vp, vp, vp, vp, vp, i64, vp, i32, vp, i32,
+                                       vp, vp, vp, vp, vp, sz, vp],
             "csa2_index_reindex": [cfgp, vp, vp, vp, vp, i64, vp, i32, vp, i32, vp, vp, vp, vp,
                                    vp, sz, vp],
             "csa2_index_prefill": [cfgp, vp, vp, vp, i32, i32, vp, i64, vp, i32, vp, vp, vp, vp,
@@ -205,6 +207,16 @@ def csa2_index_full(cfg, q_codes, q_scales, w, idx_cache, n_blocks, block_table,
     _call("csa2_index_full", C.byref(cfg), _p(q_codes), _p(q_scales), _p(w), _p(idx_cache),
           int(n_blocks), _p(block_table), maxb, _p(ctx_len), batch, _p(pool_blocks),
           _p(pool_len), _p(topk), _p(topk_len), _p(ws), ws.numel(), _stream(stream))
+
+
+def csa2_index_full_append(cfg, latent, idx_k, q_codes, q_scales, w, kv_cache, idx_cache,
+                           n_blocks, block_table, ctx_len, pool_blocks, pool_len, topk, topk_len,
+                           ws, stream=None):
+    batch, maxb = block_table.shape
+    _call("csa2_index_full_append", C.byref(cfg), _p(latent), _p(idx_k), _p(q_codes),
+          _p(q_scales), _p(w), _p(kv_cache), _p(idx_cache), int(n_blocks), _p(block_table), maxb,
+          _p(ctx_len), batch, _p(pool_blocks), _p(pool_len), _p(topk), _p(topk_len), _p(ws),
+          ws.numel(), _stream(stream))
 
 
 def csa2_index_reindex(cfg, q_codes, q_scales, w, idx_cache, n_blocks, block_table, ctx_len,

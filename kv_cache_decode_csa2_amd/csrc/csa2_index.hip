@@ -26,6 +26,7 @@
 #include <algorithm>
 
 #include "csa2_block.h"
+#include "csa2_quant.h"
 #include "csa2_select.h"
 
 namespace csa2 {
@@ -173,6 +174,47 @@ struct ScanArgs {
     int32_t K_blk;
     float *poolsc;
     float *poolbmax;  // rescore: pool block maxima [B][K_blk]
+    // fused append of each sequence's current token, position ctx_len[b] - 1 (Full scan
+    // only; new_key null: none): its indexer key [B][H*dI] and main latent [B][kAppD] fp32
+    // (new_lat may be null), quantised into the caches by the wave that scores its block
+    const float *new_key;
+    const float *new_lat;
+    uint8_t *idx_w;  // the indexer-key cache (the same bytes as idx_cache)
+    uint8_t *kv_w;   // the main-KV cache
+};
+
+constexpr int kAppD = 512;  // main latent dim of the fused append
+
+// MXFP4 quantisation of 32-groups spread over 8 lanes: lane l holds elements 4(l%8)..+3 of
+// group l/8.  Returns the group's E8M0 code in every lane and, in the even lane of each
+// lane pair, the code word of the pair's 8 elements (element 8i+j in bits 4j..4j+3, i =
+// (l%8)/2), the word layout of quant_fp4_regs.  The amax is a max (exact in any order) and
+// each element is encoded by fp4_code, so the codes equal quant_fp4's.
+__device__ __forceinline__ void coop_fp4(float4 v, uint32_t &word, uint32_t &scale) {
+    auto dpp = [](float x, auto ctrl) {
+        return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), decltype(ctrl)::value, 0xf, 0xf, false));
+    };
+    float am = fmaxf(fmaxf(fabsf(v.x), fabsf(v.y)), fmaxf(fabsf(v.z), fabsf(v.w)));
+    am = fmaxf(am, dpp(am, std::integral_constant<int, 0xB1>{}));   // quad [1,0,3,2]
+    am = fmaxf(am, dpp(am, std::integral_constant<int, 0x4E>{}));   // quad [2,3,0,1]
+    am = fmaxf(am, dpp(am, std::integral_constant<int, 0x141>{}));  // row_half_mirror (8 lanes)
+    const int e = group_exponent(am, 2);
+    const uint32_t c = fp4_code(v.x, e) | fp4_code(v.y, e) << 4 | fp4_code(v.z, e) << 8 |
+                       fp4_code(v.w, e) << 12;
+    const uint32_t nb = (uint32_t)__builtin_amdgcn_mov_dpp((int)c, 0xB1, 0xf, 0xf, false);
+    word = c | nb << 16;
+    scale = (uint32_t)(e + 127);
+}
+
+// The new token's inputs of one sequence as one wave loads them: key float4 chunk 64r + lane
+// in key[r], latent chunk 64r + lane in lat[r], and the table entry of its block.
+template <int H, int G>
+struct AppendRegs {
+    static constexpr int KR = (H * G * 8 + kWave - 1) / kWave;  // rounds of key chunks
+    static constexpr int LR = kAppD / 4 / kWave;                // rounds of latent chunks
+    float4 key[KR];
+    float4 lat[LR];
+    int ph;
 };
 
 // Items (8 blocks or 8 pool entries) of sequence b.
@@ -186,17 +228,21 @@ __device__ __forceinline__ int items_of(const ScanArgs &a, int b) {
     return (nb + kItemBlocks - 1) / kItemBlocks;
 }
 
-// Exclusive prefix of items per sequence in LDS (prefix[0..B]) and the clamped lengths
-// (lens[0..B-1]); returns the total.  Each length (and pool length) is loaded once.
+// Exclusive prefix of items per sequence in LDS (prefix[0..B]), the clamped lengths
+// (lens[0..B-1]) and the lengths as given (raw[0..B-1]); returns the total.  Each length
+// (and pool length) is loaded once.
 template <bool RESCORE>
-__device__ int build_item_prefix(const ScanArgs &a, int32_t *prefix, int32_t *lens, uint32_t *sh_scan) {
+__device__ int build_item_prefix(const ScanArgs &a, int32_t *prefix, int32_t *lens, int32_t *raw,
+                                 uint32_t *sh_scan) {
     uint32_t running = 0;
     for (int base = 0; base < a.B; base += kScanThreads) {
         const int b = base + (int)threadIdx.x;
         uint32_t v = 0u;
         if (b < a.B) {
-            const int L = clamp_len(a.ctx_len[b], a.maxb);
+            const int32_t Lr = a.ctx_len[b];
+            const int L = clamp_len(Lr, a.maxb);
             lens[b] = L;
+            raw[b] = Lr;
             if (RESCORE) {
                 const int pl = max(0, min(a.pool_len[b], a.K_blk));
                 v = (uint32_t)((pl + kItemBlocks - 1) / kItemBlocks);
@@ -324,15 +370,15 @@ struct StepMeta {
 // that hold output.  Loads never branch: an absent block reads physical block 0 and its
 // positions are masked.  OFF32: every key byte lies within 4 GiB of the cache base, so
 // addresses are a scalar base plus a 32-bit lane offset.
-template <int H, int G, bool RESCORE, bool OFF32>
+template <int H, int G, bool RESCORE, bool OFF32, bool APPEND>
 __global__ __launch_bounds__(kScanThreads, 2) void k_scan(ScanArgs a) {
     constexpr int BPW = 8 / H;                         // blocks per wave step
     constexpr int NSTEP = kItemBlocks / BPW;           // steps per item
     constexpr int CODES = kBlk * H * 16 * G;
     constexpr int BYTES = CODES + kBlk * H * G;
-    extern __shared__ int32_t sh_dyn[];  // item prefix [B + 1], clamped lengths [B]
+    extern __shared__ int32_t sh_dyn[];  // item prefix [B + 1], clamped lengths [B], lengths [B]
     __shared__ __align__(16) uint32_t sh_scan[kScanWaves];
-    int32_t *sh_prefix = sh_dyn, *sh_len = sh_dyn + a.B + 1;
+    int32_t *sh_prefix = sh_dyn, *sh_len = sh_dyn + a.B + 1, *sh_raw = sh_dyn + 2 * a.B + 1;
 
     const int lane = threadIdx.x & (kWave - 1);
     const int wave = __builtin_amdgcn_readfirstlane((int)threadIdx.x / kWave);
@@ -344,7 +390,7 @@ __global__ __launch_bounds__(kScanThreads, 2) void k_scan(ScanArgs a) {
     // several sequences -> a contiguous range, so each wave meets few sequences.
     const bool inter = a.B == 1;
     // pipeline depth: bookkeeping of steps k .. k+DM-1, block-table entries of steps k .. k+DPH-1
-    constexpr int DM = 7, DPH = 4;
+    constexpr int DM = 7, DPH = 4, DK = 2;  // (and keys of steps k .. k+DK-1)
     // One sequence: the query and the first steps' entries (scan: block-table entries;
     // rescoring: pool entries) depend on no length and are requested before the item prefix,
     // whose length load and barriers they overlap (entries read clamped into the row and
@@ -363,7 +409,7 @@ __global__ __launch_bounds__(kScanThreads, 2) void k_scan(ScanArgs a) {
         }
         load_query_raw<H, G>(QR, a.q_codes, a.q_scales, a.w, h);
     }
-    const int total = __builtin_amdgcn_readfirstlane(build_item_prefix<RESCORE>(a, sh_prefix, sh_len, sh_scan));
+    const int total = __builtin_amdgcn_readfirstlane(build_item_prefix<RESCORE>(a, sh_prefix, sh_len, sh_raw, sh_scan));
     const int per = (total + nwaves - 1) / nwaves;
     const int it_begin = inter ? gw : gw * per;
     const int it_end = inter ? total : min(total, it_begin + per);
@@ -454,6 +500,81 @@ __global__ __launch_bounds__(kScanThreads, 2) void k_scan(ScanArgs a) {
         else
             load_query<H, G>(Q, a.q_codes + (size_t)b * H * 16 * G, a.q_scales + (size_t)b * H * G,
                              a.w + (size_t)b * H, h);
+
+        // ---- fused append: does this segment score the block of the new token (position
+        //      pn = L_b - 1, unclamped)?  k_new: that step (uniform; -1: not here).  Its inputs
+        //      are requested now; before the keys of step k_new are loaded, the wave quantises
+        //      them and the lane that loads each key chunk of the new slot writes it first, so
+        //      that lane's own load reads its own store (the latent goes to the main-KV cache).
+        int k_new = -1, pn = -1;
+        AppendRegs<H, G> ar;
+        if (APPEND) {
+            pn = __builtin_amdgcn_readfirstlane(sh_raw[b]) - 1;
+            if (pn >= 0 && pn / kBlk < a.maxb) {
+                const int jn = pn / kBlk, itn = jn / kItemBlocks, stn = (jn % kItemBlocks) / BPW;
+                if (inter) {
+                    if (itn >= gw && (itn - gw) % nwaves == 0) k_new = (itn - gw) / nwaves * NSTEP + stn;
+                } else {
+                    const int kk = (__builtin_amdgcn_readfirstlane(sh_prefix[b]) + itn - it_begin) * NSTEP + stn;
+                    if (kk >= kseg && kk < kend) k_new = kk;
+                }
+            }
+            if (k_new >= 0) {
+                const float4 *kb = reinterpret_cast<const float4 *>(a.new_key + (size_t)b * H * G * 32);
+#pragma unroll
+                for (int r = 0; r < ar.KR; r++) ar.key[r] = kb[min(r * kWave + lane, H * G * 8 - 1)];
+                if (a.new_lat) {
+                    const float4 *lb = reinterpret_cast<const float4 *>(a.new_lat + (size_t)b * kAppD);
+#pragma unroll
+                    for (int r = 0; r < ar.LR; r++) ar.lat[r] = lb[r * kWave + lane];
+                }
+                ar.ph = table_row[pn / kBlk];
+            }
+        }
+        auto append_write = [&] {
+            const int ph = ar.ph >= 0 && (int64_t)ar.ph < a.n_blocks ? ar.ph : -1;
+            const int sn = pn % kBlk;
+            // key: groups q = h*G + g in rounds of 8; lane (pair) words, group scales
+            uint32_t kw[ar.KR], ksc[ar.KR];
+#pragma unroll
+            for (int r = 0; r < ar.KR; r++) coop_fp4(ar.key[r], kw[r], ksc[r]);
+            const bool writer = ph >= 0 && bw == (pn / kBlk) % BPW && slot == sn;
+#pragma unroll
+            for (int g = 0; g < G; g++) {
+                const int q = h * G + g, r = q / 8, src = 8 * (q % 8);
+                uint32_t wv[4], sv = 0u;
+#pragma unroll
+                for (int rr = 0; rr < ar.KR; rr++) {
+#pragma unroll
+                    for (int i = 0; i < 4; i++) {
+                        const uint32_t x = (uint32_t)__builtin_amdgcn_ds_bpermute(4 * (src + 2 * i), (int)kw[rr]);
+                        wv[i] = rr == r ? x : (rr == 0 ? x : wv[i]);
+                    }
+                    const uint32_t y = (uint32_t)__builtin_amdgcn_ds_bpermute(4 * src, (int)ksc[rr]);
+                    sv = rr == r ? y : (rr == 0 ? y : sv);
+                }
+                if (writer) {
+                    uint8_t *blk = a.idx_w + (int64_t)ph * BYTES;
+                    *reinterpret_cast<uint4 *>(blk + ((g * kBlk + sn) * H + h) * 16) = make_uint4(wv[0], wv[1], wv[2], wv[3]);
+                    blk[CODES + (sn * H + h) * G + g] = (uint8_t)sv;
+                }
+            }
+            if (a.new_lat && ph >= 0) {
+                uint8_t *row = a.kv_w + ((int64_t)ph * kBlk + sn) * (kAppD / 2 + kAppD / 32);
+#pragma unroll
+                for (int r = 0; r < ar.LR; r++) {
+                    uint32_t lw, lsc;
+                    coop_fp4(ar.lat[r], lw, lsc);
+                    const int c = r * kWave + lane, gl = c / 8;
+                    if ((c & 1) == 0) *reinterpret_cast<uint32_t *>(row + 16 * gl + 2 * (c % 8)) = lw;
+                    if (c % 8 == 0) row[kAppD / 2 + gl] = (uint8_t)lsc;
+                }
+            }
+        };
+        if (APPEND && k_new >= 0 && k_new < k + DK) {  // before the prologue's key loads
+            append_write();
+            k_new = -1;
+        }
         // pipeline state at step k: entries of steps k..k+5 (rescoring: pool entries loaded),
         // table entries of steps k..k+3 loaded, keys of steps k and k+1 loaded (one sequence:
         // k = 0 here, and the early requests above stand in for the first loads)
@@ -522,6 +643,10 @@ __global__ __launch_bounds__(kScanThreads, 2) void k_scan(ScanArgs a) {
         };
         // iterations of STEPS steps (whole items); steps past the segment end are masked
         for (; k < kend; k += STEPS) {
+            if (APPEND && k_new >= 0 && k_new - DK < k + STEPS) {  // before this iteration's key loads
+                append_write();
+                k_new = -1;
+            }
 #pragma unroll
             for (int st = 0; st < STEPS; st++) body(k + st, st % NSTEP, K[st % 4], K[(st + 2) % 4]);
         }
@@ -543,13 +668,19 @@ bool off32(const ScanArgs &a) {
 }
 template <int H, int G>
 void launch_scan(dim3 g, size_t sh, hipStream_t s, const ScanArgs &a) {
-    if (off32<H, G>(a)) k_scan<H, G, false, true><<<g, kScanThreads, sh, s>>>(a);
-    else k_scan<H, G, false, false><<<g, kScanThreads, sh, s>>>(a);
+    const bool o32 = off32<H, G>(a);
+    if (a.new_key) {  // the fused append keeps its own registers out of the plain scan
+        if (o32) k_scan<H, G, false, true, true><<<g, kScanThreads, sh, s>>>(a);
+        else k_scan<H, G, false, false, true><<<g, kScanThreads, sh, s>>>(a);
+    } else {
+        if (o32) k_scan<H, G, false, true, false><<<g, kScanThreads, sh, s>>>(a);
+        else k_scan<H, G, false, false, false><<<g, kScanThreads, sh, s>>>(a);
+    }
 }
 template <int H, int G>
 void launch_rescore(dim3 g, size_t sh, hipStream_t s, const ScanArgs &a) {
-    if (off32<H, G>(a)) k_scan<H, G, true, true><<<g, kScanThreads, sh, s>>>(a);
-    else k_scan<H, G, true, false><<<g, kScanThreads, sh, s>>>(a);
+    if (off32<H, G>(a)) k_scan<H, G, true, true, false><<<g, kScanThreads, sh, s>>>(a);
+    else k_scan<H, G, true, false, false><<<g, kScanThreads, sh, s>>>(a);
 }
 
 bool pick(int H, int dI, KernSet *ks) {
@@ -613,7 +744,7 @@ int scan_grid(int64_t items) {
     return (int)std::max<int64_t>(1, std::min<int64_t>(wgs, kScanGridMax));
 }
 
-size_t prefix_bytes(int B) { return sizeof(int32_t) * (2 * (size_t)B + 1); }
+size_t prefix_bytes(int B) { return sizeof(int32_t) * (3 * (size_t)B + 1); }
 
 }  // namespace
 
@@ -792,6 +923,42 @@ extern "C" int csa2_index_full(const csa2_config *c, const uint8_t *q_codes,
     if (!pool_blocks || !pool_len || !topk || !topk_len || !ws) return CSA2_ERR_INVALID;
     int st = csa2_index_full_scan(c, q_codes, q_scales, w, idx_cache, n_blocks, block_table,
                                   maxb, ctx_len, batch, ws, ws_bytes, stream);
+    if (st) return st;
+    return csa2_index_full_finish(c, q_codes, q_scales, w, idx_cache, n_blocks, block_table,
+                                  maxb, ctx_len, batch, pool_blocks, pool_len, topk, topk_len,
+                                  ws, ws_bytes, stream);
+}
+
+extern "C" int csa2_index_full_append(const csa2_config *c, const float *latent,
+                                      const float *idx_k, const uint8_t *q_codes,
+                                      const uint8_t *q_scales, const float *w, uint8_t *kv_cache,
+                                      uint8_t *idx_cache, int64_t n_blocks,
+                                      const int32_t *block_table, int32_t maxb,
+                                      const int32_t *ctx_len, int32_t batch, int32_t *pool_blocks,
+                                      int32_t *pool_len, int32_t *topk, int32_t *topk_len,
+                                      void *ws, size_t ws_bytes, hipStream_t stream) {
+    CSA2_CHECK_INDEX_ARGS();
+    if (!idx_k || (latent && !kv_cache) || !pool_blocks || !pool_len || !topk || !topk_len || !ws)
+        return CSA2_ERR_INVALID;
+    if (latent && c->kv_dim != kAppD) return CSA2_ERR_UNSUPPORTED;
+    const WsIdx L = ws_idx(batch, maxb, c->pool_blocks);
+    if (ws_bytes < L.total) return CSA2_ERR_WORKSPACE;
+    if (batch == 0) return CSA2_OK;
+    KernSet ks;
+    pick(c->n_idx_heads, c->idx_dim, &ks);
+    ScanArgs a = scan_args(c, q_codes, q_scales, w, idx_cache, n_blocks, block_table, maxb,
+                           ctx_len, batch);
+    uint8_t *base = (uint8_t *)ws;
+    a.pscore = (float *)(base + L.pscore);
+    a.bscore = (float *)(base + L.bscore);
+    a.bstride = ngmax_of(maxb) * kItemBlocks;
+    a.gmax = (float *)(base + L.gmax);
+    a.new_key = idx_k;
+    a.new_lat = latent;
+    a.idx_w = idx_cache;
+    a.kv_w = kv_cache;
+    ks.scan(dim3(scan_grid((int64_t)batch * ngmax_of(maxb))), prefix_bytes(batch), stream, a);
+    const int st = launched();
     if (st) return st;
     return csa2_index_full_finish(c, q_codes, q_scales, w, idx_cache, n_blocks, block_table,
                                   maxb, ctx_len, batch, pool_blocks, pool_len, topk, topk_len,

@@ -265,3 +265,46 @@ def test_fused_window_append_matches_two_calls(ahead, kk, W):
     assert torch.equal(ring_a, ring_b)
     assert np.array_equal(_np(out_a).view(np.uint32), _np(out_b).view(np.uint32))
     assert np.array_equal(_np(lse_a).view(np.uint32), _np(lse_b).view(np.uint32))
+
+
+@pytest.mark.parametrize("H,d,ctx,with_lat", [
+    (4, 64, [5000], True),              # one sequence: the new block in the owner's first steps
+    (4, 64, [300000], True),            # one sequence: the owner writes in its loop (3rd item)
+    (8, 128, [700, 5000, 64, 1, 0, 9], True),  # ragged batch, contiguous ranges per wave
+    (1, 32, [300, 17], False),          # one head, no main-KV append
+])
+def test_full_append_matches_two_calls(H, d, ctx, with_lat):
+    """csa2_index_full_append == csa2_append_global at ctx_len - 1 followed by
+    csa2_index_full: identical cache bytes (indexer keys and main KV), pools and top-k.  The
+    appended token gets fresh values, unlike the slot's bytes in the cache, so a missing or
+    misplaced write changes both the caches and the index sets."""
+    import kv_cache_decode_csa2_amd as k
+    from harness import make_table
+    wl = si.small("fapp", 170 + H + d + len(ctx), ctx, H_I=H, d_I=d, K_blk=16, k=40)
+    table, nblk = make_table(wl.ctx, seed=wl.seed, permute=True)
+    g = GpuState(wl, table, nblk, with_latent=True)
+    qc, qs, w = g.layer_q(0)
+    new_key = dev(si.normal(171, 901, (wl.B, H * d)))
+    new_lat = dev(si.normal(171, 902, (wl.B, wl.D))) if with_lat else None
+    pos = g.ctx - 1
+    res = []
+    for fused in (False, True):
+        kv, idx = g.kv.clone(), g.idx.clone()
+        pool = torch.full((wl.B, wl.K_blk), -7, dtype=torch.int32, device="cuda")
+        pl = torch.zeros(wl.B, dtype=torch.int32, device="cuda")
+        topk = torch.full((wl.B, wl.k), -7, dtype=torch.int32, device="cuda")
+        tl = torch.zeros(wl.B, dtype=torch.int32, device="cuda")
+        if fused:
+            k.csa2_index_full_append(g.cfg, new_lat, new_key, qc, qs, w, kv if with_lat else None,
+                                     idx, g.n_blocks, g.table, g.ctx, pool, pl, topk, tl, g.ws)
+        else:
+            k.csa2_append_global(g.cfg, new_lat, new_key, g.table, g.n_blocks, pos, 1,
+                                 kv if with_lat else None, idx)
+            k.csa2_index_full(g.cfg, qc, qs, w, idx, g.n_blocks, g.table, g.ctx, pool, pl, topk,
+                              tl, g.ws)
+        torch.cuda.synchronize()
+        res.append((_np(kv), _np(idx), _np(pool), _np(pl), _np(topk), _np(tl)))
+    names = ("kv cache", "idx cache", "pool", "pool_len", "topk", "topk_len")
+    for name, x, y in zip(names, res[0], res[1]):
+        assert np.array_equal(x, y), (name, _first_diff(x, y))
+    assert not np.array_equal(res[0][1], _np(g.idx)), "the append changed no key byte"
