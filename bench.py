@@ -106,10 +106,13 @@ class Bench:
         self.lse = torch.empty((B, wl.H_q), dtype=torch.float32, device="cuda")
         torch.cuda.synchronize()
 
-    def step(self, r):
+    def step(self, r, only=None):
+        """One decode group on replica r (only: just that layer, for the per-mode times)."""
         k, g, c = self.k, self.g, self.cfg
         kv, idx, ws = self.kv[r], self.idx[r], self.ws[r]
-        for lay in self.layers:
+        for li, lay in enumerate(self.layers):
+            if only is not None and li != only:
+                continue
             if lay["mode"] == "F":
                 # the token's global-KV row (position L-1) is appended inside the index call
                 k.csa2_index_full_append(c, self.tok_lat, self.tok_key, lay["qc"], lay["qs"],
@@ -462,6 +465,15 @@ def main():
     n_layers = len(wl.layers)
     value = n_layers / (ms / 1e3)
     log(f"group {ms * 1e3:.1f} us -> {value:.0f} layer-steps/s")
+    # per-mode times: each layer of the group replayed alone (its inputs -- the pool and
+    # top-k of the earlier layers -- are those the group left in place)
+    modes = {}
+    if not a.eager:
+        for li, mode in enumerate(wl.layers):
+            lg = [capture(lambda r=r: bench.step(r, only=li)) for r in range(R)]
+            timed(lambda i: lg[i % R].replay(), max(1, a.warmup // 2))
+            modes.setdefault(mode, round(timed(lambda i: lg[i % R].replay(), max(1, a.steps // 2)) * 1e3, 2))
+        log(f"per-mode us: {modes}")
 
     # scan kernel alone: a graph of back-to-back scans over rotating replicas
     reps = a.scan_reps
@@ -487,7 +499,9 @@ def main():
                      "traffic": traffic, "kernel": SCAN_KERNEL,
                      "kernel_us": round(scan_ms * 1e3, 3), "algorithmic_bytes": ab["scan"]},
         "group": {"algorithmic_bytes": ab["total"],
-                  "hbm_frac": round(ab["total"] / (ms / 1e3) / 1e9 / HBM_PEAK_GBS, 4)},
+                  "hbm_frac": round(ab["total"] / (ms / 1e3) / 1e9 / HBM_PEAK_GBS, 4),
+                  "us_per_mode": modes,
+                  "sequence_layer_steps_per_s": round(value * wl.B, 1)},
         "cpu_baseline": None,
     }
     if not a.no_cpu_baseline:
