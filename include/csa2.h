@@ -186,7 +186,8 @@ int csa2_index_full_finish(const csa2_config *cfg, const uint8_t *q_codes,
  * batch, 1, kv_cache, idx_cache) followed by csa2_index_full(cfg, q_codes, ...), bit for bit
  * (cache bytes, pool and top-k), in one scan launch and one selection launch: the wave that
  * scores the block of position ctx_len[b] - 1 quantises that token's key and writes it (and
- * the latent row) before it reads the block.  latent [batch][512] fp32 (may be NULL: no
+ * the latent row) before it reads the block.  With d_I = 128 and H_I >= 2 the append runs as
+ * a launch of its own before the scan (same results).  latent [batch][512] fp32 (may be NULL: no
  * main-KV append; kv_cache may then be NULL), idx_k [batch][H_I*d_I] fp32, on the device.
  * A sequence with ctx_len <= 0 or ctx_len > 8*maxb appends nothing (as the two calls).
  * Workspace: CSA2_OP_INDEX_FULL bytes.  UNSUPPORTED if latent is given and kv_dim != 512. */

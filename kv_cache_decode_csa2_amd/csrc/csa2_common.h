@@ -60,6 +60,13 @@ __device__ __forceinline__ int32_t load_coherent(const int32_t *p) {
 
 namespace csa2 {
 
+// Global append (MXFP4 latent row and indexer key) of n_new tokens per sequence at positions
+// pos0[b] + pos_off + t; arguments as csa2_append_global, already validated.
+int launch_append_global(const csa2_config *cfg, const float *latent, const float *idx_k,
+                         const int32_t *block_table, int32_t maxb, int64_t n_blocks,
+                         const int32_t *pos0, int32_t pos_off, int32_t batch, int32_t n_new,
+                         uint8_t *kv_cache, uint8_t *idx_cache, hipStream_t stream);
+
 constexpr int kMaxBatch = 4096;  // sequences per index call (the scan keeps a prefix in LDS)
 
 __host__ __device__ inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }

@@ -400,7 +400,7 @@ __global__ __launch_bounds__(kScanThreads, 2) void k_scan(ScanArgs a) {
     };
     Query<H, G> Q;
     QueryRaw<H, G> QR;
-    int pre[DM - 1];
+    int pre[DM - 1] = {};
     if (inter) {
 #pragma unroll
         for (int i = 0; i < (RESCORE ? DM - 1 : DPH); i++) {
@@ -475,14 +475,14 @@ __global__ __launch_bounds__(kScanThreads, 2) void k_scan(ScanArgs a) {
         const int n_ent = RESCORE ? max(0, min(sload(a.pool_len, b), a.K_blk)) : 0;
 
         // entries of step k2 of this segment (-1 past its end); rescoring loads the lane's pool
-        // entry (read clamped into the row, checked by meta_phys a step later) unless `have`
-        // holds it already
-        auto meta_entries = [&](int k2, StepMeta &m, const int *have = nullptr) {
+        // entry (read clamped into the row, checked by meta_phys a step later) unless it was
+        // requested already (`have`: its value is hv)
+        auto meta_entries = [&](int k2, StepMeta &m, bool have = false, int hv = 0) {
             m.e0 = inter ? entry0(k2) : e_start + (k2 - kseg) * BPW;
             const int e = m.e0 + bw;
             const bool live = k2 < kend && e < (RESCORE ? n_ent : nb);
             if (RESCORE) {
-                m.jraw = have ? *have : pool_row[live ? e : 0];
+                m.jraw = have ? hv : pool_row[live ? e : 0];
                 m.j = live ? 0 : -1;
             } else {
                 m.j = live ? e : -1;
@@ -580,7 +580,7 @@ __global__ __launch_bounds__(kScanThreads, 2) void k_scan(ScanArgs a) {
         // k = 0 here, and the early requests above stand in for the first loads)
         StepMeta mt[DM];
 #pragma unroll
-        for (int i = 0; i < DM - 1; i++) meta_entries(k + i, mt[i], RESCORE && inter ? &pre[i] : nullptr);
+        for (int i = 0; i < DM - 1; i++) meta_entries(k + i, mt[i], RESCORE && inter, pre[i]);
 #pragma unroll
         for (int i = 0; i < DPH; i++) {
             if (!RESCORE && inter) mt[i].ph = pre[i];
@@ -666,16 +666,23 @@ bool off32(const ScanArgs &a) {
     constexpr int64_t BYTES = kBlk * H * 17 * G;
     return a.n_blocks * BYTES <= ((int64_t)1 << 32);
 }
+// Layouts whose scan takes the global append without spilling registers (with four groups
+// per head and two or more heads the append's key and latent registers do not fit beside the
+// pipeline's; those layouts append in a launch of their own before the scan).
+constexpr bool fuse_append(int H, int G) { return G <= 2 || H == 1; }
+
 template <int H, int G>
 void launch_scan(dim3 g, size_t sh, hipStream_t s, const ScanArgs &a) {
     const bool o32 = off32<H, G>(a);
-    if (a.new_key) {  // the fused append keeps its own registers out of the plain scan
-        if (o32) k_scan<H, G, false, true, true><<<g, kScanThreads, sh, s>>>(a);
-        else k_scan<H, G, false, false, true><<<g, kScanThreads, sh, s>>>(a);
-    } else {
-        if (o32) k_scan<H, G, false, true, false><<<g, kScanThreads, sh, s>>>(a);
-        else k_scan<H, G, false, false, false><<<g, kScanThreads, sh, s>>>(a);
+    if constexpr (fuse_append(H, G)) {
+        if (a.new_key) {  // the fused append keeps its own registers out of the plain scan
+            if (o32) k_scan<H, G, false, true, true><<<g, kScanThreads, sh, s>>>(a);
+            else k_scan<H, G, false, false, true><<<g, kScanThreads, sh, s>>>(a);
+            return;
+        }
     }
+    if (o32) k_scan<H, G, false, true, false><<<g, kScanThreads, sh, s>>>(a);
+    else k_scan<H, G, false, false, false><<<g, kScanThreads, sh, s>>>(a);
 }
 template <int H, int G>
 void launch_rescore(dim3 g, size_t sh, hipStream_t s, const ScanArgs &a) {
@@ -944,6 +951,14 @@ extern "C" int csa2_index_full_append(const csa2_config *c, const float *latent,
     const WsIdx L = ws_idx(batch, maxb, c->pool_blocks);
     if (ws_bytes < L.total) return CSA2_ERR_WORKSPACE;
     if (batch == 0) return CSA2_OK;
+    if (!fuse_append(c->n_idx_heads, c->idx_dim / 32)) {
+        const int st = launch_append_global(c, latent, idx_k, block_table, maxb, n_blocks,
+                                            ctx_len, -1, batch, 1, kv_cache, idx_cache, stream);
+        if (st) return st;
+        return csa2_index_full(c, q_codes, q_scales, w, idx_cache, n_blocks, block_table, maxb,
+                               ctx_len, batch, pool_blocks, pool_len, topk, topk_len, ws,
+                               ws_bytes, stream);
+    }
     KernSet ks;
     pick(c->n_idx_heads, c->idx_dim, &ks);
     ScanArgs a = scan_args(c, q_codes, q_scales, w, idx_cache, n_blocks, block_table, maxb,

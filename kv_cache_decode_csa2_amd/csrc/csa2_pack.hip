@@ -63,9 +63,9 @@ __global__ void k_dequant_fp8(const uint8_t *codes, const uint8_t *scales, int64
 // latent, the rest the indexer key (head-major).
 __global__ void k_append_global(const float *latent, const float *idx_k,
                                 const int32_t *block_table, int32_t maxb, int64_t n_blocks,
-                                const int32_t *pos0, int32_t n_new, uint8_t *kv_cache,
-                                uint8_t *idx_cache, int32_t D, int32_t H, int32_t dI,
-                                int64_t n_rows) {
+                                const int32_t *pos0, int32_t pos_off, int32_t n_new,
+                                uint8_t *kv_cache, uint8_t *idx_cache, int32_t D, int32_t H,
+                                int32_t dI, int64_t n_rows) {
     const int gl = D / 32, gi = H * (dI / 32), gpr = gl + gi;
     const int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
     if (t >= n_rows * gpr) return;
@@ -78,7 +78,7 @@ __global__ void k_append_global(const float *latent, const float *idx_k,
     float v[32];
     load_group(is_main ? latent + row * D + grp * 32 : idx_k + row * (H * dI) + hg * 32, v);
     const int b = (int)(row / n_new);
-    const int64_t p = (int64_t)pos0[b] + (row % n_new);
+    const int64_t p = (int64_t)pos0[b] + pos_off + (row % n_new);
     if (p < 0 || p / kBlk >= maxb) return;
     const int64_t phys = block_table[(int64_t)b * maxb + p / kBlk];
     if (phys < 0 || phys >= n_blocks) return;
@@ -164,6 +164,21 @@ extern "C" int csa2_dequant_mxfp8(const uint8_t *codes, const uint8_t *scales, i
     return launched();
 }
 
+int csa2::launch_append_global(const csa2_config *cfg, const float *latent,
+                               const float *idx_k, const int32_t *block_table, int32_t maxb,
+                               int64_t n_blocks, const int32_t *pos0, int32_t pos_off,
+                               int32_t batch, int32_t n_new, uint8_t *kv_cache,
+                               uint8_t *idx_cache, hipStream_t stream) {
+    const int64_t rows = (int64_t)batch * n_new;
+    if (rows == 0) return CSA2_OK;
+    const int gpr = cfg->kv_dim / 32 + cfg->n_idx_heads * (cfg->idx_dim / 32);
+    const int64_t n = rows * gpr;
+    k_append_global<<<grid_for(n, 256), 256, 0, stream>>>(
+        latent, idx_k, block_table, maxb, n_blocks, pos0, pos_off, n_new, kv_cache, idx_cache,
+        cfg->kv_dim, cfg->n_idx_heads, cfg->idx_dim, rows);
+    return launched();
+}
+
 extern "C" int csa2_append_global(const csa2_config *cfg, const float *latent,
                                   const float *idx_k, const int32_t *block_table, int32_t maxb,
                                   int64_t n_blocks, const int32_t *pos0, int32_t batch,
@@ -174,14 +189,8 @@ extern "C" int csa2_append_global(const csa2_config *cfg, const float *latent,
         return CSA2_ERR_INVALID;
     if ((latent && !kv_cache) || (idx_k && !idx_cache) || (!latent && !idx_k))
         return CSA2_ERR_INVALID;
-    const int64_t rows = (int64_t)batch * n_new;
-    if (rows == 0) return CSA2_OK;
-    const int gpr = cfg->kv_dim / 32 + cfg->n_idx_heads * (cfg->idx_dim / 32);
-    const int64_t n = rows * gpr;
-    k_append_global<<<grid_for(n, 256), 256, 0, stream>>>(
-        latent, idx_k, block_table, maxb, n_blocks, pos0, n_new, kv_cache, idx_cache,
-        cfg->kv_dim, cfg->n_idx_heads, cfg->idx_dim, rows);
-    return launched();
+    return csa2::launch_append_global(cfg, latent, idx_k, block_table, maxb, n_blocks, pos0, 0,
+                                      batch, n_new, kv_cache, idx_cache, stream);
 }
 
 extern "C" int csa2_append_swa(const csa2_config *cfg, const float *rows, const int32_t *pos0,
