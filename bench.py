@@ -54,7 +54,8 @@ def parse():
     ap.add_argument("--counter-summary", metavar="DIR",
                     help="no GPU: write profiles/<kernel counters>.json from the FETCH_SIZE and "
                          "WRITE_SIZE csv files that two rocprofv3 --pmc runs of --counters left in "
-                         "DIR (file prefix dec_ for decode, pf_ for --workload prefill)")
+                         "DIR (file prefix dec_ for decode, pf_ for --workload prefill, sp_ for "
+                         "--workload spec_1m)")
     return ap.parse_args()
 
 
@@ -135,9 +136,11 @@ class Bench:
 class PrefillBench:
     """The prefill-chunk workload: n_q query tokens at the end of one sequence run the
     prefill indexer (matrix-core scoring + per-query selection) and the per-query sparse
-    attention over their top-k and window."""
+    attention over their top-k and window.  Speculative verification (1 + 5 draft tokens)
+    is the same step with n_q = 6.  The indexer cache is replicated (replicas rotate between
+    steps) so that the replicas together exceed the 256 MB Infinity Cache."""
 
-    def __init__(self, wl):
+    def __init__(self, wl, replicas=0):
         import kv_cache_decode_csa2_amd as k
         import synth_inputs as si
         from gpu_harness import GpuState, dev, prefill_q
@@ -149,6 +152,8 @@ class PrefillBench:
         g = GpuState(wl, table, nblk, with_latent=True)
         log(f"caches built in {time.time() - t0:.1f}s")
         self.g, self.cfg = g, g.cfg
+        self.R = replicas or max(1, -(-(1 << 30) // g.idx.numel()))
+        self.idx = [g.idx] + [g.idx.clone() for _ in range(self.R - 1)]
         self.n_q = wl.n_q
         self.q_pos0 = wl.ctx[0] - wl.n_q
         self.row = g.table[0].contiguous()
@@ -177,14 +182,14 @@ class PrefillBench:
 
     def step(self, r=0):
         k, g, c = self.k, self.g, self.cfg
-        k.csa2_index_prefill(c, self.qc, self.qs, self.w, self.q_pos0, g.idx, g.n_blocks, self.row,
+        k.csa2_index_prefill(c, self.qc, self.qs, self.w, self.q_pos0, self.idx[r], g.n_blocks, self.row,
                              self.pool, self.pool_len, self.topk, self.topk_len, self.ws)
         k.csa2_sparse_attn_prefill(c, self.qa, g.kv, g.n_blocks, self.row, self.ring, self.C,
                                    self.q_pos0, self.topk, self.topk_len, self.out, self.lse,
                                    self.ws_attn)
 
     def scan(self, r=0):
-        self.k.csa2_index_prefill_scan(self.cfg, self.qc, self.qs, self.w, self.q_pos0, self.g.idx,
+        self.k.csa2_index_prefill_scan(self.cfg, self.qc, self.qs, self.w, self.q_pos0, self.idx[r],
                                        self.g.n_blocks, self.row, self.ws)
 
 
@@ -217,27 +222,34 @@ def calibration_copy(mb):
 
 
 def main_prefill(a, wl):
-    bench = PrefillBench(wl)
+    bench = PrefillBench(wl, a.replicas)
+    R = bench.R
     if a.counters:
-        for _ in range(3):
-            bench.scan()
+        for i in range(3):
+            bench.scan(i % R)
         torch.cuda.synchronize()
         calibration_copy(a.calib_mb)
         return
+    spec = wl.name.startswith("spec")
     layout = bench.k.csa2_layout(bench.cfg)
     pw = prefill_work(wl, layout)
-    graph = None if a.eager else capture(lambda: bench.step())
-    step = (lambda i: bench.step()) if graph is None else (lambda i: graph.replay())
-    timed(step, max(1, a.warmup // 4))
-    steps = max(1, a.steps // 20)
+    if a.eager:
+        step = lambda i: bench.step(i % R)  # noqa: E731
+    else:
+        graphs = [capture(lambda r=r: bench.step(r)) for r in range(R)]
+        step = lambda i: graphs[i % R].replay()  # noqa: E731
+    warm = a.warmup if spec else max(1, a.warmup // 4)
+    timed(step, warm)
+    steps = a.steps if spec else max(1, a.steps // 20)
     ms = timed(step, steps)
-    value = bench.n_q / (ms / 1e3)
-    log(f"prefill step {ms:.3f} ms -> {value:.0f} query-tokens/s")
+    value = (1.0 if spec else bench.n_q) / (ms / 1e3)
+    log(f"{wl.name} step {ms:.4f} ms -> {value:.0f} {'verify-steps' if spec else 'query-tokens'}/s"
+        f" ({R} replicas)")
     import hashlib
     src = open(os.path.join(ROOT, "kv_cache_decode_csa2_amd", "csrc", "csa2_prefill.hip"), "rb").read()
-    traffic = traffic_for(hashlib.sha256(src).hexdigest(), "prefill_counters.json")
-    reps = 5
-    sg = capture(lambda: [bench.scan() for _ in range(reps)])
+    traffic = traffic_for(hashlib.sha256(src).hexdigest(), COUNTER_RUNS[counter_kind(wl)][3])
+    reps = 40 if spec else 5
+    sg = capture(lambda: [bench.scan(i % R) for i in range(reps)])
     timed(lambda i: sg.replay(), 1)
     scan_ms = timed(lambda i: sg.replay(), 3) / reps
     sec = scan_ms / 1e3
@@ -251,20 +263,26 @@ def main_prefill(a, wl):
            "alu": pw["alu"] / sec / 1e12}[bound]
     peak = {"hbm": HBM_PEAK_GBS, "mfma": MFMA_FP4_PEAK_TFLOPS, "alu": ALU_PEAK_TOPS}[bound]
     unit = {"hbm": "GB/s", "mfma": "TFLOP/s", "alu": "Tops/s"}[bound]
+    metric = ("CSA2 speculative-verification steps/s at 1M ctx (1 + 5 draft queries: prefill "
+              "indexer + sparse attention)" if spec else
+              "CSA2 prefill-chunk query-tokens/s (prefill indexer + sparse attention)")
     result = {
-        "metric": "CSA2 prefill-chunk query-tokens/s (prefill indexer + sparse attention)",
-        "value": round(value, 1), "unit": "query-tokens/s", "n_gpus": 1, "steps": steps,
-        "warmup": max(1, a.warmup // 4), "ms_per_step": round(ms, 4), "higher_is_better": True,
+        "metric": metric,
+        "value": round(value, 1), "unit": "verify-steps/s" if spec else "query-tokens/s",
+        "n_gpus": 1, "steps": steps,
+        "warmup": warm, "ms_per_step": round(ms, 4), "higher_is_better": True,
         "scaling": "weak", "vs_baseline": None, "dtype": "mxfp4", "data": "synthetic",
         "config": {"workload": wl.name, "queries": wl.n_q, "context": wl.ctx[0],
                    "indexer": f"{wl.H_I}x{wl.d_I} fp4", "pool_blocks": wl.K_blk, "topk": wl.k,
-                   "q_heads": wl.H_q, "window": wl.W, "graph": graph is not None},
+                   "q_heads": wl.H_q, "window": wl.W, "replicas": R, "graph": not a.eager},
         "roofline": {"bound": bound, "achieved": round(ach, 2), "peak": peak, "unit": unit,
                      "frac": round(fr[bound], 4), "traffic": traffic, "kernel": "k_prefill",
                      "kernel_us": round(scan_ms * 1e3, 2),
                      "fractions": {k_: round(v, 4) for k_, v in fr.items()}, "work": pw},
         "cpu_baseline": None,
     }
+    if spec and not a.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline_spec(wl, a.cpu_seconds)
     print(json.dumps(result), flush=True)
 
 
@@ -346,6 +364,46 @@ def cpu_baseline(wl, seconds):
                        f"(all {sum(wl.ctx)} positions scanned per Full layer), {el:.1f} s wall")
 
 
+def cpu_baseline_spec(wl, seconds):
+    """The oracle on the verification step: the prefill indexer over the n_q queries (each
+    the Full steps on its causal prefix) and their sparse attention, repeated for about
+    `seconds`."""
+    import oracle
+    import synth_inputs as si
+    from harness import OracleState, make_table
+    table, nblk = make_table(wl.ctx, seed=wl.seed, permute=False)
+    t0 = time.time()
+    o = OracleState(wl, table, nblk, with_latent=True)
+    log(f"oracle caches built in {time.time() - t0:.1f}s")
+    n_q = wl.n_q
+    q_pos0 = wl.ctx[0] - n_q
+    qc, qs = oracle.quantize_mxfp4(si.prefill_idx_q(wl, 0, n_q).reshape(n_q, -1))
+    w = si.prefill_idx_w(wl, 0, n_q)
+    C = n_q + wl.W
+    first = max(0, q_pos0 - wl.W + 1)
+    rows = si.layer_swa_rows(wl, 0, 0, q_pos0 + n_q - first)
+    ring = oracle.alloc_swa(o.cfg, 1, C)
+    oracle.append_swa(o.cfg, rows[None], np.array([first], np.int32), ring, C)
+    qa = si.prefill_attn_q(wl, 0, n_q)
+    n = 0
+    t0 = time.time()
+    while True:
+        _, _, t, tl = oracle.index_prefill(o.cfg, qc, qs, w, q_pos0, o.idx, o.table[0])
+        oracle.sparse_attn_prefill(o.cfg, qa, o.kv, o.table[0], ring[0], C, q_pos0, t, tl)
+        n += 1
+        el = time.time() - t0
+        if el >= seconds:
+            break
+    try:
+        cores = len(os.sched_getaffinity(0))
+    except AttributeError:
+        cores = os.cpu_count()
+    cores = int(os.environ.get("OMP_NUM_THREADS", cores))
+    return dict(value=n / el, unit="verify-steps/s", cores=cores, kind="oracle",
+                sample=f"{n} whole verification steps of the {wl.name} workload ({n_q} queries, "
+                       f"all {wl.ctx[0]} positions scored per query), {el:.1f} s wall")
+
+
 def traffic_for(kernel_src_hash, name="scan_long_1m_counters.json"):
     """HBM bytes per launch measured by the counter runs recorded in profiles/<name>, if they
     were taken on the current kernel source (else None)."""
@@ -365,7 +423,13 @@ COUNTER_RUNS = {  # workload kind -> (file prefix, kernel, kernel source, profil
                "long_1m: B=1, L=1,048,576, indexer 4x64 FP4"),
     "prefill": ("pf", "k_prefill<", "csa2_prefill.hip", "prefill_counters.json",
                 "prefill: 4096 queries at 258048..262143, L=262,144, indexer 8x128 FP4"),
+    "spec": ("sp", "k_prefill<", "csa2_prefill.hip", "spec_1m_counters.json",
+             "spec_1m: 6 queries at 1048570..1048575, L=1,048,576, indexer 4x64 FP4"),
 }
+
+
+def counter_kind(wl):
+    return "spec" if wl.name.startswith("spec") else ("prefill" if wl.n_q else "decode")
 
 
 def counter_summary(a, wl):
@@ -374,7 +438,7 @@ def counter_summary(a, wl):
     calibration copy of a.calib_mb MiB that --counters runs after the kernel."""
     import csv
     import hashlib
-    kind = "prefill" if wl.n_q else "decode"
+    kind = counter_kind(wl)
     prefix, kname, src_name, out_name, wl_text = COUNTER_RUNS[kind]
     raw = {}
     for ctr in ("FETCH_SIZE", "WRITE_SIZE"):
@@ -393,11 +457,11 @@ def counter_summary(a, wl):
     fetch = raw["FETCH_SIZE"][0] * 1024.0 * ff
     write = raw["WRITE_SIZE"][0] * 1024.0 * wf
     src_path = os.path.join(ROOT, "kv_cache_decode_csa2_amd", "csrc", src_name)
-    if kind == "prefill":
+    if kind != "decode":
         alg = prefill_work(wl, _layout_of(wl))["bytes"]
     else:
         alg = wl.max_ctx * (wl.H_I * (wl.d_I // 2 + wl.d_I // 32))
-    wl_flag = " --workload prefill" if kind == "prefill" else ""
+    wl_flag = f" --workload {wl.name}" if kind != "decode" else ""
     d = {
         "kernel": kname, "dispatches": raw["FETCH_SIZE"][1],
         "fetch_kib_raw": round(raw["FETCH_SIZE"][0], 1), "write_kib_raw": round(raw["WRITE_SIZE"][0], 1),

@@ -20,6 +20,8 @@ model tensors, so every tensor is synthetic):
 * ragged64  : batch 64, context lengths uniform on [4096, 131072]; dims as long_1m.
 * prefill   : 4096 queries at the end of a 262,144-token causal context,
               indexer 8 x 128, pool 2048, top-512, 64 query heads.
+* spec_1m   : speculative verification, 1 + 5 draft tokens at the end of a
+              1,048,576-token context (6 causal queries); dims as long_1m.
 """
 from __future__ import annotations
 
@@ -138,6 +140,8 @@ def workload(name: str) -> Workload:
         return Workload("ragged64", 4, 64, [int(v) for v in lens], 4, 64, 2048, 512, H_q=16)
     if name == "prefill":
         return Workload("prefill", 5, 1, [262144], 8, 128, 2048, 512, H_q=64, n_q=4096)
+    if name == "spec_1m":
+        return Workload("spec_1m", 6, 1, [1 << 20], 4, 64, 2048, 512, H_q=16, n_q=6)
     raise KeyError(name)
 
 

@@ -184,3 +184,36 @@ def test_prefill_workload_sampled():
         ro, rl = oracle.sparse_attn(o.cfg, qa[i:i + 1], o.kv, o.table, ring_o, C, ctx, to, tlo)
         ok, rel, lerr = attn_close(go[i:i + 1], gl[i:i + 1], ro, rl)
         assert ok, (i, rel, lerr)
+
+
+@pytest.mark.slow
+def test_spec_verify_1m():
+    """Speculative verification at 1M context: the token and 5 draft tokens at positions
+    1048570..1048575 of a 1,048,576-token context (indexer 4 x 64, pool 2048 blocks,
+    top-512, 16 heads, window 128) run as one 6-query prefill chunk.  Every query's pool and
+    top-k equal the oracle's (each query the Full steps at its own causal length), and its
+    attention is within 2e-3 of the fp64 oracle."""
+    wl = si.workload("spec_1m")
+    n_q, L = wl.n_q, wl.ctx[0]
+    q_pos0 = L - n_q
+    table, nblk = make_table(wl.ctx, seed=wl.seed, permute=False)
+    g = GpuState(wl, table, nblk)
+    o = OracleState(wl, table, nblk)
+    qc, qs, wg = prefill_q(wl, 0, n_q)
+    pgd, plgd, tgd, tlgd = index_prefill(g, qc, qs, wg, q_pos0)
+    C, ring_o, ring_g = _rings(wl, o, g, q_pos0, n_q)
+    qa = si.prefill_attn_q(wl, 0, n_q)
+    go, gl = _attn_prefill(g, dev(qa.view(np.int16)), ring_g, C, q_pos0, tgd, tlgd)
+    pg, plg, tg, tlg, go, gl = [_np(x) for x in (pgd, plgd, tgd, tlgd, go, gl)]
+    del g
+    torch.cuda.empty_cache()
+    qo = _oracle_q(wl, n_q)
+    po, plo, to, tlo = oracle.index_prefill(o.cfg, *qo, q_pos0, o.idx, o.table[0])
+    assert np.all(plo == wl.K_blk) and np.all(tlo == wl.k)
+    assert np.array_equal(plg, plo) and np.array_equal(tlg, tlo)
+    assert np.array_equal(pg, po), _first_diff(pg, po)
+    assert np.array_equal(tg, to), _first_diff(tg, to)
+    ro, rl = oracle.sparse_attn_prefill(o.cfg, qa, o.kv, o.table[0], ring_o[0], C, q_pos0, to, tlo)
+    ok, rel, lerr = attn_close(go, gl, ro, rl)
+    print("spec verification attention rel", rel, "lse", lerr)
+    assert ok, (rel, lerr)
