@@ -473,9 +473,9 @@ def counter_summary(a, wl):
         "source_sha256": hashlib.sha256(open(src_path, "rb").read()).hexdigest(),
         "source": f"kv_cache_decode_csa2_amd/csrc/{src_name}",
         "command": [f"rocprofv3 --pmc {c} --kernel-include-regex '{kname.rstrip('<')}|copyBuffer|copy' "
-                    f"--output-format csv -d gpurun_out/pmc -o {prefix}_{c} -- python3 bench.py"
+                    f"--output-format csv -d {a.counter_summary} -o {prefix}_{c} -- python3 bench.py"
                     f"{wl_flag} --counters" for c in ("FETCH_SIZE", "WRITE_SIZE")]
-                   + [f"python3 bench.py{wl_flag} --counter-summary gpurun_out/pmc"],
+                   + [f"python3 bench.py{wl_flag} --counter-summary {a.counter_summary}"],
         "workload": wl_text,
     }
     with open(os.path.join(ROOT, "profiles", out_name), "w") as f:
