@@ -195,7 +195,7 @@ struct PfQuery {
     float w[H];
 };
 
-template <int H, int G>
+template <int H, int G, bool SMALL>
 __global__ __launch_bounds__(kPfThreads, 2) void k_prefill(PrefillArgs a) {
     using S = PfStage<H, G>;
     // two stage buffers as distinct objects, so that the reads of one are known not to
@@ -230,12 +230,19 @@ __global__ __launch_bounds__(kPfThreads, 2) void k_prefill(PrefillArgs a) {
     __syncthreads();
     pf_dma<H, G>(a, meta, 0, stA);
 
+    // At most 16 queries (a verification step): every wave takes the one query tile and a
+    // quarter of each stage's positions (16-position tile u = wave) instead of a query tile
+    // pair of its own, which would leave three of the four waves idle.  The stage's group
+    // maxima are then combined across the waves through LDS.
+    constexpr bool small = SMALL;  // the host sets it when n_q <= 16
+    const int u_beg = small ? wave : 0, u_end = small ? wave + 1 : kPfStageBlocks / 2;
+    __shared__ float sm_gm[2][kPfWaves][16];
     // queries of this wave's tiles, their scale spans and causal limits
     PfQuery<H> Q[kPfNQ];
     int qspan[kPfNQ], qb[kPfNQ];
 #pragma unroll
     for (int jq = 0; jq < kPfNQ; jq++) {
-        qb[jq] = Q0 + (wave * kPfNQ + jq) * 16;
+        qb[jq] = small ? (jq == 0 ? Q0 : a.n_q) : Q0 + (wave * kPfNQ + jq) * 16;
         const int q = min(qb[jq] + col, a.n_q - 1);
         const uint8_t *qc = a.q_codes + (int64_t)q * H * G * 16;
         const uint8_t *qs = a.q_scales + (int64_t)q * H * G;
@@ -277,7 +284,7 @@ __global__ __launch_bounds__(kPfThreads, 2) void k_prefill(PrefillArgs a) {
 #pragma unroll
         for (int jq = 0; jq < kPfNQ; jq++) gm[jq] = -INFINITY;
 #pragma unroll 1
-        for (int u = 0; u < kPfStageBlocks / 2; u++) {  // 16-position tiles
+        for (int u = u_beg; u < u_end; u++) {  // 16-position tiles
             const int p0 = (J0 + 2 * u) * kBlk;
             // this lane's key row: position p0 + col, group g
             const int bi = 2 * u + (col >> 3), s = col & 7;
@@ -379,9 +386,24 @@ __global__ __launch_bounds__(kPfThreads, 2) void k_prefill(PrefillArgs a) {
         for (int jq = 0; jq < kPfNQ; jq++) {
             const float v = smax(gm[jq], __shfl_xor(gm[jq], 32, kWave));
             const int q = qb[jq] + col;
-            if (g == 0 && q < a.n_q && J0 * kBlk <= a.q_pos0 + q)
+            if (small) {
+                if (jq == 0 && g == 0) sm_gm[sidx & 1][wave][col] = v;
+            } else if (g == 0 && q < a.n_q && J0 * kBlk <= a.q_pos0 + q) {
                 a.gmax[(int64_t)q * a.ngmax + J0 / kPfStageBlocks] = v;
+            }
         }
+    };
+    // small: group maxima of stage sidx from the four waves' parts (after the barrier that
+    // ends the stage; the buffer of stage sidx is next written two stages later)
+    auto combine_gm = [&](int sidx) {
+        if (!small || sidx < 0 || wave != 0 || g != 0) return;
+        const int J0 = Jbeg + sidx * kPfStageBlocks;
+        const int q = Q0 + col;
+        float v = sm_gm[sidx & 1][0][col];
+#pragma unroll
+        for (int w = 1; w < kPfWaves; w++) v = smax(v, sm_gm[sidx & 1][w][col]);
+        if (q < a.n_q && J0 * kBlk <= a.q_pos0 + q)
+            a.gmax[(int64_t)q * a.ngmax + J0 / kPfStageBlocks] = v;
     };
 
     // pipeline: the DMA of stage s+1 runs while stage s is computed; a stage ends with every
@@ -390,15 +412,18 @@ __global__ __launch_bounds__(kPfThreads, 2) void k_prefill(PrefillArgs a) {
     __syncthreads();
     for (int sidx = 0; sidx < nstage; sidx += 2) {
         if (sidx + 1 < nstage) pf_dma<H, G>(a, meta, (sidx + 1) * kPfStageBlocks, stB);
+        combine_gm(sidx - 1);
         compute(stA, sidx);
         __builtin_amdgcn_s_waitcnt(0);
         __syncthreads();
         if (sidx + 1 >= nstage) break;
         if (sidx + 2 < nstage) pf_dma<H, G>(a, meta, (sidx + 2) * kPfStageBlocks, stA);
+        combine_gm(sidx);
         compute(stB, sidx + 1);
         __builtin_amdgcn_s_waitcnt(0);
         __syncthreads();
     }
+    combine_gm(nstage - 1);
 }
 
 typedef void (*PfFn)(const PrefillArgs &, hipStream_t);
@@ -407,7 +432,8 @@ template <int H, int G>
 void launch_prefill(const PrefillArgs &a, hipStream_t s) {
     const int spans = (a.nb * kBlk + 255) / 256;
     k_prefill_span<H, G><<<spans, 256, 0, s>>>(a);
-    k_prefill<H, G><<<a.n_qt * a.n_pc, kPfThreads, 0, s>>>(a);
+    if (a.n_q <= 16) k_prefill<H, G, true><<<a.n_qt * a.n_pc, kPfThreads, 0, s>>>(a);
+    else k_prefill<H, G, false><<<a.n_qt * a.n_pc, kPfThreads, 0, s>>>(a);
 }
 
 bool pick_prefill(int H, int dI, PfFn *fn) {

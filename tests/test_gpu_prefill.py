@@ -62,6 +62,11 @@ def _check(wl, n_q, permute=True, scale_fn=None, w=None):
     (4, 64, 700, 200),     # two groups per head
     (2, 32, 130, 130),     # one group per head; queries from position 0 (prefix of 1)
     (1, 128, 2100, 70),
+    # at most 16 queries: the waves split each stage's positions
+    (4, 64, 5000, 6),      # verification step: 6 queries, 3 position chunks (ragged)
+    (8, 128, 2800, 16),
+    (2, 32, 130, 1),       # one query, two stages
+    (1, 128, 2100, 9),
 ])
 def test_prefill_index_bit_exact(H, d, L, n_q):
     wl = si.small("pf", 100 + H + d + L, [L], H_I=H, d_I=d, K_blk=64, k=128, W=16)
