@@ -491,6 +491,74 @@ def _layout_of(wl):
     return L
 
 
+PCIE_PEAK_GBS = 63.0  # PCIe 5.0 x16, one direction (32 GT/s x 16 lanes, 128b/130b)
+
+
+def main_tier(a):
+    """The persistent global-KV tier at 1M context: both FP4 block caches of the long_1m
+    sequence (indexer keys and main latent rows of 1,048,576 positions) leave through
+    csa2_blocks_gather into pinned host memory and come back through csa2_blocks_scatter into
+    another physical placement.  One step = save (gather + device-to-host) and restore
+    (host-to-device + scatter) of both caches."""
+    import kv_cache_decode_csa2_amd as k
+    import synth_inputs as si
+    from gpu_harness import GpuState, dev
+    from harness import make_table
+    wl = si.workload("long_1m")
+    table, nblk = make_table(wl.ctx, seed=wl.seed, permute=False)
+    t0 = time.time()
+    g = GpuState(wl, table, nblk, with_latent=True)
+    log(f"caches built in {time.time() - t0:.1f}s")
+    valid = table >= 0
+    new_table, _ = make_table(wl.ctx, seed=wl.seed + 1, permute=True)
+    src = dev(table[valid].astype(np.int32))
+    dst = dev(new_table[valid].astype(np.int32))
+    caches = [g.idx, g.kv]
+    rows = [torch.empty((src.numel(), c.shape[1]), dtype=torch.uint8, device="cuda") for c in caches]
+    host = [torch.empty(r.shape, dtype=torch.uint8, pin_memory=True) for r in rows]
+    total = sum(r.numel() for r in rows)
+
+    def save():
+        for c, r, h in zip(caches, rows, host):
+            k.csa2_blocks_gather(c, src, r)
+            h.copy_(r, non_blocking=True)
+
+    def restore():
+        for c, r, h in zip(caches, rows, host):
+            r.copy_(h, non_blocking=True)
+            k.csa2_blocks_scatter(r, dst, c)
+
+    steps = max(1, a.steps // 20)
+    save(), restore()
+    t_save = timed(lambda i: save(), steps)
+    t_restore = timed(lambda i: restore(), steps)
+    t_gather = timed(lambda i: [k.csa2_blocks_gather(c, src, r) for c, r in zip(caches, rows)], steps)
+    t_scatter = timed(lambda i: [k.csa2_blocks_scatter(r, dst, c) for c, r in zip(caches, rows)], steps)
+    ms = t_save + t_restore
+    value = 2 * total / (ms / 1e3) / 1e9
+    log(f"tier: {total / 1e6:.1f} MB each way, save {t_save:.2f} ms, restore {t_restore:.2f} ms, "
+        f"device gather {t_gather:.3f} ms, scatter {t_scatter:.3f} ms")
+    kern_ms = (t_gather + t_scatter) / 2
+    ach = 2 * total / (kern_ms / 1e3) / 1e9  # each copy kernel reads and writes the bytes
+    result = {
+        "metric": "CSA2 global-KV tier round trip GB/s at 1M ctx (save + restore of both FP4 "
+                  "block caches through pinned host memory)",
+        "value": round(value, 2), "unit": "GB/s", "n_gpus": 1, "steps": steps, "warmup": 1,
+        "ms_per_step": round(ms, 4), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "u8", "data": "synthetic",
+        "config": {"workload": "tier_1m", "context": wl.ctx[0], "indexer": f"{wl.H_I}x{wl.d_I} fp4",
+                   "bytes_each_way": total, "pinned_host": True},
+        "roofline": {"bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(ach / HBM_PEAK_GBS, 4), "traffic": None,
+                     "kernel": "k_blocks_copy", "kernel_us": round(kern_ms * 1e3, 2)},
+        "pcie": {"save_ms": round(t_save, 3), "restore_ms": round(t_restore, 3),
+                 "save_gbs": round(total / t_save / 1e6, 2),
+                 "restore_gbs": round(total / t_restore / 1e6, 2), "peak_per_direction": PCIE_PEAK_GBS},
+        "cpu_baseline": None,
+    }
+    print(json.dumps(result), flush=True)
+
+
 def main():
     a = parse()
     if a.counter_summary:
@@ -503,8 +571,10 @@ def main():
     import hashlib
 
     import synth_inputs as si
-    wl = si.workload(a.workload)
     torch.cuda.set_device(0)
+    if a.workload == "tier_1m":
+        return main_tier(a)
+    wl = si.workload(a.workload)
     if wl.n_q:
         return main_prefill(a, wl)
     bench = Bench(wl, a.replicas)

@@ -130,6 +130,23 @@ int csa2_append_global(const csa2_config *cfg, const float *latent, const float 
                        const int32_t *pos0, int32_t batch, int32_t n_new, uint8_t *kv_cache,
                        uint8_t *idx_cache, hipStream_t stream);
 
+/* Block transfer for the persistent global-KV tier [KV] (the global caches are kept in host
+ * memory or on SSD for later prefix hits; the window cache is not): csa2_blocks_gather
+ * copies the n physical blocks blocks[0..n) (device int32) of a block cache (n_blocks blocks
+ * of block_bytes each -- csa2_layout's kv_block_bytes or idx_block_bytes) into n
+ * consecutive rows of `rows` (device, n * block_bytes bytes); csa2_blocks_scatter copies the
+ * rows back into the listed blocks, which may differ from the ones they came from (a
+ * restored sequence gets a new block table).  The caller moves `rows` between device and
+ * host memory (hipMemcpyAsync with pinned host memory).  The bytes are copied unchanged, so
+ * a restored cache indexes and attends exactly as the saved one.  Entries outside
+ * [0, n_blocks): gather writes a zero row, scatter skips the row.  INVALID if block_bytes
+ * is not a positive multiple of 16, n < 0, n_blocks <= 0 or a pointer is NULL with n > 0.
+ * Rows and cache must not overlap. */
+int csa2_blocks_gather(const uint8_t *cache, int64_t n_blocks, int64_t block_bytes,
+                       const int32_t *blocks, int32_t n, uint8_t *rows, hipStream_t stream);
+int csa2_blocks_scatter(const uint8_t *rows, const int32_t *blocks, int32_t n, uint8_t *cache,
+                        int64_t n_blocks, int64_t block_bytes, hipStream_t stream);
+
 /* Window append (every layer) [KV][W]: quantise rows[(b*n_new + t)*D ..] to MXFP8 into the
  * ring slot (pos0[b] + t) % C of sequence b.  Negative positions are skipped. */
 int csa2_append_swa(const csa2_config *cfg, const float *rows, const int32_t *pos0,

@@ -24,7 +24,8 @@ EXPORTS = [
     "csa2_index_scores", "csa2_index_full", "csa2_index_full_scan", "csa2_index_full_finish",
     "csa2_index_reindex", "csa2_index_prefill", "csa2_index_prefill_scan",
     "csa2_index_prefill_finish", "csa2_sparse_attn", "csa2_sparse_attn_append",
-    "csa2_sparse_attn_prefill", "csa2_index_full_append", "csa2_status_str",
+    "csa2_sparse_attn_prefill", "csa2_index_full_append", "csa2_blocks_gather",
+    "csa2_blocks_scatter", "csa2_status_str",
 ]
 
 
@@ -67,6 +68,8 @@ def load() -> C.CDLL:
             "csa2_dequant_mxfp8": [vp, vp, i64, i32, vp, vp],
             "csa2_append_global": [cfgp, vp, vp, vp, i32, i64, vp, i32, i32, vp, vp, vp],
             "csa2_append_swa": [cfgp, vp, vp, i32, i32, vp, i32, vp],
+            "csa2_blocks_gather": [vp, i64, i64, vp, i32, vp, vp],
+            "csa2_blocks_scatter": [vp, vp, i32, vp, i64, i64, vp],
             "csa2_index_scores": [cfgp, vp, vp, vp, vp, i64, vp, i32, vp, i32, vp, vp, vp],
             "csa2_index_full": [cfgp, vp, vp, vp, vp, i64, vp, i32, vp, i32, vp, vp, vp, vp, vp,
                                 sz, vp],
@@ -174,6 +177,20 @@ def csa2_append_swa(cfg, rows, pos0, n_new, swa_cache, C_slots, stream=None):
     batch = pos0.shape[0]
     _call("csa2_append_swa", C.byref(cfg), _p(rows), _p(pos0), batch, int(n_new),
           _p(swa_cache), int(C_slots), _stream(stream))
+
+
+def csa2_blocks_gather(cache, blocks, rows, stream=None):
+    """rows[r] = cache[blocks[r]] for the n listed physical blocks (cache [n_blocks, bytes])."""
+    n_blocks, block_bytes = cache.shape
+    _call("csa2_blocks_gather", _p(cache), int(n_blocks), int(block_bytes), _p(blocks),
+          int(blocks.numel()), _p(rows), _stream(stream))
+
+
+def csa2_blocks_scatter(rows, blocks, cache, stream=None):
+    """cache[blocks[r]] = rows[r] for the n listed physical blocks."""
+    n_blocks, block_bytes = cache.shape
+    _call("csa2_blocks_scatter", _p(rows), _p(blocks), int(blocks.numel()), _p(cache),
+          int(n_blocks), int(block_bytes), _stream(stream))
 
 
 def csa2_index_scores(cfg, q_codes, q_scales, w, idx_cache, n_blocks, block_table, ctx_len,

@@ -115,6 +115,28 @@ __global__ void k_append_swa(const float *rows, const int32_t *pos0, int32_t n_n
     quant_fp8(rows + row * D + grp * 32, dst + grp * 32, dst + D + grp);
 }
 
+// Block transfer: row r of `rows` <-> physical block blocks[r] of a block cache, in 16-byte
+// chunks (one per thread, grid-stride).  Gather writes zeros for an entry outside
+// [0, n_blocks); scatter skips it.
+template <bool GATHER>
+__global__ void k_blocks_copy(const uint8_t *src, uint8_t *dst, const int32_t *blocks,
+                              int64_t n_chunks, int32_t cpb, int64_t n_blocks) {
+    const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n_chunks; i += stride) {
+        const int64_t r = i / cpb;
+        const int c = (int)(i - r * cpb);
+        const int64_t blk = blocks[r];
+        const bool ok = blk >= 0 && blk < n_blocks;
+        const int64_t cache_chunk = blk * cpb + c;
+        if (GATHER) {
+            const uint4 v = ok ? reinterpret_cast<const uint4 *>(src)[cache_chunk] : make_uint4(0u, 0u, 0u, 0u);
+            reinterpret_cast<uint4 *>(dst)[i] = v;
+        } else if (ok) {
+            reinterpret_cast<uint4 *>(dst)[cache_chunk] = reinterpret_cast<const uint4 *>(src)[i];
+        }
+    }
+}
+
 }  // namespace csa2
 
 using namespace csa2;
@@ -203,5 +225,39 @@ extern "C" int csa2_append_swa(const csa2_config *cfg, const float *rows, const 
     const int64_t n = nrows * (cfg->kv_dim / 32);
     k_append_swa<<<grid_for(n, 256), 256, 0, stream>>>(rows, pos0, n_new, swa_cache, C,
                                                         cfg->kv_dim, nrows);
+    return launched();
+}
+
+namespace {
+int blocks_copy_args_ok(const void *a, const void *b, const int32_t *blocks, int32_t n,
+                        int64_t n_blocks, int64_t block_bytes) {
+    return n >= 0 && n_blocks > 0 && block_bytes > 0 && block_bytes % 16 == 0 &&
+           (n == 0 || (a && b && blocks));
+}
+int blocks_grid(int64_t n_chunks) {
+    const int64_t g = (n_chunks + 255) / 256;
+    return (int)(g < 8192 ? (g > 0 ? g : 1) : 8192);
+}
+}  // namespace
+
+extern "C" int csa2_blocks_gather(const uint8_t *cache, int64_t n_blocks, int64_t block_bytes,
+                                  const int32_t *blocks, int32_t n, uint8_t *rows,
+                                  hipStream_t stream) {
+    if (!blocks_copy_args_ok(cache, rows, blocks, n, n_blocks, block_bytes)) return CSA2_ERR_INVALID;
+    if (n == 0) return CSA2_OK;
+    const int32_t cpb = (int32_t)(block_bytes / 16);
+    const int64_t chunks = (int64_t)n * cpb;
+    k_blocks_copy<true><<<blocks_grid(chunks), 256, 0, stream>>>(cache, rows, blocks, chunks, cpb, n_blocks);
+    return launched();
+}
+
+extern "C" int csa2_blocks_scatter(const uint8_t *rows, const int32_t *blocks, int32_t n,
+                                   uint8_t *cache, int64_t n_blocks, int64_t block_bytes,
+                                   hipStream_t stream) {
+    if (!blocks_copy_args_ok(rows, cache, blocks, n, n_blocks, block_bytes)) return CSA2_ERR_INVALID;
+    if (n == 0) return CSA2_OK;
+    const int32_t cpb = (int32_t)(block_bytes / 16);
+    const int64_t chunks = (int64_t)n * cpb;
+    k_blocks_copy<false><<<blocks_grid(chunks), 256, 0, stream>>>(rows, cache, blocks, chunks, cpb, n_blocks);
     return launched();
 }

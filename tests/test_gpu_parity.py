@@ -308,3 +308,67 @@ def test_full_append_matches_two_calls(H, d, ctx, with_lat):
     for name, x, y in zip(names, res[0], res[1]):
         assert np.array_equal(x, y), (name, _first_diff(x, y))
     assert not np.array_equal(res[0][1], _np(g.idx)), "the append changed no key byte"
+
+
+def test_global_tier_round_trip():
+    """The persistent global-KV tier: both block caches of every sequence leave through
+    csa2_blocks_gather into pinned host memory, the device caches are cleared, and the rows
+    come back with csa2_blocks_scatter into a different physical placement (a new block
+    table).  Every logical block's bytes are unchanged, and Full, Reindex and attention give
+    bit-identical results to those before the round trip (which equal the oracle's)."""
+    import kv_cache_decode_csa2_amd as k
+    wl = si.small("tier", 41, [3000, 517, 9], H_I=4, d_I=64, K_blk=32, k=64, H_q=16, W=128)
+    table, nblk = make_table(wl.ctx, seed=41)
+    o = OracleState(wl, table, nblk)
+    g = GpuState(wl, table, nblk)
+    qF, qR = g.layer_q(0), g.layer_q(1)
+    swa, qa = g.layer_swa(0), g.attn_q(0)
+
+    def run():
+        pool, pl, tk, tl = g.index_full(*qF)
+        tkR, tlR = g.index_reindex(*qR, pool, pl)
+        out, lse = g.attn(qa, swa, tk, tl)
+        torch.cuda.synchronize()
+        return [_np(x) for x in (pool, pl, tk, tl, tkR, tlR, out, lse)]
+
+    before = run()
+    po, plo, to, tlo = oracle.index_full(o.cfg, *o.layer_q(0), o.idx, o.table, o.ctx)
+    assert np.array_equal(before[0], po) and np.array_equal(before[2], to)
+
+    valid = table >= 0
+    src = dev(table[valid].astype(np.int32))          # (sequence, logical block) order
+    new_table, _ = make_table(wl.ctx, seed=4141)       # another permutation of the blocks
+    assert not np.array_equal(new_table, table)
+    dst = dev(new_table[valid].astype(np.int32))
+    logical_bytes = {}
+    for name in ("idx", "kv"):
+        cache = getattr(g, name)
+        rows = torch.empty((src.numel(), cache.shape[1]), dtype=torch.uint8, device="cuda")
+        k.csa2_blocks_gather(cache, src, rows)
+        host = torch.empty(rows.shape, dtype=torch.uint8, pin_memory=True)
+        host.copy_(rows)
+        torch.cuda.synchronize()
+        logical_bytes[name] = host.numpy().copy()
+        cache.zero_()
+        k.csa2_blocks_scatter(host.to("cuda"), dst, cache)
+    g.table = dev(new_table)
+    torch.cuda.synchronize()
+    for name in ("idx", "kv"):
+        cache = getattr(g, name)
+        back = torch.empty((dst.numel(), cache.shape[1]), dtype=torch.uint8, device="cuda")
+        k.csa2_blocks_gather(cache, dst, back)
+        assert np.array_equal(_np(back), logical_bytes[name]), name
+    after = run()
+    for x, y in zip(before, after):
+        assert np.array_equal(x, y)
+
+    # entries outside the cache: gather writes zero rows, scatter leaves the cache alone
+    bad = dev(np.array([-1, nblk, 0], np.int32))
+    rows = torch.full((3, g.idx.shape[1]), 0xAB, dtype=torch.uint8, device="cuda")
+    k.csa2_blocks_gather(g.idx, bad, rows)
+    r = _np(rows)
+    assert not r[:2].any() and np.array_equal(r[2], _np(g.idx[0]))
+    snapshot = _np(g.idx).copy()
+    k.csa2_blocks_scatter(torch.full_like(rows, 0x5A), dev(np.array([-1, nblk, -5], np.int32)), g.idx)
+    torch.cuda.synchronize()
+    assert np.array_equal(_np(g.idx), snapshot)
