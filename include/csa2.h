@@ -7,7 +7,8 @@
  *         Reindex or Reuse mode; the first Full layer scans the whole visible context and
  *         keeps a candidate pool of at most 2048 blocks of 8 positions; later layers pick
  *         the final top-512 inside the pool; indexer Q/K and main KV are FP4, the
- *         sliding-window KV is FP8.
+ *         sliding-window KV is FP8; the global KV is kept in a persistent cache (host
+ *         memory or SSD) for later prefix hits, the window KV only briefly.
  *   [3]   10100.com/article/150771503, "三招压缩，各有分工": the decoder keeps layer-local
  *         sliding-window attention; later indexers search only the pool.
  *   [HSI] prism.simon-ai.net/article/7901, "层级稀疏索引器：精准筛选关键信息".
