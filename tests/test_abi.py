@@ -113,3 +113,28 @@ def test_attention_shape_limits():
     st = lib.csa2_sparse_attn(C.byref(c), fake, fake, 1, fake, 8, fake, 64, fake, 1, fake, fake,
                               fake, fake, fake, 1 << 30, None)   # ring smaller than window
     assert st == k.CSA2_ERR_INVALID
+
+
+def test_block_transfer_and_fused_append_host_errors():
+    """Argument errors of the block-transfer calls and of the fused Full-layer append are
+    found on the host (nothing is launched); empty calls are no-ops."""
+    lib = k.load()
+    nul, f = None, C.c_void_p(256)
+    INV = k.CSA2_ERR_INVALID
+    assert lib.csa2_blocks_gather(f, 10, 24, f, 3, f, nul) == INV       # not a multiple of 16
+    assert lib.csa2_blocks_gather(f, 10, 32, f, -1, f, nul) == INV      # n < 0
+    assert lib.csa2_blocks_gather(nul, 10, 32, f, 3, f, nul) == INV     # NULL cache
+    assert lib.csa2_blocks_scatter(f, f, 3, f, 0, 32, nul) == INV       # no blocks
+    assert lib.csa2_blocks_gather(nul, 10, 32, nul, 0, nul, nul) == k.CSA2_OK
+    assert lib.csa2_blocks_scatter(nul, nul, 0, nul, 10, 32, nul) == k.CSA2_OK
+    c = k.config(4, 64, 512, 16, 128, 64, 128, 0.044)
+    ws = k.csa2_workspace_bytes(c, k.CSA2_OP_INDEX_FULL, 1, 8)
+
+    def fused(cfg, idx_k, batch, ws_bytes):
+        return lib.csa2_index_full_append(C.byref(cfg), f, idx_k, f, f, f, f, f, 1, f, 8, f,
+                                          batch, f, f, f, f, f, ws_bytes, nul)
+    assert fused(c, nul, 1, ws) == INV                                   # no indexer key
+    assert fused(c, f, 1, 16) == k.CSA2_ERR_WORKSPACE
+    assert fused(c, f, 0, ws) == k.CSA2_OK                               # empty batch
+    c256 = k.config(4, 64, 256, 16, 128, 64, 128, 0.044)
+    assert fused(c256, f, 1, ws) == k.CSA2_ERR_UNSUPPORTED               # latent of 256
