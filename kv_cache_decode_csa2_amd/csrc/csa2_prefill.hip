@@ -68,6 +68,35 @@ __device__ __forceinline__ int64_t phys_block(const PrefillArgs &a, int j) {
     return (ph >= 0 && ph < a.n_blocks) ? ph : -1;
 }
 
+// Key span of physical block ph (0 when absent): max over the 8 positions and H heads of
+// (largest - smallest E8M0 code among the head's G groups), from its scale bytes
+// (position-major, then head, then group), read as dwords.
+template <int H, int G>
+__device__ __forceinline__ int block_span(const PrefillArgs &a, int64_t ph) {
+    constexpr int CODES = kBlk * H * 16 * G;
+    constexpr int BYTES = CODES + kBlk * H * G;
+    constexpr int NW = kBlk * H * G / 4;
+    if (ph < 0) return 0;
+    const uint32_t *sw = reinterpret_cast<const uint32_t *>(a.idx_cache + ph * BYTES + CODES);
+    uint32_t w[NW];
+#pragma unroll
+    for (int i = 0; i < NW; i++) w[i] = sw[i];
+    int span = 0;
+#pragma unroll
+    for (int sh = 0; sh < kBlk * H; sh++) {
+        int lo = 255, hi = 0;
+#pragma unroll
+        for (int g = 0; g < G; g++) {
+            const int k = sh * G + g;
+            const int e = (int)((w[k >> 2] >> (8 * (k & 3))) & 0xffu);
+            lo = min(lo, e);
+            hi = max(hi, e);
+        }
+        span = max(span, hi - lo);
+    }
+    return span;
+}
+
 // kspan[j] = max over the 8 positions and H heads of block j of
 // (largest - smallest E8M0 code among the head's G groups); 0 for absent blocks.
 template <int H, int G>
@@ -222,10 +251,14 @@ __global__ __launch_bounds__(kPfThreads, 2) void k_prefill(PrefillArgs a) {
     const bool gl = g < G;  // lanes of groups >= G carry zeros (d_I < 128)
 
     // the chunk's table entries and key spans (blocks past Jend: absent, span 0)
+    // (at most 16 queries: one workgroup per position chunk, which computes the spans of its
+    // own blocks here instead of reading them from the span pass)
     for (int i = (int)threadIdx.x; i < kPfChunkBlocks; i += kPfThreads) {
         const int j = Jbeg + i;
-        meta.phys[i] = j < Jend ? (int32_t)phys_block(a, j) : -1;
-        meta.kspan[i] = j < Jend ? a.kspan[j] : (uint8_t)0;
+        const int32_t ph = j < Jend ? (int32_t)phys_block(a, j) : -1;
+        meta.phys[i] = ph;
+        if constexpr (SMALL) meta.kspan[i] = (uint8_t)block_span<H, G>(a, ph);
+        else meta.kspan[i] = j < Jend ? a.kspan[j] : (uint8_t)0;
     }
     __syncthreads();
     pf_dma<H, G>(a, meta, 0, stA);
@@ -430,10 +463,13 @@ typedef void (*PfFn)(const PrefillArgs &, hipStream_t);
 
 template <int H, int G>
 void launch_prefill(const PrefillArgs &a, hipStream_t s) {
+    if (a.n_q <= 16) {  // spans computed inside the scoring kernel
+        k_prefill<H, G, true><<<a.n_qt * a.n_pc, kPfThreads, 0, s>>>(a);
+        return;
+    }
     const int spans = (a.nb * kBlk + 255) / 256;
     k_prefill_span<H, G><<<spans, 256, 0, s>>>(a);
-    if (a.n_q <= 16) k_prefill<H, G, true><<<a.n_qt * a.n_pc, kPfThreads, 0, s>>>(a);
-    else k_prefill<H, G, false><<<a.n_qt * a.n_pc, kPfThreads, 0, s>>>(a);
+    k_prefill<H, G, false><<<a.n_qt * a.n_pc, kPfThreads, 0, s>>>(a);
 }
 
 bool pick_prefill(int H, int dI, PfFn *fn) {

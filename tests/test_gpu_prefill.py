@@ -79,6 +79,26 @@ def test_prefill_pool_covers_everything():
     _check(wl, 400, permute=False)
 
 
+@pytest.mark.parametrize("n_q", [10, 200])
+def test_prefill_key_spans_decide_the_path(n_q):
+    """Key groups scaled by 2^20 (every head's group 0, one block in seven) with plain
+    queries: only the key spans (the span pass, or at most 16 queries the scoring kernel's
+    own) send those tiles to the per-group path, and a single product over groups this far
+    apart would lose the small groups' terms."""
+    wl = si.small("pfkspan", 122, [3000], H_I=4, d_I=64, K_blk=64, k=128, W=16)
+
+    def keys_wide(x):
+        blk = np.arange(x.shape[0]) // 8
+        x[blk % 7 == 2, :, 0:32] *= np.float32(2.0 ** 20)
+
+    orig = si.idx_keys
+    try:
+        si.idx_keys = lambda w_, b, L=None: (lambda x: (keys_wide(x), x)[1])(orig(w_, b, L))
+        _check(wl, n_q)
+    finally:
+        si.idx_keys = orig
+
+
 def test_prefill_wide_exponent_spans_take_the_exact_path():
     """Scales that spread more than 9 binades within a head vector force the per-group
     path of the matrix kernel; mixed-sign head weights exercise the fma chain's signs."""
