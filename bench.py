@@ -60,6 +60,13 @@ def parse():
 
 
 class Bench:
+    """One decode group over the whole batch, as a model runs it layer after layer: every
+    index layer quantises its fp32 indexer query (MXFP4), the Full layer appends the token's
+    global-KV row inside its index call, Reindex rescores the pool, Reuse keeps the previous
+    top-k, and every layer appends its window row inside its attention call.  Each layer
+    keeps its own outputs (top-k, attention output and log-sum-exp), so that one replay can
+    be checked layer by layer."""
+
     def __init__(self, wl, replicas):
         import kv_cache_decode_csa2_amd as k
         import synth_inputs as si
@@ -68,43 +75,53 @@ class Bench:
 
         self.k, self.wl = k, wl
         table, nblk = make_table(wl.ctx, seed=wl.seed, permute=False)
+        self.table_np, self.n_blocks = table, nblk
         t0 = time.time()
         g = GpuState(wl, table, nblk, with_latent=True)
         log(f"caches built in {time.time() - t0:.1f}s")
         self.g = g
         self.cfg = g.cfg
-        per_rep = g.kv.numel() + g.idx.numel()
-        R = replicas or max(2, int(np.ceil((1 << 30) / per_rep)))
+        layout = k.csa2_layout(self.cfg)
+        self.ab = algorithmic_bytes(wl, layout)
+        # replicas rotate so that the other replicas' group bytes (>= 512 MB) pass between
+        # two uses of one replica: the 256 MB Infinity Cache cannot hold a replica's bytes
+        R = replicas or 1 + int(np.ceil((512 << 20) / self.ab["total"]))
         self.kv = [g.kv] + [g.kv.clone() for _ in range(R - 1)]
         self.idx = [g.idx] + [g.idx.clone() for _ in range(R - 1)]
         self.R = R
         B, maxb = table.shape
         self.maxb = maxb
-        # per-layer inputs
+        i32 = dict(dtype=torch.int32, device="cuda")
+        last = np.asarray(wl.ctx, np.int64) - 1
         self.layers = []
+        src = -1
         for li, mode in enumerate(wl.layers):
-            qc, qs, w = g.layer_q(li)
-            swa = g.layer_swa(li)
-            last = np.asarray(wl.ctx, np.int64) - 1
-            lay = dict(mode=mode, qc=qc, qs=qs, w=w, q=g.attn_q(li), swa=swa,
+            lay = dict(mode=mode, q=g.attn_q(li), swa=g.layer_swa(li),
                        swa_row=dev(np.stack([si.layer_swa_rows(wl, li, b, min(wl.ctx[b], wl.W))[-1]
                                              for b in range(B)])),
-                       pos=dev(last.astype(np.int32)))
+                       pos=dev(last.astype(np.int32)),
+                       out=torch.empty((B, wl.H_q, wl.D), dtype=torch.float32, device="cuda"),
+                       lse=torch.empty((B, wl.H_q), dtype=torch.float32, device="cuda"))
+            if mode in "FR":
+                lay["qf"] = dev(si.layer_idx_q(wl, li).reshape(B, wl.H_I * wl.d_I))
+                lay["w"] = dev(si.layer_idx_w(wl, li))
+                lay["qc"] = torch.empty((B, wl.H_I * wl.d_I // 2), dtype=torch.uint8, device="cuda")
+                lay["qs"] = torch.empty((B, wl.H_I * wl.d_I // 32), dtype=torch.uint8, device="cuda")
+                lay["topk"] = torch.empty((B, wl.k), **i32)
+                lay["topk_len"] = torch.empty(B, **i32)
+                k.csa2_quantize_mxfp4(lay["qf"], lay["qc"], lay["qs"])  # (for scan() alone)
+                src = li
+            lay["src"] = src  # the layer whose top-k this layer attends
             self.layers.append(lay)
-        # the current token's global row (position L-1), re-appended every step
+        # the current token's global row (position L-1), appended by the Full layer
         self.tok_lat = dev(np.stack([si.latent_rows(wl, b, wl.ctx[b])[-1] for b in range(B)]))
         self.tok_key = dev(np.stack([si.idx_keys(wl, b)[-1] for b in range(B)]))
         self.ws = [torch.zeros(k.csa2_workspace_bytes(self.cfg, k.CSA2_OP_INDEX_FULL, B, maxb),
                                dtype=torch.uint8, device="cuda") for _ in range(R)]
         self.ws_attn = torch.zeros(k.csa2_workspace_bytes(self.cfg, k.CSA2_OP_SPARSE_ATTN, B, maxb),
                                    dtype=torch.uint8, device="cuda")
-        i32 = dict(dtype=torch.int32, device="cuda")
         self.pool = torch.empty((B, wl.K_blk), **i32)
         self.pool_len = torch.empty(B, **i32)
-        self.topk = torch.empty((B, wl.k), **i32)
-        self.topk_len = torch.empty(B, **i32)
-        self.out = torch.empty((B, wl.H_q, wl.D), dtype=torch.float32, device="cuda")
-        self.lse = torch.empty((B, wl.H_q), dtype=torch.float32, device="cuda")
         torch.cuda.synchronize()
 
     def step(self, r, only=None):
@@ -114,23 +131,98 @@ class Bench:
         for li, lay in enumerate(self.layers):
             if only is not None and li != only:
                 continue
+            if lay["mode"] in "FR":
+                k.csa2_quantize_mxfp4(lay["qf"], lay["qc"], lay["qs"])
             if lay["mode"] == "F":
                 # the token's global-KV row (position L-1) is appended inside the index call
                 k.csa2_index_full_append(c, self.tok_lat, self.tok_key, lay["qc"], lay["qs"],
                                          lay["w"], kv, idx, g.n_blocks, g.table, g.ctx,
-                                         self.pool, self.pool_len, self.topk, self.topk_len, ws)
+                                         self.pool, self.pool_len, lay["topk"], lay["topk_len"], ws)
             elif lay["mode"] == "R":
                 k.csa2_index_reindex(c, lay["qc"], lay["qs"], lay["w"], idx, g.n_blocks, g.table,
-                                     g.ctx, self.pool, self.pool_len, self.topk, self.topk_len, ws)
+                                     g.ctx, self.pool, self.pool_len, lay["topk"], lay["topk_len"],
+                                     ws)
+            s = self.layers[lay["src"]]
             # the layer's window row (position L-1) is appended inside the attention call
             k.csa2_sparse_attn_append(c, lay["swa_row"], lay["pos"], lay["q"], kv, g.n_blocks,
-                                      g.table, lay["swa"], g.C, g.ctx, self.topk, self.topk_len,
-                                      self.out, self.lse, self.ws_attn)
+                                      g.table, lay["swa"], g.C, g.ctx, s["topk"], s["topk_len"],
+                                      lay["out"], lay["lse"], self.ws_attn)
+
+    def scribble(self, r):
+        """Overwrite what the group appends (position L-1 of the global caches of replica r
+        and of every window ring) with other values, so that a replay that follows must
+        write them itself."""
+        import synth_inputs as si
+        from gpu_harness import dev
+        k, g, wl = self.k, self.g, self.wl
+        B = wl.B
+        pos = dev((np.asarray(wl.ctx, np.int64) - 1).astype(np.int32))
+        k.csa2_append_global(self.cfg, dev(si.normal(wl.seed, 4001, (B, wl.D))),
+                             dev(si.normal(wl.seed, 4002, (B, wl.H_I * wl.d_I))), g.table,
+                             g.n_blocks, pos, 1, self.kv[r], self.idx[r])
+        for li, lay in enumerate(self.layers):
+            k.csa2_append_swa(self.cfg, dev(si.normal(wl.seed, 4003 + li, (B, wl.D))), pos, 1,
+                              lay["swa"], g.C)
+        torch.cuda.synchronize()
+
+    def results(self):
+        """Per-layer outputs of the last step (host arrays): the pool of the Full layer, and
+        per layer the attended top-k, its length, the attention output and log-sum-exp."""
+        res = []
+        for lay in self.layers:
+            s = self.layers[lay["src"]]
+            res.append(dict(mode=lay["mode"], topk=s["topk"].cpu().numpy(),
+                            topk_len=s["topk_len"].cpu().numpy(), out=lay["out"].cpu().numpy(),
+                            lse=lay["lse"].cpu().numpy()))
+        return dict(pool=self.pool.cpu().numpy(), pool_len=self.pool_len.cpu().numpy(),
+                    layers=res)
 
     def scan(self, r):
         lay = self.layers[0]
         self.k.csa2_index_full_scan(self.cfg, lay["qc"], lay["qs"], lay["w"], self.idx[r],
                                     self.g.n_blocks, self.g.table, self.g.ctx, self.ws[r])
+
+
+def oracle_group(wl, o):
+    """The decode group computed by the oracle on its own caches (which hold every position
+    up to L-1, i.e. the state after the group's appends): per-layer pool, top-k and
+    attention, in the layout of Bench.results()."""
+    import oracle
+    import synth_inputs as si
+    pool = topk = None
+    res = []
+    for li, mode in enumerate(wl.layers):
+        if mode in "FR":
+            q = si.layer_idx_q(wl, li).reshape(wl.B, wl.H_I * wl.d_I)
+            qc, qs = oracle.quantize_mxfp4(q)
+            w = si.layer_idx_w(wl, li)
+        if mode == "F":
+            p, pl, t, tl = oracle.index_full(o.cfg, qc, qs, w, o.idx, o.table, o.ctx)
+            pool, topk = (p, pl), (t, tl)
+        elif mode == "R":
+            topk = oracle.index_reindex(o.cfg, qc, qs, w, o.idx, o.table, o.ctx, *pool)
+        out, lse = oracle.sparse_attn(o.cfg, si.layer_attn_q(wl, li), o.kv, o.table,
+                                      o.layer_swa(li), o.C, o.ctx, *topk)
+        res.append(dict(mode=mode, topk=topk[0], topk_len=topk[1], out=out, lse=lse))
+    return dict(pool=pool[0], pool_len=pool[1], layers=res)
+
+
+def compare_group(got, ref, tol=2e-3):
+    """Index sets bit-exact and attention within tol per (sequence, head) row; returns a
+    summary dict whose "ok" says whether everything matched."""
+    from gpu_harness import attn_close
+    sets = bool(np.array_equal(got["pool"], ref["pool"]) and
+                np.array_equal(got["pool_len"], ref["pool_len"]))
+    rel_max = lse_max = 0.0
+    attn_ok = True
+    for g_, r_ in zip(got["layers"], ref["layers"]):
+        sets = sets and bool(np.array_equal(g_["topk"], r_["topk"]) and
+                             np.array_equal(g_["topk_len"], r_["topk_len"]))
+        ok, rel, lerr = attn_close(g_["out"], g_["lse"], r_["out"], r_["lse"], tol)
+        attn_ok = attn_ok and ok
+        rel_max, lse_max = max(rel_max, rel), max(lse_max, lerr)
+    return dict(index_sets_bit_exact=sets, attn_max_rel_err=float(f"{rel_max:.3g}"),
+                lse_max_err=float(f"{lse_max:.3g}"), tolerance=tol, ok=bool(sets and attn_ok))
 
 
 class PrefillBench:
@@ -194,17 +286,22 @@ class PrefillBench:
 
 
 def prefill_work(wl, layout):
-    """Algorithmic work of the prefill scoring kernel (matrix-core scores + epilogue): causal
-    (query, position) pairs, FP4 flops, vector-ALU epilogue instructions and the HBM bytes
-    of this design (keys read once, exact position scores, block and group maxima written)."""
+    """Algorithmic work of the prefill indexer's scoring kernel: causal (query, position)
+    pairs, the FP4 flops of their scores, and the bytes the method must move -- every key
+    once plus the selection outputs (pool and top-k of every query).  The kernel's own
+    intermediate writes (an exact score per causal pair, block and group maxima) are a
+    design choice, counted apart as `design_bytes`."""
     n_q, L = wl.n_q, wl.ctx[0]
     t = np.arange(L - n_q, L, dtype=np.int64)
     pairs = int((t + 1).sum())
     blocks = int(((t + 8) // 8).sum())
     flops = 2 * pairs * wl.H_I * wl.d_I
     alu = 2 * pairs * wl.H_I  # ReLU + fma per (pair, head)
-    bytes_ = L * (layout.idx_block_bytes // 8) + 4 * pairs + 4 * blocks + 4 * ((blocks + 7) // 8)
-    return dict(pairs=pairs, flops=flops, alu=alu, bytes=bytes_)
+    keys = L * (layout.idx_block_bytes // 8)
+    outputs = n_q * (wl.K_blk + wl.k + 2) * 4
+    design = 4 * pairs + 4 * blocks + 4 * ((blocks + 7) // 8)
+    return dict(pairs=pairs, flops=flops, alu=alu, bytes=keys + outputs, key_bytes=keys,
+                output_bytes=outputs, design_bytes=design)
 
 
 MFMA_FP4_PEAK_TFLOPS = 10100.0
@@ -247,7 +344,7 @@ def main_prefill(a, wl):
         f" ({R} replicas)")
     import hashlib
     src = open(os.path.join(ROOT, "kv_cache_decode_csa2_amd", "csrc", "csa2_prefill.hip"), "rb").read()
-    traffic = traffic_for(hashlib.sha256(src).hexdigest(), COUNTER_RUNS[counter_kind(wl)][3])
+    traffic = traffic_for(hashlib.sha256(src).hexdigest(), COUNTER_RUNS[counter_kind(wl)][3], wl.name)
     reps = 40 if spec else 5
     sg = capture(lambda: [bench.scan(i % R) for i in range(reps)])
     timed(lambda i: sg.replay(), 1)
@@ -258,7 +355,9 @@ def main_prefill(a, wl):
           "alu": pw["alu"] / sec / 1e12 / ALU_PEAK_TOPS}
     log(f"prefill scoring {scan_ms:.3f} ms: hbm {fr['hbm']:.3f}, mfma {fr['mfma']:.3f}, "
         f"alu {fr['alu']:.3f} of peak")
-    bound = max(fr, key=fr.get)
+    # the chunk's scores are a dense FP4 contraction (matrix-core bound by arithmetic
+    # intensity); a verification step's 6 queries read every key for few flops (HBM bound)
+    bound = "hbm" if spec else "mfma"
     ach = {"hbm": pw["bytes"] / sec / 1e9, "mfma": pw["flops"] / sec / 1e12,
            "alu": pw["alu"] / sec / 1e12}[bound]
     peak = {"hbm": HBM_PEAK_GBS, "mfma": MFMA_FP4_PEAK_TFLOPS, "alu": ALU_PEAK_TOPS}[bound]
@@ -276,14 +375,62 @@ def main_prefill(a, wl):
                    "indexer": f"{wl.H_I}x{wl.d_I} fp4", "pool_blocks": wl.K_blk, "topk": wl.k,
                    "q_heads": wl.H_q, "window": wl.W, "replicas": R, "graph": not a.eager},
         "roofline": {"bound": bound, "achieved": round(ach, 2), "peak": peak, "unit": unit,
-                     "frac": round(fr[bound], 4), "traffic": traffic, "kernel": "k_prefill",
+                     "frac": round(fr[bound], 4), "traffic": traffic,
+                     "traffic_over_algorithmic": (round(traffic / pw["bytes"], 2)
+                                                  if traffic else None),
+                     "algorithmic_bytes": pw["bytes"], "kernel": "k_prefill",
                      "kernel_us": round(scan_ms * 1e3, 2),
                      "fractions": {k_: round(v, 4) for k_, v in fr.items()}, "work": pw},
         "cpu_baseline": None,
     }
-    if spec and not a.no_cpu_baseline:
-        result["cpu_baseline"] = cpu_baseline_spec(wl, a.cpu_seconds)
+    if not a.no_cpu_baseline:
+        result["cpu_baseline"] = (cpu_baseline_spec(wl, a.cpu_seconds) if spec else
+                                  cpu_baseline_prefill(wl, a.cpu_seconds))
     print(json.dumps(result), flush=True)
+
+
+def cpu_baseline_prefill(wl, seconds):
+    """The oracle on a bounded sample of the prefill chunk: its queries taken one at a time
+    from the end of the chunk backwards (each the Full steps on its causal prefix, then its
+    attention over its top-k and window), for about `seconds`; query-tokens/s."""
+    import oracle
+    import synth_inputs as si
+    from harness import OracleState, make_table
+    table, nblk = make_table(wl.ctx, seed=wl.seed, permute=False)
+    t0 = time.time()
+    o = OracleState(wl, table, nblk, with_latent=True)
+    log(f"oracle caches built in {time.time() - t0:.1f}s")
+    n_q = wl.n_q
+    q_pos0 = wl.ctx[0] - n_q
+    qc, qs = oracle.quantize_mxfp4(si.prefill_idx_q(wl, 0, n_q).reshape(n_q, -1))
+    w = si.prefill_idx_w(wl, 0, n_q)
+    C = n_q + wl.W
+    first = max(0, q_pos0 - wl.W + 1)
+    rows = si.layer_swa_rows(wl, 0, 0, q_pos0 + n_q - first)
+    ring = oracle.alloc_swa(o.cfg, 1, C)
+    oracle.append_swa(o.cfg, rows[None], np.array([first], np.int32), ring, C)
+    qa = si.prefill_attn_q(wl, 0, n_q)
+    n = 0
+    t0 = time.time()
+    while n < n_q:
+        i = n_q - 1 - n
+        _, _, t, tl = oracle.index_prefill(o.cfg, qc[i:i + 1], qs[i:i + 1], w[i:i + 1],
+                                           q_pos0 + i, o.idx, o.table[0])
+        oracle.sparse_attn_prefill(o.cfg, qa[i:i + 1], o.kv, o.table[0], ring[0], C, q_pos0 + i,
+                                   t, tl)
+        n += 1
+        el = time.time() - t0
+        if el >= seconds:
+            break
+    try:
+        cores = len(os.sched_getaffinity(0))
+    except AttributeError:
+        cores = os.cpu_count()
+    cores = int(os.environ.get("OMP_NUM_THREADS", cores))
+    return dict(value=n / el, unit="query-tokens/s", cores=cores, kind="oracle",
+                sample=f"the last {n} of the {n_q} queries of the {wl.name} workload, each "
+                       f"indexed over its whole causal prefix (~{wl.ctx[0]} positions) and "
+                       f"attended, {el:.1f} s wall")
 
 
 def capture(fn):
@@ -326,29 +473,20 @@ def algorithmic_bytes(wl, layout):
     return dict(scan=scan, reindex=reindex, attn=attn, total=total)
 
 
-def cpu_baseline(wl, seconds):
-    import oracle
+def cpu_baseline(wl, seconds, gpu_first=None):
+    """The oracle on whole decode groups of the workload for about `seconds` (its first
+    group is also the reference the GPU's first replay is compared with)."""
     from harness import OracleState, make_table
     table, nblk = make_table(wl.ctx, seed=wl.seed, permute=False)
     t0 = time.time()
     o = OracleState(wl, table, nblk, with_latent=True)
     log(f"oracle caches built in {time.time() - t0:.1f}s")
-    ins = []
-    for li, mode in enumerate(wl.layers):
-        ins.append((mode, o.layer_q(li), o.layer_swa(li)))
-    import synth_inputs as si
-    qa = [si.layer_attn_q(wl, li) for li in range(len(wl.layers))]
     groups = 0
+    first = None
     t0 = time.time()
     while True:
-        pool = topk = None
-        for li, (mode, q, swa) in enumerate(ins):
-            if mode == "F":
-                p, pl, t, tl = oracle.index_full(o.cfg, *q, o.idx, o.table, o.ctx)
-                pool, topk = (p, pl), (t, tl)
-            elif mode == "R":
-                topk = oracle.index_reindex(o.cfg, *q, o.idx, o.table, o.ctx, *pool)
-            oracle.sparse_attn(o.cfg, qa[li], o.kv, o.table, swa, o.C, o.ctx, *topk)
+        res = oracle_group(wl, o)
+        first = first or res
         groups += 1
         el = time.time() - t0
         if el >= seconds:
@@ -358,10 +496,15 @@ def cpu_baseline(wl, seconds):
     except AttributeError:
         cores = os.cpu_count()
     cores = int(os.environ.get("OMP_NUM_THREADS", cores))
-    return dict(value=groups * len(wl.layers) / el, unit="layer-steps/s", cores=cores,
+    base = dict(value=groups * len(wl.layers) / el, unit="layer-steps/s", cores=cores,
                 kind="oracle",
                 sample=f"{groups} full {''.join(wl.layers)} groups of the {wl.name} workload "
                        f"(all {sum(wl.ctx)} positions scanned per Full layer), {el:.1f} s wall")
+    parity = None
+    if gpu_first is not None:
+        parity = dict(checked="first replay of the group graph (replica 0) against the oracle's "
+                              "first group", **compare_group(gpu_first, first))
+    return base, parity
 
 
 def cpu_baseline_spec(wl, seconds):
@@ -404,16 +547,16 @@ def cpu_baseline_spec(wl, seconds):
                        f"all {wl.ctx[0]} positions scored per query), {el:.1f} s wall")
 
 
-def traffic_for(kernel_src_hash, name="scan_long_1m_counters.json"):
+def traffic_for(kernel_src_hash, name="scan_long_1m_counters.json", workload="long_1m"):
     """HBM bytes per launch measured by the counter runs recorded in profiles/<name>, if they
-    were taken on the current kernel source (else None)."""
+    were taken on the current kernel source and on this workload (else None)."""
     path = os.path.join(ROOT, "profiles", name)
     try:
         with open(path) as f:
             d = json.load(f)
     except (OSError, ValueError):
         return None
-    if d.get("source_sha256") != kernel_src_hash:
+    if d.get("source_sha256") != kernel_src_hash or not d.get("workload", "").startswith(workload + ":"):
         return None
     return d.get("bytes_per_launch")
 
@@ -584,8 +727,7 @@ def main():
         torch.cuda.synchronize()
         calibration_copy(a.calib_mb)
         return
-    layout = bench.k.csa2_layout(bench.cfg)
-    ab = algorithmic_bytes(wl, layout)
+    ab = bench.ab
     R = bench.R
     log(f"workload {wl.name}: {R} replicas, algorithmic bytes/group {ab['total'] / 1e6:.1f} MB")
 
@@ -594,6 +736,10 @@ def main():
     else:
         graphs = [capture(lambda r=r: bench.step(r)) for r in range(R)]
         step = lambda i: graphs[i % R].replay()  # noqa: E731
+    # the first replay's per-layer results, compared with the oracle in the CPU leg
+    step(0)
+    torch.cuda.synchronize()
+    first = bench.results()
     timed(step, a.warmup)
     ms = timed(step, a.steps)
     n_layers = len(wl.layers)
@@ -616,7 +762,7 @@ def main():
     scan_ms = timed(lambda i: sg.replay(), 5) / reps
     achieved = ab["scan"] / (scan_ms / 1e3) / 1e9
     src = open(os.path.join(ROOT, "kv_cache_decode_csa2_amd", "csrc", "csa2_index.hip"), "rb").read()
-    traffic = traffic_for(hashlib.sha256(src).hexdigest())
+    traffic = traffic_for(hashlib.sha256(src).hexdigest(), workload=wl.name)
     log(f"scan {scan_ms * 1e3:.2f} us -> {achieved:.0f} GB/s")
 
     result = {
@@ -625,6 +771,7 @@ def main():
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "mxfp4",
         "data": "synthetic",
         "config": {"workload": wl.name, "batch": wl.B, "context": wl.max_ctx,
+                   "context_min": int(min(wl.ctx)), "context_total": int(sum(wl.ctx)),
                    "indexer": f"{wl.H_I}x{wl.d_I} fp4", "pool_blocks": wl.K_blk, "topk": wl.k,
                    "q_heads": wl.H_q, "window": wl.W, "layers": wl.layers,
                    "replicas": R, "graph": not a.eager},
@@ -639,7 +786,7 @@ def main():
         "cpu_baseline": None,
     }
     if not a.no_cpu_baseline:
-        result["cpu_baseline"] = cpu_baseline(wl, a.cpu_seconds)
+        result["cpu_baseline"], result["parity"] = cpu_baseline(wl, a.cpu_seconds, first)
     print(json.dumps(result), flush=True)
 
 

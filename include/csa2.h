@@ -29,10 +29,12 @@
  *     buffers described here; the results for such entries are unspecified.
  *   - A workspace `ws` of at least csa2_workspace_bytes() bytes is needed by the index
  *     and attention calls (one per kind of call).  An index workspace needs no
- *     initialisation.  An attention workspace holds arrival counters: zero it once after
- *     allocating it (hipMemset); every attention call leaves them at zero again, so it
- *     must not be shared with other kinds of call.  Calls that share a workspace must
- *     not run concurrently.
+ *     initialisation.  An attention workspace starts with a fixed region of 1024 arrival
+ *     counters (4 KB, the same bytes for every shape): zero it once after allocating it
+ *     (hipMemset); every attention call leaves the counters at zero again, so one
+ *     attention workspace of the largest size needed serves decode, append and prefill
+ *     attention calls of any batch or query count.  It must not be shared with index
+ *     calls.  Calls that share a workspace must not run concurrently.
  */
 #ifndef CSA2_H
 #define CSA2_H
@@ -290,7 +292,8 @@ int csa2_index_prefill_finish(const csa2_config *cfg, const uint8_t *q_codes,
  * t_i + 1: the main-KV rows of topk[i][0 .. topk_len[i]) and the window rows
  * max(0, t_i + 1 - W) .. t_i.  block_table is the sequence's row of maxb entries;
  * swa_ring is the sequence's ring of C slots (position p in slot p % C), which must still
- * hold every attended window row, i.e. C >= n_q + W - 1 once the chunk's rows are in it.
+ * hold every attended window row, i.e. C >= n_q + W - 1 once the chunk's rows are in it
+ * (INVALID otherwise, with W > 0 and n_q > 0).
  * q [n_q][H_q][D] bf16 bits; out [n_q][H_q][D], lse [n_q][H_q].  q_pos0, n_q are host values
  * with q_pos0 + n_q <= 8*maxb.  Workspace: CSA2_OP_SPARSE_ATTN bytes for batch = n_q. */
 int csa2_sparse_attn_prefill(const csa2_config *cfg, const uint16_t *q,

@@ -632,6 +632,8 @@ int sparse_attn(const csa2_config *c, const float *swa_new, const int32_t *new_p
     if (attn_splits(c->topk, c->swa_window) > kMaxSplits) return CSA2_ERR_UNSUPPORTED;
     const AttnPlan plan = attn_plan(batch, c->n_q_heads, c->topk, c->swa_window);
     const int nsplit = plan.nsplit;
+    // (the plan splits only batches of fewer than kAttnCounters (sequence, head group) pairs)
+    if (nsplit > 1 && (int64_t)batch * (c->n_q_heads / 16) > kAttnCounters) return CSA2_ERR_HIP;
     const WsAttn wl = ws_attn(batch, c->n_q_heads, c->kv_dim, nsplit);
     if (ws_bytes < wl.total) return CSA2_ERR_WORKSPACE;
     if (batch == 0) return CSA2_OK;
@@ -693,6 +695,9 @@ extern "C" int csa2_sparse_attn_prefill(const csa2_config *c, const uint16_t *q,
                                         const int32_t *topk_len, float *out, float *lse,
                                         void *ws, size_t ws_bytes, hipStream_t stream) {
     if (q_pos0 < 0 || n_q < 0 || (int64_t)q_pos0 + n_q > (int64_t)maxb * kBlk)
+        return CSA2_ERR_INVALID;
+    // the ring must still hold the oldest attended window row of the chunk's first query
+    if (c && c->swa_window > 0 && n_q > 0 && (int64_t)C < (int64_t)n_q + c->swa_window - 1)
         return CSA2_ERR_INVALID;
     return sparse_attn(c, nullptr, nullptr, q, kv_cache, n_blocks, block_table, maxb, swa_ring,
                        nullptr, C, nullptr, q_pos0, n_q, topk, topk_len, out, lse, ws, ws_bytes,

@@ -97,17 +97,22 @@ __host__ __device__ inline AttnPlan attn_plan(int B, int Hq, int k, int W) {
     return AttnPlan{(units + ups - 1) / ups, ns * ups, ns};
 }
 
+// The arrival counters sit in a fixed region at the start of every attention workspace, so
+// one zero-once workspace can serve calls of any batch, query count or split plan: splits
+// (nsplit > 1) only happen for fewer than kAttnCounters (sequence, head group) pairs, and
+// pair i always counts at word i.  Partials follow the counters.
+constexpr int kAttnCounters = 1024;
 __host__ __device__ inline WsAttn ws_attn(int B, int Hq, int D, int nsplit) {
     WsAttn w;
     size_t o = 0;
+    w.count = o;   o = align256(o + sizeof(int32_t) * (size_t)kAttnCounters);
     if (nsplit <= 1) {  // one split: the kernel writes the outputs, no partials
-        w.part_o = w.part_ml = w.count = 0;
-        w.total = 256;
+        w.part_o = w.part_ml = o;
+        w.total = o;
         return w;
     }
     w.part_o = o;  o = align256(o + sizeof(float) * (size_t)B * nsplit * Hq * D);
     w.part_ml = o; o = align256(o + sizeof(float) * 2 * (size_t)B * nsplit * Hq);
-    w.count = o;   o = align256(o + sizeof(int32_t) * (size_t)B * ((Hq + 15) / 16));
     w.total = o;
     return w;
 }

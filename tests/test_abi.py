@@ -47,8 +47,9 @@ def test_workspace_sizes_grow_with_batch_and_context():
     # 640 rows = 10 chunks of 64 in 5 pairs: at 8 sequences every pair is a split, whose
     # partial numerators (16 heads x 512 fp32) sit in the workspace
     assert k.csa2_workspace_bytes(c, k.CSA2_OP_SPARSE_ATTN, 8, 1) >= 8 * 5 * 16 * 512 * 4
-    # a batch that fills the chip alone takes one split: no partials
-    assert k.csa2_workspace_bytes(c, k.CSA2_OP_SPARSE_ATTN, 4096, 1) <= 256
+    # a batch that fills the chip alone takes one split: no partials, only the fixed
+    # 1024-counter region every attention workspace starts with
+    assert k.csa2_workspace_bytes(c, k.CSA2_OP_SPARSE_ATTN, 4096, 1) == 4096
 
 
 @pytest.mark.parametrize("bad", [
@@ -113,6 +114,14 @@ def test_attention_shape_limits():
     st = lib.csa2_sparse_attn(C.byref(c), fake, fake, 1, fake, 8, fake, 64, fake, 1, fake, fake,
                               fake, fake, fake, 1 << 30, None)   # ring smaller than window
     assert st == k.CSA2_ERR_INVALID
+
+    def prefill(C_slots, n_q):
+        return lib.csa2_sparse_attn_prefill(C.byref(c), fake, fake, 1, fake, 64, fake, C_slots,
+                                            100, n_q, fake, fake, fake, fake, fake, 1 << 30, None)
+    # a prefill chunk of 10 queries with a 128-row window needs a ring of 10 + 127 slots
+    assert prefill(136, 10) == k.CSA2_ERR_INVALID
+    assert prefill(128, 2) == k.CSA2_ERR_INVALID
+    assert prefill(137, 0) == k.CSA2_OK                                   # no query: no-op
 
 
 def test_block_transfer_and_fused_append_host_errors():

@@ -315,7 +315,8 @@ def test_global_tier_round_trip():
     csa2_blocks_gather into pinned host memory, the device caches are cleared, and the rows
     come back with csa2_blocks_scatter into a different physical placement (a new block
     table).  Every logical block's bytes are unchanged, and Full, Reindex and attention give
-    bit-identical results to those before the round trip (which equal the oracle's)."""
+    bit-identical results to those before the round trip; after the restore, pool and top-k
+    of both index layers equal the oracle's and attention is within 2e-3 of it."""
     import kv_cache_decode_csa2_amd as k
     wl = si.small("tier", 41, [3000, 517, 9], H_I=4, d_I=64, K_blk=32, k=64, H_q=16, W=128)
     table, nblk = make_table(wl.ctx, seed=41)
@@ -361,6 +362,15 @@ def test_global_tier_round_trip():
     after = run()
     for x, y in zip(before, after):
         assert np.array_equal(x, y)
+    # and the restored caches index and attend as the oracle does on its own caches
+    assert np.array_equal(after[0], po) and np.array_equal(after[1], plo)
+    assert np.array_equal(after[2], to) and np.array_equal(after[3], tlo)
+    tRo, tlRo = oracle.index_reindex(o.cfg, *o.layer_q(1), o.idx, o.table, o.ctx, po, plo)
+    assert np.array_equal(after[4], tRo) and np.array_equal(after[5], tlRo)
+    ro, rl = oracle.sparse_attn(o.cfg, si.layer_attn_q(wl, 0), o.kv, o.table, o.layer_swa(0),
+                                o.C, o.ctx, to, tlo)
+    ok, rel, lerr = attn_close(after[6], after[7], ro, rl)
+    assert ok, (rel, lerr)
 
     # entries outside the cache: gather writes zero rows, scatter leaves the cache alone
     bad = dev(np.array([-1, nblk, 0], np.int32))

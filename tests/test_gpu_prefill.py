@@ -27,6 +27,56 @@ def _first_diff(a, b, n=5):
     return [(tuple(i), a[tuple(i)], b[tuple(i)]) for i in idx]
 
 
+def _ngmax(maxb):
+    return (((maxb + 7) // 8) + 3) & ~3
+
+
+def _al(x):
+    return (x + 255) & ~255
+
+
+def _ws_scores(ws, n_q, maxb, blk0=0, blk1=None):
+    """The scoring kernel's outputs in the prefill workspace, for blocks [blk0, blk1): position
+    scores [block][query][slot], block maxima [group][query][block % 8] and group maxima
+    [query][group] (the layout the selection reads), as host arrays."""
+    blk1 = maxb if blk1 is None else blk1
+    row = n_q * 8 * 4
+    ps = ws[blk0 * row:blk1 * row].view(torch.float32).reshape(blk1 - blk0, n_q, 8)
+    ng = _ngmax(maxb)
+    ob = _al(maxb * row)
+    g0, g1 = blk0 // 8, (blk1 + 7) // 8
+    bs = ws[ob + g0 * row:ob + g1 * row].view(torch.float32).reshape(g1 - g0, n_q, 8)
+    og = _al(ob + ng * row)
+    gm = ws[og:og + n_q * ng * 4].view(torch.float32).reshape(n_q, ng)[:, g0:g1]
+    return _np(ps), _np(bs), _np(gm)
+
+
+def _check_scores(o, qo, q_pos0, queries, ps, bs, gm, blk0, blk1):
+    """Scores of the listed queries at positions 8*blk0 .. 8*blk1-1 (their causal part)
+    equal the oracle's bit for bit; so do the block maxima of those blocks and the maxima
+    of the groups of 8 blocks that lie wholly inside the range."""
+    table_row = o.table[0]
+    for i in queries:
+        t = q_pos0 + i
+        p0 = blk0 * 8
+        n = min(blk1 * 8, t + 1) - p0
+        if n <= 0:
+            continue
+        ref = oracle.index_scores(o.cfg, qo[0][i], qo[1][i], qo[2][i], o.idx, table_row[blk0:], n)
+        got = ps[:, i, :].reshape(-1)[:n]
+        assert np.array_equal(got.view(np.uint32), ref.view(np.uint32)), (i, _first_diff(got, ref))
+        rb = oracle.block_scores(ref, n)
+        gb = bs.reshape(-1, bs.shape[1], 8)[:, i, :].reshape(-1)[blk0 % 8:][:len(rb)]
+        assert np.array_equal(gb.view(np.uint32), rb.view(np.uint32)), (i, "block maxima")
+        for gi in range((blk0 + 7) // 8, (blk1 + 7) // 8):
+            j0 = gi * 8 - blk0
+            vis = rb[j0:j0 + 8]
+            whole = gi * 8 + 8 <= blk1 or blk1 * 8 > t  # every visible block of it is in range
+            if len(vis) == 0 or not whole:
+                continue
+            assert gm[i, gi - blk0 // 8] == vis.max(), (i, gi, "group maximum")
+
+
 def _oracle_q(wl, n_q, scale_fn=None, w=None):
     q = si.prefill_idx_q(wl, 0, n_q)
     if scale_fn is not None:
@@ -47,8 +97,14 @@ def _check(wl, n_q, permute=True, scale_fn=None, w=None):
     if w is not None:
         wg = torch.from_numpy(np.ascontiguousarray(w, np.float32)).cuda()
     assert np.array_equal(_np(qc), qo[0]) and np.array_equal(_np(qs), qo[1])
-    pg, plg, tg, tlg = index_prefill(g, qc, qs, wg, q_pos0)
+    maxb = table.shape[1]
+    ws = torch.empty(k.csa2_workspace_bytes(g.cfg, k.CSA2_OP_INDEX_PREFILL, n_q, maxb),
+                     dtype=torch.uint8, device="cuda")
+    pg, plg, tg, tlg = index_prefill(g, qc, qs, wg, q_pos0, ws=ws)
     torch.cuda.synchronize()
+    # what the selection read: every causal score, block and group maximum of every query
+    ps, bs, gm = _ws_scores(ws, n_q, maxb)
+    _check_scores(o, qo, q_pos0, range(n_q), ps, bs, gm, 0, maxb)
     assert np.array_equal(_np(plg), plo), _first_diff(_np(plg), plo)
     assert np.array_equal(_np(pg), po), _first_diff(_np(pg), po)
     assert np.array_equal(_np(tlg), tlo), _first_diff(_np(tlg), tlo)
@@ -175,32 +231,50 @@ def test_prefill_attention_within_tolerance(L, n_q, H_q, W):
 def test_prefill_workload_sampled():
     """The prefill workload at full size: 4096 queries at positions 258048..262143 of a
     262,144-token context, indexer 8 x 128, pool 2048 blocks, top-512, then attention of
-    64 heads over each query's top-512 and window.  Six queries are checked against the
-    oracle (index sets bit-exact, attention within 2e-3); every query is checked for the
-    properties that hold at any size (lengths, ascending order, top-k inside the pool,
-    causality)."""
+    64 heads over each query's top-k and window.  Against the oracle:
+    * every score, block maximum and group maximum of two whole 128-query tiles (queries
+      0..127 and 2048..2175) over four 2048-position chunks each -- the first, a middle one
+      and the chunks that hold the tiles' causal boundary -- bit for bit;
+    * pool, top-k and attention of the queries on both sides of a query-tile boundary
+      (127 | 128), of a position-chunk boundary (query 2047 at position 260095 ends chunk
+      126, query 2048 opens chunk 127) and of the first and last query.
+    Every query is checked for the properties that hold at any size (lengths, ascending
+    order, top-k inside the pool, causality)."""
     wl = si.workload("prefill")
     n_q, L = wl.n_q, wl.ctx[0]
     q_pos0 = L - n_q
     table, nblk = make_table(wl.ctx, seed=wl.seed, permute=False)
+    maxb = table.shape[1]
     g = GpuState(wl, table, nblk)
     o = OracleState(wl, table, nblk)
     qc, qs, wg = prefill_q(wl, 0, n_q)
-    pgd, plgd, tgd, tlgd = index_prefill(g, qc, qs, wg, q_pos0)
+    ws = torch.empty(k.csa2_workspace_bytes(g.cfg, k.CSA2_OP_INDEX_PREFILL, n_q, maxb),
+                     dtype=torch.uint8, device="cuda")
+    pgd, plgd, tgd, tlgd = index_prefill(g, qc, qs, wg, q_pos0, ws=ws)
     pg, plg, tg, tlg = [_np(x) for x in (pgd, plgd, tgd, tlgd)]
     C, ring_o, ring_g = _rings(wl, o, g, q_pos0, n_q)
     qa = si.prefill_attn_q(wl, 0, n_q)
     go, gl = _attn_prefill(g, dev(qa.view(np.int16)), ring_g, C, q_pos0, tgd, tlgd)
     go, gl = _np(go), _np(gl)
-    del g
+    qo = _oracle_q(wl, n_q)
+    # whole tiles x chunks (chunk = 256 blocks = 2048 positions)
+    for tile0 in (0, 2048):
+        t_first = q_pos0 + tile0
+        diag = t_first // 2048
+        for c in sorted({0, 63, diag, diag + 1}):
+            if c * 2048 >= L:
+                continue
+            ps, bs, gm = _ws_scores(ws, n_q, maxb, c * 256, (c + 1) * 256)
+            _check_scores(o, qo, q_pos0, range(tile0, tile0 + 128), ps, bs, gm, c * 256,
+                          (c + 1) * 256)
+    del ws, g
     torch.cuda.empty_cache()
     assert np.all(plg == wl.K_blk) and np.all(tlg == wl.k)
     assert np.all(np.diff(pg, axis=1) > 0) and np.all(np.diff(tg, axis=1) > 0)
     t = q_pos0 + np.arange(n_q)
     assert np.all(tg[:, -1] <= t) and np.all(pg[:, -1] <= t // 8)
     assert all(np.isin(tg[i] // 8, pg[i]).all() for i in range(0, n_q, 97))
-    qo = _oracle_q(wl, n_q)
-    for i in (0, 1, 127, 128, 2049, n_q - 1):
+    for i in (0, 1, 127, 128, 2047, 2048, n_q - 1):
         ctx = np.array([q_pos0 + i + 1], np.int32)
         po, plo, to, tlo = oracle.index_full(o.cfg, qo[0][i:i + 1], qo[1][i:i + 1],
                                              qo[2][i:i + 1], o.idx, o.table, ctx)
