@@ -55,7 +55,9 @@ enum {
     CSA2_ERR_INVALID = -1,     /* null pointer, bad size, dims % 32 != 0, k > 8*K_blk, ... */
     CSA2_ERR_UNSUPPORTED = -2, /* a shape this build has no kernel for */
     CSA2_ERR_WORKSPACE = -3,   /* ws_bytes < csa2_workspace_bytes() */
-    CSA2_ERR_HIP = -4          /* a kernel launch failed */
+    CSA2_ERR_HIP = -4,         /* a kernel launch failed */
+    CSA2_ERR_SCRATCH = -5      /* csa2_sparse_attn_noalloc: the shape needs more than its
+                                  static scratch (16 MiB) */
 };
 
 enum {
@@ -302,6 +304,24 @@ int csa2_sparse_attn_prefill(const csa2_config *cfg, const uint16_t *q,
                              int32_t C, int32_t q_pos0, int32_t n_q, const int32_t *topk,
                              const int32_t *topk_len, float *out, float *lse, void *ws,
                              size_t ws_bytes, hipStream_t stream);
+
+/* csa2_sparse_attn without a workspace, for callers that cannot allocate device memory
+ * (code under HIP graph capture, tight serving loops, harnesses that forbid hipMalloc):
+ * the same arguments, kernels and results as csa2_sparse_attn, bit for bit, with the split
+ * partials and arrival counters in a 16 MiB device array the library holds on each GPU it
+ * runs on (for the life of the process).  It allocates nothing, and calls no allocating
+ * routine.  The first call on a device looks the array's address up (hipGetSymbolAddress,
+ * the device current) and clears its counters with a fill kernel on `stream`; every call
+ * leaves them at zero again.  All calls on one GPU share the array, so calls that overlap
+ * on one GPU (other streams, other threads) race: serialise them.  A shape whose partials
+ * exceed the array (csa2_workspace_bytes(CSA2_OP_SPARSE_ATTN) > 16 MiB; with k = 512 and
+ * W = 128: 16 heads at batch 102..1023, 64 heads at batch 26..255) returns CSA2_ERR_SCRATCH
+ * and launches nothing. */
+int csa2_sparse_attn_noalloc(const csa2_config *cfg, const uint16_t *q, const uint8_t *kv_cache,
+                             int64_t n_blocks, const int32_t *block_table, int32_t maxb,
+                             const uint8_t *swa_cache, int32_t C, const int32_t *ctx_len,
+                             int32_t batch, const int32_t *topk, const int32_t *topk_len,
+                             float *out, float *lse, hipStream_t stream);
 
 /* Human-readable status. */
 const char *csa2_status_str(int status);

@@ -15,6 +15,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libcsa2.so")
 
 CSA2_OK, CSA2_ERR_INVALID, CSA2_ERR_UNSUPPORTED, CSA2_ERR_WORKSPACE, CSA2_ERR_HIP = 0, -1, -2, -3, -4
+CSA2_ERR_SCRATCH = -5
 CSA2_OP_INDEX_FULL, CSA2_OP_INDEX_REINDEX, CSA2_OP_SPARSE_ATTN, CSA2_OP_INDEX_PREFILL = 1, 2, 3, 4
 CSA2_BLOCK = 8
 
@@ -25,7 +26,7 @@ EXPORTS = [
     "csa2_index_reindex", "csa2_index_prefill", "csa2_index_prefill_scan",
     "csa2_index_prefill_finish", "csa2_sparse_attn", "csa2_sparse_attn_append",
     "csa2_sparse_attn_prefill", "csa2_index_full_append", "csa2_blocks_gather",
-    "csa2_blocks_scatter", "csa2_status_str",
+    "csa2_blocks_scatter", "csa2_sparse_attn_noalloc", "csa2_status_str",
 ]
 
 
@@ -87,6 +88,8 @@ def load() -> C.CDLL:
                                           vp, vp, sz, vp],
             "csa2_sparse_attn": [cfgp, vp, vp, i64, vp, i32, vp, i32, vp, i32, vp, vp, vp, vp, vp,
                                  sz, vp],
+            "csa2_sparse_attn_noalloc": [cfgp, vp, vp, i64, vp, i32, vp, i32, vp, i32, vp, vp, vp,
+                                         vp, vp],
             "csa2_sparse_attn_prefill": [cfgp, vp, vp, i64, vp, i32, vp, i32, i32, i32, vp, vp,
                                          vp, vp, vp, sz, vp],
             "csa2_sparse_attn_append": [cfgp, vp, vp, vp, vp, i64, vp, i32, vp, i32, vp, i32, vp, vp,
@@ -290,3 +293,12 @@ def csa2_sparse_attn_prefill(cfg, q, kv_cache, n_blocks, table_row, swa_ring, C_
     _call("csa2_sparse_attn_prefill", C.byref(cfg), _p(q), _p(kv_cache), int(n_blocks),
           _p(table_row), table_row.numel(), _p(swa_ring), int(C_slots), int(q_pos0), int(n_q),
           _p(topk), _p(topk_len), _p(out), _p(lse), _p(ws), ws.numel(), _stream(stream))
+
+
+def csa2_sparse_attn_noalloc(cfg, q, kv_cache, n_blocks, block_table, swa_cache, C_slots, ctx_len,
+                             topk, topk_len, out, lse, stream=None):
+    """csa2_sparse_attn with the library's static per-device scratch instead of a workspace."""
+    batch, maxb = block_table.shape
+    _call("csa2_sparse_attn_noalloc", C.byref(cfg), _p(q), _p(kv_cache), int(n_blocks),
+          _p(block_table), maxb, _p(swa_cache), int(C_slots), _p(ctx_len), batch, _p(topk),
+          _p(topk_len), _p(out), _p(lse), _stream(stream))

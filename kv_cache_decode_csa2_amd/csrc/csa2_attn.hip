@@ -28,6 +28,8 @@
 //      arrive (an atomic counter) combines them.
 // The appended window row of the fused append is staged in LDS by DMA at kernel start and
 // quantised once by the stream whose chunk attends it.
+#include <mutex>
+
 #include "csa2_quant.h"
 
 namespace csa2 {
@@ -616,14 +618,52 @@ using namespace csa2;
 
 namespace {
 
+// ------------------------------------------------------------------ static scratch
+//
+// csa2_sparse_attn_noalloc keeps the split partials and arrival counters of its calls in
+// this file-scope device array instead of a caller workspace; each GPU the library runs on
+// holds its own copy until the process ends.  In host code `scratch` names a host-side
+// stand-in, so its device address is looked up once per device (hipGetSymbolAddress, with
+// that device current) and only that address reaches kernels.
+constexpr size_t kScratchBytes = (size_t)16 << 20;
+constexpr int kMaxDevices = 64;
+static __device__ __align__(256) uint8_t scratch[kScratchBytes];
+
+std::mutex g_scratch_mu;
+void *g_scratch_dev[kMaxDevices] = {};
+
+__global__ void k_zero_words(int32_t *p, int n) {
+    const int i = (int)(blockIdx.x * blockDim.x + threadIdx.x);
+    if (i < n) p[i] = 0;
+}
+
+// The scratch address of the current device; on the first call for a device its arrival
+// counters are cleared (a fill kernel on `stream`), after which every call leaves them at
+// zero again.
+int scratch_of_current_device(hipStream_t stream, void **out) {
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return CSA2_ERR_HIP;
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_dev[dev]) {
+        void *p = nullptr;
+        if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return CSA2_ERR_HIP;
+        k_zero_words<<<(kAttnCounters + 255) / 256, 256, 0, stream>>>((int32_t *)p, kAttnCounters);
+        if (hipGetLastError() != hipSuccess) return CSA2_ERR_HIP;
+        g_scratch_dev[dev] = p;
+    }
+    *out = g_scratch_dev[dev];
+    return CSA2_OK;
+}
+
 int sparse_attn(const csa2_config *c, const float *swa_new, const int32_t *new_pos,
                 const uint16_t *q, const uint8_t *kv_cache, int64_t n_blocks,
                 const int32_t *block_table, int32_t maxb, const uint8_t *swa_cache,
                 uint8_t *swa_out, int32_t C, const int32_t *ctx_len, int32_t q_pos0,
                 int32_t batch, const int32_t *topk, const int32_t *topk_len, float *out,
-                float *lse, void *ws, size_t ws_bytes, hipStream_t stream) {
+                float *lse, void *ws, size_t ws_bytes, hipStream_t stream,
+                bool use_scratch = false) {
     if (!c || !q || !kv_cache || n_blocks <= 0 || !block_table || maxb <= 0 ||
-        batch < 0 || !topk || !topk_len || !out || !lse || !ws || c->topk <= 0 ||
+        batch < 0 || !topk || !topk_len || !out || !lse || (!ws && !use_scratch) || c->topk <= 0 ||
         c->swa_window < 0 || c->n_q_heads <= 0 || c->kv_dim <= 0)
         return CSA2_ERR_INVALID;
     if (c->swa_window > 0 && (!swa_cache || C < c->swa_window)) return CSA2_ERR_INVALID;
@@ -635,6 +675,13 @@ int sparse_attn(const csa2_config *c, const float *swa_new, const int32_t *new_p
     // (the plan splits only batches of fewer than kAttnCounters (sequence, head group) pairs)
     if (nsplit > 1 && (int64_t)batch * (c->n_q_heads / 16) > kAttnCounters) return CSA2_ERR_HIP;
     const WsAttn wl = ws_attn(batch, c->n_q_heads, c->kv_dim, nsplit);
+    if (use_scratch) {
+        if (wl.total > kScratchBytes) return CSA2_ERR_SCRATCH;
+        if (batch == 0) return CSA2_OK;
+        const int st = scratch_of_current_device(stream, &ws);
+        if (st) return st;
+        ws_bytes = kScratchBytes;
+    }
     if (ws_bytes < wl.total) return CSA2_ERR_WORKSPACE;
     if (batch == 0) return CSA2_OK;
     AttnArgs a{};
@@ -716,4 +763,17 @@ extern "C" int csa2_sparse_attn_append(const csa2_config *c, const float *swa_ro
     return sparse_attn(c, swa_rows, pos, q, kv_cache, n_blocks, block_table, maxb, swa_cache,
                        swa_cache, C, ctx_len, 0, batch, topk, topk_len, out, lse, ws, ws_bytes,
                        stream);
+}
+
+extern "C" int csa2_sparse_attn_noalloc(const csa2_config *c, const uint16_t *q,
+                                        const uint8_t *kv_cache, int64_t n_blocks,
+                                        const int32_t *block_table, int32_t maxb,
+                                        const uint8_t *swa_cache, int32_t C,
+                                        const int32_t *ctx_len, int32_t batch,
+                                        const int32_t *topk, const int32_t *topk_len, float *out,
+                                        float *lse, hipStream_t stream) {
+    if (!ctx_len) return CSA2_ERR_INVALID;
+    return sparse_attn(c, nullptr, nullptr, q, kv_cache, n_blocks, block_table, maxb, swa_cache,
+                       nullptr, C, ctx_len, 0, batch, topk, topk_len, out, lse, nullptr, 0, stream,
+                       true);
 }

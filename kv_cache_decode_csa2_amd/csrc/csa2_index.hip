@@ -817,6 +817,7 @@ extern "C" const char *csa2_status_str(int s) {
     case CSA2_ERR_UNSUPPORTED: return "unsupported shape";
     case CSA2_ERR_WORKSPACE: return "workspace too small";
     case CSA2_ERR_HIP: return "HIP launch failure";
+    case CSA2_ERR_SCRATCH: return "shape needs more than the 16 MiB static scratch";
     default: return "unknown status";
     }
 }
