@@ -92,14 +92,12 @@ class Bench:
         B, maxb = table.shape
         self.maxb = maxb
         i32 = dict(dtype=torch.int32, device="cuda")
-        last = np.asarray(wl.ctx, np.int64) - 1
         self.layers = []
         src = -1
         for li, mode in enumerate(wl.layers):
             lay = dict(mode=mode, q=g.attn_q(li), swa=g.layer_swa(li),
                        swa_row=dev(np.stack([si.layer_swa_rows(wl, li, b, min(wl.ctx[b], wl.W))[-1]
                                              for b in range(B)])),
-                       pos=dev(last.astype(np.int32)),
                        out=torch.empty((B, wl.H_q, wl.D), dtype=torch.float32, device="cuda"),
                        lse=torch.empty((B, wl.H_q), dtype=torch.float32, device="cuda"))
             if mode in "FR":
@@ -125,28 +123,31 @@ class Bench:
         torch.cuda.synchronize()
 
     def step(self, r, only=None):
-        """One decode group on replica r (only: just that layer, for the per-mode times)."""
+        """One decode group on replica r (only: just that layer, for the per-mode times):
+        one fused layer call per layer (the indexer query's quantise, the token's appends,
+        the index step of the layer's mode and its attention)."""
         k, g, c = self.k, self.g, self.cfg
         kv, idx, ws = self.kv[r], self.idx[r], self.ws[r]
         for li, lay in enumerate(self.layers):
             if only is not None and li != only:
                 continue
-            if lay["mode"] in "FR":
-                k.csa2_quantize_mxfp4(lay["qf"], lay["qc"], lay["qs"])
             if lay["mode"] == "F":
-                # the token's global-KV row (position L-1) is appended inside the index call
-                k.csa2_index_full_append(c, self.tok_lat, self.tok_key, lay["qc"], lay["qs"],
-                                         lay["w"], kv, idx, g.n_blocks, g.table, g.ctx,
-                                         self.pool, self.pool_len, lay["topk"], lay["topk_len"], ws)
+                k.csa2_decode_full_layer(c, lay["qf"], lay["w"], self.tok_lat, self.tok_key,
+                                         lay["swa_row"], lay["q"], kv, idx, g.n_blocks, g.table,
+                                         lay["swa"], g.C, g.ctx, self.pool, self.pool_len,
+                                         lay["topk"], lay["topk_len"], lay["out"], lay["lse"], ws,
+                                         self.ws_attn)
             elif lay["mode"] == "R":
-                k.csa2_index_reindex(c, lay["qc"], lay["qs"], lay["w"], idx, g.n_blocks, g.table,
-                                     g.ctx, self.pool, self.pool_len, lay["topk"], lay["topk_len"],
-                                     ws)
-            s = self.layers[lay["src"]]
-            # the layer's window row (position L-1) is appended inside the attention call
-            k.csa2_sparse_attn_append(c, lay["swa_row"], lay["pos"], lay["q"], kv, g.n_blocks,
-                                      g.table, lay["swa"], g.C, g.ctx, s["topk"], s["topk_len"],
-                                      lay["out"], lay["lse"], self.ws_attn)
+                k.csa2_decode_reindex_layer(c, lay["qf"], lay["w"], lay["swa_row"], lay["q"], kv,
+                                            idx, g.n_blocks, g.table, lay["swa"], g.C, g.ctx,
+                                            self.pool, self.pool_len, lay["topk"],
+                                            lay["topk_len"], lay["out"], lay["lse"], ws,
+                                            self.ws_attn)
+            else:
+                s = self.layers[lay["src"]]
+                k.csa2_decode_reuse_layer(c, lay["swa_row"], lay["q"], kv, g.n_blocks, g.table,
+                                          lay["swa"], g.C, g.ctx, s["topk"], s["topk_len"],
+                                          lay["out"], lay["lse"], self.ws_attn)
 
     def scribble(self, r):
         """Overwrite what the group appends (position L-1 of the global caches of replica r
@@ -181,6 +182,15 @@ class Bench:
         lay = self.layers[0]
         self.k.csa2_index_full_scan(self.cfg, lay["qc"], lay["qs"], lay["w"], self.idx[r],
                                     self.g.n_blocks, self.g.table, self.g.ctx, self.ws[r])
+
+
+def kernels_per_mode(wl):
+    """Kernel launches of one layer of each mode in the step (the fused layer calls): Full =
+    scan (with the query quantise and global append) + selection + attention, plus a global
+    append of its own for 8 x 128-style layouts (four 32-groups per head, two or more heads);
+    Reindex = rescoring scan + selection + attention; Reuse = attention."""
+    own_append = wl.d_I // 32 > 2 and wl.H_I > 1
+    return {"F": 4 if own_append else 3, "R": 3, "U": 1}
 
 
 def oracle_group(wl, o):
@@ -780,6 +790,8 @@ def main():
                      "traffic": traffic, "kernel": SCAN_KERNEL,
                      "kernel_us": round(scan_ms * 1e3, 3), "algorithmic_bytes": ab["scan"]},
         "group": {"algorithmic_bytes": ab["total"],
+                  "kernels_per_mode": kernels_per_mode(wl),
+                  "pages_kernels_per_reuse_layer": {"decode": 11, "prefill": 15},
                   "hbm_frac": round(ab["total"] / (ms / 1e3) / 1e9 / HBM_PEAK_GBS, 4),
                   "us_per_mode": modes,
                   "sequence_layer_steps_per_s": round(value * wl.B, 1)},

@@ -305,6 +305,51 @@ int csa2_sparse_attn_prefill(const csa2_config *cfg, const uint16_t *q,
                              const int32_t *topk_len, float *out, float *lse, void *ws,
                              size_t ws_bytes, hipStream_t stream);
 
+/* One decode layer per call (N4 of the design: the steps of a layer fused into as few
+ * launches as their data dependences allow).  Modes as [KV] defines them: a Full layer
+ * appends its token and scans the whole visible context into a pool and a top-k, a Reindex
+ * layer rescores the latest pool, a Reuse layer keeps the latest top-k; every layer appends
+ * its token's window row and attends its top-k rows plus its window [3][W].  The token is
+ * the one at position ctx_len[b] - 1 of each sequence.  Each call equals, bit for bit, the
+ * separate calls it stands for (outputs, cache and ring bytes):
+ *   full:    csa2_quantize_mxfp4(q_idx); csa2_index_full_append(tok_latent, tok_key, ...);
+ *            csa2_sparse_attn_append(swa_row, pos = ctx_len - 1, ...)
+ *   reindex: csa2_quantize_mxfp4(q_idx); csa2_index_reindex(...); csa2_sparse_attn_append
+ *   reuse:   csa2_sparse_attn_append(swa_row, pos = ctx_len - 1, ...) with the given topk
+ * The indexer query is quantised inside the scan, so the kernels per layer are: Full 3
+ * (scan with the query quantise and the global append, selection, attention with the window
+ * append; 4 when d_I = 128 and H_I >= 2, whose global append runs first), Reindex 3
+ * (rescoring scan, selection, attention), Reuse 1.  q_idx [batch][H_I*d_I] fp32 (head-major),
+ * w_idx [batch][H_I] fp32, tok_latent [batch][D] fp32 (may be NULL: no main-KV append),
+ * tok_key [batch][H_I*d_I] fp32, swa_row [batch][D] fp32, q_attn [batch][H_q][D] bf16 bits.
+ * ws_index: CSA2_OP_INDEX_FULL bytes; ws_attn: CSA2_OP_SPARSE_ATTN bytes (zeroed once, as
+ * for csa2_sparse_attn).  Host-side argument errors of any step return before anything is
+ * launched. */
+int csa2_decode_full_layer(const csa2_config *cfg, const float *q_idx, const float *w_idx,
+                           const float *tok_latent, const float *tok_key, const float *swa_row,
+                           const uint16_t *q_attn, uint8_t *kv_cache, uint8_t *idx_cache,
+                           int64_t n_blocks, const int32_t *block_table, int32_t maxb,
+                           uint8_t *swa_cache, int32_t C, const int32_t *ctx_len, int32_t batch,
+                           int32_t *pool_blocks, int32_t *pool_len, int32_t *topk,
+                           int32_t *topk_len, float *out, float *lse, void *ws_index,
+                           size_t ws_index_bytes, void *ws_attn, size_t ws_attn_bytes,
+                           hipStream_t stream);
+int csa2_decode_reindex_layer(const csa2_config *cfg, const float *q_idx, const float *w_idx,
+                              const float *swa_row, const uint16_t *q_attn,
+                              const uint8_t *kv_cache, const uint8_t *idx_cache,
+                              int64_t n_blocks, const int32_t *block_table, int32_t maxb,
+                              uint8_t *swa_cache, int32_t C, const int32_t *ctx_len,
+                              int32_t batch, const int32_t *pool_blocks, const int32_t *pool_len,
+                              int32_t *topk, int32_t *topk_len, float *out, float *lse,
+                              void *ws_index, size_t ws_index_bytes, void *ws_attn,
+                              size_t ws_attn_bytes, hipStream_t stream);
+int csa2_decode_reuse_layer(const csa2_config *cfg, const float *swa_row, const uint16_t *q_attn,
+                            const uint8_t *kv_cache, int64_t n_blocks, const int32_t *block_table,
+                            int32_t maxb, uint8_t *swa_cache, int32_t C, const int32_t *ctx_len,
+                            int32_t batch, const int32_t *topk, const int32_t *topk_len,
+                            float *out, float *lse, void *ws_attn, size_t ws_attn_bytes,
+                            hipStream_t stream);
+
 /* csa2_sparse_attn without a workspace, for callers that cannot allocate device memory
  * (code under HIP graph capture, tight serving loops, harnesses that forbid hipMalloc):
  * the same arguments, kernels and results as csa2_sparse_attn, bit for bit, with the split

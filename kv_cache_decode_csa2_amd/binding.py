@@ -26,7 +26,8 @@ EXPORTS = [
     "csa2_index_reindex", "csa2_index_prefill", "csa2_index_prefill_scan",
     "csa2_index_prefill_finish", "csa2_sparse_attn", "csa2_sparse_attn_append",
     "csa2_sparse_attn_prefill", "csa2_index_full_append", "csa2_blocks_gather",
-    "csa2_blocks_scatter", "csa2_sparse_attn_noalloc", "csa2_status_str",
+    "csa2_blocks_scatter", "csa2_sparse_attn_noalloc", "csa2_decode_full_layer",
+    "csa2_decode_reindex_layer", "csa2_decode_reuse_layer", "csa2_status_str",
 ]
 
 
@@ -88,6 +89,12 @@ def load() -> C.CDLL:
                                           vp, vp, sz, vp],
             "csa2_sparse_attn": [cfgp, vp, vp, i64, vp, i32, vp, i32, vp, i32, vp, vp, vp, vp, vp,
                                  sz, vp],
+            "csa2_decode_full_layer": [cfgp, vp, vp, vp, vp, vp, vp, vp, vp, i64, vp, i32, vp, i32,
+                                       vp, i32, vp, vp, vp, vp, vp, vp, vp, sz, vp, sz, vp],
+            "csa2_decode_reindex_layer": [cfgp, vp, vp, vp, vp, vp, vp, i64, vp, i32, vp, i32, vp,
+                                          i32, vp, vp, vp, vp, vp, vp, vp, sz, vp, sz, vp],
+            "csa2_decode_reuse_layer": [cfgp, vp, vp, vp, i64, vp, i32, vp, i32, vp, i32, vp, vp,
+                                        vp, vp, vp, sz, vp],
             "csa2_sparse_attn_noalloc": [cfgp, vp, vp, i64, vp, i32, vp, i32, vp, i32, vp, vp, vp,
                                          vp, vp],
             "csa2_sparse_attn_prefill": [cfgp, vp, vp, i64, vp, i32, vp, i32, i32, i32, vp, vp,
@@ -302,3 +309,34 @@ def csa2_sparse_attn_noalloc(cfg, q, kv_cache, n_blocks, block_table, swa_cache,
     _call("csa2_sparse_attn_noalloc", C.byref(cfg), _p(q), _p(kv_cache), int(n_blocks),
           _p(block_table), maxb, _p(swa_cache), int(C_slots), _p(ctx_len), batch, _p(topk),
           _p(topk_len), _p(out), _p(lse), _stream(stream))
+
+
+def csa2_decode_full_layer(cfg, q_idx, w_idx, tok_latent, tok_key, swa_row, q_attn, kv_cache,
+                           idx_cache, n_blocks, block_table, swa_cache, C_slots, ctx_len,
+                           pool_blocks, pool_len, topk, topk_len, out, lse, ws_index, ws_attn,
+                           stream=None):
+    batch, maxb = block_table.shape
+    _call("csa2_decode_full_layer", C.byref(cfg), _p(q_idx), _p(w_idx), _p(tok_latent),
+          _p(tok_key), _p(swa_row), _p(q_attn), _p(kv_cache), _p(idx_cache), int(n_blocks),
+          _p(block_table), maxb, _p(swa_cache), int(C_slots), _p(ctx_len), batch,
+          _p(pool_blocks), _p(pool_len), _p(topk), _p(topk_len), _p(out), _p(lse), _p(ws_index),
+          ws_index.numel(), _p(ws_attn), ws_attn.numel(), _stream(stream))
+
+
+def csa2_decode_reindex_layer(cfg, q_idx, w_idx, swa_row, q_attn, kv_cache, idx_cache, n_blocks,
+                              block_table, swa_cache, C_slots, ctx_len, pool_blocks, pool_len,
+                              topk, topk_len, out, lse, ws_index, ws_attn, stream=None):
+    batch, maxb = block_table.shape
+    _call("csa2_decode_reindex_layer", C.byref(cfg), _p(q_idx), _p(w_idx), _p(swa_row),
+          _p(q_attn), _p(kv_cache), _p(idx_cache), int(n_blocks), _p(block_table), maxb,
+          _p(swa_cache), int(C_slots), _p(ctx_len), batch, _p(pool_blocks), _p(pool_len),
+          _p(topk), _p(topk_len), _p(out), _p(lse), _p(ws_index), ws_index.numel(), _p(ws_attn),
+          ws_attn.numel(), _stream(stream))
+
+
+def csa2_decode_reuse_layer(cfg, swa_row, q_attn, kv_cache, n_blocks, block_table, swa_cache,
+                            C_slots, ctx_len, topk, topk_len, out, lse, ws_attn, stream=None):
+    batch, maxb = block_table.shape
+    _call("csa2_decode_reuse_layer", C.byref(cfg), _p(swa_row), _p(q_attn), _p(kv_cache),
+          int(n_blocks), _p(block_table), maxb, _p(swa_cache), int(C_slots), _p(ctx_len), batch,
+          _p(topk), _p(topk_len), _p(out), _p(lse), _p(ws_attn), ws_attn.numel(), _stream(stream))

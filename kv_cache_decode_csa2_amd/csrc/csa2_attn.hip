@@ -30,6 +30,7 @@
 // quantised once by the stream whose chunk attends it.
 #include <mutex>
 
+#include "csa2_layer.h"
 #include "csa2_quant.h"
 
 namespace csa2 {
@@ -71,6 +72,7 @@ struct AttnArgs {
     // slot new_pos[b] % C before it is attended
     const float *swa_new;
     const int32_t *new_pos;
+    int32_t new_pos_off;  // the appended position is new_pos[b] + new_pos_off
     uint8_t *swa_out;
 };
 
@@ -262,7 +264,7 @@ __global__ __launch_bounds__(NS * kStreamThreads, 3 - NS) void k_attn(AttnArgs a
     const int L = clamp_ctx(a.ctx_len ? len_v : a.q_pos0 + b + 1, a.maxb);
     const int tl = max(0, min(tl_v, a.k));
     const int w0 = max(0, L - a.W), nwin = L - w0;
-    const int np_b = a.swa_new ? np_v : -1;
+    const int np_b = a.swa_new ? np_v + a.new_pos_off : -1;
 
     // ---- the appended row, when one of this workgroup's chunks attends it: its 16 quantising
     //      threads (lanes 0..15 of the stream's first wave) stage the fp32 row in LDS by DMA
@@ -656,12 +658,12 @@ int scratch_of_current_device(hipStream_t stream, void **out) {
 }
 
 int sparse_attn(const csa2_config *c, const float *swa_new, const int32_t *new_pos,
-                const uint16_t *q, const uint8_t *kv_cache, int64_t n_blocks,
+                int32_t new_pos_off, const uint16_t *q, const uint8_t *kv_cache, int64_t n_blocks,
                 const int32_t *block_table, int32_t maxb, const uint8_t *swa_cache,
                 uint8_t *swa_out, int32_t C, const int32_t *ctx_len, int32_t q_pos0,
                 int32_t batch, const int32_t *topk, const int32_t *topk_len, float *out,
                 float *lse, void *ws, size_t ws_bytes, hipStream_t stream,
-                bool use_scratch = false) {
+                bool use_scratch = false, bool dry = false) {
     if (!c || !q || !kv_cache || n_blocks <= 0 || !block_table || maxb <= 0 ||
         batch < 0 || !topk || !topk_len || !out || !lse || (!ws && !use_scratch) || c->topk <= 0 ||
         c->swa_window < 0 || c->n_q_heads <= 0 || c->kv_dim <= 0)
@@ -683,7 +685,7 @@ int sparse_attn(const csa2_config *c, const float *swa_new, const int32_t *new_p
         ws_bytes = kScratchBytes;
     }
     if (ws_bytes < wl.total) return CSA2_ERR_WORKSPACE;
-    if (batch == 0) return CSA2_OK;
+    if (batch == 0 || dry) return CSA2_OK;
     AttnArgs a{};
     a.q = q;
     a.kv = kv_cache;
@@ -714,6 +716,7 @@ int sparse_attn(const csa2_config *c, const float *swa_new, const int32_t *new_p
     a.lse = lse;
     a.swa_new = swa_new;
     a.new_pos = new_pos;
+    a.new_pos_off = new_pos_off;
     a.swa_out = swa_out;
     if (plan.ns == 2) k_attn<2><<<dim3(nsplit, batch * a.HG), 2 * kStreamThreads, 0, stream>>>(a);
     else k_attn<1><<<dim3(nsplit, batch * a.HG), kStreamThreads, 0, stream>>>(a);
@@ -722,6 +725,25 @@ int sparse_attn(const csa2_config *c, const float *swa_new, const int32_t *new_p
 
 }  // namespace
 
+namespace csa2 {
+
+// The window append of the token at position ctx_len[b] - 1 fused with attention (the layer
+// calls): csa2_sparse_attn_append with pos = ctx_len - 1.
+int sparse_attn_layer(const csa2_config *c, const float *swa_rows, const uint16_t *q,
+                      const uint8_t *kv_cache, int64_t n_blocks, const int32_t *block_table,
+                      int32_t maxb, uint8_t *swa_cache, int32_t C, const int32_t *ctx_len,
+                      int32_t batch, const int32_t *topk, const int32_t *topk_len, float *out,
+                      float *lse, void *ws, size_t ws_bytes, hipStream_t stream, bool dry) {
+    if (!swa_rows || !swa_cache || !ctx_len) return CSA2_ERR_INVALID;
+    // (a dry run checks the host-side arguments; topk may not exist yet, any non-null stands in)
+    const int32_t *tk = dry && !topk ? ctx_len : topk, *tl = dry && !topk_len ? ctx_len : topk_len;
+    return sparse_attn(c, swa_rows, ctx_len, -1, q, kv_cache, n_blocks, block_table, maxb,
+                       swa_cache, swa_cache, C, ctx_len, 0, batch, tk, tl, out, lse, ws,
+                       ws_bytes, stream, false, dry);
+}
+
+}  // namespace csa2
+
 extern "C" int csa2_sparse_attn(const csa2_config *c, const uint16_t *q, const uint8_t *kv_cache,
                                 int64_t n_blocks, const int32_t *block_table, int32_t maxb,
                                 const uint8_t *swa_cache, int32_t C, const int32_t *ctx_len,
@@ -729,7 +751,7 @@ extern "C" int csa2_sparse_attn(const csa2_config *c, const uint16_t *q, const u
                                 float *out, float *lse, void *ws, size_t ws_bytes,
                                 hipStream_t stream) {
     if (!ctx_len) return CSA2_ERR_INVALID;
-    return sparse_attn(c, nullptr, nullptr, q, kv_cache, n_blocks, block_table, maxb, swa_cache,
+    return sparse_attn(c, nullptr, nullptr, 0, q, kv_cache, n_blocks, block_table, maxb, swa_cache,
                        nullptr, C, ctx_len, 0, batch, topk, topk_len, out, lse, ws, ws_bytes,
                        stream);
 }
@@ -746,7 +768,7 @@ extern "C" int csa2_sparse_attn_prefill(const csa2_config *c, const uint16_t *q,
     // the ring must still hold the oldest attended window row of the chunk's first query
     if (c && c->swa_window > 0 && n_q > 0 && (int64_t)C < (int64_t)n_q + c->swa_window - 1)
         return CSA2_ERR_INVALID;
-    return sparse_attn(c, nullptr, nullptr, q, kv_cache, n_blocks, block_table, maxb, swa_ring,
+    return sparse_attn(c, nullptr, nullptr, 0, q, kv_cache, n_blocks, block_table, maxb, swa_ring,
                        nullptr, C, nullptr, q_pos0, n_q, topk, topk_len, out, lse, ws, ws_bytes,
                        stream);
 }
@@ -760,7 +782,7 @@ extern "C" int csa2_sparse_attn_append(const csa2_config *c, const float *swa_ro
                                        const int32_t *topk_len, float *out, float *lse, void *ws,
                                        size_t ws_bytes, hipStream_t stream) {
     if (!swa_rows || !pos || !swa_cache || !ctx_len) return CSA2_ERR_INVALID;
-    return sparse_attn(c, swa_rows, pos, q, kv_cache, n_blocks, block_table, maxb, swa_cache,
+    return sparse_attn(c, swa_rows, pos, 0, q, kv_cache, n_blocks, block_table, maxb, swa_cache,
                        swa_cache, C, ctx_len, 0, batch, topk, topk_len, out, lse, ws, ws_bytes,
                        stream);
 }
@@ -773,7 +795,7 @@ extern "C" int csa2_sparse_attn_noalloc(const csa2_config *c, const uint16_t *q,
                                         const int32_t *topk, const int32_t *topk_len, float *out,
                                         float *lse, hipStream_t stream) {
     if (!ctx_len) return CSA2_ERR_INVALID;
-    return sparse_attn(c, nullptr, nullptr, q, kv_cache, n_blocks, block_table, maxb, swa_cache,
+    return sparse_attn(c, nullptr, nullptr, 0, q, kv_cache, n_blocks, block_table, maxb, swa_cache,
                        nullptr, C, ctx_len, 0, batch, topk, topk_len, out, lse, nullptr, 0, stream,
                        true);
 }

@@ -26,6 +26,7 @@
 #include <algorithm>
 
 #include "csa2_block.h"
+#include "csa2_layer.h"
 #include "csa2_quant.h"
 #include "csa2_select.h"
 
@@ -154,6 +155,7 @@ __device__ __forceinline__ float combine_heads(const Query<H, G> &Q, float r, in
 struct ScanArgs {
     const uint8_t *q_codes;
     const uint8_t *q_scales;
+    const float *q_f32;  // the unquantised query [B][H*dI] (non-null: quantised in the kernel)
     const float *w;
     const uint8_t *idx_cache;
     int64_t n_blocks;
@@ -216,6 +218,53 @@ struct AppendRegs {
     float4 lat[LR];
     int ph;
 };
+
+// The unquantised query of one sequence as one wave loads it: float4 chunk 64r + lane in
+// f[r] (every element loaded once per wave).
+template <int H, int G>
+struct QueryF32 {
+    static constexpr int R = (H * G * 8 + kWave - 1) / kWave;  // rounds of chunks
+    float4 f[R];
+};
+
+template <int H, int G>
+__device__ __forceinline__ void load_query_f32(QueryF32<H, G> &F, const float *qf) {
+    const float4 *src = reinterpret_cast<const float4 *>(qf);
+    const int lane = lane_id();
+#pragma unroll
+    for (int r = 0; r < F.R; r++) F.f[r] = src[min(r * kWave + lane, H * G * 8 - 1)];
+}
+
+// MXFP4 codes and scales of the loaded query for head h, in the layout load_query_raw reads:
+// every 32-group is encoded by 8 lanes (coop_fp4, the encoder of the append kernels, so the
+// codes equal csa2_quantize_mxfp4's), then each lane gathers its head's groups.
+template <int H, int G>
+__device__ __forceinline__ void quant_query(QueryRaw<H, G> &R, const QueryF32<H, G> &F,
+                                            const float *w, int h) {
+    uint32_t kw[F.R], ksc[F.R];
+#pragma unroll
+    for (int r = 0; r < F.R; r++) coop_fp4(F.f[r], kw[r], ksc[r]);
+    R.s = 0u;
+#pragma unroll
+    for (int g = 0; g < G; g++) {
+        const int q = h * G + g, rq = q / 8, src = 8 * (q % 8);
+        uint32_t wv[4], sv = 0u;
+#pragma unroll
+        for (int rr = 0; rr < F.R; rr++) {
+#pragma unroll
+            for (int i = 0; i < 4; i++) {
+                const uint32_t x = (uint32_t)__builtin_amdgcn_ds_bpermute(4 * (src + 2 * i), (int)kw[rr]);
+                wv[i] = rr == rq ? x : (rr == 0 ? x : wv[i]);
+            }
+            const uint32_t y = (uint32_t)__builtin_amdgcn_ds_bpermute(4 * src, (int)ksc[rr]);
+            sv = rr == rq ? y : (rr == 0 ? y : sv);
+        }
+        R.c[g] = make_uint4(wv[0], wv[1], wv[2], wv[3]);
+        R.s |= sv << (8 * g);
+    }
+#pragma unroll
+    for (int j = 0; j < H; j++) R.w[j] = w[j];
+}
 
 // Items (8 blocks or 8 pool entries) of sequence b.
 template <bool RESCORE>
@@ -400,6 +449,8 @@ __global__ __launch_bounds__(kScanThreads, 2) void k_scan(ScanArgs a) {
     };
     Query<H, G> Q;
     QueryRaw<H, G> QR;
+    QueryF32<H, G> QF;
+    const bool qf32 = a.q_f32 != nullptr;
     int pre[DM - 1] = {};
     if (inter) {
 #pragma unroll
@@ -407,7 +458,14 @@ __global__ __launch_bounds__(kScanThreads, 2) void k_scan(ScanArgs a) {
             const int e = entry0(i) + bw;
             pre[i] = RESCORE ? a.pool[min(e, a.K_blk - 1)] : a.table[min(e, a.maxb - 1)];
         }
-        load_query_raw<H, G>(QR, a.q_codes, a.q_scales, a.w, h);
+        if (qf32) {
+            load_query_f32<H, G>(QF, a.q_f32);
+            // a query of several rounds is encoded at once (its floats would stay live across
+            // the prefix); one round is encoded after it, overlapping the load with the prefix
+            if constexpr (QueryF32<H, G>::R > 1) quant_query<H, G>(QR, QF, a.w, h);
+        } else {
+            load_query_raw<H, G>(QR, a.q_codes, a.q_scales, a.w, h);
+        }
     }
     const int total = __builtin_amdgcn_readfirstlane(build_item_prefix<RESCORE>(a, sh_prefix, sh_len, sh_raw, sh_scan));
     const int per = (total + nwaves - 1) / nwaves;
@@ -495,11 +553,18 @@ __global__ __launch_bounds__(kScanThreads, 2) void k_scan(ScanArgs a) {
             m.ph = table_row[m.j >= 0 ? m.j : 0];
         };
 
-        if (inter)
+        if (inter) {
+            if constexpr (QueryF32<H, G>::R == 1)
+                if (qf32) quant_query<H, G>(QR, QF, a.w, h);
             decode_query<H, G>(Q, QR);
-        else
+        } else if (qf32) {
+            load_query_f32<H, G>(QF, a.q_f32 + (size_t)b * H * 32 * G);
+            quant_query<H, G>(QR, QF, a.w + (size_t)b * H, h);
+            decode_query<H, G>(Q, QR);
+        } else {
             load_query<H, G>(Q, a.q_codes + (size_t)b * H * 16 * G, a.q_scales + (size_t)b * H * G,
                              a.w + (size_t)b * H, h);
+        }
 
         // ---- fused append: does this segment score the block of the new token (position
         //      pn = L_b - 1, unclamped)?  k_new: that step (uniform; -1: not here).  Its inputs
@@ -729,10 +794,11 @@ int launched() { return hipGetLastError() == hipSuccess ? CSA2_OK : CSA2_ERR_HIP
 
 ScanArgs scan_args(const csa2_config *c, const uint8_t *qc, const uint8_t *qs, const float *w,
                    const uint8_t *idx, int64_t n_blocks, const int32_t *table, int32_t maxb,
-                   const int32_t *ctx, int32_t B) {
+                   const int32_t *ctx, int32_t B, const float *q_f32 = nullptr) {
     ScanArgs a{};
     a.q_codes = qc;
     a.q_scales = qs;
+    a.q_f32 = q_f32;
     a.w = w;
     a.idx_cache = idx;
     a.n_blocks = n_blocks;
@@ -828,8 +894,8 @@ namespace {
     do {                                                                                    \
         const int st_ = check_cfg(c);                                                       \
         if (st_) return st_;                                                                \
-        if (!q_codes || !q_scales || !w || !idx_cache || n_blocks <= 0 || !block_table ||   \
-            maxb <= 0 || !ctx_len || batch < 0)                                             \
+        if (((!q_codes || !q_scales) && !q_f32) || !w || !idx_cache || n_blocks <= 0 ||     \
+            !block_table || maxb <= 0 || !ctx_len || batch < 0)                             \
             return CSA2_ERR_INVALID;                                                        \
         if (batch > kMaxBatch) return CSA2_ERR_UNSUPPORTED;                                 \
     } while (0)
@@ -865,6 +931,7 @@ extern "C" int csa2_index_scores(const csa2_config *c, const uint8_t *q_codes,
                                  const int32_t *block_table, int32_t maxb,
                                  const int32_t *ctx_len, int32_t batch, float *scores,
                                  float *block_scores, hipStream_t stream) {
+    const float *q_f32 = nullptr;
     CSA2_CHECK_INDEX_ARGS();
     if (batch == 0 || (!scores && !block_scores)) return CSA2_OK;
     KernSet ks;
@@ -883,6 +950,7 @@ extern "C" int csa2_index_full_scan(const csa2_config *c, const uint8_t *q_codes
                                     const int32_t *block_table, int32_t maxb,
                                     const int32_t *ctx_len, int32_t batch, void *ws,
                                     size_t ws_bytes, hipStream_t stream) {
+    const float *q_f32 = nullptr;
     CSA2_CHECK_INDEX_ARGS();
     if (!ws) return CSA2_ERR_INVALID;
     const WsIdx L = ws_idx(batch, maxb, c->pool_blocks);
@@ -909,6 +977,7 @@ extern "C" int csa2_index_full_finish(const csa2_config *c, const uint8_t *q_cod
                                       int32_t *pool_blocks, int32_t *pool_len, int32_t *topk,
                                       int32_t *topk_len, void *ws, size_t ws_bytes,
                                       hipStream_t stream) {
+    const float *q_f32 = nullptr;
     CSA2_CHECK_INDEX_ARGS();
     if (!pool_blocks || !pool_len || !topk || !topk_len || !ws) return CSA2_ERR_INVALID;
     if (ws_bytes < ws_idx(batch, maxb, c->pool_blocks).total) return CSA2_ERR_WORKSPACE;
@@ -927,6 +996,7 @@ extern "C" int csa2_index_full(const csa2_config *c, const uint8_t *q_codes,
                                const int32_t *ctx_len, int32_t batch, int32_t *pool_blocks,
                                int32_t *pool_len, int32_t *topk, int32_t *topk_len, void *ws,
                                size_t ws_bytes, hipStream_t stream) {
+    const float *q_f32 = nullptr;
     CSA2_CHECK_INDEX_ARGS();
     if (!pool_blocks || !pool_len || !topk || !topk_len || !ws) return CSA2_ERR_INVALID;
     int st = csa2_index_full_scan(c, q_codes, q_scales, w, idx_cache, n_blocks, block_table,
@@ -937,6 +1007,85 @@ extern "C" int csa2_index_full(const csa2_config *c, const uint8_t *q_codes,
                                   ws, ws_bytes, stream);
 }
 
+namespace csa2 {
+
+int index_full_append(const csa2_config *c, const float *latent, const float *idx_k,
+                      const uint8_t *q_codes, const uint8_t *q_scales, const float *q_f32,
+                      const float *w, uint8_t *kv_cache, uint8_t *idx_cache, int64_t n_blocks,
+                      const int32_t *block_table, int32_t maxb, const int32_t *ctx_len,
+                      int32_t batch, int32_t *pool_blocks, int32_t *pool_len, int32_t *topk,
+                      int32_t *topk_len, void *ws, size_t ws_bytes, hipStream_t stream) {
+    CSA2_CHECK_INDEX_ARGS();
+    if (!idx_k || (latent && !kv_cache) || !pool_blocks || !pool_len || !topk || !topk_len || !ws)
+        return CSA2_ERR_INVALID;
+    if (latent && c->kv_dim != kAppD) return CSA2_ERR_UNSUPPORTED;
+    const WsIdx L = ws_idx(batch, maxb, c->pool_blocks);
+    if (ws_bytes < L.total) return CSA2_ERR_WORKSPACE;
+    if (batch == 0) return CSA2_OK;
+    const bool fused = fuse_append(c->n_idx_heads, c->idx_dim / 32);
+    if (!fused) {
+        const int st = launch_append_global(c, latent, idx_k, block_table, maxb, n_blocks,
+                                            ctx_len, -1, batch, 1, kv_cache, idx_cache, stream);
+        if (st) return st;
+    }
+    KernSet ks;
+    pick(c->n_idx_heads, c->idx_dim, &ks);
+    ScanArgs a = scan_args(c, q_codes, q_scales, w, idx_cache, n_blocks, block_table, maxb,
+                           ctx_len, batch, q_f32);
+    uint8_t *base = (uint8_t *)ws;
+    a.pscore = (float *)(base + L.pscore);
+    a.bscore = (float *)(base + L.bscore);
+    a.bstride = ngmax_of(maxb) * kItemBlocks;
+    a.gmax = (float *)(base + L.gmax);
+    if (fused) {
+        a.new_key = idx_k;
+        a.new_lat = latent;
+        a.idx_w = idx_cache;
+        a.kv_w = kv_cache;
+    }
+    ks.scan(dim3(scan_grid((int64_t)batch * ngmax_of(maxb))), prefix_bytes(batch), stream, a);
+    const int st = launched();
+    if (st) return st;
+    SelectArgs sa = select_args(c, ctx_len, maxb, batch, ws);
+    sa.pool_blocks = pool_blocks;
+    sa.pool_len = pool_len;
+    sa.topk = topk;
+    sa.topk_len = topk_len;
+    return launch_select(sa, false, stream);
+}
+
+int index_reindex(const csa2_config *c, const uint8_t *q_codes, const uint8_t *q_scales,
+                  const float *q_f32, const float *w, const uint8_t *idx_cache, int64_t n_blocks,
+                  const int32_t *block_table, int32_t maxb, const int32_t *ctx_len, int32_t batch,
+                  const int32_t *pool_blocks, const int32_t *pool_len, int32_t *topk,
+                  int32_t *topk_len, void *ws, size_t ws_bytes, hipStream_t stream) {
+    CSA2_CHECK_INDEX_ARGS();
+    if (!pool_blocks || !pool_len || !topk || !topk_len || !ws) return CSA2_ERR_INVALID;
+    const WsIdx L = ws_idx(batch, maxb, c->pool_blocks);
+    if (ws_bytes < L.total) return CSA2_ERR_WORKSPACE;
+    if (batch == 0) return CSA2_OK;
+    KernSet ks;
+    pick(c->n_idx_heads, c->idx_dim, &ks);
+    ScanArgs a = scan_args(c, q_codes, q_scales, w, idx_cache, n_blocks, block_table, maxb,
+                           ctx_len, batch, q_f32);
+    a.pool = pool_blocks;
+    a.pool_len = pool_len;
+    a.poolsc = (float *)((uint8_t *)ws + L.poolsc);
+    a.poolbmax = (float *)((uint8_t *)ws + L.poolbmax);
+    const int64_t items = (int64_t)batch * ((c->pool_blocks + kItemBlocks - 1) / kItemBlocks);
+    ks.rescore(dim3(scan_grid(items)), prefix_bytes(batch), stream, a);
+    const int st = launched();
+    if (st) return st;
+    SelectArgs s = select_args(c, ctx_len, maxb, batch, ws);
+    s.pool_blocks = const_cast<int32_t *>(pool_blocks);
+    s.pool_len = const_cast<int32_t *>(pool_len);
+    s.topk = topk;
+    s.topk_len = topk_len;
+    return launch_select(s, true, stream);
+}
+
+}  // namespace csa2
+
 extern "C" int csa2_index_full_append(const csa2_config *c, const float *latent,
                                       const float *idx_k, const uint8_t *q_codes,
                                       const uint8_t *q_scales, const float *w, uint8_t *kv_cache,
@@ -945,40 +1094,10 @@ extern "C" int csa2_index_full_append(const csa2_config *c, const float *latent,
                                       const int32_t *ctx_len, int32_t batch, int32_t *pool_blocks,
                                       int32_t *pool_len, int32_t *topk, int32_t *topk_len,
                                       void *ws, size_t ws_bytes, hipStream_t stream) {
-    CSA2_CHECK_INDEX_ARGS();
-    if (!idx_k || (latent && !kv_cache) || !pool_blocks || !pool_len || !topk || !topk_len || !ws)
-        return CSA2_ERR_INVALID;
-    if (latent && c->kv_dim != kAppD) return CSA2_ERR_UNSUPPORTED;
-    const WsIdx L = ws_idx(batch, maxb, c->pool_blocks);
-    if (ws_bytes < L.total) return CSA2_ERR_WORKSPACE;
-    if (batch == 0) return CSA2_OK;
-    if (!fuse_append(c->n_idx_heads, c->idx_dim / 32)) {
-        const int st = launch_append_global(c, latent, idx_k, block_table, maxb, n_blocks,
-                                            ctx_len, -1, batch, 1, kv_cache, idx_cache, stream);
-        if (st) return st;
-        return csa2_index_full(c, q_codes, q_scales, w, idx_cache, n_blocks, block_table, maxb,
-                               ctx_len, batch, pool_blocks, pool_len, topk, topk_len, ws,
-                               ws_bytes, stream);
-    }
-    KernSet ks;
-    pick(c->n_idx_heads, c->idx_dim, &ks);
-    ScanArgs a = scan_args(c, q_codes, q_scales, w, idx_cache, n_blocks, block_table, maxb,
-                           ctx_len, batch);
-    uint8_t *base = (uint8_t *)ws;
-    a.pscore = (float *)(base + L.pscore);
-    a.bscore = (float *)(base + L.bscore);
-    a.bstride = ngmax_of(maxb) * kItemBlocks;
-    a.gmax = (float *)(base + L.gmax);
-    a.new_key = idx_k;
-    a.new_lat = latent;
-    a.idx_w = idx_cache;
-    a.kv_w = kv_cache;
-    ks.scan(dim3(scan_grid((int64_t)batch * ngmax_of(maxb))), prefix_bytes(batch), stream, a);
-    const int st = launched();
-    if (st) return st;
-    return csa2_index_full_finish(c, q_codes, q_scales, w, idx_cache, n_blocks, block_table,
-                                  maxb, ctx_len, batch, pool_blocks, pool_len, topk, topk_len,
-                                  ws, ws_bytes, stream);
+    if (!q_codes || !q_scales) return CSA2_ERR_INVALID;
+    return index_full_append(c, latent, idx_k, q_codes, q_scales, nullptr, w, kv_cache, idx_cache,
+                             n_blocks, block_table, maxb, ctx_len, batch, pool_blocks, pool_len,
+                             topk, topk_len, ws, ws_bytes, stream);
 }
 
 extern "C" int csa2_index_reindex(const csa2_config *c, const uint8_t *q_codes,
@@ -989,25 +1108,8 @@ extern "C" int csa2_index_reindex(const csa2_config *c, const uint8_t *q_codes,
                                   const int32_t *pool_blocks, const int32_t *pool_len,
                                   int32_t *topk, int32_t *topk_len, void *ws, size_t ws_bytes,
                                   hipStream_t stream) {
-    CSA2_CHECK_INDEX_ARGS();
-    if (!pool_blocks || !pool_len || !topk || !topk_len || !ws) return CSA2_ERR_INVALID;
-    const WsIdx L = ws_idx(batch, maxb, c->pool_blocks);
-    if (ws_bytes < L.total) return CSA2_ERR_WORKSPACE;
-    if (batch == 0) return CSA2_OK;
-    KernSet ks;
-    pick(c->n_idx_heads, c->idx_dim, &ks);
-    ScanArgs a = scan_args(c, q_codes, q_scales, w, idx_cache, n_blocks, block_table, maxb,
-                           ctx_len, batch);
-    a.pool = pool_blocks;
-    a.pool_len = pool_len;
-    a.poolsc = (float *)((uint8_t *)ws + L.poolsc);
-    a.poolbmax = (float *)((uint8_t *)ws + L.poolbmax);
-    const int64_t items = (int64_t)batch * ((c->pool_blocks + kItemBlocks - 1) / kItemBlocks);
-    ks.rescore(dim3(scan_grid(items)), prefix_bytes(batch), stream, a);
-    SelectArgs s = select_args(c, ctx_len, maxb, batch, ws);
-    s.pool_blocks = const_cast<int32_t *>(pool_blocks);
-    s.pool_len = const_cast<int32_t *>(pool_len);
-    s.topk = topk;
-    s.topk_len = topk_len;
-    return launch_select(s, true, stream);
+    if (!q_codes || !q_scales) return CSA2_ERR_INVALID;
+    return index_reindex(c, q_codes, q_scales, nullptr, w, idx_cache, n_blocks, block_table, maxb,
+                         ctx_len, batch, pool_blocks, pool_len, topk, topk_len, ws, ws_bytes,
+                         stream);
 }

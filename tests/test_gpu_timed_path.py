@@ -210,3 +210,74 @@ def test_scan_with_64bit_offsets(H, d):
     assert np.array_equal(_np(g.kv), o.kv), _first_diff(_np(g.kv), o.kv)
     assert np.array_equal(_np(pool), po) and np.array_equal(_np(tk), to)
     assert np.array_equal(_np(tl), tlo) and np.array_equal(_np(pl), plo)
+
+
+# ------------------------------------------------------------------ fused layer calls
+
+@pytest.mark.parametrize("H,d,ctx,with_lat", [
+    (4, 64, [5000], True),                      # one sequence (interleaved scan items)
+    (4, 64, [700, 5000, 64, 1, 9], True),       # ragged batch
+    (8, 128, [3000, 517, 9], True),             # the global append runs before the scan
+    (1, 32, [300, 17], False),                  # one head, no main-KV append
+])
+def test_layer_calls_equal_the_separate_calls(H, d, ctx, with_lat):
+    """csa2_decode_full_layer / _reindex_layer / _reuse_layer == the separate calls they
+    stand for (query quantise, fused global append + Full index or Reindex, fused window
+    append + attention at ctx_len - 1), bit for bit: cache and ring bytes, pool, top-k,
+    attention output and log-sum-exp.  The token's rows are fresh values, unlike the cache's."""
+    wl = si.small("lay", 340 + H + d + len(ctx), ctx, H_I=H, d_I=d, K_blk=32, k=96, W=64,
+                  layers="FRU")
+    table, nblk = make_table(wl.ctx, seed=wl.seed)
+    g = GpuState(wl, table, nblk)
+    B = wl.B
+    i32 = dict(dtype=torch.int32, device="cuda")
+    qf = [dev(si.layer_idx_q(wl, li).reshape(B, H * d)) for li in range(2)]
+    w = [dev(si.layer_idx_w(wl, li)) for li in range(2)]
+    qa = [g.attn_q(li) for li in range(3)]
+    swa_row = [dev(si.normal(341, 10 + li, (B, wl.D))) for li in range(3)]
+    tok_key = dev(si.normal(341, 20, (B, H * d)))
+    tok_lat = dev(si.normal(341, 21, (B, wl.D))) if with_lat else None
+    rings0 = [g.layer_swa(li) for li in range(3)]
+    res = []
+    for fused in (False, True):
+        kv, idx = g.kv.clone(), g.idx.clone()
+        rings = [r.clone() for r in rings0]
+        pool = torch.full((B, wl.K_blk), -7, **i32)
+        pl = torch.zeros(B, **i32)
+        tk = [torch.full((B, wl.k), -7, **i32) for _ in range(2)]
+        tl = [torch.zeros(B, **i32) for _ in range(2)]
+        outs = [torch.full((B, wl.H_q, wl.D), float("nan"), device="cuda") for _ in range(3)]
+        lses = [torch.full((B, wl.H_q), float("nan"), device="cuda") for _ in range(3)]
+        wsa = torch.zeros_like(g.ws_attn)
+        if fused:
+            k.csa2_decode_full_layer(g.cfg, qf[0], w[0], tok_lat, tok_key, swa_row[0], qa[0], kv,
+                                     idx, g.n_blocks, g.table, rings[0], g.C, g.ctx, pool, pl,
+                                     tk[0], tl[0], outs[0], lses[0], g.ws, wsa)
+            k.csa2_decode_reindex_layer(g.cfg, qf[1], w[1], swa_row[1], qa[1], kv, idx,
+                                        g.n_blocks, g.table, rings[1], g.C, g.ctx, pool, pl,
+                                        tk[1], tl[1], outs[1], lses[1], g.ws, wsa)
+            k.csa2_decode_reuse_layer(g.cfg, swa_row[2], qa[2], kv, g.n_blocks, g.table, rings[2],
+                                      g.C, g.ctx, tk[1], tl[1], outs[2], lses[2], wsa)
+        else:
+            pos = g.ctx - 1
+            for li in range(3):
+                if li < 2:
+                    qc = torch.empty((B, H * d // 2), dtype=torch.uint8, device="cuda")
+                    qs = torch.empty((B, H * d // 32), dtype=torch.uint8, device="cuda")
+                    k.csa2_quantize_mxfp4(qf[li], qc, qs)
+                if li == 0:
+                    k.csa2_index_full_append(g.cfg, tok_lat, tok_key, qc, qs, w[0],
+                                             kv if with_lat else None, idx, g.n_blocks, g.table,
+                                             g.ctx, pool, pl, tk[0], tl[0], g.ws)
+                elif li == 1:
+                    k.csa2_index_reindex(g.cfg, qc, qs, w[1], idx, g.n_blocks, g.table, g.ctx,
+                                         pool, pl, tk[1], tl[1], g.ws)
+                t = min(li, 1)
+                k.csa2_sparse_attn_append(g.cfg, swa_row[li], pos, qa[li], kv, g.n_blocks,
+                                          g.table, rings[li], g.C, g.ctx, tk[t], tl[t], outs[li],
+                                          lses[li], wsa)
+        torch.cuda.synchronize()
+        res.append([_np(x) for x in [kv, idx, *rings, pool, pl, *tk, *tl, *outs, *lses]])
+    for i, (x, y) in enumerate(zip(*res)):
+        assert np.array_equal(x.view(np.uint8), y.view(np.uint8)), (i, _first_diff(x, y))
+    assert not np.array_equal(res[1][1], _np(g.idx)), "the layer call appended no key"
