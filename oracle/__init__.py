@@ -36,7 +36,8 @@ def build(force: bool = False) -> str:
 class Cfg(C.Structure):
     _fields_ = [("n_idx_heads", C.c_int32), ("idx_dim", C.c_int32), ("kv_dim", C.c_int32),
                 ("n_q_heads", C.c_int32), ("swa_window", C.c_int32),
-                ("pool_blocks", C.c_int32), ("topk", C.c_int32), ("sm_scale", C.c_float)]
+                ("pool_blocks", C.c_int32), ("topk", C.c_int32), ("sm_scale", C.c_float),
+                ("shared_key", C.c_int32)]
 
 
 _lib = None
@@ -64,18 +65,24 @@ def _check(rc, what):
         raise ValueError(f"oracle {what}: invalid arguments (status {rc})")
 
 
-def cfg(H_I, d_I, D, H_q, W, K_blk, k, sm_scale) -> Cfg:
-    return Cfg(H_I, d_I, D, H_q, W, K_blk, k, sm_scale)
+def cfg(H_I, d_I, D, H_q, W, K_blk, k, sm_scale, shared_key=False) -> Cfg:
+    return Cfg(H_I, d_I, D, H_q, W, K_blk, k, sm_scale, int(shared_key))
 
 
 def cfg_of(wl) -> Cfg:
-    return Cfg(wl.H_I, wl.d_I, wl.D, wl.H_q, wl.W, wl.K_blk, wl.k, wl.sm_scale)
+    return Cfg(wl.H_I, wl.d_I, wl.D, wl.H_q, wl.W, wl.K_blk, wl.k, wl.sm_scale,
+               int(getattr(wl, "shared_key", False)))
 
 
 # ------------------------------------------------------------------------- layout sizes
 
+def key_heads(c: Cfg) -> int:
+    """Indexer keys stored per position: one per head, or one shared by all heads."""
+    return 1 if c.shared_key else c.n_idx_heads
+
+
 def idx_block_bytes(c: Cfg) -> int:
-    return BLK * c.n_idx_heads * (c.idx_dim // 2 + c.idx_dim // 32)
+    return BLK * key_heads(c) * (c.idx_dim // 2 + c.idx_dim // 32)
 
 
 def kv_row_bytes(c: Cfg) -> int:
@@ -143,7 +150,7 @@ def dequant_mxfp8(codes: np.ndarray, scales: np.ndarray) -> np.ndarray:
 # ------------------------------------------------------------------------- caches
 
 def append_global(c: Cfg, latent, idx_k, table, pos0, kv_cache, idx_cache):
-    """latent [B, n, D] fp32 (or None), idx_k [B, n, H_I, d_I] fp32 (or None)."""
+    """latent [B, n, D] fp32 (or None), idx_k [B, n, KH, d_I] fp32 (or None), KH = key_heads(c)."""
     table = np.ascontiguousarray(table, np.int32)
     pos0 = np.ascontiguousarray(pos0, np.int32)
     B, maxb = table.shape

@@ -32,6 +32,9 @@
  *       fixed order: per 32-group an exact integer dot of doubled codes N_j, then
  *       t_j = N_j * 2^(E_j - 2), D_h = ((t_0 + t_1) + t_2) + ..., r_h = max(D_h, +0),
  *       s = fma(w_{H-1}, r_{H-1}, ... fma(w_0, r_0, +0)).
+ *       Shared-key reading (a "next" variant, config field shared_key = 1): each position
+ *       stores ONE d_I key, and s(p) = sum_h w_h * ReLU(q_h . k_p) with the same fixed
+ *       order (query head h's group j meets the key's group j).
  *   R6  block score = max of s over the visible positions of an 8-position block.
  *   R7  selection order (score desc, index asc); outputs ascending, -1 padded.
  *   R9  attention: K = V = dequantised latent (512), joint softmax over the selected
@@ -57,6 +60,8 @@ typedef struct {
     int32_t pool_blocks; /* K_blk */
     int32_t topk;        /* k */
     float sm_scale;
+    int32_t shared_key;  /* 0: one key per head per position; 1: one key per position, scored
+                            by all H_I query heads (the shared-key indexer reading) */
 } o_cfg;
 
 enum { O_OK = 0, O_BAD = -1, O_PRECOND = -5 };
@@ -210,8 +215,11 @@ int csa2o_dequant_mxfp8(const uint8_t *codes, const uint8_t *scales, int64_t n_r
  * Window ring: sequence b, slot t at (b*C + t)*(D + D/32): D FP8 codes, D/32 scales;
  *   position p lives in slot p % C.                                                 */
 
+/* Key heads stored per position: H_I, or 1 when every query head scores the same key. */
+static int key_heads(const o_cfg *c) { return c->shared_key ? 1 : c->n_idx_heads; }
+
 static size_t idx_block_bytes(const o_cfg *c) {
-    return (size_t)BLK * c->n_idx_heads * (c->idx_dim / 2 + c->idx_dim / 32);
+    return (size_t)BLK * key_heads(c) * (c->idx_dim / 2 + c->idx_dim / 32);
 }
 static size_t kv_row_bytes(const o_cfg *c) { return (size_t)c->kv_dim / 2 + c->kv_dim / 32; }
 static size_t swa_row_bytes(const o_cfg *c) { return (size_t)c->kv_dim + c->kv_dim / 32; }
@@ -219,13 +227,14 @@ static size_t swa_row_bytes(const o_cfg *c) { return (size_t)c->kv_dim + c->kv_d
 static int cfg_ok(const o_cfg *c) {
     return c && c->n_idx_heads > 0 && c->idx_dim > 0 && c->idx_dim % 32 == 0 &&
            c->kv_dim > 0 && c->kv_dim % 32 == 0 && c->n_q_heads > 0 && c->swa_window >= 0 &&
-           c->pool_blocks > 0 && c->topk > 0;
+           c->pool_blocks > 0 && c->topk > 0 && (c->shared_key == 0 || c->shared_key == 1);
 }
 
-/* Write position p's indexer key (one MXFP4 row of H*d_I, head-major) into its block. */
+/* Write position p's indexer key (one MXFP4 row of KH*d_I, head-major, KH = key heads)
+ * into its block. */
 static void put_idx_key(const o_cfg *c, uint8_t *blk, int s, const uint8_t *codes,
                         const uint8_t *scales) {
-    int H = c->n_idx_heads, G = c->idx_dim / 32;
+    int H = key_heads(c), G = c->idx_dim / 32;
     size_t codes_bytes = (size_t)BLK * H * c->idx_dim / 2;
     for (int h = 0; h < H; h++)
         for (int g = 0; g < G; g++) {
@@ -237,7 +246,7 @@ static void put_idx_key(const o_cfg *c, uint8_t *blk, int s, const uint8_t *code
 /* Read position p's key back as a head-major MXFP4 row. */
 static void get_idx_key(const o_cfg *c, const uint8_t *blk, int s, uint8_t *codes,
                         uint8_t *scales) {
-    int H = c->n_idx_heads, G = c->idx_dim / 32;
+    int H = key_heads(c), G = c->idx_dim / 32;
     size_t codes_bytes = (size_t)BLK * H * c->idx_dim / 2;
     for (int h = 0; h < H; h++)
         for (int g = 0; g < G; g++) {
@@ -252,7 +261,7 @@ int csa2o_append_global(const o_cfg *c, const float *latent, const float *idx_k,
                         int32_t B, int32_t n_new, uint8_t *kv_cache, uint8_t *idx_cache,
                         int64_t n_blocks) {
     if (!cfg_ok(c) || B < 0 || n_new < 0) return O_BAD;
-    int D = c->kv_dim, HI = c->n_idx_heads * c->idx_dim;
+    int D = c->kv_dim, HI = key_heads(c) * c->idx_dim;
     for (int b = 0; b < B; b++)
         for (int t = 0; t < n_new; t++) {
             int64_t p = (int64_t)pos0[b] + t;
@@ -302,8 +311,10 @@ static int doubled(int code) { return (int)(2.0 * csa2o_fp4_value(code)); }
 
 static int nib(const uint8_t *codes, int i) { return (codes[i / 2] >> ((i & 1) * 4)) & 15; }
 
-/* Score of one key (head-major MXFP4 row of H*d_I) against the query; returns O_PRECOND
- * through *bad when a group exponent leaves the range where t_j is an exact fp32. */
+/* Score of one key against the query (head-major MXFP4 row of H*d_I); the key is a
+ * head-major row of H*d_I, or of d_I when the key is shared by the heads (query head h then
+ * meets the same key groups g = 0..G-1).  Returns O_PRECOND through *bad when a group
+ * exponent leaves the range where t_j is an exact fp32. */
 static float score_key(const o_cfg *c, const uint8_t *qc, const uint8_t *qs, const float *w,
                        const uint8_t *kc, const uint8_t *ks, int *bad) {
     int H = c->n_idx_heads, G = c->idx_dim / 32;
@@ -311,10 +322,12 @@ static float score_key(const o_cfg *c, const uint8_t *qc, const uint8_t *qs, con
     for (int h = 0; h < H; h++) {
         float Dh = 0.0f;
         for (int g = 0; g < G; g++) {
-            int base = (h * G + g) * 32;
+            int base = (h * G + g) * 32;                      /* query group */
+            int kg = c->shared_key ? g : h * G + g;           /* key group */
             long N = 0;
-            for (int i = 0; i < 32; i++) N += (long)doubled(nib(qc, base + i)) * doubled(nib(kc, base + i));
-            int E = ((int)qs[h * G + g] - 127) + ((int)ks[h * G + g] - 127);
+            for (int i = 0; i < 32; i++)
+                N += (long)doubled(nib(qc, base + i)) * doubled(nib(kc, kg * 32 + i));
+            int E = ((int)qs[h * G + g] - 127) + ((int)ks[kg] - 127);
             if (N != 0 && (E - 2 > 100 || E - 2 < -100)) *bad = 1; /* t_j exact */
             float t = ldexpf((float)N, E - 2);
             Dh = Dh + t;

@@ -22,6 +22,9 @@ model tensors, so every tensor is synthetic):
               indexer 8 x 128, pool 2048, top-512, 64 query heads.
 * spec_1m   : speculative verification, 1 + 5 draft tokens at the end of a
               1,048,576-token context (6 causal queries); dims as long_1m.
+* b8_64k_shared, long_1m_shared : the shared-key indexer variant (one 128-dim key per
+              position scored by 8 query heads) at the batch-8 64K and one-sequence 1M
+              sizes.
 """
 from __future__ import annotations
 
@@ -117,7 +120,12 @@ class Workload:
     layers: str = "FRU"  # layer modes of one decode group
     planted: int = 0     # planted high-similarity blocks (long_1m)
     n_q: int = 0         # prefill queries (prefill only)
+    shared_key: bool = False  # one d_I indexer key per position, scored by all H_I heads
     extra: dict = field(default_factory=dict)
+
+    @property
+    def key_heads(self) -> int:
+        return 1 if self.shared_key else self.H_I
 
     @property
     def sm_scale(self) -> float:
@@ -142,23 +150,30 @@ def workload(name: str) -> Workload:
         return Workload("prefill", 5, 1, [262144], 8, 128, 2048, 512, H_q=64, n_q=4096)
     if name == "spec_1m":
         return Workload("spec_1m", 6, 1, [1 << 20], 4, 64, 2048, 512, H_q=16, n_q=6)
+    if name == "b8_64k_shared":  # the shared-key indexer at the batch-8 decode dims
+        return Workload("b8_64k_shared", 7, 8, [65536] * 8, 8, 128, 2048, 512, H_q=64,
+                        layers="FRURU", shared_key=True)
+    if name == "long_1m_shared":  # the shared-key indexer, 8 heads x 128, one 1M sequence
+        return Workload("long_1m_shared", 8, 1, [1 << 20], 8, 128, 2048, 512, H_q=16,
+                        shared_key=True)
     raise KeyError(name)
 
 
 def small(name: str, seed: int, ctx, H_I=4, d_I=64, K_blk=16, k=32, H_q=16, D=512, W=128,
-          layers="FRU", planted=0) -> Workload:
+          layers="FRU", planted=0, shared_key=False) -> Workload:
     """A reduced workload for tests that the oracle finishes in seconds."""
     ctx = list(ctx)
     return Workload(name, seed, len(ctx), ctx, H_I, d_I, K_blk, k, D=D, H_q=H_q, W=W,
-                    layers=layers, planted=planted)
+                    layers=layers, planted=planted, shared_key=shared_key)
 
 
 # ----------------------------------------------------------------------------- tensors
 
 def idx_keys(wl: Workload, b: int, L: int | None = None) -> np.ndarray:
-    """fp32 indexer keys of sequence b, shape [L, H_I, d_I] (before quantisation)."""
+    """fp32 indexer keys of sequence b, shape [L, KH, d_I] (before quantisation), KH = H_I
+    keys per position, or 1 with a shared key."""
     L = wl.ctx[b] if L is None else L
-    x = normal(wl.seed, T_IDX_K + 1000 * b, (L, wl.H_I, wl.d_I))
+    x = normal(wl.seed, T_IDX_K + 1000 * b, (L, wl.key_heads, wl.d_I))
     if wl.planted:
         plant_keys(wl, b, x)
     return x
