@@ -187,9 +187,10 @@ class Bench:
 def kernels_per_mode(wl):
     """Kernel launches of one layer of each mode in the step (the fused layer calls): Full =
     scan (with the query quantise and global append) + selection + attention, plus a global
-    append of its own for 8 x 128-style layouts (four 32-groups per head, two or more heads);
-    Reindex = rescoring scan + selection + attention; Reuse = attention."""
-    own_append = wl.d_I // 32 > 2 and wl.H_I > 1
+    append of its own for 8 x 128-style layouts (four 32-groups per head, two or more heads)
+    and for the shared-key variant; Reindex = rescoring scan + selection + attention; Reuse =
+    attention."""
+    own_append = (wl.d_I // 32 > 2 and wl.H_I > 1) or wl.shared_key
     return {"F": 4 if own_append else 3, "R": 3, "U": 1}
 
 
@@ -782,12 +783,15 @@ def main():
         "data": "synthetic",
         "config": {"workload": wl.name, "batch": wl.B, "context": wl.max_ctx,
                    "context_min": int(min(wl.ctx)), "context_total": int(sum(wl.ctx)),
-                   "indexer": f"{wl.H_I}x{wl.d_I} fp4", "pool_blocks": wl.K_blk, "topk": wl.k,
+                   "indexer": f"{wl.H_I}x{wl.d_I} fp4" + (" (one shared key per position)"
+                                                            if wl.shared_key else ""),
+                   "pool_blocks": wl.K_blk, "topk": wl.k,
                    "q_heads": wl.H_q, "window": wl.W, "layers": wl.layers,
                    "replicas": R, "graph": not a.eager},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
-                     "traffic": traffic, "kernel": SCAN_KERNEL,
+                     "traffic": traffic,
+                     "kernel": SCAN_KERNEL + ("_shared" if wl.shared_key else ""),
                      "kernel_us": round(scan_ms * 1e3, 3), "algorithmic_bytes": ab["scan"]},
         "group": {"algorithmic_bytes": ab["total"],
                   "kernels_per_mode": kernels_per_mode(wl),

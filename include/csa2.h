@@ -77,22 +77,26 @@ typedef struct csa2_config {
     int32_t pool_blocks; /* K_blk: pool capacity in blocks (1 .. 2048) [KV]          */
     int32_t topk;        /* k: final selection (1 .. 8*K_blk) [KV]                   */
     float sm_scale;      /* softmax scale applied to q.k                             */
+    int32_t shared_key;  /* 0: one indexer key per head per position (H_I keys);
+                            1: one d_I key per position, scored by all H_I query heads
+                            (the shared-key indexer variant; the index calls take the
+                            same query, the caches hold KH = 1 key per position)     */
 } csa2_config;
 
 /* Byte sizes of the cache layouts (all multiples of 16).
  *
  * Global caches are paged: physical block `phys` of 8 positions holds
- *   idx_cache + phys*idx_block_bytes : indexer keys of the 8 positions.  With H = H_I and
- *       G = d_I/32, the 16 bytes of FP4 codes of group g of head h of the position in slot s
- *       sit at 16*((g*8 + s)*H + h); the E8M0 scale of that group sits at
- *       8*H*d_I/2 + (s*H + h)*G + g.
+ *   idx_cache + phys*idx_block_bytes : indexer keys of the 8 positions.  With H the key heads
+ *       (H_I, or 1 with shared_key) and G = d_I/32, the 16 bytes of FP4 codes of group g of
+ *       head h of the position in slot s sit at 16*((g*8 + s)*H + h); the E8M0 scale of that
+ *       group sits at 8*H*d_I/2 + (s*H + h)*G + g.
  *   kv_cache + phys*kv_block_bytes : main latent rows, slot s at s*kv_row_bytes:
  *       D/2 bytes of FP4 codes (element 2i in the low nibble) then D/32 E8M0 scales.
  * block_table[b*maxb + j] is the physical block of positions 8j..8j+7 of sequence b.
  * Window ring (one per layer): sequence b, slot t at (b*C + t)*swa_row_bytes: D E4M3FN
  *   codes then D/32 E8M0 scales; position p lives in slot p % C, C >= W.                */
 typedef struct csa2_layout_info {
-    size_t idx_block_bytes; /* 8*H_I*(d_I/2 + d_I/32) */
+    size_t idx_block_bytes; /* 8*KH*(d_I/2 + d_I/32), KH = 1 with shared_key else H_I */
     size_t kv_row_bytes;    /* D/2 + D/32             */
     size_t kv_block_bytes;  /* 8*kv_row_bytes         */
     size_t swa_row_bytes;   /* D + D/32               */
@@ -126,7 +130,8 @@ int csa2_dequant_mxfp8(const uint8_t *codes, const uint8_t *scales, int64_t n_ro
 
 /* Full-layer append [KV]: for each sequence b and t < n_new, quantise position
  * p = pos0[b] + t -- main latent row latent[(b*n_new + t)*D ..] (MXFP4) and indexer key
- * idx_k[(b*n_new + t)*H_I*d_I ..] (head-major, MXFP4 per head group) -- into the block
+ * idx_k[(b*n_new + t)*KH*d_I ..] (head-major, MXFP4 per head group; KH = 1 with shared_key,
+ * else H_I) -- into the block
  * table's block p/8, slot p%8.  Either latent or idx_k may be NULL to skip that cache.
  * pos0 [batch] is a device array; positions whose block is outside the table or whose
  * physical block is outside [0, n_blocks) are skipped. */

@@ -34,7 +34,8 @@ EXPORTS = [
 class csa2_config(C.Structure):
     _fields_ = [("n_idx_heads", C.c_int32), ("idx_dim", C.c_int32), ("kv_dim", C.c_int32),
                 ("n_q_heads", C.c_int32), ("swa_window", C.c_int32),
-                ("pool_blocks", C.c_int32), ("topk", C.c_int32), ("sm_scale", C.c_float)]
+                ("pool_blocks", C.c_int32), ("topk", C.c_int32), ("sm_scale", C.c_float),
+                ("shared_key", C.c_int32)]
 
 
 class csa2_layout_info(C.Structure):
@@ -139,8 +140,8 @@ def _call(name, *args):
         raise Csa2Error(name, st)
 
 
-def config(H_I, d_I, D, H_q, W, K_blk, k, sm_scale) -> csa2_config:
-    return csa2_config(H_I, d_I, D, H_q, W, K_blk, k, sm_scale)
+def config(H_I, d_I, D, H_q, W, K_blk, k, sm_scale, shared_key=False) -> csa2_config:
+    return csa2_config(H_I, d_I, D, H_q, W, K_blk, k, sm_scale, int(shared_key))
 
 
 def csa2_layout(cfg: csa2_config) -> csa2_layout_info:

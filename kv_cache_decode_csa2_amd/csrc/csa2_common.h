@@ -28,6 +28,9 @@ __device__ __forceinline__ uint32_t order_key(float f) {
 
 __device__ __forceinline__ int lane_id() { return threadIdx.x & (kWave - 1); }
 
+// Indexer keys stored per position: one per head, or one shared by all query heads.
+inline int key_heads(const csa2_config *c) { return c->shared_key ? 1 : c->n_idx_heads; }
+
 // Inclusive scan over the 64 lanes of a wave: DPP row shifts within rows of 16 lanes,
 // then row broadcasts of lanes 15 and 31 into the rows above.
 __device__ __forceinline__ uint32_t wave_incl_scan(uint32_t v) {

@@ -719,6 +719,291 @@ __global__ __launch_bounds__(kScanThreads, 2) void k_scan(ScanArgs a) {
     }
 }
 
+// ------------------------------------------------------------------ k_scan_shared
+//
+// The shared-key variant of the scan (one d_I key per position scored by all H query
+// heads).  Per 16-position tile one scaled-FP4 matrix instruction
+// (v_mfma_scale_f32_16x16x128_f8f6f4) forms every (head, position) dot: operand A holds the
+// query heads (rows), operand B the tile's keys (columns), each lane one 32-group of one row
+// or column with its E8M0 scale, so that lane (column c, g) reads the 16 code bytes of group
+// g of position c straight from the block layout.  The result lane (position c, g) holds
+// heads 4g .. 4g+3.  Exactness as in the prefill kernel: the matrix core adds the scaled
+// group products in an undisclosed order, which equals the defined fp32 group order whenever
+// every partial sum is representable -- |N_g| <= 4608 < 2^13, so an exponent span
+// max_g E_g - min_g E_g <= 9 keeps every partial inside 24 bits.  An item whose key span plus
+// the query's exceeds that takes one instruction per group (the other groups' key lanes
+// zeroed, each product exact) and adds the groups in order.  Epilogue: ReLU, the fma chain
+// over heads in head order, block and group maxima -- the outputs k_scan writes, read by the
+// same selection.  Pipeline per wave over its items: pool entries three items ahead
+// (rescoring), block-table entries two ahead, keys one ahead.
+
+typedef int v8i_t __attribute__((ext_vector_type(8)));
+constexpr int kSpanExactShared = 9;
+
+__device__ __forceinline__ f32x4_t mfma_fp4_sk(const uint4 &a, const uint4 &b, uint32_t sa,
+                                               uint32_t sb) {
+    const v8i_t av = {(int)a.x, (int)a.y, (int)a.z, (int)a.w, 0, 0, 0, 0};
+    const v8i_t bv = {(int)b.x, (int)b.y, (int)b.z, (int)b.w, 0, 0, 0, 0};
+    const f32x4_t z = {0.f, 0.f, 0.f, 0.f};
+    // formats 4/4: both operands FP4 E2M1; scales in byte 0 of sa and sb
+    return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(av, bv, z, 4, 4, 0, (int)sa, 0, (int)sb);
+}
+
+// max(x, +0) exactly as defined (every negative value and -0 give +0) in one integer max.
+__device__ __forceinline__ float relu_bits(float x) { return __int_as_float(max(__float_as_int(x), 0)); }
+
+// Largest minus smallest of the n low bytes of w.
+template <int N>
+__device__ __forceinline__ int byte_span(uint32_t w) {
+    int lo = 255, hi = 0;
+#pragma unroll
+    for (int i = 0; i < N; i++) {
+        const int v = (int)((w >> (8 * i)) & 255u);
+        lo = min(lo, v);
+        hi = max(hi, v);
+    }
+    return hi - lo;
+}
+
+__device__ __forceinline__ int wave_max_i(int v) {
+    return (int)wave_reduce_to63((uint32_t)v, [](uint32_t x, uint32_t y) { return x > y ? x : y; });
+}
+
+// The MXFP4 codes and E8M0 scale of query group q (head-major index, runtime per lane) from
+// the loaded fp32 query: every group encoded by 8 lanes (coop_fp4), then this lane's group
+// gathered with ds_bpermute.
+template <int H, int G>
+__device__ __forceinline__ void quant_query_group(const QueryF32<H, G> &F, int q, uint4 &codes,
+                                                  uint32_t &scale) {
+    constexpr int R = QueryF32<H, G>::R;
+    uint32_t kw[R], ksc[R];
+#pragma unroll
+    for (int r = 0; r < R; r++) coop_fp4(F.f[r], kw[r], ksc[r]);
+    const int rq = q / 8, src = 8 * (q % 8);
+    uint32_t wv[4], sv = 0u;
+#pragma unroll
+    for (int rr = 0; rr < R; rr++) {
+#pragma unroll
+        for (int i = 0; i < 4; i++) {
+            const uint32_t x = (uint32_t)__builtin_amdgcn_ds_bpermute(4 * (src + 2 * i), (int)kw[rr]);
+            wv[i] = rr == rq ? x : (rr == 0 ? x : wv[i]);
+        }
+        const uint32_t y = (uint32_t)__builtin_amdgcn_ds_bpermute(4 * src, (int)ksc[rr]);
+        sv = rr == rq ? y : (rr == 0 ? y : sv);
+    }
+    codes = make_uint4(wv[0], wv[1], wv[2], wv[3]);
+    scale = sv;
+}
+
+template <int H, int G, bool RESCORE>
+__global__ __launch_bounds__(kScanThreads, 2) void k_scan_shared(ScanArgs a) {
+    constexpr int CODES = kBlk * 16 * G;  // code bytes of a block (one key per position)
+    constexpr int BYTES = CODES + kBlk * G;
+    constexpr int T = 4;                  // 16-position tiles per item
+    extern __shared__ int32_t sh_dyn[];   // item prefix [B + 1], clamped lengths [B], lengths [B]
+    __shared__ __align__(16) uint32_t sh_scan[kScanWaves];
+    int32_t *sh_prefix = sh_dyn, *sh_len = sh_dyn + a.B + 1, *sh_raw = sh_dyn + 2 * a.B + 1;
+
+    const int lane = lane_id(), col = lane & 15, g = lane >> 4, slot = col & 7;
+    const int wave = __builtin_amdgcn_readfirstlane((int)threadIdx.x / kWave);
+    const int nwaves = (int)gridDim.x * kScanWaves;
+    const int gw = (int)blockIdx.x * kScanWaves + wave;
+    const bool inter = a.B == 1;
+    const int total = __builtin_amdgcn_readfirstlane(build_item_prefix<RESCORE>(a, sh_prefix, sh_len, sh_raw, sh_scan));
+    const int per = (total + nwaves - 1) / nwaves;
+    const int it_begin = inter ? gw : gw * per;
+    const int it_end = inter ? total : min(total, it_begin + per);
+    if (it_begin >= it_end) return;
+    const int n_items = inter ? (total - gw + nwaves - 1) / nwaves : it_end - it_begin;
+
+    // the uniform part of item k of this wave: sequence, first entry, existence
+    struct ItemU {
+        int b, e0;
+        bool ok;
+    };
+    auto item_u = [&](int k) -> ItemU {
+        ItemU u;
+        u.ok = k < n_items;
+        const int it = inter ? gw + (u.ok ? k : 0) * nwaves : it_begin + (u.ok ? k : 0);
+        u.b = a.B > 1 ? __builtin_amdgcn_readfirstlane(seq_of_item(sh_prefix, a.B, it)) : 0;
+        u.e0 = (it - __builtin_amdgcn_readfirstlane(sh_prefix[u.b])) * kItemBlocks;
+        return u;
+    };
+    auto nb_of = [&](int b) { return (__builtin_amdgcn_readfirstlane(sh_len[b]) + kBlk - 1) / kBlk; };
+    auto nent_of = [&](int b) {
+        return RESCORE ? max(0, min(sload(a.pool_len, b), a.K_blk)) : 0;
+    };
+    // per lane and tile t: the item's entry of this lane's position, 2t + col/8
+    auto entry = [&](const ItemU &u, int t) { return u.e0 + 2 * t + (col >> 3); };
+
+    // Pipeline rings (indices static: the loop is unrolled by 4 and items advance by 4):
+    // pool entries of items k+1 .. k+3 (rescoring), logical block (-1: none) and table entry
+    // of items k+1, k+2, key codes, scale words and visibility of items k, k+1.  Loads never
+    // branch: items past the wave's last read its first item's entries and are not stored.
+    int praw[4][T];
+    int lj[2][T], lph[2][T];
+    uint4 kc[2][T];
+    uint32_t ksw[2][T];  // the position's G scale bytes from byte 0
+    int vis[2][T];       // logical block of the key (-1: no key)
+
+    auto load_pool = [&](int k, int (&pr)[T]) {
+        if constexpr (RESCORE) {
+            const ItemU u = item_u(k);
+            const int32_t *pool_row = a.pool + (int64_t)u.b * a.K_blk;
+#pragma unroll
+            for (int t = 0; t < T; t++) pr[t] = pool_row[min(entry(u, t), a.K_blk - 1)];
+        }
+    };
+    auto load_table = [&](int k, const int (&pr)[T], int (&j_out)[T], int (&ph_out)[T]) {
+        const ItemU u = item_u(k);
+        const int nb = nb_of(u.b);
+        const int n_ent = nent_of(u.b);
+        const int32_t *table_row = a.table + (int64_t)u.b * a.maxb;
+#pragma unroll
+        for (int t = 0; t < T; t++) {
+            const int e = entry(u, t);
+            int j;
+            if constexpr (RESCORE) {
+                const int jr = pr[t];
+                j = u.ok && e < n_ent && jr >= 0 && jr < nb ? jr : -1;
+            } else {
+                j = u.ok && e < nb ? e : -1;
+            }
+            j_out[t] = j;
+            ph_out[t] = table_row[j >= 0 ? j : 0];
+        }
+    };
+    auto load_keys = [&](const int (&jj)[T], const int (&pp)[T], uint4 (&kc_out)[T],
+                         uint32_t (&ks_out)[T], int (&vis_out)[T]) {
+#pragma unroll
+        for (int t = 0; t < T; t++) {
+            const int j = jj[t], ph = pp[t];
+            const bool ok = j >= 0 && ph >= 0 && (int64_t)ph < a.n_blocks;
+            const uint8_t *blk = a.idx_cache + (int64_t)(ok ? ph : 0) * BYTES;
+            kc_out[t] = *reinterpret_cast<const uint4 *>(blk + 16 * (min(g, G - 1) * kBlk + slot));
+            const uint32_t sb = (uint32_t)(CODES + slot * G);
+            ks_out[t] = *reinterpret_cast<const uint32_t *>(blk + (sb & ~3u)) >> (8 * (sb & 3u));
+            vis_out[t] = ok ? j : -1;
+        }
+    };
+
+    // the query of the current sequence: operand A lanes (head col, group g), head weights,
+    // and the query's largest scale span
+    int cur_b = -1;
+    uint4 qa = make_uint4(0u, 0u, 0u, 0u);
+    uint32_t qsc = 127u;
+    float W[H];
+    int qspan = 0;
+    auto load_query_for = [&](int b) {
+        const int hq = min(col, H - 1), gq = min(g, G - 1);
+        uint4 c;
+        uint32_t sc;
+        if (a.q_f32) {
+            QueryF32<H, G> F;
+            load_query_f32<H, G>(F, a.q_f32 + (size_t)b * H * 32 * G);
+            quant_query_group<H, G>(F, hq * G + gq, c, sc);
+        } else {
+            c = *reinterpret_cast<const uint4 *>(a.q_codes + ((size_t)b * H * G + hq * G + gq) * 16);
+            sc = a.q_scales[(size_t)b * H * G + hq * G + gq];
+        }
+        const bool real = col < H && g < G;
+        qa = real ? c : make_uint4(0u, 0u, 0u, 0u);
+        qsc = real ? sc : 127u;
+#pragma unroll
+        for (int h = 0; h < H; h++) W[h] = a.w[(size_t)b * H + h];
+        // the query's largest scale span: lanes (head, group) of the real groups
+        int lo = real ? (int)sc : 255, hi = real ? (int)sc : 0;
+#pragma unroll
+        for (int o = 16; o < 64; o <<= 1) {  // over the groups of a head (lanes col + 16 i)
+            lo = min(lo, __shfl_xor(lo, o, kWave));
+            hi = max(hi, __shfl_xor(hi, o, kWave));
+        }
+        qspan = __builtin_amdgcn_readlane((int)wave_max_i(col < H ? hi - lo : 0), 63);
+    };
+
+    // one item: scores of its 64 positions, block maxima, its maximum; stored if it exists
+    auto compute = [&](int k, const uint4 (&kk)[T], const uint32_t (&kw)[T], const int (&vv)[T]) {
+        const ItemU u = item_u(k);
+        if (!u.ok) return;  // uniform
+        if (u.b != cur_b) {  // uniform: a new sequence's query
+            load_query_for(u.b);
+            cur_b = u.b;
+        }
+        const int L = __builtin_amdgcn_readfirstlane(sh_len[u.b]);
+        const int n_lim = RESCORE ? nent_of(u.b) : nb_of(u.b);
+        // exact single products for the whole item, unless some key's span is too wide
+        int ksp = 0;
+#pragma unroll
+        for (int t = 0; t < T; t++) ksp = max(ksp, vv[t] >= 0 ? byte_span<G>(kw[t]) : 0);
+        const bool single = __builtin_amdgcn_readlane((int)wave_max_i(ksp), 63) + qspan <= kSpanExactShared;
+        float acc_p = -INFINITY;
+#pragma unroll
+        for (int t = 0; t < T; t++) {
+            const uint4 kb = g < G ? kk[t] : make_uint4(0u, 0u, 0u, 0u);
+            const uint32_t ksb = g < G ? (kw[t] >> (8 * g)) & 255u : 127u;
+            f32x4_t d;
+            if (single) {
+                d = mfma_fp4_sk(qa, kb, qsc, ksb);
+            } else {
+                d = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int g2 = 0; g2 < G; g2++) {
+                    const f32x4_t tg = mfma_fp4_sk(qa, g == g2 ? kb : make_uint4(0u, 0u, 0u, 0u), qsc, ksb);
+#pragma unroll
+                    for (int e = 0; e < 4; e++) d[e] = d[e] + tg[e];
+                }
+            }
+            // lane (position col, g): heads 4g .. 4g+3; s = fma(w_{H-1}, r_{H-1}, ... fma(w_0, r_0, +0))
+            float sc;
+            if constexpr (H <= 4) {
+                sc = 0.0f;
+#pragma unroll
+                for (int e = 0; e < H; e++) sc = __builtin_fmaf(W[e], relu_bits(d[e]), sc);
+            } else {
+                float lo = 0.0f;
+#pragma unroll
+                for (int e = 0; e < 4; e++) lo = __builtin_fmaf(W[e], relu_bits(d[e]), lo);
+                sc = __shfl(lo, max(lane - 16, 0), kWave);  // heads 0..3 of the position
+#pragma unroll
+                for (int e = 0; e < 4; e++) sc = __builtin_fmaf(W[4 + e], relu_bits(d[e]), sc);
+            }
+            const int jv = vv[t];
+            const float val = jv >= 0 && jv * kBlk + slot < L ? sc : -INFINITY;
+            // position 16t + c of the item into lane 16t + c
+            const float v = __shfl(val, (H > 4 ? 16 : 0) + col, kWave);
+            acc_p = g == t ? v : acc_p;
+        }
+        // block maxima (every lane of an 8-lane group), the item's maximum into lane 63
+        const float m = block_max_lanes<1>(acc_p);
+        const float bmax = __shfl(m, 8 * (lane & 7), kWave);
+        const float g63 = blocks_to_lane63<1>(m);
+        float *ps_row = RESCORE ? a.poolsc + (int64_t)u.b * a.K_blk * kBlk : a.pscore + (int64_t)u.b * a.maxb * kBlk;
+        float *pb_row = RESCORE ? a.poolbmax + (int64_t)u.b * a.K_blk : a.bscore + (int64_t)u.b * a.bstride;
+        if ((RESCORE || a.pscore) && u.e0 + lane / kBlk < n_lim) ps_row[(int64_t)u.e0 * kBlk + lane] = acc_p;
+        if ((RESCORE || a.bscore) && lane < kBlk && u.e0 + lane < n_lim) pb_row[u.e0 + lane] = bmax;
+        if (!RESCORE && a.gmax && lane == kWave - 1) a.gmax[(int64_t)u.b * a.ngmax + u.e0 / kItemBlocks] = g63;
+    };
+
+    // prologue: pool entries of items 0..2, table entries of items 0 and 1, keys of item 0
+    load_pool(0, praw[0]);
+    load_pool(1, praw[1]);
+    load_pool(2, praw[2]);
+    load_table(0, praw[0], lj[0], lph[0]);
+    load_table(1, praw[1], lj[1], lph[1]);
+    load_keys(lj[0], lph[0], kc[0], ksw[0], vis[0]);
+    for (int k0 = 0; k0 < n_items; k0 += 4) {
+#pragma unroll
+        for (int st = 0; st < 4; st++) {
+            const int k = k0 + st;
+            load_pool(k + 3, praw[(st + 3) % 4]);
+            load_table(k + 2, praw[(st + 2) % 4], lj[st % 2], lph[st % 2]);
+            load_keys(lj[(st + 1) % 2], lph[(st + 1) % 2], kc[(st + 1) % 2], ksw[(st + 1) % 2],
+                      vis[(st + 1) % 2]);
+            compute(k, kc[st % 2], ksw[st % 2], vis[st % 2]);
+        }
+    }
+}
+
 // ------------------------------------------------------------------ dispatch
 
 typedef void (*ScanFn)(dim3, size_t, hipStream_t, const ScanArgs &);
@@ -755,6 +1040,27 @@ void launch_rescore(dim3 g, size_t sh, hipStream_t s, const ScanArgs &a) {
     else k_scan<H, G, true, false, false><<<g, kScanThreads, sh, s>>>(a);
 }
 
+template <int H, int G>
+void launch_scan_shared(dim3 g, size_t sh, hipStream_t s, const ScanArgs &a) {
+    k_scan_shared<H, G, false><<<g, kScanThreads, sh, s>>>(a);
+}
+template <int H, int G>
+void launch_rescore_shared(dim3 g, size_t sh, hipStream_t s, const ScanArgs &a) {
+    k_scan_shared<H, G, true><<<g, kScanThreads, sh, s>>>(a);
+}
+
+bool pick_shared(int H, int dI, KernSet *ks) {
+    const int G = dI / 32;
+#define CSA2_CASE(h, g) \
+    if (H == h && G == g) { *ks = {launch_scan_shared<h, g>, launch_rescore_shared<h, g>}; return true; }
+    CSA2_CASE(1, 1) CSA2_CASE(1, 2) CSA2_CASE(1, 4)
+    CSA2_CASE(2, 1) CSA2_CASE(2, 2) CSA2_CASE(2, 4)
+    CSA2_CASE(4, 1) CSA2_CASE(4, 2) CSA2_CASE(4, 4)
+    CSA2_CASE(8, 1) CSA2_CASE(8, 2) CSA2_CASE(8, 4)
+#undef CSA2_CASE
+    return false;
+}
+
 bool pick(int H, int dI, KernSet *ks) {
     const int G = dI / 32;
 #define CSA2_CASE(h, g) \
@@ -767,15 +1073,22 @@ bool pick(int H, int dI, KernSet *ks) {
     return false;
 }
 
+// The kernels of a configuration: per-head keys or one shared key per position.
+bool pick_cfg(const csa2_config *c, KernSet *ks) {
+    return c->shared_key ? pick_shared(c->n_idx_heads, c->idx_dim, ks)
+                         : pick(c->n_idx_heads, c->idx_dim, ks);
+}
+
 int check_index_cfg(const csa2_config *c) {
     if (!c) return CSA2_ERR_INVALID;
     if (c->n_idx_heads <= 0 || c->idx_dim <= 0 || c->idx_dim % 32 || c->kv_dim <= 0 ||
         c->kv_dim % 32 || c->n_q_heads <= 0 || c->swa_window < 0 || c->pool_blocks <= 0 ||
-        c->topk <= 0 || (int64_t)c->topk > 8 * (int64_t)c->pool_blocks)
+        c->topk <= 0 || (int64_t)c->topk > 8 * (int64_t)c->pool_blocks ||
+        (c->shared_key != 0 && c->shared_key != 1))
         return CSA2_ERR_INVALID;
     if (c->pool_blocks > CSA2_MAX_POOL_BLOCKS) return CSA2_ERR_UNSUPPORTED;
     KernSet ks;
-    if (!pick(c->n_idx_heads, c->idx_dim, &ks)) return CSA2_ERR_UNSUPPORTED;
+    if (!pick_cfg(c, &ks)) return CSA2_ERR_UNSUPPORTED;
     return CSA2_OK;
 }
 
@@ -842,9 +1155,9 @@ static WsIdx ws_idx(int B, int maxb, int K_blk) {
 
 extern "C" int csa2_layout(const csa2_config *c, csa2_layout_info *out) {
     if (!c || !out || c->n_idx_heads <= 0 || c->idx_dim <= 0 || c->idx_dim % 32 ||
-        c->kv_dim <= 0 || c->kv_dim % 32)
+        c->kv_dim <= 0 || c->kv_dim % 32 || (c->shared_key != 0 && c->shared_key != 1))
         return CSA2_ERR_INVALID;
-    out->idx_block_bytes = (size_t)kBlk * c->n_idx_heads * (c->idx_dim / 2 + c->idx_dim / 32);
+    out->idx_block_bytes = (size_t)kBlk * key_heads(c) * (c->idx_dim / 2 + c->idx_dim / 32);
     out->kv_row_bytes = (size_t)c->kv_dim / 2 + c->kv_dim / 32;
     out->kv_block_bytes = kBlk * out->kv_row_bytes;
     out->swa_row_bytes = (size_t)c->kv_dim + c->kv_dim / 32;
@@ -935,7 +1248,7 @@ extern "C" int csa2_index_scores(const csa2_config *c, const uint8_t *q_codes,
     CSA2_CHECK_INDEX_ARGS();
     if (batch == 0 || (!scores && !block_scores)) return CSA2_OK;
     KernSet ks;
-    pick(c->n_idx_heads, c->idx_dim, &ks);
+    pick_cfg(c, &ks);
     ScanArgs a = scan_args(c, q_codes, q_scales, w, idx_cache, n_blocks, block_table, maxb,
                            ctx_len, batch);
     a.pscore = scores;
@@ -957,7 +1270,7 @@ extern "C" int csa2_index_full_scan(const csa2_config *c, const uint8_t *q_codes
     if (ws_bytes < L.total) return CSA2_ERR_WORKSPACE;
     if (batch == 0) return CSA2_OK;
     KernSet ks;
-    pick(c->n_idx_heads, c->idx_dim, &ks);
+    pick_cfg(c, &ks);
     ScanArgs a = scan_args(c, q_codes, q_scales, w, idx_cache, n_blocks, block_table, maxb,
                            ctx_len, batch);
     uint8_t *base = (uint8_t *)ws;
@@ -1022,14 +1335,14 @@ int index_full_append(const csa2_config *c, const float *latent, const float *id
     const WsIdx L = ws_idx(batch, maxb, c->pool_blocks);
     if (ws_bytes < L.total) return CSA2_ERR_WORKSPACE;
     if (batch == 0) return CSA2_OK;
-    const bool fused = fuse_append(c->n_idx_heads, c->idx_dim / 32);
+    const bool fused = !c->shared_key && fuse_append(c->n_idx_heads, c->idx_dim / 32);
     if (!fused) {
         const int st = launch_append_global(c, latent, idx_k, block_table, maxb, n_blocks,
                                             ctx_len, -1, batch, 1, kv_cache, idx_cache, stream);
         if (st) return st;
     }
     KernSet ks;
-    pick(c->n_idx_heads, c->idx_dim, &ks);
+    pick_cfg(c, &ks);
     ScanArgs a = scan_args(c, q_codes, q_scales, w, idx_cache, n_blocks, block_table, maxb,
                            ctx_len, batch, q_f32);
     uint8_t *base = (uint8_t *)ws;
@@ -1065,7 +1378,7 @@ int index_reindex(const csa2_config *c, const uint8_t *q_codes, const uint8_t *q
     if (ws_bytes < L.total) return CSA2_ERR_WORKSPACE;
     if (batch == 0) return CSA2_OK;
     KernSet ks;
-    pick(c->n_idx_heads, c->idx_dim, &ks);
+    pick_cfg(c, &ks);
     ScanArgs a = scan_args(c, q_codes, q_scales, w, idx_cache, n_blocks, block_table, maxb,
                            ctx_len, batch, q_f32);
     a.pool = pool_blocks;

@@ -146,7 +146,7 @@ int grid_for(int64_t n, int bs) { return (int)((n + bs - 1) / bs); }
 int launched() { return hipGetLastError() == hipSuccess ? CSA2_OK : CSA2_ERR_HIP; }
 bool cfg_dims_ok(const csa2_config *c) {
     return c && c->kv_dim > 0 && c->kv_dim % 32 == 0 && c->n_idx_heads > 0 &&
-           c->idx_dim > 0 && c->idx_dim % 32 == 0;
+           c->idx_dim > 0 && c->idx_dim % 32 == 0 && (c->shared_key == 0 || c->shared_key == 1);
 }
 }  // namespace
 
@@ -193,11 +193,12 @@ int csa2::launch_append_global(const csa2_config *cfg, const float *latent,
                                uint8_t *idx_cache, hipStream_t stream) {
     const int64_t rows = (int64_t)batch * n_new;
     if (rows == 0) return CSA2_OK;
-    const int gpr = cfg->kv_dim / 32 + cfg->n_idx_heads * (cfg->idx_dim / 32);
+    const int kh = key_heads(cfg);
+    const int gpr = cfg->kv_dim / 32 + kh * (cfg->idx_dim / 32);
     const int64_t n = rows * gpr;
     k_append_global<<<grid_for(n, 256), 256, 0, stream>>>(
         latent, idx_k, block_table, maxb, n_blocks, pos0, pos_off, n_new, kv_cache, idx_cache,
-        cfg->kv_dim, cfg->n_idx_heads, cfg->idx_dim, rows);
+        cfg->kv_dim, kh, cfg->idx_dim, rows);
     return launched();
 }
 

@@ -522,6 +522,7 @@ int prefill_setup(const csa2_config *c, const uint8_t *q_codes, const uint8_t *q
         maxb <= 0 || q_pos0 < 0 || n_q < 0 || !ws)
         return CSA2_ERR_INVALID;
     if ((int64_t)q_pos0 + n_q > (int64_t)maxb * kBlk) return CSA2_ERR_INVALID;
+    if (c->shared_key) return CSA2_ERR_UNSUPPORTED;  // the prefill kernels read per-head keys
     const WsPrefill L = ws_prefill(n_q, maxb);
     if (ws_bytes < L.total) return CSA2_ERR_WORKSPACE;
     if (!pick_prefill(c->n_idx_heads, c->idx_dim, fn)) return CSA2_ERR_UNSUPPORTED;

@@ -13,7 +13,8 @@ APPEND_CHUNK = 1 << 17  # positions per append call (bounds host memory)
 
 
 def cfg_of(wl: si.Workload) -> k.csa2_config:
-    return k.config(wl.H_I, wl.d_I, wl.D, wl.H_q, wl.W, wl.K_blk, wl.k, wl.sm_scale)
+    return k.config(wl.H_I, wl.d_I, wl.D, wl.H_q, wl.W, wl.K_blk, wl.k, wl.sm_scale,
+                    wl.shared_key)
 
 
 def dev(x, dtype=None):
