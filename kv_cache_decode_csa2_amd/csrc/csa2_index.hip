@@ -168,6 +168,7 @@ struct ScanArgs {
     float *pscore;
     float *bscore;
     float *gmax;
+    int32_t *arrive;  // [B] arrival counters of the two-phase selection, zeroed here (or null)
     int32_t ngmax;
     int32_t bstride;  // row stride of bscore (floats)
     // rescore mode: pool [B][K_blk], pool_len [B] -> pool scores [B][K_blk*8]
@@ -421,6 +422,8 @@ struct StepMeta {
 // addresses are a scalar base plus a 32-bit lane offset.
 template <int H, int G, bool RESCORE, bool OFF32, bool APPEND>
 __global__ __launch_bounds__(kScanThreads, 2) void k_scan(ScanArgs a) {
+    if (a.arrive && blockIdx.x == 0)  // (read by the selection, which runs after this kernel)
+        for (int i = (int)threadIdx.x; i < a.B; i += kScanThreads) a.arrive[i] = 0;
     constexpr int BPW = 8 / H;                         // blocks per wave step
     constexpr int NSTEP = kItemBlocks / BPW;           // steps per item
     constexpr int CODES = kBlk * H * 16 * G;
@@ -797,6 +800,8 @@ __device__ __forceinline__ void quant_query_group(const QueryF32<H, G> &F, int q
 
 template <int H, int G, bool RESCORE>
 __global__ __launch_bounds__(kScanThreads, 2) void k_scan_shared(ScanArgs a) {
+    if (a.arrive && blockIdx.x == 0)  // (read by the selection, which runs after this kernel)
+        for (int i = (int)threadIdx.x; i < a.B; i += kScanThreads) a.arrive[i] = 0;
     constexpr int CODES = kBlk * 16 * G;  // code bytes of a block (one key per position)
     constexpr int BYTES = CODES + kBlk * G;
     constexpr int T = 4;                  // 16-position tiles per item
@@ -1137,10 +1142,25 @@ size_t prefix_bytes(int B) { return sizeof(int32_t) * (3 * (size_t)B + 1); }
 // Workspace of the index calls: position scores, block maxima, group maxima (Full) and
 // pool scores (Reindex).  No initialisation is needed.
 namespace csa2 {
+
+int sel2_workgroups(const csa2_config *c, int32_t maxb) {
+    // below 2 K_blk groups most groups hold candidates and the last workgroup would select
+    // from nearly every block: the one-workgroup selection is faster there (measured at
+    // 64K-128K contexts; the two-phase form wins from 256K on)
+    const int ng = (maxb + kItemBlocks - 1) / kItemBlocks;
+    if (ng < 2 * c->pool_blocks || c->pool_blocks < c->topk) return 0;
+    const int nw = (ng + kSel2GroupsPerW - 1) / kSel2GroupsPerW;
+    return nw <= kSel2MaxW ? nw : 0;
+}
+
 struct WsIdx {
-    size_t pscore, bscore, gmax, poolsc, poolbmax, total;
+    size_t pscore, bscore, gmax, poolsc, poolbmax;
+    size_t cand, mu_sc, mu_blk, cnt, arrive;  // two-phase Full selection (nw > 0)
+    int nw;
+    size_t total;
 };
-static WsIdx ws_idx(int B, int maxb, int K_blk) {
+static WsIdx ws_idx(const csa2_config *c, int B, int maxb) {
+    const int K_blk = c->pool_blocks;
     WsIdx w;
     size_t o = 0;
     w.pscore = o;  o = align256(o + sizeof(float) * (size_t)B * maxb * kBlk);
@@ -1148,6 +1168,13 @@ static WsIdx ws_idx(int B, int maxb, int K_blk) {
     w.gmax = o;    o = align256(o + sizeof(float) * (size_t)B * ngmax_of(maxb));
     w.poolsc = o;  o = align256(o + sizeof(float) * (size_t)B * K_blk * kBlk);
     w.poolbmax = o; o = align256(o + sizeof(float) * (size_t)B * K_blk);
+    w.nw = sel2_workgroups(c, maxb);
+    const size_t regs = (size_t)B * w.nw;
+    w.cand = o;    o = align256(o + sizeof(uint2) * regs * kSel2GroupsPerW * kItemBlocks);
+    w.mu_sc = o;   o = align256(o + sizeof(float) * regs * kSel2MuCap * kBlk);
+    w.mu_blk = o;  o = align256(o + sizeof(int32_t) * regs * kSel2MuCap);
+    w.cnt = o;     o = align256(o + sizeof(int32_t) * regs * 2);
+    w.arrive = o;  o = align256(o + sizeof(int32_t) * (w.nw ? (size_t)B : 0));
     w.total = o;
     return w;
 }
@@ -1170,7 +1197,7 @@ extern "C" int csa2_workspace_bytes(const csa2_config *c, int op, int32_t batch,
     if (op == CSA2_OP_INDEX_FULL || op == CSA2_OP_INDEX_REINDEX) {
         const int st = check_cfg(c);
         if (st) return st;
-        *bytes = ws_idx(batch, maxb, c->pool_blocks).total;
+        *bytes = ws_idx(c, batch, maxb).total;
         return CSA2_OK;
     }
     if (op == CSA2_OP_INDEX_PREFILL) {
@@ -1215,7 +1242,7 @@ namespace {
 
 SelectArgs select_args(const csa2_config *c, const int32_t *ctx, int32_t maxb, int32_t B,
                        void *ws) {
-    const WsIdx L = ws_idx(B, maxb, c->pool_blocks);
+    const WsIdx L = ws_idx(c, B, maxb);
     uint8_t *base = (uint8_t *)ws;
     SelectArgs s{};
     s.ctx_len = ctx;
@@ -1233,7 +1260,20 @@ SelectArgs select_args(const csa2_config *c, const int32_t *ctx, int32_t maxb, i
     s.ngmax = ngmax_of(maxb);
     s.poolsc = (const float *)(base + L.poolsc);
     s.poolbmax = (const float *)(base + L.poolbmax);
+    s.sel2.nw = L.nw;
+    if (L.nw) {
+        s.sel2.cand = (uint2 *)(base + L.cand);
+        s.sel2.mu_sc = (float *)(base + L.mu_sc);
+        s.sel2.mu_blk = (int32_t *)(base + L.mu_blk);
+        s.sel2.cnt = (int32_t *)(base + L.cnt);
+        s.sel2.arrive = (int32_t *)(base + L.arrive);
+    }
     return s;
+}
+
+// The Full selection: two-phase where it serves, else one workgroup per sequence.
+int launch_full_select(const SelectArgs &s, hipStream_t stream) {
+    return s.sel2.nw ? launch_select_full2(s, stream) : launch_select(s, false, stream);
 }
 
 }  // namespace
@@ -1266,7 +1306,7 @@ extern "C" int csa2_index_full_scan(const csa2_config *c, const uint8_t *q_codes
     const float *q_f32 = nullptr;
     CSA2_CHECK_INDEX_ARGS();
     if (!ws) return CSA2_ERR_INVALID;
-    const WsIdx L = ws_idx(batch, maxb, c->pool_blocks);
+    const WsIdx L = ws_idx(c, batch, maxb);
     if (ws_bytes < L.total) return CSA2_ERR_WORKSPACE;
     if (batch == 0) return CSA2_OK;
     KernSet ks;
@@ -1278,6 +1318,7 @@ extern "C" int csa2_index_full_scan(const csa2_config *c, const uint8_t *q_codes
     a.bscore = (float *)(base + L.bscore);
     a.bstride = ngmax_of(maxb) * kItemBlocks;
     a.gmax = (float *)(base + L.gmax);
+    a.arrive = L.nw ? (int32_t *)(base + L.arrive) : nullptr;
     ks.scan(dim3(scan_grid((int64_t)batch * ngmax_of(maxb))), prefix_bytes(batch), stream, a);
     return launched();
 }
@@ -1293,14 +1334,14 @@ extern "C" int csa2_index_full_finish(const csa2_config *c, const uint8_t *q_cod
     const float *q_f32 = nullptr;
     CSA2_CHECK_INDEX_ARGS();
     if (!pool_blocks || !pool_len || !topk || !topk_len || !ws) return CSA2_ERR_INVALID;
-    if (ws_bytes < ws_idx(batch, maxb, c->pool_blocks).total) return CSA2_ERR_WORKSPACE;
+    if (ws_bytes < ws_idx(c, batch, maxb).total) return CSA2_ERR_WORKSPACE;
     if (batch == 0) return CSA2_OK;
     SelectArgs s = select_args(c, ctx_len, maxb, batch, ws);
     s.pool_blocks = pool_blocks;
     s.pool_len = pool_len;
     s.topk = topk;
     s.topk_len = topk_len;
-    return launch_select(s, false, stream);
+    return launch_full_select(s, stream);
 }
 
 extern "C" int csa2_index_full(const csa2_config *c, const uint8_t *q_codes,
@@ -1332,7 +1373,7 @@ int index_full_append(const csa2_config *c, const float *latent, const float *id
     if (!idx_k || (latent && !kv_cache) || !pool_blocks || !pool_len || !topk || !topk_len || !ws)
         return CSA2_ERR_INVALID;
     if (latent && c->kv_dim != kAppD) return CSA2_ERR_UNSUPPORTED;
-    const WsIdx L = ws_idx(batch, maxb, c->pool_blocks);
+    const WsIdx L = ws_idx(c, batch, maxb);
     if (ws_bytes < L.total) return CSA2_ERR_WORKSPACE;
     if (batch == 0) return CSA2_OK;
     const bool fused = !c->shared_key && fuse_append(c->n_idx_heads, c->idx_dim / 32);
@@ -1350,6 +1391,7 @@ int index_full_append(const csa2_config *c, const float *latent, const float *id
     a.bscore = (float *)(base + L.bscore);
     a.bstride = ngmax_of(maxb) * kItemBlocks;
     a.gmax = (float *)(base + L.gmax);
+    a.arrive = L.nw ? (int32_t *)(base + L.arrive) : nullptr;
     if (fused) {
         a.new_key = idx_k;
         a.new_lat = latent;
@@ -1364,7 +1406,7 @@ int index_full_append(const csa2_config *c, const float *latent, const float *id
     sa.pool_len = pool_len;
     sa.topk = topk;
     sa.topk_len = topk_len;
-    return launch_select(sa, false, stream);
+    return launch_full_select(sa, stream);
 }
 
 int index_reindex(const csa2_config *c, const uint8_t *q_codes, const uint8_t *q_scales,
@@ -1374,7 +1416,7 @@ int index_reindex(const csa2_config *c, const uint8_t *q_codes, const uint8_t *q
                   int32_t *topk_len, void *ws, size_t ws_bytes, hipStream_t stream) {
     CSA2_CHECK_INDEX_ARGS();
     if (!pool_blocks || !pool_len || !topk || !topk_len || !ws) return CSA2_ERR_INVALID;
-    const WsIdx L = ws_idx(batch, maxb, c->pool_blocks);
+    const WsIdx L = ws_idx(c, batch, maxb);
     if (ws_bytes < L.total) return CSA2_ERR_WORKSPACE;
     if (batch == 0) return CSA2_OK;
     KernSet ks;

@@ -8,6 +8,23 @@
 
 namespace csa2 {
 
+// Regions of the two-phase Full selection (decode contexts with more blocks than the pool):
+// per sequence b and gather workgroup w (groups [w*1024, (w+1)*1024)), the candidate blocks
+// as (order key, block) pairs, the blocks that reach the top-k bound with their 8 position
+// scores, and the two counts (-1: more bound-reaching blocks than the region holds).
+constexpr int kSel2GroupsPerW = 1024;
+constexpr int kSel2MuCap = 256;   // bound-reaching blocks per region
+constexpr int kSel2MaxW = 64;     // gather workgroups per sequence (contexts up to 4M)
+constexpr int kSel2LdsCap = 8192; // candidates the last workgroup selects from (in LDS)
+struct Sel2Ws {
+    int32_t nw;        // gather workgroups per sequence (0: the one-workgroup selection)
+    uint2 *cand;       // [B][nw][kSel2GroupsPerW * 8]
+    float *mu_sc;      // [B][nw][kSel2MuCap][8]
+    int32_t *mu_blk;   // [B][nw][kSel2MuCap]
+    int32_t *cnt;      // [B][nw][2]
+    int32_t *arrive;   // [B] arrivals: zeroed by the scan, reset by the last workgroup
+};
+
 struct SelectArgs {
     const int32_t *ctx_len;  // [B] device lengths; NULL: L_b = q_pos0 + b + 1 (prefill)
     int32_t q_pos0;
@@ -30,12 +47,21 @@ struct SelectArgs {
     int32_t *pool_len;     // Full: out; Reindex: in
     int32_t *topk;
     int32_t *topk_len;
+    Sel2Ws sel2;  // two-phase Full selection (sel2.nw > 0)
 };
+
+// Gather workgroups per sequence of the two-phase Full selection for a table of width maxb
+// (0 when the one-workgroup selection serves: every sequence fits the pool, K_blk < k, or the
+// context is beyond kSel2MaxW workgroups).
+int sel2_workgroups(const csa2_config *cfg, int32_t maxb);
 
 // Enqueues the selection: one workgroup per sequence b < a.B.  Full: pool from the block
 // and group maxima, then top-k from the position scores.  Reindex: top-k from the rescored
 // pool.  Returns a csa2 status.
 int launch_select(const SelectArgs &a, bool reindex, hipStream_t stream);
+
+// The two-phase Full selection (grid sel2.nw x B); a.sel2 filled.
+int launch_select_full2(const SelectArgs &a, hipStream_t stream);
 
 // Row stride of the group maxima of a table of width maxb (multiple of 4 floats).
 int ngmax_of(int maxb);

@@ -498,6 +498,23 @@ __device__ __forceinline__ void select_topk(const SelectArgs &a, int b, int L, c
     if (tid == 0) a.topk_len[b] = (int32_t)need;
 }
 
+// Full mode in one workgroup: the pool from the group and block maxima, then the top-k inside
+// it from the stored position scores, both written out.  graw: the thread's 16 group maxima.
+__device__ __forceinline__ void full_select_one_wg(const SelectArgs &a, int b, int L, int nb,
+                                                   SelectShared &sm, const float4 (&graw)[kIPT / 4]) {
+    const int tid = threadIdx.x;
+    uint32_t thr;
+    uint32_t kmax;
+    const int plen = select_pool(a, b, nb, sm, graw, &thr, &kmax);
+    const int np = min(plen, nb);
+    select_topk<false>(a, b, L, sm.pool, np, thr, kmax, sm);
+    // the pool leaves last: stores complete in issue order with loads, so a store issued
+    // before the top-k's score loads would have delayed their use by its write round trip
+    int32_t *pool_out = a.pool_blocks + (int64_t)b * a.K_blk;
+    for (int i = tid; i < a.K_blk; i += kSelThreads) pool_out[i] = i < np ? sm.pool[i] : -1;
+    if (tid == 0) a.pool_len[b] = np;
+}
+
 template <bool REINDEX>
 __global__ __launch_bounds__(kSelThreads) void k_select(SelectArgs a) {
     extern __shared__ __align__(16) uint8_t sh_raw[];
@@ -529,19 +546,290 @@ __global__ __launch_bounds__(kSelThreads) void k_select(SelectArgs a) {
         select_topk<true>(a, b, L, a.pool_blocks + (int64_t)b * a.K_blk, plen, 0u, 0u, sm);
         return;
     }
-    uint32_t thr;
-    uint32_t kmax;
-    const int plen = select_pool(a, b, nb, sm, graw, &thr, &kmax);
-    const int np = min(plen, nb);
-    select_topk<false>(a, b, L, sm.pool, np, thr, kmax, sm);
-    // the pool leaves last: stores complete in issue order with loads, so a store issued
-    // before the top-k's score loads would have delayed their use by its write round trip
-    int32_t *pool_out = a.pool_blocks + (int64_t)b * a.K_blk;
-    for (int i = tid; i < a.K_blk; i += kSelThreads) pool_out[i] = i < np ? sm.pool[i] : -1;
-    if (tid == 0) a.pool_len[b] = np;
+    full_select_one_wg(a, b, L, nb, sm, graw);
+}
+
+// ------------------------------------------------------------------ two-phase Full selection
+//
+// One gather workgroup per 1024 groups of a sequence, the last of them to arrive finishing
+// the selection.  Each gather workgroup reads every group maximum of its sequence and, in the
+// same round trip, the block maxima of its own groups (read whether or not they will be
+// needed), so that no single workgroup gathers the pool's scattered blocks (on one CU those
+// reads had cost ~9 us).  Bounds from the group maxima in one histogram pass:
+//   lam = the lower edge of the bin that holds the K_blk-th largest group maximum.  K_blk
+//         distinct blocks (the groups' maximal blocks) reach the K_blk-th largest group
+//         maximum, so every pool block scores >= lam and lies in a group whose maximum is
+//         >= lam: the pool is the exact top-K_blk of these candidates.
+//   mu  = the same edge for the k-th largest group maximum.  k distinct positions score
+//         >= mu, so the k best positions all score >= mu and lie in blocks whose maximum is
+//         >= mu.  With K_blk >= k those k positions are the k best of the pool (a block that
+//         outranks a block holding one of them holds a position that outranks it), i.e. the
+//         top-k of the definition.
+// A gather workgroup writes its candidate blocks (order key, block) and the position scores of
+// its blocks >= mu to its region; the last one reads the regions and selects both exactly.
+// The last workgroup keeps the candidates in LDS (at most kSel2LdsCap) and one bound-reaching
+// block per thread.  Sequences that fit the pool, and candidate sets beyond those limits
+// (heavy ties), take the one-workgroup selection in the last workgroup instead.
+
+// One histogram pass over the keys (0: no item) with two targets: lower edges of the bins
+// holding the K1-th and the K2-th largest key (K1, K2 <= the number of keys).
+template <class Src>
+__device__ void two_bounds(const Src &src, uint32_t K1, uint32_t K2, SelShared &sm,
+                           uint32_t *e1, uint32_t *e2) {
+    const int tid = threadIdx.x, lane = lane_id(), wave = threadIdx.x / kWave;
+    uint32_t lo = 0xFFFFFFFFu, hi = 0u, n = 0u;
+    src.each([&](uint32_t key) {
+        lo = min(lo, key ? key : 0xFFFFFFFFu);
+        hi = max(hi, key);
+        n += key != 0u;
+    });
+    block_min_max_count(lo, hi, n, sm);
+    if (n == 0u || lo >= hi) {  // no key, or all equal
+        *e1 = *e2 = n ? lo : 0u;
+        return;
+    }
+    const uint32_t w = hi - lo;
+    const int s = max(0, 32 - __clz((int)w) - 11);  // (w >> s) < 2048
+    const int nbins = (int)(w >> s) + 1, li0 = nbins - 1;
+    src.each([&](uint32_t key) {
+        const uint32_t off = key - lo;  // wraps for key 0
+        if (key != 0u && off <= w) atomicAdd(&sm.hist[li0 - (int)(off >> s)], 1u);
+    });
+    __syncthreads();
+    // thread t: reversed bins 2t, 2t + 1 (highest bin first), read and cleared
+    const int r0 = 2 * tid;
+    uint2 hv = make_uint2(0u, 0u);
+    if (r0 < nbins) {
+        hv = *reinterpret_cast<const uint2 *>(&sm.hist[r0]);
+        *reinterpret_cast<uint2 *>(&sm.hist[r0]) = make_uint2(0u, 0u);
+    }
+    const uint32_t c0 = hv.x, c1 = r0 + 1 < nbins ? hv.y : 0u, v = c0 + c1;
+    const uint32_t incl = wave_incl_scan(v);
+    if (lane == kWave - 1) sm.scan[wave] = incl;
+    __syncthreads();
+    uint32_t pw = 0u;
+#pragma unroll
+    for (int i = 0; i < kSelThreads / kWave; i += 4) {
+        const uint4 q = *reinterpret_cast<const uint4 *>(&sm.scan[i]);
+        const uint32_t x[4] = {q.x, q.y, q.z, q.w};
+#pragma unroll
+        for (int j = 0; j < 4; j++) pw += i + j < wave ? x[j] : 0u;
+    }
+    const uint32_t before = pw + incl - v;
+    const uint32_t T[2] = {K1, K2};
+#pragma unroll
+    for (int i = 0; i < 2; i++)
+        if (before < T[i] && T[i] <= before + v)
+            sm.res[i] = (uint32_t)(li0 - (T[i] <= before + c0 ? r0 : r0 + 1));
+    __syncthreads();
+    *e1 = lo + (sm.res[0] << s);
+    *e2 = lo + (sm.res[1] << s);
+    __syncthreads();  // (res is written again by later selections)
+}
+
+__global__ __launch_bounds__(kSelThreads) void k_select_full2(SelectArgs a) {
+    extern __shared__ __align__(16) uint8_t sh_raw[];
+    SelectShared &sm = *reinterpret_cast<SelectShared *>(sh_raw);
+    __shared__ int32_t sh_pre[kSel2MaxW + 1], sh_mpre[kSel2MaxW + 1];
+    __shared__ int32_t sh_flag[2];
+    const Sel2Ws &q = a.sel2;
+    const int nw = q.nw, w = blockIdx.x, b = blockIdx.y, tid = threadIdx.x;
+    // requests: the thread's 16 group maxima (clamped into the row, masked once the length
+    // is known), the length, and the 8 block maxima of this workgroup's group gi
+    float4 graw[kIPT / 4];
+    const float *gm = a.gmax + (int64_t)b * a.ngmax;
+#pragma unroll
+    for (int i = 0; i < kIPT / 4; i++) {
+        const int gix = min(tid * kIPT + 4 * i, a.ngmax - 4);
+        graw[i] = *reinterpret_cast<const float4 *>(gm + gix);
+    }
+    const int gi = w * kSel2GroupsPerW + tid;
+    const float4 *bsrc = reinterpret_cast<const float4 *>(a.bscore + (int64_t)b * a.bs_b +
+                                                         (int64_t)min(gi, a.ngmax - 1) * a.bs_g);
+    float4 bm0 = bsrc[0], bm1 = bsrc[1];
+    const int L = clamp_len(a.ctx_len[b], a.maxb);
+#pragma unroll
+    for (int i = 0; i < kIPT / 4; i++)
+        asm volatile("" : "+v"(graw[i].x), "+v"(graw[i].y), "+v"(graw[i].z), "+v"(graw[i].w));
+    asm volatile("" : "+v"(bm0.x), "+v"(bm0.y), "+v"(bm0.z), "+v"(bm0.w));
+    asm volatile("" : "+v"(bm1.x), "+v"(bm1.y), "+v"(bm1.z), "+v"(bm1.w));
+    const int nb = (L + kBlk - 1) / kBlk, ng = (nb + kItemBlocks - 1) / kItemBlocks;
+    for (int i = tid; i < kHistBins; i += kSelThreads) sm.sel.hist[i] = 0u;  // kept zero between passes
+    __syncthreads();
+    const bool fast = nb > a.K_blk && a.K_blk >= a.k && ng > a.k;  // uniform per sequence
+    uint32_t lam = 0u, mu = 0u;
+    int cnt_c = 0, cnt_m = 0;
+    const int64_t reg = (int64_t)b * nw + w;
+    if (fast) {
+        RegItems<kIPT> g;
+#pragma unroll
+        for (int i = 0; i < kIPT; i += 4) {
+            const float f[4] = {graw[i / 4].x, graw[i / 4].y, graw[i / 4].z, graw[i / 4].w};
+#pragma unroll
+            for (int t = 0; t < 4; t++) g.key[i + t] = tid * kIPT + i + t < ng ? order_key(f[t]) : 0u;
+        }
+        two_bounds(g, (uint32_t)min(a.K_blk, ng), (uint32_t)a.k, sm.sel, &lam, &mu);
+        if (ng <= a.K_blk) lam = 1u;  // every group holds pool candidates (real keys are >= 1)
+        // this workgroup's candidates: the blocks >= lam of group gi (whose maximum is then
+        // >= lam), and among them the blocks >= mu
+        const float bv[kItemBlocks] = {bm0.x, bm0.y, bm0.z, bm0.w, bm1.x, bm1.y, bm1.z, bm1.w};
+        uint32_t ck[kItemBlocks];
+        uint32_t nc = 0u, nm = 0u;
+#pragma unroll
+        for (int i = 0; i < kItemBlocks; i++) {
+            const int j = gi * kItemBlocks + i;
+            const uint32_t key = order_key(bv[i]);
+            ck[i] = gi < ng && j < nb && key >= lam ? key : 0u;
+            nc += ck[i] != 0u;
+            nm += ck[i] != 0u && ck[i] >= mu;
+        }
+        uint32_t tot;
+        const uint32_t ex = block_excl_scan<kSelThreads>(nc | (nm << 16), sm.sel.scan, &tot);
+        const uint32_t tot_c = tot & 0xFFFFu, tot_m = tot >> 16;
+        uint32_t oc = ex & 0xFFFFu, om = ex >> 16;
+        uint2 *cand = q.cand + reg * (kSel2GroupsPerW * kItemBlocks);
+        const bool mu_fits = tot_m <= (uint32_t)kSel2MuCap;
+        // candidates to the region; the bound-reaching blocks to LDS, in block order
+#pragma unroll
+        for (int i = 0; i < kItemBlocks; i++) {
+            const int j = gi * kItemBlocks + i;
+            if (ck[i] != 0u) cand[oc++] = make_uint2(ck[i], (uint32_t)j);
+            if (mu_fits && ck[i] != 0u && ck[i] >= mu) sm.pool[om++] = j;
+        }
+        __syncthreads();
+        // their position scores, one block per thread
+        if (mu_fits && tid < (int)tot_m) {
+            const int j = sm.pool[tid];
+            const float4 *src = reinterpret_cast<const float4 *>(a.pscore + (int64_t)b * a.ps_b + (int64_t)j * a.ps_j);
+            const float4 x0 = src[0], x1 = src[1];
+            float4 *dst = reinterpret_cast<float4 *>(q.mu_sc + (reg * kSel2MuCap + tid) * kBlk);
+            dst[0] = x0;
+            dst[1] = x1;
+            q.mu_blk[reg * kSel2MuCap + tid] = j;
+        }
+        cnt_c = (int)tot_c;
+        cnt_m = mu_fits ? (int)tot_m : -1;
+    }
+    if (tid == 0) {
+        q.cnt[reg * 2] = cnt_c;
+        q.cnt[reg * 2 + 1] = cnt_m;
+    }
+    // the last workgroup of the sequence to arrive finishes (every wave's stores are ordered
+    // before the barrier; thread 0's agent-scope release publishes them, the last one's acquire
+    // covers the other workgroups' regions)
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+    __syncthreads();
+    if (tid == 0)
+        sh_flag[0] = __hip_atomic_fetch_add(q.arrive + b, 1, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT) ==
+                     nw - 1;
+    __syncthreads();
+    if (!sh_flag[0]) return;  // uniform
+    if (tid == 0) __hip_atomic_store(q.arrive + b, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    bool ok = fast;
+    if (ok) {
+        if (tid < nw) {
+            sh_pre[tid + 1] = q.cnt[((int64_t)b * nw + tid) * 2];
+            sh_mpre[tid + 1] = q.cnt[((int64_t)b * nw + tid) * 2 + 1];
+        }
+        __syncthreads();
+        if (tid == 0) {
+            int okf = 1;
+            sh_pre[0] = sh_mpre[0] = 0;
+            for (int i = 1; i <= nw; i++) {
+                okf &= sh_mpre[i] >= 0;
+                sh_pre[i] += sh_pre[i - 1];
+                sh_mpre[i] = sh_mpre[i - 1] + max(sh_mpre[i], 0);
+            }
+            sh_flag[1] = okf && sh_pre[nw] <= kSel2LdsCap && sh_mpre[nw] <= kSelThreads;
+        }
+        __syncthreads();
+        ok = sh_flag[1];
+    }
+    if (!ok) {  // the one-workgroup selection (its group maxima read again: a rare path)
+        __syncthreads();
+#pragma unroll
+        for (int i = 0; i < kIPT / 4; i++) {
+            const int gix = min(tid * kIPT + 4 * i, a.ngmax - 4);
+            graw[i] = *reinterpret_cast<const float4 *>(gm + gix);
+        }
+        full_select_one_wg(a, b, L, nb, sm, graw);
+        return;
+    }
+    const int n_c = sh_pre[nw], n_m = sh_mpre[nw];
+    uint2 *lds_c = reinterpret_cast<uint2 *>(sh_raw + sizeof(SelectShared));  // [kSel2LdsCap]
+    auto region_of = [&](const int32_t *pre, int i) {  // largest r with pre[r] <= i
+        int lo = 0, hi = nw - 1;
+        while (lo < hi) {
+            const int mid = (lo + hi + 1) >> 1;
+            if (pre[mid] <= i) lo = mid;
+            else hi = mid - 1;
+        }
+        return lo;
+    };
+    // candidates i = tid + 1024 r (strided, so that every wave shares the histogram atomics)
+    // into registers for the threshold and into LDS in index order for the emission
+    RegItems<kSel2LdsCap / kSelThreads> c;
+#pragma unroll
+    for (int r = 0; r < kSel2LdsCap / kSelThreads; r++) {
+        const int i = tid + kSelThreads * r;
+        const bool in = i < n_c;
+        const int rw = in ? region_of(sh_pre, i) : 0;
+        const uint2 v = q.cand[((int64_t)b * nw + rw) * (kSel2GroupsPerW * kItemBlocks) + (in ? i - sh_pre[rw] : 0)];
+        c.key[r] = in ? v.x : 0u;
+        if (in) lds_c[i] = v;
+    }
+    // the bound-reaching block tid (blocks in order, one per thread) and its position scores
+    const int e = tid;
+    const int mw = e < n_m ? region_of(sh_mpre, e) : 0;
+    const int64_t mslot = ((int64_t)b * nw + mw) * kSel2MuCap + (e < n_m ? e - sh_mpre[mw] : 0);
+    const int32_t mb = e < n_m ? q.mu_blk[mslot] : -1;
+    const float4 *msrc = reinterpret_cast<const float4 *>(q.mu_sc + mslot * kBlk);
+    const float4 ms0 = msrc[0], ms1 = msrc[1];
+    __syncthreads();
+    // pool: the exact top-K_blk of the candidates, emitted ascending from LDS (thread t owns
+    // candidates [8t, 8t + 8))
+    {
+        const SelResult r = range_select(c, (uint32_t)a.K_blk, sm.sel);
+        constexpr int PT = kSel2LdsCap / kSelThreads;
+        RegItems<PT> o;
+        int32_t oid[PT];
+#pragma unroll
+        for (int j = 0; j < PT; j++) {
+            const int i = tid * PT + j;
+            const uint2 v = i < n_c ? lds_c[i] : make_uint2(0u, 0u);
+            o.key[j] = v.x;
+            oid[j] = (int32_t)v.y;
+        }
+        uint32_t tie_base = 0, out_base = 0;
+        emit_selected(o, [&](int j) { return oid[j]; }, r, a.pool_blocks + (int64_t)b * a.K_blk,
+                      (uint32_t)a.K_blk, tie_base, out_base, sm.sel);
+    }
+    // top-k: the exact top-k of the positions >= mu of the blocks >= mu, ascending
+    RegItems<kBlk> p;
+    {
+        const float sc[kBlk] = {ms0.x, ms0.y, ms0.z, ms0.w, ms1.x, ms1.y, ms1.z, ms1.w};
+#pragma unroll
+        for (int t = 0; t < kBlk; t++) {
+            const uint32_t key = order_key(sc[t]);
+            p.key[t] = mb >= 0 && mb * kBlk + t < L && key >= mu ? key : 0u;
+        }
+    }
+    select_emit(p, [&](int t) { return mb * kBlk + t; }, (uint32_t)a.k,
+                a.topk + (int64_t)b * a.k, (uint32_t)a.k, sm);
+    if (tid == 0) {
+        a.pool_len[b] = a.K_blk;
+        a.topk_len[b] = a.k;
+    }
 }
 
 constexpr size_t kSelectShared = sizeof(SelectShared);
+
+int launch_select_full2(const SelectArgs &a, hipStream_t stream) {
+    if (a.B <= 0) return CSA2_OK;
+    k_select_full2<<<dim3(a.sel2.nw, a.B), kSelThreads, kSelectShared + sizeof(uint2) * kSel2LdsCap,
+                     stream>>>(a);
+    return hipGetLastError() == hipSuccess ? CSA2_OK : CSA2_ERR_HIP;
+}
 
 int launch_select(const SelectArgs &a, bool reindex, hipStream_t stream) {
     if (a.B <= 0) return CSA2_OK;

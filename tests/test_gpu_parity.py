@@ -382,3 +382,44 @@ def test_global_tier_round_trip():
     k.csa2_blocks_scatter(torch.full_like(rows, 0x5A), dev(np.array([-1, nblk, -5], np.int32)), g.idx)
     torch.cuda.synchronize()
     assert np.array_equal(_np(g.idx), snapshot)
+
+
+# ------------------------------------------------------------------ two-phase Full selection
+
+@pytest.mark.parametrize("ctx,K_blk,k", [
+    ([150000, 3000, 100, 70000, 9000], 256, 100),   # 3 and 2 gather workgroups, a sequence
+                                                     # that fits the pool, ragged tails
+    ([40000, 200000], 1024, 512),                    # sequence 0 has ng <= K_blk: all of its
+                                                     # groups hold candidates
+    ([20000, 333], 64, 64),                          # K_blk == k
+])
+def test_full_two_phase_selection(ctx, K_blk, k):
+    """Contexts with more blocks than the pool take the two-phase Full selection (gather
+    workgroups per 1024 groups, the last one selecting pool and top-k from the compact
+    candidates) once the table has at least 2 K_blk groups; pools, top-k, Reindex and
+    attention equal the oracle's."""
+    wl = si.small("tp", 610 + K_blk + len(ctx), ctx, H_I=4, d_I=64, K_blk=K_blk, k=k, W=32,
+                  layers="FRU")
+    print(_run_group(wl, permute=True))
+
+
+def test_full_two_phase_ties_fall_back():
+    """Every key of the first 30000 positions equal: thousands of blocks tie at the top, so
+    the regions of bound-reaching blocks overflow and the last workgroup runs the
+    one-workgroup selection;
+    the results still equal the oracle's (lower index first among equal scores)."""
+    wl = si.small("tpt", 620, [60000, 5000], H_I=4, d_I=64, K_blk=256, k=256, W=16)
+    row = si.normal(620, 999, (1, wl.H_I, wl.d_I))
+    orig = si.idx_keys
+
+    def keys(w, b, L=None):
+        x = orig(w, b, L)
+        if b == 0:
+            x[:30000] = row
+        return x
+
+    try:
+        si.idx_keys = keys
+        print(_run_group(wl, with_attn=False))
+    finally:
+        si.idx_keys = orig
