@@ -39,6 +39,8 @@ constexpr int kStreamThreads = 256;  // one chunk stream: 4 waves of 16 rows
 constexpr int kD = 512;            // latent dim handled by these kernels
 constexpr int kPStride = 64 + 4;   // padded row of the P tile (floats)
 constexpr int kMaxSplits = 512;    // splits a merge handles (k + W <= 32768)
+constexpr int kBufferWord3 = 0x00020000;  // buffer resource word 3 of the gfx9 family
+constexpr int kSc1 = 16;                  // buffer access cache policy: agent scope (sc1)
 
 struct AttnArgs {
     const uint16_t *q;
@@ -134,7 +136,7 @@ struct AttnShared {
     float ptile[16 * kPStride];
     float red_m[4][16], red_l[4][16];
     __align__(16) uint8_t fresh_row[kD + kD / 32];  // the appended window row (MXFP8)
-    int any_valid, last;
+    int last;
 };
 
 // Combine the splits of (b, head group hg), run by the last split to finish:
@@ -142,16 +144,23 @@ struct AttnShared {
 // running maximum over batches of splits.  With T = 16 NS threads per head, thread
 // (head h = tid / T, q = tid % T) owns dims 4q + 4Ti of head h, so T threads read one
 // partial row in 16T-byte runs; a batch's rows and (max, sum) pairs are all loaded before
-// any is used (one memory round trip per batch).  An empty split's row was never written:
-// its values are discarded by a select, which keeps the loads unconditional.
+// any is used (one memory round trip per batch).  The loads are agent-scope coherent (they
+// bypass lines this XCD's caches may hold from earlier calls), so the merge needs no cache
+// invalidation.  An empty split's row was never written: its values are discarded by a
+// select, which keeps the loads unconditional.
 template <int NS>
 __device__ __forceinline__ void merge_splits(const AttnArgs &a, int b, int hg) {
     constexpr int T = 16 * NS, NV = kD / 4 / T, NB = NS == 2 ? 5 : 4;
     const int tid = threadIdx.x, h = tid / T, q = tid % T;
-    const int64_t row0 = (int64_t)b * a.nsplit * a.Hq + hg * 16 + h;  // split 0, head h
-    const float4 *src = reinterpret_cast<const float4 *>(a.part_o + row0 * kD) + q;
-    const float2 *mlp = reinterpret_cast<const float2 *>(a.part_ml) + row0;
-    const int64_t sstride = (int64_t)a.Hq * kD / 4;  // float4s between splits
+    // buffer resources over this (b, hg)'s partials (split 0 .. nsplit-1, 16 heads each);
+    // the loads carry the agent scope bit (sc1)
+    const int64_t sstride = (int64_t)a.Hq * kD;  // floats between splits
+    const uint32_t o_bytes = (uint32_t)(sizeof(float) * ((a.nsplit - 1) * sstride + 16 * kD));
+    const __amdgpu_buffer_rsrc_t ro = __builtin_amdgcn_make_buffer_rsrc(
+        a.part_o + ((int64_t)b * a.nsplit * a.Hq + hg * 16) * kD, 0, o_bytes, kBufferWord3);
+    const __amdgpu_buffer_rsrc_t rml = __builtin_amdgcn_make_buffer_rsrc(
+        a.part_ml + 2 * ((int64_t)b * a.nsplit * a.Hq + hg * 16), 0,
+        (uint32_t)(sizeof(float) * 2 * ((a.nsplit - 1) * a.Hq + 16)), kBufferWord3);
     float4 acc[NV];
 #pragma unroll
     for (int i = 0; i < NV; i++) acc[i] = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
@@ -162,9 +171,12 @@ __device__ __forceinline__ void merge_splits(const AttnArgs &a, int b, int hg) {
 #pragma unroll
         for (int u = 0; u < NB; u++) {
             const int sp = min(s0 + u, a.nsplit - 1);
-            st[u] = mlp[(int64_t)sp * a.Hq];
+            st[u] = __builtin_bit_cast(float2, __builtin_amdgcn_raw_buffer_load_b64(
+                rml, (int)(sizeof(float) * 2 * (sp * a.Hq + h)), 0, kSc1));
 #pragma unroll
-            for (int i = 0; i < NV; i++) v[u][i] = src[sp * sstride + T * i];
+            for (int i = 0; i < NV; i++)
+                v[u][i] = __builtin_bit_cast(float4, __builtin_amdgcn_raw_buffer_load_b128(
+                    ro, (int)(sizeof(float) * (sp * sstride + h * kD + 4 * (q + T * i))), 0, kSc1));
         }
         float mu[NB], mb = M;
 #pragma unroll
@@ -206,15 +218,16 @@ __device__ __forceinline__ void merge_splits(const AttnArgs &a, int b, int hg) {
 }
 
 // NS chunk streams of 4 waves per workgroup.  NS = 2 (batches too small to fill the chip):
-// streams 0 and 1 take chunks c0 and c0 + 1 of each pair side by side, and stream 1's state
-// joins stream 0's through LDS at the end, which halves the splits the merge reads; the 16
-// query rows are loaded once into LDS for both.  NS = 1: one stream, query rows loaded by
-// every wave straight into registers.
+// streams 0 and 1 take chunks c0 and c0 + 1 of each pair side by side, and the two states
+// join through LDS at the end (each stream finishing half of the dims), which halves the
+// splits the merge reads.  NS = 2 loads the 16 query rows once into LDS and every wave
+// takes its slice into registers while the row addresses resolve; NS = 1 loads the slices
+// straight into registers.
 template <int NS>
 __global__ __launch_bounds__(NS * kStreamThreads, 3 - NS) void k_attn(AttnArgs a) {
     __shared__ __align__(16) AttnShared shs[NS];
-    __shared__ __align__(16) uint4 qtile[NS == 2 ? 16 * (kD / 8 + 1) : 1];  // 16 query rows, padded
     __shared__ __align__(16) float4 fstage[kD / 4];  // the appended fp32 row, staged by DMA
+    __shared__ __align__(16) uint4 qtile[NS == 2 ? 16 * (kD / 8 + 1) : 1];  // 16 query rows, padded
 
     const int s = blockIdx.x, b = blockIdx.y / a.HG, hg = blockIdx.y % a.HG;
     const int tid = threadIdx.x, lane = tid & 63;
@@ -228,7 +241,7 @@ __global__ __launch_bounds__(NS * kStreamThreads, 3 - NS) void k_attn(AttnArgs a
     //      entries of the stream's first two chunks (read clamped into the row, masked once
     //      the length arrives).  NS = 2: the 16 query rows (16 KB) go to LDS, 32 bytes per
     //      thread, rows 65 16-byte chunks apart (8 lanes reading one chunk of 8 rows hit
-    //      distinct banks), and are read before each S.
+    //      distinct banks), so that the workgroup fetches them once.
     bf16x8_t qa[16];
     uint4 qv[2];
     if (NS == 2) {
@@ -247,12 +260,16 @@ __global__ __launch_bounds__(NS * kStreamThreads, 3 - NS) void k_attn(AttnArgs a
     const int32_t np_v = *(a.swa_new ? a.new_pos + b : a.topk_len + b);
     const int r_loc = 16 * wave + c16;
     const int nchunk = attn_splits(a.k, a.W);
-    const int c_beg = s * a.cps, c_end = min(nchunk, (s + 1) * a.cps);
+    // split s takes every nsplit-th chunk from chunk s (so that the window's chunks, whose
+    // rows are twice as long, go to different splits); stream st of the split takes the
+    // split's chunks st, st + NS, ...: chunk s + nsplit (i NS + st) in its i-th step
+    const int cstep = NS * a.nsplit;
+    const int c_first = s + a.nsplit * st;
     auto topk_raw = [&](int c) -> int32_t {
         const int rg = c * kAttnRows + r_loc;
         return a.topk[(int64_t)b * a.k + min(rg, a.k - 1)];
     };
-    const int32_t e_first = topk_raw(c_beg + st), e_second = topk_raw(c_beg + st + NS);
+    const int32_t e_first = topk_raw(c_first), e_second = topk_raw(c_first + cstep);
     if (NS == 2) {
 #pragma unroll
         for (int j = 0; j < 2; j++) {
@@ -272,7 +289,7 @@ __global__ __launch_bounds__(NS * kStreamThreads, 3 - NS) void k_attn(AttnArgs a
     const bool in_win = np_b >= w0 && np_b < L && np_b - w0 < a.W;
     const int fc = a.swa_new && np_b >= 0 && in_win ? (a.k + np_b - w0) / kAttnRows : -1;  // its chunk
     if (fc >= 0) {
-        if (fc >= c_beg && fc < c_end && (NS == 1 || (fc & 1) == st) && ts < kD / 32) {
+        if (fc % a.nsplit == s && (fc / a.nsplit) % NS == st && ts < kD / 32) {
             const uint8_t *src = reinterpret_cast<const uint8_t *>(a.swa_new + (int64_t)b * kD) + 128 * ts;
 #pragma unroll
             for (int j = 0; j < 8; j++)
@@ -301,12 +318,12 @@ __global__ __launch_bounds__(NS * kStreamThreads, 3 - NS) void k_attn(AttnArgs a
     for (int n = 0; n < 8; n++) o[n] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
 
     // The top-k row chain, pipelined across the stream's chunks: while chunk c is computed,
-    // the block-table entry of chunk c + NS and the top-k entry of chunk c + 2 NS are in
-    // flight (entry -1 / block -1: no row).  Reads are clamped into their rows and masked, so
-    // no load sits behind a branch.
+    // the block-table entry of the stream's next chunk and the top-k entry of the one after
+    // are in flight (entry -1 / block -1: no row).  Reads are clamped into their rows and
+    // masked, so no load sits behind a branch.
     auto entry_of = [&](int c, int32_t raw) -> int {
         const int rg = c * kAttnRows + r_loc;
-        return c < c_end && rg < a.k && rg < tl ? raw : -1;
+        return c < nchunk && rg < a.k && rg < tl ? raw : -1;
     };
     auto topk_at = [&](int c) -> int { return entry_of(c, topk_raw(c)); };
     auto block_of = [&](int p) -> int64_t {
@@ -314,17 +331,23 @@ __global__ __launch_bounds__(NS * kStreamThreads, 3 - NS) void k_attn(AttnArgs a
         const int64_t ph = a.table[(int64_t)b * a.tstride + (in ? p : 0) / kBlk];
         return in && ph >= 0 && ph < a.n_blocks ? ph : -1;
     };
-    int p_cur = entry_of(c_beg + st, e_first), p_nxt = entry_of(c_beg + st + NS, e_second);
+    int p_cur = entry_of(c_first, e_first), p_nxt = entry_of(c_first + cstep, e_second);
+    // whether chunk c holds a row to attend (uniform: a function of the sequence's lengths)
+    auto chunk_rows = [&](int c) -> bool {
+        const int r0 = c * kAttnRows, r1 = r0 + kAttnRows, wend = a.k + min(nwin, a.W);
+        return c < nchunk && (r0 < min(tl, a.k) || (r1 > a.k && r0 < wend));
+    };
     int64_t ph_cur = block_of(p_cur);
+    if (NS == 2) __syncthreads();  // the query tile is in LDS
 
-    // the split's chunks [c_beg, c_end) in groups of NS: stream st takes chunk c0 + st
-    for (int c0 = c_beg; c0 < c_end; c0 += NS) {
-        const int c = c0 + st;
+    // the split's chunks in steps of NS: stream st takes chunk c0 + nsplit st
+    for (int c0 = s; c0 < nchunk; c0 += cstep) {
+        const int c = c0 + a.nsplit * st;
         const int rg = c * kAttnRows + r_loc;
-        // ---- locate this lane's row (none when the stream's chunk is past the split)
+        // ---- locate this lane's row (none when the stream's chunk is past the last)
         const uint8_t *rp = nullptr;
         bool fp8 = false, fresh = false;
-        if (c >= c_end) {
+        if (c >= nchunk) {
         } else if (rg < a.k) {
             if (ph_cur >= 0)
                 rp = a.kv + ph_cur * (kBlk * (kD / 2 + kD / 32)) + (p_cur % kBlk) * (kD / 2 + kD / 32);
@@ -340,7 +363,7 @@ __global__ __launch_bounds__(NS * kStreamThreads, 3 - NS) void k_attn(AttnArgs a
         const bool valid = rp != nullptr;
         {  // the chain of the next chunks (see above)
             const int64_t ph_nxt = block_of(p_nxt);
-            const int p_nn = topk_at(c + 2 * NS);
+            const int p_nn = topk_at(c + 2 * cstep);
             p_cur = p_nxt;
             ph_cur = ph_nxt;
             p_nxt = p_nn;
@@ -400,73 +423,75 @@ __global__ __launch_bounds__(NS * kStreamThreads, 3 - NS) void k_attn(AttnArgs a
         if (NS == 2) {
             load_row();
             quant_fresh();
-        }
-        if (ts == 0) sh.any_valid = 0;
-        __syncthreads();  // also: the previous chunks are done with V, P and the reductions
-        if (valid) sh.any_valid = 1;
-        __syncthreads();
-        if (!shs[0].any_valid && !shs[NS - 1].any_valid) continue;  // uniform over the workgroup
-        if (NS == 1) {
-            if (fc == c0) {  // uniform: fc and c0 are the workgroup's
-                quant_fresh();
-                __syncthreads();
-            }
-            load_row();
-        }
-
-        // ---- exact conversion to bf16: kb[t] = dims g4*128 + 8t .. +8 of the row
-        bf16x8_t kb[16];
-        if (valid && !fp8) {
-#pragma unroll
-            for (int t = 0; t < 16; t++) {
-                const uint32_t wd = word_of(uu[t >> 2], t & 3);
-                const float sc = e8m0_to_f32((sc4 >> (8 * (t >> 2))) & 255u);
-                kb[t] = join4(__builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(wd, sc, 0),
-                              __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(wd, sc, 1),
-                              __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(wd, sc, 2),
-                              __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(wd, sc, 3));
-            }
-        } else if (valid) {
-            if (fresh) {  // the appended row from LDS (bytewise scales: kept an LDS read)
-                const uint4 *src = reinterpret_cast<const uint4 *>(sh.fresh_row + g4 * 128);
-#pragma unroll
-                for (int i = 0; i < 8; i++) uu[i] = src[i];
-                const uint8_t *fs = sh.fresh_row + kD + 4 * g4;
-                sc4 = fs[0] | (uint32_t)fs[1] << 8 | (uint32_t)fs[2] << 16 | (uint32_t)fs[3] << 24;
-            }
-#pragma unroll
-            for (int t = 0; t < 16; t++) {
-                const uint32_t w0d = word_of(uu[t >> 1], 2 * (t & 1)), w1d = word_of(uu[t >> 1], 2 * (t & 1) + 1);
-                const float sc = e8m0_to_f32((sc4 >> (8 * (t >> 2))) & 255u);
-                kb[t] = join4(__builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w0d, sc, false),
-                              __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w0d, sc, true),
-                              __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w1d, sc, false),
-                              __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w1d, sc, true));
-            }
-        } else {
-#pragma unroll
-            for (int t = 0; t < 16; t++)
-#pragma unroll
-                for (int i = 0; i < 8; i++) kb[t][i] = (__bf16)0.0f;
-        }
-
-        // ---- V into LDS, row-major: this lane's 128 dims as 16-byte stores
-#pragma unroll
-        for (int t = 0; t < 16; t++)
-            *reinterpret_cast<bf16x8_t *>(&sh.vt[r_loc * kVStride + g4 * 128 + 8 * t]) = kb[t];
-
-        // ---- S = Q K^T for this wave's 16 rows and the 16 heads (NS = 2: the query slice is
-        //      read from the LDS tile here, so that it holds no registers across the loop)
-        if (NS == 2) {
+            // this lane's query slice, while the row bytes are in flight (held only until S,
+            // so that P V has the registers to read its V tiles ahead)
 #pragma unroll
             for (int t = 0; t < 16; t++) {
                 const uint4 u = qtile[c16 * 65 + g4 * 16 + t];
                 qa[t] = *reinterpret_cast<const bf16x8_t *>(&u);
             }
         }
-        f32x4_t acc = {0.0f, 0.0f, 0.0f, 0.0f};
+        if (!chunk_rows(c0) && !(NS == 2 && chunk_rows(c0 + a.nsplit))) continue;  // uniform
+        __syncthreads();  // the previous chunks are done with V, P and the reductions
+        if (NS == 1) {
+            if (fc == c) {  // uniform: fc and c are the workgroup's
+                quant_fresh();
+                __syncthreads();
+            }
+            load_row();
+        }
+
+        // ---- exact conversion to bf16, one piece kb = dims g4*128 + 8t .. +8 of the row at a
+        //      time: stored to the V tile row-major and taken as the B operand of S = Q K^T
+        //      for this wave's 16 rows and the 16 heads right away
+        if (valid && fresh) {  // the appended row from LDS (bytewise scales: kept an LDS read)
+            const uint4 *src = reinterpret_cast<const uint4 *>(sh.fresh_row + g4 * 128);
 #pragma unroll
-        for (int t = 0; t < 16; t++) acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[t], kb[t], acc, 0, 0, 0);
+            for (int i = 0; i < 8; i++) uu[i] = src[i];
+            const uint8_t *fs = sh.fresh_row + kD + 4 * g4;
+            sc4 = fs[0] | (uint32_t)fs[1] << 8 | (uint32_t)fs[2] << 16 | (uint32_t)fs[3] << 24;
+        }
+        f32x4_t acc = {0.0f, 0.0f, 0.0f, 0.0f};
+        auto kb_fp4 = [&](int t) {
+            const uint32_t wd = word_of(uu[t >> 2], t & 3);
+            const float sc = e8m0_to_f32((sc4 >> (8 * (t >> 2))) & 255u);
+            return join4(__builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(wd, sc, 0),
+                         __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(wd, sc, 1),
+                         __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(wd, sc, 2),
+                         __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(wd, sc, 3));
+        };
+        auto kb_fp8 = [&](int t) {
+            const uint32_t w0d = word_of(uu[t >> 1], 2 * (t & 1)), w1d = word_of(uu[t >> 1], 2 * (t & 1) + 1);
+            const float sc = e8m0_to_f32((sc4 >> (8 * (t >> 2))) & 255u);
+            return join4(__builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w0d, sc, false),
+                         __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w0d, sc, true),
+                         __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w1d, sc, false),
+                         __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w1d, sc, true));
+        };
+        auto put = [&](int t, bf16x8_t kb) {
+            *reinterpret_cast<bf16x8_t *>(&sh.vt[r_loc * kVStride + g4 * 128 + 8 * t]) = kb;
+            acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[t], kb, acc, 0, 0, 0);
+        };
+        // wave-uniform fast paths (every row of the wave a main row, or every row a window
+        // row) keep branches out of the 16 steps
+        if (__all(valid && !fp8)) {
+#pragma unroll
+            for (int t = 0; t < 16; t++) put(t, kb_fp4(t));
+        } else if (__all(valid && fp8)) {
+#pragma unroll
+            for (int t = 0; t < 16; t++) put(t, kb_fp8(t));
+        } else {
+#pragma unroll
+            for (int t = 0; t < 16; t++) {
+                bf16x8_t kb;
+                if (valid && !fp8) kb = kb_fp4(t);
+                else if (valid) kb = kb_fp8(t);
+                else
+#pragma unroll
+                    for (int i = 0; i < 8; i++) kb[i] = (__bf16)0.0f;
+                put(t, kb);
+            }
+        }
         // lane holds S[head 4*g4 + j][row c16 of this wave]
         float sv[4];
 #pragma unroll
@@ -528,50 +553,63 @@ __global__ __launch_bounds__(NS * kStreamThreads, 3 - NS) void k_attn(AttnArgs a
         }
     }
 
-    // ---- stream 1's state joins stream 0's through LDS (stream 1's V tile, 32 KB of it)
+    // ---- the two streams' states join through LDS: stream st finishes column tiles
+    //      4 st .. 4 st + 3 of its waves (ok) and hands the other four (og) to the other
+    //      stream through its own V tile (free now); both arrive at the same M and sum (the
+    //      same two products added, in either order).  The halves are picked by selects, so
+    //      that the LDS reads are issued together.
+    f32x4_t ok[4];
     if (NS == 2) {
     __syncthreads();  // both streams are done with their V tiles
-    float *xo = reinterpret_cast<float *>(shs[NS - 1].vt);
-    if (st == 1) {
+    float *xo_out = reinterpret_cast<float *>(shs[st].vt);
+    const float *xo_in = reinterpret_cast<const float *>(shs[NS - 1 - st].vt);
 #pragma unroll
-        for (int n = 0; n < 8; n++)
-#pragma unroll
-            for (int j = 0; j < 4; j++) xo[(4 * n + j) * kStreamThreads + ts] = o[n][j];
-        if (c16 == 0)
-#pragma unroll
-            for (int j = 0; j < 4; j++) {
-                shs[NS - 1].red_m[wave][4 * g4 + j] = M[j];
-                shs[NS - 1].red_l[wave][4 * g4 + j] = lsum[j];
-            }
-    }
-    __syncthreads();
-    if (st == 0) {
+    for (int n = 0; n < 4; n++)
 #pragma unroll
         for (int j = 0; j < 4; j++) {
-            const float m1 = shs[NS - 1].red_m[wave][4 * g4 + j], l1 = shs[NS - 1].red_l[wave][4 * g4 + j];
-            const float mn = fmaxf(M[j], m1);
-            const float a0 = M[j] == mn ? 1.0f : exp2f((M[j] - mn) * a.scale_log2);
-            const float a1 = m1 == mn ? 1.0f : exp2f((m1 - mn) * a.scale_log2);
-            M[j] = mn;
-            lsum[j] = lsum[j] * a0 + l1 * a1;
-#pragma unroll
-            for (int n = 0; n < 8; n++) o[n][j] = o[n][j] * a0 + xo[(4 * n + j) * kStreamThreads + ts] * a1;
+            ok[n][j] = st ? o[n + 4][j] : o[n][j];
+            xo_out[(4 * n + j) * kStreamThreads + ts] = st ? o[n][j] : o[n + 4][j];
         }
+    if (c16 == 0)
+#pragma unroll
+        for (int j = 0; j < 4; j++) {
+            shs[st].red_m[wave][4 * g4 + j] = M[j];
+            shs[st].red_l[wave][4 * g4 + j] = lsum[j];
+        }
+    __syncthreads();
+    float xi[4][4];
+#pragma unroll
+    for (int n = 0; n < 4; n++)
+#pragma unroll
+        for (int j = 0; j < 4; j++) xi[n][j] = xo_in[(4 * n + j) * kStreamThreads + ts];
+#pragma unroll
+    for (int j = 0; j < 4; j++) {
+        const float m1 = shs[NS - 1 - st].red_m[wave][4 * g4 + j], l1 = shs[NS - 1 - st].red_l[wave][4 * g4 + j];
+        const float mn = fmaxf(M[j], m1);
+        const float a0 = M[j] == mn ? 1.0f : exp2f((M[j] - mn) * a.scale_log2);
+        const float a1 = m1 == mn ? 1.0f : exp2f((m1 - mn) * a.scale_log2);
+        M[j] = mn;
+        lsum[j] = lsum[j] * a0 + l1 * a1;
+#pragma unroll
+        for (int n = 0; n < 4; n++) ok[n][j] = ok[n][j] * a0 + xi[n][j] * a1;
     }
     }
+    // the column tiles this thread writes: NS = 2 tiles 4 st + n of ok, NS = 1 all of o
+    constexpr int NT = NS == 2 ? 4 : 8;
+    auto tile_val = [&](int n) -> const f32x4_t & { return NS == 2 ? ok[n] : o[n]; };
+    const int nt0 = NS == 2 ? 4 * st : 0;
 
-    // ---- one split: normalised output and log-sum-exp; several: the partial state
     if (a.nsplit == 1) {
-        if (st == 0) {
 #pragma unroll
-            for (int n = 0; n < 8; n++) {
-                const int d = 16 * (8 * wave + n) + c16;
+        for (int n = 0; n < NT; n++) {
+            const int d = 16 * (8 * wave + nt0 + n) + c16;
 #pragma unroll
-                for (int j = 0; j < 4; j++) {
-                    const int h = hg * 16 + 4 * g4 + j;
-                    a.out[((int64_t)b * a.Hq + h) * kD + d] = lsum[j] > 0.0f ? o[n][j] * (1.0f / lsum[j]) : 0.0f;
-                }
+            for (int j = 0; j < 4; j++) {
+                const int h = hg * 16 + 4 * g4 + j;
+                a.out[((int64_t)b * a.Hq + h) * kD + d] = lsum[j] > 0.0f ? tile_val(n)[j] * (1.0f / lsum[j]) : 0.0f;
             }
+        }
+        if (st == 0) {
             if (wave == 0 && c16 == 0)
 #pragma unroll
                 for (int j = 0; j < 4; j++)
@@ -580,33 +618,39 @@ __global__ __launch_bounds__(NS * kStreamThreads, 3 - NS) void k_attn(AttnArgs a
         }
         return;
     }
-    if (st == 0) {
+    // The partial state goes out with agent-scope stores, which write through this XCD's L2
+    // to memory.  The last split of (b, hg) to arrive combines them all: every wave waits for
+    // its own partial stores to complete before the barrier, thread 0 then counts the split
+    // in (a relaxed agent-scope atomic), and the last split reads the partials with
+    // agent-scope loads.  Write-through stores and coherent loads replace a release fence and
+    // an acquire, whose L2 write-back and invalidation many splits would otherwise run at once.
+    auto put_coherent = [](float *p, float v) {
+        __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    };
+    {
         const int64_t pbase = ((int64_t)b * a.nsplit + s) * a.Hq + hg * 16;
-        if (wave == 0 && c16 == 0)
+        if (st == 0 && wave == 0 && c16 == 0)
 #pragma unroll
             for (int j = 0; j < 4; j++) {
                 const int64_t i = pbase + 4 * g4 + j;
-                a.part_ml[2 * i] = lsum[j] > 0.0f ? M[j] : -INFINITY;
-                a.part_ml[2 * i + 1] = lsum[j];
+                put_coherent(a.part_ml + 2 * i, lsum[j] > 0.0f ? M[j] : -INFINITY);
+                put_coherent(a.part_ml + 2 * i + 1, lsum[j]);
             }
         if (lsum[0] > 0.0f || lsum[1] > 0.0f || lsum[2] > 0.0f || lsum[3] > 0.0f) {
             float *po = a.part_o + pbase * kD;
 #pragma unroll
-            for (int n = 0; n < 8; n++) {
-                const int d = 16 * (8 * wave + n) + c16;
+            for (int n = 0; n < NT; n++) {
+                const int d = 16 * (8 * wave + nt0 + n) + c16;
 #pragma unroll
-                for (int j = 0; j < 4; j++) po[(4 * g4 + j) * kD + d] = o[n][j];
+                for (int j = 0; j < 4; j++) put_coherent(po + (4 * g4 + j) * kD + d, tile_val(n)[j]);
             }
         }
     }
-    // The last split of (b, hg) to arrive combines them all.  Every wave's stores are
-    // ordered before the barrier; thread 0's agent-scope release then publishes them
-    // device-wide and its acquire (for the last split) covers the other splits' partials.
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
-    int32_t *cnt = a.count + (int64_t)b * a.HG + hg;
+    int32_t *const cnt = a.count + (int64_t)b * a.HG + hg;
     if (tid == 0)
-        shs[0].last = __hip_atomic_fetch_add(cnt, 1, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT) ==
+        shs[0].last = __hip_atomic_fetch_add(cnt, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
                       a.nsplit - 1;
     __syncthreads();
     if (!shs[0].last) return;  // uniform
