@@ -83,7 +83,8 @@ typedef struct csa2_config {
                             same query, the caches hold KH = 1 key per position)     */
 } csa2_config;
 
-/* Byte sizes of the cache layouts (all multiples of 16).
+/* Byte sizes of the cache layouts (multiples of 16, except idx_block_bytes = 136 KH with
+ * d_I = 32: a multiple of 8 when KH is odd).
  *
  * Global caches are paged: physical block `phys` of 8 positions holds
  *   idx_cache + phys*idx_block_bytes : indexer keys of the 8 positions.  With H the key heads

@@ -36,9 +36,8 @@
 namespace csa2 {
 
 constexpr int kStreamThreads = 256;  // one chunk stream: 4 waves of 16 rows
-constexpr int kD = 512;            // latent dim handled by these kernels
+constexpr int kD = kAttnDim;       // latent dim handled by these kernels
 constexpr int kPStride = 64 + 4;   // padded row of the P tile (floats)
-constexpr int kMaxSplits = 512;    // splits a merge handles (k + W <= 32768)
 constexpr int kBufferWord3 = 0x00020000;  // buffer resource word 3 of the gfx9 family
 constexpr int kSc1 = 16;                  // buffer access cache policy: agent scope (sc1)
 
@@ -709,13 +708,12 @@ int sparse_attn(const csa2_config *c, const float *swa_new, const int32_t *new_p
                 float *lse, void *ws, size_t ws_bytes, hipStream_t stream,
                 bool use_scratch = false, bool dry = false) {
     if (!c || !q || !kv_cache || n_blocks <= 0 || !block_table || maxb <= 0 ||
-        batch < 0 || !topk || !topk_len || !out || !lse || (!ws && !use_scratch) || c->topk <= 0 ||
-        c->swa_window < 0 || c->n_q_heads <= 0 || c->kv_dim <= 0)
+        batch < 0 || !topk || !topk_len || !out || !lse || (!ws && !use_scratch))
         return CSA2_ERR_INVALID;
+    if (const int st = attn_cfg_status(c); st == CSA2_ERR_INVALID) return st;
     if (c->swa_window > 0 && (!swa_cache || C < c->swa_window)) return CSA2_ERR_INVALID;
     if (swa_new && (!new_pos || !swa_out || C <= 0)) return CSA2_ERR_INVALID;
-    if (c->kv_dim != kD || c->n_q_heads % 16 || c->n_q_heads > 128) return CSA2_ERR_UNSUPPORTED;
-    if (attn_splits(c->topk, c->swa_window) > kMaxSplits) return CSA2_ERR_UNSUPPORTED;
+    if (const int st = attn_cfg_status(c)) return st;
     const AttnPlan plan = attn_plan(batch, c->n_q_heads, c->topk, c->swa_window);
     const int nsplit = plan.nsplit;
     // (the plan splits only batches of fewer than kAttnCounters (sequence, head group) pairs)

@@ -82,6 +82,20 @@ struct WsAttn {
 };
 __host__ __device__ inline int attn_splits(int k, int W) { return (k + W + kAttnRows - 1) / kAttnRows; }
 
+constexpr int kAttnDim = 512;        // latent dim of the attention kernels
+constexpr int kAttnMaxSplits = 512;  // 64-row chunks a merge handles (k + W <= 32768)
+
+// Status of cfg's attention shape: CSA2_ERR_INVALID for values out of range,
+// CSA2_ERR_UNSUPPORTED for a shape without a kernel (the attention calls and the attention
+// workspace query both apply it).
+inline int attn_cfg_status(const csa2_config *c) {
+    if (!c || c->topk <= 0 || c->swa_window < 0 || c->n_q_heads <= 0 || c->kv_dim <= 0)
+        return CSA2_ERR_INVALID;
+    if (c->kv_dim != kAttnDim || c->n_q_heads % 16 || c->n_q_heads > 128) return CSA2_ERR_UNSUPPORTED;
+    if (attn_splits(c->topk, c->swa_window) > kAttnMaxSplits) return CSA2_ERR_UNSUPPORTED;
+    return CSA2_OK;
+}
+
 // Row chunks of 64 per workgroup stream.  A batch of at least 512 (sequence, head group)
 // pairs fills the chip with one-stream workgroups (splits up to about 1024 workgroups);
 // smaller batches take two-stream workgroups, each owning cps consecutive chunks (cps even),

@@ -1207,8 +1207,7 @@ extern "C" int csa2_workspace_bytes(const csa2_config *c, int op, int32_t batch,
         return CSA2_OK;
     }
     if (op == CSA2_OP_SPARSE_ATTN) {
-        if (c->n_q_heads <= 0 || c->kv_dim <= 0 || c->topk <= 0 || c->swa_window < 0)
-            return CSA2_ERR_INVALID;
+        if (const int st = attn_cfg_status(c)) return st;
         *bytes = ws_attn(batch, c->n_q_heads, c->kv_dim,
                          attn_plan(batch, c->n_q_heads, c->topk, c->swa_window).nsplit).total;
         return CSA2_OK;
