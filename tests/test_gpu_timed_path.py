@@ -219,6 +219,7 @@ def test_scan_with_64bit_offsets(H, d):
     (4, 64, [700, 5000, 64, 1, 9], True),       # ragged batch
     (8, 128, [3000, 517, 9], True),             # the global append runs before the scan
     (1, 32, [300, 17], False),                  # one head, no main-KV append
+    (4, 64, [150000, 3000], True),              # the two-phase Full selection (3 gather WGs)
 ])
 def test_layer_calls_equal_the_separate_calls(H, d, ctx, with_lat):
     """csa2_decode_full_layer / _reindex_layer / _reuse_layer == the separate calls they
