@@ -366,8 +366,8 @@ int csa2_decode_reuse_layer(const csa2_config *cfg, const float *swa_row, const 
  * leaves them at zero again.  All calls on one GPU share the array, so calls that overlap
  * on one GPU (other streams, other threads) race: serialise them.  A shape whose partials
  * exceed the array (csa2_workspace_bytes(CSA2_OP_SPARSE_ATTN) > 16 MiB; with k = 512 and
- * W = 128: 16 heads at batch 102..1023, 64 heads at batch 26..255) returns CSA2_ERR_SCRATCH
- * and launches nothing. */
+ * W = 128: 16 heads at batch 512..1023, 64 heads at 128..255, 128 heads at 64..127) returns
+ * CSA2_ERR_SCRATCH and launches nothing. */
 int csa2_sparse_attn_noalloc(const csa2_config *cfg, const uint16_t *q, const uint8_t *kv_cache,
                              int64_t n_blocks, const int32_t *block_table, int32_t maxb,
                              const uint8_t *swa_cache, int32_t C, const int32_t *ctx_len,

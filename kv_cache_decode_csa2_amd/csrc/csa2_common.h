@@ -98,8 +98,10 @@ inline int attn_cfg_status(const csa2_config *c) {
 
 // Row chunks of 64 per workgroup stream.  A batch of at least 512 (sequence, head group)
 // pairs fills the chip with one-stream workgroups (splits up to about 1024 workgroups);
-// smaller batches take two-stream workgroups, each owning cps consecutive chunks (cps even),
-// about 512 of them.
+// smaller batches take two-stream workgroups, each owning up to cps chunks (cps even).  A
+// two-stream workgroup holds nearly all of a CU's LDS, so the splits aim at one wave of them
+// on the 256 CUs: more would run as a second wave, which costs more than the extra chunks
+// each workgroup takes instead.
 struct AttnPlan {
     int nsplit, cps, ns;  // splits, chunks per split, chunk streams per workgroup
 };
@@ -108,7 +110,7 @@ __host__ __device__ inline AttnPlan attn_plan(int B, int Hq, int k, int W) {
     const int groups = (B > 0 ? B : 1) * (Hq / 16 > 0 ? Hq / 16 : 1);
     const int ns = groups >= 512 ? 1 : 2;
     const int units = (nchunk + ns - 1) / ns;  // chunks, or chunk pairs
-    int sp = ((ns == 1 ? 1024 : 512) + groups - 1) / groups;
+    int sp = ns == 1 ? (1024 + groups - 1) / groups : 256 / groups;
     sp = sp < 1 ? 1 : (sp > units ? units : sp);
     const int ups = (units + sp - 1) / sp;  // units per split
     return AttnPlan{(units + ups - 1) / ups, ns * ups, ns};

@@ -140,7 +140,7 @@ int main() {
     expect(csa2_sparse_attn(&c, u16, u8, 8, i32, 1, u8, 256, i32, 8, i32, i32, f32, f32, p, 64, s), {WSE, INV}, "attn ws");
     expect(csa2_sparse_attn_append(&c, f32, nullptr, u16, u8, 8, i32, 1, u8, 256, i32, 1, i32, i32, f32, f32, p, 1 << 20, s), {INV}, "attn_append null");
     expect(csa2_sparse_attn_prefill(&c, u16, u8, 8, i32, 16, u8, 128, 0, 8, i32, i32, f32, f32, p, 1 << 20, s), {INV}, "attn_prefill ring");
-    expect(csa2_sparse_attn_noalloc(&c, u16, u8, 8, i32, 1, u8, 256, i32, 500, i32, i32, f32, f32, s), {CSA2_ERR_SCRATCH, INV}, "noalloc scratch");
+    expect(csa2_sparse_attn_noalloc(&c, u16, u8, 8, i32, 1, u8, 256, i32, 600, i32, i32, f32, f32, s), {CSA2_ERR_SCRATCH}, "noalloc scratch");
     // fused layer calls
     expect(csa2_decode_full_layer(&c, f32, f32, f32, f32, f32, u16, u8, u8, 8, i32, 1, u8, 256, i32, 1,
                                   i32, i32, i32, i32, f32, f32, p, 0, p, 1 << 20, s), {WSE, INV}, "full_layer ws");

@@ -151,12 +151,12 @@ def test_block_transfer_and_fused_append_host_errors():
 
 def test_noalloc_attention_rejects_shapes_beyond_its_scratch():
     """csa2_sparse_attn_noalloc checks the shape against its 16 MiB static scratch on the host
-    before any HIP call: 16 heads at batch 200 (three splits of 16 x 512 fp32 partials per
-    sequence, about 20 MB) is refused; argument errors come first."""
+    before any HIP call: 16 heads at batch 600 (two splits of 16 x 512 fp32 partials per
+    sequence, about 39 MB) is refused; argument errors come first."""
     lib = k.load()
     f = C.c_void_p(256)
     c = k.config(4, 64, 512, 16, 128, 2048, 512, 0.044)
-    st = lib.csa2_sparse_attn_noalloc(C.byref(c), f, f, 1, f, 8, f, 128, f, 200, f, f, f, f, None)
+    st = lib.csa2_sparse_attn_noalloc(C.byref(c), f, f, 1, f, 8, f, 128, f, 600, f, f, f, f, None)
     assert st == k.CSA2_ERR_SCRATCH
     assert "static scratch" in k.status_str(st)
     st = lib.csa2_sparse_attn_noalloc(C.byref(c), f, f, 1, f, 8, f, 64, f, 200, f, f, f, f, None)
