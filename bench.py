@@ -295,13 +295,19 @@ class PrefillBench:
         self.k.csa2_index_prefill_scan(self.cfg, self.qc, self.qs, self.w, self.q_pos0, self.idx[r],
                                        self.g.n_blocks, self.row, self.ws)
 
+    def index(self, r=0):
+        k, g, c = self.k, self.g, self.cfg
+        k.csa2_index_prefill(c, self.qc, self.qs, self.w, self.q_pos0, self.idx[r], g.n_blocks, self.row,
+                             self.pool, self.pool_len, self.topk, self.topk_len, self.ws)
+
 
 def prefill_work(wl, layout):
-    """Algorithmic work of the prefill indexer's scoring kernel: causal (query, position)
-    pairs, the FP4 flops of their scores, and the bytes the method must move -- every key
-    once plus the selection outputs (pool and top-k of every query).  The kernel's own
-    intermediate writes (an exact score per causal pair, block and group maxima) are a
-    design choice, counted apart as `design_bytes`."""
+    """Algorithmic work of the prefill indexer's scoring: causal (query, position) pairs, the
+    FP4 flops of their scores, and the bytes the method must move -- every key once plus the
+    selection outputs (pool and top-k of every query).  The kernels' own intermediate writes
+    are a design choice, counted apart as `design_bytes`: one pass writes an exact score per
+    causal pair (at most 16 queries), or the maxima pass writes block and group maxima and the
+    rescoring pass the scores of about k flagged blocks per query (8 scores each)."""
     n_q, L = wl.n_q, wl.ctx[0]
     t = np.arange(L - n_q, L, dtype=np.int64)
     pairs = int((t + 1).sum())
@@ -310,7 +316,8 @@ def prefill_work(wl, layout):
     alu = 2 * pairs * wl.H_I  # ReLU + fma per (pair, head)
     keys = L * (layout.idx_block_bytes // 8)
     outputs = n_q * (wl.K_blk + wl.k + 2) * 4
-    design = 4 * pairs + 4 * blocks + 4 * ((blocks + 7) // 8)
+    maxima = 4 * blocks + 4 * ((blocks + 7) // 8)
+    design = 4 * pairs + maxima if n_q <= 16 else maxima + n_q * wl.k * 8 * 4
     return dict(pairs=pairs, flops=flops, alu=alu, bytes=keys + outputs, key_bytes=keys,
                 output_bytes=outputs, design_bytes=design)
 
@@ -334,7 +341,7 @@ def main_prefill(a, wl):
     R = bench.R
     if a.counters:
         for i in range(3):
-            bench.scan(i % R)
+            bench.step(i % R)
         torch.cuda.synchronize()
         calibration_copy(a.calib_mb)
         return
@@ -361,6 +368,11 @@ def main_prefill(a, wl):
     timed(lambda i: sg.replay(), 1)
     scan_ms = timed(lambda i: sg.replay(), 3) / reps
     sec = scan_ms / 1e3
+    # the whole indexer call (the scoring pass, the pool selection, for more than 16 queries the
+    # rescoring of the flagged blocks, the top-k selection)
+    ig = capture(lambda: [bench.index(i % R) for i in range(reps)])
+    timed(lambda i: ig.replay(), 1)
+    index_ms = timed(lambda i: ig.replay(), 3) / reps
     fr = {"hbm": pw["bytes"] / sec / 1e9 / HBM_PEAK_GBS,
           "mfma": pw["flops"] / sec / 1e12 / MFMA_FP4_PEAK_TFLOPS,
           "alu": pw["alu"] / sec / 1e12 / ALU_PEAK_TOPS}
@@ -389,8 +401,12 @@ def main_prefill(a, wl):
                      "frac": round(fr[bound], 4), "traffic": traffic,
                      "traffic_over_algorithmic": (round(traffic / pw["bytes"], 2)
                                                   if traffic else None),
-                     "algorithmic_bytes": pw["bytes"], "kernel": "k_prefill",
+                     "algorithmic_bytes": pw["bytes"],
+                     "kernel": "k_prefill" if spec else "k_prefill maxima pass",
                      "kernel_us": round(scan_ms * 1e3, 2),
+                     "index_us": round(index_ms * 1e3, 2),
+                     "index_frac": round({"hbm": pw["bytes"] / (index_ms / 1e3) / 1e9 / HBM_PEAK_GBS,
+                                          "mfma": pw["flops"] / (index_ms / 1e3) / 1e12 / MFMA_FP4_PEAK_TFLOPS}[bound], 4),
                      "fractions": {k_: round(v, 4) for k_, v in fr.items()}, "work": pw},
         "cpu_baseline": None,
     }
@@ -586,6 +602,25 @@ def counter_kind(wl):
     return "spec" if wl.name.startswith("spec") else ("prefill" if wl.n_q else "decode")
 
 
+def _targs(kname, name):
+    """Template arguments of a kernel name that starts with kname ('k_scan<', 'k_prefill<')."""
+    return name.split(kname, 1)[1].split(">", 1)[0] if kname in name else ""
+
+
+def _counted(kind, kname, name):
+    """The dispatches a counter summary covers: the Full-mode scan (not the Reindex rescoring,
+    k_scan<H, G, true, ...>); the prefill chunk's maxima pass (k_prefill<H, G, false, 1>); the
+    verification step's one-pass kernel (k_prefill<H, G, true, 0>)."""
+    if kname not in name:
+        return False
+    t = _targs(kname, name)
+    if kind == "decode":
+        return ", true," not in t[:12]
+    if kind == "prefill":
+        return t.endswith("false, 1")
+    return t.endswith("true, 0")
+
+
 def counter_summary(a, wl):
     """HBM bytes per launch of the dominant kernel from two rocprofv3 --pmc runs (FETCH_SIZE,
     WRITE_SIZE; KiB per dispatch), each scaled by what the same counter reads for the
@@ -598,8 +633,11 @@ def counter_summary(a, wl):
     for ctr in ("FETCH_SIZE", "WRITE_SIZE"):
         with open(os.path.join(a.counter_summary, f"{prefix}_{ctr}_counter_collection.csv")) as f:
             rows = [r for r in csv.DictReader(f) if r["Counter_Name"] == ctr]
-        kern = [float(r["Counter_Value"]) for r in rows
-                if kname in r["Kernel_Name"] and ", true," not in r["Kernel_Name"].split(kname)[1][:12]]
+        kern = [float(r["Counter_Value"]) for r in rows if _counted(kind, kname, r["Kernel_Name"])]
+        if kind == "prefill":
+            resc = [float(r["Counter_Value"]) for r in rows
+                    if kname in r["Kernel_Name"] and _targs(kname, r["Kernel_Name"]).endswith(", 2")]
+            raw["rescore_" + ctr] = sum(resc) / max(1, len(resc))
         copies = [float(r["Counter_Value"]) for r in rows if "copyBuffer" in r["Kernel_Name"]]
         if not kern or not copies:
             raise SystemExit(f"{ctr}: no {kname} or copy dispatches in {a.counter_summary}")
@@ -623,6 +661,10 @@ def counter_summary(a, wl):
                         "write_kib_raw": raw["WRITE_SIZE"][2], "fetch_factor": round(ff, 4),
                         "write_factor": round(wf, 4)},
         "fetch_bytes": int(fetch), "write_bytes": int(write), "bytes_per_launch": int(fetch + write),
+        **({"rescoring_pass": {"kernel": "k_prefill<H, G, false, 2>",
+                               "fetch_bytes": int(raw["rescore_FETCH_SIZE"] * 1024.0 * ff),
+                               "write_bytes": int(raw["rescore_WRITE_SIZE"] * 1024.0 * wf)}}
+           if kind == "prefill" else {}),
         "algorithmic_bytes": int(alg),
         "source_sha256": hashlib.sha256(open(src_path, "rb").read()).hexdigest(),
         "source": f"kv_cache_decode_csa2_amd/csrc/{src_name}",

@@ -281,8 +281,12 @@ int csa2_sparse_attn_append(const csa2_config *cfg, const float *swa_rows, const
                             float *lse, void *ws, size_t ws_bytes, hipStream_t stream);
 
 /* csa2_index_prefill in two phases on the same workspace and arguments: the scoring (key
- * spans + the matrix-core kernel: position scores, block and group maxima of every query)
- * and the per-query selection.  prefill == prefill_scan followed by prefill_finish. */
+ * spans + the matrix-core kernel: block and group maxima of every query, and with at most
+ * 16 queries every causal position score) and the per-query selection (with more than 16
+ * queries: the pools, then a second matrix-core pass that recomputes the position scores of
+ * the pool blocks whose maximum reaches the k-th largest maximum of the pool -- the only
+ * blocks the top-k can draw from -- then the top-k).  prefill == prefill_scan followed by
+ * prefill_finish. */
 int csa2_index_prefill_scan(const csa2_config *cfg, const uint8_t *q_codes,
                             const uint8_t *q_scales, const float *w, int32_t q_pos0,
                             int32_t n_q, const uint8_t *idx_cache, int64_t n_blocks,

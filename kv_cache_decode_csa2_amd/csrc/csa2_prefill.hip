@@ -18,12 +18,21 @@
 // The epilogue (ReLU, fma chain over heads in head order, causal mask, block and group
 // maxima) runs on the vector ALUs and writes what the Full-mode selection reads.
 //
+// With more than 16 queries no position score is stored by the scoring pass: it keeps the
+// block and group maxima, the selection takes the pools from them, and a second pass over
+// the same tiles recomputes only the scores the top-k can need (the pool blocks whose
+// maximum reaches the k-th largest pool block maximum, about k per query), skipping every
+// 16 x 16 tile that holds none of them.
+//
 // Kernels:
-//   k_prefill_span  per logical block: the largest exponent span of any key head vector.
-//   k_prefill<H,G>  a workgroup = 128 queries x 2048 positions; keys staged through LDS in
-//                   stages of 8 blocks (double-buffered), queries and head weights held in
-//                   registers, 4 waves x 2 query tiles of 16.
-//   k_select        (shared with Full mode) one workgroup per query.
+//   k_prefill_span    per logical block: the largest exponent span of any key head vector.
+//   k_prefill<H,G,.,MODE>  a workgroup = 128 queries x 2048 positions; keys staged through
+//                     LDS in stages of 8 blocks (double-buffered), queries and head weights
+//                     held in registers, 4 waves x 2 query tiles of 16.  MODE: scores and
+//                     maxima (at most 16 queries), maxima only, or the flagged rescoring.
+//   k_select          (at most 16 queries, shared with Full mode) one workgroup per query;
+//   k_select_pf_pool / k_select_pf_topk  (more queries) the two selection phases around
+//                     the rescoring pass.
 #include <algorithm>
 
 #include "csa2_common.h"
@@ -59,6 +68,7 @@ struct PrefillArgs {
     float *bscore;         // group-major: (q, j) at ((j/8)*n_q + q)*8 + j%8
     float *gmax;           // [n_q][ngmax]
     int32_t ngmax;
+    uint32_t *need;        // flags of the blocks to rescore: 8 words per (chunk, query)
     int32_t n_qt, n_pc;    // query tiles, position chunks
 };
 
@@ -144,26 +154,61 @@ struct PfStage {
 
 // Block-table entries and key spans of a workgroup's position chunk, staged once in LDS so
 // that no per-stage lookup waits on global memory.
-struct PfMeta {
+struct __align__(16) PfMeta {
     int32_t phys[kPfChunkBlocks];  // physical block, -1 when absent
     uint8_t kspan[kPfChunkBlocks];
 };
 
 typedef __attribute__((address_space(3))) void *lds_ptr_t;
 
+// Byte offset, inside a block's codes, of the 16-byte chunk that lane `lane` of a 1 KB LDS
+// DMA row fetches: LDS slot c holds global chunk (c/H)*H + ((c%H) ^ ((c/H) mod H)); for a row
+// starting at a multiple of 64 slots, (c/H) mod H depends on the lane only.
+template <int H>
+__device__ __forceinline__ uint32_t pf_swizzle16(int lane) {
+    const int hs = lane % H, row = lane / H;
+    return (uint32_t)((lane - hs + (hs ^ (row & (H - 1)))) * 16);
+}
+
 // Stage the keys of blocks jrel .. jrel+7 of the chunk into dst with LDS DMA
-// (global_load_lds): one instruction moves 64 lanes x 16 bytes into 1 KB of consecutive LDS,
-// lane i to byte 16*i, so each lane fetches the global chunk that the swizzled layout puts
-// at its slot.  Padding slots fetch chunk 0 of a block.  Absent blocks read physical block 0.
+// (global_load_lds): one instruction moves 64 lanes x 16 (or 4) bytes into 1 KB (256 B) of
+// consecutive LDS, lane i to byte 16*i (4*i), so each lane fetches the global chunk that the
+// swizzled layout puts at its slot.  Absent blocks read physical block 0.
+// When a block's codes and scale bytes are whole rows (at least 8 heads x 32-groups), every
+// row lies inside one block: its physical block is wave-uniform (a scalar base) and each lane
+// adds a fixed offset (sw16, from pf_swizzle16).  Otherwise rows span blocks and each lane
+// looks its block up.
 template <int H, int G>
 __device__ __forceinline__ void pf_dma(const PrefillArgs &a, const PfMeta &meta, int jrel,
-                                       PfStage<H, G> &dst) {
+                                       PfStage<H, G> &dst, uint32_t sw16) {
     using S = PfStage<H, G>;
     constexpr int BYTES = S::CODES + S::SCB;
     constexpr int CPB = S::CODES / 16;  // code chunks per block
     constexpr int SPB = S::BSTR / 16;   // LDS slots per staged block
     constexpr int DPB = S::SCB / 4;     // scale dwords per block
-    const int lane = lane_id(), wave = (int)threadIdx.x / kWave;
+    const int lane = lane_id();
+    const int wave = __builtin_amdgcn_readfirstlane((int)threadIdx.x / kWave);
+    if constexpr (S::CODES % 1024 == 0 && S::SCB % 256 == 0) {
+        // wave w stages blocks 2w and 2w + 1 of the stage, all of their rows
+        constexpr int CR = S::CODES / 1024, SR = S::SCB / 256;
+        static_assert(kPfStageBlocks == 2 * kPfWaves, "two blocks per wave");
+        const int2 ph2 = *reinterpret_cast<const int2 *>(&meta.phys[jrel + 2 * wave]);
+        const int32_t phv[2] = {__builtin_amdgcn_readfirstlane(ph2.x), __builtin_amdgcn_readfirstlane(ph2.y)};
+#pragma unroll
+        for (int i = 0; i < 2; i++) {
+            const int blk = 2 * wave + i;
+            const uint8_t *base = a.idx_cache + (int64_t)(phv[i] >= 0 ? phv[i] : 0) * BYTES;
+#pragma unroll
+            for (int k = 0; k < CR; k++)
+                __builtin_amdgcn_global_load_lds(base + k * 1024 + sw16,
+                                                 (lds_ptr_t)(dst.codes + blk * S::BSTR + k * 1024), 16, 0, 0);
+#pragma unroll
+            for (int k = 0; k < SR; k++)
+                __builtin_amdgcn_global_load_lds(base + S::CODES + k * 256 + lane * 4,
+                                                 (lds_ptr_t)(dst.scales + (blk * S::SCB + k * 256) / 4), 4, 0, 0);
+        }
+        return;
+    }
 #pragma unroll
     for (int r = wave; r < S::SLOTS / kWave; r += kPfWaves) {
         const int slot = kWave * r + lane;
@@ -216,6 +261,19 @@ __device__ __forceinline__ float relu0(float x) { return __int_as_float(max(__fl
 // Maximum of scores (finite or -inf, never NaN) without the IEEE-mode canonicalisation.
 __device__ __forceinline__ float smax(float a, float b) { return __builtin_elementwise_maximum(a, b); }
 
+// max(x, x of lane ^ 16) in the vector unit: the row swap of v_permlane16_swap leaves x of
+// lanes l and l ^ 16 in the two results of every lane.
+__device__ __forceinline__ float smax_xor16(float x) {
+    const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return smax(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+
+// max(x, x of lane ^ 32), likewise with v_permlane32_swap.
+__device__ __forceinline__ float smax_xor32(float x) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return smax(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+
 // Query tile held by a lane: column q (16 queries), group g = lane / 16 of every head.
 template <int H>
 struct PfQuery {
@@ -224,14 +282,19 @@ struct PfQuery {
     float w[H];
 };
 
-template <int H, int G, bool SMALL>
+// MODE: kPfAll, scores and maxima (at most 16 queries); kPfMaxima, block and group maxima
+// only; kPfRescore, the position scores of the flagged (query, block) pairs only, computed
+// for the 16 x 16 tiles holding one.
+constexpr int kPfAll = 0, kPfMaxima = 1, kPfRescore = 2;
+
+template <int H, int G, bool SMALL, int MODE>
 __global__ __launch_bounds__(kPfThreads, 2) void k_prefill(PrefillArgs a) {
     using S = PfStage<H, G>;
     // two stage buffers as distinct objects, so that the reads of one are known not to
     // alias the DMA into the other
     __shared__ S stA, stB;
     __shared__ PfMeta meta;
-
+    __shared__ uint4 nd[MODE == kPfRescore ? kPfQT * 2 : 1];  // flags of the tile's queries
     // workgroup -> (position chunk, query tile); the workgroups of one chunk are consecutive
     // on one XCD (dispatch places workgroup i on XCD i % 8) so its keys are fetched once
     const int T = a.n_qt * a.n_pc;
@@ -243,7 +306,18 @@ __global__ __launch_bounds__(kPfThreads, 2) void k_prefill(PrefillArgs a) {
     const int Jbeg = pc * kPfChunkBlocks;
     // blocks this tile can see: j*8 <= q_pos0 + qlast
     const int Jend = min(min(a.nb, Jbeg + kPfChunkBlocks), (a.q_pos0 + qlast) / kBlk + 1);
-    if (Jbeg >= Jend) return;  // uniform per workgroup
+    if (Jbeg >= Jend) return;  // uniform per workgroup (no query of the tile sees the chunk)
+    // the flags of this (chunk, query tile): cleared by the maxima pass, read by the
+    // rescoring pass (thread i: query Q0 + i/2, words 4*(i%2) .. +3)
+    if constexpr (MODE != kPfAll) {
+        const int qi = Q0 + (int)threadIdx.x / 2;
+        uint4 *fw = reinterpret_cast<uint4 *>(a.need + ((int64_t)pc * a.n_q + qi) * 8) + threadIdx.x % 2;
+        if constexpr (MODE == kPfMaxima) {
+            if (qi < a.n_q) *fw = make_uint4(0u, 0u, 0u, 0u);
+        } else {
+            nd[threadIdx.x] = qi < a.n_q ? *fw : make_uint4(0u, 0u, 0u, 0u);
+        }
+    }
     const int nstage = (Jend - Jbeg + kPfStageBlocks - 1) / kPfStageBlocks;
 
     const int lane = lane_id(), wave = (int)threadIdx.x / kWave;
@@ -261,7 +335,8 @@ __global__ __launch_bounds__(kPfThreads, 2) void k_prefill(PrefillArgs a) {
         else meta.kspan[i] = j < Jend ? a.kspan[j] : (uint8_t)0;
     }
     __syncthreads();
-    pf_dma<H, G>(a, meta, 0, stA);
+    const uint32_t sw16 = pf_swizzle16<H>(lane_id());
+    pf_dma<H, G>(a, meta, 0, stA, sw16);
 
     // At most 16 queries (a verification step): every wave takes the one query tile and a
     // quarter of each stage's positions (16-position tile u = wave) instead of a query tile
@@ -270,6 +345,10 @@ __global__ __launch_bounds__(kPfThreads, 2) void k_prefill(PrefillArgs a) {
     constexpr bool small = SMALL;  // the host sets it when n_q <= 16
     const int u_beg = small ? wave : 0, u_end = small ? wave + 1 : kPfStageBlocks / 2;
     __shared__ float sm_gm[2][kPfWaves][16];
+    // group maxima of the current run of 8 stages (lane g: stages g and 4 + g of the run)
+    float gbuf[kPfNQ][2];
+#pragma unroll
+    for (int jq = 0; jq < kPfNQ; jq++) gbuf[jq][0] = gbuf[jq][1] = -INFINITY;
     // queries of this wave's tiles, their scale spans and causal limits
     PfQuery<H> Q[kPfNQ];
     int qspan[kPfNQ], qb[kPfNQ];
@@ -314,10 +393,39 @@ __global__ __launch_bounds__(kPfThreads, 2) void k_prefill(PrefillArgs a) {
         float *ps_stage = a.pscore + (int64_t)J0 * a.n_q * kBlk;
         float *bs_stage = a.bscore + (int64_t)(J0 >> 3) * a.n_q * kBlk;
         float gm[kPfNQ];
+        // maxima pass: the block maxima of the stage, one per 16-position tile (lane g < 2:
+        // block 2u, else 2u + 1), stored once at the end of the stage (32 contiguous bytes
+        // per query, so no line of the array is written back part-filled)
+        f32x4_t bmv[kPfNQ];
 #pragma unroll
-        for (int jq = 0; jq < kPfNQ; jq++) gm[jq] = -INFINITY;
+        for (int jq = 0; jq < kPfNQ; jq++) {
+            gm[jq] = -INFINITY;
+            bmv[jq] = f32x4_t{-INFINITY, -INFINITY, -INFINITY, -INFINITY};
+        }
+        // rescoring: the stage's 8 block flags of the lane's query (own) and of any query of
+        // the 16-query tile (anyf, wave-uniform)
+        uint32_t own[kPfNQ], anyf[kPfNQ];
+        if constexpr (MODE == kPfRescore) {
+            const uint32_t *ndw = reinterpret_cast<const uint32_t *>(nd);
+#pragma unroll
+            for (int jq = 0; jq < kPfNQ; jq++) {
+                const int ql = qb[jq] - Q0 + col;  // < kPfQT
+                own[jq] = (ndw[ql * 8 + (sidx >> 2)] >> (8 * (sidx & 3))) & 0xffu;
+                uint32_t x = own[jq];
+#pragma unroll
+                for (int o = 1; o < 16; o <<= 1) x |= __shfl_xor(x, o, kWave);
+                anyf[jq] = __builtin_amdgcn_readfirstlane(x);
+            }
+        }
 #pragma unroll 1
         for (int u = u_beg; u < u_end; u++) {  // 16-position tiles
+            if constexpr (MODE == kPfMaxima) {
+#pragma unroll
+                for (int jq = 0; jq < kPfNQ; jq++) bmv[jq] = f32x4_t{bmv[jq][1], bmv[jq][2], bmv[jq][3], -INFINITY};
+            }
+            if constexpr (MODE == kPfRescore) {
+                if (!(((anyf[0] | anyf[kPfNQ - 1]) >> (2 * u)) & 3u)) continue;  // nothing flagged
+            }
             const int p0 = (J0 + 2 * u) * kBlk;
             // this lane's key row: position p0 + col, group g
             const int bi = 2 * u + (col >> 3), s = col & 7;
@@ -352,12 +460,84 @@ __global__ __launch_bounds__(kPfThreads, 2) void k_prefill(PrefillArgs a) {
             const uint32_t ksp_w = u < 2 ? ks8.x : ks8.y;
             const uint32_t kspan_t = max((ksp_w >> (16 * (u & 1))) & 0xffu, (ksp_w >> (16 * (u & 1) + 8)) & 0xffu);
             const bool pres0 = (present >> (2 * u)) & 1u, pres1 = (present >> (2 * u + 1)) & 1u;
+            // query tile jq takes part in this position tile (uniform)
+            auto active = [&](int jq) {
+                if (qb[jq] >= a.n_q) return false;                                  // no queries
+                if (p0 > a.q_pos0 + min(qb[jq] + 15, a.n_q - 1)) return false;      // all masked
+                if constexpr (MODE == kPfRescore) return ((anyf[jq] >> (2 * u)) & 3u) != 0u;  // flagged
+                return true;
+            };
+            // causal / presence mask, block maxima and stores of tile jq's scores
+            auto tail = [&](int jq, f32x4_t sc) {
+                // lane: query qb + col, positions p0 + 4*g + e
+                const int tmin = a.q_pos0 + qb[jq];
+                const int q = qb[jq] + col;
+                const int t = a.q_pos0 + q;
+                const int pl = p0 + 4 * g;
+                const bool pres = g < 2 ? pres0 : pres1;
+                if (p0 + 15 > tmin || !pres0 || !pres1) {
+#pragma unroll
+                    for (int e = 0; e < 4; e++)
+                        if (!pres || pl + e > t) sc[e] = -INFINITY;
+                }
+                float m = 0.f;
+                if constexpr (MODE != kPfRescore) {
+                    m = smax_xor16(smax(smax(sc[0], sc[1]), smax(sc[2], sc[3])));
+                    gm[jq] = smax(gm[jq], m);
+                }
+                // uniform stage bases, 32-bit lane offsets (< 8 blocks of n_q rows); lanes g and
+                // g ^ 1 hold the same block maximum and store it to the same address
+                const uint32_t po = (uint32_t)(((2 * u + (g >> 1)) * a.n_q + q) * kBlk + 4 * (g & 1));
+                const uint32_t bo = (uint32_t)(q * kBlk + 2 * u + (g >> 1));
+                if constexpr (MODE == kPfMaxima) {
+                    bmv[jq][3] = m;
+                } else if (qb[jq] + 15 < a.n_q && J0 + 2 * u + 1 < a.nb) {  // every lane's (query, block) exists
+                    if (MODE == kPfAll || ((own[jq] >> (2 * u + (g >> 1))) & 1u))
+                        *reinterpret_cast<f32x4_t *>(ps_stage + po) = sc;
+                    if (MODE == kPfAll) bs_stage[bo] = m;
+                } else if (q < a.n_q && J0 + 2 * u + (g >> 1) < a.nb) {
+                    // blocks past nb (the tile's second block when nb is odd) are not stored:
+                    // the score arrays hold blocks 0 .. nb - 1 only
+                    if (MODE == kPfAll || ((own[jq] >> (2 * u + (g >> 1))) & 1u))
+                        *reinterpret_cast<f32x4_t *>(ps_stage + po) = sc;
+                    if (MODE == kPfAll) bs_stage[bo] = m;
+                }
+            };
+            if constexpr (kPfNQ == 2 && H % 4 == 0) {
+                // both query tiles on the one-product path: the second tile's products are
+                // issued between the first tile's epilogue steps, so the matrix core works
+                // while the vector unit runs the ReLU / fma chain
+                if (active(0) && active(1) && (int)kspan_t + max(qspan[0], qspan[1]) <= kSpanExact) {
+                    f32x4_t d0[H], d1[H];
+                    f32x4_t sc0 = {0.f, 0.f, 0.f, 0.f}, sc1 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                    for (int h = 0; h < H; h++) d0[h] = mfma_pick(kc[h], Q[0].c[h], ksc[h], Q[0].s[h / 4], h % 4);
+#pragma unroll
+                    for (int h = 0; h < H; h++) {
+                        d1[h] = mfma_pick(kc[h], Q[1].c[h], ksc[h], Q[1].s[h / 4], h % 4);
+#pragma unroll
+                        for (int e = 0; e < 4; e++) sc0[e] = __builtin_fmaf(Q[0].w[h], relu0(d0[h][e]), sc0[e]);
+                    }
+#pragma unroll
+                    for (int h = 0; h < H; h++)
+#pragma unroll
+                        for (int e = 0; e < 4; e++) sc1[e] = __builtin_fmaf(Q[1].w[h], relu0(d1[h][e]), sc1[e]);
+                    __builtin_amdgcn_sched_group_barrier(0x008, H, 0);
+#pragma unroll
+                    for (int h = 0; h < H; h++) {
+                        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                        __builtin_amdgcn_sched_group_barrier(0x002, 8, 0);
+                    }
+                    // both chains end here, before the stores' branches (nothing sinks below)
+                    asm volatile("" : "+v"(sc0), "+v"(sc1));
+                    tail(0, sc0);
+                    tail(1, sc1);
+                    continue;
+                }
+            }
 #pragma unroll
             for (int jq = 0; jq < kPfNQ; jq++) {
-                if (qb[jq] >= a.n_q) continue;                       // no queries (uniform)
-                const int tmin = a.q_pos0 + qb[jq];
-                const int tmax = a.q_pos0 + min(qb[jq] + 15, a.n_q - 1);
-                if (p0 > tmax) continue;                             // all masked (uniform)
+                if (!active(jq)) continue;                           // uniform
                 const bool exact = (int)kspan_t + qspan[jq] <= kSpanExact;
                 f32x4_t sc = {0.f, 0.f, 0.f, 0.f};
                 // four heads at a time: their products are issued before the epilogue
@@ -391,38 +571,57 @@ __global__ __launch_bounds__(kPfThreads, 2) void k_prefill(PrefillArgs a) {
                         for (int e = 0; e < 4; e++)
                             sc[e] = __builtin_fmaf(Q[jq].w[h0 + i], relu0(d[i][e]), sc[e]);
                 }
-                // lane: query qb + col, positions p0 + 4*g + e
-                const int q = qb[jq] + col;
-                const int t = a.q_pos0 + q;
-                const int pl = p0 + 4 * g;
-                const bool pres = g < 2 ? pres0 : pres1;
-                if (p0 + 15 > tmin || !pres0 || !pres1) {
+                tail(jq, sc);
+            }
+        }
+        if constexpr (MODE == kPfRescore) return;
+        if constexpr (MODE == kPfMaxima) {
+            // lane g = 0 holds the maxima of blocks 0, 2, 4, 6 and lane g = 2 those of 1, 3, 5,
+            // 7 (the same query): they swap and store blocks 0..3 and 4..7.  A group past nb
+            // (the stage's tail) holds -inf there; the array covers whole groups.
 #pragma unroll
-                    for (int e = 0; e < 4; e++)
-                        if (!pres || pl + e > t) sc[e] = -INFINITY;
-                }
-                float m = smax(smax(sc[0], sc[1]), smax(sc[2], sc[3]));
-                m = smax(m, __shfl_xor(m, 16, kWave));
-                gm[jq] = smax(gm[jq], m);
-                // blocks past nb (the tile's second block when nb is odd) are not stored:
-                // the score arrays hold blocks 0 .. nb - 1 only
-                const int jb = J0 + 2 * u + (g >> 1);
-                if (q < a.n_q && jb < a.nb) {
-                    // uniform stage bases, 32-bit lane offsets (< 8 blocks of n_q rows)
-                    const uint32_t po = (uint32_t)(((2 * u + (g >> 1)) * a.n_q + q) * kBlk + 4 * (g & 1));
-                    *reinterpret_cast<f32x4_t *>(ps_stage + po) = sc;
-                    if ((g & 1) == 0) bs_stage[(uint32_t)(q * kBlk + 2 * u + (g >> 1))] = m;
+            for (int jq = 0; jq < kPfNQ; jq++) {
+                f32x4_t o;
+#pragma unroll
+                for (int i = 0; i < 4; i++) o[i] = __shfl_xor(bmv[jq][i], 32, kWave);
+                const int q = qb[jq] + col;
+                if (q < a.n_q && (g & 1) == 0) {
+                    const f32x4_t v = g == 0 ? f32x4_t{bmv[jq][0], o[0], bmv[jq][1], o[1]}
+                                             : f32x4_t{o[2], bmv[jq][2], o[3], bmv[jq][3]};
+                    *reinterpret_cast<f32x4_t *>(bs_stage + q * kBlk + (g == 0 ? 0 : 4)) = v;
                 }
             }
         }
 #pragma unroll
         for (int jq = 0; jq < kPfNQ; jq++) {
-            const float v = smax(gm[jq], __shfl_xor(gm[jq], 32, kWave));
+            const float v = smax_xor32(gm[jq]);  // every lane of query col holds it
             const int q = qb[jq] + col;
             if (small) {
                 if (jq == 0 && g == 0) sm_gm[sidx & 1][wave][col] = v;
-            } else if (g == 0 && q < a.n_q && J0 * kBlk <= a.q_pos0 + q) {
-                a.gmax[(int64_t)q * a.ngmax + J0 / kPfStageBlocks] = v;
+                continue;
+            }
+            // group maxima leave in runs of 8 stages, 32 contiguous bytes per query: lane g
+            // keeps stages s0 + g and s0 + 4 + g of the run; groups past the query's causal
+            // end (uncomputed or masked) hold -inf, which the selection never reads
+            const bool mine = (sidx & 3) == g, hi = (sidx >> 2) & 1;
+            gbuf[jq][0] = mine && !hi ? v : gbuf[jq][0];
+            gbuf[jq][1] = mine && hi ? v : gbuf[jq][1];
+            if ((sidx & 7) == 7 || sidx == nstage - 1) {  // uniform
+                const int s0 = sidx & ~7;
+                float vals[8];
+#pragma unroll
+                for (int r = 0; r < 2; r++)
+#pragma unroll
+                    for (int gg = 0; gg < 4; gg++) vals[4 * r + gg] = __shfl(gbuf[jq][r], col + 16 * gg, kWave);
+#pragma unroll
+                for (int i = 0; i < 8; i++) if (s0 + i > sidx) vals[i] = -INFINITY;
+                gbuf[jq][0] = gbuf[jq][1] = -INFINITY;
+                const int G0 = Jbeg / kPfStageBlocks + s0;  // a multiple of 8 (rows: multiples of 4)
+                if (g == 0 && q < a.n_q) {
+                    float *dst = a.gmax + (int64_t)q * a.ngmax + G0;
+                    if (G0 < a.ngmax) *reinterpret_cast<f32x4_t *>(dst) = f32x4_t{vals[0], vals[1], vals[2], vals[3]};
+                    if (G0 + 4 < a.ngmax) *reinterpret_cast<f32x4_t *>(dst + 4) = f32x4_t{vals[4], vals[5], vals[6], vals[7]};
+                }
             }
         }
     };
@@ -444,13 +643,13 @@ __global__ __launch_bounds__(kPfThreads, 2) void k_prefill(PrefillArgs a) {
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
     for (int sidx = 0; sidx < nstage; sidx += 2) {
-        if (sidx + 1 < nstage) pf_dma<H, G>(a, meta, (sidx + 1) * kPfStageBlocks, stB);
+        if (sidx + 1 < nstage) pf_dma<H, G>(a, meta, (sidx + 1) * kPfStageBlocks, stB, sw16);
         combine_gm(sidx - 1);
         compute(stA, sidx);
         __builtin_amdgcn_s_waitcnt(0);
         __syncthreads();
         if (sidx + 1 >= nstage) break;
-        if (sidx + 2 < nstage) pf_dma<H, G>(a, meta, (sidx + 2) * kPfStageBlocks, stA);
+        if (sidx + 2 < nstage) pf_dma<H, G>(a, meta, (sidx + 2) * kPfStageBlocks, stA, sw16);
         combine_gm(sidx);
         compute(stB, sidx + 1);
         __builtin_amdgcn_s_waitcnt(0);
@@ -459,17 +658,23 @@ __global__ __launch_bounds__(kPfThreads, 2) void k_prefill(PrefillArgs a) {
     combine_gm(nstage - 1);
 }
 
-typedef void (*PfFn)(const PrefillArgs &, hipStream_t);
+typedef void (*PfFn)(const PrefillArgs &, int, hipStream_t);
 
+// pass 0: scores and maxima (at most 16 queries: spans computed inside the scoring kernel),
+// or spans and maxima; pass 1: the rescoring of the flagged blocks (more than 16 queries).
 template <int H, int G>
-void launch_prefill(const PrefillArgs &a, hipStream_t s) {
-    if (a.n_q <= 16) {  // spans computed inside the scoring kernel
-        k_prefill<H, G, true><<<a.n_qt * a.n_pc, kPfThreads, 0, s>>>(a);
+void launch_prefill(const PrefillArgs &a, int pass, hipStream_t s) {
+    if (a.n_q <= 16) {
+        if (pass == 0) k_prefill<H, G, true, kPfAll><<<a.n_qt * a.n_pc, kPfThreads, 0, s>>>(a);
         return;
     }
-    const int spans = (a.nb * kBlk + 255) / 256;
-    k_prefill_span<H, G><<<spans, 256, 0, s>>>(a);
-    k_prefill<H, G, false><<<a.n_qt * a.n_pc, kPfThreads, 0, s>>>(a);
+    if (pass == 0) {
+        const int spans = (a.nb * kBlk + 255) / 256;
+        k_prefill_span<H, G><<<spans, 256, 0, s>>>(a);
+        k_prefill<H, G, false, kPfMaxima><<<a.n_qt * a.n_pc, kPfThreads, 0, s>>>(a);
+    } else {
+        k_prefill<H, G, false, kPfRescore><<<a.n_qt * a.n_pc, kPfThreads, 0, s>>>(a);
+    }
 }
 
 bool pick_prefill(int H, int dI, PfFn *fn) {
@@ -484,25 +689,33 @@ bool pick_prefill(int H, int dI, PfFn *fn) {
     return false;
 }
 
+// Workspace of a prefill chunk: position scores (block-major), block and group maxima, key
+// spans; with more than 16 queries also the block flags (8 words per chunk of 256 blocks and
+// query), the flagged blocks (K_blk per query) and their per-query bounds.
 struct WsPrefill {
-    size_t pscore, bscore, gmax, kspan, total;
+    size_t pscore, bscore, gmax, kspan, need, list, meta, total;
 };
-WsPrefill ws_prefill(int n_q, int maxb) {
+WsPrefill ws_prefill(int n_q, int maxb, int K_blk) {
     WsPrefill w;
     const int ng = ngmax_of(maxb);
+    const int npc = (maxb + kPfChunkBlocks - 1) / kPfChunkBlocks;
+    const bool two = n_q > 16;
     size_t o = 0;
     w.pscore = o; o = align256(o + sizeof(float) * (size_t)n_q * maxb * kBlk);
     w.bscore = o; o = align256(o + sizeof(float) * (size_t)n_q * ng * kPfStageBlocks);
     w.gmax = o;   o = align256(o + sizeof(float) * (size_t)n_q * ng);
     w.kspan = o;  o = align256(o + (size_t)ng * kPfStageBlocks);
+    w.need = o;   o = align256(o + (two ? sizeof(uint32_t) * 8 * (size_t)npc * n_q : 0));
+    w.list = o;   o = align256(o + (two ? sizeof(int32_t) * (size_t)K_blk * n_q : 0));
+    w.meta = o;   o = align256(o + (two ? sizeof(uint4) * (size_t)n_q : 0));
     w.total = o;
     return w;
 }
 
 }  // namespace
 
-size_t prefill_ws_bytes(const csa2_config *, int32_t n_q, int32_t maxb) {
-    return ws_prefill(std::max(n_q, 0), maxb).total;
+size_t prefill_ws_bytes(const csa2_config *c, int32_t n_q, int32_t maxb) {
+    return ws_prefill(std::max(n_q, 0), maxb, c->pool_blocks).total;
 }
 
 }  // namespace csa2
@@ -523,7 +736,7 @@ int prefill_setup(const csa2_config *c, const uint8_t *q_codes, const uint8_t *q
         return CSA2_ERR_INVALID;
     if ((int64_t)q_pos0 + n_q > (int64_t)maxb * kBlk) return CSA2_ERR_INVALID;
     if (c->shared_key) return CSA2_ERR_UNSUPPORTED;  // the prefill kernels read per-head keys
-    const WsPrefill L = ws_prefill(n_q, maxb);
+    const WsPrefill L = ws_prefill(n_q, maxb, c->pool_blocks);
     if (ws_bytes < L.total) return CSA2_ERR_WORKSPACE;
     if (!pick_prefill(c->n_idx_heads, c->idx_dim, fn)) return CSA2_ERR_UNSUPPORTED;
     uint8_t *base = (uint8_t *)ws;
@@ -542,6 +755,7 @@ int prefill_setup(const csa2_config *c, const uint8_t *q_codes, const uint8_t *q
     a->pscore = (float *)(base + L.pscore);
     a->bscore = (float *)(base + L.bscore);
     a->gmax = (float *)(base + L.gmax);
+    a->need = (uint32_t *)(base + L.need);
     a->ngmax = ngmax_of(maxb);
     a->n_qt = (n_q + kPfQT - 1) / kPfQT;
     a->n_pc = (a->nb + kPfChunkBlocks - 1) / kPfChunkBlocks;
@@ -561,7 +775,7 @@ extern "C" int csa2_index_prefill_scan(const csa2_config *c, const uint8_t *q_co
                                  block_table, maxb, ws, ws_bytes, &a, &fn);
     if (st) return st;
     if (n_q == 0) return CSA2_OK;
-    fn(a, stream);
+    fn(a, 0, stream);
     return hipGetLastError() == hipSuccess ? CSA2_OK : CSA2_ERR_HIP;
 }
 
@@ -598,7 +812,19 @@ extern "C" int csa2_index_prefill_finish(const csa2_config *c, const uint8_t *q_
     s.pool_len = pool_len;
     s.topk = topk;
     s.topk_len = topk_len;
-    return launch_select(s, false, stream);
+    if (n_q <= 16) return launch_select(s, false, stream);
+    // more queries: the maxima pass left the position scores out; select the pools and flag
+    // the blocks the top-k reads, rescore those, then select the top-k
+    const WsPrefill L = ws_prefill(n_q, maxb, c->pool_blocks);
+    uint8_t *base = (uint8_t *)ws;
+    s.pf_need = a.need;
+    s.pf_list = (int32_t *)(base + L.list);
+    s.pf_meta = (uint4 *)(base + L.meta);
+    int r = launch_select_prefill(s, 0, stream);
+    if (r) return r;
+    fn(a, 1, stream);
+    if (hipGetLastError() != hipSuccess) return CSA2_ERR_HIP;
+    return launch_select_prefill(s, 1, stream);
 }
 
 extern "C" int csa2_index_prefill(const csa2_config *c, const uint8_t *q_codes,

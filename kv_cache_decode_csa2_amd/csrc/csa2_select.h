@@ -48,6 +48,13 @@ struct SelectArgs {
     int32_t *topk;
     int32_t *topk_len;
     Sel2Ws sel2;  // two-phase Full selection (sel2.nw > 0)
+    // Prefill in two passes (csa2_index_prefill with more than 16 queries): flags of the
+    // blocks whose position scores the top-k reads, 8 words per (chunk of 256 blocks, query)
+    // at pf_need[(chunk*B + b)*8]; those blocks of each query, ascending, at pf_list[b*K_blk];
+    // per query (lower bound key of its k-th best score, upper bound key, count) in pf_meta.
+    uint32_t *pf_need;
+    int32_t *pf_list;
+    uint4 *pf_meta;
 };
 
 // Gather workgroups per sequence of the two-phase Full selection for a table of width maxb
@@ -62,6 +69,12 @@ int launch_select(const SelectArgs &a, bool reindex, hipStream_t stream);
 
 // The two-phase Full selection (grid sel2.nw x B); a.sel2 filled.
 int launch_select_full2(const SelectArgs &a, hipStream_t stream);
+
+// Prefill selection in two phases around the rescoring pass.  Phase 0: the pool of every
+// query (written out) and its flagged blocks (pf_need, pf_list, pf_meta; pf_need zeroed
+// beforehand).  Phase 1: the top-k of every query from the position scores of its flagged
+// blocks.
+int launch_select_prefill(const SelectArgs &a, int phase, hipStream_t stream);
 
 // Row stride of the group maxima of a table of width maxb (multiple of 4 floats).
 int ngmax_of(int maxb);

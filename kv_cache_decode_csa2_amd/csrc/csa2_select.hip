@@ -549,6 +549,89 @@ __global__ __launch_bounds__(kSelThreads) void k_select(SelectArgs a) {
     full_select_one_wg(a, b, L, nb, sm, graw);
 }
 
+// ------------------------------------------------------------------ prefill in two passes
+//
+// The prefill scoring pass keeps block and group maxima only; the selection then runs in two
+// phases around a second scoring pass that recomputes the position scores of the blocks the
+// top-k can draw from.  With theta the k-th largest block maximum of the pool, the k pool
+// blocks reaching it each hold a distinct position scoring >= theta, so the k-th best pool
+// position scores >= theta and every top-k position lies in a pool block whose maximum is
+// >= theta: those blocks (the flagged blocks) hold the whole candidate set.  When the pool
+// has fewer than k blocks or at most k visible positions, every pool block is flagged.
+
+// Phase 0, one workgroup per query: pool, theta, flagged blocks.
+__global__ __launch_bounds__(kSelThreads) void k_select_pf_pool(SelectArgs a) {
+    extern __shared__ __align__(16) uint8_t sh_raw[];
+    SelectShared &sm = *reinterpret_cast<SelectShared *>(sh_raw);
+    const int b = blockIdx.x, tid = threadIdx.x;
+    float4 graw[kIPT / 4];
+    const float *gm = a.gmax + (int64_t)b * a.ngmax;
+#pragma unroll
+    for (int i = 0; i < kIPT / 4; i++) {
+        const int gi = min(tid * kIPT + 4 * i, a.ngmax - 4);  // clamped into the row
+        graw[i] = *reinterpret_cast<const float4 *>(gm + gi);
+    }
+    const int L = clamp_len(a.q_pos0 + b + 1, a.maxb);
+    const int nb = (L + kBlk - 1) / kBlk;
+    for (int i = tid; i < kHistBins; i += kSelThreads) sm.sel.hist[i] = 0u;
+    __syncthreads();
+    uint32_t thr, kmax;
+    const int np = min(select_pool(a, b, nb, sm, graw, &thr, &kmax), nb);
+    // block maxima and visible positions of the pool entries 2t, 2t+1
+    const BlockRow bs{a.bscore + (int64_t)b * a.bs_b, a.bs_g};
+    int pj[2];
+    float v[2];
+#pragma unroll
+    for (int q = 0; q < 2; q++) {
+        const int e = 2 * tid + q;
+        pj[q] = e < np ? sm.pool[e] : -1;
+        v[q] = bs[max(pj[q], 0)];
+    }
+    RegItems<2> bm;
+    uint32_t nvis = 0u;
+#pragma unroll
+    for (int q = 0; q < 2; q++) {
+        bm.key[q] = pj[q] >= 0 ? order_key(v[q]) : 0u;
+        nvis += pj[q] >= 0 ? (uint32_t)min(kBlk, L - pj[q] * kBlk) : 0u;
+    }
+    const uint32_t n_vis = block_sum<kSelThreads>(nvis, sm.sel.scan);
+    uint32_t theta = 0u;
+    if (np >= a.k && n_vis > (uint32_t)a.k) theta = range_select(bm, (uint32_t)a.k, sm.sel).thr;
+    uint32_t fl = 0u;
+#pragma unroll
+    for (int q = 0; q < 2; q++) fl |= pj[q] >= 0 && bm.key[q] >= theta ? 1u << q : 0u;
+    uint32_t cnt;
+    uint32_t o = block_excl_scan<kSelThreads>((uint32_t)__popc(fl), sm.sel.scan, &cnt);
+    int32_t *lst = a.pf_list + (int64_t)b * a.K_blk;
+#pragma unroll
+    for (int q = 0; q < 2; q++) {
+        if (fl & (1u << q)) {
+            const int j = pj[q];
+            lst[o++] = j;
+            atomicOr(&a.pf_need[((int64_t)(j >> 8) * a.B + b) * 8 + ((j & 255) >> 5)], 1u << (j & 31));
+        }
+    }
+    int32_t *pool_out = a.pool_blocks + (int64_t)b * a.K_blk;
+    for (int i = tid; i < a.K_blk; i += kSelThreads) pool_out[i] = i < np ? sm.pool[i] : -1;
+    if (tid == 0) {
+        a.pool_len[b] = np;
+        a.pf_meta[b] = make_uint4(theta, kmax, cnt, 0u);
+    }
+}
+
+// Phase 1, one workgroup per query: the top-k among the positions of the flagged blocks that
+// score >= theta (the position scores of exactly those blocks were recomputed).
+__global__ __launch_bounds__(kSelThreads) void k_select_pf_topk(SelectArgs a) {
+    extern __shared__ __align__(16) uint8_t sh_raw[];
+    SelectShared &sm = *reinterpret_cast<SelectShared *>(sh_raw);
+    const int b = blockIdx.x, tid = threadIdx.x;
+    const uint4 m = a.pf_meta[b];
+    const int L = clamp_len(a.q_pos0 + b + 1, a.maxb);
+    for (int i = tid; i < kHistBins; i += kSelThreads) sm.sel.hist[i] = 0u;
+    __syncthreads();
+    select_topk<false>(a, b, L, a.pf_list + (int64_t)b * a.K_blk, (int)m.z, m.x, m.y, sm);
+}
+
 // ------------------------------------------------------------------ two-phase Full selection
 //
 // One gather workgroup per 1024 groups of a sequence, the last of them to arrive finishing
@@ -828,6 +911,13 @@ int launch_select_full2(const SelectArgs &a, hipStream_t stream) {
     if (a.B <= 0) return CSA2_OK;
     k_select_full2<<<dim3(a.sel2.nw, a.B), kSelThreads, kSelectShared + sizeof(uint2) * kSel2LdsCap,
                      stream>>>(a);
+    return hipGetLastError() == hipSuccess ? CSA2_OK : CSA2_ERR_HIP;
+}
+
+int launch_select_prefill(const SelectArgs &a, int phase, hipStream_t stream) {
+    if (a.B <= 0) return CSA2_OK;
+    if (phase == 0) k_select_pf_pool<<<a.B, kSelThreads, kSelectShared, stream>>>(a);
+    else k_select_pf_topk<<<a.B, kSelThreads, kSelectShared, stream>>>(a);
     return hipGetLastError() == hipSuccess ? CSA2_OK : CSA2_ERR_HIP;
 }
 

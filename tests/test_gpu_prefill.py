@@ -51,10 +51,53 @@ def _ws_scores(ws, n_q, maxb, blk0=0, blk1=None):
     return _np(ps), _np(bs), _np(gm)
 
 
-def _check_scores(o, qo, q_pos0, queries, ps, bs, gm, blk0, blk1):
+def _ws_flags(ws, n_q, maxb, K_blk):
+    """More than 16 queries (two scoring passes): per query the flagged blocks (those whose
+    position scores the rescoring pass wrote) from the ascending list and its count, and
+    from the flag words [chunk of 256 blocks][query][8 words]."""
+    ng = _ngmax(maxb)
+    row = n_q * 8 * 4
+    ob = _al(maxb * row)
+    og = _al(ob + ng * row)
+    oks = _al(og + n_q * ng * 4)
+    on = _al(oks + ng * 8)
+    npc = (maxb + 255) // 256
+    ol = _al(on + 8 * npc * n_q * 4)
+    om = _al(ol + K_blk * n_q * 4)
+    words = _np(ws[on:on + 8 * npc * n_q * 4].view(torch.int32)).view(np.uint32).reshape(npc, n_q, 8)
+    lst = _np(ws[ol:ol + K_blk * n_q * 4].view(torch.int32)).reshape(n_q, K_blk)
+    meta = _np(ws[om:om + 16 * n_q].view(torch.int32)).view(np.uint32).reshape(n_q, 4)
+    listed = [lst[i, :meta[i, 2]].copy() for i in range(n_q)]
+    bits = np.unpackbits(words.transpose(1, 0, 2).reshape(n_q, -1).view(np.uint8),
+                         axis=1, bitorder="little")
+    flagged = [np.flatnonzero(bits[i]).astype(np.int32) for i in range(n_q)]
+    return listed, flagged
+
+
+def _check_flags(o, qo, q_pos0, n_q, pool, plen, listed, flagged, k_top):
+    """The flagged blocks of each query: the flag words and the list agree, ascending; they
+    lie in the pool and hold every pool block whose maximum reaches the k-th largest maximum
+    of the pool (all of the pool when it has fewer than k blocks or at most k positions)."""
+    for i in range(n_q):
+        t = q_pos0 + i
+        assert np.array_equal(listed[i], flagged[i]), (i, "flag words / list")
+        pl = pool[i, :plen[i]]
+        assert np.isin(listed[i], pl).all(), (i, "flagged outside the pool")
+        ref = oracle.index_scores(o.cfg, qo[0][i], qo[1][i], qo[2][i], o.idx, o.table[0], t + 1)
+        bm = oracle.block_scores(ref, t + 1)[pl]
+        nvis = sum(min(8, t + 1 - 8 * j) for j in pl)
+        if len(pl) >= k_top and nvis > k_top:
+            need = pl[bm >= np.sort(bm)[-k_top]]
+        else:
+            need = pl
+        assert np.isin(need, listed[i]).all(), (i, "a block the top-k can draw from is not flagged")
+
+
+def _check_scores(o, qo, q_pos0, queries, ps, bs, gm, blk0, blk1, flagged=None):
     """Scores of the listed queries at positions 8*blk0 .. 8*blk1-1 (their causal part)
-    equal the oracle's bit for bit; so do the block maxima of those blocks and the maxima
-    of the groups of 8 blocks that lie wholly inside the range."""
+    equal the oracle's bit for bit (with `flagged`, only those of each query's flagged
+    blocks: the rest are never written); so do the block maxima of those blocks and the
+    maxima of the groups of 8 blocks that lie wholly inside the range."""
     table_row = o.table[0]
     for i in queries:
         t = q_pos0 + i
@@ -63,8 +106,13 @@ def _check_scores(o, qo, q_pos0, queries, ps, bs, gm, blk0, blk1):
         if n <= 0:
             continue
         ref = oracle.index_scores(o.cfg, qo[0][i], qo[1][i], qo[2][i], o.idx, table_row[blk0:], n)
-        got = ps[:, i, :].reshape(-1)[:n]
-        assert np.array_equal(got.view(np.uint32), ref.view(np.uint32)), (i, _first_diff(got, ref))
+        got, want = ps[:, i, :].reshape(-1)[:n], ref
+        if flagged is not None:
+            fb = flagged[i][(flagged[i] >= blk0) & (flagged[i] < blk1)] - blk0
+            sel = (fb[:, None] * 8 + np.arange(8)[None, :]).reshape(-1)
+            sel = sel[sel < n]
+            got, want = got[sel], ref[sel]
+        assert np.array_equal(got.view(np.uint32), want.view(np.uint32)), (i, _first_diff(got, want))
         rb = oracle.block_scores(ref, n)
         gb = bs.reshape(-1, bs.shape[1], 8)[:, i, :].reshape(-1)[blk0 % 8:][:len(rb)]
         assert np.array_equal(gb.view(np.uint32), rb.view(np.uint32)), (i, "block maxima")
@@ -102,9 +150,14 @@ def _check(wl, n_q, permute=True, scale_fn=None, w=None):
                      dtype=torch.uint8, device="cuda")
     pg, plg, tg, tlg = index_prefill(g, qc, qs, wg, q_pos0, ws=ws)
     torch.cuda.synchronize()
-    # what the selection read: every causal score, block and group maximum of every query
+    # what the selection read: the block and group maxima of every query, and every causal
+    # score (at most 16 queries) or those of the flagged blocks
     ps, bs, gm = _ws_scores(ws, n_q, maxb)
-    _check_scores(o, qo, q_pos0, range(n_q), ps, bs, gm, 0, maxb)
+    flagged = None
+    if n_q > 16:
+        listed, flagged = _ws_flags(ws, n_q, maxb, wl.K_blk)
+        _check_flags(o, qo, q_pos0, n_q, po, plo, listed, flagged, wl.k)
+    _check_scores(o, qo, q_pos0, range(n_q), ps, bs, gm, 0, maxb, flagged)
     assert np.array_equal(_np(plg), plo), _first_diff(_np(plg), plo)
     assert np.array_equal(_np(pg), po), _first_diff(_np(pg), po)
     assert np.array_equal(_np(tlg), tlo), _first_diff(_np(tlg), tlo)
@@ -257,7 +310,12 @@ def test_prefill_workload_sampled():
     go, gl = _attn_prefill(g, dev(qa.view(np.int16)), ring_g, C, q_pos0, tgd, tlgd)
     go, gl = _np(go), _np(gl)
     qo = _oracle_q(wl, n_q)
-    # whole tiles x chunks (chunk = 256 blocks = 2048 positions)
+    listed, flagged = _ws_flags(ws, n_q, maxb, wl.K_blk)
+    for i in range(n_q):
+        assert np.array_equal(listed[i], flagged[i]), (i, "flag words / list")
+        assert np.isin(listed[i], pg[i]).all() and len(listed[i]) >= wl.k, (i, "flagged blocks")
+    # whole tiles x chunks (chunk = 256 blocks = 2048 positions): maxima, and the scores of
+    # the flagged blocks
     for tile0 in (0, 2048):
         t_first = q_pos0 + tile0
         diag = t_first // 2048
@@ -266,7 +324,7 @@ def test_prefill_workload_sampled():
                 continue
             ps, bs, gm = _ws_scores(ws, n_q, maxb, c * 256, (c + 1) * 256)
             _check_scores(o, qo, q_pos0, range(tile0, tile0 + 128), ps, bs, gm, c * 256,
-                          (c + 1) * 256)
+                          (c + 1) * 256, flagged)
     del ws, g
     torch.cuda.empty_cache()
     assert np.all(plg == wl.K_blk) and np.all(tlg == wl.k)
