@@ -43,15 +43,28 @@ namespace {
 
 typedef int v8i_t __attribute__((ext_vector_type(8)));
 
-constexpr int kPfThreads = 256;
-constexpr int kPfWaves = kPfThreads / kWave;
 constexpr int kPfNQ = 2;                          // 16-query tiles per wave
-constexpr int kPfQT = kPfWaves * kPfNQ * 16;      // queries per workgroup
+constexpr int kPfMaximaWaves = 4, kPfRescoreWaves = 8;
 constexpr int kPfStageBlocks = 8;                 // blocks per LDS stage (one group maximum)
 constexpr int kPfChunkStages = 32;                // stages per workgroup (2048 positions)
 constexpr int kPfChunkBlocks = kPfChunkStages * kPfStageBlocks;
 constexpr int kSpanExact = 9;                     // largest exact exponent span
 constexpr int kBlockPad = 128;                    // LDS bytes between staged blocks
+
+// MODE: kPfAll, scores and maxima (at most 16 queries); kPfMaxima, block and group maxima
+// only; kPfRescore, the position scores of the flagged (query, block) pairs only, computed
+// for the 16 x 16 tiles holding one.
+constexpr int kPfAll = 0, kPfMaxima = 1, kPfRescore = 2;
+
+// Waves of a workgroup (each holds kPfNQ query tiles of 16 and shares the staged keys).
+// The maxima pass runs two 4-wave workgroups per CU, whose waves share SIMDs without a
+// common barrier; the sparser rescoring pass amortises each staged stage over 8 waves.
+template <int MODE>
+struct PfShape {
+    static constexpr int waves = MODE == kPfRescore ? kPfRescoreWaves : kPfMaximaWaves;
+    static constexpr int threads = waves * kWave;
+    static constexpr int qt = waves * kPfNQ * 16;  // queries per workgroup
+};
 
 struct PrefillArgs {
     const uint8_t *q_codes;   // [n_q][H*G*16]
@@ -178,7 +191,7 @@ __device__ __forceinline__ uint32_t pf_swizzle16(int lane) {
 // row lies inside one block: its physical block is wave-uniform (a scalar base) and each lane
 // adds a fixed offset (sw16, from pf_swizzle16).  Otherwise rows span blocks and each lane
 // looks its block up.
-template <int H, int G>
+template <int H, int G, int kPfWaves>
 __device__ __forceinline__ void pf_dma(const PrefillArgs &a, const PfMeta &meta, int jrel,
                                        PfStage<H, G> &dst, uint32_t sw16) {
     using S = PfStage<H, G>;
@@ -189,15 +202,15 @@ __device__ __forceinline__ void pf_dma(const PrefillArgs &a, const PfMeta &meta,
     const int lane = lane_id();
     const int wave = __builtin_amdgcn_readfirstlane((int)threadIdx.x / kWave);
     if constexpr (S::CODES % 1024 == 0 && S::SCB % 256 == 0) {
-        // wave w stages blocks 2w and 2w + 1 of the stage, all of their rows
+        // wave w stages blocks BPW*w .. BPW*w + BPW - 1 of the stage, all of their rows
         constexpr int CR = S::CODES / 1024, SR = S::SCB / 256;
-        static_assert(kPfStageBlocks == 2 * kPfWaves, "two blocks per wave");
-        const int2 ph2 = *reinterpret_cast<const int2 *>(&meta.phys[jrel + 2 * wave]);
-        const int32_t phv[2] = {__builtin_amdgcn_readfirstlane(ph2.x), __builtin_amdgcn_readfirstlane(ph2.y)};
+        constexpr int BPW = kPfStageBlocks / kPfWaves;
+        static_assert(BPW * kPfWaves == kPfStageBlocks, "whole blocks per wave");
 #pragma unroll
-        for (int i = 0; i < 2; i++) {
-            const int blk = 2 * wave + i;
-            const uint8_t *base = a.idx_cache + (int64_t)(phv[i] >= 0 ? phv[i] : 0) * BYTES;
+        for (int i = 0; i < BPW; i++) {
+            const int blk = BPW * wave + i;
+            const int32_t ph = __builtin_amdgcn_readfirstlane(meta.phys[jrel + blk]);
+            const uint8_t *base = a.idx_cache + (int64_t)(ph >= 0 ? ph : 0) * BYTES;
 #pragma unroll
             for (int k = 0; k < CR; k++)
                 __builtin_amdgcn_global_load_lds(base + k * 1024 + sw16,
@@ -282,14 +295,11 @@ struct PfQuery {
     float w[H];
 };
 
-// MODE: kPfAll, scores and maxima (at most 16 queries); kPfMaxima, block and group maxima
-// only; kPfRescore, the position scores of the flagged (query, block) pairs only, computed
-// for the 16 x 16 tiles holding one.
-constexpr int kPfAll = 0, kPfMaxima = 1, kPfRescore = 2;
-
 template <int H, int G, bool SMALL, int MODE>
-__global__ __launch_bounds__(kPfThreads, 2) void k_prefill(PrefillArgs a) {
+__global__ __launch_bounds__(PfShape<MODE>::threads, 8 / PfShape<MODE>::waves) void k_prefill(PrefillArgs a) {
     using S = PfStage<H, G>;
+    constexpr int kPfWaves = PfShape<MODE>::waves, kPfThreads = PfShape<MODE>::threads;
+    constexpr int kPfQT = PfShape<MODE>::qt;
     // two stage buffers as distinct objects, so that the reads of one are known not to
     // alias the DMA into the other
     __shared__ S stA, stB;
@@ -306,17 +316,19 @@ __global__ __launch_bounds__(kPfThreads, 2) void k_prefill(PrefillArgs a) {
     const int Jbeg = pc * kPfChunkBlocks;
     // blocks this tile can see: j*8 <= q_pos0 + qlast
     const int Jend = min(min(a.nb, Jbeg + kPfChunkBlocks), (a.q_pos0 + qlast) / kBlk + 1);
-    if (Jbeg >= Jend) return;  // uniform per workgroup (no query of the tile sees the chunk)
-    // the flags of this (chunk, query tile): cleared by the maxima pass, read by the
-    // rescoring pass (thread i: query Q0 + i/2, words 4*(i%2) .. +3)
-    if constexpr (MODE != kPfAll) {
+    // the flags of this (chunk, query tile): cleared by the maxima pass (by every workgroup,
+    // including those that see nothing of the chunk, as the rescoring pass tiles the queries
+    // differently), read by the rescoring pass (thread i: query Q0 + i/2, words 4*(i%2) .. +3)
+    if constexpr (MODE == kPfMaxima) {
         const int qi = Q0 + (int)threadIdx.x / 2;
-        uint4 *fw = reinterpret_cast<uint4 *>(a.need + ((int64_t)pc * a.n_q + qi) * 8) + threadIdx.x % 2;
-        if constexpr (MODE == kPfMaxima) {
-            if (qi < a.n_q) *fw = make_uint4(0u, 0u, 0u, 0u);
-        } else {
-            nd[threadIdx.x] = qi < a.n_q ? *fw : make_uint4(0u, 0u, 0u, 0u);
-        }
+        if (qi < a.n_q)
+            reinterpret_cast<uint4 *>(a.need + ((int64_t)pc * a.n_q + qi) * 8)[threadIdx.x % 2] = make_uint4(0u, 0u, 0u, 0u);
+    }
+    if (Jbeg >= Jend) return;  // uniform per workgroup (no query of the tile sees the chunk)
+    if constexpr (MODE == kPfRescore) {
+        const int qi = Q0 + (int)threadIdx.x / 2;
+        nd[threadIdx.x] = qi < a.n_q ? reinterpret_cast<const uint4 *>(a.need + ((int64_t)pc * a.n_q + qi) * 8)[threadIdx.x % 2]
+                                     : make_uint4(0u, 0u, 0u, 0u);
     }
     const int nstage = (Jend - Jbeg + kPfStageBlocks - 1) / kPfStageBlocks;
 
@@ -336,7 +348,7 @@ __global__ __launch_bounds__(kPfThreads, 2) void k_prefill(PrefillArgs a) {
     }
     __syncthreads();
     const uint32_t sw16 = pf_swizzle16<H>(lane_id());
-    pf_dma<H, G>(a, meta, 0, stA, sw16);
+    pf_dma<H, G, kPfWaves>(a, meta, 0, stA, sw16);
 
     // At most 16 queries (a verification step): every wave takes the one query tile and a
     // quarter of each stage's positions (16-position tile u = wave) instead of a query tile
@@ -643,13 +655,13 @@ __global__ __launch_bounds__(kPfThreads, 2) void k_prefill(PrefillArgs a) {
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
     for (int sidx = 0; sidx < nstage; sidx += 2) {
-        if (sidx + 1 < nstage) pf_dma<H, G>(a, meta, (sidx + 1) * kPfStageBlocks, stB, sw16);
+        if (sidx + 1 < nstage) pf_dma<H, G, kPfWaves>(a, meta, (sidx + 1) * kPfStageBlocks, stB, sw16);
         combine_gm(sidx - 1);
         compute(stA, sidx);
         __builtin_amdgcn_s_waitcnt(0);
         __syncthreads();
         if (sidx + 1 >= nstage) break;
-        if (sidx + 2 < nstage) pf_dma<H, G>(a, meta, (sidx + 2) * kPfStageBlocks, stA, sw16);
+        if (sidx + 2 < nstage) pf_dma<H, G, kPfWaves>(a, meta, (sidx + 2) * kPfStageBlocks, stA, sw16);
         combine_gm(sidx);
         compute(stB, sidx + 1);
         __builtin_amdgcn_s_waitcnt(0);
@@ -660,20 +672,28 @@ __global__ __launch_bounds__(kPfThreads, 2) void k_prefill(PrefillArgs a) {
 
 typedef void (*PfFn)(const PrefillArgs &, int, hipStream_t);
 
+// Launch of one scoring kernel: query tiles of the mode's workgroup size x position chunks.
+template <int H, int G, bool SMALL, int MODE>
+void launch_mode(PrefillArgs a, hipStream_t s) {
+    using P = PfShape<MODE>;
+    a.n_qt = (a.n_q + P::qt - 1) / P::qt;
+    k_prefill<H, G, SMALL, MODE><<<a.n_qt * a.n_pc, P::threads, 0, s>>>(a);
+}
+
 // pass 0: scores and maxima (at most 16 queries: spans computed inside the scoring kernel),
 // or spans and maxima; pass 1: the rescoring of the flagged blocks (more than 16 queries).
 template <int H, int G>
 void launch_prefill(const PrefillArgs &a, int pass, hipStream_t s) {
     if (a.n_q <= 16) {
-        if (pass == 0) k_prefill<H, G, true, kPfAll><<<a.n_qt * a.n_pc, kPfThreads, 0, s>>>(a);
+        if (pass == 0) launch_mode<H, G, true, kPfAll>(a, s);
         return;
     }
     if (pass == 0) {
         const int spans = (a.nb * kBlk + 255) / 256;
         k_prefill_span<H, G><<<spans, 256, 0, s>>>(a);
-        k_prefill<H, G, false, kPfMaxima><<<a.n_qt * a.n_pc, kPfThreads, 0, s>>>(a);
+        launch_mode<H, G, false, kPfMaxima>(a, s);
     } else {
-        k_prefill<H, G, false, kPfRescore><<<a.n_qt * a.n_pc, kPfThreads, 0, s>>>(a);
+        launch_mode<H, G, false, kPfRescore>(a, s);
     }
 }
 
@@ -757,7 +777,6 @@ int prefill_setup(const csa2_config *c, const uint8_t *q_codes, const uint8_t *q
     a->gmax = (float *)(base + L.gmax);
     a->need = (uint32_t *)(base + L.need);
     a->ngmax = ngmax_of(maxb);
-    a->n_qt = (n_q + kPfQT - 1) / kPfQT;
     a->n_pc = (a->nb + kPfChunkBlocks - 1) / kPfChunkBlocks;
     return CSA2_OK;
 }
