@@ -34,6 +34,7 @@ namespace csa2 {
 
 constexpr int kScanThreads = 256;
 constexpr int kScanWaves = kScanThreads / kWave;
+constexpr int kHold = 8;  // item outputs a scan wave holds in LDS before storing them
 constexpr int kScanGridMax = 512;   // workgroups of a scan (grid-stride over waves): two per
                                     // CU, so that each wave runs enough steps to amortise its
                                     // pipeline fill
@@ -431,6 +432,14 @@ __global__ __launch_bounds__(kScanThreads, 2) void k_scan(ScanArgs a) {
     extern __shared__ int32_t sh_dyn[];  // item prefix [B + 1], clamped lengths [B], lengths [B]
     __shared__ __align__(16) uint32_t sh_scan[kScanWaves];
     int32_t *sh_prefix = sh_dyn, *sh_len = sh_dyn + a.B + 1, *sh_raw = sh_dyn + 2 * a.B + 1;
+    // Item outputs are held in LDS and stored after the wave's key loads (every kHold items):
+    // stores count with the loads in the in-order vmcnt, and interleaved with the stream of
+    // key loads they measured ~3.5 us per scan at 1M positions.  Per held item: the 64
+    // position scores, the block and group maxima (lanes 0..7, 63) and (sequence, first
+    // entry, in segment, entry limit).
+    __shared__ __align__(16) float sh_hold[kScanWaves][kHold][2][kWave];
+    __shared__ __align__(16) int4 sh_hmeta[kScanWaves][kHold];
+    int nhold = 0;  // uniform
 
     const int lane = threadIdx.x & (kWave - 1);
     const int wave = __builtin_amdgcn_readfirstlane((int)threadIdx.x / kWave);
@@ -513,6 +522,30 @@ __global__ __launch_bounds__(kScanThreads, 2) void k_scan(ScanArgs a) {
         }
     };
     float gm = -INFINITY;
+    const bool ps_on = RESCORE || a.pscore, pb_on = RESCORE || a.bscore, pg_on = !RESCORE && a.gmax;
+    // the held items' stores (lanes without output are masked off: no store of theirs reaches
+    // memory)
+    auto flush = [&] {
+        for (int i = 0; i < nhold; i++) {
+            const int4 m = sh_hmeta[wave][i];
+            const int hb = __builtin_amdgcn_readfirstlane(m.x), he = __builtin_amdgcn_readfirstlane(m.y);
+            const bool hok = __builtin_amdgcn_readfirstlane(m.z) != 0;
+            const int hlim = __builtin_amdgcn_readfirstlane(m.w);
+            const float vp = sh_hold[wave][i][0][lane], vs = sh_hold[wave][i][1][lane];
+            float *ps = (RESCORE ? a.poolsc + (int64_t)hb * a.K_blk * kBlk : a.pscore + (int64_t)hb * a.maxb * kBlk) +
+                        (int64_t)he * kBlk + lane;
+            float *pb = (RESCORE ? a.poolbmax + (int64_t)hb * a.K_blk : a.bscore + (int64_t)hb * a.bstride) + he + lane;
+            const bool pos_ok = hok && he + lane / kBlk < hlim;
+            bool pb_ok = lane < kBlk && hok && he + lane < hlim && pb_on;
+            if (!RESCORE && lane == kWave - 1) {
+                pb_ok = hok && pg_on;
+                pb = a.gmax + (int64_t)hb * a.ngmax + he / kItemBlocks;
+            }
+            if (pos_ok && ps_on) *ps = vp;
+            if (pb_ok) *pb = vs;
+        }
+        nhold = 0;
+    };
 
     // The wave's steps split into segments of one sequence each (items are 8-aligned, so a
     // segment starts at an item boundary).  Per segment: the query, row bases and lengths;
@@ -658,10 +691,6 @@ __global__ __launch_bounds__(kScanThreads, 2) void k_scan(ScanArgs a) {
         load_keys(mt[0], K[0]);
         load_keys(mt[1], K[1]);
 
-        float *ps_row = RESCORE ? a.poolsc + (int64_t)b * a.K_blk * kBlk : a.pscore + (int64_t)b * a.maxb * kBlk;
-        float *pb_row = RESCORE ? a.poolbmax + (int64_t)b * a.K_blk : a.bscore + (int64_t)b * a.bstride;
-        float *pg_row = RESCORE ? nullptr : a.gmax + (int64_t)b * a.ngmax;
-        const bool ps_on = RESCORE || a.pscore, pb_on = RESCORE || a.bscore, pg_on = !RESCORE && a.gmax;
         const int n_lim = RESCORE ? n_ent : nb;  // entries of the segment's row
 
         // scores and block maxima of the current item, gathered so that lane l holds position
@@ -686,31 +715,25 @@ __global__ __launch_bounds__(kScanThreads, 2) void k_scan(ScanArgs a) {
                 gm = __builtin_elementwise_maximum(si == 0 ? -INFINITY : gm, m);
             }
             if (si == NSTEP - 1) {
-                // item stores: 64 position scores, 8 block maxima (+ the group maximum)
+                // the item's outputs (64 position scores, 8 block maxima, the group maximum
+                // in lane 63) wait in LDS
                 const int e_item = mt[0].e0 - (NSTEP - 1) * BPW;
-                const bool item_ok = k2 < kend;
-                const bool pos_ok = item_ok && e_item + lane / kBlk < n_lim;
-                // (lanes without output are masked off: no store of theirs reaches memory)
-                float *ps = ps_row + (int64_t)e_item * kBlk + lane;
-                float *pb = pb_row + e_item + lane;
                 float vstore = acc_b;
-                bool pb_ok = lane < kBlk && item_ok && e_item + lane < n_lim && pb_on;
                 if (!RESCORE) {
                     const float g63 = blocks_to_lane63<H>(gm);
-                    if (lane == kWave - 1) {
-                        vstore = g63;
-                        pb_ok = item_ok && pg_on;
-                        pb = pg_row + e_item / kItemBlocks;
-                    }
+                    if (lane == kWave - 1) vstore = g63;
                 }
-                if (pos_ok && ps_on) *ps = acc_p;
-                if (pb_ok) *pb = vstore;
+                sh_hold[wave][nhold][0][lane] = acc_p;
+                sh_hold[wave][nhold][1][lane] = vstore;
+                if (lane == 0) sh_hmeta[wave][nhold] = make_int4(b, e_item, k2 < kend ? 1 : 0, n_lim);
+                nhold++;
             }
 #pragma unroll
             for (int i = 0; i < DM - 1; i++) mt[i] = mt[i + 1];
         };
         // iterations of STEPS steps (whole items); steps past the segment end are masked
         for (; k < kend; k += STEPS) {
+            if (nhold + STEPS / NSTEP > kHold) flush();  // room for this iteration's items
             if (APPEND && k_new >= 0 && k_new - DK < k + STEPS) {  // before this iteration's key loads
                 append_write();
                 k_new = -1;
@@ -718,8 +741,8 @@ __global__ __launch_bounds__(kScanThreads, 2) void k_scan(ScanArgs a) {
 #pragma unroll
             for (int st = 0; st < STEPS; st++) body(k + st, st % NSTEP, K[st % 4], K[(st + 2) % 4]);
         }
-        (void)ps_on;
     }
+    flush();
 }
 
 // ------------------------------------------------------------------ k_scan_shared

@@ -256,12 +256,17 @@ def _attn_prefill(g, q, ring, C, q_pos0, topk, tl):
     return out, lse
 
 
-@pytest.mark.parametrize("L,n_q,H_q,W", [(3000, 200, 32, 32), (300, 300, 16, 128)])
-def test_prefill_attention_within_tolerance(L, n_q, H_q, W):
+@pytest.mark.parametrize("L,n_q,H_q,W,k_top", [
+    (3000, 200, 32, 32, 128),   # one workgroup per (query, head pair)
+    (300, 300, 16, 128, 128),   # one head group: the split kernel
+    (2000, 150, 64, 128, 128),  # two head pairs per query
+    (300, 300, 64, 32, 96),     # a chunk holding both top-k and window rows; short prefixes
+])
+def test_prefill_attention_within_tolerance(L, n_q, H_q, W, k_top):
     """Per-query sparse attention of a prefill chunk: each query's own top-k (from the GPU
     prefill indexer, checked equal to the oracle's) plus its own window from the shared
     ring; within 2e-3 of the fp64 oracle."""
-    wl = si.small("pfat", 130 + L, [L], H_I=8, d_I=128, K_blk=64, k=128, H_q=H_q, W=W)
+    wl = si.small("pfat", 130 + L, [L], H_I=8, d_I=128, K_blk=64, k=k_top, H_q=H_q, W=W)
     q_pos0 = L - n_q
     table, nblk = make_table(wl.ctx, seed=wl.seed)
     o = OracleState(wl, table, nblk)
