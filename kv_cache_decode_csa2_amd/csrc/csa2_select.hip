@@ -710,6 +710,105 @@ __device__ void two_bounds(const Src &src, uint32_t K1, uint32_t K2, SelShared &
     __syncthreads();  // (res is written again by later selections)
 }
 
+// Prefix sums of the regions' candidate counts (pre) and bound-reaching block counts (mpre)
+// of sequence b, and whether the two-phase selection holds: every region kept its
+// bound-reaching blocks, the candidates fit LDS and the bound-reaching blocks one per thread.
+// The two finishing workgroups take the same decision from the same counts.
+__device__ __forceinline__ bool full2_counts(const Sel2Ws &q, int b, int32_t *pre, int32_t *mpre, int32_t *flag) {
+    const int nw = q.nw, tid = threadIdx.x;
+    if (tid < nw) {
+        pre[tid + 1] = q.cnt[((int64_t)b * nw + tid) * 2];
+        mpre[tid + 1] = q.cnt[((int64_t)b * nw + tid) * 2 + 1];
+    }
+    __syncthreads();
+    if (tid == 0) {
+        int okf = 1;
+        pre[0] = mpre[0] = 0;
+        for (int i = 1; i <= nw; i++) {
+            okf &= mpre[i] >= 0;
+            pre[i] += pre[i - 1];
+            mpre[i] = mpre[i - 1] + max(mpre[i], 0);
+        }
+        flag[1] = okf && pre[nw] <= kSel2LdsCap && mpre[nw] <= kSelThreads;
+    }
+    __syncthreads();
+    return flag[1] != 0;
+}
+
+// Iterations (of a short sleep) after which the top-k workgroup stops waiting for the gather
+// workgroups of its sequence.  They were dispatched before it (lower workgroup index) and so
+// are resident or done; the bound only guards against a broken launch.
+constexpr uint32_t kSel2WaitLimit = 1u << 24;
+
+// The top-k workgroup of the two-phase selection (index nw of its sequence), run beside the
+// gather workgroups: mu from the group maxima (the same histogram pass, so the same value
+// the gather workgroups use), then, once every gather workgroup has arrived, the exact top-k
+// of the positions >= mu of the bound-reaching blocks, while the last gather workgroup selects
+// the pool.  Off the fast path (or when the regions overflowed) the last gather workgroup
+// selects both.  Resets the sequence's arrival counter for the next call.
+__device__ __forceinline__ void full2_topk(const SelectArgs &a, int b, int L, bool fast,
+                                        const float4 (&graw)[kIPT / 4], int ng, SelectShared &sm,
+                                        int32_t *sh_mpre, int32_t *sh_flag) {
+    const Sel2Ws &q = a.sel2;
+    const int nw = q.nw, tid = threadIdx.x;
+    __shared__ int32_t sh_pre2[kSel2MaxW + 1];
+    uint32_t mu = 0u;
+    if (fast) {
+        RegItems<kIPT> g;
+#pragma unroll
+        for (int i = 0; i < kIPT; i += 4) {
+            const float f[4] = {graw[i / 4].x, graw[i / 4].y, graw[i / 4].z, graw[i / 4].w};
+#pragma unroll
+            for (int t = 0; t < 4; t++) g.key[i + t] = tid * kIPT + i + t < ng ? order_key(f[t]) : 0u;
+        }
+        uint32_t lam;
+        two_bounds(g, (uint32_t)min(a.K_blk, ng), (uint32_t)a.k, sm.sel, &lam, &mu);
+    }
+    // wait for the gather workgroups: relaxed coherent polls (an acquire per poll would
+    // invalidate this XCD's caches under the gather workgroups' reads), then one agent-scope
+    // acquire, after which their regions are visible
+    if (tid == 0) {
+        uint32_t it = 0;
+        while (__hip_atomic_load(q.arrive + b, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < nw &&
+               ++it < kSel2WaitLimit)
+            __builtin_amdgcn_s_sleep(2);
+        __hip_atomic_store(q.arrive + b, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+    __syncthreads();
+    if (!fast || !full2_counts(q, b, sh_pre2, sh_mpre, sh_flag)) return;  // uniform
+    const int n_m = sh_mpre[nw];
+    // the bound-reaching block tid (blocks in order, one per thread) and its position scores
+    const int e = tid;
+    int mw = 0;
+    if (e < n_m) {  // largest region r with mpre[r] <= e
+        int lo = 0, hi = nw - 1;
+        while (lo < hi) {
+            const int mid = (lo + hi + 1) >> 1;
+            if (sh_mpre[mid] <= e) lo = mid;
+            else hi = mid - 1;
+        }
+        mw = lo;
+    }
+    const int64_t mslot = ((int64_t)b * nw + mw) * kSel2MuCap + (e < n_m ? e - sh_mpre[mw] : 0);
+    const int32_t mb = e < n_m ? q.mu_blk[mslot] : -1;
+    const float4 *msrc = reinterpret_cast<const float4 *>(q.mu_sc + mslot * kBlk);
+    const float4 ms0 = msrc[0], ms1 = msrc[1];
+    RegItems<kBlk> p;
+    {
+        const float sc[kBlk] = {ms0.x, ms0.y, ms0.z, ms0.w, ms1.x, ms1.y, ms1.z, ms1.w};
+#pragma unroll
+        for (int t = 0; t < kBlk; t++) {
+            const uint32_t key = order_key(sc[t]);
+            p.key[t] = mb >= 0 && mb * kBlk + t < L && key >= mu ? key : 0u;
+        }
+    }
+    // top-k: the exact top-k of the positions >= mu of the blocks >= mu, ascending
+    select_emit(p, [&](int t) { return mb * kBlk + t; }, (uint32_t)a.k,
+                a.topk + (int64_t)b * a.k, (uint32_t)a.k, sm);
+    if (tid == 0) a.topk_len[b] = a.k;
+}
+
 __global__ __launch_bounds__(kSelThreads) void k_select_full2(SelectArgs a) {
     extern __shared__ __align__(16) uint8_t sh_raw[];
     SelectShared &sm = *reinterpret_cast<SelectShared *>(sh_raw);
@@ -743,6 +842,10 @@ __global__ __launch_bounds__(kSelThreads) void k_select_full2(SelectArgs a) {
     uint32_t lam = 0u, mu = 0u;
     int cnt_c = 0, cnt_m = 0;
     const int64_t reg = (int64_t)b * nw + w;
+    if (w == nw) {  // the top-k workgroup (uniform)
+        full2_topk(a, b, L, fast, graw, ng, sm, sh_mpre, sh_flag);
+        return;
+    }
     if (fast) {
         RegItems<kIPT> g;
 #pragma unroll
@@ -807,27 +910,7 @@ __global__ __launch_bounds__(kSelThreads) void k_select_full2(SelectArgs a) {
                      nw - 1;
     __syncthreads();
     if (!sh_flag[0]) return;  // uniform
-    if (tid == 0) __hip_atomic_store(q.arrive + b, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    bool ok = fast;
-    if (ok) {
-        if (tid < nw) {
-            sh_pre[tid + 1] = q.cnt[((int64_t)b * nw + tid) * 2];
-            sh_mpre[tid + 1] = q.cnt[((int64_t)b * nw + tid) * 2 + 1];
-        }
-        __syncthreads();
-        if (tid == 0) {
-            int okf = 1;
-            sh_pre[0] = sh_mpre[0] = 0;
-            for (int i = 1; i <= nw; i++) {
-                okf &= sh_mpre[i] >= 0;
-                sh_pre[i] += sh_pre[i - 1];
-                sh_mpre[i] = sh_mpre[i - 1] + max(sh_mpre[i], 0);
-            }
-            sh_flag[1] = okf && sh_pre[nw] <= kSel2LdsCap && sh_mpre[nw] <= kSelThreads;
-        }
-        __syncthreads();
-        ok = sh_flag[1];
-    }
+    const bool ok = fast && full2_counts(a.sel2, b, sh_pre, sh_mpre, sh_flag);
     if (!ok) {  // the one-workgroup selection (its group maxima read again: a rare path)
         __syncthreads();
 #pragma unroll
@@ -861,13 +944,7 @@ __global__ __launch_bounds__(kSelThreads) void k_select_full2(SelectArgs a) {
         c.key[r] = in ? v.x : 0u;
         if (in) lds_c[i] = v;
     }
-    // the bound-reaching block tid (blocks in order, one per thread) and its position scores
-    const int e = tid;
-    const int mw = e < n_m ? region_of(sh_mpre, e) : 0;
-    const int64_t mslot = ((int64_t)b * nw + mw) * kSel2MuCap + (e < n_m ? e - sh_mpre[mw] : 0);
-    const int32_t mb = e < n_m ? q.mu_blk[mslot] : -1;
-    const float4 *msrc = reinterpret_cast<const float4 *>(q.mu_sc + mslot * kBlk);
-    const float4 ms0 = msrc[0], ms1 = msrc[1];
+    (void)n_m;
     __syncthreads();
     // pool: the exact top-K_blk of the candidates, emitted ascending from LDS (thread t owns
     // candidates [8t, 8t + 8))
@@ -887,29 +964,16 @@ __global__ __launch_bounds__(kSelThreads) void k_select_full2(SelectArgs a) {
         emit_selected(o, [&](int j) { return oid[j]; }, r, a.pool_blocks + (int64_t)b * a.K_blk,
                       (uint32_t)a.K_blk, tie_base, out_base, sm.sel);
     }
-    // top-k: the exact top-k of the positions >= mu of the blocks >= mu, ascending
-    RegItems<kBlk> p;
-    {
-        const float sc[kBlk] = {ms0.x, ms0.y, ms0.z, ms0.w, ms1.x, ms1.y, ms1.z, ms1.w};
-#pragma unroll
-        for (int t = 0; t < kBlk; t++) {
-            const uint32_t key = order_key(sc[t]);
-            p.key[t] = mb >= 0 && mb * kBlk + t < L && key >= mu ? key : 0u;
-        }
-    }
-    select_emit(p, [&](int t) { return mb * kBlk + t; }, (uint32_t)a.k,
-                a.topk + (int64_t)b * a.k, (uint32_t)a.k, sm);
-    if (tid == 0) {
-        a.pool_len[b] = a.K_blk;
-        a.topk_len[b] = a.k;
-    }
+    if (tid == 0) a.pool_len[b] = a.K_blk;
 }
 
 constexpr size_t kSelectShared = sizeof(SelectShared);
 
 int launch_select_full2(const SelectArgs &a, hipStream_t stream) {
     if (a.B <= 0) return CSA2_OK;
-    k_select_full2<<<dim3(a.sel2.nw, a.B), kSelThreads, kSelectShared + sizeof(uint2) * kSel2LdsCap,
+    // nw gather workgroups per sequence, then its top-k workgroup (the highest index, so that
+    // its gather workgroups are dispatched before it)
+    k_select_full2<<<dim3(a.sel2.nw + 1, a.B), kSelThreads, kSelectShared + sizeof(uint2) * kSel2LdsCap,
                      stream>>>(a);
     return hipGetLastError() == hipSuccess ? CSA2_OK : CSA2_ERR_HIP;
 }
