@@ -738,7 +738,7 @@ __device__ __forceinline__ bool full2_counts(const Sel2Ws &q, int b, int32_t *pr
 // Iterations (of a short sleep) after which the top-k workgroup stops waiting for the gather
 // workgroups of its sequence.  They were dispatched before it (lower workgroup index) and so
 // are resident or done; the bound only guards against a broken launch.
-constexpr uint32_t kSel2WaitLimit = 1u << 24;
+constexpr uint32_t kSel2WaitLimit = 1u << 20;
 
 // The top-k workgroup of the two-phase selection (index nw of its sequence), run beside the
 // gather workgroups: mu from the group maxima (the same histogram pass, so the same value
