@@ -559,11 +559,20 @@ __global__ __launch_bounds__(kSelThreads) void k_select(SelectArgs a) {
 // >= theta: those blocks (the flagged blocks) hold the whole candidate set.  When the pool
 // has fewer than k blocks or at most k visible positions, every pool block is flagged.
 
+// Query of workgroup `bid` of a grid of n: runs of 4 consecutive queries on one XCD (dispatch
+// places workgroup i on XCD i % 8), whose block-maxima reads share cache lines (the layout
+// puts 4 queries' 8 block maxima of a group in one 128-byte line).
+__device__ __forceinline__ int pf_query_of(int bid, int n) {
+    if (n % 32 != 0) return bid;
+    const int x = bid % 8, slot = bid / 8;
+    return 4 * (8 * (slot / 4) + x) + slot % 4;
+}
+
 // Phase 0, one workgroup per query: pool, theta, flagged blocks.
 __global__ __launch_bounds__(kSelThreads) void k_select_pf_pool(SelectArgs a) {
     extern __shared__ __align__(16) uint8_t sh_raw[];
     SelectShared &sm = *reinterpret_cast<SelectShared *>(sh_raw);
-    const int b = blockIdx.x, tid = threadIdx.x;
+    const int b = pf_query_of((int)blockIdx.x, (int)gridDim.x), tid = threadIdx.x;
     float4 graw[kIPT / 4];
     const float *gm = a.gmax + (int64_t)b * a.ngmax;
 #pragma unroll
