@@ -35,7 +35,7 @@
 //                     the rescoring pass.
 #include <algorithm>
 
-#include "csa2_common.h"
+#include "csa2_block.h"
 #include "csa2_select.h"
 
 namespace csa2 {
@@ -82,6 +82,7 @@ struct PrefillArgs {
     float *gmax;           // [n_q][ngmax]
     int32_t ngmax;
     uint32_t *need;        // flags of the blocks to rescore: 8 words per (chunk, query)
+    int32_t *arrive;       // [n_q] arrivals of the two-phase selection (null: not used)
     int32_t n_qt, n_pc;    // query tiles, position chunks
 };
 
@@ -305,6 +306,8 @@ __global__ __launch_bounds__(PfShape<MODE>::threads, 8 / PfShape<MODE>::waves) v
     __shared__ S stA, stB;
     __shared__ PfMeta meta;
     __shared__ uint4 nd[MODE == kPfRescore ? kPfQT * 2 : 1];  // flags of the tile's queries
+    if (SMALL && a.arrive && blockIdx.x == 0 && (int)threadIdx.x < a.n_q)  // (read by the selection)
+        a.arrive[threadIdx.x] = 0;
     // workgroup -> (position chunk, query tile); the workgroups of one chunk are consecutive
     // on one XCD (dispatch places workgroup i on XCD i % 8) so its keys are fetched once
     const int T = a.n_qt * a.n_pc;
@@ -711,11 +714,15 @@ bool pick_prefill(int H, int dI, PfFn *fn) {
 
 // Workspace of a prefill chunk: position scores (block-major), block and group maxima, key
 // spans; with more than 16 queries also the block flags (8 words per chunk of 256 blocks and
-// query), the flagged blocks (K_blk per query) and their per-query bounds.
+// query), the flagged blocks (K_blk per query) and their per-query bounds; with at most 16
+// queries over a long table, the regions of the two-phase Full selection.
 struct WsPrefill {
-    size_t pscore, bscore, gmax, kspan, need, list, meta, total;
+    size_t pscore, bscore, gmax, kspan, need, list, meta;
+    int nw;
+    size_t cand, mu_sc, mu_blk, cnt, arrive, total;
 };
-WsPrefill ws_prefill(int n_q, int maxb, int K_blk) {
+WsPrefill ws_prefill(const csa2_config *c, int n_q, int maxb) {
+    const int K_blk = c->pool_blocks;
     WsPrefill w;
     const int ng = ngmax_of(maxb);
     const int npc = (maxb + kPfChunkBlocks - 1) / kPfChunkBlocks;
@@ -728,6 +735,13 @@ WsPrefill ws_prefill(int n_q, int maxb, int K_blk) {
     w.need = o;   o = align256(o + (two ? sizeof(uint32_t) * 8 * (size_t)npc * n_q : 0));
     w.list = o;   o = align256(o + (two ? sizeof(int32_t) * (size_t)K_blk * n_q : 0));
     w.meta = o;   o = align256(o + (two ? sizeof(uint4) * (size_t)n_q : 0));
+    w.nw = two ? 0 : sel2_workgroups(c, maxb);
+    const size_t regs = (size_t)n_q * w.nw;
+    w.cand = o;   o = align256(o + sizeof(uint2) * regs * kSel2GroupsPerW * kItemBlocks);
+    w.mu_sc = o;  o = align256(o + sizeof(float) * regs * kSel2MuCap * kBlk);
+    w.mu_blk = o; o = align256(o + sizeof(int32_t) * regs * kSel2MuCap);
+    w.cnt = o;    o = align256(o + sizeof(int32_t) * regs * 2);
+    w.arrive = o; o = align256(o + sizeof(int32_t) * (w.nw ? (size_t)n_q : 0));
     w.total = o;
     return w;
 }
@@ -735,7 +749,7 @@ WsPrefill ws_prefill(int n_q, int maxb, int K_blk) {
 }  // namespace
 
 size_t prefill_ws_bytes(const csa2_config *c, int32_t n_q, int32_t maxb) {
-    return ws_prefill(std::max(n_q, 0), maxb, c->pool_blocks).total;
+    return ws_prefill(c, std::max(n_q, 0), maxb).total;
 }
 
 }  // namespace csa2
@@ -756,7 +770,7 @@ int prefill_setup(const csa2_config *c, const uint8_t *q_codes, const uint8_t *q
         return CSA2_ERR_INVALID;
     if ((int64_t)q_pos0 + n_q > (int64_t)maxb * kBlk) return CSA2_ERR_INVALID;
     if (c->shared_key) return CSA2_ERR_UNSUPPORTED;  // the prefill kernels read per-head keys
-    const WsPrefill L = ws_prefill(n_q, maxb, c->pool_blocks);
+    const WsPrefill L = ws_prefill(c, n_q, maxb);
     if (ws_bytes < L.total) return CSA2_ERR_WORKSPACE;
     if (!pick_prefill(c->n_idx_heads, c->idx_dim, fn)) return CSA2_ERR_UNSUPPORTED;
     uint8_t *base = (uint8_t *)ws;
@@ -776,6 +790,7 @@ int prefill_setup(const csa2_config *c, const uint8_t *q_codes, const uint8_t *q
     a->bscore = (float *)(base + L.bscore);
     a->gmax = (float *)(base + L.gmax);
     a->need = (uint32_t *)(base + L.need);
+    a->arrive = L.nw ? (int32_t *)(base + L.arrive) : nullptr;
     a->ngmax = ngmax_of(maxb);
     a->n_pc = (a->nb + kPfChunkBlocks - 1) / kPfChunkBlocks;
     return CSA2_OK;
@@ -831,11 +846,22 @@ extern "C" int csa2_index_prefill_finish(const csa2_config *c, const uint8_t *q_
     s.pool_len = pool_len;
     s.topk = topk;
     s.topk_len = topk_len;
-    if (n_q <= 16) return launch_select(s, false, stream);
+    const WsPrefill L = ws_prefill(c, n_q, maxb);
+    uint8_t *base = (uint8_t *)ws;
+    if (n_q <= 16) {
+        if (!L.nw) return launch_select(s, false, stream);
+        // a long table: the two-phase selection per query (the scoring kernel cleared the
+        // arrival counters)
+        s.sel2.nw = L.nw;
+        s.sel2.cand = (uint2 *)(base + L.cand);
+        s.sel2.mu_sc = (float *)(base + L.mu_sc);
+        s.sel2.mu_blk = (int32_t *)(base + L.mu_blk);
+        s.sel2.cnt = (int32_t *)(base + L.cnt);
+        s.sel2.arrive = (int32_t *)(base + L.arrive);
+        return launch_select_full2(s, stream);
+    }
     // more queries: the maxima pass left the position scores out; select the pools and flag
     // the blocks the top-k reads, rescore those, then select the top-k
-    const WsPrefill L = ws_prefill(n_q, maxb, c->pool_blocks);
-    uint8_t *base = (uint8_t *)ws;
     s.pf_need = a.need;
     s.pf_list = (int32_t *)(base + L.list);
     s.pf_meta = (uint4 *)(base + L.meta);

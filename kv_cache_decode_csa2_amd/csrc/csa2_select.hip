@@ -838,7 +838,7 @@ __global__ __launch_bounds__(kSelThreads) void k_select_full2(SelectArgs a) {
     const float4 *bsrc = reinterpret_cast<const float4 *>(a.bscore + (int64_t)b * a.bs_b +
                                                          (int64_t)min(gi, a.ngmax - 1) * a.bs_g);
     float4 bm0 = bsrc[0], bm1 = bsrc[1];
-    const int L = clamp_len(a.ctx_len[b], a.maxb);
+    const int L = clamp_len(a.ctx_len ? a.ctx_len[b] : a.q_pos0 + b + 1, a.maxb);
 #pragma unroll
     for (int i = 0; i < kIPT / 4; i++)
         asm volatile("" : "+v"(graw[i].x), "+v"(graw[i].y), "+v"(graw[i].z), "+v"(graw[i].w));

@@ -182,6 +182,15 @@ def test_prefill_index_bit_exact(H, d, L, n_q):
     _check(wl, n_q)
 
 
+@pytest.mark.parametrize("L,n_q", [(12000, 6), (9000, 16)])
+def test_prefill_few_queries_two_phase_selection(L, n_q):
+    """At most 16 queries over a table of at least 2 K_blk groups with K_blk >= k: the
+    selection runs in two phases (gather workgroups, the last one selecting the pool, a top-k
+    workgroup per query); pools and top-k equal the oracle's per query."""
+    wl = si.small("pf2p", 140 + L, [L], H_I=4, d_I=64, K_blk=64, k=48, W=16)
+    _check(wl, n_q)
+
+
 def test_prefill_pool_covers_everything():
     # most prefixes have at most K_blk blocks: the pool is every visible block
     wl = si.small("pfcov", 120, [900], H_I=4, d_I=128, K_blk=128, k=300, W=16)
