@@ -19,17 +19,19 @@
 // maxima) runs on the vector ALUs and writes what the Full-mode selection reads.
 //
 // With more than 16 queries no position score is stored by the scoring pass: it keeps the
-// block and group maxima, the selection takes the pools from them, and a second pass over
-// the same tiles recomputes only the scores the top-k can need (the pool blocks whose
-// maximum reaches the k-th largest pool block maximum, about k per query), skipping every
-// 16 x 16 tile that holds none of them.
+// block and group maxima, the selection takes the pools from them, and a second pass
+// recomputes only the scores the top-k can need (the pool blocks whose maximum reaches the
+// k-th largest pool block maximum, about k per query), block by block for the queries that
+// flagged each block.
 //
 // Kernels:
 //   k_prefill_span    per logical block: the largest exponent span of any key head vector.
 //   k_prefill<H,G,.,MODE>  a workgroup = 128 queries x 2048 positions; keys staged through
 //                     LDS in stages of 8 blocks (double-buffered), queries and head weights
 //                     held in registers, 4 waves x 2 query tiles of 16.  MODE: scores and
-//                     maxima (at most 16 queries), maxima only, or the flagged rescoring.
+//                     maxima (at most 16 queries), or maxima only.
+//   k_prefill_rescore (more than 16 queries) one workgroup per stage of 8 blocks: the
+//                     flagged blocks' scores for the queries that flagged them.
 //   k_select          (at most 16 queries, shared with Full mode) one workgroup per query;
 //   k_select_pf_pool / k_select_pf_topk  (more queries) the two selection phases around
 //                     the rescoring pass.
@@ -44,7 +46,6 @@ namespace {
 typedef int v8i_t __attribute__((ext_vector_type(8)));
 
 constexpr int kPfNQ = 2;                          // 16-query tiles per wave
-constexpr int kPfMaximaWaves = 4, kPfRescoreWaves = 8;
 constexpr int kPfStageBlocks = 8;                 // blocks per LDS stage (one group maximum)
 constexpr int kPfChunkStages = 32;                // stages per workgroup (2048 positions)
 constexpr int kPfChunkBlocks = kPfChunkStages * kPfStageBlocks;
@@ -52,16 +53,14 @@ constexpr int kSpanExact = 9;                     // largest exact exponent span
 constexpr int kBlockPad = 128;                    // LDS bytes between staged blocks
 
 // MODE: kPfAll, scores and maxima (at most 16 queries); kPfMaxima, block and group maxima
-// only; kPfRescore, the position scores of the flagged (query, block) pairs only, computed
-// for the 16 x 16 tiles holding one.
-constexpr int kPfAll = 0, kPfMaxima = 1, kPfRescore = 2;
+// only.
+constexpr int kPfAll = 0, kPfMaxima = 1;
 
-// Waves of a workgroup (each holds kPfNQ query tiles of 16 and shares the staged keys).
-// The maxima pass runs two 4-wave workgroups per CU, whose waves share SIMDs without a
-// common barrier; the sparser rescoring pass amortises each staged stage over 8 waves.
+// A scoring workgroup: 4 waves, each holding kPfNQ query tiles of 16 and sharing the staged
+// keys (two workgroups per CU, whose waves share SIMDs without a common barrier).
 template <int MODE>
 struct PfShape {
-    static constexpr int waves = MODE == kPfRescore ? kPfRescoreWaves : kPfMaximaWaves;
+    static constexpr int waves = 4;
     static constexpr int threads = waves * kWave;
     static constexpr int qt = waves * kPfNQ * 16;  // queries per workgroup
 };
@@ -81,7 +80,8 @@ struct PrefillArgs {
     float *bscore;         // group-major: (q, j) at ((j/8)*n_q + q)*8 + j%8
     float *gmax;           // [n_q][ngmax]
     int32_t ngmax;
-    uint32_t *need;        // flags of the blocks to rescore: 8 words per (chunk, query)
+    uint32_t *need;        // flags of the blocks to rescore: word w of chunk c, query q at (c*8 + w)*n_q + q
+    uint8_t *qspan;        // [n_q] largest scale-exponent span of any head vector of the query
     int32_t *arrive;       // [n_q] arrivals of the two-phase selection (null: not used)
     int32_t n_qt, n_pc;    // query tiles, position chunks
 };
@@ -305,7 +305,6 @@ __global__ __launch_bounds__(PfShape<MODE>::threads, 8 / PfShape<MODE>::waves) v
     // alias the DMA into the other
     __shared__ S stA, stB;
     __shared__ PfMeta meta;
-    __shared__ uint4 nd[MODE == kPfRescore ? kPfQT * 2 : 1];  // flags of the tile's queries
     if (SMALL && a.arrive && blockIdx.x == 0 && (int)threadIdx.x < a.n_q)  // (read by the selection)
         a.arrive[threadIdx.x] = 0;
     // workgroup -> (position chunk, query tile); the workgroups of one chunk are consecutive
@@ -319,20 +318,16 @@ __global__ __launch_bounds__(PfShape<MODE>::threads, 8 / PfShape<MODE>::waves) v
     const int Jbeg = pc * kPfChunkBlocks;
     // blocks this tile can see: j*8 <= q_pos0 + qlast
     const int Jend = min(min(a.nb, Jbeg + kPfChunkBlocks), (a.q_pos0 + qlast) / kBlk + 1);
-    // the flags of this (chunk, query tile): cleared by the maxima pass (by every workgroup,
-    // including those that see nothing of the chunk, as the rescoring pass tiles the queries
-    // differently), read by the rescoring pass (thread i: query Q0 + i/2, words 4*(i%2) .. +3)
+    // the flags of this (chunk, query tile), set by the pool selection and read by the
+    // rescoring pass: cleared here by every workgroup, including those that see nothing of
+    // the chunk
     if constexpr (MODE == kPfMaxima) {
-        const int qi = Q0 + (int)threadIdx.x / 2;
-        if (qi < a.n_q)
-            reinterpret_cast<uint4 *>(a.need + ((int64_t)pc * a.n_q + qi) * 8)[threadIdx.x % 2] = make_uint4(0u, 0u, 0u, 0u);
+        for (int i = (int)threadIdx.x; i < 8 * kPfQT; i += kPfThreads) {
+            const int qi = Q0 + i % kPfQT;
+            if (qi < a.n_q) a.need[((int64_t)pc * 8 + i / kPfQT) * a.n_q + qi] = 0u;
+        }
     }
     if (Jbeg >= Jend) return;  // uniform per workgroup (no query of the tile sees the chunk)
-    if constexpr (MODE == kPfRescore) {
-        const int qi = Q0 + (int)threadIdx.x / 2;
-        nd[threadIdx.x] = qi < a.n_q ? reinterpret_cast<const uint4 *>(a.need + ((int64_t)pc * a.n_q + qi) * 8)[threadIdx.x % 2]
-                                     : make_uint4(0u, 0u, 0u, 0u);
-    }
     const int nstage = (Jend - Jbeg + kPfStageBlocks - 1) / kPfStageBlocks;
 
     const int lane = lane_id(), wave = (int)threadIdx.x / kWave;
@@ -390,6 +385,8 @@ __global__ __launch_bounds__(PfShape<MODE>::threads, 8 / PfShape<MODE>::waves) v
             }
             span = max(span, hi - lo);
         }
+        // the query's own span, for the rescoring pass (from the first position chunk)
+        if (MODE == kPfMaxima && pc == 0 && g == 0 && qb[jq] + col < a.n_q) a.qspan[qb[jq] + col] = (uint8_t)span;
         // wave maximum (queries past n_q repeat query n_q - 1)
 #pragma unroll
         for (int o = 1; o < kWave; o <<= 1) span = max(span, __shfl_xor(span, o, kWave));
@@ -417,29 +414,13 @@ __global__ __launch_bounds__(PfShape<MODE>::threads, 8 / PfShape<MODE>::waves) v
             gm[jq] = -INFINITY;
             bmv[jq] = f32x4_t{-INFINITY, -INFINITY, -INFINITY, -INFINITY};
         }
-        // rescoring: the stage's 8 block flags of the lane's query (own) and of any query of
-        // the 16-query tile (anyf, wave-uniform)
-        uint32_t own[kPfNQ], anyf[kPfNQ];
-        if constexpr (MODE == kPfRescore) {
-            const uint32_t *ndw = reinterpret_cast<const uint32_t *>(nd);
+        // 16-position tiles, unrolled (LDS offsets become immediates and the per-tile maxima
+        // stay in place; a verification step runs one tile per wave)
 #pragma unroll
-            for (int jq = 0; jq < kPfNQ; jq++) {
-                const int ql = qb[jq] - Q0 + col;  // < kPfQT
-                own[jq] = (ndw[ql * 8 + (sidx >> 2)] >> (8 * (sidx & 3))) & 0xffu;
-                uint32_t x = own[jq];
-#pragma unroll
-                for (int o = 1; o < 16; o <<= 1) x |= __shfl_xor(x, o, kWave);
-                anyf[jq] = __builtin_amdgcn_readfirstlane(x);
-            }
-        }
-#pragma unroll 1
-        for (int u = u_beg; u < u_end; u++) {  // 16-position tiles
+        for (int u = u_beg; u < u_end; u++) {
             if constexpr (MODE == kPfMaxima) {
 #pragma unroll
                 for (int jq = 0; jq < kPfNQ; jq++) bmv[jq] = f32x4_t{bmv[jq][1], bmv[jq][2], bmv[jq][3], -INFINITY};
-            }
-            if constexpr (MODE == kPfRescore) {
-                if (!(((anyf[0] | anyf[kPfNQ - 1]) >> (2 * u)) & 3u)) continue;  // nothing flagged
             }
             const int p0 = (J0 + 2 * u) * kBlk;
             // this lane's key row: position p0 + col, group g
@@ -479,7 +460,6 @@ __global__ __launch_bounds__(PfShape<MODE>::threads, 8 / PfShape<MODE>::waves) v
             auto active = [&](int jq) {
                 if (qb[jq] >= a.n_q) return false;                                  // no queries
                 if (p0 > a.q_pos0 + min(qb[jq] + 15, a.n_q - 1)) return false;      // all masked
-                if constexpr (MODE == kPfRescore) return ((anyf[jq] >> (2 * u)) & 3u) != 0u;  // flagged
                 return true;
             };
             // causal / presence mask, block maxima and stores of tile jq's scores
@@ -495,11 +475,8 @@ __global__ __launch_bounds__(PfShape<MODE>::threads, 8 / PfShape<MODE>::waves) v
                     for (int e = 0; e < 4; e++)
                         if (!pres || pl + e > t) sc[e] = -INFINITY;
                 }
-                float m = 0.f;
-                if constexpr (MODE != kPfRescore) {
-                    m = smax_xor16(smax(smax(sc[0], sc[1]), smax(sc[2], sc[3])));
-                    gm[jq] = smax(gm[jq], m);
-                }
+                const float m = smax_xor16(smax(smax(sc[0], sc[1]), smax(sc[2], sc[3])));
+                gm[jq] = smax(gm[jq], m);
                 // uniform stage bases, 32-bit lane offsets (< 8 blocks of n_q rows); lanes g and
                 // g ^ 1 hold the same block maximum and store it to the same address
                 const uint32_t po = (uint32_t)(((2 * u + (g >> 1)) * a.n_q + q) * kBlk + 4 * (g & 1));
@@ -507,15 +484,13 @@ __global__ __launch_bounds__(PfShape<MODE>::threads, 8 / PfShape<MODE>::waves) v
                 if constexpr (MODE == kPfMaxima) {
                     bmv[jq][3] = m;
                 } else if (qb[jq] + 15 < a.n_q && J0 + 2 * u + 1 < a.nb) {  // every lane's (query, block) exists
-                    if (MODE == kPfAll || ((own[jq] >> (2 * u + (g >> 1))) & 1u))
-                        *reinterpret_cast<f32x4_t *>(ps_stage + po) = sc;
-                    if (MODE == kPfAll) bs_stage[bo] = m;
+                    *reinterpret_cast<f32x4_t *>(ps_stage + po) = sc;
+                    bs_stage[bo] = m;
                 } else if (q < a.n_q && J0 + 2 * u + (g >> 1) < a.nb) {
                     // blocks past nb (the tile's second block when nb is odd) are not stored:
                     // the score arrays hold blocks 0 .. nb - 1 only
-                    if (MODE == kPfAll || ((own[jq] >> (2 * u + (g >> 1))) & 1u))
-                        *reinterpret_cast<f32x4_t *>(ps_stage + po) = sc;
-                    if (MODE == kPfAll) bs_stage[bo] = m;
+                    *reinterpret_cast<f32x4_t *>(ps_stage + po) = sc;
+                    bs_stage[bo] = m;
                 }
             };
             if constexpr (kPfNQ == 2 && H % 4 == 0) {
@@ -589,7 +564,6 @@ __global__ __launch_bounds__(PfShape<MODE>::threads, 8 / PfShape<MODE>::waves) v
                 tail(jq, sc);
             }
         }
-        if constexpr (MODE == kPfRescore) return;
         if constexpr (MODE == kPfMaxima) {
             // lane g = 0 holds the maxima of blocks 0, 2, 4, 6 and lane g = 2 those of 1, 3, 5,
             // 7 (the same query): they swap and store blocks 0..3 and 4..7.  A group past nb
@@ -673,6 +647,210 @@ __global__ __launch_bounds__(PfShape<MODE>::threads, 8 / PfShape<MODE>::waves) v
     combine_gm(nstage - 1);
 }
 
+
+// ------------------------------------------------------------------ rescoring pass
+//
+// With more than 16 queries the selection flags, per query, the pool blocks whose maximum
+// reaches the k-th largest pool block maximum (about k of them); their position scores are
+// recomputed here, block-major: one workgroup per stage of 8 blocks stages the stage's keys
+// in LDS once, lists from the flag words the queries that flagged a block of each of its
+// four 16-position tiles, and wave u computes tile u for its listed queries, 16 at a time
+// (each lane's query gathered into the B operand), storing the scores of the flagged blocks
+// only.  Tile products, the ReLU / fma chain over heads and the causal mask are those of the
+// scoring pass, so the scores are bit-identical to the ones it would have stored.
+constexpr int kRsWaves = 4, kRsThreads = kRsWaves * kWave;
+constexpr int kRsBatch = 4096;  // queries listed per round (16-bit list entries: 12 + 2 bits)
+
+// Query q as the B operand of a 16 x 16 tile (lane column: the query, group g of every head):
+// codes, E8M0 codes packed as PfQuery::s and head weights, from whole-row vector loads.
+template <int H, int G>
+__device__ __forceinline__ void pf_gather_query(const PrefillArgs &a, int q, int g, PfQuery<H> &Q) {
+    const bool gl = g < G;
+    const int gg = gl ? g : 0;
+    const uint8_t *qc = a.q_codes + (int64_t)q * H * G * 16;
+#pragma unroll
+    for (int h = 0; h < H; h++)
+        Q.c[h] = gl ? *reinterpret_cast<const uint4 *>(qc + (h * G + gg) * 16) : make_uint4(0u, 0u, 0u, 0u);
+#pragma unroll
+    for (int i = 0; i < (H + 3) / 4; i++) Q.s[i] = 0u;
+    if constexpr (H * G >= 4) {
+        // byte h*G + g of the query's H*G scale bytes is byte ((h*G) & 3) + g of dword (h*G)/4
+        const uint32_t *qs = reinterpret_cast<const uint32_t *>(a.q_scales + (int64_t)q * H * G);
+        uint32_t dw[H * G / 4];
+#pragma unroll
+        for (int i = 0; i < H * G / 4; i++) dw[i] = qs[i];
+#pragma unroll
+        for (int h = 0; h < H; h++) {
+            const uint32_t e = gl ? (dw[(h * G) / 4] >> (8 * (((h * G) & 3) + gg))) & 0xffu : 127u;
+            Q.s[h / 4] |= e << (8 * (h % 4));
+        }
+    } else {
+        const uint8_t *qs = a.q_scales + (int64_t)q * H * G;
+#pragma unroll
+        for (int h = 0; h < H; h++) Q.s[h / 4] |= (gl ? (uint32_t)qs[h * G + gg] : 127u) << (8 * (h % 4));
+    }
+#pragma unroll
+    for (int h = 0; h < H; h++) Q.w[h] = a.w[(int64_t)q * H + h];
+}
+
+template <int H, int G>
+__global__ __launch_bounds__(kRsThreads, 2) void k_prefill_rescore(PrefillArgs a) {
+    using S = PfStage<H, G>;
+    __shared__ S st;
+    __shared__ PfMeta meta;  // entries 0..7: the stage's blocks
+    __shared__ uint16_t lst[kRsWaves][kRsBatch];  // (query - batch start) << 2 | flags of the tile's two blocks
+    __shared__ uint32_t cnt[kRsWaves];
+    const int pc = (int)blockIdx.x / (kPfChunkBlocks / kPfStageBlocks);
+    const int sg = (int)blockIdx.x % (kPfChunkBlocks / kPfStageBlocks);
+    const int J0 = pc * kPfChunkBlocks + sg * kPfStageBlocks;
+    if (J0 >= a.nb) return;  // uniform: no block of the stage is visible to any query
+    const int tid = (int)threadIdx.x, lane = lane_id();
+    const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
+    const int col = lane & 15, g = lane >> 4;
+    const bool gl = g < G;
+    if (tid < kPfStageBlocks) {
+        const int j = J0 + tid;
+        meta.phys[tid] = (int32_t)phys_block(a, j);
+        meta.kspan[tid] = j < a.nb ? a.kspan[j] : (uint8_t)0;
+    }
+    __syncthreads();
+    pf_dma<H, G, kRsWaves>(a, meta, 0, st, pf_swizzle16<H>(lane));
+
+    // this wave's 16-position tile: blocks 2u, 2u + 1 of the stage
+    const int u = wave;
+    const int p0 = (J0 + 2 * u) * kBlk;
+    const int bi = 2 * u + (col >> 3), sl = col & 7;
+    const int row = g * kBlk + sl;
+    const uint32_t kspan_t = max((uint32_t)meta.kspan[2 * u], (uint32_t)meta.kspan[2 * u + 1]);
+    const bool pres = meta.phys[2 * u + (g >> 1)] >= 0;  // the block of the lane's output rows
+    const uint32_t *nw = a.need + ((int64_t)pc * 8 + sg / 4) * a.n_q;
+    const int nsh = 8 * (sg % 4);
+
+    for (int qb = 0; qb < a.n_q; qb += kRsBatch) {
+        // list the batch's queries per tile: each lane counts its entries per tile, a wave
+        // scan places them, and one LDS atomic per tile and wave reserves the wave's range
+        constexpr int NI = kRsBatch / kRsThreads;
+        uint32_t m8[NI / 4];  // the flag bytes of the thread's NI queries, four per word
+#pragma unroll
+        for (int i = 0; i < NI / 4; i++) m8[i] = 0u;
+#pragma unroll
+        for (int i = 0; i < NI; i++) {
+            const int q = qb + i * kRsThreads + tid;
+            m8[i / 4] |= (q < a.n_q ? (nw[q] >> nsh) & 0xffu : 0u) << (8 * (i % 4));
+        }
+        if (tid < kRsWaves) cnt[tid] = 0u;
+        // per-lane counts of tiles (0, 1) and (2, 3) in 16-bit fields (wave sums <= 1024)
+        uint32_t c2[2] = {0u, 0u};
+#pragma unroll
+        for (int i = 0; i < NI; i++)
+#pragma unroll
+            for (int t = 0; t < kRsWaves; t++)
+                c2[t / 2] += (((m8[i / 4] >> (8 * (i % 4) + 2 * t)) & 3u) != 0u) ? 1u << (16 * (t % 2)) : 0u;
+        __syncthreads();
+        uint32_t o[kRsWaves];
+#pragma unroll
+        for (int t2 = 0; t2 < 2; t2++) {
+            const uint32_t incl = wave_incl_scan(c2[t2]);
+            const uint32_t tot = __shfl(incl, kWave - 1, kWave);
+            const uint32_t ex = incl - c2[t2];
+#pragma unroll
+            for (int h = 0; h < 2; h++) {
+                const int t = 2 * t2 + h;
+                const uint32_t tt = (tot >> (16 * h)) & 0xffffu;
+                uint32_t base = 0u;
+                if (lane == 0 && tt) base = atomicAdd(&cnt[t], tt);
+                o[t] = __builtin_amdgcn_readfirstlane(base) + ((ex >> (16 * h)) & 0xffffu);
+            }
+        }
+#pragma unroll
+        for (int i = 0; i < NI; i++)
+#pragma unroll
+            for (int t = 0; t < kRsWaves; t++) {
+                const uint32_t f = (m8[i / 4] >> (8 * (i % 4) + 2 * t)) & 3u;
+                if (f != 0u) lst[t][o[t]++] = (uint16_t)(((uint32_t)(i * kRsThreads + tid) << 2) | f);
+            }
+        if (qb == 0) __builtin_amdgcn_s_waitcnt(0);  // the stage's keys
+        __syncthreads();
+        const int n = (int)cnt[u];
+        if (n == 0) {  // uniform
+            __syncthreads();
+            continue;
+        }
+        // the tile's key rows, as the scoring pass reads them
+        uint4 kc[H];
+        uint32_t ksc[H];
+        {
+            const uint8_t *cb = st.codes + bi * S::BSTR;
+#pragma unroll
+            for (int h = 0; h < H; h++)
+                kc[h] = gl ? *reinterpret_cast<const uint4 *>(cb + (row * H + (h ^ (row & (H - 1)))) * 16)
+                           : make_uint4(0u, 0u, 0u, 0u);
+            const int boff = bi * S::SCB + sl * H * G + (gl ? g : 0);
+#pragma unroll
+            for (int h = 0; h < H; h++) {
+                const int o = boff + h * G;
+                ksc[h] = gl ? (st.scales[o >> 2] >> (8 * (o & 3))) : 127u;
+            }
+        }
+        // tiles of 16 listed queries; the next tile's queries are fetched while this one
+        // is computed
+#pragma unroll 1
+        for (int e0 = 0; e0 < n; e0 += 16) {
+            const bool live = e0 + col < n;
+            const uint32_t ent = lst[u][live ? e0 + col : e0];
+            const int q = qb + (int)(ent >> 2);
+            PfQuery<H> Q;
+            pf_gather_query<H, G>(a, q, g, Q);
+            int span = (int)a.qspan[q];
+#pragma unroll
+            for (int o = 1; o < 16; o <<= 1) span = max(span, __shfl_xor(span, o, kWave));
+            const int qspan_t = __builtin_amdgcn_readfirstlane(span);
+            f32x4_t sc = {0.f, 0.f, 0.f, 0.f};
+            if ((int)kspan_t + qspan_t <= kSpanExact) {
+#pragma unroll
+                for (int h0 = 0; h0 < H; h0 += 4) {
+                    constexpr int NH = H < 4 ? H : 4;
+                    f32x4_t d[NH];
+#pragma unroll
+                    for (int i = 0; i < NH; i++) d[i] = mfma_pick(kc[h0 + i], Q.c[h0 + i], ksc[h0 + i], Q.s[h0 / 4], i);
+#pragma unroll
+                    for (int i = 0; i < NH; i++)
+#pragma unroll
+                        for (int r = 0; r < 4; r++) sc[r] = __builtin_fmaf(Q.w[h0 + i], relu0(d[i][r]), sc[r]);
+                }
+            } else {
+                // exact by construction: one product per group (the other groups' key lanes
+                // zeroed), summed in group order; one head at a time (a rare path, kept small)
+#pragma unroll
+                for (int h = 0; h < H; h++) {
+                    f32x4_t d = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                    for (int g2 = 0; g2 < G; g2++) {
+                        uint4 kz = g == g2 ? kc[h] : make_uint4(0u, 0u, 0u, 0u);
+                        // (formed here, not hoisted out of the tile loop for every head and group)
+                        asm volatile("" : "+v"(kz.x), "+v"(kz.y), "+v"(kz.z), "+v"(kz.w));
+                        const f32x4_t t = mfma_pick(kz, Q.c[h], ksc[h], Q.s[h / 4], h % 4);
+#pragma unroll
+                        for (int r = 0; r < 4; r++) d[r] = d[r] + t[r];
+                    }
+#pragma unroll
+                    for (int r = 0; r < 4; r++) sc[r] = __builtin_fmaf(Q.w[h], relu0(d[r]), sc[r]);
+                }
+            }
+            // lane: query q, positions p0 + 4g .. p0 + 4g + 3 (block 2u + g/2 of the stage)
+            const int t = a.q_pos0 + q, pl = p0 + 4 * g;
+#pragma unroll
+            for (int r = 0; r < 4; r++)
+                if (!pres || pl + r > t) sc[r] = -INFINITY;
+            if (live && ((ent >> (g >> 1)) & 1u)) {
+                const int j = J0 + 2 * u + (g >> 1);
+                *reinterpret_cast<f32x4_t *>(a.pscore + ((int64_t)j * a.n_q + q) * kBlk + 4 * (g & 1)) = sc;
+            }
+        }
+        __syncthreads();  // the lists are rewritten by the next round
+    }
+}
+
 typedef void (*PfFn)(const PrefillArgs &, int, hipStream_t);
 
 // Launch of one scoring kernel: query tiles of the mode's workgroup size x position chunks.
@@ -696,7 +874,7 @@ void launch_prefill(const PrefillArgs &a, int pass, hipStream_t s) {
         k_prefill_span<H, G><<<spans, 256, 0, s>>>(a);
         launch_mode<H, G, false, kPfMaxima>(a, s);
     } else {
-        launch_mode<H, G, false, kPfRescore>(a, s);
+        k_prefill_rescore<H, G><<<a.n_pc * (kPfChunkBlocks / kPfStageBlocks), kRsThreads, 0, s>>>(a);
     }
 }
 
@@ -714,10 +892,11 @@ bool pick_prefill(int H, int dI, PfFn *fn) {
 
 // Workspace of a prefill chunk: position scores (block-major), block and group maxima, key
 // spans; with more than 16 queries also the block flags (8 words per chunk of 256 blocks and
-// query), the flagged blocks (K_blk per query) and their per-query bounds; with at most 16
+// query, word-major), the flagged blocks (K_blk per query), their per-query bounds and the
+// queries' scale spans; with at most 16
 // queries over a long table, the regions of the two-phase Full selection.
 struct WsPrefill {
-    size_t pscore, bscore, gmax, kspan, need, list, meta;
+    size_t pscore, bscore, gmax, kspan, need, list, meta, qspan;
     int nw;
     size_t cand, mu_sc, mu_blk, cnt, arrive, total;
 };
@@ -735,6 +914,7 @@ WsPrefill ws_prefill(const csa2_config *c, int n_q, int maxb) {
     w.need = o;   o = align256(o + (two ? sizeof(uint32_t) * 8 * (size_t)npc * n_q : 0));
     w.list = o;   o = align256(o + (two ? sizeof(int32_t) * (size_t)K_blk * n_q : 0));
     w.meta = o;   o = align256(o + (two ? sizeof(uint4) * (size_t)n_q : 0));
+    w.qspan = o;  o = align256(o + (two ? (size_t)n_q : 0));
     w.nw = two ? 0 : sel2_workgroups(c, maxb);
     const size_t regs = (size_t)n_q * w.nw;
     w.cand = o;   o = align256(o + sizeof(uint2) * regs * kSel2GroupsPerW * kItemBlocks);
@@ -790,6 +970,7 @@ int prefill_setup(const csa2_config *c, const uint8_t *q_codes, const uint8_t *q
     a->bscore = (float *)(base + L.bscore);
     a->gmax = (float *)(base + L.gmax);
     a->need = (uint32_t *)(base + L.need);
+    a->qspan = base + L.qspan;
     a->arrive = L.nw ? (int32_t *)(base + L.arrive) : nullptr;
     a->ngmax = ngmax_of(maxb);
     a->n_pc = (a->nb + kPfChunkBlocks - 1) / kPfChunkBlocks;

@@ -49,8 +49,9 @@ struct SelectArgs {
     int32_t *topk_len;
     Sel2Ws sel2;  // two-phase Full selection (sel2.nw > 0)
     // Prefill in two passes (csa2_index_prefill with more than 16 queries): flags of the
-    // blocks whose position scores the top-k reads, 8 words per (chunk of 256 blocks, query)
-    // at pf_need[(chunk*B + b)*8]; those blocks of each query, ascending, at pf_list[b*K_blk];
+    // blocks whose position scores the top-k reads, word w (blocks 32w .. 32w + 31) of chunk
+    // c (256 blocks) of query b at pf_need[(c*8 + w)*B + b]; those blocks of each query,
+    // ascending, at pf_list[b*K_blk];
     // per query (lower bound key of its k-th best score, upper bound key, count) in pf_meta.
     uint32_t *pf_need;
     int32_t *pf_list;

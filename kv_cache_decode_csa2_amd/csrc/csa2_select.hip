@@ -617,7 +617,7 @@ __global__ __launch_bounds__(kSelThreads) void k_select_pf_pool(SelectArgs a) {
         if (fl & (1u << q)) {
             const int j = pj[q];
             lst[o++] = j;
-            atomicOr(&a.pf_need[((int64_t)(j >> 8) * a.B + b) * 8 + ((j & 255) >> 5)], 1u << (j & 31));
+            atomicOr(&a.pf_need[((int64_t)(j >> 8) * 8 + ((j & 255) >> 5)) * a.B + b], 1u << (j & 31));
         }
     }
     int32_t *pool_out = a.pool_blocks + (int64_t)b * a.K_blk;

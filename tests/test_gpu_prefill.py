@@ -54,7 +54,7 @@ def _ws_scores(ws, n_q, maxb, blk0=0, blk1=None):
 def _ws_flags(ws, n_q, maxb, K_blk):
     """More than 16 queries (two scoring passes): per query the flagged blocks (those whose
     position scores the rescoring pass wrote) from the ascending list and its count, and
-    from the flag words [chunk of 256 blocks][query][8 words]."""
+    from the flag words [chunk of 256 blocks][word of 32 blocks][query]."""
     ng = _ngmax(maxb)
     row = n_q * 8 * 4
     ob = _al(maxb * row)
@@ -64,11 +64,11 @@ def _ws_flags(ws, n_q, maxb, K_blk):
     npc = (maxb + 255) // 256
     ol = _al(on + 8 * npc * n_q * 4)
     om = _al(ol + K_blk * n_q * 4)
-    words = _np(ws[on:on + 8 * npc * n_q * 4].view(torch.int32)).view(np.uint32).reshape(npc, n_q, 8)
+    words = _np(ws[on:on + 8 * npc * n_q * 4].view(torch.int32)).view(np.uint32).reshape(npc, 8, n_q)
     lst = _np(ws[ol:ol + K_blk * n_q * 4].view(torch.int32)).reshape(n_q, K_blk)
     meta = _np(ws[om:om + 16 * n_q].view(torch.int32)).view(np.uint32).reshape(n_q, 4)
     listed = [lst[i, :meta[i, 2]].copy() for i in range(n_q)]
-    bits = np.unpackbits(words.transpose(1, 0, 2).reshape(n_q, -1).view(np.uint8),
+    bits = np.unpackbits(np.ascontiguousarray(words.transpose(2, 0, 1)).reshape(n_q, -1).view(np.uint8),
                          axis=1, bitorder="little")
     flagged = [np.flatnonzero(bits[i]).astype(np.int32) for i in range(n_q)]
     return listed, flagged
