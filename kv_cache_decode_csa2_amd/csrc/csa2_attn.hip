@@ -228,7 +228,13 @@ __global__ __launch_bounds__(NS * kStreamThreads, 3 - NS) void k_attn(AttnArgs a
     __shared__ __align__(16) float4 fstage[kD / 4];  // the appended fp32 row, staged by DMA
     __shared__ __align__(16) uint4 qtile[NS == 2 ? 16 * (kD / 8 + 1) : 1];  // 16 query rows, padded
 
-    const int s = blockIdx.x, b = blockIdx.y / a.HG, hg = blockIdx.y % a.HG;
+    // One split per pair (prefill, large batches): XCD x (dispatch places workgroup i on XCD
+    // i % 8) takes a contiguous range of (sequence, head group) pairs in order, so the head
+    // groups of one query, which read the same rows, and neighbouring queries, whose windows
+    // overlap, share that XCD's L2.
+    int pair = (int)blockIdx.y;
+    if (a.nsplit == 1 && gridDim.y % 8 == 0) pair = (pair % 8) * (int)(gridDim.y / 8) + pair / 8;
+    const int s = blockIdx.x, b = pair / a.HG, hg = pair % a.HG;
     const int tid = threadIdx.x, lane = tid & 63;
     const int st = NS == 2 ? tid / kStreamThreads : 0, ts = tid % kStreamThreads, wave = ts >> 6;
     const int c16 = lane & 15, g4 = lane >> 4;

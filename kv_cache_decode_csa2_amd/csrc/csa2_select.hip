@@ -568,8 +568,10 @@ __device__ __forceinline__ int pf_query_of(int bid, int n) {
     return 4 * (8 * (slot / 4) + x) + slot % 4;
 }
 
-// Phase 0, one workgroup per query: pool, theta, flagged blocks.
-__global__ __launch_bounds__(kSelThreads) void k_select_pf_pool(SelectArgs a) {
+// Phase 0, one workgroup per query: pool, theta, flagged blocks.  Built for 8 waves per SIMD
+// (two workgroups per CU): thousands of these latency-bound selections run per chunk, and a
+// second resident workgroup hides their barriers and round trips at the cost of a few spills.
+__global__ __launch_bounds__(kSelThreads, 8) void k_select_pf_pool(SelectArgs a) {
     extern __shared__ __align__(16) uint8_t sh_raw[];
     SelectShared &sm = *reinterpret_cast<SelectShared *>(sh_raw);
     const int b = pf_query_of((int)blockIdx.x, (int)gridDim.x), tid = threadIdx.x;
@@ -630,7 +632,7 @@ __global__ __launch_bounds__(kSelThreads) void k_select_pf_pool(SelectArgs a) {
 
 // Phase 1, one workgroup per query: the top-k among the positions of the flagged blocks that
 // score >= theta (the position scores of exactly those blocks were recomputed).
-__global__ __launch_bounds__(kSelThreads) void k_select_pf_topk(SelectArgs a) {
+__global__ __launch_bounds__(kSelThreads, 8) void k_select_pf_topk(SelectArgs a) {
     extern __shared__ __align__(16) uint8_t sh_raw[];
     SelectShared &sm = *reinterpret_cast<SelectShared *>(sh_raw);
     const int b = blockIdx.x, tid = threadIdx.x;
