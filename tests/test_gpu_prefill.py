@@ -171,6 +171,7 @@ def _check(wl, n_q, permute=True, scale_fn=None, w=None):
     (4, 64, 700, 200),     # two groups per head
     (2, 32, 130, 130),     # one group per head; queries from position 0 (prefix of 1)
     (1, 128, 2100, 70),
+    (2, 32, 4300, 4160),   # more queries than one listing round of the rescoring pass (4096)
     # at most 16 queries: the waves split each stage's positions
     (4, 64, 5000, 6),      # verification step: 6 queries, 3 position chunks (ragged)
     (8, 128, 2800, 16),
