@@ -296,6 +296,12 @@ struct PfQuery {
     float w[H];
 };
 
+// Blocks per position chunk of a scoring workgroup.  At most 16 queries the scoring kernel
+// streams the keys with little work per byte, so its chunks are halved: twice the
+// workgroups are resident, and twice the staged bytes are in flight.
+template <bool SMALL>
+__host__ __device__ constexpr int pf_chunk_blocks() { return SMALL ? kPfChunkBlocks / 2 : kPfChunkBlocks; }
+
 template <int H, int G, bool SMALL, int MODE>
 __global__ __launch_bounds__(PfShape<MODE>::threads, 8 / PfShape<MODE>::waves) void k_prefill(PrefillArgs a) {
     using S = PfStage<H, G>;
@@ -315,9 +321,9 @@ __global__ __launch_bounds__(PfShape<MODE>::threads, 8 / PfShape<MODE>::waves) v
     const int pc = lin / a.n_qt, qt = lin % a.n_qt;
     const int Q0 = qt * kPfQT;
     const int qlast = min(a.n_q, Q0 + kPfQT) - 1;
-    const int Jbeg = pc * kPfChunkBlocks;
+    const int Jbeg = pc * pf_chunk_blocks<SMALL>();
     // blocks this tile can see: j*8 <= q_pos0 + qlast
-    const int Jend = min(min(a.nb, Jbeg + kPfChunkBlocks), (a.q_pos0 + qlast) / kBlk + 1);
+    const int Jend = min(min(a.nb, Jbeg + pf_chunk_blocks<SMALL>()), (a.q_pos0 + qlast) / kBlk + 1);
     // the flags of this (chunk, query tile), set by the pool selection and read by the
     // rescoring pass: cleared here by every workgroup, including those that see nothing of
     // the chunk
@@ -337,7 +343,7 @@ __global__ __launch_bounds__(PfShape<MODE>::threads, 8 / PfShape<MODE>::waves) v
     // the chunk's table entries and key spans (blocks past Jend: absent, span 0)
     // (at most 16 queries: one workgroup per position chunk, which computes the spans of its
     // own blocks here instead of reading them from the span pass)
-    for (int i = (int)threadIdx.x; i < kPfChunkBlocks; i += kPfThreads) {
+    for (int i = (int)threadIdx.x; i < pf_chunk_blocks<SMALL>(); i += kPfThreads) {
         const int j = Jbeg + i;
         const int32_t ph = j < Jend ? (int32_t)phys_block(a, j) : -1;
         meta.phys[i] = ph;
@@ -858,6 +864,7 @@ template <int H, int G, bool SMALL, int MODE>
 void launch_mode(PrefillArgs a, hipStream_t s) {
     using P = PfShape<MODE>;
     a.n_qt = (a.n_q + P::qt - 1) / P::qt;
+    a.n_pc = (a.nb + pf_chunk_blocks<SMALL>() - 1) / pf_chunk_blocks<SMALL>();
     k_prefill<H, G, SMALL, MODE><<<a.n_qt * a.n_pc, P::threads, 0, s>>>(a);
 }
 
