@@ -635,8 +635,7 @@ def counter_summary(a, wl):
             rows = [r for r in csv.DictReader(f) if r["Counter_Name"] == ctr]
         kern = [float(r["Counter_Value"]) for r in rows if _counted(kind, kname, r["Kernel_Name"])]
         if kind == "prefill":
-            resc = [float(r["Counter_Value"]) for r in rows
-                    if kname in r["Kernel_Name"] and _targs(kname, r["Kernel_Name"]).endswith(", 2")]
+            resc = [float(r["Counter_Value"]) for r in rows if "k_prefill_rescore<" in r["Kernel_Name"]]
             raw["rescore_" + ctr] = sum(resc) / max(1, len(resc))
         copies = [float(r["Counter_Value"]) for r in rows if "copyBuffer" in r["Kernel_Name"]]
         if not kern or not copies:
@@ -661,7 +660,7 @@ def counter_summary(a, wl):
                         "write_kib_raw": raw["WRITE_SIZE"][2], "fetch_factor": round(ff, 4),
                         "write_factor": round(wf, 4)},
         "fetch_bytes": int(fetch), "write_bytes": int(write), "bytes_per_launch": int(fetch + write),
-        **({"rescoring_pass": {"kernel": "k_prefill<H, G, false, 2>",
+        **({"rescoring_pass": {"kernel": "k_prefill_rescore<H, G>",
                                "fetch_bytes": int(raw["rescore_FETCH_SIZE"] * 1024.0 * ff),
                                "write_bytes": int(raw["rescore_WRITE_SIZE"] * 1024.0 * wf)}}
            if kind == "prefill" else {}),
