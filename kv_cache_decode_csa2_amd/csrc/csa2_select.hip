@@ -614,13 +614,29 @@ __global__ __launch_bounds__(kSelThreads, 8) void k_select_pf_pool(SelectArgs a)
     uint32_t cnt;
     uint32_t o = block_excl_scan<kSelThreads>((uint32_t)__popc(fl), sm.sel.scan, &cnt);
     int32_t *lst = a.pf_list + (int64_t)b * a.K_blk;
+    // the query's flag words (word i: blocks 32i .. 32i + 31, i.e. word (i % 8) of chunk i / 8)
+    // are built in LDS (the group list is free now) and stored once each, nonzero ones only;
+    // a table too long for that sets them with global atomics
+    const int nwords = (nb + 31) / 32;
+    const bool lds_bits = nwords <= 2 * kSelThreads;  // uniform
+    uint32_t *fb = reinterpret_cast<uint32_t *>(sm.flag);
+    if (lds_bits) {
+        for (int i = tid; i < nwords; i += kSelThreads) fb[i] = 0u;
+        __syncthreads();
+    }
 #pragma unroll
     for (int q = 0; q < 2; q++) {
         if (fl & (1u << q)) {
             const int j = pj[q];
             lst[o++] = j;
-            atomicOr(&a.pf_need[((int64_t)(j >> 8) * 8 + ((j & 255) >> 5)) * a.B + b], 1u << (j & 31));
+            if (lds_bits) atomicOr(&fb[j >> 5], 1u << (j & 31));
+            else atomicOr(&a.pf_need[(int64_t)(j >> 5) * a.B + b], 1u << (j & 31));
         }
+    }
+    if (lds_bits) {
+        __syncthreads();
+        for (int i = tid; i < nwords; i += kSelThreads)
+            if (fb[i]) a.pf_need[(int64_t)i * a.B + b] = fb[i];
     }
     int32_t *pool_out = a.pool_blocks + (int64_t)b * a.K_blk;
     for (int i = tid; i < a.K_blk; i += kSelThreads) pool_out[i] = i < np ? sm.pool[i] : -1;
