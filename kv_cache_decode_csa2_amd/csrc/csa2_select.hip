@@ -401,6 +401,64 @@ __device__ __forceinline__ int select_pool(const SelectArgs &a, int b, int nb, S
     return K;
 }
 
+// One histogram pass over the keys (0: no item) with two targets: lower edges of the bins
+// holding the K1-th and the K2-th largest key (K1, K2 <= the number of keys); kmax (when
+// given) receives the largest key.
+template <class Src>
+__device__ void two_bounds(const Src &src, uint32_t K1, uint32_t K2, SelShared &sm,
+                           uint32_t *e1, uint32_t *e2, uint32_t *kmax = nullptr) {
+    const int tid = threadIdx.x, lane = lane_id(), wave = threadIdx.x / kWave;
+    uint32_t lo = 0xFFFFFFFFu, hi = 0u, n = 0u;
+    src.each([&](uint32_t key) {
+        lo = min(lo, key ? key : 0xFFFFFFFFu);
+        hi = max(hi, key);
+        n += key != 0u;
+    });
+    block_min_max_count(lo, hi, n, sm);
+    if (kmax) *kmax = n ? hi : 0u;
+    if (n == 0u || lo >= hi) {  // no key, or all equal
+        *e1 = *e2 = n ? lo : 0u;
+        return;
+    }
+    const uint32_t w = hi - lo;
+    const int s = max(0, 32 - __clz((int)w) - 11);  // (w >> s) < 2048
+    const int nbins = (int)(w >> s) + 1, li0 = nbins - 1;
+    src.each([&](uint32_t key) {
+        const uint32_t off = key - lo;  // wraps for key 0
+        if (key != 0u && off <= w) atomicAdd(&sm.hist[li0 - (int)(off >> s)], 1u);
+    });
+    __syncthreads();
+    // thread t: reversed bins 2t, 2t + 1 (highest bin first), read and cleared
+    const int r0 = 2 * tid;
+    uint2 hv = make_uint2(0u, 0u);
+    if (r0 < nbins) {
+        hv = *reinterpret_cast<const uint2 *>(&sm.hist[r0]);
+        *reinterpret_cast<uint2 *>(&sm.hist[r0]) = make_uint2(0u, 0u);
+    }
+    const uint32_t c0 = hv.x, c1 = r0 + 1 < nbins ? hv.y : 0u, v = c0 + c1;
+    const uint32_t incl = wave_incl_scan(v);
+    if (lane == kWave - 1) sm.scan[wave] = incl;
+    __syncthreads();
+    uint32_t pw = 0u;
+#pragma unroll
+    for (int i = 0; i < kSelThreads / kWave; i += 4) {
+        const uint4 q = *reinterpret_cast<const uint4 *>(&sm.scan[i]);
+        const uint32_t x[4] = {q.x, q.y, q.z, q.w};
+#pragma unroll
+        for (int j = 0; j < 4; j++) pw += i + j < wave ? x[j] : 0u;
+    }
+    const uint32_t before = pw + incl - v;
+    const uint32_t T[2] = {K1, K2};
+#pragma unroll
+    for (int i = 0; i < 2; i++)
+        if (before < T[i] && T[i] <= before + v)
+            sm.res[i] = (uint32_t)(li0 - (T[i] <= before + c0 ? r0 : r0 + 1));
+    __syncthreads();
+    *e1 = lo + (sm.res[0] << s);
+    *e2 = lo + (sm.res[1] << s);
+    __syncthreads();  // (res is written again by later selections)
+}
+
 // Top-k among the visible positions of the pool.  Thread t owns pool entries 2t and 2t+1.
 // Only positions scoring >= a lower bound of the k-th largest position score are
 // candidates.  Full: the pool threshold (each of the plen pool blocks has a position at
@@ -464,7 +522,12 @@ __device__ __forceinline__ void select_topk(const SelectArgs &a, int b, int L, c
     if (need > 0 && need < (n_vis >> 16) && need <= n_ent) {
         // Reindex: kmax receives the largest rescored block maximum, the upper end of every
         // candidate key
-        if (REINDEX) lam = n_ent > need ? range_select(bm, need, sm.sel, false, 0u, 0u, &kmax).thr : 0u;
+        // (a lower bound serves: one histogram pass gives the lower edge of the bin holding
+        // the need-th largest rescored maximum, and the exact selection below is bounded by it)
+        if (REINDEX && n_ent > need) {
+            uint32_t e2;
+            two_bounds(bm, need, need, sm.sel, &lam, &e2, &kmax);
+        }
         else lam = pool_thr;
     }
     // candidate positions scoring >= lam (Reindex: of entries whose maximum reaches lam)
@@ -680,62 +743,6 @@ __global__ __launch_bounds__(kSelThreads, 8) void k_select_pf_topk(SelectArgs a)
 // The last workgroup keeps the candidates in LDS (at most kSel2LdsCap) and one bound-reaching
 // block per thread.  Sequences that fit the pool, and candidate sets beyond those limits
 // (heavy ties), take the one-workgroup selection in the last workgroup instead.
-
-// One histogram pass over the keys (0: no item) with two targets: lower edges of the bins
-// holding the K1-th and the K2-th largest key (K1, K2 <= the number of keys).
-template <class Src>
-__device__ void two_bounds(const Src &src, uint32_t K1, uint32_t K2, SelShared &sm,
-                           uint32_t *e1, uint32_t *e2) {
-    const int tid = threadIdx.x, lane = lane_id(), wave = threadIdx.x / kWave;
-    uint32_t lo = 0xFFFFFFFFu, hi = 0u, n = 0u;
-    src.each([&](uint32_t key) {
-        lo = min(lo, key ? key : 0xFFFFFFFFu);
-        hi = max(hi, key);
-        n += key != 0u;
-    });
-    block_min_max_count(lo, hi, n, sm);
-    if (n == 0u || lo >= hi) {  // no key, or all equal
-        *e1 = *e2 = n ? lo : 0u;
-        return;
-    }
-    const uint32_t w = hi - lo;
-    const int s = max(0, 32 - __clz((int)w) - 11);  // (w >> s) < 2048
-    const int nbins = (int)(w >> s) + 1, li0 = nbins - 1;
-    src.each([&](uint32_t key) {
-        const uint32_t off = key - lo;  // wraps for key 0
-        if (key != 0u && off <= w) atomicAdd(&sm.hist[li0 - (int)(off >> s)], 1u);
-    });
-    __syncthreads();
-    // thread t: reversed bins 2t, 2t + 1 (highest bin first), read and cleared
-    const int r0 = 2 * tid;
-    uint2 hv = make_uint2(0u, 0u);
-    if (r0 < nbins) {
-        hv = *reinterpret_cast<const uint2 *>(&sm.hist[r0]);
-        *reinterpret_cast<uint2 *>(&sm.hist[r0]) = make_uint2(0u, 0u);
-    }
-    const uint32_t c0 = hv.x, c1 = r0 + 1 < nbins ? hv.y : 0u, v = c0 + c1;
-    const uint32_t incl = wave_incl_scan(v);
-    if (lane == kWave - 1) sm.scan[wave] = incl;
-    __syncthreads();
-    uint32_t pw = 0u;
-#pragma unroll
-    for (int i = 0; i < kSelThreads / kWave; i += 4) {
-        const uint4 q = *reinterpret_cast<const uint4 *>(&sm.scan[i]);
-        const uint32_t x[4] = {q.x, q.y, q.z, q.w};
-#pragma unroll
-        for (int j = 0; j < 4; j++) pw += i + j < wave ? x[j] : 0u;
-    }
-    const uint32_t before = pw + incl - v;
-    const uint32_t T[2] = {K1, K2};
-#pragma unroll
-    for (int i = 0; i < 2; i++)
-        if (before < T[i] && T[i] <= before + v)
-            sm.res[i] = (uint32_t)(li0 - (T[i] <= before + c0 ? r0 : r0 + 1));
-    __syncthreads();
-    *e1 = lo + (sm.res[0] << s);
-    *e2 = lo + (sm.res[1] << s);
-    __syncthreads();  // (res is written again by later selections)
-}
 
 // Prefix sums of the regions' candidate counts (pre) and bound-reaching block counts (mpre)
 // of sequence b, and whether the two-phase selection holds: every region kept its
