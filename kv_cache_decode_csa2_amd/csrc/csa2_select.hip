@@ -786,7 +786,7 @@ __device__ __forceinline__ void full2_topk(const SelectArgs &a, int b, int L, bo
     const Sel2Ws &q = a.sel2;
     const int nw = q.nw, tid = threadIdx.x;
     __shared__ int32_t sh_pre2[kSel2MaxW + 1];
-    uint32_t mu = 0u;
+    uint32_t mu = 0u, ghi = 0u;
     if (fast) {
         RegItems<kIPT> g;
 #pragma unroll
@@ -796,7 +796,7 @@ __device__ __forceinline__ void full2_topk(const SelectArgs &a, int b, int L, bo
             for (int t = 0; t < 4; t++) g.key[i + t] = tid * kIPT + i + t < ng ? order_key(f[t]) : 0u;
         }
         uint32_t lam;
-        two_bounds(g, (uint32_t)min(a.K_blk, ng), (uint32_t)a.k, sm.sel, &lam, &mu);
+        two_bounds(g, (uint32_t)min(a.K_blk, ng), (uint32_t)a.k, sm.sel, &lam, &mu, &ghi);
     }
     // wait for the gather workgroups: relaxed coherent polls (an acquire per poll would
     // invalidate this XCD's caches under the gather workgroups' reads), then one agent-scope
@@ -837,9 +837,10 @@ __device__ __forceinline__ void full2_topk(const SelectArgs &a, int b, int L, bo
             p.key[t] = mb >= 0 && mb * kBlk + t < L && key >= mu ? key : 0u;
         }
     }
-    // top-k: the exact top-k of the positions >= mu of the blocks >= mu, ascending
+    // top-k: the exact top-k of the positions >= mu of the blocks >= mu, ascending (every
+    // such key lies in [mu, largest group maximum])
     select_emit(p, [&](int t) { return mb * kBlk + t; }, (uint32_t)a.k,
-                a.topk + (int64_t)b * a.k, (uint32_t)a.k, sm);
+                a.topk + (int64_t)b * a.k, (uint32_t)a.k, sm, ghi != 0u, mu, ghi);
     if (tid == 0) a.topk_len[b] = a.k;
 }
 
@@ -873,7 +874,7 @@ __global__ __launch_bounds__(kSelThreads) void k_select_full2(SelectArgs a) {
     for (int i = tid; i < kHistBins; i += kSelThreads) sm.sel.hist[i] = 0u;  // kept zero between passes
     __syncthreads();
     const bool fast = nb > a.K_blk && a.K_blk >= a.k && ng > a.k;  // uniform per sequence
-    uint32_t lam = 0u, mu = 0u;
+    uint32_t lam = 0u, mu = 0u, ghi = 0u;
     int cnt_c = 0, cnt_m = 0;
     const int64_t reg = (int64_t)b * nw + w;
     if (w == nw) {  // the top-k workgroup (uniform)
@@ -888,7 +889,7 @@ __global__ __launch_bounds__(kSelThreads) void k_select_full2(SelectArgs a) {
 #pragma unroll
             for (int t = 0; t < 4; t++) g.key[i + t] = tid * kIPT + i + t < ng ? order_key(f[t]) : 0u;
         }
-        two_bounds(g, (uint32_t)min(a.K_blk, ng), (uint32_t)a.k, sm.sel, &lam, &mu);
+        two_bounds(g, (uint32_t)min(a.K_blk, ng), (uint32_t)a.k, sm.sel, &lam, &mu, &ghi);
         if (ng <= a.K_blk) lam = 1u;  // every group holds pool candidates (real keys are >= 1)
         // this workgroup's candidates: the blocks >= lam of group gi (whose maximum is then
         // >= lam), and among them the blocks >= mu
@@ -983,7 +984,8 @@ __global__ __launch_bounds__(kSelThreads) void k_select_full2(SelectArgs a) {
     // pool: the exact top-K_blk of the candidates, emitted ascending from LDS (thread t owns
     // candidates [8t, 8t + 8))
     {
-        const SelResult r = range_select(c, (uint32_t)a.K_blk, sm.sel);
+        // every candidate key lies in [lam, largest group maximum]
+        const SelResult r = range_select(c, (uint32_t)a.K_blk, sm.sel, ghi != 0u, lam, ghi);
         constexpr int PT = kSel2LdsCap / kSelThreads;
         RegItems<PT> o;
         int32_t oid[PT];
