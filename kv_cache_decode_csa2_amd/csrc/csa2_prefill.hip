@@ -399,6 +399,15 @@ __global__ __launch_bounds__(PfShape<MODE>::threads, 8 / PfShape<MODE>::waves) v
         qspan[jq] = __builtin_amdgcn_readfirstlane(span);
     }
 
+    // the lane's byte offset, inside a stage, of head h's 16-byte chunk of its key row in
+    // 16-position tile 0 (tile u adds 2u blocks): fixed for the kernel, so every LDS read
+    // of the keys is this register plus an immediate
+    uint32_t koff[H];
+#pragma unroll
+    for (int h = 0; h < H; h++) {
+        const int row = g * kBlk + (col & 7);
+        koff[h] = (uint32_t)((col >> 3) * S::BSTR + (row * H + (h ^ (row & (H - 1)))) * 16);
+    }
     // scores of one staged stage: 4 tiles of 16 positions x the wave's 2 tiles of 16 queries
     auto compute = [&](const S &cur, int sidx) {
         const int J0 = Jbeg + sidx * kPfStageBlocks;
@@ -435,11 +444,10 @@ __global__ __launch_bounds__(PfShape<MODE>::threads, 8 / PfShape<MODE>::waves) v
             uint4 kc[H];
             uint32_t ksc[H];
             {
-                const uint8_t *cb = cur.codes + bi * S::BSTR;
+                const uint8_t *cb = cur.codes + 2 * u * S::BSTR;
 #pragma unroll
                 for (int h = 0; h < H; h++)
-                    kc[h] = gl ? *reinterpret_cast<const uint4 *>(cb + (row * H + (h ^ (row & (H - 1)))) * 16)
-                               : make_uint4(0u, 0u, 0u, 0u);
+                    kc[h] = gl ? *reinterpret_cast<const uint4 *>(cb + koff[h]) : make_uint4(0u, 0u, 0u, 0u);
                 if constexpr (H * G >= 4) {
                     // the position's H*G scale bytes start on a dword; byte h*G + g of
                     // them is byte ((h*G) & 3) + g of dword (h*G) / 4
