@@ -176,6 +176,8 @@ def _check(wl, n_q, permute=True, scale_fn=None, w=None):
     (4, 64, 5000, 6),      # verification step: 6 queries, 3 position chunks (ragged)
     (8, 128, 2800, 16),
     (2, 32, 130, 1),       # one query, two stages
+    (4, 64, 50, 2),        # one stage (the second buffer repeats it)
+    (4, 64, 100, 5),       # two stages
     (1, 128, 2100, 9),
 ])
 def test_prefill_index_bit_exact(H, d, L, n_q):
@@ -218,11 +220,12 @@ def test_prefill_key_spans_decide_the_path(n_q):
         si.idx_keys = orig
 
 
-def test_prefill_wide_exponent_spans_take_the_exact_path():
+@pytest.mark.parametrize("n_q", [260, 12])
+def test_prefill_wide_exponent_spans_take_the_exact_path(n_q):
     """Scales that spread more than 9 binades within a head vector force the per-group
-    path of the matrix kernel; mixed-sign head weights exercise the fma chain's signs."""
+    path of the matrix kernel (at most 16 queries: spans over four groups taken from the
+    staged scales); mixed-sign head weights exercise the fma chain's signs."""
     wl = si.small("pfspan", 121, [3000], H_I=8, d_I=128, K_blk=64, k=128, W=16)
-    n_q = 260
 
     def keys_wide(x):
         blk = np.arange(x.shape[0]) // 8
