@@ -375,8 +375,7 @@ __global__ __launch_bounds__(NS * kStreamThreads, 3 - NS) void k_attn(AttnArgs a
         }
         // ---- this lane's row bytes: a main row's 64 code bytes and 4 scale bytes of dims
         //      g4*128 .., a window row's 128 and 4 (the appended row comes from LDS instead).
-        //      NS = 2 requests them before the barriers below, so that they overlap them
-        //      (NS = 1, whose query slice holds 64 registers across the loop, after them).
+        //      They are requested before the barriers below, so that they overlap them.
         uint4 uu[8];
         uint32_t sc4 = 0u;
         auto load_row = [&] {
@@ -425,8 +424,8 @@ __global__ __launch_bounds__(NS * kStreamThreads, 3 - NS) void k_attn(AttnArgs a
             }
         }
         };
+        load_row();
         if (NS == 2) {
-            load_row();
             quant_fresh();
             // this lane's query slice, while the row bytes are in flight (held only until S,
             // so that P V has the registers to read its V tiles ahead)
@@ -438,12 +437,9 @@ __global__ __launch_bounds__(NS * kStreamThreads, 3 - NS) void k_attn(AttnArgs a
         }
         if (!chunk_rows(c0) && !(NS == 2 && chunk_rows(c0 + a.nsplit))) continue;  // uniform
         __syncthreads();  // the previous chunks are done with V, P and the reductions
-        if (NS == 1) {
-            if (fc == c) {  // uniform: fc and c are the workgroup's
-                quant_fresh();
-                __syncthreads();
-            }
-            load_row();
+        if (NS == 1 && fc == c) {  // uniform: fc and c are the workgroup's
+            quant_fresh();
+            __syncthreads();
         }
 
         // ---- exact conversion to bf16, one piece kb = dims g4*128 + 8t .. +8 of the row at a
