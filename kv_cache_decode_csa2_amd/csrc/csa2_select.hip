@@ -844,13 +844,27 @@ __device__ __forceinline__ void full2_topk(const SelectArgs &a, int b, int L, bo
     if (tid == 0) a.topk_len[b] = a.k;
 }
 
+// XMAP (several sequences, nw a multiple of 8): a one-dimensional grid in which gather
+// workgroup w of every sequence lands on XCD w % 8 (dispatch places workgroup i on XCD
+// i % 8), so that the sequences' workgroups of one group range, which read the same lines of
+// the interleaved block and position scores, share that XCD's L2.  Workgroup 8 k + x takes
+// w = 8 (k / B) + x of sequence k % B (w > nw: none, it returns); every top-k workgroup
+// (w = nw) still has a higher index than all gather workgroups.
+template <bool XMAP>
 __global__ __launch_bounds__(kSelThreads) void k_select_full2(SelectArgs a) {
     extern __shared__ __align__(16) uint8_t sh_raw[];
     SelectShared &sm = *reinterpret_cast<SelectShared *>(sh_raw);
     __shared__ int32_t sh_pre[kSel2MaxW + 1], sh_mpre[kSel2MaxW + 1];
     __shared__ int32_t sh_flag[2];
     const Sel2Ws &q = a.sel2;
-    const int nw = q.nw, w = blockIdx.x, b = blockIdx.y, tid = threadIdx.x;
+    int w = blockIdx.x, b = blockIdx.y;
+    if constexpr (XMAP) {
+        const int id = (int)blockIdx.x, k = id >> 3;
+        b = k % a.B;
+        w = 8 * (k / a.B) + (id & 7);
+        if (w > q.nw) return;  // (uniform, before any barrier)
+    }
+    const int nw = q.nw, tid = threadIdx.x;
     // requests: the thread's 16 group maxima (clamped into the row, masked once the length
     // is known), the length, and the 8 block maxima of this workgroup's group gi
     float4 graw[kIPT / 4];
@@ -1009,8 +1023,11 @@ int launch_select_full2(const SelectArgs &a, hipStream_t stream) {
     if (a.B <= 0) return CSA2_OK;
     // nw gather workgroups per sequence, then its top-k workgroup (the highest index, so that
     // its gather workgroups are dispatched before it)
-    k_select_full2<<<dim3(a.sel2.nw + 1, a.B), kSelThreads, kSelectShared + sizeof(uint2) * kSel2LdsCap,
-                     stream>>>(a);
+    const size_t shm = kSelectShared + sizeof(uint2) * kSel2LdsCap;
+    if (a.B > 1 && a.sel2.nw % 8 == 0)
+        k_select_full2<true><<<8 * a.B * ((a.sel2.nw + 1 + 7) / 8), kSelThreads, shm, stream>>>(a);
+    else
+        k_select_full2<false><<<dim3(a.sel2.nw + 1, a.B), kSelThreads, shm, stream>>>(a);
     return hipGetLastError() == hipSuccess ? CSA2_OK : CSA2_ERR_HIP;
 }
 
