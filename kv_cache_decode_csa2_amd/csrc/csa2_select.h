@@ -68,7 +68,8 @@ int sel2_workgroups(const csa2_config *cfg, int32_t maxb);
 // pool.  Returns a csa2 status.
 int launch_select(const SelectArgs &a, bool reindex, hipStream_t stream);
 
-// The two-phase Full selection (grid sel2.nw x B); a.sel2 filled.
+// The two-phase Full selection (sel2.nw + 1 workgroups per sequence; with several sequences
+// and sel2.nw a multiple of 8, laid out by XCD); a.sel2 filled.
 int launch_select_full2(const SelectArgs &a, hipStream_t stream);
 
 // Prefill selection in two phases around the rescoring pass.  Phase 0: the pool of every

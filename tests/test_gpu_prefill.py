@@ -362,6 +362,31 @@ def test_prefill_workload_sampled():
 
 
 @pytest.mark.slow
+def test_spec_verify_selection_by_xcd():
+    """Three queries at the end of a 500,000-token context: 7,813 groups, so 8 gather
+    workgroups per query and the two-phase selection's XCD layout (gather workgroup w of every
+    query on XCD w % 8, idle workgroups in the padded grid).  Every query's pool and top-k
+    equal the oracle's."""
+    import dataclasses
+    wl = dataclasses.replace(si.workload("spec_1m"), ctx=[500000], n_q=3)
+    n_q, L = wl.n_q, wl.ctx[0]
+    q_pos0 = L - n_q
+    table, nblk = make_table(wl.ctx, seed=wl.seed, permute=False)
+    g = GpuState(wl, table, nblk)
+    o = OracleState(wl, table, nblk)
+    qc, qs, wg = prefill_q(wl, 0, n_q)
+    pgd, plgd, tgd, tlgd = index_prefill(g, qc, qs, wg, q_pos0)
+    pg, plg, tg, tlg = [_np(x) for x in (pgd, plgd, tgd, tlgd)]
+    del g
+    torch.cuda.empty_cache()
+    qo = _oracle_q(wl, n_q)
+    po, plo, to, tlo = oracle.index_prefill(o.cfg, *qo, q_pos0, o.idx, o.table[0])
+    assert np.all(plo == wl.K_blk) and np.all(tlo == wl.k)
+    assert np.array_equal(plg, plo) and np.array_equal(tlg, tlo)
+    assert np.array_equal(pg, po), _first_diff(pg, po)
+    assert np.array_equal(tg, to), _first_diff(tg, to)
+
+
 def test_spec_verify_1m():
     """Speculative verification at 1M context: the token and 5 draft tokens at positions
     1048570..1048575 of a 1,048,576-token context (indexer 4 x 64, pool 2048 blocks,
